@@ -1,0 +1,146 @@
+"""Seeded synthetic inputs for the gated delta rule forward.
+
+This module is shared by the CPU oracle's tests and the HIP library's tests
+and benchmark, and holds none of the method's arithmetic: it only draws
+random tensors, shapes them, and rounds them to the input precision.
+
+Recipe (the distributions come from the workloads the library is measured on;
+the pages give q, k, v, a log-decay g and a write strength beta in the
+jax-linear-attention page's "Quick start", where g = logsigmoid(noise)/4 and
+beta = sigmoid(noise); the workloads here use /16 for g):
+
+  * q, k ~ N(0, 1) per element, each (token, head) row L2-normalised in fp32;
+  * v ~ N(0, 1);
+  * beta = sigmoid(N(0, 1)), g = logsigmoid(N(0, 1)) / 16, both fp32;
+  * bf16 inputs are the fp32 values rounded to nearest-even;
+  * h0, when asked for, ~ N(0, std) in fp32 (std = 0.02 for packed batches);
+  * packed lengths are geometric on {1, 2, ...} with the given mean, drawn
+    until they cover the total, the last one clipped so the sum is exact.
+
+Every tensor draws from its own PCG64 stream spawned from the config seed, so
+a tensor can be drawn in blocks of tokens (and the blocked draw equals the
+whole draw; tested).  bf16 tensors are returned as uint16 bit patterns; use
+`widen` for the exact fp32 values.
+"""
+import numpy as np
+
+_STREAMS = ("q", "k", "v", "g", "beta", "h0", "lengths")
+
+# Elements drawn per block (bounds peak host memory for very long inputs).
+_BLOCK_ELEMS = 1 << 24
+
+
+def _streams(seed):
+    children = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    return {name: np.random.Generator(np.random.PCG64(c)) for name, c in zip(_STREAMS, children)}
+
+
+def bf16_bits(x32):
+    """Round fp32 values to bf16, nearest-even, as uint16 bit patterns.
+    (Inputs here are finite and far from the fp32 range limits.)"""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    u = u + (((u >> 16) & 1) + np.uint32(0x7FFF))
+    return (u >> 16).astype(np.uint16)
+
+
+def widen(x):
+    """Exact fp32 values of an input tensor (uint16 bf16 bits, or fp32)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return np.asarray(x, dtype=np.float32)
+
+
+def _normal_rows(rng, rows, width, std=1.0, normalise=False, out_dtype="f32"):
+    """rows x width N(0, std) draws, drawn in blocks of rows; optionally each
+    row divided by its fp32 L2 norm; returned as fp32 or bf16 bits."""
+    dt = np.uint16 if out_dtype == "bf16" else np.float32
+    out = np.empty((rows, width), dtype=dt)
+    step = max(1, _BLOCK_ELEMS // max(width, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        x = rng.standard_normal((r1 - r0, width), dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        if normalise:
+            x /= np.sqrt(np.sum(x * x, axis=1, dtype=np.float32, keepdims=True))
+        out[r0:r1] = bf16_bits(x) if out_dtype == "bf16" else x
+    return out
+
+
+def geometric_lengths(total, mean, seed):
+    """Document lengths on {1, 2, ...}, geometric with the given mean, drawn
+    until they cover `total` tokens; the last is clipped so they sum to it."""
+    rng = _streams(seed)["lengths"]
+    lengths = []
+    s = 0
+    while s < total:
+        n = int(rng.geometric(1.0 / mean))
+        n = min(n, total - s)
+        lengths.append(n)
+        s += n
+    return lengths
+
+
+def cu_from_lengths(lengths):
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
+
+
+def make(B, T, Hqk, Hv, dk, dv, dtype, seed, h0_std=None, cu_seqlens=None):
+    """Inputs for one forward call.
+
+    Returns a dict with q, k [B, T, Hqk, dk], v [B, T, Hv, dv] (uint16 bf16
+    bits, or fp32), g, beta [B, T, Hv] fp32, h0 [N, Hv, dk, dv] fp32 or None,
+    cu_seqlens int32 [N + 1] or None, and the sizes."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
+    rs = _streams(seed)
+    q = _normal_rows(rs["q"], B * T * Hqk, dk, normalise=True, out_dtype=dtype)
+    k = _normal_rows(rs["k"], B * T * Hqk, dk, normalise=True, out_dtype=dtype)
+    v = _normal_rows(rs["v"], B * T * Hv, dv, out_dtype=dtype)
+    zg = rs["g"].standard_normal(B * T * Hv, dtype=np.float32).astype(np.float64)
+    zb = rs["beta"].standard_normal(B * T * Hv, dtype=np.float32).astype(np.float64)
+    # logsigmoid(z) = -log(1 + exp(-z)), sigmoid(z) = 1 / (1 + exp(-z))
+    g = (-np.logaddexp(0.0, -zg) / 16.0).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-zb))).astype(np.float32)
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    h0 = None
+    if h0_std is not None:
+        h0 = _normal_rows(rs["h0"], N * Hv * dk, dv, std=h0_std).reshape(N, Hv, dk, dv)
+    return {
+        "q": q.reshape(B, T, Hqk, dk), "k": k.reshape(B, T, Hqk, dk),
+        "v": v.reshape(B, T, Hv, dv),
+        "g": g.reshape(B, T, Hv), "beta": beta.reshape(B, T, Hv),
+        "h0": h0,
+        "cu_seqlens": None if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int32),
+        "dtype": dtype, "B": B, "T": T, "Hqk": Hqk, "Hv": Hv, "dk": dk, "dv": dv, "N": N,
+    }
+
+
+# The workloads: a tiny fp32 case, the 8 x 2K headline, a packed batch with
+# grouped value heads, and one long row.  Seeds are 1000 + index.
+CONFIGS = {
+    "tiny_f32": dict(B=1, T=256, Hqk=2, Hv=2, dk=64, dv=64, dtype="f32", seed=1000),
+    "headline_bf16": dict(B=8, T=2048, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16",
+                          seed=1001),
+    "packed_gva_bf16": dict(total=16384, mean_len=1024, Hqk=16, Hv=32, dk=128, dv=128,
+                            dtype="bf16", seed=1002, h0_std=0.02),
+    "long_bf16": dict(B=1, T=1_064_960, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16",
+                      seed=1003),
+}
+
+
+def make_config(name, **override):
+    """Inputs of a named workload; keyword overrides change its sizes (tests
+    use them to shrink a workload while keeping its recipe)."""
+    c = dict(CONFIGS[name])
+    c.update(override)
+    if "total" in c:
+        lengths = geometric_lengths(c["total"], c["mean_len"], c["seed"])
+        cu = cu_from_lengths(lengths)
+        return make(1, c["total"], c["Hqk"], c["Hv"], c["dk"], c["dv"], c["dtype"],
+                    c["seed"], h0_std=c.get("h0_std"), cu_seqlens=cu)
+    return make(c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"], c["dtype"], c["seed"],
+                h0_std=c.get("h0_std"))

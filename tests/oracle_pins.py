@@ -1,0 +1,301 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the
+oracle itself.
+
+Each pin takes `fwd`, a function with the signature of oracle.gdn_fwd, so the
+same pins run against the oracle (test_oracle.py) and against deliberately
+broken copies of it (test_oracle_mutants.py).  A pin raises AssertionError on
+failure.
+
+The recurrence being pinned is the gated delta rule of Gated DeltaNet (the
+December 2024 paper by Yang, Kautz and Hatamizadeh that the Qwen FlashQLA
+article names under "The bottleneck nobody wanted to talk about"):
+S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T, o_t = S_t q_t, with
+a_t = exp(g_t) (g is a natural-log decay; jax-linear-attention page,
+"Quick start") and the state returned as M = S^T of shape [dk, dv].
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_inputs(rng, B, T, Hqk, Hv, dk, dv, unit_keys=True):
+    q = rng.standard_normal((B, T, Hqk, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, Hqk, dk)).astype(np.float32)
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True).astype(np.float32)
+    v = rng.standard_normal((B, T, Hv, dv)).astype(np.float32)
+    g = (-np.logaddexp(0, -rng.standard_normal((B, T, Hv))) / 4).astype(np.float32)
+    beta = (1 / (1 + np.exp(-rng.standard_normal((B, T, Hv))))).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300)
+    assert err <= rtol, f"{what}: relative error {err:.3e} > {rtol:.1e}"
+
+
+# --- closed forms -----------------------------------------------------------
+
+def pin_single_token(fwd):
+    """One token from a zero state: o = beta (k . q) v and M = beta k v^T."""
+    rng = _rng(1)
+    q, k, v, g, beta = _rand_inputs(rng, 2, 1, 3, 3, 5, 4)
+    o, ht = fwd(q, k, v, g, beta)
+    kq = np.einsum("bthd,bthd->bth", k.astype(np.float64), q.astype(np.float64))
+    want_o = beta[..., None] * kq[..., None] * v
+    _close(o, want_o, 1e-14, "single-token output")
+    want_M = beta[:, 0, :, None, None] * k[:, 0, :, :, None].astype(np.float64) \
+        * v[:, 0, :, None, :].astype(np.float64)
+    _close(ht, want_M, 1e-14, "single-token state")
+
+
+def pin_beta0_a1_state_unchanged(fwd):
+    """beta = 0 and a = 1: the state never changes; o_t = M0^T q_t."""
+    rng = _rng(2)
+    q, k, v, g, beta = _rand_inputs(rng, 1, 9, 2, 2, 6, 3)
+    g[:] = 0
+    beta[:] = 0
+    h0 = rng.standard_normal((1, 2, 6, 3))
+    o, ht = fwd(q, k, v, g, beta, h0=h0)
+    assert np.array_equal(ht, h0), "state changed with beta = 0, a = 1"
+    want = np.einsum("bthi,bhic->bthc", q.astype(np.float64), h0)
+    _close(o, want, 1e-14, "read-only output")
+
+
+def pin_beta0_decay_product(fwd):
+    """beta = 0: M_t = (a_1 ... a_t) M0, so o_t = exp(g_1 + ... + g_t) M0^T q_t."""
+    rng = _rng(3)
+    q, k, v, g, beta = _rand_inputs(rng, 1, 11, 1, 1, 4, 5)
+    beta[:] = 0
+    h0 = rng.standard_normal((1, 1, 4, 5))
+    o, ht = fwd(q, k, v, g, beta, h0=h0)
+    cum = np.cumsum(g[0, :, 0].astype(np.float64))
+    want = np.exp(cum)[:, None] * (q[0, :, 0].astype(np.float64) @ h0[0, 0])
+    _close(o[0, :, 0], want, 1e-13, "decay-only output")
+    _close(ht, np.exp(cum[-1]) * h0, 1e-13, "decay-only state")
+
+
+def pin_full_forgetting(fwd):
+    """g = -100 (a = e^-100): each token sees only itself, o_t = beta_t (k_t . q_t) v_t."""
+    rng = _rng(4)
+    q, k, v, g, beta = _rand_inputs(rng, 1, 7, 2, 4, 8, 3)
+    g[:] = -100.0
+    o, _ = fwd(q, k, v, g, beta)
+    kq = np.einsum("bthd,bthd->bth", k.astype(np.float64), q.astype(np.float64))
+    kq = np.repeat(kq, 2, axis=2)  # value head j reads q/k head j // 2
+    want = beta[..., None] * kq[..., None] * v
+    _close(o, want, 1e-13, "full-forgetting output")
+
+
+def pin_exact_write(fwd):
+    """beta = 1 with |k| = 1 exactly: the delta rule overwrites, M_t^T k_t = v_t.
+    Keys have four entries of +-1/2 (so |k|^2 = 1 in binary) and q_t = k_t."""
+    rng = _rng(5)
+    T, dk, dv = 10, 12, 3
+    k = np.zeros((1, T, 1, dk), np.float32)
+    for t in range(T):
+        idx = rng.choice(dk, 4, replace=False)
+        k[0, t, 0, idx] = rng.choice([-0.5, 0.5], 4)
+    q = k.copy()
+    v = rng.standard_normal((1, T, 1, dv)).astype(np.float32)
+    g = (-rng.random((1, T, 1)) * 0.3).astype(np.float32)
+    beta = np.ones((1, T, 1), np.float32)
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    o, _ = fwd(q, k, v, g, beta, h0=h0)
+    _close(o, v, 1e-14, "exact overwrite")
+
+
+def _hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def pin_orthonormal_keys_linear_attention(fwd):
+    """Orthonormal keys, a = 1, beta = 1, zero state: every delta equals its v,
+    so the output is causal linear attention o_t = sum_{s<=t} (k_s . q_t) v_s.
+    Keys are distinct rows of the 16 x 16 Hadamard matrix over 4 (exact)."""
+    rng = _rng(6)
+    dk, dv, T = 16, 5, 12
+    rows = rng.choice(dk, T, replace=False)
+    K = (_hadamard(dk)[rows] / 4.0) * rng.choice([-1.0, 1.0], (T, 1))
+    Q = rng.standard_normal((T, dk)).astype(np.float32)
+    V = rng.standard_normal((T, dv)).astype(np.float32)
+    q, k, v = Q[None, :, None], K.astype(np.float32)[None, :, None], V[None, :, None]
+    g = np.zeros((1, T, 1), np.float32)
+    beta = np.ones((1, T, 1), np.float32)
+    o, ht = fwd(q, k, v, g, beta)
+    scores = np.tril(Q.astype(np.float64) @ K.T)  # [t, s] = q_t . k_s for s <= t
+    want = scores @ V.astype(np.float64)
+    _close(o[0, :, 0], want, 1e-14, "linear-attention output")
+    _close(ht[0, 0], K.T @ V.astype(np.float64), 1e-14, "linear-attention state")
+
+
+def pin_linearity(fwd):
+    """For fixed q, k, g, beta the map (v, h0) -> (o, ht) is linear, and o is
+    homogeneous in q (ht does not depend on q); scale multiplies o only."""
+    rng = _rng(7)
+    q, k, v1, g, beta = _rand_inputs(rng, 2, 13, 2, 2, 6, 4)
+    v2 = rng.standard_normal(v1.shape).astype(np.float32)
+    h1 = rng.standard_normal((2, 2, 6, 4))
+    h2 = rng.standard_normal((2, 2, 6, 4))
+    o1, s1 = fwd(q, k, v1, g, beta, h0=h1)
+    o2, s2 = fwd(q, k, v2, g, beta, h0=h2)
+    o12, s12 = fwd(q, k, v1 + v2, g, beta, h0=h1 + h2)
+    # v1 + v2 rounds to fp32; compare against the fp32 sum's own run.
+    _close(o12, o1 + o2, 1e-6, "additivity (output)")
+    _close(s12, s1 + s2, 1e-6, "additivity (state)")
+    o4, s4 = fwd(q, k, 4 * v1, g, beta, h0=4 * h1)
+    assert np.array_equal(o4, 4 * o1) and np.array_equal(s4, 4 * s1), "not homogeneous in (v, h0)"
+    oq, sq = fwd(0.5 * q, k, v1, g, beta, h0=h1)
+    assert np.array_equal(oq, 0.5 * o1) and np.array_equal(sq, s1), "not homogeneous in q"
+    os_, ss = fwd(q, k, v1, g, beta, scale=0.125, h0=h1)
+    assert np.array_equal(os_, 0.125 * o1) and np.array_equal(ss, s1), "scale misapplied"
+
+
+def pin_exact_rational(fwd):
+    """Brute force in exact rational arithmetic on a tiny case, written in the
+    untransposed form S_t = a S_{t-1}(I - b k k^T) + b v k^T, o_t = S_t q_t.
+    a is taken as the exact value of the fp64 exp(g) the oracle forms, so the
+    only difference left is the oracle's fp64 rounding."""
+    rng = _rng(8)
+    T, dk, dv = 6, 3, 2
+    pick = lambda *s: (rng.integers(-4, 5, s) / 4.0).astype(np.float32)
+    q, k, v = pick(1, T, 1, dk), pick(1, T, 1, dk), pick(1, T, 1, dv)
+    beta = (rng.integers(1, 5, (1, T, 1)) / 4.0).astype(np.float32)
+    g = (-rng.random((1, T, 1))).astype(np.float32)
+    h0 = pick(1, 1, dk, dv).astype(np.float64)
+    F = Fraction
+    S = [[F(float(h0[0, 0, i, c])) for i in range(dk)] for c in range(dv)]  # S = M^T
+    want_o = np.zeros((T, dv))
+    for t in range(T):
+        a = F(math.exp(float(g[0, t, 0])))
+        b = F(float(beta[0, t, 0]))
+        kt = [F(float(x)) for x in k[0, t, 0]]
+        vt = [F(float(x)) for x in v[0, t, 0]]
+        qt = [F(float(x)) for x in q[0, t, 0]]
+        P = [[(1 if i == j else 0) - b * kt[i] * kt[j] for j in range(dk)] for i in range(dk)]
+        S = [[a * sum(S[c][m] * P[m][i] for m in range(dk)) + b * vt[c] * kt[i]
+              for i in range(dk)] for c in range(dv)]
+        for c in range(dv):
+            want_o[t, c] = float(sum(S[c][i] * qt[i] for i in range(dk)))
+    want_M = np.array([[float(S[c][i]) for c in range(dv)] for i in range(dk)])
+    o, ht = fwd(q, k, v, g, beta, h0=h0)
+    _close(o[0, :, 0], want_o, 1e-14, "rational brute force (output)")
+    _close(ht[0, 0], want_M, 1e-14, "rational brute force (state)")
+
+
+def pin_hand_worked(fwd):
+    """The two-token example worked by hand in tests/golden."""
+    with open(os.path.join(GOLDEN, "two_tokens_by_hand.json")) as f:
+        ex = json.load(f)
+    arr = lambda name: np.asarray(ex[name], np.float32)
+    o, ht = fwd(arr("q"), arr("k"), arr("v"), arr("g"), arr("beta"))
+    np.testing.assert_allclose(o, np.asarray(ex["o"]), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(ht, np.asarray(ex["state"]), rtol=0, atol=1e-6)
+
+
+# --- invariants and the independent chunked route ---------------------------
+
+def pin_chunked_route(fwd):
+    """The chunk-parallel algebra (oracle/chunked.py: explicit solve of
+    I + A, no blocking) equals the token recurrence for chunk sizes
+    1, 2, 3, 8 and 64, T not a multiple of the chunk, grouped value heads, a
+    random initial state, a scale, and a packed batch."""
+    from oracle import chunked
+    rng = _rng(9)
+    q, k, v, g, beta = _rand_inputs(rng, 2, 70, 2, 4, 8, 5)
+    h0 = rng.standard_normal((2, 4, 8, 5))
+    o, ht = fwd(q, k, v, g, beta, scale=0.7, h0=h0)
+    for C in (1, 2, 3, 8, 64):
+        oc, hc = chunked.fwd(q, k, v, g, beta, C, scale=0.7, h0=h0)
+        _close(o, oc, 1e-12, f"chunked C={C} output")
+        _close(ht, hc, 1e-12, f"chunked C={C} state")
+    cu = np.array([0, 5, 5, 38, 70])
+    qp, kp, vp, gp, bp = (x[:1] for x in (q, k, v, g, beta))
+    hp = rng.standard_normal((4, 4, 8, 5))
+    o, ht = fwd(qp, kp, vp, gp, bp, h0=hp, cu_seqlens=cu)
+    oc, hc = chunked.fwd(qp, kp, vp, gp, bp, 16, h0=hp, cu_seqlens=cu)
+    _close(o, oc, 1e-12, "chunked packed output")
+    _close(ht, hc, 1e-12, "chunked packed state")
+
+
+def pin_packed_equals_separate(fwd):
+    """A packed row with cu_seqlens gives, bit for bit, the per-document calls
+    (the per-document reset, jax-linear-attention page, "How it works"); an
+    empty document returns its initial state."""
+    rng = _rng(10)
+    lengths = [7, 0, 1, 19, 4]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q, k, v, g, beta = _rand_inputs(rng, 1, T, 2, 4, 6, 3)
+    h0 = rng.standard_normal((len(lengths), 4, 6, 3))
+    o, ht = fwd(q, k, v, g, beta, h0=h0, cu_seqlens=cu)
+    for n in range(len(lengths)):
+        a, b = cu[n], cu[n + 1]
+        if a == b:
+            assert np.array_equal(ht[n], h0[n]), "empty document changed its state"
+            continue
+        on, hn = fwd(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], h0=h0[n:n + 1])
+        assert np.array_equal(o[:, a:b], on), f"document {n}: output differs"
+        assert np.array_equal(ht[n:n + 1], hn), f"document {n}: state differs"
+
+
+def pin_chained_halves(fwd):
+    """One call over T tokens equals two calls over the halves with the first
+    half's final state passed as the second half's initial state, bit for bit
+    (the chained-halves property in the jax-linear-attention page's
+    "Highlights")."""
+    rng = _rng(11)
+    q, k, v, g, beta = _rand_inputs(rng, 2, 30, 1, 2, 5, 4)
+    h0 = rng.standard_normal((2, 2, 5, 4))
+    o, ht = fwd(q, k, v, g, beta, h0=h0)
+    s = 13
+    o1, h1 = fwd(q[:, :s], k[:, :s], v[:, :s], g[:, :s], beta[:, :s], h0=h0)
+    o2, h2 = fwd(q[:, s:], k[:, s:], v[:, s:], g[:, s:], beta[:, s:], h0=h1)
+    assert np.array_equal(o, np.concatenate([o1, o2], axis=1)), "halves: output differs"
+    assert np.array_equal(ht, h2), "halves: state differs"
+
+
+def pin_grouped_heads(fwd):
+    """Grouped value heads: value head j reads q/k head j // G (consecutive value
+    heads share), so a call with Hv = 3 Hqk equals single-head calls."""
+    rng = _rng(12)
+    q, k, v, g, beta = _rand_inputs(rng, 1, 9, 2, 6, 4, 3)
+    o, ht = fwd(q, k, v, g, beta)
+    for j in range(6):
+        hk = j // 3
+        oj, hj = fwd(q[:, :, hk:hk + 1], k[:, :, hk:hk + 1], v[:, :, j:j + 1],
+                     g[:, :, j:j + 1], beta[:, :, j:j + 1])
+        assert np.array_equal(o[:, :, j:j + 1], oj) and np.array_equal(ht[:, j:j + 1], hj), \
+            f"value head {j} does not read q/k head {hk}"
+
+
+def pin_thread_invariance(fwd):
+    """The result does not depend on the number of host threads."""
+    rng = _rng(13)
+    q, k, v, g, beta = _rand_inputs(rng, 3, 17, 2, 2, 8, 70)
+    o1, h1 = fwd(q, k, v, g, beta, nthreads=1)
+    o7, h7 = fwd(q, k, v, g, beta, nthreads=7)
+    assert np.array_equal(o1, o7) and np.array_equal(h1, h7), "thread count changes the result"
+
+
+ALL_PINS = [
+    pin_single_token, pin_beta0_a1_state_unchanged, pin_beta0_decay_product,
+    pin_full_forgetting, pin_exact_write, pin_orthonormal_keys_linear_attention,
+    pin_linearity, pin_exact_rational, pin_hand_worked, pin_chunked_route,
+    pin_packed_equals_separate, pin_chained_halves, pin_grouped_heads,
+    pin_thread_invariance,
+]

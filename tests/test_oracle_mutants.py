@@ -1,0 +1,70 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake (a dropped term, a wrong sign, a wrong index or
+operand, a transposed layout) in a copy of oracle/gdn_oracle.c, builds it on
+the CPU, and checks that at least one pin fails.  Every mutant stays memory
+safe (indices remain in bounds), so a mutant can only give wrong numbers.
+"""
+import functools
+import os
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
+
+H0_IDX = "P->h0[(((int64_t)n * P->Hv + j) * dk + i) * dv + c0 + c]"
+HT_IDX = "P->ht[(((int64_t)n * P->Hv + j) * dk + i) * dv + c0 + c]"
+UPD = "M[(int64_t)i * w + c] = a * M[(int64_t)i * w + c] + ki * delta[c];"
+
+MUTANTS = {
+    "prediction_not_decayed": ("delta[c] = b * ((double)vt[c] - a * y);",
+                               "delta[c] = b * ((double)vt[c] - y);"),
+    "beta_dropped": ("delta[c] = b * ((double)vt[c] - a * y);",
+                     "delta[c] = ((double)vt[c] - a * y);"),
+    "prediction_sign": ("delta[c] = b * ((double)vt[c] - a * y);",
+                        "delta[c] = b * ((double)vt[c] + a * y);"),
+    "state_not_decayed": (UPD, "M[(int64_t)i * w + c] = M[(int64_t)i * w + c] + ki * delta[c];"),
+    "write_decayed_too": (UPD, "M[(int64_t)i * w + c] = a * (M[(int64_t)i * w + c] + ki * delta[c]);"),
+    "output_reads_k": ("acc += M[(int64_t)i * w + c] * (double)qt[i];",
+                       "acc += M[(int64_t)i * w + c] * (double)kt[i];"),
+    "prediction_reads_q": ("y += M[(int64_t)i * w + c] * (double)kt[i];",
+                           "y += M[(int64_t)i * w + c] * (double)qt[i];"),
+    "grouped_heads_interleaved": ("const int32_t hk = j / G;", "const int32_t hk = j % P->Hqk;"),
+    "decay_half_log": ("const double a = exp((double)P->g[p * P->Hv + j]);",
+                       "const double a = exp(0.5 * (double)P->g[p * P->Hv + j]);"),
+    "beta_complement": ("const double b = (double)P->beta[p * P->Hv + j];",
+                        "const double b = 1.0 - (double)P->beta[p * P->Hv + j];"),
+    "initial_state_ignored": ("P->h0 ? P->h0[", "0 ? P->h0["),
+    "initial_state_transposed": (H0_IDX, "P->h0[(((int64_t)n * P->Hv + j) * dv + c0 + c) * dk + i]"),
+    "final_state_transposed": (HT_IDX, "P->ht[(((int64_t)n * P->Hv + j) * dv + c0 + c) * dk + i]"),
+    "scale_dropped": ("ot[c] = P->scale * acc;", "ot[c] = acc;"),
+    "document_start_skipped": ("p0 = P->cu[n];", "p0 = P->cu[n] + (P->cu[n] < P->cu[n + 1]);"),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def _source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = _source()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle_build.build(str(path), str(tmp_path / f"lib{name}.so"))
+    fwd = functools.partial(oracle.gdn_fwd, lib_path=lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(fwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant {name}"
