@@ -1,0 +1,156 @@
+"""Python binding of libgdn, the chunkwise Gated DeltaNet forward for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgdn.so.  PyTorch provides device memory and the stream.  The
+names follow the C ABI in include/gdn.h.  There is no fallback: without the
+built library (python -m gated_deltanet_chunked_chunk_amd.build) every call
+raises.
+"""
+import ctypes
+import os
+
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_status_string",
+           "gdn_last_hip_error", "gdn_version", "GdnError", "library_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
+          3: "GDN_ERR_MISALIGNED", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load():
+    """The loaded libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m gated_deltanet_chunked_chunk_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
+                                  ctypes.c_float, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_last_hip_error.restype = ctypes.c_int
+    lib.gdn_last_hip_error.argtypes = []
+    lib.gdn_version.restype = I32
+    lib.gdn_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status):
+    return load().gdn_status_string(int(status)).decode()
+
+
+def gdn_last_hip_error():
+    return load().gdn_last_hip_error()
+
+
+def gdn_version():
+    return load().gdn_version()
+
+
+def _dtype_code(torch, dt):
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise GdnError(2, f"unsupported dtype {dt}")
+
+
+def gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
+    return load().gdn_chunk_fwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
+                  cu_seqlens_host=None, output_final_state=True, out=None, final_state=None,
+                  workspace=None, stream=None):
+    """o, ht = gdn_chunk_fwd(q, k, v, g, beta, ...) on the current HIP stream.
+
+    q, k: [B, T, H_qk, dk]; v: [B, T, H_v, dv] (bf16 or fp32, one dtype);
+    g, beta: [B, T, H_v] fp32; initial_state: [N, H_v, dk, dv] fp32 or None;
+    cu_seqlens: int32 [N + 1] device tensor for a packed row (B = 1), with an
+    optional host copy (list or CPU tensor) that is then validated.
+    Returns (o [B, T, H_v, dv], ht [N, H_v, dk, dv] fp32 or None).  `out`,
+    `final_state` and `workspace` may be given preallocated.
+    """
+    import torch
+    lib = load()
+    tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)]
+    if initial_state is not None:
+        tensors.append(("initial_state", initial_state))
+    if cu_seqlens is not None:
+        tensors.append(("cu_seqlens", cu_seqlens))
+    for name, t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise GdnError(1, f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise GdnError(1, f"{name} must be contiguous")
+    dt = _dtype_code(torch, q.dtype)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError(1, "q, k and v must share one dtype")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise GdnError(1, "g and beta must be fp32")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise GdnError(1, "q, k must be [B, T, H_qk, dk] and v [B, T, H_v, dv]")
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise GdnError(1, "g and beta must be [B, T, H_v]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise GdnError(1, "cu_seqlens must be a 1-d int32 tensor")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    host_arr = None
+    if cu_seqlens_host is not None:
+        if cu_seqlens is None or len(cu_seqlens_host) != N + 1:
+            raise GdnError(1, "cu_seqlens_host needs cu_seqlens of the same length")
+        host_arr = (ctypes.c_int32 * (N + 1))(*[int(x) for x in cu_seqlens_host])
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or initial_state.shape != (N, Hv, dk, dv):
+            raise GdnError(1, "initial_state must be fp32 [N, H_v, dk, dv]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if not output_final_state:
+        final_state = None
+    ws_bytes = lib.gdn_chunk_fwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.gdn_chunk_fwd(dt, B, T, Hqk, Hv, dk, dv, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
+                           float(scale), ptr(initial_state), ptr(cu_seqlens),
+                           None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
+                           N if cu_seqlens is not None else 0, ptr(out), ptr(final_state),
+                           ptr(workspace), 0 if workspace is None else workspace.numel(),
+                           stream)
+    if st != 0:
+        msg = gdn_status_string(st)
+        if st == 5:
+            msg += f" (hipError_t {gdn_last_hip_error()})"
+        raise GdnError(st, msg)
+    return out, final_state

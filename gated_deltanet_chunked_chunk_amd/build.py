@@ -1,0 +1,62 @@
+"""Build libgdn.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+Run as `python -m gated_deltanet_chunked_chunk_amd.build` or call build().
+The library is written next to this file; the Python binding loads it from
+there and refuses to run without it.
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libgdn.so")
+OBJDIR = os.path.join(HERE, "_build")
+
+SOURCES = ["gdn_api.cpp", "gdn_fwd_bf16.hip", "gdn_fwd_f32.hip"]
+
+ARCH = "gfx950"
+# Packed fp32 instructions are disabled: the compiler would otherwise form
+# v_pk_* fp32 operations from ordinary float code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+         "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}", *DEVICE_FLAGS]
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src, extra):
+    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(extra=(), verbose=False):
+    """Compile every source for gfx950 and link libgdn.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(LIB, file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

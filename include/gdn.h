@@ -1,0 +1,130 @@
+/*
+ * gdn.h -- C ABI of libgdn: the chunkwise Gated DeltaNet forward on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the gated delta rule of Gated DeltaNet (the December 2024
+ * paper by Yang, Kautz and Hatamizadeh that the Qwen FlashQLA article names
+ * under "The bottleneck nobody wanted to talk about"), per sequence and per
+ * value head, with an fp32 state:
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,     o_t = scale * S_t q_t
+ *
+ * where a_t = exp(g_t): g is the natural-log decay and b = beta the write
+ * strength, the two gate inputs of the jax-linear-attention page's
+ * "Quick start", whose call takes q, k, v of shape [B, T, H, D] and returns
+ * (o, state) with an fp32 state of shape (B, H, K, V).  The state is exchanged
+ * as M = S^T, element (i, j) coupling key dimension i to value dimension j.
+ * The call evaluates the recurrence in chunk-parallel form (chunks of 64
+ * tokens), the form the same page lists next to the token-by-token
+ * reference under "How it works"; the result is the recurrence's, up to
+ * rounding.
+ *
+ * Packed documents: with cu_seqlens the single row of tokens holds N
+ * documents, document n being tokens [cu[n], cu[n+1]); the state restarts at
+ * every document start (the per-document reset of "How it works" on the
+ * jax-linear-attention page; FLA's variable-length inputs on the
+ * flash-linear-attention review page, "The library changes shape under
+ * you").  Grouped value heads: H_v = G * H_qk and value head j reads q/k head
+ * j / G.
+ *
+ * Conventions for every entry point:
+ *   - all tensors are dense, row-major (last index fastest), in device memory
+ *     the caller allocated and owns; the library allocates no device memory
+ *     and keeps no state between calls other than its compiled kernels;
+ *   - work is enqueued on `stream` and nothing synchronises: results are
+ *     valid once the stream has reached this point;
+ *   - a status other than GDN_OK means nothing was enqueued (except
+ *     GDN_ERR_HIP, where a launch failed: outputs are then undefined);
+ *   - nothing is thrown across the ABI.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null required pointer, size out of range, bad cu_seqlens */
+    GDN_ERR_UNSUPPORTED = 2, /* a shape or dtype this build has no kernel for */
+    GDN_ERR_MISALIGNED = 3,  /* a pointer not aligned to 16 bytes */
+    GDN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query said */
+    GDN_ERR_HIP = 5          /* a HIP launch failed; see gdn_last_hip_error() */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,  /* q, k, v and o in IEEE fp32 */
+    GDN_BF16 = 1  /* q, k, v and o in bfloat16 (o rounded to nearest even) */
+} gdn_dtype;
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 when it
+ * needs none; the pointer may then be NULL).  Returns 0 as well for sizes the
+ * forward would reject, so validate through gdn_chunk_fwd.
+ *
+ * n_seqs: the number of documents when cu_seqlens will be passed, else B.
+ */
+size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
+                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs);
+
+/*
+ * The chunked forward.
+ *
+ *   dtype        dtype of q, k, v and o.
+ *   B, T         batch rows and tokens per row (T >= 1).  With cu_seqlens,
+ *                B must be 1 and T is the total packed length.
+ *   H_qk, H_v    q/k heads and value heads; H_v % H_qk == 0.
+ *   dk, dv       key and value head dimensions.  Supported: bf16 with
+ *                dk = 128 and dv in {64, 128}; fp32 with dk, dv in {64, 128}.
+ *   q, k         [B, T, H_qk, dk]
+ *   v            [B, T, H_v, dv]
+ *   g            [B, T, H_v] fp32, natural-log decay (a = exp(g)); finite.
+ *   beta         [B, T, H_v] fp32, write strength.
+ *   scale        multiplies the output (1.0 gives o_t = S_t q_t).
+ *   h0           [N, H_v, dk, dv] fp32 initial states, or NULL for zeros.
+ *   cu_seqlens   device int32 [N + 1] document offsets, or NULL (then the
+ *                documents are the B rows and N = B).
+ *   cu_seqlens_host  optional host copy of cu_seqlens.  When given it is
+ *                validated (cu[0] = 0, non-decreasing, cu[N] = T) and the
+ *                chunk schedule is built from it on the host; when NULL the
+ *                device array is trusted and the schedule is built on the
+ *                device.  Empty documents are allowed: their final state is
+ *                their initial state.
+ *   n_seqs       N when cu_seqlens is given (>= 1); ignored otherwise.
+ *   o            [B, T, H_v, dv] output, dtype `dtype`.
+ *   ht           [N, H_v, dk, dv] fp32 final states, or NULL to skip them.
+ *   workspace    device scratch of at least gdn_chunk_fwd_workspace_size()
+ *                bytes, 256-byte aligned, owned by the caller and not read
+ *                after the call's work completes.
+ *   stream       HIP stream to enqueue on (NULL = the default stream).
+ *
+ * Every pointer must be 16-byte aligned.  o and ht must not overlap the
+ * inputs.
+ */
+gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                         int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float scale, const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                         int32_t n_seqs, void *o, float *ht, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* A static, human-readable name for a status. */
+const char *gdn_status_string(gdn_status status);
+
+/* The HIP error of the last GDN_ERR_HIP returned on this thread. */
+hipError_t gdn_last_hip_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,69 @@
+"""Helpers for the GPU tests: move generator inputs to the device, run the HIP
+path through the binding, and compare with the oracle."""
+import numpy as np
+import torch
+
+import gated_deltanet_chunked_chunk_amd as gdn
+import gdn_inputs as gi
+import oracle
+
+# Tolerances on relative L2 error against the fp64 oracle (whole tensor):
+# bf16 inputs: output <= 1e-2, final state <= 1e-3; fp32 inputs: 1e-5 / 1e-6.
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-6)}
+
+
+def rel_l2(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return float(np.linalg.norm((x - ref).ravel()) / (den if den > 0 else 1.0))
+
+
+def to_device(d, dev="cuda"):
+    """Device tensors for a generator dict (bf16 bits become bf16 tensors)."""
+    out = {}
+    for name in ("q", "k", "v"):
+        x = d[name]
+        if x.dtype == np.uint16:
+            out[name] = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            out[name] = torch.from_numpy(x).to(dev)
+    out["g"] = torch.from_numpy(d["g"]).to(dev)
+    out["beta"] = torch.from_numpy(d["beta"]).to(dev)
+    out["h0"] = None if d["h0"] is None else torch.from_numpy(d["h0"]).to(dev)
+    cu = d["cu_seqlens"]
+    out["cu"] = None if cu is None else torch.from_numpy(cu).to(dev)
+    out["cu_host"] = None if cu is None else [int(x) for x in cu]
+    return out
+
+
+def run_gpu(d, scale=1.0, dev="cuda", host_cu=True):
+    t = to_device(d, dev)
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=scale,
+                              initial_state=t["h0"], cu_seqlens=t["cu"],
+                              cu_seqlens_host=t["cu_host"] if host_cu else None)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), ht.cpu().numpy()
+
+
+def run_oracle(d, scale=1.0):
+    q, k, v = (gi.widen(d[x]) for x in ("q", "k", "v"))
+    h0 = None if d["h0"] is None else d["h0"].astype(np.float64)
+    return oracle.gdn_fwd(q, k, v, d["g"], d["beta"], scale=scale, h0=h0,
+                          cu_seqlens=d["cu_seqlens"])
+
+
+def check(d, scale=1.0, label=""):
+    """Run both sides, assert the tolerances, return the two errors."""
+    print(f"[gpu case] {label} B={d['B']} T={d['T']} Hqk={d['Hqk']} Hv={d['Hv']} "
+          f"dk={d['dk']} dv={d['dv']} dtype={d['dtype']} N={d['N']}", flush=True)
+    o, ht = run_gpu(d, scale)
+    ro, rht = run_oracle(d, scale)
+    eo, eh = rel_l2(o, ro), rel_l2(ht, rht)
+    tol_o, tol_h = TOL[d["dtype"]]
+    print(f"  rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} (tol {tol_h:.0e})",
+          flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht))
+    assert eo <= tol_o, f"output rel-L2 {eo:.3e} > {tol_o}"
+    assert eh <= tol_h, f"state rel-L2 {eh:.3e} > {tol_h}"
+    return eo, eh

@@ -1,0 +1,139 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case uses the seeded generator with the workloads' recipe; sizes span
+several chunks and a ragged tail, and the named workloads run at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from gpu_util import TOL, check, rel_l2, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32_workload():
+    """B=1, T=256, H=2, d=64, fp32: the whole workload."""
+    check(gi.make_config("tiny_f32"), label="tiny fp32")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_fp32_ragged(T):
+    d = gi.make(2, T, 2, 4, 64, 128, "f32", 2000 + T, h0_std=0.5)
+    check(d, scale=0.75, label=f"fp32 ragged T={T}")
+
+
+def test_fp32_dk128():
+    check(gi.make(1, 130, 1, 2, 128, 64, "f32", 2100, h0_std=0.1), label="fp32 dk128 dv64")
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 200])
+def test_bf16_ragged(T):
+    """Several chunks and a ragged tail, grouped heads, an initial state, a scale."""
+    d = gi.make(2, T, 2, 4, 128, 128, "bf16", 3000 + T, h0_std=0.3)
+    check(d, scale=0.5, label=f"bf16 ragged T={T}")
+
+
+def test_bf16_dv64():
+    check(gi.make(2, 190, 3, 3, 128, 64, "bf16", 3300, h0_std=0.1), label="bf16 dv64")
+
+
+def test_bf16_strong_decay_and_zero_beta():
+    """Extremes of the gates: g = -30 (near-total forgetting) on some tokens,
+    beta = 0 on others, g = 0 on the rest."""
+    d = gi.make(1, 300, 2, 2, 128, 128, "bf16", 3400, h0_std=0.2)
+    rng = np.random.default_rng(0)
+    sel = rng.random(d["g"].shape)
+    d["g"] = np.where(sel < 0.1, np.float32(-30.0), np.where(sel < 0.3, np.float32(0.0), d["g"]))
+    d["beta"] = np.where(rng.random(d["beta"].shape) < 0.2, np.float32(0.0), d["beta"])
+    check(d, label="bf16 gate extremes")
+
+
+def test_headline_workload_full_size():
+    """B=8, T=2048, H=16, d=128, bf16, zero state: the benchmarked launch."""
+    check(gi.make_config("headline_bf16"), label="headline 8x2048x16x128")
+
+
+def test_packed_grouped_workload_full_size():
+    """16,384 tokens in geometric documents, H_qk=16, H_v=32, h0 ~ N(0, 0.02)."""
+    check(gi.make_config("packed_gva_bf16"), label="packed GVA 16384")
+
+
+def test_packed_equals_separate_bitwise():
+    """A packed row gives the per-document results bit for bit: each document
+    starts its own chunks, so its arithmetic does not depend on its offset."""
+    lengths = [1, 130, 0, 64, 77, 5]
+    cu = gi.cu_from_lengths(lengths)
+    d = gi.make(1, int(cu[-1]), 2, 4, 128, 128, "bf16", 3500, h0_std=0.1, cu_seqlens=cu)
+    o, ht = run_gpu(d)
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if a == b:
+            assert np.array_equal(ht[n], d["h0"][n]), "empty document changed its state"
+            continue
+        dn = dict(d, q=d["q"][:, a:b], k=d["k"][:, a:b], v=d["v"][:, a:b], g=d["g"][:, a:b],
+                  beta=d["beta"][:, a:b], h0=d["h0"][n:n + 1], cu_seqlens=None, T=b - a, N=1)
+        on, hn = run_gpu(dn)
+        assert np.array_equal(o[:, a:b], on), f"document {n}: output differs"
+        assert np.array_equal(ht[n:n + 1], hn), f"document {n}: state differs"
+
+
+def test_packed_device_schedule_matches_host_validated():
+    d = gi.make_config("packed_gva_bf16", total=3000)
+    o1, h1 = run_gpu(d, host_cu=True)
+    o2, h2 = run_gpu(d, host_cu=False)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_chained_halves():
+    """A long row run whole equals its two halves with the state passed on."""
+    d = gi.make(1, 4096 + 37, 2, 2, 128, 128, "bf16", 3600)
+    o, ht = run_gpu(d)
+    s = 2048 + 13
+    d1 = dict(d, q=d["q"][:, :s], k=d["k"][:, :s], v=d["v"][:, :s], g=d["g"][:, :s],
+              beta=d["beta"][:, :s], T=s)
+    o1, h1 = run_gpu(d1)
+    d2 = dict(d, q=d["q"][:, s:], k=d["k"][:, s:], v=d["v"][:, s:], g=d["g"][:, s:],
+              beta=d["beta"][:, s:], h0=h1, T=d["T"] - s)
+    o2, h2 = run_gpu(d2)
+    tol_o, tol_h = TOL["bf16"]
+    assert rel_l2(np.concatenate([o1, o2], axis=1), o) <= tol_o
+    assert rel_l2(h2, ht) <= tol_h
+    ro, rht = run_oracle(d)
+    assert rel_l2(o2, ro[:, s:]) <= tol_o and rel_l2(h2, rht) <= tol_h
+
+
+def test_deterministic():
+    d = gi.make(2, 333, 2, 2, 128, 128, "bf16", 3700, h0_std=0.1)
+    a = run_gpu(d)
+    b = run_gpu(d)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_nan_stays_in_its_document():
+    """A NaN in one document's values leaves every other document finite and
+    unchanged."""
+    cu = gi.cu_from_lengths([100, 100, 100])
+    d = gi.make(1, 300, 1, 2, 128, 128, "bf16", 3800, h0_std=0.1, cu_seqlens=cu)
+    o_ref, h_ref = run_gpu(d)
+    v = d["v"].copy()
+    v[0, 150, 0, 3] = 0x7FC0  # bf16 quiet NaN in document 1, value head 0
+    o, ht = run_gpu(dict(d, v=v))
+    assert np.array_equal(o[:, :100], o_ref[:, :100]) and np.array_equal(o[:, 200:], o_ref[:, 200:])
+    assert np.array_equal(ht[0], h_ref[0]) and np.array_equal(ht[2], h_ref[2])
+    assert not np.all(np.isfinite(o[:, 150:200, 0]))
+
+
+def test_no_final_state_and_preallocated_output():
+    import gated_deltanet_chunked_chunk_amd as gdn
+    from gpu_util import to_device
+    d = gi.make(1, 100, 1, 1, 128, 128, "bf16", 3900)
+    t = to_device(d)
+    out = torch.full((1, 100, 1, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], out=out,
+                              output_final_state=False)
+    torch.cuda.synchronize()
+    assert ht is None and o.data_ptr() == out.data_ptr()
+    ro, _ = run_oracle(d)
+    assert rel_l2(o.float().cpu().numpy(), ro) <= TOL["bf16"][0]
