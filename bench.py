@@ -1,0 +1,271 @@
+"""Benchmark of gdn_chunk_fwd on one MI355X.
+
+A step is one forward call over the headline workload: B=8 rows of T=2048
+tokens, H=16 heads, dk=dv=128, bf16 q/k/v, fp32 gates, zero initial state,
+output and fp32 final state (synthetic inputs, seeded; the recipe is in
+gdn_inputs.py).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line with the throughput (tokens/s), the roofline of the
+kernel (HBM-bound: algorithmic bytes per launch over the measured launch
+time, against the 8 TB/s HBM3E peak), and the CPU oracle timed on this host.
+Everything else goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD = "headline_bf16"
+KERNEL_NAME = "gdn_fwd_bf16_dk128"
+KERNEL_SOURCES = ["gated_deltanet_chunked_chunk_amd/csrc/gdn_fwd_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline_bf16.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(B, T, Hqk, Hv, dk, dv, in_bytes=2, h0=False):
+    """Each input read once, each output written once."""
+    tokens = B * T
+    qk = 2 * tokens * Hqk * dk * in_bytes
+    v = tokens * Hv * dv * in_bytes
+    gates = 2 * tokens * Hv * 4
+    o = tokens * Hv * dv * in_bytes
+    states = B * Hv * dk * dv * 4 * (2 if h0 else 1)
+    return qk + v + gates + o + states
+
+
+def chunked_flops(B, T, Hv, dk, dv, C=64):
+    """Contractions of the chunk form, dense per chunk: K K^T, Q K^T (2 C^2 dk
+    each), K h and Q h (2 C dk dv each), T'Y and P Delta (2 C^2 dv each),
+    K^T Delta (2 C dk dv), the triangular inverse (C^3 / 3)."""
+    chunks = B * Hv * (-(-T // C))
+    per = 2 * C * C * (2 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3
+    return chunks * per
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if it is missing or was taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(d, target_s=10.0):
+    """The fp64 oracle on this host: whole-workload runs, repeated until
+    about target_s seconds of wall clock have passed (at least one run)."""
+    import gdn_inputs as gi
+    import oracle
+    q, k, v = (gi.widen(d[x]) for x in ("q", "k", "v"))
+    threads = oracle.default_threads()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gdn_fwd(q, k, v, d["g"], d["beta"], nthreads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or runs >= 50:
+            break
+    tokens = d["B"] * d["T"] * runs
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload (B={d['B']}, T={d['T']}, H={d['Hv']}, d={d['dk']}), "
+                      f"{runs} run(s) in {el:.2f} s, fp64 token recurrence, "
+                      f"{threads} threads"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="cache-flush write between the per-launch timings")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} was asked for)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_chunked_chunk_amd as gdn
+    import gdn_inputs as gi
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gdn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c = gi.CONFIGS[WORKLOAD]
+    log(f"[bench] generating {WORKLOAD} inputs")
+    d = gi.make_config(WORKLOAD)
+    B, T, Hqk, Hv, dk, dv = d["B"], d["T"], d["Hqk"], d["Hv"], d["dk"], d["dv"]
+    dt = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = dt(d["q"]), dt(d["k"]), dt(d["v"])
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    o = torch.empty((B, T, Hv, dv), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht, stream=stream.cuda_stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # The timed region: exactly K back-to-back steps.
+    log(f"[bench] timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens = B * T
+    value = tokens * args.steps / (ms_total * 1e-3)
+
+    # Per-launch durations with HIP events on the launch stream: once back to
+    # back, once with the caches flushed by a large write before each launch.
+    def per_launch(n, flush):
+        buf = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if flush else None
+        times = []
+        for i in range(n):
+            if flush:
+                buf.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return np.array(times)
+
+    n_launch = min(max(args.steps, 10), 100)
+    t_b2b = per_launch(n_launch, False)
+    t_fl = per_launch(n_launch, True)
+    nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
+    flops = chunked_flops(B, T, Hv, dk, dv)
+    launch_ms = float(np.mean(t_b2b))
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    # A device copy of the same byte count, for context (not the denominator).
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    dstb = torch.empty_like(src)
+    dstb.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dstb.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dstb
+
+    # Spot check of the timed output against the oracle on one sampled head.
+    import oracle
+    import gdn_inputs as gi2
+    bs, hs = 5, 11
+    qq, kk, vv = (gi2.widen(d[x][bs:bs + 1, :, hs:hs + 1]) for x in ("q", "k", "v"))
+    ro, rh = oracle.gdn_fwd(qq, kk, vv, d["g"][bs:bs + 1, :, hs:hs + 1],
+                            d["beta"][bs:bs + 1, :, hs:hs + 1])
+    go = o[bs:bs + 1, :, hs:hs + 1].float().cpu().numpy()
+    gh = ht[bs:bs + 1, hs:hs + 1].cpu().numpy()
+    err_o = float(np.linalg.norm(go - ro) / np.linalg.norm(ro))
+    err_h = float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))
+    log(f"[bench] sampled head (b={bs}, h={hs}) rel-L2: output {err_o:.2e}, state {err_h:.2e}")
+
+    baseline = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        baseline = cpu_baseline(d)
+        baseline["cpu_model"] = cpu_model()
+
+    result = {
+        "metric": "GDN chunked fwd tokens/s (8x2K, H16, d128, bf16); % of roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), "
+                "beta=sigmoid(N(0,1)), g=logsigmoid(N(0,1))/16)",
+        "config": {"workload": f"{WORKLOAD}: B={B} T={T} H_qk={Hqk} H_v={Hv} dk={dk} dv={dv} "
+                               f"chunk=64, zero initial state, output + final state",
+                   "B": B, "T": T, "H": Hv, "dk": dk, "dv": dv, "chunk": 64,
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": KERNEL_NAME,
+            "algorithmic_bytes_per_launch": nbytes,
+            "launch_ms_mean": launch_ms,
+            "launch_ms_median": float(np.median(t_b2b)),
+            "launch_ms_flushed_mean": float(np.mean(t_fl)),
+            "frac_flushed": nbytes / (float(np.mean(t_fl)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "mfma_bf16_tflops": flops / (launch_ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "copy_gbps": copy_gbps,
+        },
+        "cpu_baseline": baseline,
+        "check": {"sampled_head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h},
+        "wall_s_timed_region": wall,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

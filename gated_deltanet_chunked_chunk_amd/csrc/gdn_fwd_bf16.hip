@@ -3,40 +3,51 @@
 // One workgroup (4 waves) owns one (sequence, value head, 64-column value
 // tile) and walks the sequence's chunks of 64 tokens in order.  Value columns
 // of the state evolve independently (every step of the recurrence acts on
-// them column by column), so splitting dv across workgroups is exact.  Each
-// wave owns 16 of the 64 columns and keeps its slice of the fp32 state,
-// M = S^T restricted to [128 x 16], in MFMA accumulator registers for the
-// whole sequence: the serial chain between chunks never leaves the wave.
+// them column by column), so splitting dv across workgroups is exact.  Wave w
+// owns value columns [16w, 16w + 16) of the tile and keeps its [128 x 16]
+// slice of the fp32 state M = S^T in MFMA accumulators for the whole
+// sequence: the serial chain between chunks never leaves the wave.
 //
-// Per chunk (gamma = in-chunk cumulative log-decay, L = valid rows):
-//   (a2) gamma, exp(gamma), exp(gamma_L - gamma)                   wave 0
-//   (a3) A = strictly-lower (beta exp(gamma_r - gamma_s) K K^T)    MFMA, 10 tiles
-//        P = lower-incl.   (exp(gamma_r - gamma_s) Q K^T)          MFMA, 10 tiles
-//   (a4) T' = (I + A)^-1 diag(beta): 16x16 diagonal blocks by forward
-//        substitution, off-diagonal blocks by fp32 MFMA products
-//   (a5) Y = V - diag(exp gamma) K M0;  Delta = T' Y                MFMA
-//   (a6) M_L = exp(gamma_L) M0 + K^T diag(exp(gamma_L - gamma)) Delta
-//   (a7) O = scale (diag(exp gamma) Q M0 + P Delta)
-// These are the chunk equations of the gated delta rule (derived from the
-// token recurrence S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T of
-// Gated DeltaNet; the jax-linear-attention page, "How it works", names the
-// chunk-parallel form next to the token-by-token one).
+// The chunk equations (derived from the token recurrence
+// S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T of Gated DeltaNet; the
+// jax-linear-attention page, "How it works", names this chunk-parallel form
+// next to the token-by-token one).  With gamma the in-chunk cumulative
+// log-decay and M0 the state entering the chunk:
+//   A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s), s < r     (a3)
+//   (I + A) Delta = diag(beta) Y,  Y = V - diag(exp gamma) K M0     (a4, a5)
+//   M_L = exp(gamma_L) M0 + K^T diag(exp(gamma_L - gamma)) Delta    (a6)
+//   O = scale (diag(exp gamma) Q M0 + P Delta),
+//       P[r][s] = exp(gamma_r - gamma_s) (q_r . k_s), s <= r        (a7)
+// The UT transform is applied by block forward substitution over four
+// 16-row blocks: Delta_i = D_i (diag(beta_i) Y_i - sum_{j<i} A_ij Delta_j)
+// with D_i = (I + A_ii)^-1, so only the four 16 x 16 diagonal inverses are
+// formed explicitly (by fp32 forward substitution, one wave each).
 //
-// Precision: K, Q and V are exact bf16 and their products accumulate in fp32.
-// Operands that are computed (the state, T', Y, Delta') are fp32; on the
-// state chain they enter the MFMA as hi + lo bf16 pairs (x = hi + lo with
+// Per chunk, four workgroup barriers (LDS only: global loads of the next
+// chunk stay in flight across them):
+//   stage    registers -> LDS (K, Q, V rows; wave 0: gamma tables)
+//   phase 1  K M0, Q M0; K K^T and Q K^T tiles -> -A (hi/lo), A_ii, P; Y
+//   phase 2  D_i
+//   phase 3  Delta; state update; O += P Delta; output staging
+//
+// Precision: K, Q, V are exact bf16 and every product accumulates in fp32.
+// Computed operands on the state chain (D_i, A_ij, the right-hand sides,
+// Delta and Delta') enter the MFMA as hi + lo bf16 pairs (x = hi + lo,
 // hi = bf16(x), lo = bf16(x - hi); split-bfloat16, Henry, Tang & Heinecke,
-// ARITH 2019): T' Y takes three products (hi hi, hi lo, lo hi), K^T Delta' two
-// (K is exact).  K M0, Q M0 and P Delta use the hi part only: their error
-// stays far below the output tolerance and, for K M0, is damped by T'.
+// ARITH 2019), three products per pair of split operands and two where one
+// side is exact.  K M0, Q M0 and P Delta use hi parts only: their error stays
+// well inside the output tolerance, and K M0's is damped by the solve.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16.  Lane l supplies A[l%16][8*(l/16)+j] and
-// B[8*(l/16)+j][l%16] (j = 0..7) and receives C[4*(l/16)+r][l%16] (r = 0..3).
-// A result tile in that C layout feeds the next product as its B operand
-// without leaving the registers when the contraction runs over the tile's
-// rows: lane group g then supplies rows {4g..4g+3} of two stacked 16-row
-// tiles, and the A operand reads the same permuted k indices (two 8-byte LDS
-// reads at k = 4g and k = 16 + 4g of each 32-wide step).
+// MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16)+j] and
+// B[8(l/16)+j][l%16] (j = 0..7), receives C[4(l/16)+r][l%16] (r = 0..3).  A
+// C-layout tile feeds a later product as its B operand straight from
+// registers when the contraction runs over the tile's rows: lane group g
+// supplies rows {4g..4g+3} of two stacked 16-row tiles, and the A operand is
+// read with the same permuted k order (two 8-byte reads at k = 4g and
+// 16 + 4g of each 32-wide step).  K^T and V fragments come from the row-major
+// tiles through the LDS transpose read ds_read_b64_tr_b16: within 16 lanes,
+// lane 16g+i receives element i%4 of the 8-byte words addressed by lanes
+// 16g + 4j + i/4, j = 0..3.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,6 +57,8 @@ namespace gdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -53,87 +66,93 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 constexpr int kC = 64;          // chunk length
 constexpr int kDK = 128;        // key dimension
 constexpr int kDVT = 64;        // value columns per workgroup
-constexpr int kThreads = 256;   // 4 waves; wave w owns value columns [16w, 16w + 16)
-constexpr int kSK = kDK + 8;    // row stride (elements) of the [64][128] bf16 tiles
-constexpr int kST = kC + 8;     // row stride of the [*][64] bf16 tiles
-constexpr int kSA = kC + 4;     // row stride of the [64][64] fp32 tiles
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kSK = kDK + 8;    // row stride (elements) of the K and Q tiles
+constexpr int kST = kC + 8;     // row stride of the 64-wide bf16 tiles
+constexpr int kSD = 16 + 8;     // row stride of the D blocks
 
-struct Smem {
+struct alignas(16) Smem {
     uint16_t K[kC * kSK];       // K chunk, [row][dk]
-    uint16_t Q[kC * kSK];       // Q chunk, [row][dk]; reused as Tf (fp32) by the solve
-    uint16_t KT[kDK * kST];     // K chunk transposed, [dk][row]
-    uint16_t VT[kDVT * kST];    // V tile transposed, [dv][row]
-    uint16_t P[kC * kST];       // (Q K^T) * decay mask, [row][col]
-    uint16_t Th[kC * kST];      // T' hi, [row][col]
-    uint16_t Tl[kC * kST];      // T' lo
-    uint16_t O[kC * kST];       // output staging, [row][dv]
-    float AT[kC * kSA];         // A transposed, [col][row]
+    uint16_t Q[kC * kSK];       // Q chunk, [row][dk]
+    uint16_t V[kC * kST];       // value tile, [row][col]
+    uint16_t Anh[kC * kST];     // -A hi, off-diagonal 16-blocks below the diagonal
+    uint16_t Anl[kC * kST];     // -A lo
+    uint16_t P[kC * kST];       // P, lower 16-blocks (upper blocks stay zero)
+    uint16_t O[kC * kST];       // output staging, [row][col]
+    uint16_t Dh[kC * kSD];      // D_i hi at rows 16 i .. 16 i + 15
+    uint16_t Dl[kC * kSD];      // D_i lo
+    float Ad[4 * 16 * 16];      // Ad[i][r][p][m] = A_ii[4 m + p][r]
     float gam[kC];              // gamma_r
     float eg[kC];               // exp(gamma_r)
     float el[kC];               // exp(gamma_L - gamma_r)
     float bt[kC];               // beta_r
     float eL;                   // exp(gamma_L)
 };
-static_assert(sizeof(uint16_t) * kC * kSK == sizeof(float) * kC * kSA, "Tf must fit in Q");
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf2f(uint16_t x) {
-    return __uint_as_float(static_cast<unsigned>(x) << 16);
+// Workgroup barrier that waits only for this wave's LDS (and scalar) accesses.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
 }
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// A operand with the permuted k order: k = 4g .. 4g+3 and 16+4g .. 16+4g+3
-// of the 32-wide step starting at `p` (p already offset to the lane's row).
-__device__ __forceinline__ bf16x8 frag_perm(const uint16_t *p, int g) {
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(p + 4 * g);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(p + 16 + 4 * g);
-    const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+__device__ __forceinline__ float bf2f(uint16_t x) {
+    return __uint_as_float(static_cast<unsigned>(x) << 16);
+}
+
+__device__ __forceinline__ bf16x8 cat(u32x2 a, u32x2 b) {
+    const u32x4 v = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// A or B operand in the plain order: k = 8g .. 8g+7 of the step at `p`.
-__device__ __forceinline__ bf16x8 frag_plain(const uint16_t *p, int g) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p + 8 * g));
+__device__ __forceinline__ u32x2 ld8(const uint16_t *p) {
+    return *reinterpret_cast<const u32x2 *>(p);
 }
 
-// B operand from two stacked C-layout tiles (rows 0..15 and 16..31 of a step).
-__device__ __forceinline__ bf16x8 pack_hi(f32x4 a, f32x4 b) {
-    bf16x8 r;
-    r[0] = static_cast<__bf16>(a[0]); r[1] = static_cast<__bf16>(a[1]);
-    r[2] = static_cast<__bf16>(a[2]); r[3] = static_cast<__bf16>(a[3]);
-    r[4] = static_cast<__bf16>(b[0]); r[5] = static_cast<__bf16>(b[1]);
-    r[6] = static_cast<__bf16>(b[2]); r[7] = static_cast<__bf16>(b[3]);
-    return r;
+// A operand in the permuted k order of a 32-wide step starting at p (p is
+// already offset to the lane's row): k = 4g..4g+3 and 16+4g..16+4g+3.
+__device__ __forceinline__ bf16x8 frag_perm(const uint16_t *p, int g) {
+    return cat(ld8(p + 4 * g), ld8(p + 16 + 4 * g));
 }
 
-__device__ __forceinline__ void split(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
-    hi = pack_hi(a, b);
-    f32x4 ra, rb;
+// Transpose read of 4 bf16 (see the file comment).
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Four fp32 values as 4 bf16 (hi) and the rounding residuals as 4 bf16 (lo).
+__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
+    uint16_t h[4], l[4];
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-        ra[i] = a[i] - static_cast<float>(hi[i]);
-        rb[i] = b[i] - static_cast<float>(hi[4 + i]);
+        h[i] = f2bf(x[i]);
+        l[i] = f2bf(x[i] - bf2f(h[i]));
     }
-    lo = pack_hi(ra, rb);
+    hi = u32x2{h[0] | (unsigned)h[1] << 16, h[2] | (unsigned)h[3] << 16};
+    lo = u32x2{l[0] | (unsigned)l[1] << 16, l[2] | (unsigned)l[3] << 16};
 }
 
-// The 10 lower-triangular 16x16 tiles of a 64x64 matrix, as (row, col) blocks.
-__constant__ int8_t kLowerTiles[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1},
-                                          {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
+__device__ __forceinline__ u32x2 pack4(f32x4 x) {
+    return u32x2{f2bf(x[0]) | (unsigned)f2bf(x[1]) << 16, f2bf(x[2]) | (unsigned)f2bf(x[3]) << 16};
+}
+
+constexpr u32x2 kZero2 = {0u, 0u};
 
 struct Prefetch {
-    u32x4 k[4];   // rows tid/16 + 16 i, columns 8 (tid % 16) .. + 7
+    u32x4 k[4];   // K rows tid/16 + 16 i, columns 8 (tid % 16) .. + 7
     u32x4 q[4];
-    u32x4 v[2];   // rows tid/8 + 32 i, columns 8 (tid % 8) .. + 7 of the value tile
+    u32x4 v[2];   // value-tile rows tid/8 + 32 i, columns 8 (tid % 8) .. + 7
     float g, b;   // wave 0: row = lane
 };
 
@@ -160,11 +179,9 @@ __device__ __forceinline__ void load_chunk(Prefetch &pf, const FwdArgs &a, int64
     for (int i = 0; i < 2; ++i) {
         const int row = tid / 8 + 32 * i;
         const int col = 8 * (tid % 8);
-        if (row < L)
-            pf.v[i] = *reinterpret_cast<const u32x4 *>(vq + ((p + row) * a.Hv + j) * (int64_t)a.dv
-                                                      + c0 + col);
-        else
-            pf.v[i] = zero;
+        pf.v[i] = row < L ? *reinterpret_cast<const u32x4 *>(
+                                vq + ((p + row) * a.Hv + j) * (int64_t)a.dv + c0 + col)
+                          : zero;
     }
     if (tid < kC) {
         const bool ok = tid < L;
@@ -180,19 +197,12 @@ __device__ __forceinline__ void store_chunk(const Prefetch &pf, Smem &S, int tid
         const int col = 8 * (tid % 16);
         *reinterpret_cast<u32x4 *>(S.K + row * kSK + col) = pf.k[i];
         *reinterpret_cast<u32x4 *>(S.Q + row * kSK + col) = pf.q[i];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            S.KT[(col + e) * kST + row] =
-                static_cast<uint16_t>(pf.k[i][e / 2] >> (16 * (e % 2)));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int row = tid / 8 + 32 * i;
         const int col = 8 * (tid % 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            S.VT[(col + e) * kST + row] =
-                static_cast<uint16_t>(pf.v[i][e / 2] >> (16 * (e % 2)));
+        *reinterpret_cast<u32x4 *>(S.V + row * kST + col) = pf.v[i];
     }
 }
 
@@ -215,113 +225,99 @@ __device__ __forceinline__ void chunk_gamma(const Prefetch &pf, Smem &S, int lan
         S.eL = __expf(gL);
 }
 
-// (a4) T = (I + A)^-1 in fp32, A strictly lower, stored transposed in S.AT;
-// result in Tf = S.Q viewed as fp32 [64][kSA].  Then T' = T diag(beta) as
-// hi/lo bf16 into S.Th / S.Tl (lower blocks only; upper blocks stay zero).
-__device__ __forceinline__ void solve_ut(Smem &S, int tid) {
-    float *Tf = reinterpret_cast<float *>(S.Q);
-    const int wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-
-    // Diagonal blocks: wave 0, lane = 16 b + c solves column c of block b by
-    // forward substitution (right-looking: once x_r is final, subtract its
-    // multiple from the rows below).
-    if (wv == 0) {
-        const int b = lane >> 4, c = lane & 15;
-        float x[16];
+// (a3) The lower 16-blocks of K K^T and Q K^T that wave W forms: A row block
+// 3 - W (blocks j = 0 .. 3 - W) and P row block W (j = 0 .. W), five in all.
+// Block (i, j) is computed as K_j K_i^T (resp. K_j Q_i^T), whose C layout puts
+// row 16 i + l%16, columns 16 j + 4 (l/16) .. + 3 of the wanted block in lane
+// l: the row-major 8-byte pieces the A operands are read in later.
+template <int W>
+__device__ __forceinline__ void chunk_tiles(const bf16x8 (&kf)[4][4], const bf16x8 (&qf)[4][4],
+                                            Smem &S, int lr, int lg) {
+    constexpr int IA = 3 - W;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            x[i] = (i == c) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 15; ++r) {
-            const float *col = S.AT + (16 * b + r) * kSA + 16 * b;  // A[16b + *][16b + r]
-            float a16[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(col + 4 * q4);
-                a16[4 * q4 + 0] = t[0]; a16[4 * q4 + 1] = t[1];
-                a16[4 * q4 + 2] = t[2]; a16[4 * q4 + 3] = t[3];
-            }
-#pragma unroll
-            for (int r2 = r + 1; r2 < 16; ++r2)
-                x[r2] -= a16[r2] * x[r];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            Tf[(16 * b + i) * kSA + 16 * b + c] = x[i];
-    }
-    __syncthreads();
-
-    // Off-diagonal blocks X_ij (i > j): X_ij = -D_i sum_{k=j}^{i-1} A_ik X_kj,
-    // D_i = X_ii.  fp32 MFMA 16x16x4: lane l supplies A[l%16][l/16] and
-    // B[l/16][l%16], receives C[4(l/16)+r][l%16].
-    auto Aik = [&](int i, int k, int kk) {  // A_ik[lr][kk]
-        return S.AT[(16 * k + kk) * kSA + 16 * i + lr];
-    };
-    auto Tblk = [&](int i, int j, int rr, int cc) -> float & {
-        return Tf[(16 * i + rr) * kSA + 16 * j + cc];
-    };
-    // c += A_ik X_kj (both from LDS)
-    auto prod_lds = [&](int i, int k, int j, f32x4 c) {
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp)
-            c = mma_f32(Aik(i, k, 4 * kp + lg), Tblk(k, j, 4 * kp + lg, lr), c);
-        return c;
-    };
-    // -D_i Z with Z in C layout
-    auto neg_dinv = [&](int i, f32x4 z) {
+    for (int j = 0; j <= IA; ++j) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kp = 0; kp < 4; ++kp)
-            c = mma_f32(Tblk(i, i, lr, 4 * lg + kp), z[kp], c);
-        return -c;
-    };
-    auto store_blk = [&](int i, int j, f32x4 c) {
+        for (int kk = 0; kk < 4; ++kk)
+            c = mma(kf[j][kk], kf[IA][kk], c);
+        const int row = 16 * IA + lr;
+        const float gr = S.gam[row], br = S.bt[row];
+        if (j < IA) {
+            f32x4 val;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Tblk(i, j, 4 * lg + r, lr) = c[r];
-    };
-    auto load_blk = [&](int i, int j) {
-        f32x4 c;
+            for (int r = 0; r < 4; ++r)
+                val[r] = -br * __expf(gr - S.gam[16 * j + 4 * lg + r]) * c[r];
+            u32x2 hi, lo;
+            split4(val, hi, lo);
+            *reinterpret_cast<u32x2 *>(S.Anh + row * kST + 16 * j + 4 * lg) = hi;
+            *reinterpret_cast<u32x2 *>(S.Anl + row * kST + 16 * j + 4 * lg) = lo;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            c[r] = Tblk(i, j, 4 * lg + r, lr);
-        return c;
-    };
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-    // Level 1: X_10, X_21, X_32; wave 3 forms A_20 D_0, A_31 D_1, A_30 D_0 into
-    // unused upper blocks (0,2), (1,3), (0,3).
-    if (wv < 3) {
-        const int i = wv + 1, j = wv;
-        store_blk(i, j, neg_dinv(i, prod_lds(i, j, j, zero)));
-    } else {
-        store_blk(0, 2, prod_lds(2, 0, 0, zero));
-        store_blk(1, 3, prod_lds(3, 1, 1, zero));
-        store_blk(0, 3, prod_lds(3, 0, 0, zero));
+            for (int r = 0; r < 4; ++r) {
+                const int col = 4 * lg + r;  // column within the block; the row is lr
+                const float v = col < lr ? br * __expf(gr - S.gam[16 * IA + col]) * c[r] : 0.0f;
+                S.Ad[IA * 256 + col * 16 + (lr & 3) * 4 + (lr >> 2)] = v;
+            }
+        }
     }
-    __syncthreads();
-    // Level 2: X_20, X_31; wave 2 accumulates A_31 X_10 into (0,3).
-    if (wv == 0) {
-        store_blk(2, 0, neg_dinv(2, prod_lds(2, 1, 0, load_blk(0, 2))));
-    } else if (wv == 1) {
-        store_blk(3, 1, neg_dinv(3, prod_lds(3, 2, 1, load_blk(1, 3))));
-    } else if (wv == 2) {
-        store_blk(0, 3, prod_lds(3, 1, 0, load_blk(0, 3)));
+#pragma unroll
+    for (int j = 0; j <= W; ++j) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            c = mma(kf[j][kk], qf[W][kk], c);
+        const int row = 16 * W + lr;
+        const float gr = S.gam[row];
+        f32x4 val;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int col = 16 * j + 4 * lg + r;
+            val[r] = col <= row ? __expf(gr - S.gam[col]) * c[r] : 0.0f;
+        }
+        *reinterpret_cast<u32x2 *>(S.P + row * kST + 16 * j + 4 * lg) = pack4(val);
     }
-    __syncthreads();
-    // Level 3: X_30.
-    if (wv == 0)
-        store_blk(3, 0, neg_dinv(3, prod_lds(3, 2, 0, load_blk(0, 3))));
-    __syncthreads();
+}
 
-    // T' = T diag(beta) as hi + lo bf16, lower blocks.
-    for (int e = tid; e < 10 * 256; e += kThreads) {
-        const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int r = 16 * kLowerTiles[blk][0] + rr, s = 16 * kLowerTiles[blk][1] + cc;
-        const float t = (s <= r) ? Tf[r * kSA + s] * S.bt[s] : 0.0f;
-        const uint16_t hi = f2bf(t);
-        S.Th[r * kST + s] = hi;
-        S.Tl[r * kST + s] = f2bf(t - bf2f(hi));
+// x from the lane of the quad whose index is S (DPP quad_perm(S, S, S, S)).
+template <int Sel>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), Sel | (Sel << 2) | (Sel << 4) | (Sel << 6), 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float quad_bcast(float x, int sel) {
+    switch (sel) {
+    case 0: return quad_bcast<0>(x);
+    case 1: return quad_bcast<1>(x);
+    case 2: return quad_bcast<2>(x);
+    default: return quad_bcast<3>(x);
+    }
+}
+
+// (a4) D_w = (I + A_ww)^-1 by forward substitution in fp32, by wave w: lane
+// 4c + p holds rows p, p+4, p+8, p+12 of column c.  Once x_r is final it is
+// broadcast within the lane quad and subtracted from the rows below.
+__device__ __forceinline__ void diag_inverse(Smem &S, int w, int lane) {
+    const int c = lane >> 2, p = lane & 3;
+    float x[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        x[m] = (4 * m + p == c) ? 1.0f : 0.0f;
+    const float *ad = S.Ad + w * 256 + p * 4;
+#pragma unroll
+    for (int r = 0; r < 15; ++r) {
+        const f32x4 acol = *reinterpret_cast<const f32x4 *>(ad + r * 16);  // A[4m + p][r]
+        const float xr = quad_bcast(x[r / 4], r % 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (4 * m + p > r)
+                x[m] -= acol[m] * xr;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint16_t hi = f2bf(x[m]);
+        S.Dh[(16 * w + 4 * m + p) * kSD + c] = hi;
+        S.Dl[(16 * w + 4 * m + p) * kSD + c] = f2bf(x[m] - bf2f(hi));
     }
 }
 
@@ -356,12 +352,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         p1 = p0 + a.T;
     }
 
-    // Upper blocks of P and T' are read as zeros by the products below.
-    for (int i = tid; i < kC * kST; i += kThreads) {
+    // Upper blocks of P are read as zeros.
+    for (int i = tid; i < kC * kST; i += kThreads)
         S.P[i] = 0;
-        S.Th[i] = 0;
-        S.Tl[i] = 0;
-    }
 
     // This wave's state slice: h[mt][r] = M[16 mt + 4 lg + r][c0 + 16 wv + lr].
     const int col = c0 + 16 * wv + lr;
@@ -384,13 +377,23 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
             chunk_gamma(pf, S, lane);
         if (p + kC < p1)
             load_chunk(pf, a, p + kC, (int)min<int64_t>(kC, p1 - p - kC), hk, j, c0, tid);
-        __syncthreads();
+        lds_barrier();
 
-        // (a5, a7 first half) X = K M0 and Q M0 on this wave's 16 columns.
+        // ---- phase 1 ----------------------------------------------------
+        bf16x8 kf[4][4], qf[4][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int off = (16 * mi + lr) * kSK + 32 * kk;
+                kf[mi][kk] = frag_perm(S.K + off, lg);
+                qf[mi][kk] = frag_perm(S.Q + off, lg);
+            }
+        // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0).
         bf16x8 hb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            hb[kk] = pack_hi(h[2 * kk], h[2 * kk + 1]);
+            hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
         f32x4 X[4], Oa[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
@@ -398,113 +401,110 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
             Oa[mi] = X[mi];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int off = (16 * mi + lr) * kSK + 32 * kk;
-                X[mi] = mma(frag_perm(S.K + off, lg), hb[kk], X[mi]);
-                Oa[mi] = mma(frag_perm(S.Q + off, lg), hb[kk], Oa[mi]);
+                X[mi] = mma(kf[mi][kk], hb[kk], X[mi]);
+                Oa[mi] = mma(qf[mi][kk], hb[kk], Oa[mi]);
             }
         }
-
-        // (a3) K K^T -> A (transposed, fp32) and Q K^T -> P (bf16), lower tiles.
-#pragma unroll
-        for (int tt = wv; tt < 20; tt += 4) {
-            const int isq = tt >= 10;
-            const int mi = kLowerTiles[tt % 10][0], ni = kLowerTiles[tt % 10][1];
-            const uint16_t *src = isq ? S.Q : S.K;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc = mma(frag_plain(src + (16 * mi + lr) * kSK + 32 * kk, lg),
-                          frag_plain(S.K + (16 * ni + lr) * kSK + 32 * kk, lg), acc);
-            const int s = 16 * ni + lr;
-            const float gs_ = S.gam[s];
-            if (!isq) {
-                f32x4 outv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * mi + 4 * lg + r;
-                    outv[r] = (s < row) ? S.bt[row] * __expf(S.gam[row] - gs_) * acc[r] : 0.0f;
-                }
-                *reinterpret_cast<f32x4 *>(S.AT + s * kSA + 16 * mi + 4 * lg) = outv;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * mi + 4 * lg + r;
-                    const float pv = (s <= row) ? __expf(S.gam[row] - gs_) * acc[r] : 0.0f;
-                    S.P[row * kST + s] = f2bf(pv);
-                }
-            }
+        // (a3) this wave's blocks of -A, A_ii and P.
+        switch (wv) {
+        case 0: chunk_tiles<0>(kf, qf, S, lr, lg); break;
+        case 1: chunk_tiles<1>(kf, qf, S, lr, lg); break;
+        case 2: chunk_tiles<2>(kf, qf, S, lr, lg); break;
+        default: chunk_tiles<3>(kf, qf, S, lr, lg); break;
         }
-
-        // Y = V - diag(exp gamma) X as hi/lo B operands; O scaled by exp(gamma).
-        bf16x8 yh[2], yl[2];
-        {
-            f32x4 Y[4];
-            const int vc = 16 * wv + lr;
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
-                const int row0 = 16 * mi + 4 * lg;
-                const u32x2 vv = *reinterpret_cast<const u32x2 *>(S.VT + vc * kST + row0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
-                    const float e = S.eg[row0 + r];
-                    Y[mi][r] = vr - e * X[mi][r];
-                    Oa[mi][r] *= e;
-                }
-            }
-            split(Y[0], Y[1], yh[0], yl[0]);
-            split(Y[2], Y[3], yh[1], yl[1]);
-        }
-        __syncthreads();
-
-        // (a4) UT transform.
-        solve_ut(S, tid);
-        __syncthreads();
-
-        // (a5) Delta = T' Y, three products per step (T' lower triangular:
-        // row tiles 0, 1 need only the first 32-wide step).
-        f32x4 D[4];
+        // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
+        f32x4 R[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            D[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const u32x2 vv = ld_tr(S.V + (16 * mi + 4 * lg + (lr >> 2)) * kST + 16 * wv + 4 * (lr & 3));
 #pragma unroll
-            for (int kk = 0; kk <= mi / 2; ++kk) {
-                const int off = (16 * mi + lr) * kST + 32 * kk;
-                const bf16x8 th = frag_perm(S.Th + off, lg);
-                const bf16x8 tl = frag_perm(S.Tl + off, lg);
-                D[mi] = mma(th, yh[kk], D[mi]);
-                D[mi] = mma(th, yl[kk], D[mi]);
-                D[mi] = mma(tl, yh[kk], D[mi]);
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mi + 4 * lg + r;
+                const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
+                const float e = S.eg[row];
+                R[mi][r] = S.bt[row] * (vr - e * X[mi][r]);
+                Oa[mi][r] *= e;
             }
         }
-        bf16x8 dh[2], dl[2], db[2];
-        {
-            f32x4 Dp[4];
+        lds_barrier();
+
+        // ---- phase 2 ----------------------------------------------------
+        diag_inverse(S, wv, lane);
+        lds_barrier();
+
+        // ---- phase 3 ----------------------------------------------------
+        // (a4, a5) Delta_i = D_i (R_i - sum_{j<i} A_ij Delta_j), split products.
+        u32x2 dh[4], dl[4];
+        f32x4 D[4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Dp[mi][r] = S.el[16 * mi + 4 * lg + r] * D[mi][r];
-            split(Dp[0], Dp[1], dh[0], dl[0]);
-            split(Dp[2], Dp[3], dh[1], dl[1]);
-            db[0] = pack_hi(D[0], D[1]);
-            db[1] = pack_hi(D[2], D[3]);
+        for (int i = 0; i < 4; ++i) {
+            f32x4 c = R[i];
+            const int ao = (16 * i + lr) * kST;
+            if (i == 1) {
+                const bf16x8 ah = cat(ld8(S.Anh + ao + 4 * lg), kZero2);
+                const bf16x8 al = cat(ld8(S.Anl + ao + 4 * lg), kZero2);
+                c = mma(ah, cat(dh[0], kZero2), c);
+                c = mma(ah, cat(dl[0], kZero2), c);
+                c = mma(al, cat(dh[0], kZero2), c);
+            } else if (i >= 2) {
+                const bf16x8 ah = frag_perm(S.Anh + ao, lg);
+                const bf16x8 al = frag_perm(S.Anl + ao, lg);
+                c = mma(ah, cat(dh[0], dh[1]), c);
+                c = mma(ah, cat(dl[0], dl[1]), c);
+                c = mma(al, cat(dh[0], dh[1]), c);
+                if (i == 3) {
+                    const bf16x8 bh = cat(ld8(S.Anh + ao + 32 + 4 * lg), kZero2);
+                    const bf16x8 bl = cat(ld8(S.Anl + ao + 32 + 4 * lg), kZero2);
+                    c = mma(bh, cat(dh[2], kZero2), c);
+                    c = mma(bh, cat(dl[2], kZero2), c);
+                    c = mma(bl, cat(dh[2], kZero2), c);
+                }
+            }
+            u32x2 rh, rl;
+            split4(c, rh, rl);
+            const int dofs = (16 * i + lr) * kSD + 4 * lg;
+            const bf16x8 Dhi = cat(ld8(S.Dh + dofs), kZero2);
+            const bf16x8 Dlo = cat(ld8(S.Dl + dofs), kZero2);
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = mma(Dhi, cat(rh, kZero2), d);
+            d = mma(Dhi, cat(rl, kZero2), d);
+            d = mma(Dlo, cat(rh, kZero2), d);
+            D[i] = d;
+            split4(d, dh[i], dl[i]);
         }
 
-        // (a6) M_L = exp(gamma_L) M0 + K^T Delta'.
+        // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta.
+        bf16x8 dph[2], dpl[2];
+        {
+            u32x2 ph[4], pl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x[r] = S.el[16 * i + 4 * lg + r] * D[i][r];
+                split4(x, ph[i], pl[i]);
+            }
+            dph[0] = cat(ph[0], ph[1]);
+            dph[1] = cat(ph[2], ph[3]);
+            dpl[0] = cat(pl[0], pl[1]);
+            dpl[1] = cat(pl[2], pl[3]);
+        }
         const float eL = S.eL;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             h[mt] *= eL;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 akt = frag_perm(S.KT + (16 * mt + lr) * kST + 32 * kk, lg);
-                h[mt] = mma(akt, dh[kk], h[mt]);
-                h[mt] = mma(akt, dl[kk], h[mt]);
+                const uint16_t *kp = S.K + (32 * kk + 4 * lg + (lr >> 2)) * kSK + 16 * mt + 4 * (lr & 3);
+                const bf16x8 akt = cat(ld_tr(kp), ld_tr(kp + 16 * kSK));
+                h[mt] = mma(akt, dph[kk], h[mt]);
+                h[mt] = mma(akt, dpl[kk], h[mt]);
             }
         }
 
-        // (a7) O += P Delta, scaled, staged through LDS for coalesced stores.
+        // (a7) O += P Delta (hi parts), staged through LDS for coalesced stores.
+        const bf16x8 db[2] = {cat(dh[0], dh[1]), cat(dh[2], dh[3])};
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -514,7 +514,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
             for (int r = 0; r < 4; ++r)
                 S.O[(16 * mi + 4 * lg + r) * kST + 16 * wv + lr] = f2bf(a.scale * Oa[mi][r]);
         }
-        __syncthreads();
+        lds_barrier();
+
         uint16_t *o = static_cast<uint16_t *>(a.o);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
