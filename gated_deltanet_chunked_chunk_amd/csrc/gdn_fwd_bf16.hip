@@ -1,12 +1,23 @@
 // Chunkwise gated delta rule forward, bf16 inputs, dk = 128, for gfx950.
 //
-// One workgroup (4 waves) owns one (sequence, value head, 64-column value
-// tile) and walks the sequence's chunks of 64 tokens in order.  Value columns
-// of the state evolve independently (every step of the recurrence acts on
-// them column by column), so splitting dv across workgroups is exact.  Wave w
-// owns value columns [16w, 16w + 16) of the tile and keeps its [128 x 16]
-// slice of the fp32 state M = S^T in MFMA accumulators for the whole
-// sequence: the serial chain between chunks never leaves the wave.
+// One workgroup owns one (sequence, value head, 64-column value tile) and
+// walks the sequence's chunks of 64 tokens in order.  Value columns of the
+// state evolve independently (every step of the recurrence acts on them
+// column by column), so splitting dv across workgroups is exact.
+//
+// The workgroup has eight waves in two roles, one of each on every SIMD:
+//   state waves 0..3   wave s owns value columns [16s, 16s + 16) and keeps
+//                      its [128 x 16] slice of the fp32 state M = S^T in MFMA
+//                      accumulators for the whole sequence; per chunk it runs
+//                      the state-dependent steps (a5)-(a7).
+//   helper waves 4..7  prepare the next chunk while the state waves work on
+//                      the current one: stage K, Q, V and the gates from HBM
+//                      into LDS, the cumulative decay (a2), the blocks of
+//                      K K^T and Q K^T (a3) and the diagonal inverses (a4).
+// Chunk c is read from LDS buffer c % 2 while chunk c + 1 is written into the
+// other, and one workgroup barrier per chunk hands the buffers over.  The
+// helper waves meet once more among themselves per chunk (an LDS counter)
+// between staging and the products that read the staged rows.
 //
 // The chunk equations (derived from the token recurrence
 // S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T of Gated DeltaNet; the
@@ -21,14 +32,7 @@
 // The UT transform is applied by block forward substitution over four
 // 16-row blocks: Delta_i = D_i (diag(beta_i) Y_i - sum_{j<i} A_ij Delta_j)
 // with D_i = (I + A_ii)^-1, so only the four 16 x 16 diagonal inverses are
-// formed explicitly (by fp32 forward substitution, one wave each).
-//
-// Per chunk, four workgroup barriers (LDS only: global loads of the next
-// chunk stay in flight across them):
-//   stage    registers -> LDS (K, Q, V rows; wave 0: gamma tables)
-//   phase 1  K M0, Q M0; K K^T and Q K^T tiles -> -A (hi/lo), A_ii, P; Y
-//   phase 2  D_i
-//   phase 3  Delta; state update; O += P Delta; output staging
+// formed explicitly (fp32 forward substitution, one helper wave each).
 //
 // Precision: K, Q, V are exact bf16 and every product accumulates in fp32.
 // Computed operands on the state chain (D_i, A_ij, the right-hand sides,
@@ -48,6 +52,10 @@
 // tiles through the LDS transpose read ds_read_b64_tr_b16: within 16 lanes,
 // lane 16g+i receives element i%4 of the 8-byte words addressed by lanes
 // 16g + 4j + i/4, j = 0..3.
+//
+// Global loads are raw buffer loads whose range ends at the chunk's last
+// valid row, so rows past the end of a sequence read as zeros (zero k, q,
+// v, g and beta: they contribute nothing) without branches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,7 +66,6 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -66,27 +73,36 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 constexpr int kC = 64;          // chunk length
 constexpr int kDK = 128;        // key dimension
 constexpr int kDVT = 64;        // value columns per workgroup
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kThreads = 512;   // 4 state waves + 4 helper waves
 constexpr int kSK = kDK + 8;    // row stride (elements) of the K and Q tiles
 constexpr int kST = kC + 8;     // row stride of the 64-wide bf16 tiles
-constexpr int kSD = 16 + 8;     // row stride of the D blocks
+constexpr int kSD = 16 + 8;     // row stride of the 16-wide bf16 tiles
+constexpr int kSN = 48 + 8;     // row stride of -A (rows 16..63, columns 0..47)
+constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 
-struct alignas(16) Smem {
-    uint16_t K[kC * kSK];       // K chunk, [row][dk]
-    uint16_t Q[kC * kSK];       // Q chunk, [row][dk]
+// One chunk's worth of shared operands.
+struct alignas(16) ChunkBuf {
+    uint16_t K[kC * kSK];       // K rows, [row][dk]
+    uint16_t Q[kC * kSK];       // Q rows, [row][dk]
     uint16_t V[kC * kST];       // value tile, [row][col]
-    uint16_t Anh[kC * kST];     // -A hi, off-diagonal 16-blocks below the diagonal
-    uint16_t Anl[kC * kST];     // -A lo
     uint16_t P[kC * kST];       // P, lower 16-blocks (upper blocks stay zero)
-    uint16_t O[kC * kST];       // output staging, [row][col]
-    uint16_t Dh[kC * kSD];      // D_i hi at rows 16 i .. 16 i + 15
+    uint16_t Anh[48 * kSN];     // -A hi, row r - 16, blocks below the diagonal
+    uint16_t Anl[48 * kSN];     // -A lo
+    uint16_t Dh[kC * kSD];      // D_i hi, rows 16 i .. 16 i + 15
     uint16_t Dl[kC * kSD];      // D_i lo
-    float Ad[4 * 16 * 16];      // Ad[i][r][p][m] = A_ii[4 m + p][r]
     float gam[kC];              // gamma_r
     float eg[kC];               // exp(gamma_r)
     float el[kC];               // exp(gamma_L - gamma_r)
     float bt[kC];               // beta_r
     float eL;                   // exp(gamma_L)
+    float pad_[3];
+};
+
+struct alignas(16) Smem {
+    ChunkBuf buf[2];
+    float Ad[4][256];           // helper wave h: its diagonal block, Ad[r][p][m] = A_ii[4m + p][r]
+    uint16_t Ost[4][kC * kSD];  // state wave s: output staging, [row][col]
+    int hsync;                  // helper-wave meeting counter
 };
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -149,140 +165,28 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
 
 constexpr u32x2 kZero2 = {0u, 0u};
 
-struct Prefetch {
-    u32x4 k[4];   // K rows tid/16 + 16 i, columns 8 (tid % 16) .. + 7
-    u32x4 q[4];
-    u32x4 v[2];   // value-tile rows tid/8 + 32 i, columns 8 (tid % 8) .. + 7
-    float g, b;   // wave 0: row = lane
-};
-
-__device__ __forceinline__ void load_chunk(Prefetch &pf, const FwdArgs &a, int64_t p, int L,
-                                           int hk, int j, int c0, int tid) {
-    const uint16_t *kq = static_cast<const uint16_t *>(a.k);
-    const uint16_t *qq = static_cast<const uint16_t *>(a.q);
-    const uint16_t *vq = static_cast<const uint16_t *>(a.v);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = tid / 16 + 16 * i;
-        const int col = 8 * (tid % 16);
-        if (row < L) {
-            const int64_t off = ((p + row) * a.Hqk + hk) * (int64_t)kDK + col;
-            pf.k[i] = *reinterpret_cast<const u32x4 *>(kq + off);
-            pf.q[i] = *reinterpret_cast<const u32x4 *>(qq + off);
-        } else {
-            pf.k[i] = zero;
-            pf.q[i] = zero;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = tid / 8 + 32 * i;
-        const int col = 8 * (tid % 8);
-        pf.v[i] = row < L ? *reinterpret_cast<const u32x4 *>(
-                                vq + ((p + row) * a.Hv + j) * (int64_t)a.dv + c0 + col)
-                          : zero;
-    }
-    if (tid < kC) {
-        const bool ok = tid < L;
-        pf.g = ok ? a.g[(p + tid) * a.Hv + j] : 0.0f;
-        pf.b = ok ? a.beta[(p + tid) * a.Hv + j] : 0.0f;
-    }
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, RowMask, 0xF, false));
 }
 
-__device__ __forceinline__ void store_chunk(const Prefetch &pf, Smem &S, int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = tid / 16 + 16 * i;
-        const int col = 8 * (tid % 16);
-        *reinterpret_cast<u32x4 *>(S.K + row * kSK + col) = pf.k[i];
-        *reinterpret_cast<u32x4 *>(S.Q + row * kSK + col) = pf.q[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = tid / 8 + 32 * i;
-        const int col = 8 * (tid % 8);
-        *reinterpret_cast<u32x4 *>(S.V + row * kST + col) = pf.v[i];
-    }
+// Inclusive prefix sum over the 64 lanes (row_shr within rows of 16, then
+// row_bcast:15 and row_bcast:31 across rows).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp<0x111, 0xF>(x);
+    x += dpp<0x112, 0xF>(x);
+    x += dpp<0x114, 0xF>(x);
+    x += dpp<0x118, 0xF>(x);
+    x += dpp<0x142, 0xA>(x);
+    x += dpp<0x143, 0xC>(x);
+    return x;
 }
 
-// (a2) In-chunk cumulative log-decay, by wave 0 (lane r holds g_r; rows past
-// the valid length carry g = 0, so gamma_63 = gamma_{L-1}).
-__device__ __forceinline__ void chunk_gamma(const Prefetch &pf, Smem &S, int lane) {
-    float x = pf.g;
-#pragma unroll
-    for (int d = 1; d < 64; d *= 2) {
-        const float y = __shfl_up(x, d, 64);
-        if (lane >= d)
-            x += y;
-    }
-    const float gL = __shfl(x, 63, 64);
-    S.gam[lane] = x;
-    S.eg[lane] = __expf(x);
-    S.el[lane] = __expf(gL - x);
-    S.bt[lane] = pf.b;
-    if (lane == 0)
-        S.eL = __expf(gL);
-}
-
-// (a3) The lower 16-blocks of K K^T and Q K^T that wave W forms: A row block
-// 3 - W (blocks j = 0 .. 3 - W) and P row block W (j = 0 .. W), five in all.
-// Block (i, j) is computed as K_j K_i^T (resp. K_j Q_i^T), whose C layout puts
-// row 16 i + l%16, columns 16 j + 4 (l/16) .. + 3 of the wanted block in lane
-// l: the row-major 8-byte pieces the A operands are read in later.
-template <int W>
-__device__ __forceinline__ void chunk_tiles(const bf16x8 (&kf)[4][4], const bf16x8 (&qf)[4][4],
-                                            Smem &S, int lr, int lg) {
-    constexpr int IA = 3 - W;
-#pragma unroll
-    for (int j = 0; j <= IA; ++j) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            c = mma(kf[j][kk], kf[IA][kk], c);
-        const int row = 16 * IA + lr;
-        const float gr = S.gam[row], br = S.bt[row];
-        if (j < IA) {
-            f32x4 val;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                val[r] = -br * __expf(gr - S.gam[16 * j + 4 * lg + r]) * c[r];
-            u32x2 hi, lo;
-            split4(val, hi, lo);
-            *reinterpret_cast<u32x2 *>(S.Anh + row * kST + 16 * j + 4 * lg) = hi;
-            *reinterpret_cast<u32x2 *>(S.Anl + row * kST + 16 * j + 4 * lg) = lo;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int col = 4 * lg + r;  // column within the block; the row is lr
-                const float v = col < lr ? br * __expf(gr - S.gam[16 * IA + col]) * c[r] : 0.0f;
-                S.Ad[IA * 256 + col * 16 + (lr & 3) * 4 + (lr >> 2)] = v;
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j <= W; ++j) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            c = mma(kf[j][kk], qf[W][kk], c);
-        const int row = 16 * W + lr;
-        const float gr = S.gam[row];
-        f32x4 val;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int col = 16 * j + 4 * lg + r;
-            val[r] = col <= row ? __expf(gr - S.gam[col]) * c[r] : 0.0f;
-        }
-        *reinterpret_cast<u32x2 *>(S.P + row * kST + 16 * j + 4 * lg) = pack4(val);
-    }
-}
-
-// x from the lane of the quad whose index is S (DPP quad_perm(S, S, S, S)).
+// x from the lane of the quad whose index is Sel.
 template <int Sel>
 __device__ __forceinline__ float quad_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), Sel | (Sel << 2) | (Sel << 4) | (Sel << 6), 0xF, 0xF, false));
+    return dpp<Sel | (Sel << 2) | (Sel << 4) | (Sel << 6), 0xF>(x);
 }
 
 __device__ __forceinline__ float quad_bcast(float x, int sel) {
@@ -294,37 +198,327 @@ __device__ __forceinline__ float quad_bcast(float x, int sel) {
     }
 }
 
-// (a4) D_w = (I + A_ww)^-1 by forward substitution in fp32, by wave w: lane
-// 4c + p holds rows p, p+4, p+8, p+12 of column c.  Once x_r is final it is
-// broadcast within the lane quad and subtracted from the rows below.
-__device__ __forceinline__ void diag_inverse(Smem &S, int w, int lane) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// Everything a workgroup needs to address its sequence.
+struct Item {
+    int64_t p0;      // first token (flattened over the rows)
+    int nchunks;
+    int len;         // tokens in the sequence
+    int j, hk, c0, n;
+};
+
+// Helper-wave registers holding the next chunk's global data.
+struct Stage {
+    u32x4 k[4];   // K rows t/16 + 16 i, columns 8 (t % 16) .. + 7 (t = helper thread)
+    u32x4 q[4];
+    u32x4 v[2];   // value-tile rows t/8 + 32 i, columns 8 (t % 8) .. + 7
+    float g, b;   // row = lane
+};
+
+__device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const Item &it, int c,
+                                           int t, int lane) {
+    const int64_t p = it.p0 + (int64_t)kC * c;
+    const int L = min(kC, it.len - kC * c);
+    const uint32_t krow = (uint32_t)a.Hqk * kDK * 2;  // bytes between tokens
+    const uint32_t vrow = (uint32_t)a.Hv * a.dv * 2;
+    const uint32_t grow = (uint32_t)a.Hv * 4;
+    const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (p * a.Hqk + it.hk) * kDK;
+    const uint16_t *qb = static_cast<const uint16_t *>(a.q) + (p * a.Hqk + it.hk) * kDK;
+    const uint16_t *vb = static_cast<const uint16_t *>(a.v) + (p * a.Hv + it.j) * a.dv + it.c0;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb, (L - 1) * krow + kDK * 2);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (L - 1) * krow + kDK * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb, (L - 1) * vrow + kDVT * 2);
+    const __amdgpu_buffer_rsrc_t rg = rsrc(a.g + p * a.Hv + it.j, (L - 1) * grow + 4);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(a.beta + p * a.Hv + it.j, (L - 1) * grow + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (t / 16 + 16 * i) * krow + 16 * (t % 16);
+        st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (t / 8 + 32 * i) * vrow + 16 * (t % 8), 0, 0);
+    st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * grow, 0, 0));
+    st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * grow, 0, 0));
+}
+
+// (a3) The lower 16-blocks of K K^T and Q K^T that helper wave W forms: A row
+// block 3 - W (blocks j = 0 .. 3 - W) and P row block W (j = 0 .. W), five in
+// all.  Block (i, j) is computed as K_j K_i^T (resp. K_j Q_i^T), whose C
+// layout puts row 16 i + l%16, columns 16 j + 4 (l/16) .. + 3 of the wanted
+// block in lane l: the row-major 8-byte pieces the A operands are read in.
+template <int W>
+__device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int lg) {
+    constexpr int IA = 3 - W;
+    bf16x8 kr[4], qr[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        kr[kk] = frag_perm(B.K + (16 * IA + lr) * kSK + 32 * kk, lg);
+        qr[kk] = frag_perm(B.Q + (16 * W + lr) * kSK + 32 * kk, lg);
+    }
+#pragma unroll
+    for (int j = 0; j <= (IA > W ? IA : W); ++j) {
+        bf16x8 kj[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kj[kk] = frag_perm(B.K + (16 * j + lr) * kSK + 32 * kk, lg);
+        if (j <= IA) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                c = mma(kj[kk], kr[kk], c);
+            const int row = 16 * IA + lr;
+            const float gr = B.gam[row], br = B.bt[row];
+            if (j < IA) {
+                f32x4 val;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    val[r] = -br * __expf(gr - B.gam[16 * j + 4 * lg + r]) * c[r];
+                u32x2 hi, lo;
+                split4(val, hi, lo);
+                const int o = (row - 16) * kSN + 16 * j + 4 * lg;
+                *reinterpret_cast<u32x2 *>(B.Anh + o) = hi;
+                *reinterpret_cast<u32x2 *>(B.Anl + o) = lo;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = 4 * lg + r;  // column within the block; the row is lr
+                    ad[col * 16 + (lr & 3) * 4 + (lr >> 2)] =
+                        col < lr ? br * __expf(gr - B.gam[16 * IA + col]) * c[r] : 0.0f;
+                }
+            }
+        }
+        if (j <= W) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                c = mma(kj[kk], qr[kk], c);
+            const int row = 16 * W + lr;
+            const float gr = B.gam[row];
+            f32x4 val;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = 16 * j + 4 * lg + r;
+                val[r] = col <= row ? __expf(gr - B.gam[col]) * c[r] : 0.0f;
+            }
+            *reinterpret_cast<u32x2 *>(B.P + row * kST + 16 * j + 4 * lg) = pack4(val);
+        }
+    }
+}
+
+// (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32 (i = 3 - helper
+// index): lane 4c + p holds rows p, p+4, p+8, p+12 of column c.  Once x_r is
+// final it is broadcast within the lane quad and subtracted from the rows
+// below.
+__device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i, int lane) {
     const int c = lane >> 2, p = lane & 3;
     float x[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         x[m] = (4 * m + p == c) ? 1.0f : 0.0f;
-    const float *ad = S.Ad + w * 256 + p * 4;
+    f32x4 acol[15];
+#pragma unroll
+    for (int r = 0; r < 15; ++r)
+        acol[r] = *reinterpret_cast<const f32x4 *>(ad + r * 16 + p * 4);  // A[4m + p][r]
 #pragma unroll
     for (int r = 0; r < 15; ++r) {
-        const f32x4 acol = *reinterpret_cast<const f32x4 *>(ad + r * 16);  // A[4m + p][r]
         const float xr = quad_bcast(x[r / 4], r % 4);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             if (4 * m + p > r)
-                x[m] -= acol[m] * xr;
+                x[m] -= acol[r][m] * xr;
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const uint16_t hi = f2bf(x[m]);
-        S.Dh[(16 * w + 4 * m + p) * kSD + c] = hi;
-        S.Dl[(16 * w + 4 * m + p) * kSD + c] = f2bf(x[m] - bf2f(hi));
+        B.Dh[(16 * i + 4 * m + p) * kSD + c] = hi;
+        B.Dl[(16 * i + 4 * m + p) * kSD + c] = f2bf(x[m] - bf2f(hi));
+    }
+}
+
+// Helper waves: put chunk c (already in `st`) into LDS buffer B with its
+// decay tables, A blocks, P and diagonal inverses.
+__device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, const Stage &st, int hw,
+                                               int t, int lane, int &meet) {
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = t / 16 + 16 * i, col = 8 * (t % 16);
+        *reinterpret_cast<u32x4 *>(B.K + row * kSK + col) = st.k[i];
+        *reinterpret_cast<u32x4 *>(B.Q + row * kSK + col) = st.q[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<u32x4 *>(B.V + (t / 8 + 32 * i) * kST + 8 * (t % 8)) = st.v[i];
+    if (hw == 0) {
+        // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
+        const float x = wave_prefix_sum(st.g);
+        const float gL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+        B.gam[lane] = x;
+        B.eg[lane] = __expf(x);
+        B.el[lane] = __expf(gL - x);
+        B.bt[lane] = st.b;
+        if (lane == 0)
+            B.eL = __expf(gL);
+    }
+    // Meet the other helper waves: the staged rows and gamma are in LDS.
+    meet += 4;
+    if (lane == 0)
+        __hip_atomic_fetch_add(&S.hsync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
+        __builtin_amdgcn_s_sleep(1);
+
+    float *ad = S.Ad[hw];
+    switch (hw) {
+    case 0: chunk_blocks<0>(B, ad, lr, lg); break;
+    case 1: chunk_blocks<1>(B, ad, lr, lg); break;
+    case 2: chunk_blocks<2>(B, ad, lr, lg); break;
+    default: chunk_blocks<3>(B, ad, lr, lg); break;
+    }
+    diag_inverse(B, ad, 3 - hw, lane);
+}
+
+// State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16).
+__device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
+                                            const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
+    const int lr = lane & 15, lg = lane >> 4;
+    // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0).
+    bf16x8 hb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+    f32x4 X[4], Oa[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Oa[mi] = X[mi];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int off = (16 * mi + lr) * kSK + 32 * kk;
+            X[mi] = mma(frag_perm(B.K + off, lg), hb[kk], X[mi]);
+            Oa[mi] = mma(frag_perm(B.Q + off, lg), hb[kk], Oa[mi]);
+        }
+    }
+    // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
+    f32x4 R[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const u32x2 vv = ld_tr(B.V + (16 * mi + 4 * lg + (lr >> 2)) * kST + 16 * s + 4 * (lr & 3));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mi + 4 * lg + r;
+            const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
+            const float e = B.eg[row];
+            R[mi][r] = B.bt[row] * (vr - e * X[mi][r]);
+            Oa[mi][r] *= e;
+        }
+    }
+
+    // (a4, a5) Delta_i = D_i (R_i - sum_{j<i} A_ij Delta_j), split products.
+    u32x2 dh[4], dl[4];
+    f32x4 D[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x4 cc = R[i];
+        if (i == 1) {
+            const int ao = lr * kSN + 4 * lg;
+            const bf16x8 ah = cat(ld8(B.Anh + ao), kZero2);
+            const bf16x8 al = cat(ld8(B.Anl + ao), kZero2);
+            cc = mma(ah, cat(dh[0], kZero2), cc);
+            cc = mma(ah, cat(dl[0], kZero2), cc);
+            cc = mma(al, cat(dh[0], kZero2), cc);
+        } else if (i >= 2) {
+            const int ao = (16 * (i - 1) + lr) * kSN;
+            const bf16x8 ah = frag_perm(B.Anh + ao, lg);
+            const bf16x8 al = frag_perm(B.Anl + ao, lg);
+            cc = mma(ah, cat(dh[0], dh[1]), cc);
+            cc = mma(ah, cat(dl[0], dl[1]), cc);
+            cc = mma(al, cat(dh[0], dh[1]), cc);
+            if (i == 3) {
+                const bf16x8 bh = cat(ld8(B.Anh + ao + 32 + 4 * lg), kZero2);
+                const bf16x8 bl = cat(ld8(B.Anl + ao + 32 + 4 * lg), kZero2);
+                cc = mma(bh, cat(dh[2], kZero2), cc);
+                cc = mma(bh, cat(dl[2], kZero2), cc);
+                cc = mma(bl, cat(dh[2], kZero2), cc);
+            }
+        }
+        u32x2 rh, rl;
+        split4(cc, rh, rl);
+        const int dofs = (16 * i + lr) * kSD + 4 * lg;
+        const bf16x8 Dhi = cat(ld8(B.Dh + dofs), kZero2);
+        const bf16x8 Dlo = cat(ld8(B.Dl + dofs), kZero2);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma(Dhi, cat(rh, kZero2), d);
+        d = mma(Dhi, cat(rl, kZero2), d);
+        d = mma(Dlo, cat(rh, kZero2), d);
+        D[i] = d;
+        split4(d, dh[i], dl[i]);
+    }
+
+    // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta.
+    bf16x8 dph[2], dpl[2];
+    {
+        u32x2 ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x[r] = B.el[16 * i + 4 * lg + r] * D[i][r];
+            split4(x, ph[i], pl[i]);
+        }
+        dph[0] = cat(ph[0], ph[1]);
+        dph[1] = cat(ph[2], ph[3]);
+        dpl[0] = cat(pl[0], pl[1]);
+        dpl[1] = cat(pl[2], pl[3]);
+    }
+    const float eL = B.eL;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        h[mt] *= eL;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint16_t *kp = B.K + (32 * kk + 4 * lg + (lr >> 2)) * kSK + 16 * mt + 4 * (lr & 3);
+            const bf16x8 akt = cat(ld_tr(kp), ld_tr(kp + 16 * kSK));
+            h[mt] = mma(akt, dph[kk], h[mt]);
+            h[mt] = mma(akt, dpl[kk], h[mt]);
+        }
+    }
+
+    // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
+    // its own LDS staging area (no other wave touches it).
+    const bf16x8 db[2] = {cat(dh[0], dh[1]), cat(dh[2], dh[3])};
+    uint16_t *ost = S.Ost[s];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int kk = 0; kk <= mi / 2; ++kk)
+            Oa[mi] = mma(frag_perm(B.P + (16 * mi + lr) * kST + 32 * kk, lg), db[kk], Oa[mi]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            ost[(16 * mi + 4 * lg + r) * kSD + lr] = f2bf(a.scale * Oa[mi][r]);
+    }
+    const int L = min(kC, it.len - kC * c);
+    const int64_t p = it.p0 + (int64_t)kC * c;
+    uint16_t *o = static_cast<uint16_t *>(a.o);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int piece = lane + 64 * q, row = piece >> 1, half = piece & 1;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(ost + row * kSD + 8 * half);
+        if (row < L)
+            *reinterpret_cast<u32x4 *>(o + ((p + row) * a.Hv + it.j) * (int64_t)a.dv + it.c0 +
+                                       16 * s + 8 * half) = val;
     }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     __shared__ Smem S;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
 
     // Work item.  Items that read the same q/k head (the dv tiles and the
     // grouped value heads of one q/k head) are kept on one XCD: blocks are
@@ -338,196 +532,73 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         const int xcd = w % 8, local = w / 8;
         w = ((local / gs) * 8 + xcd) * gs + local % gs;
     }
+    Item it;
     const int tile = w % n_tiles;
-    const int j = (w / n_tiles) % a.Hv;
-    const int n = w / (n_tiles * a.Hv);
-    const int hk = j / G;
-    const int c0 = tile * kDVT;
-    int64_t p0, p1;
+    it.j = (w / n_tiles) % a.Hv;
+    it.n = w / (n_tiles * a.Hv);
+    it.hk = it.j / G;
+    it.c0 = tile * kDVT;
+    int64_t p1;
     if (a.cu) {
-        p0 = a.cu[n];
-        p1 = a.cu[n + 1];
+        it.p0 = a.cu[it.n];
+        p1 = a.cu[it.n + 1];
     } else {
-        p0 = (int64_t)n * a.T;
-        p1 = p0 + a.T;
+        it.p0 = (int64_t)it.n * a.T;
+        p1 = it.p0 + a.T;
     }
+    it.len = (int)(p1 - it.p0);
+    it.nchunks = (it.len + kC - 1) / kC;
 
-    // Upper blocks of P are read as zeros.
-    for (int i = tid; i < kC * kST; i += kThreads)
-        S.P[i] = 0;
+    for (int i = tid; i < kC * kST; i += kThreads) {
+        S.buf[0].P[i] = 0;
+        S.buf[1].P[i] = 0;
+    }
+    if (tid == 0)
+        S.hsync = 0;
+    __syncthreads();
 
-    // This wave's state slice: h[mt][r] = M[16 mt + 4 lg + r][c0 + 16 wv + lr].
-    const int col = c0 + 16 * wv + lr;
-    const int64_t hbase = ((int64_t)n * a.Hv + j) * kDK * (int64_t)a.dv;
+    const bool state = wv < 4;
+    const int s = wv & 3;      // state wave: value-column group; helper wave: helper index
+    const int t = tid - 256;   // helper thread index
+    const int lg = lane >> 4, lr = lane & 15;
+    const int col = it.c0 + 16 * s + lr;
+    const int64_t hbase = ((int64_t)it.n * a.Hv + it.j) * kDK * (int64_t)a.dv;
+
     f32x4 h[8];
+    Stage st;
+    int meet = 0;
+    if (state) {
+        if (a.h0) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            h[mt][r] = a.h0 ? a.h0[hbase + (int64_t)(16 * mt + 4 * lg + r) * a.dv + col] : 0.0f;
-
-    Prefetch pf;
-    if (p0 < p1)
-        load_chunk(pf, a, p0, (int)min<int64_t>(kC, p1 - p0), hk, j, c0, tid);
-
-    for (int64_t p = p0; p < p1; p += kC) {
-        const int L = (int)min<int64_t>(kC, p1 - p);
-        store_chunk(pf, S, tid);
-        if (wv == 0)
-            chunk_gamma(pf, S, lane);
-        if (p + kC < p1)
-            load_chunk(pf, a, p + kC, (int)min<int64_t>(kC, p1 - p - kC), hk, j, c0, tid);
-        lds_barrier();
-
-        // ---- phase 1 ----------------------------------------------------
-        bf16x8 kf[4][4], qf[4][4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int off = (16 * mi + lr) * kSK + 32 * kk;
-                kf[mi][kk] = frag_perm(S.K + off, lg);
-                qf[mi][kk] = frag_perm(S.Q + off, lg);
-            }
-        // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0).
-        bf16x8 hb[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
-        f32x4 X[4], Oa[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Oa[mi] = X[mi];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                X[mi] = mma(kf[mi][kk], hb[kk], X[mi]);
-                Oa[mi] = mma(qf[mi][kk], hb[kk], Oa[mi]);
-            }
-        }
-        // (a3) this wave's blocks of -A, A_ii and P.
-        switch (wv) {
-        case 0: chunk_tiles<0>(kf, qf, S, lr, lg); break;
-        case 1: chunk_tiles<1>(kf, qf, S, lr, lg); break;
-        case 2: chunk_tiles<2>(kf, qf, S, lr, lg); break;
-        default: chunk_tiles<3>(kf, qf, S, lr, lg); break;
-        }
-        // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
-        f32x4 R[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const u32x2 vv = ld_tr(S.V + (16 * mi + 4 * lg + (lr >> 2)) * kST + 16 * wv + 4 * (lr & 3));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mi + 4 * lg + r;
-                const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
-                const float e = S.eg[row];
-                R[mi][r] = S.bt[row] * (vr - e * X[mi][r]);
-                Oa[mi][r] *= e;
-            }
-        }
-        lds_barrier();
-
-        // ---- phase 2 ----------------------------------------------------
-        diag_inverse(S, wv, lane);
-        lds_barrier();
-
-        // ---- phase 3 ----------------------------------------------------
-        // (a4, a5) Delta_i = D_i (R_i - sum_{j<i} A_ij Delta_j), split products.
-        u32x2 dh[4], dl[4];
-        f32x4 D[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 c = R[i];
-            const int ao = (16 * i + lr) * kST;
-            if (i == 1) {
-                const bf16x8 ah = cat(ld8(S.Anh + ao + 4 * lg), kZero2);
-                const bf16x8 al = cat(ld8(S.Anl + ao + 4 * lg), kZero2);
-                c = mma(ah, cat(dh[0], kZero2), c);
-                c = mma(ah, cat(dl[0], kZero2), c);
-                c = mma(al, cat(dh[0], kZero2), c);
-            } else if (i >= 2) {
-                const bf16x8 ah = frag_perm(S.Anh + ao, lg);
-                const bf16x8 al = frag_perm(S.Anl + ao, lg);
-                c = mma(ah, cat(dh[0], dh[1]), c);
-                c = mma(ah, cat(dl[0], dl[1]), c);
-                c = mma(al, cat(dh[0], dh[1]), c);
-                if (i == 3) {
-                    const bf16x8 bh = cat(ld8(S.Anh + ao + 32 + 4 * lg), kZero2);
-                    const bf16x8 bl = cat(ld8(S.Anl + ao + 32 + 4 * lg), kZero2);
-                    c = mma(bh, cat(dh[2], kZero2), c);
-                    c = mma(bh, cat(dl[2], kZero2), c);
-                    c = mma(bl, cat(dh[2], kZero2), c);
-                }
-            }
-            u32x2 rh, rl;
-            split4(c, rh, rl);
-            const int dofs = (16 * i + lr) * kSD + 4 * lg;
-            const bf16x8 Dhi = cat(ld8(S.Dh + dofs), kZero2);
-            const bf16x8 Dlo = cat(ld8(S.Dl + dofs), kZero2);
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = mma(Dhi, cat(rh, kZero2), d);
-            d = mma(Dhi, cat(rl, kZero2), d);
-            d = mma(Dlo, cat(rh, kZero2), d);
-            D[i] = d;
-            split4(d, dh[i], dl[i]);
-        }
-
-        // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta.
-        bf16x8 dph[2], dpl[2];
-        {
-            u32x2 ph[4], pl[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 x;
+            for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    x[r] = S.el[16 * i + 4 * lg + r] * D[i][r];
-                split4(x, ph[i], pl[i]);
-            }
-            dph[0] = cat(ph[0], ph[1]);
-            dph[1] = cat(ph[2], ph[3]);
-            dpl[0] = cat(pl[0], pl[1]);
-            dpl[1] = cat(pl[2], pl[3]);
-        }
-        const float eL = S.eL;
+                    h[mt][r] = a.h0[hbase + (int64_t)(16 * mt + 4 * lg + r) * a.dv + col];
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            h[mt] *= eL;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const uint16_t *kp = S.K + (32 * kk + 4 * lg + (lr >> 2)) * kSK + 16 * mt + 4 * (lr & 3);
-                const bf16x8 akt = cat(ld_tr(kp), ld_tr(kp + 16 * kSK));
-                h[mt] = mma(akt, dph[kk], h[mt]);
-                h[mt] = mma(akt, dpl[kk], h[mt]);
-            }
+            for (int mt = 0; mt < 8; ++mt)
+                h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    } else if (it.nchunks > 0) {
+        stage_load(st, a, it, 0, t, lane);
+        helper_prepare(S, S.buf[0], st, s, t, lane, meet);
+        if (it.nchunks > 1)
+            stage_load(st, a, it, 1, t, lane);
+    }
+    lds_barrier();
 
-        // (a7) O += P Delta (hi parts), staged through LDS for coalesced stores.
-        const bf16x8 db[2] = {cat(dh[0], dh[1]), cat(dh[2], dh[3])};
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-            for (int kk = 0; kk <= mi / 2; ++kk)
-                Oa[mi] = mma(frag_perm(S.P + (16 * mi + lr) * kST + 32 * kk, lg), db[kk], Oa[mi]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S.O[(16 * mi + 4 * lg + r) * kST + 16 * wv + lr] = f2bf(a.scale * Oa[mi][r]);
+    for (int c = 0; c < it.nchunks; ++c) {
+        if (state) {
+            state_chunk(S, S.buf[c & 1], a, it, c, s, lane, h);
+        } else if (c + 1 < it.nchunks) {
+            helper_prepare(S, S.buf[(c + 1) & 1], st, s, t, lane, meet);
+            if (c + 2 < it.nchunks)
+                stage_load(st, a, it, c + 2, t, lane);
         }
         lds_barrier();
-
-        uint16_t *o = static_cast<uint16_t *>(a.o);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = tid / 8 + 32 * i;
-            const int cc = 8 * (tid % 8);
-            if (row < L)
-                *reinterpret_cast<u32x4 *>(o + ((p + row) * a.Hv + j) * (int64_t)a.dv + c0 + cc) =
-                    *reinterpret_cast<const u32x4 *>(S.O + row * kST + cc);
-        }
     }
 
-    if (a.ht) {
+    if (state && a.ht) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
