@@ -74,18 +74,36 @@ constexpr int kC = 64;          // chunk length
 constexpr int kDK = 128;        // key dimension
 constexpr int kDVT = 64;        // value columns per workgroup
 constexpr int kThreads = 512;   // 4 state waves + 4 helper waves
-constexpr int kSK = kDK + 8;    // row stride (elements) of the K and Q tiles
-constexpr int kST = kC + 8;     // row stride of the 64-wide bf16 tiles
-constexpr int kSD = 16 + 8;     // row stride of the 16-wide bf16 tiles
-constexpr int kSN = 48 + 8;     // row stride of -A (rows 16..63, columns 0..47)
+// Row strides (elements) of the padded tiles, chosen = 2 (mod 32) 4-byte words
+// so that 16 rows read at one column fall in distinct LDS banks.
+constexpr int kSP = kC + 4;     // P
+constexpr int kSN = 48 + 4;     // -A (rows 16..63, columns 0..47)
+constexpr int kSD = 16 + 4;     // D blocks
+constexpr int kSO = 16 + 8;     // output staging (16-byte aligned rows)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
+
+// K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the 8-byte chunks
+// of each row permuted: chunk c of row r is stored at chunk c ^ g(r) (low four
+// bits).  For K and Q, g(r) = 4 (r % 4) + (r / 4) % 4, which spreads both
+// access patterns over distinct banks: 16 rows read at one column (MFMA
+// fragments) and 4 consecutive rows x 32 bytes (transpose reads).  V is only
+// read the second way, with g(r) = 4 (r % 4).
+__device__ __forceinline__ int swz_kq(int row) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+__device__ __forceinline__ int kq_at(int row, int chunk) {  // element offset of an 8-byte chunk
+    return row * kDK + ((chunk ^ swz_kq(row)) << 2);
+}
+__device__ __forceinline__ int v_at(int row, int chunk) {
+    return row * kDVT + ((chunk ^ ((row & 3) << 2)) << 2);
+}
 
 // One chunk's worth of shared operands.
 struct alignas(16) ChunkBuf {
-    uint16_t K[kC * kSK];       // K rows, [row][dk]
-    uint16_t Q[kC * kSK];       // Q rows, [row][dk]
-    uint16_t V[kC * kST];       // value tile, [row][col]
-    uint16_t P[kC * kST];       // P, lower 16-blocks (upper blocks stay zero)
+    uint16_t K[kC * kDK];       // K rows, [row][dk], chunks permuted
+    uint16_t Q[kC * kDK];       // Q rows, [row][dk], chunks permuted
+    uint16_t V[kC * kDVT];      // value tile, [row][col], chunks permuted
+    uint16_t P[kC * kSP];       // P, lower 16-blocks (upper blocks stay zero)
     uint16_t Anh[48 * kSN];     // -A hi, row r - 16, blocks below the diagonal
     uint16_t Anl[48 * kSN];     // -A lo
     uint16_t Dh[kC * kSD];      // D_i hi, rows 16 i .. 16 i + 15
@@ -101,7 +119,7 @@ struct alignas(16) ChunkBuf {
 struct alignas(16) Smem {
     ChunkBuf buf[2];
     float Ad[4][256];           // helper wave h: its diagonal block, Ad[r][p][m] = A_ii[4m + p][r]
-    uint16_t Ost[4][kC * kSD];  // state wave s: output staging, [row][col]
+    uint16_t Ost[4][kC * kSO];  // state wave s: output staging, [row][col]
     int hsync;                  // helper-wave meeting counter
 };
 
@@ -140,6 +158,11 @@ __device__ __forceinline__ bf16x8 frag_perm(const uint16_t *p, int g) {
     return cat(ld8(p + 4 * g), ld8(p + 16 + 4 * g));
 }
 
+// The same fragment from a chunk-permuted K or Q tile: row `row`, k-step kk.
+__device__ __forceinline__ bf16x8 frag_kq(const uint16_t *t, int row, int kk, int g) {
+    return cat(ld8(t + kq_at(row, 8 * kk + g)), ld8(t + kq_at(row, 8 * kk + 4 + g)));
+}
+
 // Transpose read of 4 bf16 (see the file comment).
 __device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -164,6 +187,16 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
 }
 
 constexpr u32x2 kZero2 = {0u, 0u};
+
+__device__ __forceinline__ f32x4 ld4f(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+
+// Keeps the compiler from moving instructions across this point, so loads
+// issued before it overlap the MFMAs after it.
+__device__ __forceinline__ void sched_fence() {
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int Ctrl, int RowMask>
 __device__ __forceinline__ float dpp(float x) {
@@ -255,41 +288,46 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
 template <int W>
 __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int lg) {
     constexpr int IA = 3 - W;
-    bf16x8 kr[4], qr[4];
+    constexpr int JN = (IA > W ? IA : W) + 1;  // column blocks visited
+    bf16x8 kr[4], qr[4], kj[2][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        kr[kk] = frag_perm(B.K + (16 * IA + lr) * kSK + 32 * kk, lg);
-        qr[kk] = frag_perm(B.Q + (16 * W + lr) * kSK + 32 * kk, lg);
+        kr[kk] = frag_kq(B.K, 16 * IA + lr, kk, lg);
+        qr[kk] = frag_kq(B.Q, 16 * W + lr, kk, lg);
+        kj[0][kk] = frag_kq(B.K, lr, kk, lg);
     }
+    const float gA = B.gam[16 * IA + lr], bA = B.bt[16 * IA + lr];
+    const float gP = B.gam[16 * W + lr];
 #pragma unroll
-    for (int j = 0; j <= (IA > W ? IA : W); ++j) {
-        bf16x8 kj[4];
+    for (int j = 0; j < JN; ++j) {
+        if (j + 1 < JN) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            kj[kk] = frag_perm(B.K + (16 * j + lr) * kSK + 32 * kk, lg);
+            for (int kk = 0; kk < 4; ++kk)
+                kj[(j + 1) & 1][kk] = frag_kq(B.K, 16 * (j + 1) + lr, kk, lg);
+        }
+        const f32x4 gc = ld4f(B.gam + 16 * j + 4 * lg);  // gamma of this lane's 4 columns
+        sched_fence();
         if (j <= IA) {
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[kk], kr[kk], c);
-            const int row = 16 * IA + lr;
-            const float gr = B.gam[row], br = B.bt[row];
+                c = mma(kj[j & 1][kk], kr[kk], c);
             if (j < IA) {
                 f32x4 val;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    val[r] = -br * __expf(gr - B.gam[16 * j + 4 * lg + r]) * c[r];
+                    val[r] = -bA * __expf(gA - gc[r]) * c[r];
                 u32x2 hi, lo;
                 split4(val, hi, lo);
-                const int o = (row - 16) * kSN + 16 * j + 4 * lg;
+                const int o = (16 * IA + lr - 16) * kSN + 16 * j + 4 * lg;
                 *reinterpret_cast<u32x2 *>(B.Anh + o) = hi;
                 *reinterpret_cast<u32x2 *>(B.Anl + o) = lo;
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int col = 4 * lg + r;  // column within the block; the row is lr
-                    ad[col * 16 + (lr & 3) * 4 + (lr >> 2)] =
-                        col < lr ? br * __expf(gr - B.gam[16 * IA + col]) * c[r] : 0.0f;
+                    const float e = __expf(fminf(gA - gc[r], 0.0f));
+                    ad[col * 16 + (lr & 3) * 4 + (lr >> 2)] = col < lr ? bA * e * c[r] : 0.0f;
                 }
             }
         }
@@ -297,17 +335,17 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[kk], qr[kk], c);
-            const int row = 16 * W + lr;
-            const float gr = B.gam[row];
+                c = mma(kj[j & 1][kk], qr[kk], c);
             f32x4 val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int col = 16 * j + 4 * lg + r;
-                val[r] = col <= row ? __expf(gr - B.gam[col]) * c[r] : 0.0f;
+                const float e = __expf(fminf(gP - gc[r], 0.0f));
+                val[r] = col <= 16 * W + lr ? e * c[r] : 0.0f;
             }
-            *reinterpret_cast<u32x2 *>(B.P + row * kST + 16 * j + 4 * lg) = pack4(val);
+            *reinterpret_cast<u32x2 *>(B.P + (16 * W + lr) * kSP + 16 * j + 4 * lg) = pack4(val);
         }
+        sched_fence();
     }
 }
 
@@ -321,17 +359,20 @@ __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         x[m] = (4 * m + p == c) ? 1.0f : 0.0f;
-    f32x4 acol[15];
 #pragma unroll
-    for (int r = 0; r < 15; ++r)
-        acol[r] = *reinterpret_cast<const f32x4 *>(ad + r * 16 + p * 4);  // A[4m + p][r]
+    for (int r0 = 0; r0 < 15; r0 += 8) {
+        f32x4 acol[8];
 #pragma unroll
-    for (int r = 0; r < 15; ++r) {
-        const float xr = quad_bcast(x[r / 4], r % 4);
+        for (int r = r0; r < r0 + 8 && r < 15; ++r)
+            acol[r - r0] = *reinterpret_cast<const f32x4 *>(ad + r * 16 + p * 4);  // A[4m + p][r]
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            if (4 * m + p > r)
-                x[m] -= acol[r][m] * xr;
+        for (int r = r0; r < r0 + 8 && r < 15; ++r) {
+            const float xr = quad_bcast(x[r / 4], r % 4);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (4 * m + p > r)
+                    x[m] -= acol[r - r0][m] * xr;
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -342,19 +383,27 @@ __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i
 }
 
 // Helper waves: put chunk c (already in `st`) into LDS buffer B with its
-// decay tables, A blocks, P and diagonal inverses.
-__device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, const Stage &st, int hw,
-                                               int t, int lane, int &meet) {
+// decay tables, A blocks, P and diagonal inverses.  Once `st` is in LDS it is
+// refilled with chunk `next` (if next >= 0), so those loads are in flight
+// during the products below and the state waves' whole next chunk.
+__device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
+                                               int lane, int &meet, const FwdArgs &a,
+                                               const Item &it, int next) {
     const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = t / 16 + 16 * i, col = 8 * (t % 16);
-        *reinterpret_cast<u32x4 *>(B.K + row * kSK + col) = st.k[i];
-        *reinterpret_cast<u32x4 *>(B.Q + row * kSK + col) = st.q[i];
+        // 16 bytes = chunks 2m, 2m+1; under the permutation they stay adjacent
+        // and swap places when g(row) is odd.
+        const int row = t / 16 + 16 * i, m = t % 16, g = swz_kq(row);
+        const int at = row * kDK + (((2 * m) ^ (g & ~1)) << 2);
+        const bool sw = g & 1;
+        const u32x4 kv = st.k[i], qv = st.q[i];
+        *reinterpret_cast<u32x4 *>(B.K + at) = sw ? u32x4{kv.z, kv.w, kv.x, kv.y} : kv;
+        *reinterpret_cast<u32x4 *>(B.Q + at) = sw ? u32x4{qv.z, qv.w, qv.x, qv.y} : qv;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<u32x4 *>(B.V + (t / 8 + 32 * i) * kST + 8 * (t % 8)) = st.v[i];
+        *reinterpret_cast<u32x4 *>(B.V + v_at(t / 8 + 32 * i, 2 * (t % 8))) = st.v[i];
     if (hw == 0) {
         // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
         const float x = wave_prefix_sum(st.g);
@@ -366,6 +415,8 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, const Stage
         if (lane == 0)
             B.eL = __expf(gL);
     }
+    if (next >= 0)
+        stage_load(st, a, it, next, t, lane);
     // Meet the other helper waves: the staged rows and gamma are in LDS.
     meet += 4;
     if (lane == 0)
@@ -387,35 +438,68 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, const Stage
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
-    // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0).
+    // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0),
+    // fragments loaded one row block ahead of the products.
     bf16x8 hb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
         hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
     f32x4 X[4], Oa[4];
+    bf16x8 fk[2][4], fq[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        fk[0][kk] = frag_kq(B.K, lr, kk, lg);
+        fq[0][kk] = frag_kq(B.Q, lr, kk, lg);
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
+        if (mi < 3) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                fk[(mi + 1) & 1][kk] = frag_kq(B.K, 16 * (mi + 1) + lr, kk, lg);
+                fq[(mi + 1) & 1][kk] = frag_kq(B.Q, 16 * (mi + 1) + lr, kk, lg);
+            }
+        }
+        sched_fence();
         X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
         Oa[mi] = X[mi];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int off = (16 * mi + lr) * kSK + 32 * kk;
-            X[mi] = mma(frag_perm(B.K + off, lg), hb[kk], X[mi]);
-            Oa[mi] = mma(frag_perm(B.Q + off, lg), hb[kk], Oa[mi]);
+            X[mi] = mma(fk[mi & 1][kk], hb[kk], X[mi]);
+            Oa[mi] = mma(fq[mi & 1][kk], hb[kk], Oa[mi]);
         }
+        sched_fence();
     }
     // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
     f32x4 R[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        const u32x2 vv = ld_tr(B.V + (16 * mi + 4 * lg + (lr >> 2)) * kST + 16 * s + 4 * (lr & 3));
+        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
+        const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
+        const u32x2 vv = ld_tr(B.V + v_at(16 * mi + 4 * lg + (lr >> 2), 4 * s + (lr & 3)));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mi + 4 * lg + r;
             const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
-            const float e = B.eg[row];
-            R[mi][r] = B.bt[row] * (vr - e * X[mi][r]);
-            Oa[mi][r] *= e;
+            R[mi][r] = bt4[r] * (vr - eg4[r] * X[mi][r]);
+            Oa[mi][r] *= eg4[r];
+        }
+    }
+    // Operands of the solve: -A blocks and D_i (hi and lo).
+    bf16x8 a1h, a1l, a2h, a2l, a3h, a3l, b3h, b3l, Dhi[4], Dlo[4];
+    {
+        a1h = cat(ld8(B.Anh + lr * kSN + 4 * lg), kZero2);
+        a1l = cat(ld8(B.Anl + lr * kSN + 4 * lg), kZero2);
+        a2h = frag_perm(B.Anh + (16 + lr) * kSN, lg);
+        a2l = frag_perm(B.Anl + (16 + lr) * kSN, lg);
+        a3h = frag_perm(B.Anh + (32 + lr) * kSN, lg);
+        a3l = frag_perm(B.Anl + (32 + lr) * kSN, lg);
+        b3h = cat(ld8(B.Anh + (32 + lr) * kSN + 32 + 4 * lg), kZero2);
+        b3l = cat(ld8(B.Anl + (32 + lr) * kSN + 32 + 4 * lg), kZero2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dofs = (16 * i + lr) * kSD + 4 * lg;
+            Dhi[i] = cat(ld8(B.Dh + dofs), kZero2);
+            Dlo[i] = cat(ld8(B.Dl + dofs), kZero2);
         }
     }
 
@@ -426,51 +510,40 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     for (int i = 0; i < 4; ++i) {
         f32x4 cc = R[i];
         if (i == 1) {
-            const int ao = lr * kSN + 4 * lg;
-            const bf16x8 ah = cat(ld8(B.Anh + ao), kZero2);
-            const bf16x8 al = cat(ld8(B.Anl + ao), kZero2);
-            cc = mma(ah, cat(dh[0], kZero2), cc);
-            cc = mma(ah, cat(dl[0], kZero2), cc);
-            cc = mma(al, cat(dh[0], kZero2), cc);
-        } else if (i >= 2) {
-            const int ao = (16 * (i - 1) + lr) * kSN;
-            const bf16x8 ah = frag_perm(B.Anh + ao, lg);
-            const bf16x8 al = frag_perm(B.Anl + ao, lg);
-            cc = mma(ah, cat(dh[0], dh[1]), cc);
-            cc = mma(ah, cat(dl[0], dl[1]), cc);
-            cc = mma(al, cat(dh[0], dh[1]), cc);
-            if (i == 3) {
-                const bf16x8 bh = cat(ld8(B.Anh + ao + 32 + 4 * lg), kZero2);
-                const bf16x8 bl = cat(ld8(B.Anl + ao + 32 + 4 * lg), kZero2);
-                cc = mma(bh, cat(dh[2], kZero2), cc);
-                cc = mma(bh, cat(dl[2], kZero2), cc);
-                cc = mma(bl, cat(dh[2], kZero2), cc);
-            }
+            cc = mma(a1h, cat(dh[0], kZero2), cc);
+            cc = mma(a1h, cat(dl[0], kZero2), cc);
+            cc = mma(a1l, cat(dh[0], kZero2), cc);
+        } else if (i == 2) {
+            cc = mma(a2h, cat(dh[0], dh[1]), cc);
+            cc = mma(a2h, cat(dl[0], dl[1]), cc);
+            cc = mma(a2l, cat(dh[0], dh[1]), cc);
+        } else if (i == 3) {
+            cc = mma(a3h, cat(dh[0], dh[1]), cc);
+            cc = mma(a3h, cat(dl[0], dl[1]), cc);
+            cc = mma(a3l, cat(dh[0], dh[1]), cc);
+            cc = mma(b3h, cat(dh[2], kZero2), cc);
+            cc = mma(b3h, cat(dl[2], kZero2), cc);
+            cc = mma(b3l, cat(dh[2], kZero2), cc);
         }
         u32x2 rh, rl;
         split4(cc, rh, rl);
-        const int dofs = (16 * i + lr) * kSD + 4 * lg;
-        const bf16x8 Dhi = cat(ld8(B.Dh + dofs), kZero2);
-        const bf16x8 Dlo = cat(ld8(B.Dl + dofs), kZero2);
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma(Dhi, cat(rh, kZero2), d);
-        d = mma(Dhi, cat(rl, kZero2), d);
-        d = mma(Dlo, cat(rh, kZero2), d);
+        d = mma(Dhi[i], cat(rh, kZero2), d);
+        d = mma(Dhi[i], cat(rl, kZero2), d);
+        d = mma(Dlo[i], cat(rh, kZero2), d);
         D[i] = d;
         split4(d, dh[i], dl[i]);
     }
 
-    // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta.
+    // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta,
+    // K^T fragments loaded one tile ahead of the products.
     bf16x8 dph[2], dpl[2];
     {
         u32x2 ph[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f32x4 x;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                x[r] = B.el[16 * i + 4 * lg + r] * D[i][r];
-            split4(x, ph[i], pl[i]);
+            const f32x4 el4 = ld4f(B.el + 16 * i + 4 * lg);
+            split4(el4 * D[i], ph[i], pl[i]);
         }
         dph[0] = cat(ph[0], ph[1]);
         dph[1] = cat(ph[2], ph[3]);
@@ -478,30 +551,50 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         dpl[1] = cat(pl[2], pl[3]);
     }
     const float eL = B.eL;
+    // K^T fragment of dk tile mt, k-step kk: rows 32 kk + 4 lg + j (+16), column 16 mt + lr.
+    auto ktf = [&](int mt, int kk) {
+        const int row = 32 * kk + 4 * lg + (lr >> 2), chunk = 4 * mt + (lr & 3);
+        return cat(ld_tr(B.K + kq_at(row, chunk)), ld_tr(B.K + kq_at(row + 16, chunk)));
+    };
+    bf16x8 kt[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        kt[0][kk] = ktf(0, kk);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
+        if (mt < 7) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                kt[(mt + 1) & 1][kk] = ktf(mt + 1, kk);
+        }
+        sched_fence();
         h[mt] *= eL;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const uint16_t *kp = B.K + (32 * kk + 4 * lg + (lr >> 2)) * kSK + 16 * mt + 4 * (lr & 3);
-            const bf16x8 akt = cat(ld_tr(kp), ld_tr(kp + 16 * kSK));
-            h[mt] = mma(akt, dph[kk], h[mt]);
-            h[mt] = mma(akt, dpl[kk], h[mt]);
+            h[mt] = mma(kt[mt & 1][kk], dph[kk], h[mt]);
+            h[mt] = mma(kt[mt & 1][kk], dpl[kk], h[mt]);
         }
+        sched_fence();
     }
 
     // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
     // its own LDS staging area (no other wave touches it).
     const bf16x8 db[2] = {cat(dh[0], dh[1]), cat(dh[2], dh[3])};
+    bf16x8 pf[6];
+#pragma unroll
+    for (int mi = 0, n = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int kk = 0; kk <= mi / 2; ++kk, ++n)
+            pf[n] = frag_perm(B.P + (16 * mi + lr) * kSP + 32 * kk, lg);
     uint16_t *ost = S.Ost[s];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0, n = 0; mi < 4; ++mi) {
 #pragma unroll
-        for (int kk = 0; kk <= mi / 2; ++kk)
-            Oa[mi] = mma(frag_perm(B.P + (16 * mi + lr) * kST + 32 * kk, lg), db[kk], Oa[mi]);
+        for (int kk = 0; kk <= mi / 2; ++kk, ++n)
+            Oa[mi] = mma(pf[n], db[kk], Oa[mi]);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            ost[(16 * mi + 4 * lg + r) * kSD + lr] = f2bf(a.scale * Oa[mi][r]);
+            ost[(16 * mi + 4 * lg + r) * kSO + lr] = f2bf(a.scale * Oa[mi][r]);
     }
     const int L = min(kC, it.len - kC * c);
     const int64_t p = it.p0 + (int64_t)kC * c;
@@ -509,7 +602,7 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int piece = lane + 64 * q, row = piece >> 1, half = piece & 1;
-        const u32x4 val = *reinterpret_cast<const u32x4 *>(ost + row * kSD + 8 * half);
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(ost + row * kSO + 8 * half);
         if (row < L)
             *reinterpret_cast<u32x4 *>(o + ((p + row) * a.Hv + it.j) * (int64_t)a.dv + it.c0 +
                                        16 * s + 8 * half) = val;
@@ -549,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     it.len = (int)(p1 - it.p0);
     it.nchunks = (it.len + kC - 1) / kC;
 
-    for (int i = tid; i < kC * kST; i += kThreads) {
+    for (int i = tid; i < kC * kSP; i += kThreads) {
         S.buf[0].P[i] = 0;
         S.buf[1].P[i] = 0;
     }
@@ -581,9 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         }
     } else if (it.nchunks > 0) {
         stage_load(st, a, it, 0, t, lane);
-        helper_prepare(S, S.buf[0], st, s, t, lane, meet);
-        if (it.nchunks > 1)
-            stage_load(st, a, it, 1, t, lane);
+        helper_prepare(S, S.buf[0], st, s, t, lane, meet, a, it, it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
 
@@ -591,9 +682,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         if (state) {
             state_chunk(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare(S, S.buf[(c + 1) & 1], st, s, t, lane, meet);
-            if (c + 2 < it.nchunks)
-                stage_load(st, a, it, c + 2, t, lane);
+            helper_prepare(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+                           c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
     }
