@@ -82,20 +82,28 @@ constexpr int kSD = 16 + 4;     // D blocks
 constexpr int kSO = 16 + 8;     // output staging (16-byte aligned rows)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 
-// K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the 8-byte chunks
-// of each row permuted: chunk c of row r is stored at chunk c ^ g(r) (low four
-// bits).  For K and Q, g(r) = 4 (r % 4) + (r / 4) % 4, which spreads both
-// access patterns over distinct banks: 16 rows read at one column (MFMA
-// fragments) and 4 consecutive rows x 32 bytes (transpose reads).  V is only
-// read the second way, with g(r) = 4 (r % 4).
-__device__ __forceinline__ int swz_kq(int row) {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
+// K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the 16-byte slots
+// of each row permuted: slot c of row r is stored at slot c ^ sigma(r).  For
+// K and Q, sigma(r) = 2 (r % 4) + (r / 4) % 2, so that MFMA fragment reads (8
+// consecutive rows, one 16-byte slot each) fall in distinct banks; V uses
+// sigma(r) = 2 (r % 4), which also spreads its transpose reads (4 rows x 32
+// bytes) over distinct banks.
+__device__ __forceinline__ int sig_kq(int row) {
+    return ((row & 3) << 1) | ((row >> 2) & 1);
 }
-__device__ __forceinline__ int kq_at(int row, int chunk) {  // element offset of an 8-byte chunk
-    return row * kDK + ((chunk ^ swz_kq(row)) << 2);
+__device__ __forceinline__ int kq_slot(int row, int slot) {  // element offset of a 16-byte slot
+    return row * kDK + ((slot ^ sig_kq(row)) << 3);
 }
-__device__ __forceinline__ int v_at(int row, int chunk) {
+__device__ __forceinline__ int v_at(int row, int chunk) {  // element offset of an 8-byte chunk
     return row * kDVT + ((chunk ^ ((row & 3) << 2)) << 2);
+}
+
+// The fp32 state is kept with its key rows permuted: accumulator tile mt, row
+// 4g + r holds key dimension pi(16 mt + 4g + r) = 32 (mt / 2) + 8 g + 4 (mt % 2)
+// + r.  Then the two stacked accumulator tiles 2k, 2k+1 of lane group g hold
+// key dims 32 k + 8 g .. + 7 in order: the B operand of K M0 in natural k order.
+__device__ __forceinline__ int key_of(int mt, int g, int r) {
+    return 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + r;
 }
 
 // One chunk's worth of shared operands.
@@ -118,7 +126,7 @@ struct alignas(16) ChunkBuf {
 
 struct alignas(16) Smem {
     ChunkBuf buf[2];
-    float Ad[4][256];           // helper wave h: its diagonal block, Ad[r][p][m] = A_ii[4m + p][r]
+    float Ad[4][256];           // helper wave h: its diagonal block A_ii, column-major
     uint16_t Ost[4][kC * kSO];  // state wave s: output staging, [row][col]
     int hsync;                  // helper-wave meeting counter
 };
@@ -126,6 +134,8 @@ struct alignas(16) Smem {
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+
 
 // Workgroup barrier that waits only for this wave's LDS (and scalar) accesses.
 __device__ __forceinline__ void lds_barrier() {
@@ -158,9 +168,25 @@ __device__ __forceinline__ bf16x8 frag_perm(const uint16_t *p, int g) {
     return cat(ld8(p + 4 * g), ld8(p + 16 + 4 * g));
 }
 
-// The same fragment from a chunk-permuted K or Q tile: row `row`, k-step kk.
-__device__ __forceinline__ bf16x8 frag_kq(const uint16_t *t, int row, int kk, int g) {
-    return cat(ld8(t + kq_at(row, 8 * kk + g)), ld8(t + kq_at(row, 8 * kk + 4 + g)));
+// Fragment addressing in a slot-permuted K or Q tile.  A fragment of row
+// 16 m + lr, k-step kk is the 16-byte slot 4 kk + lg (key dims 32 kk + 8 lg ..
+// + 7).  The permutation of rows 16 m + lr depends on lr only, so each lane
+// keeps one element offset per k-step parity and the fragment is at
+// t + 2048 m + 64 (kk / 2) + base[kk & 1].
+struct KqBase {
+    int b[2];
+};
+
+__device__ __forceinline__ KqBase kq_base(int lr, int lg) {
+    KqBase r;
+    r.b[0] = kq_slot(lr, lg);
+    r.b[1] = kq_slot(lr, 4 + lg);
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 frag_kq(const uint16_t *t, const KqBase &kb, int m, int kk) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4 *>(t + 2048 * m + 64 * (kk >> 1) + kb.b[kk & 1]));
 }
 
 // Transpose read of 4 bf16 (see the file comment).
@@ -187,6 +213,12 @@ __device__ __forceinline__ u32x2 pack4(f32x4 x) {
 }
 
 constexpr u32x2 kZero2 = {0u, 0u};
+
+// K = 16 product: lane l supplies A[l%16][4(l/16)+j] and B[4(l/16)+j][l%16]
+// (j = 0..3), the rows 4g..4g+3 a C-layout tile gives lane group g.
+__device__ __forceinline__ f32x4 mma16(u32x2 a, u32x2 b, f32x4 c) {
+    return mma(cat(a, kZero2), cat(b, kZero2), c);
+}
 
 __device__ __forceinline__ f32x4 ld4f(const float *p) {
     return *reinterpret_cast<const f32x4 *>(p);
@@ -289,12 +321,13 @@ template <int W>
 __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int lg) {
     constexpr int IA = 3 - W;
     constexpr int JN = (IA > W ? IA : W) + 1;  // column blocks visited
+    const KqBase kb = kq_base(lr, lg);
     bf16x8 kr[4], qr[4], kj[2][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        kr[kk] = frag_kq(B.K, 16 * IA + lr, kk, lg);
-        qr[kk] = frag_kq(B.Q, 16 * W + lr, kk, lg);
-        kj[0][kk] = frag_kq(B.K, lr, kk, lg);
+        kr[kk] = frag_kq(B.K, kb, IA, kk);
+        qr[kk] = frag_kq(B.Q, kb, W, kk);
+        kj[0][kk] = frag_kq(B.K, kb, 0, kk);
     }
     const float gA = B.gam[16 * IA + lr], bA = B.bt[16 * IA + lr];
     const float gP = B.gam[16 * W + lr];
@@ -303,7 +336,7 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
         if (j + 1 < JN) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kj[(j + 1) & 1][kk] = frag_kq(B.K, 16 * (j + 1) + lr, kk, lg);
+                kj[(j + 1) & 1][kk] = frag_kq(B.K, kb, j + 1, kk);
         }
         const f32x4 gc = ld4f(B.gam + 16 * j + 4 * lg);  // gamma of this lane's 4 columns
         sched_fence();
@@ -327,7 +360,7 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
                 for (int r = 0; r < 4; ++r) {
                     const int col = 4 * lg + r;  // column within the block; the row is lr
                     const float e = __expf(fminf(gA - gc[r], 0.0f));
-                    ad[col * 16 + (lr & 3) * 4 + (lr >> 2)] = col < lr ? bA * e * c[r] : 0.0f;
+                    ad[col * 16 + lr] = col < lr ? bA * e * c[r] : 0.0f;
                 }
             }
         }
@@ -350,35 +383,38 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
 }
 
 // (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32 (i = 3 - helper
-// index): lane 4c + p holds rows p, p+4, p+8, p+12 of column c.  Once x_r is
-// final it is broadcast within the lane quad and subtracted from the rows
-// below.
+// index).  Lane c (of each 16-lane group; the groups repeat the work) holds
+// column c of D in registers; once x_r is final, A[r2][r] x_r is subtracted
+// from every row r2 > r.  Column r of A_ii is read by all lanes at once (an
+// LDS broadcast; ad holds the block column-major).
 __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i, int lane) {
-    const int c = lane >> 2, p = lane & 3;
-    float x[4];
+    const int c = lane & 15;
+    float x[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-        x[m] = (4 * m + p == c) ? 1.0f : 0.0f;
+    for (int r = 0; r < 16; ++r)
+        x[r] = (r == c) ? 1.0f : 0.0f;
+    f32x4 col[2][4];
 #pragma unroll
-    for (int r0 = 0; r0 < 15; r0 += 8) {
-        f32x4 acol[8];
+    for (int q = 0; q < 4; ++q)
+        col[0][q] = ld4f(ad + 4 * q);
 #pragma unroll
-        for (int r = r0; r < r0 + 8 && r < 15; ++r)
-            acol[r - r0] = *reinterpret_cast<const f32x4 *>(ad + r * 16 + p * 4);  // A[4m + p][r]
+    for (int r = 0; r < 15; ++r) {
+        if (r + 1 < 15) {
 #pragma unroll
-        for (int r = r0; r < r0 + 8 && r < 15; ++r) {
-            const float xr = quad_bcast(x[r / 4], r % 4);
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                if (4 * m + p > r)
-                    x[m] -= acol[r - r0][m] * xr;
+            for (int q = (r + 1) / 4; q < 4; ++q)
+                col[(r + 1) & 1][q] = ld4f(ad + 16 * (r + 1) + 4 * q);
         }
-    }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const uint16_t hi = f2bf(x[m]);
-        B.Dh[(16 * i + 4 * m + p) * kSD + c] = hi;
-        B.Dl[(16 * i + 4 * m + p) * kSD + c] = f2bf(x[m] - bf2f(hi));
+        for (int r2 = r + 1; r2 < 16; ++r2)
+            x[r2] -= col[r & 1][r2 / 4][r2 % 4] * x[r];
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint16_t hi = f2bf(x[r]);
+            B.Dh[(16 * i + r) * kSD + c] = hi;
+            B.Dl[(16 * i + r) * kSD + c] = f2bf(x[r] - bf2f(hi));
+        }
     }
 }
 
@@ -392,14 +428,9 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // 16 bytes = chunks 2m, 2m+1; under the permutation they stay adjacent
-        // and swap places when g(row) is odd.
-        const int row = t / 16 + 16 * i, m = t % 16, g = swz_kq(row);
-        const int at = row * kDK + (((2 * m) ^ (g & ~1)) << 2);
-        const bool sw = g & 1;
-        const u32x4 kv = st.k[i], qv = st.q[i];
-        *reinterpret_cast<u32x4 *>(B.K + at) = sw ? u32x4{kv.z, kv.w, kv.x, kv.y} : kv;
-        *reinterpret_cast<u32x4 *>(B.Q + at) = sw ? u32x4{qv.z, qv.w, qv.x, qv.y} : qv;
+        const int at = kq_slot(t / 16 + 16 * i, t % 16);
+        *reinterpret_cast<u32x4 *>(B.K + at) = st.k[i];
+        *reinterpret_cast<u32x4 *>(B.Q + at) = st.q[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -446,18 +477,19 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
     f32x4 X[4], Oa[4];
     bf16x8 fk[2][4], fq[2][4];
+    const KqBase kb = kq_base(lr, lg);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        fk[0][kk] = frag_kq(B.K, lr, kk, lg);
-        fq[0][kk] = frag_kq(B.Q, lr, kk, lg);
+        fk[0][kk] = frag_kq(B.K, kb, 0, kk);
+        fq[0][kk] = frag_kq(B.Q, kb, 0, kk);
     }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         if (mi < 3) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                fk[(mi + 1) & 1][kk] = frag_kq(B.K, 16 * (mi + 1) + lr, kk, lg);
-                fq[(mi + 1) & 1][kk] = frag_kq(B.Q, 16 * (mi + 1) + lr, kk, lg);
+                fk[(mi + 1) & 1][kk] = frag_kq(B.K, kb, mi + 1, kk);
+                fq[(mi + 1) & 1][kk] = frag_kq(B.Q, kb, mi + 1, kk);
             }
         }
         sched_fence();
@@ -471,12 +503,13 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         sched_fence();
     }
     // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
+    const int vbase = v_at(4 * lg + (lr >> 2), 4 * s + (lr & 3));  // row block 0; + 16 rows per mi
     f32x4 R[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
         const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
-        const u32x2 vv = ld_tr(B.V + v_at(16 * mi + 4 * lg + (lr >> 2), 4 * s + (lr & 3)));
+        const u32x2 vv = ld_tr(B.V + vbase + 16 * kDVT * mi);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
@@ -485,21 +518,22 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         }
     }
     // Operands of the solve: -A blocks and D_i (hi and lo).
-    bf16x8 a1h, a1l, a2h, a2l, a3h, a3l, b3h, b3l, Dhi[4], Dlo[4];
+    u32x2 a1h, a1l, b3h, b3l, Dhi[4], Dlo[4];
+    bf16x8 a2h, a2l, a3h, a3l;
     {
-        a1h = cat(ld8(B.Anh + lr * kSN + 4 * lg), kZero2);
-        a1l = cat(ld8(B.Anl + lr * kSN + 4 * lg), kZero2);
+        a1h = ld8(B.Anh + lr * kSN + 4 * lg);
+        a1l = ld8(B.Anl + lr * kSN + 4 * lg);
         a2h = frag_perm(B.Anh + (16 + lr) * kSN, lg);
         a2l = frag_perm(B.Anl + (16 + lr) * kSN, lg);
         a3h = frag_perm(B.Anh + (32 + lr) * kSN, lg);
         a3l = frag_perm(B.Anl + (32 + lr) * kSN, lg);
-        b3h = cat(ld8(B.Anh + (32 + lr) * kSN + 32 + 4 * lg), kZero2);
-        b3l = cat(ld8(B.Anl + (32 + lr) * kSN + 32 + 4 * lg), kZero2);
+        b3h = ld8(B.Anh + (32 + lr) * kSN + 32 + 4 * lg);
+        b3l = ld8(B.Anl + (32 + lr) * kSN + 32 + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int dofs = (16 * i + lr) * kSD + 4 * lg;
-            Dhi[i] = cat(ld8(B.Dh + dofs), kZero2);
-            Dlo[i] = cat(ld8(B.Dl + dofs), kZero2);
+            Dhi[i] = ld8(B.Dh + dofs);
+            Dlo[i] = ld8(B.Dl + dofs);
         }
     }
 
@@ -510,9 +544,9 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     for (int i = 0; i < 4; ++i) {
         f32x4 cc = R[i];
         if (i == 1) {
-            cc = mma(a1h, cat(dh[0], kZero2), cc);
-            cc = mma(a1h, cat(dl[0], kZero2), cc);
-            cc = mma(a1l, cat(dh[0], kZero2), cc);
+            cc = mma16(a1h, dh[0], cc);
+            cc = mma16(a1h, dl[0], cc);
+            cc = mma16(a1l, dh[0], cc);
         } else if (i == 2) {
             cc = mma(a2h, cat(dh[0], dh[1]), cc);
             cc = mma(a2h, cat(dl[0], dl[1]), cc);
@@ -521,16 +555,16 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
             cc = mma(a3h, cat(dh[0], dh[1]), cc);
             cc = mma(a3h, cat(dl[0], dl[1]), cc);
             cc = mma(a3l, cat(dh[0], dh[1]), cc);
-            cc = mma(b3h, cat(dh[2], kZero2), cc);
-            cc = mma(b3h, cat(dl[2], kZero2), cc);
-            cc = mma(b3l, cat(dh[2], kZero2), cc);
+            cc = mma16(b3h, dh[2], cc);
+            cc = mma16(b3h, dl[2], cc);
+            cc = mma16(b3l, dh[2], cc);
         }
         u32x2 rh, rl;
         split4(cc, rh, rl);
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma(Dhi[i], cat(rh, kZero2), d);
-        d = mma(Dhi[i], cat(rl, kZero2), d);
-        d = mma(Dlo[i], cat(rh, kZero2), d);
+        d = mma16(Dhi[i], rh, d);
+        d = mma16(Dhi[i], rl, d);
+        d = mma16(Dlo[i], rh, d);
         D[i] = d;
         split4(d, dh[i], dl[i]);
     }
@@ -551,10 +585,18 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         dpl[1] = cat(pl[2], pl[3]);
     }
     const float eL = B.eL;
-    // K^T fragment of dk tile mt, k-step kk: rows 32 kk + 4 lg + j (+16), column 16 mt + lr.
+    // K^T fragment of accumulator tile mt, k-step kk: rows 32 kk + 4 lg + j
+    // (+16), key dim pi(16 mt + lr).  Lane 4 j + q of each 16-lane group points
+    // at row 32 kk + 4 lg + j, key dims 32 (mt / 2) + 8 q + 4 (mt % 2) .. + 3:
+    // half (mt % 2) of slot 4 (mt / 2) + q.
+    const int ktrow = 4 * lg + (lr >> 2);
+    int ktb[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        ktb[hh] = ktrow * kDK + (((4 * hh + (lr & 3)) ^ sig_kq(ktrow)) << 3);
     auto ktf = [&](int mt, int kk) {
-        const int row = 32 * kk + 4 * lg + (lr >> 2), chunk = 4 * mt + (lr & 3);
-        return cat(ld_tr(B.K + kq_at(row, chunk)), ld_tr(B.K + kq_at(row + 16, chunk)));
+        const uint16_t *p = B.K + ktb[(mt >> 1) & 1] + 64 * (mt >> 2) + 4 * (mt & 1) + 32 * kk * kDK;
+        return cat(ld_tr(p), ld_tr(p + 16 * kDK));
     };
     bf16x8 kt[2][2];
 #pragma unroll
@@ -666,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[mt][r] = a.h0[hbase + (int64_t)(16 * mt + 4 * lg + r) * a.dv + col];
+                    h[mt][r] = a.h0[hbase + (int64_t)key_of(mt, lg, r) * a.dv + col];
         } else {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
@@ -693,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a.ht[hbase + (int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = h[mt][r];
+                a.ht[hbase + (int64_t)key_of(mt, lg, r) * a.dv + col] = h[mt][r];
     }
 }
 
