@@ -1,0 +1,163 @@
+"""rocprofv3 helpers behind the roofline figures that bench.py reports.
+
+    python3 profile_traffic.py launch [--launches N]
+        The benchmark's workload launched N times back to back, then the
+        calibration copy: torch.bitwise_not over a 256 MiB int32 buffer into
+        another (reads 256 MiB, writes 256 MiB).  Run it once under
+        `rocprofv3 --pmc FETCH_SIZE` and once under `rocprofv3 --pmc WRITE_SIZE`.
+
+    python3 profile_traffic.py traffic FETCH_DIR WRITE_DIR --command CMD
+        Reads the two counter CSVs, scales the kernel's FETCH_SIZE and
+        WRITE_SIZE (KiB per dispatch) by what the same counters read for the
+        calibration copy, and writes profiles/traffic_headline_bf16.json (read
+        by bench.py) and a text summary beside it.
+
+    python3 profile_traffic.py stats STATS_DIR --command CMD
+        Writes profiles/kernel_stats_headline_bf16.md from a
+        `rocprofv3 --kernel-trace --stats` run of bench.py.
+"""
+import argparse
+import csv
+import glob
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+CAL_BYTES = 256 << 20
+CAL_KERNEL = "bitwise_not"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def launch(n):
+    import numpy as np
+    import torch
+    import gated_deltanet_chunked_chunk_amd as gdn
+    import gdn_inputs as gi
+    gdn.load()
+    dev = torch.device("cuda:0")
+    d = gi.make_config(bench.WORKLOAD)
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    g, b = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+    o = torch.empty((d["B"], d["T"], d["Hv"], d["dv"]), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((d["B"], d["Hv"], d["dk"], d["dv"]), dtype=torch.float32, device=dev)
+    for i in range(n):
+        gdn.gdn_chunk_fwd(q, k, v, g, b, out=o, final_state=ht)
+        torch.cuda.synchronize()
+        print(f"[launch] {i + 1}/{n}", flush=True)
+    src = torch.zeros(CAL_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print("[launch] calibration copy done", flush=True)
+
+
+def read_counter(dirname, counter):
+    """{kernel name: [value per dispatch]} for one counter."""
+    files = glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {dirname}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def pick(per, needle):
+    hits = [(k, v) for k, v in per.items() if needle in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {needle!r}, found {[k for k, _ in hits]}")
+    return hits[0]
+
+
+def traffic(fetch_dir, write_dir, command):
+    alg = bench.algorithmic_bytes(8, 2048, 16, 16, 128, 128)
+    out = {"kernel": bench.KERNEL_NAME, "workload": bench.WORKLOAD,
+           "kernel_source_sha256": bench.kernel_source_hash(),
+           "algorithmic_bytes_per_launch": alg,
+           "calibration": f"torch.bitwise_not, int32, {CAL_BYTES} bytes read and {CAL_BYTES} written",
+           "command": command}
+    total = 0.0
+    for counter, dirname in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = read_counter(dirname, counter)
+        kname, kv = pick(per, bench.KERNEL_NAME)
+        cname, cv = pick(per, CAL_KERNEL)
+        cal_kib = sum(cv) / len(cv)
+        factor = CAL_BYTES / (cal_kib * 1024.0)
+        kib = sum(kv) / len(kv)
+        b = kib * 1024.0 * factor
+        out[counter] = {"kernel_kib_per_dispatch": kib, "dispatches": len(kv),
+                        "calibration_kib": cal_kib, "scale_factor": factor, "bytes": b}
+        total += b
+    out["bytes_per_launch"] = total
+    out["traffic_over_algorithmic"] = total / alg
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "traffic_headline_bf16.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# HBM traffic of {bench.KERNEL_NAME}, {bench.WORKLOAD} (B=8 T=2048 H=16 d=128 bf16)",
+             "", "Commands:", "", "```", command, "```", "",
+             "| counter | kernel KiB/dispatch | copy KiB (256 MiB known) | scale | bytes/launch |",
+             "|---|---|---|---|---|"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = out[c]
+        lines.append(f"| {c} | {r['kernel_kib_per_dispatch']:.0f} | {r['calibration_kib']:.0f} | "
+                     f"{r['scale_factor']:.4f} | {r['bytes']:.0f} |")
+    lines += ["", f"Total {total:.0f} B per launch; algorithmic {alg} B; ratio "
+                  f"{total / alg:.3f}.", f"Kernel source sha256 {out['kernel_source_sha256']}."]
+    with open(os.path.join(PROFILES, "traffic_headline_bf16.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats(dirname, command):
+    files = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {dirname}")
+    with open(files[0], newline="") as f:
+        rows = list(csv.DictReader(f))
+    lines = [f"# Kernel time, bench.py on {bench.WORKLOAD} (B=8 T=2048 H=16 d=128 bf16)",
+             "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) <= 70 else name[:67] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(os.path.join(PROFILES, "kernel_stats_headline_bf16.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("launch")
+    a.add_argument("--launches", type=int, default=5)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--command", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_dir")
+    s.add_argument("--command", required=True)
+    args = ap.parse_args()
+    if args.cmd == "launch":
+        launch(args.launches)
+    elif args.cmd == "traffic":
+        traffic(args.fetch_dir, args.write_dir, args.command)
+    else:
+        stats(args.stats_dir, args.command)
+
+
+if __name__ == "__main__":
+    main()
