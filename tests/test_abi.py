@@ -62,7 +62,8 @@ def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE
     (dict(q=FAKE + 8), MISALIGNED), (dict(o=FAKE + 4), MISALIGNED),
     (dict(h0=FAKE + 2), MISALIGNED), (dict(ht=FAKE + 12), MISALIGNED),
     (dict(cu=FAKE, n_seqs=2, B=2), INVALID), (dict(cu=FAKE, n_seqs=0), INVALID),
-    (dict(cu=FAKE, n_seqs=2, cu_host=[0, 10, 64]), MISALIGNED),  # host copy valid; then alignment
+    # a valid host copy passes its checks; the misaligned g then fails the call
+    (dict(cu=FAKE, n_seqs=2, cu_host=[0, 10, 64], g=FAKE + 4), MISALIGNED),
     (dict(cu=FAKE + 4, n_seqs=2, cu_host=[0, 10, 64]), MISALIGNED),
     (dict(cu=FAKE, n_seqs=2, cu_host=[1, 10, 64]), INVALID),
     (dict(cu=FAKE, n_seqs=2, cu_host=[0, 10, 63]), INVALID),
@@ -71,8 +72,6 @@ def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE
     (dict(B=1 << 40, T=1 << 40), INVALID),
 ])
 def test_rejects_before_launch(kw, status):
-    if kw.get("cu_host") == [0, 10, 64] and kw.get("cu") == FAKE:
-        kw = dict(kw, g=FAKE + 4)  # keep the call failing on the host
     assert call(**kw) == status
 
 
