@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -78,7 +80,8 @@ constexpr int kThreads = 512;   // 4 state waves + 4 helper waves
 // so that 16 rows read at one column fall in distinct LDS banks.
 constexpr int kSP = kC + 4;     // P
 constexpr int kSN = 48 + 4;     // -A (rows 16..63, columns 0..47)
-constexpr int kSD = 16 + 4;     // D blocks
+constexpr int kSDT = 16;        // D blocks, transposed (one 32-byte row per column)
+constexpr int kAD = 20;         // column stride of the helpers' A_ii copies (conflict-free column reads)
 constexpr int kSO = 16 + 8;     // output staging (16-byte aligned rows)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 
@@ -114,8 +117,8 @@ struct alignas(16) ChunkBuf {
     uint16_t P[kC * kSP];       // P, lower 16-blocks (upper blocks stay zero)
     uint16_t Anh[48 * kSN];     // -A hi, row r - 16, blocks below the diagonal
     uint16_t Anl[48 * kSN];     // -A lo
-    uint16_t Dh[kC * kSD];      // D_i hi, rows 16 i .. 16 i + 15
-    uint16_t Dl[kC * kSD];      // D_i lo
+    uint16_t DhT[kC * kSDT];    // D_i^T hi: row 16 i + c is column c of D_i
+    uint16_t DlT[kC * kSDT];    // D_i^T lo
     float gam[kC];              // gamma_r
     float eg[kC];               // exp(gamma_r)
     float el[kC];               // exp(gamma_L - gamma_r)
@@ -126,7 +129,7 @@ struct alignas(16) ChunkBuf {
 
 struct alignas(16) Smem {
     ChunkBuf buf[2];
-    float Ad[4][256];           // helper wave h: its diagonal block A_ii, column-major
+    float Ad[4][16 * kAD];      // helper wave h: -A_ii of its diagonal block, column-major
     uint16_t Ost[4][kC * kSO];  // state wave s: output staging, [row][col]
     int hsync;                  // helper-wave meeting counter
 };
@@ -317,6 +320,13 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
 // all.  Block (i, j) is computed as K_j K_i^T (resp. K_j Q_i^T), whose C
 // layout puts row 16 i + l%16, columns 16 j + 4 (l/16) .. + 3 of the wanted
 // block in lane l: the row-major 8-byte pieces the A operands are read in.
+// The diagonal block A_ii goes first, so that its inverse can start as soon
+// as the other blocks are done.
+template <int W>
+__device__ __forceinline__ constexpr int block_order(int n) {
+    return n == 0 ? 3 - W : (n <= 3 - W ? n - 1 : n);
+}
+
 template <int W>
 __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int lg) {
     constexpr int IA = 3 - W;
@@ -327,16 +337,17 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
     for (int kk = 0; kk < 4; ++kk) {
         kr[kk] = frag_kq(B.K, kb, IA, kk);
         qr[kk] = frag_kq(B.Q, kb, W, kk);
-        kj[0][kk] = frag_kq(B.K, kb, 0, kk);
+        kj[0][kk] = frag_kq(B.K, kb, block_order<W>(0), kk);
     }
     const float gA = B.gam[16 * IA + lr], bA = B.bt[16 * IA + lr];
     const float gP = B.gam[16 * W + lr];
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
-        if (j + 1 < JN) {
+    for (int n = 0; n < JN; ++n) {
+        const int j = block_order<W>(n);
+        if (n + 1 < JN) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                kj[(j + 1) & 1][kk] = frag_kq(B.K, kb, j + 1, kk);
+                kj[(n + 1) & 1][kk] = frag_kq(B.K, kb, block_order<W>(n + 1), kk);
         }
         const f32x4 gc = ld4f(B.gam + 16 * j + 4 * lg);  // gamma of this lane's 4 columns
         sched_fence();
@@ -344,7 +355,7 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[j & 1][kk], kr[kk], c);
+                c = mma(kj[n & 1][kk], kr[kk], c);
             if (j < IA) {
                 f32x4 val;
 #pragma unroll
@@ -360,7 +371,7 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
                 for (int r = 0; r < 4; ++r) {
                     const int col = 4 * lg + r;  // column within the block; the row is lr
                     const float e = __expf(fminf(gA - gc[r], 0.0f));
-                    ad[col * 16 + lr] = col < lr ? bA * e * c[r] : 0.0f;
+                    ad[col * kAD + lr] = col < lr ? -(bA * e * c[r]) : 0.0f;
                 }
             }
         }
@@ -368,7 +379,7 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[j & 1][kk], qr[kk], c);
+                c = mma(kj[n & 1][kk], qr[kk], c);
             f32x4 val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -382,40 +393,53 @@ __device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int
     }
 }
 
+// x += (a from lane R of this lane's 16-lane row) * b: one v_fmac_f32 with a
+// DPP row_newbcast source.
+template <int R>
+__device__ __forceinline__ void fmac_rowbcast(float &x, float a, float b) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x) : "v"(a), "v"(b), "i"(R));
+}
+
+template <int R>
+__device__ __forceinline__ void dinv_step(float (&x)[16], const f32x4 (&na)[4]) {
+#pragma unroll
+    for (int r2 = R + 1; r2 < 16; ++r2)
+        fmac_rowbcast<R>(x[r2], na[r2 / 4][r2 % 4], x[R]);
+}
+
+template <int... R>
+__device__ __forceinline__ void dinv_steps(float (&x)[16], const f32x4 (&na)[4],
+                                           std::integer_sequence<int, R...>) {
+    (dinv_step<R>(x, na), ...);
+}
+
 // (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32 (i = 3 - helper
-// index).  Lane c (of each 16-lane group; the groups repeat the work) holds
-// column c of D in registers; once x_r is final, A[r2][r] x_r is subtracted
-// from every row r2 > r.  Column r of A_ii is read by all lanes at once (an
-// LDS broadcast; ad holds the block column-major).
+// index).  Lane c (of each 16-lane row; the rows repeat the work) holds
+// column c of -A_ii and computes column c of D_i: once x_r is final,
+// A[r2][r] x_r is subtracted from every row r2 > r, with A[r2][r] taken from
+// lane r by a row broadcast.  Lane row g then writes rows 4g .. 4g + 3 of
+// column c, as hi and lo bf16, into the transposed copy D_i^T.
 __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i, int lane) {
-    const int c = lane & 15;
+    const int c = lane & 15, lg = lane >> 4;
+    f32x4 na[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        na[q] = ld4f(ad + c * kAD + 4 * q);
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         x[r] = (r == c) ? 1.0f : 0.0f;
-    f32x4 col[2][4];
+    dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
+    f32x4 v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        col[0][q] = ld4f(ad + 4 * q);
-#pragma unroll
-    for (int r = 0; r < 15; ++r) {
-        if (r + 1 < 15) {
-#pragma unroll
-            for (int q = (r + 1) / 4; q < 4; ++q)
-                col[(r + 1) & 1][q] = ld4f(ad + 16 * (r + 1) + 4 * q);
-        }
-#pragma unroll
-        for (int r2 = r + 1; r2 < 16; ++r2)
-            x[r2] -= col[r & 1][r2 / 4][r2 % 4] * x[r];
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint16_t hi = f2bf(x[r]);
-            B.Dh[(16 * i + r) * kSD + c] = hi;
-            B.Dl[(16 * i + r) * kSD + c] = f2bf(x[r] - bf2f(hi));
-        }
-    }
+    for (int rr = 0; rr < 4; ++rr)
+        v[rr] = lg == 0 ? x[rr] : lg == 1 ? x[4 + rr] : lg == 2 ? x[8 + rr] : x[12 + rr];
+    u32x2 hi, lo;
+    split4(v, hi, lo);
+    const int o = (16 * i + c) * kSDT + 4 * lg;
+    *reinterpret_cast<u32x2 *>(B.DhT + o) = hi;
+    *reinterpret_cast<u32x2 *>(B.DlT + o) = lo;
 }
 
 // Helper waves: put chunk c (already in `st`) into LDS buffer B with its
@@ -529,11 +553,14 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         a3l = frag_perm(B.Anl + (32 + lr) * kSN, lg);
         b3h = ld8(B.Anh + (32 + lr) * kSN + 32 + 4 * lg);
         b3l = ld8(B.Anl + (32 + lr) * kSN + 32 + 4 * lg);
+        // D_i fragments (row lr, columns 4 lg .. + 3) from the transposed
+        // copy: lane 4 j + m of each 16-lane group points at column 4 lg + j,
+        // rows 4 m .. 4 m + 3.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int dofs = (16 * i + lr) * kSD + 4 * lg;
-            Dhi[i] = ld8(B.Dh + dofs);
-            Dlo[i] = ld8(B.Dl + dofs);
+            const int dofs = (16 * i + 4 * lg + (lr >> 2)) * kSDT + 4 * (lr & 3);
+            Dhi[i] = ld_tr(B.DhT + dofs);
+            Dlo[i] = ld_tr(B.DlT + dofs);
         }
     }
 
