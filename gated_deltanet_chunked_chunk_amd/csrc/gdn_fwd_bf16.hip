@@ -67,6 +67,7 @@ namespace gdn {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
@@ -199,16 +200,31 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// Four fp32 values as 4 bf16 (hi) and the rounding residuals as 4 bf16 (lo).
+// A packed bf16 pair held in an SGPR.  Used for the constant operands of
+// v_dot2c_f32_bf16: given as a compile-time constant, (-1, 0) is encoded as
+// the inline constant -1.0, which the hardware reads as the fp32 bit pattern
+// 0xbf800000, i.e. the pair (0, -1).
+template <unsigned V>
+__device__ __forceinline__ bf16x2 packed_bf16_sgpr() {
+    unsigned r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+    return __builtin_bit_cast(bf16x2, r);
+}
+
+// Four fp32 values as 4 bf16 (hi, round to nearest even) and the rounding
+// residuals as 4 bf16 (lo).  x - hi is exact in fp32; it is formed by a bf16
+// dot product of the packed pair with (-1, 0) or (0, -1) accumulated onto x.
 __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = f2bf(x[i]);
-        l[i] = f2bf(x[i] - bf2f(h[i]));
-    }
-    hi = u32x2{h[0] | (unsigned)h[1] << 16, h[2] | (unsigned)h[3] << 16};
-    lo = u32x2{l[0] | (unsigned)l[1] << 16, l[2] | (unsigned)l[3] << 16};
+    const bf16x2 h01 = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+    const bf16x2 h23 = {static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+    const bf16x2 m0 = packed_bf16_sgpr<0x0000bf80u>();  // (-1, 0)
+    const bf16x2 m1 = packed_bf16_sgpr<0xbf800000u>();  // (0, -1)
+    const bf16x2 l01 = {static_cast<__bf16>(__builtin_amdgcn_fdot2_f32_bf16(h01, m0, x[0], false)),
+                        static_cast<__bf16>(__builtin_amdgcn_fdot2_f32_bf16(h01, m1, x[1], false))};
+    const bf16x2 l23 = {static_cast<__bf16>(__builtin_amdgcn_fdot2_f32_bf16(h23, m0, x[2], false)),
+                        static_cast<__bf16>(__builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false))};
+    hi = u32x2{__builtin_bit_cast(unsigned, h01), __builtin_bit_cast(unsigned, h23)};
+    lo = u32x2{__builtin_bit_cast(unsigned, l01), __builtin_bit_cast(unsigned, l23)};
 }
 
 __device__ __forceinline__ u32x2 pack4(f32x4 x) {
@@ -418,8 +434,8 @@ __device__ __forceinline__ void dinv_steps(float (&x)[16], const f32x4 (&na)[4],
 // index).  Lane c (of each 16-lane row; the rows repeat the work) holds
 // column c of -A_ii and computes column c of D_i: once x_r is final,
 // A[r2][r] x_r is subtracted from every row r2 > r, with A[r2][r] taken from
-// lane r by a row broadcast.  Lane row g then writes rows 4g .. 4g + 3 of
-// column c, as hi and lo bf16, into the transposed copy D_i^T.
+// lane r by a row broadcast.  Column c is then stored, as hi and lo bf16, as
+// row c of the transposed copy D_i^T.
 __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i, int lane) {
     const int c = lane & 15, lg = lane >> 4;
     f32x4 na[4];
@@ -431,15 +447,26 @@ __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i
     for (int r = 0; r < 16; ++r)
         x[r] = (r == c) ? 1.0f : 0.0f;
     dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
-    f32x4 v;
+    // Lane row 0 writes column c of D_i as row 16 i + c of D_i^T (32 bytes
+    // of hi, 32 bytes of lo); the other rows computed the same values.
+    if (lg == 0) {
+        u32x4 hi[2], lo[2];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-        v[rr] = lg == 0 ? x[rr] : lg == 1 ? x[4 + rr] : lg == 2 ? x[8 + rr] : x[12 + rr];
-    u32x2 hi, lo;
-    split4(v, hi, lo);
-    const int o = (16 * i + c) * kSDT + 4 * lg;
-    *reinterpret_cast<u32x2 *>(B.DhT + o) = hi;
-    *reinterpret_cast<u32x2 *>(B.DlT + o) = lo;
+        for (int q = 0; q < 4; ++q) {
+            u32x2 h2, l2;
+            split4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, h2, l2);
+            hi[q >> 1][2 * (q & 1)] = h2.x;
+            hi[q >> 1][2 * (q & 1) + 1] = h2.y;
+            lo[q >> 1][2 * (q & 1)] = l2.x;
+            lo[q >> 1][2 * (q & 1) + 1] = l2.y;
+        }
+        u32x4 *dh = reinterpret_cast<u32x4 *>(B.DhT + (16 * i + c) * kSDT);
+        u32x4 *dl = reinterpret_cast<u32x4 *>(B.DlT + (16 * i + c) * kSDT);
+        dh[0] = hi[0];
+        dh[1] = hi[1];
+        dl[0] = lo[0];
+        dl[1] = lo[1];
+    }
 }
 
 // Helper waves: put chunk c (already in `st`) into LDS buffer B with its
