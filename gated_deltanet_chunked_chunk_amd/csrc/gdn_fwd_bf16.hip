@@ -476,6 +476,7 @@ __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int next) {
+    hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
     const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
