@@ -77,29 +77,35 @@ constexpr int kC = 64;          // chunk length
 constexpr int kDK = 128;        // key dimension
 constexpr int kDVT = 64;        // value columns per workgroup
 constexpr int kThreads = 512;   // 4 state waves + 4 helper waves
-// Row strides (elements) of the padded tiles, chosen = 2 (mod 32) 4-byte words
-// so that 16 rows read at one column fall in distinct LDS banks.
-constexpr int kSP = kC + 4;     // P
-constexpr int kSN = 48 + 4;     // -A (rows 16..63, columns 0..47)
+// LDS is 64 banks of 4 bytes, 256 bytes per cycle.  Measured on gfx950 with
+// the bank-conflict counter: a 16-byte-per-lane access serves 16 lanes per
+// cycle, those of one half-wave with equal parity of lane bits 2..4; an
+// 8-byte access serves 32 lanes per cycle.  Row strides of the padded tiles are 4 (mod 8)
+// 4-byte words, so that the 8-byte fragment reads (16 rows x 2 column groups
+// per cycle) fall in distinct banks.
+constexpr int kSP = kC + 8;     // P
+constexpr int kSN = 48 + 8;     // -A (rows 16..63, columns 0..47)
 constexpr int kSDT = 16;        // D blocks, transposed (one 32-byte row per column)
 constexpr int kAD = 20;         // column stride of the helpers' A_ii copies (conflict-free column reads)
-constexpr int kSO = 16 + 8;     // output staging (16-byte aligned rows)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 
-// K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the 16-byte slots
-// of each row permuted: slot c of row r is stored at slot c ^ sigma(r).  For
-// K and Q, sigma(r) = 2 (r % 4) + (r / 4) % 2, so that MFMA fragment reads (8
-// consecutive rows, one 16-byte slot each) fall in distinct banks; V uses
-// sigma(r) = 2 (r % 4), which also spreads its transpose reads (4 rows x 32
-// bytes) over distinct banks.
+// K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the pieces of each
+// row permuted.  A K or Q row is 256 bytes, one bank cycle: its 16-byte slot c
+// is stored at slot c ^ sigma(r), where sigma permutes the bits of r % 16
+// (bits 0, 1, 2, 3 of r become bits 0, 2, 3, 1).  Then MFMA fragment reads
+// (16 rows, slot 4 kk + lane group) are conflict-free for the lanes served
+// together, and the transpose reads of K (8 rows x 4 half-slots at the same
+// offset) meet at most two to a bank.  A V row is 128 bytes: its 8-byte chunk
+// c is stored at c ^ 4 ((r / 2) % 4), which makes the transpose reads (8 rows
+// x 4 chunks) conflict-free.
 __device__ __forceinline__ int sig_kq(int row) {
-    return ((row & 3) << 1) | ((row >> 2) & 1);
+    return (row & 1) | ((row >> 2) & 2) | ((row & 2) << 1) | ((row & 4) << 1);
 }
 __device__ __forceinline__ int kq_slot(int row, int slot) {  // element offset of a 16-byte slot
-    return row * kDK + ((slot ^ sig_kq(row)) << 3);
+    return row * kDK + ((slot ^ sig_kq(row & 15)) << 3);
 }
 __device__ __forceinline__ int v_at(int row, int chunk) {  // element offset of an 8-byte chunk
-    return row * kDVT + ((chunk ^ ((row & 3) << 2)) << 2);
+    return row * kDVT + ((chunk ^ (((row >> 1) & 3) << 2)) << 2);
 }
 
 // The fp32 state is kept with its key rows permuted: accumulator tile mt, row
@@ -131,7 +137,7 @@ struct alignas(16) ChunkBuf {
 struct alignas(16) Smem {
     ChunkBuf buf[2];
     float Ad[4][16 * kAD];      // helper wave h: -A_ii of its diagonal block, column-major
-    uint16_t Ost[4][kC * kSO];  // state wave s: output staging, [row][col]
+    uint16_t Ost[4][16 * kC];   // state wave s: output staging, [col][row], words permuted
     int hsync;                  // helper-wave meeting counter
 };
 
@@ -174,23 +180,24 @@ __device__ __forceinline__ bf16x8 frag_perm(const uint16_t *p, int g) {
 
 // Fragment addressing in a slot-permuted K or Q tile.  A fragment of row
 // 16 m + lr, k-step kk is the 16-byte slot 4 kk + lg (key dims 32 kk + 8 lg ..
-// + 7).  The permutation of rows 16 m + lr depends on lr only, so each lane
-// keeps one element offset per k-step parity and the fragment is at
-// t + 2048 m + 64 (kk / 2) + base[kk & 1].
+// + 7).  The permutation of rows 16 m + lr depends on lr only, and the slot
+// index 4 kk + lg = 4 kk ^ lg, so the element offset is base ^ (32 kk) with
+// base the offset of slot lg: the fragment is at t + 2048 m + (base ^ 32 kk).
 struct KqBase {
-    int b[2];
+    int b;
 };
 
+// The base is passed through an empty asm so that the four XORed offsets are
+// formed where they are used instead of being hoisted out of the chunk loop
+// and kept live through it.
 __device__ __forceinline__ KqBase kq_base(int lr, int lg) {
-    KqBase r;
-    r.b[0] = kq_slot(lr, lg);
-    r.b[1] = kq_slot(lr, 4 + lg);
-    return r;
+    int b = kq_slot(lr, lg);
+    asm volatile("" : "+v"(b));
+    return KqBase{b};
 }
 
 __device__ __forceinline__ bf16x8 frag_kq(const uint16_t *t, const KqBase &kb, int m, int kk) {
-    return __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4 *>(t + 2048 * m + 64 * (kk >> 1) + kb.b[kk & 1]));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(t + 2048 * m + (kb.b ^ (32 * kk))));
 }
 
 // Transpose read of 4 bf16 (see the file comment).
@@ -645,12 +652,10 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     // at row 32 kk + 4 lg + j, key dims 32 (mt / 2) + 8 q + 4 (mt % 2) .. + 3:
     // half (mt % 2) of slot 4 (mt / 2) + q.
     const int ktrow = 4 * lg + (lr >> 2);
-    int ktb[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-        ktb[hh] = ktrow * kDK + (((4 * hh + (lr & 3)) ^ sig_kq(ktrow)) << 3);
+    int ktb = kq_slot(ktrow, lr & 3);  // slot 4 a + (lr & 3) is at ktb ^ (32 a)
+    asm volatile("" : "+v"(ktb));
     auto ktf = [&](int mt, int kk) {
-        const uint16_t *p = B.K + ktb[(mt >> 1) & 1] + 64 * (mt >> 2) + 4 * (mt & 1) + 32 * kk * kDK;
+        const uint16_t *p = B.K + (ktb ^ (32 * (mt >> 1))) + 4 * (mt & 1) + 32 * kk * kDK;
         return cat(ld_tr(p), ld_tr(p + 16 * kDK));
     };
     bf16x8 kt[2][2];
@@ -675,7 +680,10 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     }
 
     // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
-    // its own LDS staging area (no other wave touches it).
+    // its own LDS staging area (no other wave touches it).  The staging copy
+    // is column-major: lane (g, c) writes its four rows 16 mi + 4 g .. + 3 of
+    // column c as one 8-byte word; four transpose reads then give lane L the
+    // 16 columns of row L.  Word w of column c is stored at w ^ ost_x(c).
     const bf16x8 db[2] = {cat(dh[0], dh[1]), cat(dh[2], dh[3])};
     bf16x8 pf[6];
 #pragma unroll
@@ -684,25 +692,28 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         for (int kk = 0; kk <= mi / 2; ++kk, ++n)
             pf[n] = frag_perm(B.P + (16 * mi + lr) * kSP + 32 * kk, lg);
     uint16_t *ost = S.Ost[s];
+    auto ost_x = [](int col) {
+        return (((col >> 1) & 1) << 3) ^ (((col >> 2) & 1) << 1) ^ (((col >> 3) & 1) << 2);
+    };
 #pragma unroll
     for (int mi = 0, n = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int kk = 0; kk <= mi / 2; ++kk, ++n)
             Oa[mi] = mma(pf[n], db[kk], Oa[mi]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ost[(16 * mi + 4 * lg + r) * kSO + lr] = f2bf(a.scale * Oa[mi][r]);
+        *reinterpret_cast<u32x2 *>(ost + lr * kC + 4 * ((4 * mi + lg) ^ ost_x(lr))) =
+            pack4(a.scale * Oa[mi]);
     }
     const int L = min(kC, it.len - kC * c);
     const int64_t p = it.p0 + (int64_t)kC * c;
-    uint16_t *o = static_cast<uint16_t *>(a.o);
+    uint16_t *o = static_cast<uint16_t *>(a.o) + ((p + lane) * a.Hv + it.j) * (int64_t)a.dv + it.c0 + 16 * s;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int piece = lane + 64 * q, row = piece >> 1, half = piece & 1;
-        const u32x4 val = *reinterpret_cast<const u32x4 *>(ost + row * kSO + 8 * half);
-        if (row < L)
-            *reinterpret_cast<u32x4 *>(o + ((p + row) * a.Hv + it.j) * (int64_t)a.dv + it.c0 +
-                                       16 * s + 8 * half) = val;
+    for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = 8 * hf + (lr >> 2), c1 = c0 + 4;
+        const int w = 4 * lg + (lr & 3);
+        const u32x2 r0 = ld_tr(ost + c0 * kC + 4 * (w ^ ost_x(c0)));
+        const u32x2 r1 = ld_tr(ost + c1 * kC + 4 * (w ^ ost_x(c1)));
+        if (lane < L)
+            *reinterpret_cast<u32x4 *>(o + 8 * hf) = u32x4{r0.x, r0.y, r1.x, r1.y};
     }
 }
 
