@@ -136,7 +136,7 @@ struct alignas(16) ChunkBuf {
 
 struct alignas(16) Smem {
     ChunkBuf buf[2];
-    float Ad[4][16 * kAD];      // helper wave h: -A_ii of its diagonal block, column-major
+    float Ad[4][16 * kAD];      // -A_ii of the diagonal blocks, column-major (helper wave 0)
     uint16_t Ost[4][16 * kC];   // state wave s: output staging, [col][row], words permuted
     int hsync;                  // helper-wave meeting counter
 };
@@ -338,81 +338,74 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
     st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * grow, 0, 0));
 }
 
-// (a3) The lower 16-blocks of K K^T and Q K^T that helper wave W forms: A row
-// block 3 - W (blocks j = 0 .. 3 - W) and P row block W (j = 0 .. W), five in
-// all.  Block (i, j) is computed as K_j K_i^T (resp. K_j Q_i^T), whose C
-// layout puts row 16 i + l%16, columns 16 j + 4 (l/16) .. + 3 of the wanted
-// block in lane l: the row-major 8-byte pieces the A operands are read in.
-// The diagonal block A_ii goes first, so that its inverse can start as soon
-// as the other blocks are done.
-template <int W>
-__device__ __forceinline__ constexpr int block_order(int n) {
-    return n == 0 ? 3 - W : (n <= 3 - W ? n - 1 : n);
+// (a3) The lower 16-blocks of K K^T and Q K^T.  Block (i, j) is computed as
+// K_j X_i^T (X = K or Q), whose C layout puts row 16 i + l%16, columns
+// 16 j + 4 (l/16) .. + 3 of the wanted block in lane l: the row-major 8-byte
+// pieces the A operands of the solve are read in.
+__device__ __forceinline__ void load_block(bf16x8 (&f)[4], const uint16_t *t, const KqBase &kb, int m) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        f[kk] = frag_kq(t, kb, m, kk);
 }
 
-template <int W>
-__device__ __forceinline__ void chunk_blocks(ChunkBuf &B, float *ad, int lr, int lg) {
-    constexpr int IA = 3 - W;
-    constexpr int JN = (IA > W ? IA : W) + 1;  // column blocks visited
-    const KqBase kb = kq_base(lr, lg);
-    bf16x8 kr[4], qr[4], kj[2][4];
+__device__ __forceinline__ f32x4 block_product(const bf16x8 (&xi)[4], const bf16x8 (&kj)[4]) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        kr[kk] = frag_kq(B.K, kb, IA, kk);
-        qr[kk] = frag_kq(B.Q, kb, W, kk);
-        kj[0][kk] = frag_kq(B.K, kb, block_order<W>(0), kk);
+    for (int kk = 0; kk < 4; ++kk)
+        c = mma(kj[kk], xi[kk], c);
+    return c;
+}
+
+// -A block (I, J), I > J: -beta_r exp(gamma_r - gamma_s) (k_r . k_s), hi + lo.
+template <int I, int J>
+__device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], const bf16x8 (&kj)[4],
+                                        int lr, int lg) {
+    const f32x4 c = block_product(ki, kj);
+    const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
+    const f32x4 gc = ld4f(B.gam + 16 * J + 4 * lg);
+    f32x4 val;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        val[r] = -b * __expf(g - gc[r]) * c[r];
+    u32x2 hi, lo;
+    split4(val, hi, lo);
+    const int o = (16 * I + lr - 16) * kSN + 16 * J + 4 * lg;
+    *reinterpret_cast<u32x2 *>(B.Anh + o) = hi;
+    *reinterpret_cast<u32x2 *>(B.Anl + o) = lo;
+}
+
+// P block (I, J), I >= J: exp(gamma_r - gamma_s) (q_r . k_s), s <= r.
+template <int I, int J>
+__device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], const bf16x8 (&kj)[4],
+                                        int lr, int lg) {
+    const f32x4 c = block_product(qi, kj);
+    const float g = B.gam[16 * I + lr];
+    const f32x4 gc = ld4f(B.gam + 16 * J + 4 * lg);
+    f32x4 val;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (J < I) {
+            val[r] = __expf(g - gc[r]) * c[r];
+        } else {
+            const float e = __expf(fminf(g - gc[r], 0.0f));
+            val[r] = 4 * lg + r <= lr ? e * c[r] : 0.0f;
+        }
     }
-    const float gA = B.gam[16 * IA + lr], bA = B.bt[16 * IA + lr];
-    const float gP = B.gam[16 * W + lr];
+    *reinterpret_cast<u32x2 *>(B.P + (16 * I + lr) * kSP + 16 * J + 4 * lg) = pack4(val);
+}
+
+// Diagonal block A_II (strictly lower part, negated) into ad, column-major.
+template <int I>
+__device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
+                                           int lr, int lg) {
+    const f32x4 c = block_product(ki, ki);
+    const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
+    const f32x4 gc = ld4f(B.gam + 16 * I + 4 * lg);
 #pragma unroll
-    for (int n = 0; n < JN; ++n) {
-        const int j = block_order<W>(n);
-        if (n + 1 < JN) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                kj[(n + 1) & 1][kk] = frag_kq(B.K, kb, block_order<W>(n + 1), kk);
-        }
-        const f32x4 gc = ld4f(B.gam + 16 * j + 4 * lg);  // gamma of this lane's 4 columns
-        sched_fence();
-        if (j <= IA) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[n & 1][kk], kr[kk], c);
-            if (j < IA) {
-                f32x4 val;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    val[r] = -bA * __expf(gA - gc[r]) * c[r];
-                u32x2 hi, lo;
-                split4(val, hi, lo);
-                const int o = (16 * IA + lr - 16) * kSN + 16 * j + 4 * lg;
-                *reinterpret_cast<u32x2 *>(B.Anh + o) = hi;
-                *reinterpret_cast<u32x2 *>(B.Anl + o) = lo;
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = 4 * lg + r;  // column within the block; the row is lr
-                    const float e = __expf(fminf(gA - gc[r], 0.0f));
-                    ad[col * kAD + lr] = col < lr ? -(bA * e * c[r]) : 0.0f;
-                }
-            }
-        }
-        if (j <= W) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                c = mma(kj[n & 1][kk], qr[kk], c);
-            f32x4 val;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int col = 16 * j + 4 * lg + r;
-                const float e = __expf(fminf(gP - gc[r], 0.0f));
-                val[r] = col <= 16 * W + lr ? e * c[r] : 0.0f;
-            }
-            *reinterpret_cast<u32x2 *>(B.P + (16 * W + lr) * kSP + 16 * j + 4 * lg) = pack4(val);
-        }
-        sched_fence();
+    for (int r = 0; r < 4; ++r) {
+        const int col = 4 * lg + r;  // column within the block; the row is lr
+        const float e = __expf(fminf(g - gc[r], 0.0f));
+        ad[col * kAD + lr] = col < lr ? -(b * e * c[r]) : 0.0f;
     }
 }
 
@@ -437,14 +430,14 @@ __device__ __forceinline__ void dinv_steps(float (&x)[16], const f32x4 (&na)[4],
     (dinv_step<R>(x, na), ...);
 }
 
-// (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32 (i = 3 - helper
-// index).  Lane c (of each 16-lane row; the rows repeat the work) holds
-// column c of -A_ii and computes column c of D_i: once x_r is final,
-// A[r2][r] x_r is subtracted from every row r2 > r, with A[r2][r] taken from
-// lane r by a row broadcast.  Column c is then stored, as hi and lo bf16, as
-// row c of the transposed copy D_i^T.
-__device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i, int lane) {
-    const int c = lane & 15, lg = lane >> 4;
+// (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32, the four blocks
+// in one wave: lane row g works on block g (from its copy of -A_gg in Ad[g]),
+// and lane c of the row computes column c: once x_r is final, A[r2][r] x_r is
+// subtracted from every row r2 > r, with A[r2][r] taken from lane r by a row
+// broadcast.  Column c is stored, as hi and lo bf16, as row 16 g + c of D^T.
+__device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    const float *ad = S.Ad[g];
     f32x4 na[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -454,25 +447,77 @@ __device__ __forceinline__ void diag_inverse(ChunkBuf &B, const float *ad, int i
     for (int r = 0; r < 16; ++r)
         x[r] = (r == c) ? 1.0f : 0.0f;
     dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
-    // Lane row 0 writes column c of D_i as row 16 i + c of D_i^T (32 bytes
-    // of hi, 32 bytes of lo); the other rows computed the same values.
-    if (lg == 0) {
-        u32x4 hi[2], lo[2];
+    u32x4 hi[2], lo[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u32x2 h2, l2;
-            split4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, h2, l2);
-            hi[q >> 1][2 * (q & 1)] = h2.x;
-            hi[q >> 1][2 * (q & 1) + 1] = h2.y;
-            lo[q >> 1][2 * (q & 1)] = l2.x;
-            lo[q >> 1][2 * (q & 1) + 1] = l2.y;
-        }
-        u32x4 *dh = reinterpret_cast<u32x4 *>(B.DhT + (16 * i + c) * kSDT);
-        u32x4 *dl = reinterpret_cast<u32x4 *>(B.DlT + (16 * i + c) * kSDT);
-        dh[0] = hi[0];
-        dh[1] = hi[1];
-        dl[0] = lo[0];
-        dl[1] = lo[1];
+    for (int q = 0; q < 4; ++q) {
+        u32x2 h2, l2;
+        split4(f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, h2, l2);
+        hi[q >> 1][2 * (q & 1)] = h2.x;
+        hi[q >> 1][2 * (q & 1) + 1] = h2.y;
+        lo[q >> 1][2 * (q & 1)] = l2.x;
+        lo[q >> 1][2 * (q & 1) + 1] = l2.y;
+    }
+    u32x4 *dh = reinterpret_cast<u32x4 *>(B.DhT + (16 * g + c) * kSDT);
+    u32x4 *dl = reinterpret_cast<u32x4 *>(B.DlT + (16 * g + c) * kSDT);
+    dh[0] = hi[0];
+    dh[1] = hi[1];
+    dl[0] = lo[0];
+    dl[1] = lo[1];
+}
+
+// The per-chunk products, split over the helper waves: helper 0 forms the
+// four diagonal blocks of A and their inverses; helpers 1 .. 3 form the
+// off-diagonal blocks of A and the blocks of P (six, five and five blocks).
+__device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg, int lane) {
+    const KqBase kb = kq_base(lr, lg);
+    if (hw == 0) {
+        bf16x8 k[2][4];
+        load_block(k[0], B.K, kb, 0);
+        load_block(k[1], B.K, kb, 1);
+        diag_block<0>(S.Ad[0], B, k[0], lr, lg);
+        load_block(k[0], B.K, kb, 2);
+        diag_block<1>(S.Ad[1], B, k[1], lr, lg);
+        load_block(k[1], B.K, kb, 3);
+        diag_block<2>(S.Ad[2], B, k[0], lr, lg);
+        diag_block<3>(S.Ad[3], B, k[1], lr, lg);
+        diag_inverse_all(B, S, lane);
+    } else if (hw == 1) {  // A30 A31 A32, P00 P10 P11
+        bf16x8 k3[4], q[4], kj[2][4];
+        load_block(k3, B.K, kb, 3);
+        load_block(kj[0], B.K, kb, 0);
+        load_block(q, B.Q, kb, 0);
+        load_block(kj[1], B.K, kb, 1);
+        a_block<3, 0>(B, k3, kj[0], lr, lg);
+        p_block<0, 0>(B, q, kj[0], lr, lg);
+        load_block(q, B.Q, kb, 1);
+        a_block<3, 1>(B, k3, kj[1], lr, lg);
+        p_block<1, 0>(B, q, kj[0], lr, lg);
+        load_block(kj[0], B.K, kb, 2);
+        p_block<1, 1>(B, q, kj[1], lr, lg);
+        a_block<3, 2>(B, k3, kj[0], lr, lg);
+    } else if (hw == 2) {  // A20 A21, P20 P21 P22
+        bf16x8 k2[4], q2[4], kj[2][4];
+        load_block(k2, B.K, kb, 2);
+        load_block(q2, B.Q, kb, 2);
+        load_block(kj[0], B.K, kb, 0);
+        load_block(kj[1], B.K, kb, 1);
+        a_block<2, 0>(B, k2, kj[0], lr, lg);
+        p_block<2, 0>(B, q2, kj[0], lr, lg);
+        a_block<2, 1>(B, k2, kj[1], lr, lg);
+        p_block<2, 1>(B, q2, kj[1], lr, lg);
+        p_block<2, 2>(B, q2, k2, lr, lg);
+    } else {  // A10, P30 P31 P32 P33
+        bf16x8 k1[4], q3[4], kj[2][4];
+        load_block(k1, B.K, kb, 1);
+        load_block(q3, B.Q, kb, 3);
+        load_block(kj[0], B.K, kb, 0);
+        load_block(kj[1], B.K, kb, 2);
+        a_block<1, 0>(B, k1, kj[0], lr, lg);
+        p_block<3, 0>(B, q3, kj[0], lr, lg);
+        p_block<3, 1>(B, q3, k1, lr, lg);
+        load_block(kj[0], B.K, kb, 3);
+        p_block<3, 2>(B, q3, kj[1], lr, lg);
+        p_block<3, 3>(B, q3, kj[0], lr, lg);
     }
 }
 
@@ -494,7 +539,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         *reinterpret_cast<u32x4 *>(B.V + v_at(t / 8 + 32 * i, 2 * (t % 8))) = st.v[i];
-    if (hw == 0) {
+    if (hw == 3) {
         // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
         const float x = wave_prefix_sum(st.g);
         const float gL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
@@ -514,14 +559,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
         __builtin_amdgcn_s_sleep(1);
 
-    float *ad = S.Ad[hw];
-    switch (hw) {
-    case 0: chunk_blocks<0>(B, ad, lr, lg); break;
-    case 1: chunk_blocks<1>(B, ad, lr, lg); break;
-    case 2: chunk_blocks<2>(B, ad, lr, lg); break;
-    default: chunk_blocks<3>(B, ad, lr, lg); break;
-    }
-    diag_inverse(B, ad, 3 - hw, lane);
+    helper_products(S, B, hw, lr, lg, lane);
 }
 
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16).
