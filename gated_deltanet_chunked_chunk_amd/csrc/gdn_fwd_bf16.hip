@@ -589,7 +589,6 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
                 fq[(mi + 1) & 1][kk] = frag_kq(B.Q, kb, mi + 1, kk);
             }
         }
-        sched_fence();
         X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
         Oa[mi] = X[mi];
 #pragma unroll
@@ -597,7 +596,6 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
             X[mi] = mma(fk[mi & 1][kk], hb[kk], X[mi]);
             Oa[mi] = mma(fq[mi & 1][kk], hb[kk], Oa[mi]);
         }
-        sched_fence();
     }
     // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
     const int vbase = v_at(4 * lg + (lr >> 2), 4 * s + (lr & 3));  // row block 0; + 16 rows per mi
@@ -707,14 +705,12 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
             for (int kk = 0; kk < 2; ++kk)
                 kt[(mt + 1) & 1][kk] = ktf(mt + 1, kk);
         }
-        sched_fence();
         h[mt] *= eL;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             h[mt] = mma(kt[mt & 1][kk], dph[kk], h[mt]);
             h[mt] = mma(kt[mt & 1][kk], dpl[kk], h[mt]);
         }
-        sched_fence();
     }
 
     // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
