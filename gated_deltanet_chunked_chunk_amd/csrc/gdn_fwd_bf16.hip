@@ -250,12 +250,6 @@ __device__ __forceinline__ f32x4 ld4f(const float *p) {
     return *reinterpret_cast<const f32x4 *>(p);
 }
 
-// Keeps the compiler from moving instructions across this point, so loads
-// issued before it overlap the MFMAs after it.
-__device__ __forceinline__ void sched_fence() {
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int Ctrl, int RowMask>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(
