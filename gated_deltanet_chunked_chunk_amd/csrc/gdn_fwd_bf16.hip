@@ -544,12 +544,12 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         if (lane == 0)
             B.eL = __expf(gL);
     }
-    if (next >= 0)
-        stage_load(st, a, it, next, t, lane);
     // Meet the other helper waves: the staged rows and gamma are in LDS.
     meet += 4;
     if (lane == 0)
         __hip_atomic_fetch_add(&S.hsync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (next >= 0)
+        stage_load(st, a, it, next, t, lane);
     while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
         __builtin_amdgcn_s_sleep(1);
 
