@@ -132,6 +132,46 @@ CONFIGS = {
 }
 
 
+def make_device(B, T, Hqk, Hv, dk, dv, seed, device="cuda"):
+    """Inputs of the same recipe (bf16 q, k, v; fp32 g, beta; no initial
+    state) drawn on the device with torch's Philox generator seeded with
+    `seed`, for workloads too large to draw on the host in reasonable time
+    (the long row: 6.5e9 normal draws).  Rows are drawn in blocks, so peak
+    device memory stays near the size of the returned tensors.  Returns device
+    tensors q, k [B, T, Hqk, dk], v [B, T, Hv, dv] (bf16) and g, beta
+    [B, T, Hv] (fp32)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def rows(n, width, normalise):
+        out = torch.empty((n, width), dtype=torch.bfloat16, device=device)
+        step = max(1, (1 << 26) // width)
+        for r0 in range(0, n, step):
+            r1 = min(n, r0 + step)
+            x = torch.randn((r1 - r0, width), generator=gen, device=device, dtype=torch.float32)
+            if normalise:
+                x /= torch.sqrt(torch.sum(x * x, dim=1, keepdim=True))
+            out[r0:r1] = x.to(torch.bfloat16)  # round to nearest even
+        return out
+
+    q = rows(B * T * Hqk, dk, True).view(B, T, Hqk, dk)
+    k = rows(B * T * Hqk, dk, True).view(B, T, Hqk, dk)
+    v = rows(B * T * Hv, dv, False).view(B, T, Hv, dv)
+    zg = torch.randn(B * T * Hv, generator=gen, device=device, dtype=torch.float32)
+    zb = torch.randn(B * T * Hv, generator=gen, device=device, dtype=torch.float32)
+    g = (torch.nn.functional.logsigmoid(zg) / 16.0).view(B, T, Hv)
+    beta = torch.sigmoid(zb).view(B, T, Hv)
+    return {"q": q, "k": k, "v": v, "g": g, "beta": beta,
+            "B": B, "T": T, "Hqk": Hqk, "Hv": Hv, "dk": dk, "dv": dv}
+
+
+def sampled_heads(seed, Hv, n=2):
+    """The v-heads a test compares with the oracle, drawn with the seed."""
+    rng = np.random.default_rng(seed)
+    return sorted(int(j) for j in rng.choice(Hv, size=n, replace=False))
+
+
 def make_config(name, **override):
     """Inputs of a named workload; keyword overrides change its sizes (tests
     use them to shrink a workload while keeping its recipe)."""

@@ -104,6 +104,36 @@ def test_chained_halves():
     assert rel_l2(o2, ro[:, s:]) <= tol_o and rel_l2(h2, rht) <= tol_h
 
 
+def test_long_row_full_size():
+    """The long row (T = 1,064,960; 16,640 chunks per head) at full size: run
+    whole and as two chained halves (equal bitwise: the halves split at a chunk
+    boundary), and both compared with the oracle on two sampled heads."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    c = gi.CONFIGS["long_bf16"]
+    B, T, H, dk, dv = c["B"], c["T"], c["Hv"], c["dk"], c["dv"]
+    print(f"[gpu case] long row B={B} T={T} H={H} dk={dk} dv={dv} bf16 (device-drawn inputs)",
+          flush=True)
+    t = gi.make_device(B, T, c["Hqk"], H, dk, dv, c["seed"])
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    o, ht = gdn.gdn_chunk_fwd(q, k, v, g, beta)
+    s = T // 2
+    o1, h1 = gdn.gdn_chunk_fwd(q[:, :s], k[:, :s], v[:, :s], g[:, :s], beta[:, :s])
+    o2, h2 = gdn.gdn_chunk_fwd(q[:, s:], k[:, s:], v[:, s:], g[:, s:], beta[:, s:],
+                               initial_state=h1)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :s], o1) and torch.equal(o[:, s:], o2) and torch.equal(ht, h2)
+    heads = gi.sampled_heads(c["seed"], H)
+    sel = lambda x: x[:, :, heads].float().cpu().numpy()
+    ro, rht = run_oracle({"q": sel(q), "k": sel(k), "v": sel(v), "g": sel(g), "beta": sel(beta),
+                          "h0": None, "cu_seqlens": None})
+    eo = rel_l2(sel(o), ro)
+    eh = rel_l2(ht[:, heads].cpu().numpy(), rht)
+    tol_o, tol_h = TOL["bf16"]
+    print(f"  heads {heads}: rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} "
+          f"(tol {tol_h:.0e})", flush=True)
+    assert eo <= tol_o and eh <= tol_h
+
+
 def test_deterministic():
     d = gi.make(2, 333, 2, 2, 128, 128, "bf16", 3700, h0_std=0.1)
     a = run_gpu(d)

@@ -49,3 +49,21 @@ def test_packed_lengths():
     assert cu[0] == 0 and cu[-1] == 4096 and np.all(np.diff(cu) >= 1)
     assert d["h0"].shape == (len(cu) - 1, 32, 128, 128)
     assert abs(float(d["h0"].std()) - 0.02) < 1e-3
+
+
+def test_device_draw_recipe_on_cpu():
+    """The device-side generator (used for the long row) keeps the recipe:
+    unit q/k rows before the bf16 cast, g <= 0, 0 < beta < 1, seeded."""
+    import torch
+    a = gi.make_device(1, 300, 2, 4, 64, 32, seed=9, device="cpu")
+    b = gi.make_device(1, 300, 2, 4, 64, 32, seed=9, device="cpu")
+    assert a["q"].shape == (1, 300, 2, 64) and a["v"].shape == (1, 300, 4, 32)
+    assert a["q"].dtype == torch.bfloat16 and a["g"].dtype == torch.float32
+    for x in ("q", "k", "v", "g", "beta"):
+        assert torch.equal(a[x], b[x])
+    norms = a["q"].float().norm(dim=-1)
+    assert torch.all((norms - 1).abs() < 1e-2)
+    assert torch.all(a["g"] <= 0) and torch.all((a["beta"] > 0) & (a["beta"] < 1))
+    assert abs(float(a["v"].float().std()) - 1.0) < 0.05
+    heads = gi.sampled_heads(9, 16)
+    assert len(set(heads)) == 2 and all(0 <= j < 16 for j in heads)
