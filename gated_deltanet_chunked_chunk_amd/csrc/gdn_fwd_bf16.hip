@@ -606,59 +606,48 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
             Oa[mi][r] *= eg4[r];
         }
     }
-    // Operands of the solve: -A blocks and D_i (hi and lo).
-    u32x2 a1h, a1l, b3h, b3l, Dhi[4], Dlo[4];
-    bf16x8 a2h, a2l, a3h, a3l;
-    {
-        a1h = ld8(B.Anh + lr * kSN + 4 * lg);
-        a1l = ld8(B.Anl + lr * kSN + 4 * lg);
-        a2h = frag_perm(B.Anh + (16 + lr) * kSN, lg);
-        a2l = frag_perm(B.Anl + (16 + lr) * kSN, lg);
-        a3h = frag_perm(B.Anh + (32 + lr) * kSN, lg);
-        a3l = frag_perm(B.Anl + (32 + lr) * kSN, lg);
-        b3h = ld8(B.Anh + (32 + lr) * kSN + 32 + 4 * lg);
-        b3l = ld8(B.Anl + (32 + lr) * kSN + 32 + 4 * lg);
-        // D_i fragments (row lr, columns 4 lg .. + 3) from the transposed
-        // copy: lane 4 j + m of each 16-lane group points at column 4 lg + j,
-        // rows 4 m .. 4 m + 3.
+    // Operands of the solve.  Each block of -A and each D_i is one A operand
+    // holding its hi part in k positions 8g..8g+3 and its lo part in
+    // 8g+4..8g+7 (lane group g, columns 4g..4g+3 of row lr); multiplied by a
+    // B operand that holds one bf16 part of the right-hand side twice, one
+    // 32-deep product gives (hi + lo) x part.
+    bf16x8 An[6], Dd[4];  // blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int dofs = (16 * i + 4 * lg + (lr >> 2)) * kSDT + 4 * (lr & 3);
-            Dhi[i] = ld_tr(B.DhT + dofs);
-            Dlo[i] = ld_tr(B.DlT + dofs);
+    for (int i = 1, n = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < i; ++j, ++n) {
+            const int o = (16 * (i - 1) + lr) * kSN + 16 * j + 4 * lg;
+            An[n] = cat(ld8(B.Anh + o), ld8(B.Anl + o));
         }
+    // D_i fragments (row lr, columns 4 lg .. + 3) from the transposed
+    // copy: lane 4 j + m of each 16-lane group points at column 4 lg + j,
+    // rows 4 m .. 4 m + 3.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int dofs = (16 * i + 4 * lg + (lr >> 2)) * kSDT + 4 * (lr & 3);
+        Dd[i] = cat(ld_tr(B.DhT + dofs), ld_tr(B.DlT + dofs));
     }
 
-    // (a4, a5) Delta_i = D_i (R_i - sum_{j<i} A_ij Delta_j), split products.
+    // (a4, a5) Delta_i = D_i (R_i - sum_{j<i} A_ij Delta_j).  Once Delta_j is
+    // known its products go into every later right-hand side, the next one
+    // first: the dependent chain is two products per block step.
     u32x2 dh[4], dl[4];
     f32x4 D[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f32x4 cc = R[i];
-        if (i == 1) {
-            cc = mma16(a1h, dh[0], cc);
-            cc = mma16(a1h, dl[0], cc);
-            cc = mma16(a1l, dh[0], cc);
-        } else if (i == 2) {
-            cc = mma(a2h, cat(dh[0], dh[1]), cc);
-            cc = mma(a2h, cat(dl[0], dl[1]), cc);
-            cc = mma(a2l, cat(dh[0], dh[1]), cc);
-        } else if (i == 3) {
-            cc = mma(a3h, cat(dh[0], dh[1]), cc);
-            cc = mma(a3h, cat(dl[0], dl[1]), cc);
-            cc = mma(a3l, cat(dh[0], dh[1]), cc);
-            cc = mma16(b3h, dh[2], cc);
-            cc = mma16(b3h, dl[2], cc);
-            cc = mma16(b3l, dh[2], cc);
-        }
         u32x2 rh, rl;
-        split4(cc, rh, rl);
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma16(Dhi[i], rh, d);
-        d = mma16(Dhi[i], rl, d);
-        d = mma16(Dlo[i], rh, d);
+        split4(R[i], rh, rl);
+        f32x4 d = mma(Dd[i], cat(rh, rh), f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mma(Dd[i], cat(rl, rl), d);
         D[i] = d;
         split4(d, dh[i], dl[i]);
+        const bf16x8 bh = cat(dh[i], dh[i]), bl = cat(dl[i], dl[i]);
+#pragma unroll
+        for (int r = i + 1; r < 4; ++r) {
+            const int n = (r - 1) * r / 2 + i;  // block (r, i)
+            R[r] = mma(An[n], bh, R[r]);
+            R[r] = mma(An[n], bl, R[r]);
+        }
     }
 
     // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta,
