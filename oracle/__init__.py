@@ -1,4 +1,4 @@
-"""CPU oracle for the gated delta rule forward.
+"""CPU oracle for the gated delta rule, forward and reverse mode.
 
 TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  It shares no code with the HIP
@@ -7,6 +7,8 @@ library and imports nothing from it.
 Two independent routes to the same fp64 result:
   * gdn_fwd   -- the token-by-token recurrence in plain C (gdn_oracle.c),
                  threaded over independent (sequence, head, column block) units;
+  * gdn_bwd   -- its reverse mode, token by token in plain C, threaded over
+                 (sequence, head) units;
   * chunked   -- the chunk-parallel algebra in numpy (chunked.py).
 
 Every function here is pinned by the CPU tests (closed forms, invariants,
@@ -43,6 +45,11 @@ def _bind(lib):
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, ctypes.c_double,
                   P, P, ctypes.c_int64, P, P, ctypes.c_int32]
+    f = lib.gdn_oracle_bwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, ctypes.c_double,
+                  P, P, P, ctypes.c_int64, P, P, P, P, P, P, ctypes.c_int32]
     return lib
 
 
@@ -103,3 +110,48 @@ def gdn_fwd(q, k, v, g, beta, scale=1.0, h0=None, cu_seqlens=None, nthreads=None
     if rc != 0:
         raise RuntimeError(f"gdn_oracle_fwd failed with code {rc}")
     return o, ht
+
+
+def gdn_bwd(q, k, v, g, beta, do, scale=1.0, h0=None, dht=None, cu_seqlens=None,
+            nthreads=None, lib_path=None):
+    """Token-by-token fp64 reverse mode: the gradients of
+    L = sum(do * o) + sum(dht * ht) for the forward of `gdn_fwd` with the same
+    arguments.  do: [B, T, Hv, dv]; dht: [N, Hv, dk, dv] or None.  Returns
+    (dq, dk [B, T, Hqk, dk], dv [B, T, Hv, dv], dg, dbeta [B, T, Hv],
+    dh0 [N, Hv, dk, dv]), all fp64."""
+    lib = _load(lib_path)
+    q, k, v, g, beta, do = (_f32(x) for x in (q, k, v, g, beta, do))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) \
+            or beta.shape != (B, T, Hv) or do.shape != v.shape:
+        raise ValueError("shape mismatch")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        N = cu.shape[0] - 1
+        cu_p = cu.ctypes.data
+    else:
+        cu = None
+        N = B
+        cu_p = None
+    for name, x in (("h0", h0), ("dht", dht)):
+        if x is not None and np.shape(x) != (N, Hv, dk, dv):
+            raise ValueError(f"{name} shape mismatch")
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    dht = None if dht is None else np.ascontiguousarray(dht, dtype=np.float64)
+    dq = np.zeros((B, T, Hqk, dk), dtype=np.float64)
+    dk_ = np.zeros((B, T, Hqk, dk), dtype=np.float64)
+    dv_ = np.zeros((B, T, Hv, dv), dtype=np.float64)
+    dg = np.zeros((B, T, Hv), dtype=np.float64)
+    dbeta = np.zeros((B, T, Hv), dtype=np.float64)
+    dh0 = np.zeros((N, Hv, dk, dv), dtype=np.float64)
+    rc = lib.gdn_oracle_bwd(B, T, Hqk, Hv, dk, dv, q.ctypes.data, k.ctypes.data,
+                            v.ctypes.data, g.ctypes.data, beta.ctypes.data, do.ctypes.data,
+                            float(scale), None if h0 is None else h0.ctypes.data,
+                            None if dht is None else dht.ctypes.data, cu_p, N,
+                            dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data, dg.ctypes.data,
+                            dbeta.ctypes.data, dh0.ctypes.data,
+                            int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"gdn_oracle_bwd failed with code {rc}")
+    return dq, dk_, dv_, dg, dbeta, dh0

@@ -299,3 +299,118 @@ ALL_PINS = [
     pin_packed_equals_separate, pin_chained_halves, pin_grouped_heads,
     pin_thread_invariance,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Reverse mode.  Each pin takes `fwd` and `bwd` (the signatures of
+# oracle.gdn_fwd and oracle.gdn_bwd); the loss is L = sum(do * o) + sum(dht * ht).
+
+def _bwd_case(rng, B, T, Hqk, Hv, dk, dv, N):
+    q, k, v, g, beta = _rand_inputs(rng, B, T, Hqk, Hv, dk, dv)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True).astype(np.float32)
+    do = rng.standard_normal((B, T, Hv, dv)).astype(np.float32)
+    h0 = rng.standard_normal((N, Hv, dk, dv)) * 0.3
+    dht = rng.standard_normal((N, Hv, dk, dv))
+    return q, k, v, g, beta, do, h0, dht
+
+
+def pin_bwd_finite_differences(fwd, bwd):
+    """Every gradient equals the central difference of the forward loss.  A
+    packed batch of two documents with grouped value heads, an initial state,
+    a loss on the final state and a scale.  fp32 inputs move by 2^-12, which
+    fp32 holds exactly at these magnitudes; the difference quotient is then
+    accurate to about 1e-8 (its error is second order in the step)."""
+    rng = _rng(101)
+    cu = np.array([0, 7, 16])
+    q, k, v, g, beta, do, h0, dht = _bwd_case(rng, 1, 16, 1, 2, 8, 8, 2)
+    scale = 0.7
+
+    def loss(args, h0_):
+        o, ht = fwd(*args, scale=scale, h0=h0_, cu_seqlens=cu)
+        return float(np.sum(do.astype(np.float64) * o) + np.sum(dht * ht))
+
+    grads = bwd(q, k, v, g, beta, do, scale=scale, h0=h0, dht=dht, cu_seqlens=cu)
+    base = [q, k, v, g, beta]
+    h = 2.0 ** -12
+    for gi, name in enumerate(("q", "k", "v", "g", "beta")):
+        x = base[gi]
+        fd = np.zeros(x.shape)
+        for idx in np.ndindex(x.shape):
+            args = list(base)
+            xp = x.copy(); xp[idx] += np.float32(h); args[gi] = xp
+            lp = loss(args, h0)
+            xm = x.copy(); xm[idx] -= np.float32(h); args[gi] = xm
+            lm = loss(args, h0)
+            fd[idx] = (lp - lm) / (2 * h)
+        _close(grads[gi], fd, 1e-6, f"d{name} against finite differences")
+    fd = np.zeros(h0.shape)
+    for idx in np.ndindex(h0.shape):
+        hp = h0.copy(); hp[idx] += 1e-6
+        hm = h0.copy(); hm[idx] -= 1e-6
+        fd[idx] = (loss(base, hp) - loss(base, hm)) / 2e-6
+    _close(grads[5], fd, 1e-6, "dh0 against finite differences")
+
+
+def pin_bwd_single_token(fwd, bwd):
+    """One token from a zero state: o = scale b (k.q) v and ht = b k v^T, so
+    with u = v.do and w = k^T dht v:
+    dq = scale b u k, dk = scale b u q + b dht v, dv = scale b (k.q) do + b dht^T k,
+    db = scale (k.q) u + w, dg = 0, dh0 = a (I - b k k^T)(scale q do^T + dht)."""
+    rng = _rng(102)
+    q, k, v, g, beta, do, _, dht = _bwd_case(rng, 1, 1, 1, 1, 6, 5, 1)
+    scale = 1.3
+    dq, dk, dv, dg, db, dh0 = bwd(q, k, v, g, beta, do, scale=scale, dht=dht)
+    q_, k_, v_, o_ = (x[0, 0, 0].astype(np.float64) for x in (q, k, v, do))
+    a, b = math.exp(float(g[0, 0, 0])), float(beta[0, 0, 0])
+    D = dht[0, 0]
+    u, kq = float(v_ @ o_), float(k_ @ q_)
+    _close(dq[0, 0, 0], scale * b * u * k_, 1e-13, "dq")
+    _close(dk[0, 0, 0], scale * b * u * q_ + b * (D @ v_), 1e-13, "dk")
+    _close(dv[0, 0, 0], scale * b * kq * o_ + b * (D.T @ k_), 1e-13, "dv")
+    _close(db[0, 0, 0], scale * kq * u + float(k_ @ D @ v_), 1e-13, "dbeta")
+    assert dg[0, 0, 0] == 0.0, "dg from a zero state"
+    dM = scale * np.outer(q_, o_) + D
+    _close(dh0[0, 0], a * (dM - b * np.outer(k_, k_ @ dM)), 1e-13, "dh0")
+
+
+def pin_bwd_linear_in_upstream(fwd, bwd):
+    """The gradients are linear in the upstream gradients (do, dht) jointly."""
+    rng = _rng(103)
+    q, k, v, g, beta, do1, h0, dht1 = _bwd_case(rng, 2, 11, 2, 4, 5, 3, 2)
+    # upstream values on a 2^-8 grid, so alpha * do1 + do2 is exact in fp32
+    do1 = (np.round(do1 * 256) / 256).astype(np.float32)
+    do2 = (np.round(rng.standard_normal(do1.shape) * 256) / 256).astype(np.float32)
+    dht2 = rng.standard_normal(dht1.shape)
+    alpha = 0.5
+    g1 = bwd(q, k, v, g, beta, do1, h0=h0, dht=dht1)
+    g2 = bwd(q, k, v, g, beta, do2, h0=h0, dht=dht2)
+    g3 = bwd(q, k, v, g, beta, (alpha * do1 + do2).astype(np.float32), h0=h0,
+             dht=alpha * dht1 + dht2)
+    for a_, b_, c_, name in zip(g1, g2, g3, ("dq", "dk", "dv", "dg", "dbeta", "dh0")):
+        _close(c_, alpha * a_ + b_, 1e-11, f"{name} linear in the upstream gradient")
+
+
+def pin_bwd_packed_equals_separate(fwd, bwd):
+    """A packed call's gradients equal per-document calls', bitwise."""
+    rng = _rng(104)
+    lengths = [5, 0, 9, 1]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    q, k, v, g, beta, do, h0, dht = _bwd_case(rng, 1, T, 1, 2, 4, 3, len(lengths))
+    packed = bwd(q, k, v, g, beta, do, h0=h0, dht=dht, cu_seqlens=cu)
+    for n, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        if a == b:
+            assert np.array_equal(packed[5][n], h0[n] * 0 + dht[n]), "empty document: dh0 = dht"
+            continue
+        sl = slice(a, b)
+        sep = bwd(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl], do[:, sl],
+                  h0=h0[n:n + 1], dht=dht[n:n + 1])
+        for x, y in zip(packed[:5], sep[:5]):
+            assert np.array_equal(x[:, sl], y), f"document {n} differs when packed"
+        assert np.array_equal(packed[5][n], sep[5][0]), f"dh0 of document {n}"
+
+
+BWD_PINS = [
+    pin_bwd_finite_differences, pin_bwd_single_token, pin_bwd_linear_in_upstream,
+    pin_bwd_packed_equals_separate,
+]

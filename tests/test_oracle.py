@@ -1,14 +1,20 @@
 """The CPU oracle against its pins (closed forms, exact brute force, a hand-worked
-example, the independent chunked route, and invariants)."""
+example, the independent chunked route, invariants, and for the reverse mode
+finite differences and closed forms)."""
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, BWD_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
 def test_oracle_pin(pin):
     pin(oracle.gdn_fwd)
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_oracle_bwd_pin(pin):
+    pin(oracle.gdn_fwd, oracle.gdn_bwd)
 
 
 def test_oracle_rejects_bad_arguments():

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from oracle import build as oracle_build
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, BWD_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gdn_oracle.c")
 
@@ -68,3 +68,45 @@ def test_pins_catch_mutant(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the mutant {name}"
+
+
+# Mistakes in the reverse mode; the forward pins never run it, so these must be
+# caught by the reverse-mode pins (with the correct forward for the finite
+# differences).
+BWD_MUTANTS = {
+    "bwd_dq_unscaled": ("dq[i] = P->scale * acc;", "dq[i] = acc;"),
+    "bwd_dy_sign": ("acc2 += a * Mprev[(int64_t)i * dv + c] * (-b * W->dd[c]);",
+                    "acc2 += a * Mprev[(int64_t)i * dv + c] * (b * W->dd[c]);"),
+    "bwd_dk_write_term_dropped": ("dkk[i] = acc + acc2;", "dkk[i] = acc2;"),
+    "bwd_dg_not_scaled_by_a": ("P->dg[row] = a * dga;", "P->dg[row] = dga;"),
+    "bwd_state_grad_not_decayed": ("dM[e] = a * dP[e];", "dM[e] = dP[e];"),
+    "bwd_dbeta_without_prediction": ("dbeta += dd * ((double)vt[c] - W->y[c]);",
+                                     "dbeta += dd * (double)vt[c];"),
+    "bwd_dv_missing_beta": ("dvv[c] = b * dd;", "dvv[c] = dd;"),
+    "bwd_output_grad_previous_state": ("acc += Mt[(int64_t)i * dv + c] * (double)dot[c];",
+                                       "acc += Mprev[(int64_t)i * dv + c] * (double)dot[c];"),
+    "bwd_final_state_grad_ignored": ("dM[e] = P->dht ? P->dht[", "dM[e] = 0 ? P->dht["),
+    "bwd_group_sum_first_head_only": ("for (int32_t gi = 0; gi < G; ++gi) {",
+                                      "for (int32_t gi = 0; gi < 1; ++gi) {"),
+    "bwd_dP_without_prediction_term": (
+        "const double v_ = dM[(int64_t)i * dv + c] + (double)kt[i] * (-b * W->dd[c]);",
+        "const double v_ = dM[(int64_t)i * dv + c];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_catch_mutant(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = _source()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle_build.build(str(path), str(tmp_path / f"lib{name}.so"))
+    bwd = functools.partial(oracle.gdn_bwd, lib_path=lib)
+    caught = []
+    for pin in BWD_PINS:
+        try:
+            pin(oracle.gdn_fwd, bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no reverse-mode pin catches the mutant {name}"
