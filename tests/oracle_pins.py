@@ -410,7 +410,23 @@ def pin_bwd_packed_equals_separate(fwd, bwd):
         assert np.array_equal(packed[5][n], sep[5][0]), f"dh0 of document {n}"
 
 
+def pin_bwd_chunked_route(fwd, bwd):
+    """The chunk-parallel reverse mode (numpy, explicit solves; the algebra the
+    GPU backward uses) equals the token-by-token reverse mode at several chunk
+    sizes, with documents, grouped heads, initial states and a state loss."""
+    import oracle
+    rng = _rng(105)
+    cu = np.array([0, 5, 70, 70, 131])
+    q, k, v, g, beta, do, h0, dht = _bwd_case(rng, 1, 131, 2, 4, 8, 6, 4)
+    ref = bwd(q, k, v, g, beta, do, scale=0.8, h0=h0, dht=dht, cu_seqlens=cu)
+    for C in (1, 3, 8, 64):
+        out = oracle.chunked.bwd(q, k, v, g, beta, do, C, scale=0.8, h0=h0, dht=dht,
+                                 cu_seqlens=cu)
+        for x, y, name in zip(out, ref, ("dq", "dk", "dv", "dg", "dbeta", "dh0")):
+            _close(x, y, 1e-12, f"chunked {name} at C={C}")
+
+
 BWD_PINS = [
     pin_bwd_finite_differences, pin_bwd_single_token, pin_bwd_linear_in_upstream,
-    pin_bwd_packed_equals_separate,
+    pin_bwd_packed_equals_separate, pin_bwd_chunked_route,
 ]
