@@ -1,4 +1,5 @@
-"""Python binding of libgdn, the chunkwise Gated DeltaNet forward for MI355X.
+"""Python binding of libgdn, the chunkwise Gated DeltaNet forward and backward
+for MI355X.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of libgdn.so.  PyTorch provides device memory and the stream.  The
@@ -9,7 +10,8 @@ raises.
 import ctypes
 import os
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_status_string",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd",
+           "gdn_chunk_bwd_workspace_size", "gdn_status_string",
            "gdn_last_hip_error", "gdn_version", "GdnError", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +48,12 @@ def load():
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
                                   ctypes.c_float, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
+                                  ctypes.c_float, P, P, P, I32, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_hip_error.restype = ctypes.c_int
@@ -76,29 +84,16 @@ def _dtype_code(torch, dt):
     raise GdnError(2, f"unsupported dtype {dt}")
 
 
-def gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
-    return load().gdn_chunk_fwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs)
-
-
-def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
-                  cu_seqlens_host=None, output_final_state=True, out=None, final_state=None,
-                  workspace=None, stream=None):
-    """o, ht = gdn_chunk_fwd(q, k, v, g, beta, ...) on the current HIP stream.
-
-    q, k: [B, T, H_qk, dk]; v: [B, T, H_v, dv] (bf16 or fp32, one dtype);
-    g, beta: [B, T, H_v] fp32; initial_state: [N, H_v, dk, dv] fp32 or None;
-    cu_seqlens: int32 [N + 1] device tensor for a packed row (B = 1), with an
-    optional host copy (list or CPU tensor) that is then validated.
-    Returns (o [B, T, H_v, dv], ht [N, H_v, dk, dv] fp32 or None).  `out`,
-    `final_state` and `workspace` may be given preallocated.
-    """
-    import torch
-    lib = load()
+def _check_inputs(torch, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                  extra=()):
+    """Validates the forward's inputs (and `extra` named device tensors);
+    returns (dtype code, B, T, H_qk, H_v, dk, dv, N, host cu array or None)."""
     tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)]
     if initial_state is not None:
         tensors.append(("initial_state", initial_state))
     if cu_seqlens is not None:
         tensors.append(("cu_seqlens", cu_seqlens))
+    tensors += [(n, t) for n, t in extra if t is not None]
     for name, t in tensors:
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise GdnError(1, f"{name} must be a device tensor")
@@ -129,6 +124,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
     if initial_state is not None:
         if initial_state.dtype != torch.float32 or initial_state.shape != (N, Hv, dk, dv):
             raise GdnError(1, "initial_state must be fp32 [N, H_v, dk, dv]")
+    return dt, B, T, Hqk, Hv, dk, dv, N, host_arr
+
+
+def _raise(st):
+    msg = gdn_status_string(st)
+    if st == 5:
+        msg += f" (hipError_t {gdn_last_hip_error()})"
+    raise GdnError(st, msg)
+
+
+def gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
+    return load().gdn_chunk_fwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
+                  cu_seqlens_host=None, output_final_state=True, out=None, final_state=None,
+                  workspace=None, stream=None):
+    """o, ht = gdn_chunk_fwd(q, k, v, g, beta, ...) on the current HIP stream.
+
+    q, k: [B, T, H_qk, dk]; v: [B, T, H_v, dv] (bf16 or fp32, one dtype);
+    g, beta: [B, T, H_v] fp32; initial_state: [N, H_v, dk, dv] fp32 or None;
+    cu_seqlens: int32 [N + 1] device tensor for a packed row (B = 1), with an
+    optional host copy (list or CPU tensor) that is then validated.
+    Returns (o [B, T, H_v, dv], ht [N, H_v, dk, dv] fp32 or None).  `out`,
+    `final_state` and `workspace` may be given preallocated.
+    """
+    import torch
+    lib = load()
+    dt, B, T, Hqk, Hv, dk, dv, N, host_arr = _check_inputs(torch, q, k, v, g, beta,
+                                                            initial_state, cu_seqlens,
+                                                            cu_seqlens_host)
     dev = q.device
     if out is None:
         out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
@@ -149,8 +175,50 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
                            ptr(workspace), 0 if workspace is None else workspace.numel(),
                            stream)
     if st != 0:
-        msg = gdn_status_string(st)
-        if st == 5:
-            msg += f" (hipError_t {gdn_last_hip_error()})"
-        raise GdnError(st, msg)
+        _raise(st)
     return out, final_state
+
+
+def gdn_chunk_bwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
+    return load().gdn_chunk_bwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs)
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
+                  cu_seqlens=None, cu_seqlens_host=None, workspace=None, stream=None):
+    """dq, dk, dv, dg, dbeta, dh0 = gdn_chunk_bwd(q, k, v, g, beta, do, ...):
+    the gradients of sum(do * o) + sum(dht * ht) for the forward with the same
+    arguments, on the current HIP stream.  do: [B, T, H_v, dv] in the dtype of
+    q; dht: [N, H_v, dk, dv] fp32 or None.  dq, dk, dv come back in the input
+    dtype, dg, dbeta and dh0 in fp32.  The workspace (bytes from
+    gdn_chunk_bwd_workspace_size) is allocated here unless given."""
+    import torch
+    lib = load()
+    dt, B, T, Hqk, Hv, dk, dv, N, host_arr = _check_inputs(
+        torch, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+        extra=(("do", do), ("dht", dht)))
+    if do.dtype != q.dtype or do.shape != v.shape:
+        raise GdnError(1, "do must match v in shape and dtype")
+    if dht is not None and (dht.dtype != torch.float32 or dht.shape != (N, Hv, dk, dv)):
+        raise GdnError(1, "dht must be fp32 [N, H_v, dk, dv]")
+    dev = q.device
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta)
+    dh0 = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    ws_bytes = lib.gdn_chunk_bwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.gdn_chunk_bwd(dt, B, T, Hqk, Hv, dk, dv, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
+                           float(scale), ptr(initial_state), ptr(cu_seqlens),
+                           None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
+                           N if cu_seqlens is not None else 0, ptr(do), ptr(dht), ptr(dq),
+                           ptr(dk_), ptr(dv_), ptr(dg), ptr(dbeta), ptr(dh0), ptr(workspace),
+                           0 if workspace is None else workspace.numel(), stream)
+    if st != 0:
+        _raise(st)
+    return dq, dk_, dv_, dg, dbeta, dh0

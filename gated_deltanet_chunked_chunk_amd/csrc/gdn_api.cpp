@@ -108,6 +108,105 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     return GDN_OK;
 }
 
+// Chunks of 64 tokens over all sequences: exact for batch rows; with
+// cu_seqlens the bound ceil(T / 64) + N covers any split into N documents.
+static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N) {
+    const int64_t per_row = (T + 63) / 64;
+    return packed ? per_row + N : B * per_row;
+}
+
+size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
+                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs) {
+    if (dtype != GDN_BF16 || dk != 128 || (dv != 64 && dv != 128) || B < 1 || T < 1 ||
+        H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || n_seqs < 1)
+        return 0;
+    // Packed documents need B == 1; the packed bound also covers one row.
+    return gdn::bwd_workspace_bytes(bwd_chunks(B, T, B == 1, B == 1 ? n_seqs : (int32_t)B), H_v,
+                                    dk, dv);
+}
+
+gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                         int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float scale, const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                         int32_t n_seqs, const void *dout, const float *dht, void *dq,
+                         void *dk_, void *dv_, float *dg, float *dbeta, float *dh0,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
+        return GDN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !g || !beta || !dout || !dq || !dk_ || !dv_ || !dg || !dbeta)
+        return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return GDN_ERR_UNSUPPORTED;
+    if (H_v % H_qk != 0 || dtype != GDN_BF16 || dk != 128 || (dv != 64 && dv != 128))
+        return GDN_ERR_UNSUPPORTED;
+    const int64_t hmax = H_v > H_qk ? H_v : H_qk;
+    if (B > INT64_MAX / T || B * T > INT64_MAX / (hmax * 128))
+        return GDN_ERR_INVALID_ARG;
+    int32_t N = (int32_t)B;
+    if (cu_seqlens) {
+        if (B != 1 || n_seqs < 1)
+            return GDN_ERR_INVALID_ARG;
+        N = n_seqs;
+        if (cu_seqlens_host) {
+            if (cu_seqlens_host[0] != 0 || (int64_t)cu_seqlens_host[N] != T)
+                return GDN_ERR_INVALID_ARG;
+            for (int32_t i = 0; i < N; ++i)
+                if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+                    return GDN_ERR_INVALID_ARG;
+        }
+    } else if (cu_seqlens_host) {
+        return GDN_ERR_INVALID_ARG;
+    } else if (B > INT32_MAX) {
+        return GDN_ERR_INVALID_ARG;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(h0) || !aligned16(cu_seqlens) || !aligned16(dout) || !aligned16(dht) ||
+        !aligned16(dq) || !aligned16(dk_) || !aligned16(dv_) || !aligned16(dg) ||
+        !aligned16(dbeta) || !aligned16(dh0))
+        return GDN_ERR_MISALIGNED;
+    const int64_t n_chunks = bwd_chunks(B, T, cu_seqlens != nullptr, N);
+    if (n_chunks > INT32_MAX)
+        return GDN_ERR_INVALID_ARG;
+    const size_t need = gdn::bwd_workspace_bytes(n_chunks, H_v, dk, dv);
+    if (!workspace || workspace_bytes < need)
+        return GDN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return GDN_ERR_MISALIGNED;
+
+    gdn::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.h0 = h0;
+    a.cu = cu_seqlens;
+    a.dout = dout;
+    a.dht = dht;
+    a.dq = dq;
+    a.dk_ = dk_;
+    a.dv_ = dv_;
+    a.dg = dg;
+    a.dbeta = dbeta;
+    a.dh0 = dh0;
+    a.T = T;
+    a.n_chunks = n_chunks;
+    a.Hqk = H_qk;
+    a.Hv = H_v;
+    a.dk = dk;
+    a.dv = dv;
+    a.n_seqs = N;
+    a.scale = scale;
+    gdn::bwd_carve(a, workspace);
+    const hipError_t e = gdn::launch_bwd_bf16(a, stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
 const char *gdn_status_string(gdn_status status) {
     switch (status) {
     case GDN_OK: return "GDN_OK";

@@ -1,0 +1,1085 @@
+// Chunkwise gated delta rule backward, bf16 inputs, dk = 128, for gfx950.
+//
+// Reverse mode of the forward in gdn_fwd_bf16.hip: the gradients of
+// L = sum(do * o) + sum(dht * ht) with respect to q, k, v, g, beta and h0.
+// The pages name the backward as the follow-on of the forward call and give
+// no formulas for it; the chunk equations below are the chain rule applied to
+// the forward's chunk equations (with gamma the in-chunk cumulative
+// log-decay, e = exp(gamma), l = exp(gamma_L - gamma), D[r][s] =
+// exp(gamma_r - gamma_s) for s <= r, M0 the state entering the chunk, dML the
+// gradient of the state leaving it and dO = scale * do):
+//
+//   forward   A = beta_r D (K K^T) strictly below the diagonal, T = (I + A)^-1
+//             X = K M0, rhs = diag(beta) (V - diag(e) X), Delta = T rhs
+//             P = D * (Q K^T) on and below the diagonal
+//             O = diag(e) Q M0 + P Delta,  M_L = exp(gamma_L) M0 + K^T diag(l) Delta
+//   reverse   dDelta = diag(l) K dML + P^T dO,  drhs = T^T dDelta
+//             dM0 = exp(gamma_L) dML + Q^T diag(e) dO - K^T diag(beta e) drhs
+//             dV = diag(beta) drhs,  dA = -drhs Delta^T (strictly lower)
+//             dQ = diag(e) dO M0^T + (dP * D) K,          dP = dO Delta^T
+//             dK = -diag(beta e) drhs M0^T + diag(l) Delta dML^T + (dP * D)^T Q
+//                  + (S + S^T) K,  S = diag(beta) (dA * D)
+//             dbeta, and dgamma from e, l, exp(gamma_L) and D, then
+//             dg = the reverse cumulative sum of dgamma over the chunk.
+//
+// Four kernels:
+//   bwd_prep     per (chunk, value head), all in parallel: gamma, K K^T and
+//                Q K^T (MFMA), A, T = (I + A)^-1 (the four 16 x 16 diagonal
+//                inverses by fp32 forward substitution with row broadcasts,
+//                the blocks below them by block recursion in fp32), and P.
+//                Writes T (fp32), P (bf16) and gamma to the workspace.
+//   bwd_fstate   per (sequence, value head, 64 value columns), chunks in
+//                order: the forward state recurrence with the dense T, writing
+//                each chunk's entering state M0 to the workspace.
+//   bwd_dstate   per (sequence, value head, 64 value columns), chunks in
+//                reverse: the state-gradient recurrence, writing each chunk's
+//                dML to the workspace; dh0 is the gradient after chunk 0.
+//   bwd_chunk    per (chunk, q/k head), all in parallel: the token gradients
+//                of the chunk from M0 and dML, summed over the value heads
+//                that share the q/k head (dq, dk) and over value columns.
+//
+// Precision: products accumulate in fp32 on bf16 MFMA.  The two state
+// recurrences carry fp32 states and use hi + lo bf16 pairs for computed
+// operands (T, the right-hand sides, Delta', dDelta, dX, e dO); the state
+// itself enters products as its hi part, as in the forward.  In bwd_chunk the
+// states, Delta and the other computed operands enter as single bf16
+// roundings except T, rhs and dDelta (hi + lo).
+//
+// MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16)+j] and
+// B[8(l/16)+j][l%16] (j = 0..7), receives C[4(l/16)+r][l%16] (r = 0..3).
+// ds_read_b64_tr_b16: within 16 lanes, lane 16g+i receives element i%4 of the
+// 8-byte words addressed by lanes 16g + 4j + i/4, j = 0..3.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+constexpr int kC = 64;     // chunk length
+constexpr int kDK = 128;   // key dimension
+constexpr int kVT = 64;    // value columns per state workgroup
+constexpr int kLK = 136;   // row stride (bf16) of K and Q tiles
+constexpr int kL64 = 72;   // row stride (bf16) of 64-wide tiles
+constexpr int kL32 = 40;   // row stride (bf16) of 32-wide tiles
+constexpr int kLF = 65;    // row stride (fp32) of 64-wide fp32 tiles
+constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ float bf2f(uint16_t x) {
+    return __uint_as_float(static_cast<unsigned>(x) << 16);
+}
+
+__device__ __forceinline__ bf16x8 cat(u32x2 a, u32x2 b) {
+    const u32x4 v = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t *p) {
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ u32x2 pack4(f32x4 x) {
+    return u32x2{f2bf(x[0]) | (unsigned)f2bf(x[1]) << 16, f2bf(x[2]) | (unsigned)f2bf(x[3]) << 16};
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32).
+__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
+    f32x4 r;
+    uint16_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = f2bf(x[i]);
+        r[i] = x[i] - bf2f(h[i]);
+    }
+    hi = u32x2{h[0] | (unsigned)h[1] << 16, h[2] | (unsigned)h[3] << 16};
+    lo = pack4(r);
+}
+
+// Fragments from bf16 tiles in LDS (row stride ld elements).
+// A operand rows [row0 + lr][k0 + 8 lg .. + 7] of a row-major tile; also the
+// B operand of X^T for a row-major X[n][k].
+__device__ __forceinline__ bf16x8 frag_rows(const uint16_t *t, int ld, int row0, int k0, int lr,
+                                            int lg) {
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4 *>(t + (row0 + lr) * ld + k0 + 8 * lg));
+}
+
+// The same rows in the permuted k order of a B operand assembled from two
+// C-layout tiles: positions 8g..8g+3 hold k0 + 4g .., 8g+4..8g+7 hold
+// k0 + 16 + 4g ...
+__device__ __forceinline__ bf16x8 frag_rows_perm(const uint16_t *t, int ld, int row0, int k0,
+                                                 int lr, int lg) {
+    const uint16_t *p = t + (row0 + lr) * ld + k0 + 4 * lg;
+    return cat(ld8(p), ld8(p + 16));
+}
+
+// From a row-major X[k][col]: lane (lr, lg) receives X[k0 + 8 lg + j][col0 + lr],
+// j = 0..7: the B operand of X, or the A operand of X^T.
+__device__ __forceinline__ bf16x8 frag_cols(const uint16_t *t, int ld, int k0, int col0, int lr,
+                                            int lg) {
+    const uint16_t *p = t + (k0 + 8 * lg + (lr >> 2)) * ld + col0 + 4 * (lr & 3);
+    return cat(ld_tr(p), ld_tr(p + 4 * ld));
+}
+
+// The same in the permuted k order (rows k0 + 4g + j and k0 + 16 + 4g + j).
+__device__ __forceinline__ bf16x8 frag_cols_perm(const uint16_t *t, int ld, int k0, int col0,
+                                                 int lr, int lg) {
+    const uint16_t *p = t + (k0 + 4 * lg + (lr >> 2)) * ld + col0 + 4 * (lr & 3);
+    return cat(ld_tr(p), ld_tr(p + 16 * ld));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, RowMask, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp<0x111, 0xF>(x);
+    x += dpp<0x112, 0xF>(x);
+    x += dpp<0x114, 0xF>(x);
+    x += dpp<0x118, 0xF>(x);
+    x += dpp<0x142, 0xA>(x);
+    x += dpp<0x143, 0xC>(x);
+    return x;
+}
+
+// Sum over the 16 lanes of this lane's row.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __shfl_xor(x, 1, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 8, 16);
+    return x;
+}
+
+// x += (a from lane R of this lane's 16-lane row) * b.
+template <int R>
+__device__ __forceinline__ void fmac_rowbcast(float &x, float a, float b) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x) : "v"(a), "v"(b), "i"(R));
+}
+
+template <int R>
+__device__ __forceinline__ void dinv_step(float (&x)[16], const float (&na)[16]) {
+#pragma unroll
+    for (int r2 = R + 1; r2 < 16; ++r2)
+        fmac_rowbcast<R>(x[r2], na[r2], x[R]);
+}
+
+template <int... R>
+__device__ __forceinline__ void dinv_steps(float (&x)[16], const float (&na)[16],
+                                           std::integer_sequence<int, R...>) {
+    (dinv_step<R>(x, na), ...);
+}
+
+// Where chunk gc of the whole call lies.
+struct ChunkLoc {
+    int n;          // sequence
+    int c;          // chunk within the sequence
+    int64_t p;      // first token
+    int L;          // valid tokens
+};
+
+__device__ __forceinline__ int64_t seq_start(const BwdArgs &a, int n) {
+    return a.cu ? (int64_t)a.cu[n] : (int64_t)n * a.T;
+}
+
+__device__ __forceinline__ int64_t seq_len(const BwdArgs &a, int n) {
+    return a.cu ? (int64_t)a.cu[n + 1] - a.cu[n] : a.T;
+}
+
+// First chunk index of sequence n.
+__device__ __forceinline__ int64_t chunk_base(const BwdArgs &a, int n) {
+    if (!a.cu)
+        return (int64_t)n * ((a.T + kC - 1) / kC);
+    int64_t b = 0;
+    for (int m = 0; m < n; ++m)
+        b += (seq_len(a, m) + kC - 1) / kC;
+    return b;
+}
+
+__device__ __forceinline__ bool locate(const BwdArgs &a, int64_t gc, ChunkLoc &cl) {
+    if (!a.cu) {
+        const int64_t nch = (a.T + kC - 1) / kC;
+        const int64_t n = gc / nch;
+        if (n >= a.n_seqs)
+            return false;
+        cl.n = (int)n;
+        cl.c = (int)(gc % nch);
+    } else {
+        int64_t b = 0;
+        int n = 0;
+        for (; n < a.n_seqs; ++n) {
+            const int64_t nc = (seq_len(a, n) + kC - 1) / kC;
+            if (gc < b + nc)
+                break;
+            b += nc;
+        }
+        if (n >= a.n_seqs)
+            return false;
+        cl.n = n;
+        cl.c = (int)(gc - b);
+    }
+    cl.p = seq_start(a, cl.n) + (int64_t)kC * cl.c;
+    cl.L = (int)min<int64_t>(kC, seq_len(a, cl.n) - (int64_t)kC * cl.c);
+    return true;
+}
+
+// Rows [p, p + L) of a [*, H, width] bf16 tensor at head h into an LDS tile
+// [64][ld]; rows past L read as zeros.  256 threads, 16-byte pieces.
+template <int Width>
+__device__ __forceinline__ void stage_rows_bf16(uint16_t *dst, int ld, const void *src, int64_t p,
+                                                int L, int H, int h, int col0, int rowlen,
+                                                int tid) {
+    const uint32_t row_bytes = (uint32_t)H * rowlen * 2;
+    const uint16_t *base = static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)rowlen + col0;
+    const __amdgpu_buffer_rsrc_t r = rsrc(base, (uint32_t)(L - 1) * row_bytes + Width * 2);
+    constexpr int kPieces = Width / 8;  // 16-byte pieces per row
+#pragma unroll
+    for (int i = tid; i < kC * kPieces; i += 256) {
+        const int row = i / kPieces, pc = i % kPieces;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, row * row_bytes + 16 * pc, 0, 0);
+        *reinterpret_cast<u32x4 *>(dst + row * ld + 8 * pc) = v;
+    }
+}
+
+// T (fp32, workspace) into hi and lo bf16 tiles [64][kL64].
+__device__ __forceinline__ void stage_T(uint16_t *Th, uint16_t *Tl, const float *Tg, int tid) {
+    for (int i = tid; i < kC * kC / 4; i += 256) {
+        const int row = i / 16, c4 = i % 16;
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(Tg + row * kC + 4 * c4);
+        u32x2 h, l;
+        split4(x, h, l);
+        *reinterpret_cast<u32x2 *>(Th + row * kL64 + 4 * c4) = h;
+        *reinterpret_cast<u32x2 *>(Tl + row * kL64 + 4 * c4) = l;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep: per (chunk, value head).
+
+__global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
+    __shared__ uint16_t Ks[kC * kLK];
+    __shared__ uint16_t Qs[kC * kLK];
+    __shared__ float Af[kC * kLF];
+    __shared__ float Tf[kC * kLF];
+    __shared__ float Wf[32 * 33];
+    __shared__ uint16_t Ps[kC * kL64];
+    __shared__ float gam[kC], bt[kC];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int64_t gc = blockIdx.x;
+    const int j = blockIdx.y;
+    ChunkLoc cl;
+    if (!locate(a, gc, cl))
+        return;
+    const int hk = j / (a.Hv / a.Hqk);
+    stage_rows_bf16<kDK>(Ks, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+    stage_rows_bf16<kDK>(Qs, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+    if (w == 0) {
+        const float gv = lane < cl.L ? a.g[(cl.p + lane) * a.Hv + j] : 0.0f;
+        const float bv = lane < cl.L ? a.beta[(cl.p + lane) * a.Hv + j] : 0.0f;
+        gam[lane] = wave_prefix_sum(gv);  // padded rows keep gamma_{L-1}
+        bt[lane] = bv;
+    }
+    for (int i = tid; i < kC * kLF; i += 256)
+        Tf[i] = 0.0f;
+    __syncthreads();
+
+    // K K^T and Q K^T, rows 16w .. 16w + 15.
+    f32x4 kk[4], qk[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        kk[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qk[ni] = kk[ni];
+#pragma unroll
+        for (int kx = 0; kx < 4; ++kx) {
+            const bf16x8 b = frag_rows(Ks, kLK, 16 * ni, 32 * kx, lr, lg);
+            kk[ni] = mma(frag_rows(Ks, kLK, 16 * w, 32 * kx, lr, lg), b, kk[ni]);
+            qk[ni] = mma(frag_rows(Qs, kLK, 16 * w, 32 * kx, lr, lg), b, qk[ni]);
+        }
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 16 * w + 4 * lg + rr, s = 16 * ni + lr;
+            const float d = s <= r ? __expf(gam[r] - gam[s]) : 0.0f;
+            Af[r * kLF + s] = s < r ? bt[r] * d * kk[ni][rr] : 0.0f;
+            Ps[r * kL64 + s] = f2bf(s <= r ? d * qk[ni][rr] : 0.0f);
+        }
+    __syncthreads();
+
+    // Diagonal blocks of T: D_i = (I + A_ii)^-1, lane row g = block g, lane c
+    // = column c; once x_r is final, A[r2][r] x_r leaves every later row.
+    if (w == 0) {
+        const int c = lr, gb = lg;
+        float na[16], x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            na[r] = -Af[(16 * gb + r) * kLF + 16 * gb + c];
+            x[r] = r == c ? 1.0f : 0.0f;
+        }
+        dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            Tf[(16 * gb + r) * kLF + 16 * gb + c] = x[r];
+    }
+    __syncthreads();
+    // T_10 = -D_1 A_10 D_0 and T_32 = -D_3 A_32 D_2.
+    for (int i = tid; i < 512; i += 256) {
+        const int b = i >> 8, r = (i >> 4) & 15, s = i & 15;
+        const float *Ar = Af + (16 + 32 * b + r) * kLF + 32 * b;
+        const float *Dc = Tf + (32 * b) * kLF + 32 * b + s;
+        float acc = 0.0f;
+        for (int k = 0; k < 16; ++k)
+            acc += Ar[k] * Dc[k * kLF];
+        Wf[(16 * b + r) * 33 + s] = acc;
+    }
+    __syncthreads();
+    for (int i = tid; i < 512; i += 256) {
+        const int b = i >> 8, r = (i >> 4) & 15, s = i & 15;
+        const float *Dr = Tf + (16 + 32 * b + r) * kLF + 16 + 32 * b;
+        float acc = 0.0f;
+        for (int k = 0; k < 16; ++k)
+            acc += Dr[k] * Wf[(16 * b + k) * 33 + s];
+        Tf[(16 + 32 * b + r) * kLF + 32 * b + s] = -acc;
+    }
+    __syncthreads();
+    // T[32:64][0:32] = -T2 A[32:64][0:32] T1.
+    for (int i = tid; i < 1024; i += 256) {
+        const int r = i >> 5, s = i & 31;
+        const float *Ar = Af + (32 + r) * kLF;
+        float acc = 0.0f;
+        for (int k = 0; k < 32; ++k)
+            acc += Ar[k] * Tf[k * kLF + s];
+        Wf[r * 33 + s] = acc;
+    }
+    __syncthreads();
+    for (int i = tid; i < 1024; i += 256) {
+        const int r = i >> 5, s = i & 31;
+        const float *Tr = Tf + (32 + r) * kLF + 32;
+        float acc = 0.0f;
+        for (int k = 0; k < 32; ++k)
+            acc += Tr[k] * Wf[k * 33 + s];
+        Tf[(32 + r) * kLF + s] = -acc;
+    }
+    __syncthreads();
+
+    const int64_t wi = gc * a.Hv + j;
+    float *To = a.ws_T + wi * (kC * kC);
+    uint16_t *Po = a.ws_P + wi * (kC * kC);
+    for (int i = tid; i < kC * kC; i += 256) {
+        To[i] = Tf[(i >> 6) * kLF + (i & 63)];
+        Po[i] = Ps[(i >> 6) * kL64 + (i & 63)];
+    }
+    if (tid < kC)
+        a.ws_gam[wi * kC + tid] = gam[tid];
+}
+
+// ---------------------------------------------------------------------------
+// The two state recurrences: one workgroup per (sequence, value head, 64
+// value columns), wave w owning columns [16w, 16w + 16).  A state slice
+// [128 x 16] lives in eight C-layout tiles: tile mt holds rows 16mt ...
+// 16mt + 15, lane (lr, lg) rows 16mt + 4lg + r of column lr.
+
+struct StateSmem {
+    uint16_t K[kC * kLK];
+    uint16_t Q[kC * kLK];
+    uint16_t X[kC * kL64];      // V (forward) or dO (reverse) tile
+    uint16_t Th[kC * kL64];
+    uint16_t Tl[kC * kL64];
+    uint16_t P[kC * kL64];
+    float e[kC], l[kC], bt[kC];
+    float eL;
+};
+
+__device__ __forceinline__ void stage_tables(StateSmem &S, const BwdArgs &a, int64_t wi, int j,
+                                             const ChunkLoc &cl, int tid) {
+    if (tid < kC) {
+        const float gm = a.ws_gam[wi * kC + tid];
+        const float gL = a.ws_gam[wi * kC + kC - 1];
+        S.e[tid] = __expf(gm);
+        S.l[tid] = __expf(gL - gm);
+        S.bt[tid] = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+        if (tid == 0)
+            S.eL = __expf(gL);
+    }
+}
+
+// The state's hi part as the B operands of a contraction over dk (permuted k).
+__device__ __forceinline__ void state_hi(const f32x4 (&h)[8], bf16x8 (&hb)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+}
+
+// Y = K S (S given by its hi part), rows 16mi .. of the chunk.
+__device__ __forceinline__ void k_times_state(const uint16_t *Ks, const bf16x8 (&hb)[4],
+                                              f32x4 (&Y)[4], int lr, int lg) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        Y[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            Y[mi] = mma(frag_rows_perm(Ks, kLK, 16 * mi, 32 * kk, lr, lg), hb[kk], Y[mi]);
+    }
+}
+
+// h += X^T Z over the chunk's tokens, X = K or Q (row-major tile), Z given
+// as hi and lo B operands (permuted token order).
+__device__ __forceinline__ void add_xt_times(const uint16_t *Xs, const bf16x8 (&zh)[2],
+                                             const bf16x8 (&zl)[2], f32x4 (&h)[8], int lr,
+                                             int lg) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 f = frag_cols_perm(Xs, kLK, 32 * kk, 16 * mt, lr, lg);
+            h[mt] = mma(f, zh[kk], h[mt]);
+            h[mt] = mma(f, zl[kk], h[mt]);
+        }
+}
+
+// Z (four C-layout tiles over the chunk's rows) as hi and lo B operands.
+__device__ __forceinline__ void tiles_split(const f32x4 (&Z)[4], bf16x8 (&zh)[2], bf16x8 (&zl)[2]) {
+    u32x2 h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        split4(Z[i], h[i], l[i]);
+    zh[0] = cat(h[0], h[1]);
+    zh[1] = cat(h[2], h[3]);
+    zl[0] = cat(l[0], l[1]);
+    zl[1] = cat(l[2], l[3]);
+}
+
+// Y = T Z (Trans = false) or T^T Z (Trans = true), T lower triangular given
+// as hi and lo tiles, Z as hi and lo B operands; products hi*hi + hi*lo + lo*hi.
+template <bool Trans>
+__device__ __forceinline__ void t_times(const uint16_t *Th, const uint16_t *Tl,
+                                        const bf16x8 (&zh)[2], const bf16x8 (&zl)[2],
+                                        f32x4 (&Y)[4], int lr, int lg) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        Y[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // T: rows 16mi.. need columns <= their rows; T^T the reverse.
+            if (!Trans && 32 * kk > 16 * mi + 15)
+                continue;
+            if (Trans && 32 * kk + 31 < 16 * mi)
+                continue;
+            const bf16x8 fh = Trans ? frag_cols_perm(Th, kL64, 32 * kk, 16 * mi, lr, lg)
+                                    : frag_rows_perm(Th, kL64, 16 * mi, 32 * kk, lr, lg);
+            const bf16x8 fl = Trans ? frag_cols_perm(Tl, kL64, 32 * kk, 16 * mi, lr, lg)
+                                    : frag_rows_perm(Tl, kL64, 16 * mi, 32 * kk, lr, lg);
+            Y[mi] = mma(fh, zh[kk], Y[mi]);
+            Y[mi] = mma(fh, zl[kk], Y[mi]);
+            Y[mi] = mma(fl, zh[kk], Y[mi]);
+        }
+    }
+}
+
+__device__ __forceinline__ void stage_T_and(StateSmem &S, const BwdArgs &a, int64_t wi, int tid) {
+    stage_T(S.Th, S.Tl, a.ws_T + wi * (kC * kC), tid);
+}
+
+__global__ __launch_bounds__(256) void bwd_fstate(BwdArgs a) {
+    __shared__ StateSmem S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int n_tiles = a.dv / kVT;
+    const int tile = blockIdx.x % n_tiles;
+    const int j = (blockIdx.x / n_tiles) % a.Hv;
+    const int n = blockIdx.x / (n_tiles * a.Hv);
+    const int hk = j / (a.Hv / a.Hqk);
+    const int col = tile * kVT + 16 * w + lr;   // this lane's value column
+    const int64_t len = seq_len(a, n);
+    const int nch = (int)((len + kC - 1) / kC);
+    const int64_t base = chunk_base(a, n);
+    const int64_t S_elems = (int64_t)kDK * a.dv;
+
+    f32x4 h[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            h[mt][r] = a.h0 ? a.h0[((int64_t)n * a.Hv + j) * S_elems +
+                                   (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
+                            : 0.0f;
+    for (int c = 0; c < nch; ++c) {
+        ChunkLoc cl;
+        cl.n = n;
+        cl.c = c;
+        cl.p = seq_start(a, n) + (int64_t)kC * c;
+        cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
+        const int64_t wi = (base + c) * a.Hv + j;
+        // The state entering chunk c.
+        float *hs = a.ws_hs + wi * S_elems;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                hs[(int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = h[mt][r];
+        stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+        stage_rows_bf16<kVT>(S.X, kL64, a.v, cl.p, cl.L, a.Hv, j, tile * kVT, a.dv, tid);
+        stage_T_and(S, a, wi, tid);
+        stage_tables(S, a, wi, j, cl, tid);
+        __syncthreads();
+
+        bf16x8 hb[4];
+        state_hi(h, hb);
+        f32x4 X[4];
+        k_times_state(S.K, hb, X, lr, lg);
+        f32x4 R[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mi + 4 * lg + r;
+                R[mi][r] = S.bt[row] * (bf2f(S.X[row * kL64 + 16 * w + lr]) - S.e[row] * X[mi][r]);
+            }
+        bf16x8 rh[2], rl[2];
+        tiles_split(R, rh, rl);
+        f32x4 Dl[4];
+        t_times<false>(S.Th, S.Tl, rh, rl, Dl, lr, lg);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Dl[mi][r] *= S.l[16 * mi + 4 * lg + r];
+        bf16x8 dh[2], dl[2];
+        tiles_split(Dl, dh, dl);
+        const float eL = S.eL;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            h[mt] *= eL;
+        add_xt_times(S.K, dh, dl, h, lr, lg);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
+    __shared__ StateSmem S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int n_tiles = a.dv / kVT;
+    const int tile = blockIdx.x % n_tiles;
+    const int j = (blockIdx.x / n_tiles) % a.Hv;
+    const int n = blockIdx.x / (n_tiles * a.Hv);
+    const int hk = j / (a.Hv / a.Hqk);
+    const int col = tile * kVT + 16 * w + lr;
+    const int64_t len = seq_len(a, n);
+    const int nch = (int)((len + kC - 1) / kC);
+    const int64_t base = chunk_base(a, n);
+    const int64_t S_elems = (int64_t)kDK * a.dv;
+    const float scale = a.scale;
+
+    f32x4 dM[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dM[mt][r] = a.dht ? a.dht[((int64_t)n * a.Hv + j) * S_elems +
+                                      (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
+                              : 0.0f;
+    for (int c = nch - 1; c >= 0; --c) {
+        ChunkLoc cl;
+        cl.n = n;
+        cl.c = c;
+        cl.p = seq_start(a, n) + (int64_t)kC * c;
+        cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
+        const int64_t wi = (base + c) * a.Hv + j;
+        // The state gradient leaving chunk c.
+        float *dhs = a.ws_dhs + wi * S_elems;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dhs[(int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = dM[mt][r];
+        stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+        stage_rows_bf16<kDK>(S.Q, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+        stage_rows_bf16<kVT>(S.X, kL64, a.dout, cl.p, cl.L, a.Hv, j, tile * kVT, a.dv, tid);
+        stage_T_and(S, a, wi, tid);
+        for (int i = tid; i < kC * kC / 8; i += 256)
+            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) =
+                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * i);
+        stage_tables(S, a, wi, j, cl, tid);
+        __syncthreads();
+
+        bf16x8 hb[4];
+        state_hi(dM, hb);
+        f32x4 U[4];
+        k_times_state(S.K, hb, U, lr, lg);
+        // dDelta = diag(l) K dML + P^T dO (dO = scale * do).
+        f32x4 dD[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            f32x4 v1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (32 * kk + 31 < 16 * mi)
+                    continue;
+                v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * mi, lr, lg),
+                         frag_cols(S.X, kL64, 32 * kk, 16 * w, lr, lg), v1);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dD[mi][r] = S.l[16 * mi + 4 * lg + r] * U[mi][r] + scale * v1[r];
+        }
+        bf16x8 zh[2], zl[2];
+        tiles_split(dD, zh, zl);
+        f32x4 dR[4];
+        t_times<true>(S.Th, S.Tl, zh, zl, dR, lr, lg);
+        // dX = -diag(beta e) drhs and diag(e) dO, as hi and lo B operands.
+        f32x4 dX[4], eO[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mi + 4 * lg + r;
+                dX[mi][r] = -S.bt[row] * S.e[row] * dR[mi][r];
+                eO[mi][r] = scale * S.e[row] * bf2f(S.X[row * kL64 + 16 * w + lr]);
+            }
+        bf16x8 xh[2], xl[2], oh[2], ol[2];
+        tiles_split(dX, xh, xl);
+        tiles_split(eO, oh, ol);
+        const float eL = S.eL;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            dM[mt] *= eL;
+        add_xt_times(S.K, xh, xl, dM, lr, lg);
+        add_xt_times(S.Q, oh, ol, dM, lr, lg);
+        __syncthreads();
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                a.dh0[((int64_t)n * a.Hv + j) * S_elems + (int64_t)(16 * mt + 4 * lg + r) * a.dv +
+                      col] = dM[mt][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_chunk: per (chunk, q/k head).  Wave w owns the chunk's rows
+// [16w, 16w + 16) of every [64 x *] result; value columns are taken 32 at a
+// time.
+
+struct ChunkSmem {
+    uint16_t K[kC * kLK];
+    uint16_t Q[kC * kLK];
+    uint16_t Th[kC * kL64];     // after the column tiles: dQK
+    uint16_t Tl[kC * kL64];     // after the column tiles: S + S^T
+    uint16_t P[kC * kL64];
+    union {
+        struct {
+            uint16_t M0[kDK * kL32];   // [dk][col]
+            uint16_t dM[kDK * kL32];
+            uint16_t V[kC * kL32];
+            uint16_t dO[kC * kL32];    // do (unscaled)
+            uint16_t rh[kC * kL32];
+            uint16_t rl[kC * kL32];
+            uint16_t Dh[kC * kL32];    // Delta
+            uint16_t zh[kC * kL32];    // dDelta hi
+            uint16_t zl[kC * kL32];    // dDelta lo
+            uint16_t dR[kC * kL32];    // drhs
+            uint16_t dY[kC * kL32];    // diag(e) dO
+            uint16_t dX[kC * kL32];    // -diag(beta e) drhs
+            uint16_t W[kC * kL32];     // diag(l) Delta
+        } t;
+        float S[kC * kLF];             // S = diag(beta) (dA * D), fp32
+    } u;
+    float gam[kC], e[kC], l[kC], bt[kC];
+    float colpart[4][kC];
+    float dgam[kC];
+    float red[256];
+};
+
+__global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
+    __shared__ ChunkSmem S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int64_t gc = blockIdx.x;
+    const int hk = blockIdx.y;
+    ChunkLoc cl;
+    if (!locate(a, gc, cl))
+        return;
+    const int G = a.Hv / a.Hqk;
+    const float scale = a.scale;
+    const int64_t S_elems = (int64_t)kDK * a.dv;
+    stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+    stage_rows_bf16<kDK>(S.Q, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+
+    f32x4 dQ[8], dK[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        dQ[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dK[i] = dQ[i];
+    }
+
+    for (int gi = 0; gi < G; ++gi) {
+        const int j = hk * G + gi;
+        const int64_t wi = gc * a.Hv + j;
+        __syncthreads();  // the previous head's readers are done
+        stage_T(S.Th, S.Tl, a.ws_T + wi * (kC * kC), tid);
+        for (int i = tid; i < kC * kC / 8; i += 256)
+            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) =
+                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * i);
+        if (tid < kC) {
+            const float gm = a.ws_gam[wi * kC + tid];
+            const float gL = a.ws_gam[wi * kC + kC - 1];
+            S.gam[tid] = gm;
+            S.e[tid] = __expf(gm);
+            S.l[tid] = __expf(gL - gm);
+            S.bt[tid] = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+        }
+        const float eL = __expf(a.ws_gam[wi * kC + kC - 1]);
+
+        f32x4 dP[4], dA[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dA[i] = dP[i];
+        }
+        float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta parts of rows 16w + 4lg + r
+        float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma parts
+        float dgL = 0.0f;                     // this thread's part of d gamma_L
+
+        for (int t0 = 0; t0 < a.dv; t0 += 32) {
+            __syncthreads();
+            // M0 and dML columns [t0, t0 + 32) as bf16 [dk][col].
+            const float *Mg = a.ws_hs + wi * S_elems + t0;
+            const float *dMg = a.ws_dhs + wi * S_elems + t0;
+            for (int i = tid; i < kDK * 8; i += 256) {
+                const int row = i >> 3, c4 = i & 7;
+                const f32x4 m = *reinterpret_cast<const f32x4 *>(Mg + (int64_t)row * a.dv + 4 * c4);
+                const f32x4 d = *reinterpret_cast<const f32x4 *>(dMg + (int64_t)row * a.dv + 4 * c4);
+                *reinterpret_cast<u32x2 *>(S.u.t.M0 + row * kL32 + 4 * c4) = pack4(m);
+                *reinterpret_cast<u32x2 *>(S.u.t.dM + row * kL32 + 4 * c4) = pack4(d);
+                dgL += eL * (m[0] * d[0] + m[1] * d[1] + m[2] * d[2] + m[3] * d[3]);
+            }
+            stage_rows_bf16<32>(S.u.t.V, kL32, a.v, cl.p, cl.L, a.Hv, j, t0, a.dv, tid);
+            stage_rows_bf16<32>(S.u.t.dO, kL32, a.dout, cl.p, cl.L, a.Hv, j, t0, a.dv, tid);
+            __syncthreads();
+
+            // X = K M0, Y = Q M0, U = K dML (rows 16w.., columns 16ni..).
+            f32x4 X[2], Y[2], U[2];
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                X[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Y[ni] = X[ni];
+                U[ni] = X[ni];
+#pragma unroll
+                for (int kx = 0; kx < 4; ++kx) {
+                    const bf16x8 fk = frag_rows(S.K, kLK, 16 * w, 32 * kx, lr, lg);
+                    const bf16x8 fq = frag_rows(S.Q, kLK, 16 * w, 32 * kx, lr, lg);
+                    const bf16x8 bm = frag_cols(S.u.t.M0, kL32, 32 * kx, 16 * ni, lr, lg);
+                    const bf16x8 bd = frag_cols(S.u.t.dM, kL32, 32 * kx, 16 * ni, lr, lg);
+                    X[ni] = mma(fk, bm, X[ni]);
+                    Y[ni] = mma(fq, bm, Y[ni]);
+                    U[ni] = mma(fk, bd, U[ni]);
+                }
+            }
+            // rhs = diag(beta) (V - diag(e) X), hi and lo.
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
+                    const float rhs =
+                        S.bt[row] * (bf2f(S.u.t.V[row * kL32 + cc]) - S.e[row] * X[ni][r]);
+                    const uint16_t hb = f2bf(rhs);
+                    S.u.t.rh[row * kL32 + cc] = hb;
+                    S.u.t.rl[row * kL32 + cc] = f2bf(rhs - bf2f(hb));
+                }
+            __syncthreads();
+
+            // Delta = T rhs; dDelta = diag(l) U + P^T dO.
+            f32x4 Dl[2], dD[2];
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                Dl[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 v1 = Dl[ni];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (32 * kk <= 16 * w + 15) {
+                        const bf16x8 th = frag_rows(S.Th, kL64, 16 * w, 32 * kk, lr, lg);
+                        const bf16x8 tl = frag_rows(S.Tl, kL64, 16 * w, 32 * kk, lr, lg);
+                        const bf16x8 bh = frag_cols(S.u.t.rh, kL32, 32 * kk, 16 * ni, lr, lg);
+                        const bf16x8 bl = frag_cols(S.u.t.rl, kL32, 32 * kk, 16 * ni, lr, lg);
+                        Dl[ni] = mma(th, bh, Dl[ni]);
+                        Dl[ni] = mma(th, bl, Dl[ni]);
+                        Dl[ni] = mma(tl, bh, Dl[ni]);
+                    }
+                    if (32 * kk + 31 >= 16 * w)
+                        v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * w, lr, lg),
+                                 frag_cols(S.u.t.dO, kL32, 32 * kk, 16 * ni, lr, lg), v1);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
+                    dD[ni][r] = S.l[row] * U[ni][r] + scale * v1[r];
+                    S.u.t.Dh[row * kL32 + cc] = f2bf(Dl[ni][r]);
+                    const uint16_t hb = f2bf(dD[ni][r]);
+                    S.u.t.zh[row * kL32 + cc] = hb;
+                    S.u.t.zl[row * kL32 + cc] = f2bf(dD[ni][r] - bf2f(hb));
+                    // d l_r = sum_c Delta dW: l_r enters dgamma_r with -l_r, gamma_L with +l_r.
+                    const float dlr = S.l[row] * Dl[ni][r] * U[ni][r];
+                    rg[r] -= dlr;
+                    dgL += dlr;
+                }
+            }
+            __syncthreads();
+
+            // drhs = T^T dDelta.
+            f32x4 dR[2];
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                dR[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (32 * kk + 31 < 16 * w)
+                        continue;
+                    const bf16x8 th = frag_cols(S.Th, kL64, 32 * kk, 16 * w, lr, lg);
+                    const bf16x8 tl = frag_cols(S.Tl, kL64, 32 * kk, 16 * w, lr, lg);
+                    const bf16x8 bh = frag_cols(S.u.t.zh, kL32, 32 * kk, 16 * ni, lr, lg);
+                    const bf16x8 bl = frag_cols(S.u.t.zl, kL32, 32 * kk, 16 * ni, lr, lg);
+                    dR[ni] = mma(th, bh, dR[ni]);
+                    dR[ni] = mma(th, bl, dR[ni]);
+                    dR[ni] = mma(tl, bh, dR[ni]);
+                }
+            }
+            // dV, the dbeta and dgamma parts, and the operands of the
+            // products over columns.
+            uint16_t *dvo = static_cast<uint16_t *>(a.dv_);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
+                    const float b = S.bt[row], e = S.e[row];
+                    const float vv = bf2f(S.u.t.V[row * kL32 + cc]);
+                    const float dov = scale * bf2f(S.u.t.dO[row * kL32 + cc]);
+                    const float dr = dR[ni][r];
+                    if (row < cl.L)
+                        dvo[((cl.p + row) * a.Hv + j) * (int64_t)a.dv + t0 + cc] = f2bf(b * dr);
+                    rb[r] += dr * (vv - e * X[ni][r]);
+                    rg[r] += e * dov * Y[ni][r] - b * e * dr * X[ni][r];
+                    S.u.t.dR[row * kL32 + cc] = f2bf(dr);
+                    S.u.t.dY[row * kL32 + cc] = f2bf(e * dov);
+                    S.u.t.dX[row * kL32 + cc] = f2bf(-b * e * dr);
+                    S.u.t.W[row * kL32 + cc] = f2bf(S.l[row] * Dl[ni][r]);
+                }
+            __syncthreads();
+
+            // dQ += dY M0^T, dK += dX M0^T + W dML^T (rows 16w.., dk tiles).
+            const bf16x8 fy = frag_rows(S.u.t.dY, kL32, 16 * w, 0, lr, lg);
+            const bf16x8 fx = frag_rows(S.u.t.dX, kL32, 16 * w, 0, lr, lg);
+            const bf16x8 fw = frag_rows(S.u.t.W, kL32, 16 * w, 0, lr, lg);
+#pragma unroll
+            for (int nj = 0; nj < 8; ++nj) {
+                const bf16x8 bm = frag_rows(S.u.t.M0, kL32, 16 * nj, 0, lr, lg);
+                const bf16x8 bd = frag_rows(S.u.t.dM, kL32, 16 * nj, 0, lr, lg);
+                dQ[nj] = mma(fy, bm, dQ[nj]);
+                dK[nj] = mma(fx, bm, dK[nj]);
+                dK[nj] = mma(fw, bd, dK[nj]);
+            }
+            // dP += do Delta^T (scaled later), dA += drhs Delta^T (negated later).
+            const bf16x8 fo = frag_rows(S.u.t.dO, kL32, 16 * w, 0, lr, lg);
+            const bf16x8 fr = frag_rows(S.u.t.dR, kL32, 16 * w, 0, lr, lg);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const bf16x8 bdl = frag_rows(S.u.t.Dh, kL32, 16 * ni, 0, lr, lg);
+                dP[ni] = mma(fo, bdl, dP[ni]);
+                dA[ni] = mma(fr, bdl, dA[ni]);
+            }
+        }
+        __syncthreads();
+
+        // K K^T and Q K^T again, for the gradients through A and P.
+        f32x4 kk4[4], qk4[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            kk4[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+            qk4[ni] = kk4[ni];
+#pragma unroll
+            for (int kx = 0; kx < 4; ++kx) {
+                const bf16x8 b = frag_rows(S.K, kLK, 16 * ni, 32 * kx, lr, lg);
+                kk4[ni] = mma(frag_rows(S.K, kLK, 16 * w, 32 * kx, lr, lg), b, kk4[ni]);
+                qk4[ni] = mma(frag_rows(S.Q, kLK, 16 * w, 32 * kx, lr, lg), b, qk4[ni]);
+            }
+        }
+        float cp[4] = {0.f, 0.f, 0.f, 0.f};  // column parts of dgamma, columns 16ni + lr
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * w + 4 * lg + r, s = 16 * ni + lr;
+                const float d = s <= row ? __expf(S.gam[row] - S.gam[s]) : 0.0f;
+                const float dpv = scale * dP[ni][r];
+                const float dav = -dA[ni][r];
+                const bool incl = s <= row, strict = s < row;
+                S.Th[row * kL64 + s] = f2bf(incl ? dpv * d : 0.0f);
+                S.u.S[row * kLF + s] = strict ? S.bt[row] * dav * d : 0.0f;
+                if (strict)
+                    rb[r] += dav * d * kk4[ni][r];
+                const float dDv = (incl ? dpv * qk4[ni][r] : 0.0f) +
+                                  (strict ? S.bt[row] * dav * kk4[ni][r] : 0.0f);
+                const float dDD = incl ? dDv * d : 0.0f;
+                rg[r] += dDD;
+                cp[ni] -= dDD;
+            }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            float x = cp[ni];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            if (lg == 0)
+                S.colpart[w][16 * ni + lr] = x;
+        }
+        S.red[tid] = dgL;
+        __syncthreads();
+        // S + S^T; the row sums.
+        for (int i = tid; i < kC * kC; i += 256) {
+            const int r = i >> 6, s = i & 63;
+            S.Tl[r * kL64 + s] = f2bf(S.u.S[r * kLF + s] + S.u.S[s * kLF + r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float xb = row16_sum(rb[r]);
+            const float xg = row16_sum(rg[r]);
+            if (lr == 0) {
+                const int row = 16 * w + 4 * lg + r;
+                if (row < cl.L)
+                    a.dbeta[(cl.p + row) * a.Hv + j] = xb;
+                S.dgam[row] = xg;
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            // dgamma, plus d gamma_L on the last row; dg is its reverse
+            // cumulative sum (padded rows carry gamma_{L-1}).
+            float tot = 0.0f;
+            for (int i = 0; i < 4; ++i)
+                tot += S.red[64 * i + lane];
+            float gl = tot;
+            for (int o = 32; o >= 1; o >>= 1)
+                gl += __shfl_xor(gl, o);
+            float dgm = S.dgam[lane] + S.colpart[0][lane] + S.colpart[1][lane] +
+                        S.colpart[2][lane] + S.colpart[3][lane];
+            if (lane == kC - 1)
+                dgm += gl;
+            S.dgam[lane] = dgm;
+        }
+        __syncthreads();
+        if (tid < cl.L) {
+            float acc = 0.0f;
+            for (int r = kC - 1; r >= tid; --r)
+                acc += S.dgam[r];
+            a.dg[(cl.p + tid) * a.Hv + j] = acc;
+        }
+        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K.
+#pragma unroll
+        for (int nj = 0; nj < 8; ++nj)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 bk = frag_cols(S.K, kLK, 32 * kk, 16 * nj, lr, lg);
+                const bf16x8 bq = frag_cols(S.Q, kLK, 32 * kk, 16 * nj, lr, lg);
+                dQ[nj] = mma(frag_rows(S.Th, kL64, 16 * w, 32 * kk, lr, lg), bk, dQ[nj]);
+                dK[nj] = mma(frag_cols(S.Th, kL64, 32 * kk, 16 * w, lr, lg), bq, dK[nj]);
+                dK[nj] = mma(frag_rows(S.Tl, kL64, 16 * w, 32 * kk, lr, lg), bk, dK[nj]);
+            }
+    }
+
+    uint16_t *dqo = static_cast<uint16_t *>(a.dq);
+    uint16_t *dko = static_cast<uint16_t *>(a.dk_);
+#pragma unroll
+    for (int nj = 0; nj < 8; ++nj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * w + 4 * lg + r;
+            if (row < cl.L) {
+                const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)kDK + 16 * nj + lr;
+                dqo[o] = f2bf(dQ[nj][r]);
+                dko[o] = f2bf(dK[nj][r]);
+            }
+        }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t n_chunks, int32_t Hv, int32_t dk, int32_t dv) {
+    const size_t ch = (size_t)n_chunks * (size_t)Hv;
+    size_t b = 0;
+    b += ch * kC * kC * sizeof(float);           // T
+    b += ch * kC * kC * sizeof(uint16_t);        // P
+    b += ch * kC * sizeof(float);                // gamma
+    b += 2 * ch * (size_t)dk * dv * sizeof(float);  // chunk states and their gradients
+    return b;
+}
+
+void bwd_carve(BwdArgs &a, void *workspace) {
+    const size_t ch = (size_t)a.n_chunks * (size_t)a.Hv;
+    char *p = static_cast<char *>(workspace);
+    a.ws_T = reinterpret_cast<float *>(p);
+    p += ch * kC * kC * sizeof(float);
+    a.ws_P = reinterpret_cast<uint16_t *>(p);
+    p += ch * kC * kC * sizeof(uint16_t);
+    a.ws_gam = reinterpret_cast<float *>(p);
+    p += ch * kC * sizeof(float);
+    a.ws_hs = reinterpret_cast<float *>(p);
+    p += ch * (size_t)a.dk * a.dv * sizeof(float);
+    a.ws_dhs = reinterpret_cast<float *>(p);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
+    if (a.n_chunks <= 0)
+        return hipSuccess;
+    if (a.n_chunks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    const dim3 chunk_grid((unsigned)a.n_chunks, (unsigned)a.Hv);
+    hipLaunchKernelGGL(bwd_prep, chunk_grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t seq_blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kVT);
+    hipLaunchKernelGGL(bwd_fstate, dim3((unsigned)seq_blocks), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bwd_dstate, dim3((unsigned)seq_blocks), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bwd_chunk, dim3((unsigned)a.n_chunks, (unsigned)a.Hqk), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -15,7 +15,9 @@ beta = sigmoid(noise); the workloads here use /16 for g):
   * bf16 inputs are the fp32 values rounded to nearest-even;
   * h0, when asked for, ~ N(0, std) in fp32 (std = 0.02 for packed batches);
   * packed lengths are geometric on {1, 2, ...} with the given mean, drawn
-    until they cover the total, the last one clipped so the sum is exact.
+    until they cover the total, the last one clipped so the sum is exact;
+  * for the backward, the upstream gradients: do ~ N(0, 1) in the input
+    dtype and dht ~ N(0, 0.02) in fp32.
 
 Every tensor draws from its own PCG64 stream spawned from the config seed, so
 a tensor can be drawn in blocks of tokens (and the blocked draw equals the
@@ -24,7 +26,7 @@ whole draw; tested).  bf16 tensors are returned as uint16 bit patterns; use
 """
 import numpy as np
 
-_STREAMS = ("q", "k", "v", "g", "beta", "h0", "lengths")
+_STREAMS = ("q", "k", "v", "g", "beta", "h0", "lengths", "do", "dht")
 
 # Elements drawn per block (bounds peak host memory for very long inputs).
 _BLOCK_ELEMS = 1 << 24
@@ -119,6 +121,17 @@ def make(B, T, Hqk, Hv, dk, dv, dtype, seed, h0_std=None, cu_seqlens=None):
     }
 
 
+def make_upstream(d, seed, dht_std=0.02):
+    """Upstream gradients for the inputs `d` of `make`: do [B, T, Hv, dv] in
+    d's dtype (uint16 bf16 bits or fp32) and dht [N, Hv, dk, dv] fp32, drawn
+    from their own streams of `seed` (the seed `d` was made with)."""
+    rs = _streams(seed)
+    B, T, Hv, dv, dk, N = d["B"], d["T"], d["Hv"], d["dv"], d["dk"], d["N"]
+    do = _normal_rows(rs["do"], B * T * Hv, dv, out_dtype=d["dtype"]).reshape(B, T, Hv, dv)
+    dht = _normal_rows(rs["dht"], N * Hv * dk, dv, std=dht_std).reshape(N, Hv, dk, dv)
+    return do, dht
+
+
 # The workloads: a tiny fp32 case, the 8 x 2K headline, a packed batch with
 # grouped value heads, and one long row.  Seeds are 1000 + index.
 CONFIGS = {
@@ -129,6 +142,8 @@ CONFIGS = {
                             dtype="bf16", seed=1002, h0_std=0.02),
     "long_bf16": dict(B=1, T=1_064_960, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16",
                       seed=1003),
+    # the headline inputs with upstream gradients, for the backward
+    "fwd_bwd_bf16": dict(B=8, T=2048, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", seed=1004),
 }
 
 

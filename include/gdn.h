@@ -1,6 +1,6 @@
 /*
- * gdn.h -- C ABI of libgdn: the chunkwise Gated DeltaNet forward on AMD
- * Instinct MI355X (gfx950).
+ * gdn.h -- C ABI of libgdn: the chunkwise Gated DeltaNet forward and its
+ * backward on AMD Instinct MI355X (gfx950).
  *
  * The operation is the gated delta rule of Gated DeltaNet (the December 2024
  * paper by Yang, Kautz and Hatamizadeh that the Qwen FlashQLA article names
@@ -113,6 +113,57 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                          int32_t n_seqs, void *o, float *ht, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace gdn_chunk_bwd needs for these sizes (0 for sizes
+ * the backward would reject).  The workspace holds, per chunk of 64 tokens and
+ * value head, the chunk's inverse (I + A)^-1 (fp32), its gated Q K^T (bf16),
+ * its cumulative decay, and the fp32 state entering the chunk and the gradient
+ * of the state leaving it: about 2 * dk * dv * 4 + 24.8 KiB per chunk and head.
+ *
+ * n_seqs: the number of documents when cu_seqlens will be passed, else B.
+ * With cu_seqlens the size covers any split of the T tokens into n_seqs
+ * documents.
+ */
+size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
+                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs);
+
+/*
+ * The chunked backward: the gradients of L = sum(do * o) + sum(dht * ht) with
+ * respect to q, k, v, g, beta and h0, for the forward gdn_chunk_fwd computes
+ * with the same arguments (the follow-on call the problem statement names;
+ * the pages give no formulas for it, so it is the reverse mode of the forward
+ * recurrence, derived by the chain rule).
+ *
+ *   dtype, B, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, h0, cu_seqlens,
+ *   cu_seqlens_host, n_seqs
+ *                as for gdn_chunk_fwd.  Supported: bf16 with dk = 128 and dv in
+ *                {64, 128}; everything else returns GDN_ERR_UNSUPPORTED.
+ *   dout         [B, T, H_v, dv] upstream gradient of o, dtype `dtype`.
+ *   dht          [N, H_v, dk, dv] fp32 upstream gradient of the final state,
+ *                or NULL for none.
+ *   dq, dk_      [B, T, H_qk, dk] outputs, dtype `dtype`; for grouped value
+ *                heads the sum over the value heads sharing the q/k head.
+ *   dv_          [B, T, H_v, dv] output, dtype `dtype`.
+ *   dg, dbeta    [B, T, H_v] fp32 outputs.
+ *   dh0          [N, H_v, dk, dv] fp32 output (the gradient of the initial
+ *                state; equal to dht for an empty document), or NULL.
+ *   workspace    device scratch of at least gdn_chunk_bwd_workspace_size()
+ *                bytes, 256-byte aligned, owned by the caller; its contents
+ *                are undefined afterwards.
+ *   stream       HIP stream to enqueue on.
+ *
+ * Every pointer must be 16-byte aligned; outputs must not overlap inputs or
+ * the workspace.  Tokens outside every document (none when cu_seqlens is
+ * valid) are left untouched in the outputs.
+ */
+gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                         int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float scale, const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                         int32_t n_seqs, const void *dout, const float *dht, void *dq,
+                         void *dk_, void *dv_, float *dg, float *dbeta, float *dh0,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* A static, human-readable name for a status. */
 const char *gdn_status_string(gdn_status status);

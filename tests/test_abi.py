@@ -87,3 +87,43 @@ def test_binding_checks_tensors_on_host():
     x = torch.zeros(1, 4, 1, 128)
     with pytest.raises(gdn.GdnError):
         gdn.gdn_chunk_fwd(x, x, x, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))  # CPU tensors
+
+
+def test_bwd_workspace_size():
+    ws = gdn.gdn_chunk_bwd_workspace_size
+    # 8 rows of 32 chunks, 16 heads: per chunk-head 64*64*4 + 64*64*2 + 64*4 + 2*128*128*4
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 64 * 4 + 2 * 128 * 128 * 4
+    assert ws(1, 8, 2048, 16, 16, 128, 128, 8) == 8 * 32 * 16 * per
+    # one packed row of 5 documents: at most ceil(T / 64) + 5 chunks
+    assert ws(1, 1, 2048, 16, 16, 128, 128, 5) == (32 + 5) * 16 * per
+    assert ws(0, 8, 2048, 16, 16, 128, 128, 8) == 0   # fp32: no backward kernel
+    assert ws(1, 8, 2048, 16, 16, 64, 128, 8) == 0    # dk = 64: none either
+
+
+def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+             beta=FAKE, h0=None, cu=None, cu_host=None, n_seqs=0, do=FAKE, dht=None, dq=FAKE,
+             dk_=FAKE, dv_=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE, ws_bytes=1 << 40):
+    lib = gdn.load()
+    host = None
+    if cu_host is not None:
+        host = ctypes.cast((ctypes.c_int32 * len(cu_host))(*cu_host), ctypes.c_void_p)
+    return lib.gdn_chunk_bwd(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, h0, cu, host,
+                             n_seqs, do, dht, dq, dk_, dv_, dg, dbeta, dh0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dk_=None), INVALID), (dict(dv_=None), INVALID), (dict(dg=None), INVALID),
+    (dict(dbeta=None), INVALID), (dict(T=0), INVALID),
+    (dict(dtype=0), UNSUPPORTED), (dict(dk=64), UNSUPPORTED), (dict(dv=96), UNSUPPORTED),
+    (dict(Hqk=2, Hv=3), UNSUPPORTED),
+    (dict(do=FAKE + 8), MISALIGNED), (dict(dht=FAKE + 4), MISALIGNED),
+    (dict(dh0=FAKE + 2), MISALIGNED), (dict(dg=FAKE + 4), MISALIGNED),
+    (dict(ws=FAKE + 16), MISALIGNED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+    (dict(cu=FAKE, n_seqs=2, B=2), INVALID),
+    (dict(cu=FAKE, n_seqs=2, cu_host=[0, 10, 63]), INVALID),
+    (dict(cu_host=[0, 64]), INVALID),
+])
+def test_bwd_rejects_before_launch(kw, status):
+    assert bwd_call(**kw) == status

@@ -1,0 +1,98 @@
+"""Parity of the HIP backward (through the C ABI) with the fp64 reverse-mode
+oracle.
+
+Each case draws seeded inputs with the workloads' recipe plus upstream
+gradients do ~ N(0, 1) and dht ~ N(0, 0.02), runs gdn_chunk_bwd on the GPU and
+oracle.gdn_bwd on the host, and compares all six gradients element by element
+(relative L2 over each whole tensor).  Sizes span several chunks and ragged
+tails; the forward-and-backward workload runs at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+from gpu_util import rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+# bf16 inputs: every gradient within 1e-2 relative L2 of the fp64 oracle (the
+# bf16 rounding of dq, dk, dv alone is about 2e-3).
+TOL_BWD = 1e-2
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def run_bwd_gpu(d, do, dht, scale=1.0):
+    import gated_deltanet_chunked_chunk_amd as gdn
+    t = to_device(d)
+    do_t = torch.from_numpy(do.view(np.int16)).cuda().view(torch.bfloat16)
+    dht_t = None if dht is None else torch.from_numpy(dht).cuda()
+    out = gdn.gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], do_t, dht=dht_t,
+                            scale=scale, initial_state=t["h0"], cu_seqlens=t["cu"],
+                            cu_seqlens_host=t["cu_host"])
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy() for x in out]
+
+
+def run_bwd_oracle(d, do, dht, scale=1.0):
+    q, k, v = (gi.widen(d[x]) for x in ("q", "k", "v"))
+    return oracle.gdn_bwd(q, k, v, d["g"], d["beta"], gi.widen(do), scale=scale,
+                          h0=None if d["h0"] is None else d["h0"].astype(np.float64),
+                          dht=None if dht is None else dht.astype(np.float64),
+                          cu_seqlens=d["cu_seqlens"])
+
+
+def check_bwd(d, seed, scale=1.0, with_dht=True, label=""):
+    do, dht = gi.make_upstream(d, seed)
+    if not with_dht:
+        dht = None
+    print(f"[gpu bwd case] {label} B={d['B']} T={d['T']} Hqk={d['Hqk']} Hv={d['Hv']} "
+          f"dv={d['dv']} N={d['N']} h0={d['h0'] is not None} dht={with_dht}", flush=True)
+    got = run_bwd_gpu(d, do, dht, scale)
+    ref = run_bwd_oracle(d, do, dht, scale)
+    errs = {}
+    for name, x, y in zip(NAMES, got, ref):
+        assert np.all(np.isfinite(x)), f"{name} not finite"
+        errs[name] = rel_l2(x, y)
+    print("  rel-L2 " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= TOL_BWD, f"{name} rel-L2 {e:.3e} > {TOL_BWD}"
+    return errs
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_bwd_ragged(T):
+    d = gi.make(2, T, 2, 2, 128, 128, "bf16", 5000 + T, h0_std=0.1)
+    check_bwd(d, 5000 + T, scale=0.75, label=f"ragged T={T}")
+
+
+def test_bwd_grouped_dv64():
+    d = gi.make(1, 150, 1, 2, 128, 64, "bf16", 5100, h0_std=0.1)
+    check_bwd(d, 5100, label="grouped heads, dv=64")
+
+
+def test_bwd_packed_with_empty_document():
+    cu = gi.cu_from_lengths([70, 0, 129, 1])
+    d = gi.make(1, 200, 2, 4, 128, 128, "bf16", 5200, h0_std=0.05, cu_seqlens=cu)
+    check_bwd(d, 5200, label="packed")
+
+
+def test_bwd_no_state_gradient():
+    d = gi.make(1, 130, 2, 2, 128, 128, "bf16", 5300)
+    check_bwd(d, 5300, with_dht=False, label="no dht, no h0")
+
+
+def test_bwd_workload_full_size():
+    """The forward-and-backward workload: B=8, T=2048, H=16, dk=dv=128."""
+    d = gi.make_config("fwd_bwd_bf16")
+    check_bwd(d, gi.CONFIGS["fwd_bwd_bf16"]["seed"], label="fwd_bwd_bf16 full size")
+
+
+def test_bwd_deterministic():
+    d = gi.make(1, 190, 2, 2, 128, 128, "bf16", 5400, h0_std=0.1)
+    do, dht = gi.make_upstream(d, 5400)
+    a = run_bwd_gpu(d, do, dht)
+    b = run_bwd_gpu(d, do, dht)
+    for x, y, n in zip(a, b, NAMES):
+        assert np.array_equal(x, y), f"{n} differs between runs"
