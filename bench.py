@@ -54,6 +54,69 @@ def chunked_flops(B, T, Hv, dk, dv, C=64):
     return chunks * per
 
 
+def bwd_algorithmic_bytes(B, T, Hqk, Hv, dk, dv, in_bytes=2):
+    """Backward: q, k, v, do, g, beta and dht read once; dq, dk, dv, dg, dbeta
+    and dh0 written once (no initial state)."""
+    tokens = B * T
+    reads = tokens * (2 * Hqk * dk + 2 * Hv * dv) * in_bytes + 2 * tokens * Hv * 4
+    writes = tokens * (2 * Hqk * dk + Hv * dv) * in_bytes + 2 * tokens * Hv * 4
+    states = 2 * B * Hv * dk * dv * 4
+    return reads + writes + states
+
+
+def measure_bwd(gdn, gi, torch, dev, steps, warmup):
+    """The backward on its workload (the headline shapes with upstream
+    gradients do and dht): milliseconds per call over `steps` back-to-back
+    calls, its HBM roofline fraction, and the oracle on one sampled head."""
+    import oracle
+    name = "fwd_bwd_bf16"
+    d = gi.make_config(name)
+    do, dht = gi.make_upstream(d, gi.CONFIGS[name]["seed"])
+    B, T, Hqk, Hv, dk, dv = d["B"], d["T"], d["Hqk"], d["Hv"], d["dk"], d["dv"]
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, dO = up(d["q"]), up(d["k"]), up(d["v"]), up(do)
+    g, beta = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+    dh = torch.from_numpy(dht).to(dev)
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.gdn_chunk_bwd(q, k, v, g, beta, dO, dht=dh, workspace=ws,
+                                     stream=stream.cuda_stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        out = call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = bwd_algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
+    bs, hs = 2, 7
+    sl = lambda x: gi.widen(x[bs:bs + 1, :, hs:hs + 1])
+    ref = oracle.gdn_bwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), d["g"][bs:bs + 1, :, hs:hs + 1],
+                         d["beta"][bs:bs + 1, :, hs:hs + 1], sl(do),
+                         dht=dht[bs:bs + 1, hs:hs + 1].astype(np.float64))
+    got = [x[bs:bs + 1, :, hs:hs + 1] if x.dim() >= 3 and x.shape[0] == B and x.shape[1] == T
+           else x[bs:bs + 1, hs:hs + 1] for x in out]
+    errs = {}
+    for nm, x, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, ref):
+        x = x.float().cpu().numpy()
+        errs[nm] = float(np.linalg.norm(x - r) / np.linalg.norm(r))
+    log("[bench] backward %.4f ms/call; sampled head rel-L2 %s" %
+        (ms, ", ".join(f"{n} {e:.2e}" for n, e in errs.items())))
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, do ~ N(0,1) bf16, "
+                        f"dht ~ N(0,0.02) fp32",
+            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes,
+                         "kernels": ["bwd_prep", "bwd_fstate", "bwd_dstate", "bwd_chunk"]},
+            "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -115,6 +178,7 @@ def main():
     # launches (about 50 ms) precede the timed region.
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -223,6 +287,11 @@ def main():
     err_h = float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))
     log(f"[bench] sampled head (b={bs}, h={hs}) rel-L2: output {err_o:.2e}, state {err_h:.2e}")
 
+    bwd = None
+    if not args.no_bwd:
+        log("[bench] backward")
+        bwd = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20)
+
     baseline = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -267,6 +336,7 @@ def main():
         },
         "cpu_baseline": baseline,
         "check": {"sampled_head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h},
+        "bwd": bwd,
         "wall_s_timed_region": wall,
     }
     print(json.dumps(result), flush=True)

@@ -12,8 +12,8 @@
         calibration copy, and writes profiles/traffic_headline_bf16.json (read
         by bench.py) and a text summary beside it.
 
-    python3 profile_traffic.py stats STATS_DIR --command CMD
-        Writes profiles/kernel_stats_headline_bf16.md from a
+    python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME]
+        Writes profiles/kernel_stats_NAME.md (default headline_bf16) from a
         `rocprofv3 --kernel-trace --stats` run of bench.py.
 """
 import argparse
@@ -118,13 +118,13 @@ def traffic(fetch_dir, write_dir, command):
     print("\n".join(lines))
 
 
-def stats(dirname, command):
+def stats(dirname, command, name="headline_bf16"):
     files = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {dirname}")
     with open(files[0], newline="") as f:
         rows = list(csv.DictReader(f))
-    lines = [f"# Kernel time, bench.py on {bench.WORKLOAD} (B=8 T=2048 H=16 d=128 bf16)",
+    lines = [f"# Kernel time, bench.py ({name}: B=8 T=2048 H=16 d=128 bf16)",
              "", "Command:", "", "```", command, "```", "",
              "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -133,7 +133,7 @@ def stats(dirname, command):
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
-    with open(os.path.join(PROFILES, "kernel_stats_headline_bf16.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"kernel_stats_{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -150,13 +150,14 @@ def main():
     s = sub.add_parser("stats")
     s.add_argument("stats_dir")
     s.add_argument("--command", required=True)
+    s.add_argument("--name", default="headline_bf16")
     args = ap.parse_args()
     if args.cmd == "launch":
         launch(args.launches)
     elif args.cmd == "traffic":
         traffic(args.fetch_dir, args.write_dir, args.command)
     else:
-        stats(args.stats_dir, args.command)
+        stats(args.stats_dir, args.command, args.name)
 
 
 if __name__ == "__main__":
