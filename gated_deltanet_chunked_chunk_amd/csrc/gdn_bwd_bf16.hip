@@ -30,10 +30,13 @@
 //                Writes T (fp32), P (bf16) and gamma to the workspace.
 //   bwd_fstate   per (sequence, value head, 64 value columns), chunks in
 //                order: the forward state recurrence with the dense T, writing
-//                each chunk's entering state M0 to the workspace.
+//                each chunk's entering state M0 to the workspace (bf16,
+//                transposed to [dv][dk]).
 //   bwd_dstate   per (sequence, value head, 64 value columns), chunks in
 //                reverse: the state-gradient recurrence, writing each chunk's
-//                dML to the workspace; dh0 is the gradient after chunk 0.
+//                dML to the workspace (bf16, [dv][dk]); dh0 is the gradient
+//                after chunk 0.  Both passes load the next chunk's operands
+//                into registers while computing the current one.
 //   bwd_chunk    per (chunk, q/k head), all in parallel: the token gradients
 //                of the chunk from M0 and dML, summed over the value heads
 //                that share the q/k head (dq, dk) and over value columns.
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     __shared__ float Af[kC * kLF];
     __shared__ float Tf[kC * kLF];
     __shared__ float Wf[32 * 33];
-    __shared__ uint16_t Ps[kC * kL64];
+    __shared__ uint16_t Ps[kC * kC];   // unpadded: keeps LDS under half a CU's
     __shared__ float gam[kC], bt[kC];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int64_t gc = blockIdx.x;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
             const int r = 16 * w + 4 * lg + rr, s = 16 * ni + lr;
             const float d = s <= r ? __expf(gam[r] - gam[s]) : 0.0f;
             Af[r * kLF + s] = s < r ? bt[r] * d * kk[ni][rr] : 0.0f;
-            Ps[r * kL64 + s] = f2bf(s <= r ? d * qk[ni][rr] : 0.0f);
+            Ps[r * kC + s] = f2bf(s <= r ? d * qk[ni][rr] : 0.0f);
         }
     __syncthreads();
 
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     uint16_t *Po = a.ws_P + wi * (kC * kC);
     for (int i = tid; i < kC * kC; i += 256) {
         To[i] = Tf[(i >> 6) * kLF + (i & 63)];
-        Po[i] = Ps[(i >> 6) * kL64 + (i & 63)];
+        Po[i] = Ps[i];
     }
     if (tid < kC)
         a.ws_gam[wi * kC + tid] = gam[tid];
@@ -423,17 +426,99 @@ struct StateSmem {
     float eL;
 };
 
-__device__ __forceinline__ void stage_tables(StateSmem &S, const BwdArgs &a, int64_t wi, int j,
-                                             const ChunkLoc &cl, int tid) {
-    if (tid < kC) {
-        const float gm = a.ws_gam[wi * kC + tid];
-        const float gL = a.ws_gam[wi * kC + kC - 1];
-        S.e[tid] = __expf(gm);
-        S.l[tid] = __expf(gL - gm);
-        S.bt[tid] = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
-        if (tid == 0)
-            S.eL = __expf(gL);
+// One chunk's operands in flight in registers: each of the 256 threads holds
+// its share of K (and Q), the value-column tile of V (or dO), T, P and the
+// gate tables, loaded while the previous chunk is computed.
+struct StatePre {
+    u32x4 k[4], q[4], x[2], p[2];
+    f32x4 t[4];
+    float gm, gL, bt;
+};
+
+template <bool Rev>
+__device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, const ChunkLoc &cl,
+                                            int hk, int j, int tile, int64_t wi, int tid) {
+    const uint32_t krow = (uint32_t)a.Hqk * kDK * 2;
+    const int64_t kofs = (cl.p * a.Hqk + hk) * (int64_t)kDK;
+    const __amdgpu_buffer_rsrc_t rk =
+        rsrc(static_cast<const uint16_t *>(a.k) + kofs, (uint32_t)(cl.L - 1) * krow + kDK * 2);
+    const __amdgpu_buffer_rsrc_t rq =
+        rsrc(static_cast<const uint16_t *>(a.q) + kofs, (uint32_t)(cl.L - 1) * krow + kDK * 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u;
+        const uint32_t off = (uint32_t)(i >> 4) * krow + 16 * (i & 15);
+        pre.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        if (Rev)
+            pre.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
+    const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
+    const void *xs = Rev ? a.dout : a.v;
+    const __amdgpu_buffer_rsrc_t rx =
+        rsrc(static_cast<const uint16_t *>(xs) + (cl.p * a.Hv + j) * (int64_t)a.dv + tile * kVT,
+             (uint32_t)(cl.L - 1) * xrow + kVT * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u;
+        pre.x[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(i >> 3) * xrow + 16 * (i & 7),
+                                                         0, 0);
+    }
+    const float *Tg = a.ws_T + wi * (kC * kC);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        pre.t[u] = *reinterpret_cast<const f32x4 *>(Tg + 4 * (tid + 256 * u));
+    if (Rev) {
+        const uint16_t *Pg = a.ws_P + wi * (kC * kC);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            pre.p[u] = *reinterpret_cast<const u32x4 *>(Pg + 8 * (tid + 256 * u));
+    }
+    if (tid < kC) {
+        pre.gm = a.ws_gam[wi * kC + tid];
+        pre.gL = a.ws_gam[wi * kC + kC - 1];
+        pre.bt = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+    }
+}
+
+template <bool Rev>
+__device__ __forceinline__ void state_commit(StateSmem &S, const StatePre &pre, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u;
+        *reinterpret_cast<u32x4 *>(S.K + (i >> 4) * kLK + 8 * (i & 15)) = pre.k[u];
+        if (Rev)
+            *reinterpret_cast<u32x4 *>(S.Q + (i >> 4) * kLK + 8 * (i & 15)) = pre.q[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u;
+        *reinterpret_cast<u32x4 *>(S.X + (i >> 3) * kL64 + 8 * (i & 7)) = pre.x[u];
+        if (Rev)
+            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) = pre.p[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u;
+        u32x2 h, l;
+        split4(pre.t[u], h, l);
+        *reinterpret_cast<u32x2 *>(S.Th + (i >> 4) * kL64 + 4 * (i & 15)) = h;
+        *reinterpret_cast<u32x2 *>(S.Tl + (i >> 4) * kL64 + 4 * (i & 15)) = l;
+    }
+    if (tid < kC) {
+        S.e[tid] = __expf(pre.gm);
+        S.l[tid] = __expf(pre.gL - pre.gm);
+        S.bt[tid] = pre.bt;
+        if (tid == 0)
+            S.eL = __expf(pre.gL);
+    }
+}
+
+// A state slice (lane column col, rows 16mt + 4lg + r) as bf16 into the
+// transposed workspace copy [dv][dk]: one 8-byte store per tile.
+__device__ __forceinline__ void store_state_t(uint16_t *dst, const f32x4 (&h)[8], int col, int lg) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<u32x2 *>(dst + (int64_t)col * kDK + 16 * mt + 4 * lg) = pack4(h[mt]);
 }
 
 // The state's hi part as the B operands of a contraction over dk (permuted k).
@@ -509,11 +594,13 @@ __device__ __forceinline__ void t_times(const uint16_t *Th, const uint16_t *Tl,
     }
 }
 
-__device__ __forceinline__ void stage_T_and(StateSmem &S, const BwdArgs &a, int64_t wi, int tid) {
-    stage_T(S.Th, S.Tl, a.ws_T + wi * (kC * kC), tid);
-}
-
-__global__ __launch_bounds__(256) void bwd_fstate(BwdArgs a) {
+// The two state recurrences, chunks in order (Rev = false: the forward
+// state, writing each chunk's entering state) or in reverse (Rev = true: the
+// state gradient, writing the gradient of each chunk's leaving state; dh0 at
+// the end).  Each chunk's operands are loaded into registers while the
+// previous chunk is computed.
+template <bool Rev>
+__device__ __forceinline__ void state_pass(const BwdArgs &a) {
     __shared__ StateSmem S;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int n_tiles = a.dv / kVT;
@@ -526,167 +613,134 @@ __global__ __launch_bounds__(256) void bwd_fstate(BwdArgs a) {
     const int nch = (int)((len + kC - 1) / kC);
     const int64_t base = chunk_base(a, n);
     const int64_t S_elems = (int64_t)kDK * a.dv;
+    const float scale = a.scale;
+    auto loc = [&](int c) {
+        ChunkLoc cl;
+        cl.n = n;
+        cl.c = c;
+        cl.p = seq_start(a, n) + (int64_t)kC * c;
+        cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
+        return cl;
+    };
 
+    const float *init = Rev ? a.dht : a.h0;
     f32x4 h[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            h[mt][r] = a.h0 ? a.h0[((int64_t)n * a.Hv + j) * S_elems +
+            h[mt][r] = init ? init[((int64_t)n * a.Hv + j) * S_elems +
                                    (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
                             : 0.0f;
-    for (int c = 0; c < nch; ++c) {
-        ChunkLoc cl;
-        cl.n = n;
-        cl.c = c;
-        cl.p = seq_start(a, n) + (int64_t)kC * c;
-        cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
+    StatePre pre;
+    if (nch > 0) {
+        const int c0 = Rev ? nch - 1 : 0;
+        state_issue<Rev>(pre, a, loc(c0), hk, j, tile, (base + c0) * a.Hv + j, tid);
+    }
+    for (int it = 0; it < nch; ++it) {
+        const int c = Rev ? nch - 1 - it : it;
+        const ChunkLoc cl = loc(c);
         const int64_t wi = (base + c) * a.Hv + j;
-        // The state entering chunk c.
-        float *hs = a.ws_hs + wi * S_elems;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                hs[(int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = h[mt][r];
-        stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
-        stage_rows_bf16<kVT>(S.X, kL64, a.v, cl.p, cl.L, a.Hv, j, tile * kVT, a.dv, tid);
-        stage_T_and(S, a, wi, tid);
-        stage_tables(S, a, wi, j, cl, tid);
+        state_commit<Rev>(S, pre, tid);
         __syncthreads();
+        if (it + 1 < nch) {
+            const int cn = Rev ? c - 1 : c + 1;
+            state_issue<Rev>(pre, a, loc(cn), hk, j, tile, (base + cn) * a.Hv + j, tid);
+        }
+        // Forward: the state entering chunk c; reverse: the gradient of the
+        // state leaving it.
+        store_state_t((Rev ? a.ws_dhs : a.ws_hs) + wi * S_elems, h, col, lg);
 
         bf16x8 hb[4];
         state_hi(h, hb);
-        f32x4 X[4];
-        k_times_state(S.K, hb, X, lr, lg);
-        f32x4 R[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mi + 4 * lg + r;
-                R[mi][r] = S.bt[row] * (bf2f(S.X[row * kL64 + 16 * w + lr]) - S.e[row] * X[mi][r]);
-            }
-        bf16x8 rh[2], rl[2];
-        tiles_split(R, rh, rl);
-        f32x4 Dl[4];
-        t_times<false>(S.Th, S.Tl, rh, rl, Dl, lr, lg);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Dl[mi][r] *= S.l[16 * mi + 4 * lg + r];
-        bf16x8 dh[2], dl[2];
-        tiles_split(Dl, dh, dl);
+        f32x4 Y[4];
+        k_times_state(S.K, hb, Y, lr, lg);
         const float eL = S.eL;
+        if (!Rev) {
+            // rhs = diag(beta) (V - diag(e) K M0); Delta' = diag(l) T rhs;
+            // M <- exp(gamma_L) M + K^T Delta'.
+            f32x4 R[4];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            h[mt] *= eL;
-        add_xt_times(S.K, dh, dl, h, lr, lg);
-        __syncthreads();
-    }
-}
-
-__global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
-    __shared__ StateSmem S;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-    const int n_tiles = a.dv / kVT;
-    const int tile = blockIdx.x % n_tiles;
-    const int j = (blockIdx.x / n_tiles) % a.Hv;
-    const int n = blockIdx.x / (n_tiles * a.Hv);
-    const int hk = j / (a.Hv / a.Hqk);
-    const int col = tile * kVT + 16 * w + lr;
-    const int64_t len = seq_len(a, n);
-    const int nch = (int)((len + kC - 1) / kC);
-    const int64_t base = chunk_base(a, n);
-    const int64_t S_elems = (int64_t)kDK * a.dv;
-    const float scale = a.scale;
-
-    f32x4 dM[8];
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mi + 4 * lg + r;
+                    R[mi][r] = S.bt[row] *
+                               (bf2f(S.X[row * kL64 + 16 * w + lr]) - S.e[row] * Y[mi][r]);
+                }
+            bf16x8 rh[2], rl[2];
+            tiles_split(R, rh, rl);
+            f32x4 Dl[4];
+            t_times<false>(S.Th, S.Tl, rh, rl, Dl, lr, lg);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dM[mt][r] = a.dht ? a.dht[((int64_t)n * a.Hv + j) * S_elems +
-                                      (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
-                              : 0.0f;
-    for (int c = nch - 1; c >= 0; --c) {
-        ChunkLoc cl;
-        cl.n = n;
-        cl.c = c;
-        cl.p = seq_start(a, n) + (int64_t)kC * c;
-        cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
-        const int64_t wi = (base + c) * a.Hv + j;
-        // The state gradient leaving chunk c.
-        float *dhs = a.ws_dhs + wi * S_elems;
+            for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+                for (int r = 0; r < 4; ++r)
+                    Dl[mi][r] *= S.l[16 * mi + 4 * lg + r];
+            bf16x8 dh[2], dl[2];
+            tiles_split(Dl, dh, dl);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dhs[(int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = dM[mt][r];
-        stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
-        stage_rows_bf16<kDK>(S.Q, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
-        stage_rows_bf16<kVT>(S.X, kL64, a.dout, cl.p, cl.L, a.Hv, j, tile * kVT, a.dv, tid);
-        stage_T_and(S, a, wi, tid);
-        for (int i = tid; i < kC * kC / 8; i += 256)
-            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) =
-                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * i);
-        stage_tables(S, a, wi, j, cl, tid);
-        __syncthreads();
-
-        bf16x8 hb[4];
-        state_hi(dM, hb);
-        f32x4 U[4];
-        k_times_state(S.K, hb, U, lr, lg);
-        // dDelta = diag(l) K dML + P^T dO (dO = scale * do).
-        f32x4 dD[4];
+            for (int mt = 0; mt < 8; ++mt)
+                h[mt] *= eL;
+            add_xt_times(S.K, dh, dl, h, lr, lg);
+        } else {
+            // dDelta = diag(l) K dML + P^T dO; drhs = T^T dDelta;
+            // dM <- exp(gamma_L) dM - K^T diag(beta e) drhs + Q^T diag(e) dO.
+            f32x4 dD[4];
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            f32x4 v1 = {0.f, 0.f, 0.f, 0.f};
+            for (int mi = 0; mi < 4; ++mi) {
+                f32x4 v1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (32 * kk + 31 < 16 * mi)
-                    continue;
-                v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * mi, lr, lg),
-                         frag_cols(S.X, kL64, 32 * kk, 16 * w, lr, lg), v1);
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (32 * kk + 31 < 16 * mi)
+                        continue;
+                    v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * mi, lr, lg),
+                             frag_cols(S.X, kL64, 32 * kk, 16 * w, lr, lg), v1);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dD[mi][r] = S.l[16 * mi + 4 * lg + r] * Y[mi][r] + scale * v1[r];
             }
+            bf16x8 zh[2], zl[2];
+            tiles_split(dD, zh, zl);
+            f32x4 dR[4];
+            t_times<true>(S.Th, S.Tl, zh, zl, dR, lr, lg);
+            f32x4 dX[4], eO[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dD[mi][r] = S.l[16 * mi + 4 * lg + r] * U[mi][r] + scale * v1[r];
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * mi + 4 * lg + r;
+                    dX[mi][r] = -S.bt[row] * S.e[row] * dR[mi][r];
+                    eO[mi][r] = scale * S.e[row] * bf2f(S.X[row * kL64 + 16 * w + lr]);
+                }
+            bf16x8 xh[2], xl[2], oh[2], ol[2];
+            tiles_split(dX, xh, xl);
+            tiles_split(eO, oh, ol);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                h[mt] *= eL;
+            add_xt_times(S.K, xh, xl, h, lr, lg);
+            add_xt_times(S.Q, oh, ol, h, lr, lg);
         }
-        bf16x8 zh[2], zl[2];
-        tiles_split(dD, zh, zl);
-        f32x4 dR[4];
-        t_times<true>(S.Th, S.Tl, zh, zl, dR, lr, lg);
-        // dX = -diag(beta e) drhs and diag(e) dO, as hi and lo B operands.
-        f32x4 dX[4], eO[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mi + 4 * lg + r;
-                dX[mi][r] = -S.bt[row] * S.e[row] * dR[mi][r];
-                eO[mi][r] = scale * S.e[row] * bf2f(S.X[row * kL64 + 16 * w + lr]);
-            }
-        bf16x8 xh[2], xl[2], oh[2], ol[2];
-        tiles_split(dX, xh, xl);
-        tiles_split(eO, oh, ol);
-        const float eL = S.eL;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            dM[mt] *= eL;
-        add_xt_times(S.K, xh, xl, dM, lr, lg);
-        add_xt_times(S.Q, oh, ol, dM, lr, lg);
         __syncthreads();
     }
-    if (a.dh0) {
+    if (Rev && a.dh0) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 a.dh0[((int64_t)n * a.Hv + j) * S_elems + (int64_t)(16 * mt + 4 * lg + r) * a.dv +
-                      col] = dM[mt][r];
+                      col] = h[mt][r];
     }
+}
+
+__global__ __launch_bounds__(256) void bwd_fstate(BwdArgs a) {
+    state_pass<false>(a);
+}
+
+__global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
+    state_pass<true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,8 +756,8 @@ struct ChunkSmem {
     uint16_t P[kC * kL64];
     union {
         struct {
-            uint16_t M0[kDK * kL32];   // [dk][col]
-            uint16_t dM[kDK * kL32];
+            uint16_t M0[32 * kLK];     // M0^T: [col][dk]
+            uint16_t dM[32 * kLK];     // dML^T
             uint16_t V[kC * kL32];
             uint16_t dO[kC * kL32];    // do (unscaled)
             uint16_t rh[kC * kL32];
@@ -724,6 +778,38 @@ struct ChunkSmem {
     float red[256];
 };
 
+// One 32-column tile of M0^T, dML^T, V and do in flight in registers.
+struct TilePre {
+    u32x4 m[2], d[2], v, o;
+};
+
+__device__ __forceinline__ void tile_issue(TilePre &pre, const BwdArgs &a, const ChunkLoc &cl,
+                                           int j, int64_t wi, int t0, int tid) {
+    const int64_t sofs = wi * (int64_t)kDK * a.dv + (int64_t)t0 * kDK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u;  // row i >> 4 (a column), piece i & 15
+        pre.m[u] = *reinterpret_cast<const u32x4 *>(a.ws_hs + sofs + 8 * i);
+        pre.d[u] = *reinterpret_cast<const u32x4 *>(a.ws_dhs + sofs + 8 * i);
+    }
+    const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
+    const int64_t xofs = (cl.p * a.Hv + j) * (int64_t)a.dv + t0;
+    const uint32_t span = (uint32_t)(cl.L - 1) * xrow + 64;
+    const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint16_t *>(a.v) + xofs, span);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t *>(a.dout) + xofs, span);
+    const uint32_t off = (uint32_t)(tid >> 2) * xrow + 16 * (tid & 3);
+    pre.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+    pre.o = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+}
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s += bf2f(a[i] & 0xffff) * bf2f(b[i] & 0xffff) + bf2f(a[i] >> 16) * bf2f(b[i] >> 16);
+    return s;
+}
+
 __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
     __shared__ ChunkSmem S;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -734,7 +820,6 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
         return;
     const int G = a.Hv / a.Hqk;
     const float scale = a.scale;
-    const int64_t S_elems = (int64_t)kDK * a.dv;
     stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
     stage_rows_bf16<kDK>(S.Q, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
 
@@ -773,22 +858,23 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
         float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma parts
         float dgL = 0.0f;                     // this thread's part of d gamma_L
 
+        TilePre pre;
+        tile_issue(pre, a, cl, j, wi, 0, tid);
         for (int t0 = 0; t0 < a.dv; t0 += 32) {
             __syncthreads();
-            // M0 and dML columns [t0, t0 + 32) as bf16 [dk][col].
-            const float *Mg = a.ws_hs + wi * S_elems + t0;
-            const float *dMg = a.ws_dhs + wi * S_elems + t0;
-            for (int i = tid; i < kDK * 8; i += 256) {
-                const int row = i >> 3, c4 = i & 7;
-                const f32x4 m = *reinterpret_cast<const f32x4 *>(Mg + (int64_t)row * a.dv + 4 * c4);
-                const f32x4 d = *reinterpret_cast<const f32x4 *>(dMg + (int64_t)row * a.dv + 4 * c4);
-                *reinterpret_cast<u32x2 *>(S.u.t.M0 + row * kL32 + 4 * c4) = pack4(m);
-                *reinterpret_cast<u32x2 *>(S.u.t.dM + row * kL32 + 4 * c4) = pack4(d);
-                dgL += eL * (m[0] * d[0] + m[1] * d[1] + m[2] * d[2] + m[3] * d[3]);
+            // M0^T and dML^T rows (columns t0 .. t0 + 31 of the states), V, do.
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = tid + 256 * u;
+                *reinterpret_cast<u32x4 *>(S.u.t.M0 + (i >> 4) * kLK + 8 * (i & 15)) = pre.m[u];
+                *reinterpret_cast<u32x4 *>(S.u.t.dM + (i >> 4) * kLK + 8 * (i & 15)) = pre.d[u];
+                dgL += eL * dot8(pre.m[u], pre.d[u]);
             }
-            stage_rows_bf16<32>(S.u.t.V, kL32, a.v, cl.p, cl.L, a.Hv, j, t0, a.dv, tid);
-            stage_rows_bf16<32>(S.u.t.dO, kL32, a.dout, cl.p, cl.L, a.Hv, j, t0, a.dv, tid);
+            *reinterpret_cast<u32x4 *>(S.u.t.V + (tid >> 2) * kL32 + 8 * (tid & 3)) = pre.v;
+            *reinterpret_cast<u32x4 *>(S.u.t.dO + (tid >> 2) * kL32 + 8 * (tid & 3)) = pre.o;
             __syncthreads();
+            if (t0 + 32 < a.dv)
+                tile_issue(pre, a, cl, j, wi, t0 + 32, tid);
 
             // X = K M0, Y = Q M0, U = K dML (rows 16w.., columns 16ni..).
             f32x4 X[2], Y[2], U[2];
@@ -801,8 +887,8 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
                 for (int kx = 0; kx < 4; ++kx) {
                     const bf16x8 fk = frag_rows(S.K, kLK, 16 * w, 32 * kx, lr, lg);
                     const bf16x8 fq = frag_rows(S.Q, kLK, 16 * w, 32 * kx, lr, lg);
-                    const bf16x8 bm = frag_cols(S.u.t.M0, kL32, 32 * kx, 16 * ni, lr, lg);
-                    const bf16x8 bd = frag_cols(S.u.t.dM, kL32, 32 * kx, 16 * ni, lr, lg);
+                    const bf16x8 bm = frag_rows(S.u.t.M0, kLK, 16 * ni, 32 * kx, lr, lg);
+                    const bf16x8 bd = frag_rows(S.u.t.dM, kLK, 16 * ni, 32 * kx, lr, lg);
                     X[ni] = mma(fk, bm, X[ni]);
                     Y[ni] = mma(fq, bm, Y[ni]);
                     U[ni] = mma(fk, bd, U[ni]);
@@ -906,8 +992,8 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
             const bf16x8 fw = frag_rows(S.u.t.W, kL32, 16 * w, 0, lr, lg);
 #pragma unroll
             for (int nj = 0; nj < 8; ++nj) {
-                const bf16x8 bm = frag_rows(S.u.t.M0, kL32, 16 * nj, 0, lr, lg);
-                const bf16x8 bd = frag_rows(S.u.t.dM, kL32, 16 * nj, 0, lr, lg);
+                const bf16x8 bm = frag_cols(S.u.t.M0, kLK, 0, 16 * nj, lr, lg);
+                const bf16x8 bd = frag_cols(S.u.t.dM, kLK, 0, 16 * nj, lr, lg);
                 dQ[nj] = mma(fy, bm, dQ[nj]);
                 dK[nj] = mma(fx, bm, dK[nj]);
                 dK[nj] = mma(fw, bd, dK[nj]);
@@ -1042,7 +1128,7 @@ size_t bwd_workspace_bytes(int64_t n_chunks, int32_t Hv, int32_t dk, int32_t dv)
     b += ch * kC * kC * sizeof(float);           // T
     b += ch * kC * kC * sizeof(uint16_t);        // P
     b += ch * kC * sizeof(float);                // gamma
-    b += 2 * ch * (size_t)dk * dv * sizeof(float);  // chunk states and their gradients
+    b += 2 * ch * (size_t)dk * dv * sizeof(uint16_t);  // chunk states and their gradients
     return b;
 }
 
@@ -1055,9 +1141,9 @@ void bwd_carve(BwdArgs &a, void *workspace) {
     p += ch * kC * kC * sizeof(uint16_t);
     a.ws_gam = reinterpret_cast<float *>(p);
     p += ch * kC * sizeof(float);
-    a.ws_hs = reinterpret_cast<float *>(p);
-    p += ch * (size_t)a.dk * a.dv * sizeof(float);
-    a.ws_dhs = reinterpret_cast<float *>(p);
+    a.ws_hs = reinterpret_cast<uint16_t *>(p);
+    p += ch * (size_t)a.dk * a.dv * sizeof(uint16_t);
+    a.ws_dhs = reinterpret_cast<uint16_t *>(p);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {

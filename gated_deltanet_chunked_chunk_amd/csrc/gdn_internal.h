@@ -53,8 +53,8 @@ struct BwdArgs {
     float *ws_T;            // [n_chunks, Hv, 64, 64]
     uint16_t *ws_P;         // [n_chunks, Hv, 64, 64]
     float *ws_gam;          // [n_chunks, Hv, 64]
-    float *ws_hs;           // [n_chunks, Hv, dk, dv]
-    float *ws_dhs;          // [n_chunks, Hv, dk, dv]
+    uint16_t *ws_hs;        // [n_chunks, Hv, dv, dk] bf16: the state entering each chunk
+    uint16_t *ws_dhs;       // [n_chunks, Hv, dv, dk] bf16: the gradient of the state leaving it
     int64_t T;              // tokens per row (batch mode)
     int64_t n_chunks;       // chunks the workspace holds (an upper bound with cu)
     int32_t Hqk, Hv, dk, dv;

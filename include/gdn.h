@@ -118,8 +118,9 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
  * Bytes of device workspace gdn_chunk_bwd needs for these sizes (0 for sizes
  * the backward would reject).  The workspace holds, per chunk of 64 tokens and
  * value head, the chunk's inverse (I + A)^-1 (fp32), its gated Q K^T (bf16),
- * its cumulative decay, and the fp32 state entering the chunk and the gradient
- * of the state leaving it: about 2 * dk * dv * 4 + 24.8 KiB per chunk and head.
+ * its cumulative decay, and (in bf16) the state entering the chunk and the
+ * gradient of the state leaving it: 2 * dk * dv * 2 bytes + 24.25 KiB per
+ * chunk and head.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  * With cu_seqlens the size covers any split of the T tokens into n_seqs

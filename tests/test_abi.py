@@ -91,8 +91,8 @@ def test_binding_checks_tensors_on_host():
 
 def test_bwd_workspace_size():
     ws = gdn.gdn_chunk_bwd_workspace_size
-    # 8 rows of 32 chunks, 16 heads: per chunk-head 64*64*4 + 64*64*2 + 64*4 + 2*128*128*4
-    per = 64 * 64 * 4 + 64 * 64 * 2 + 64 * 4 + 2 * 128 * 128 * 4
+    # 8 rows of 32 chunks, 16 heads: per chunk-head 64*64*4 + 64*64*2 + 64*4 + 2*128*128*2
+    per = 64 * 64 * 4 + 64 * 64 * 2 + 64 * 4 + 2 * 128 * 128 * 2
     assert ws(1, 8, 2048, 16, 16, 128, 128, 8) == 8 * 32 * 16 * per
     # one packed row of 5 documents: at most ceil(T / 64) + 5 chunks
     assert ws(1, 1, 2048, 16, 16, 128, 128, 5) == (32 + 5) * 16 * per
