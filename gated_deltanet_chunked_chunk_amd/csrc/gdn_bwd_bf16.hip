@@ -744,9 +744,13 @@ __global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_chunk: per (chunk, q/k head).  Wave w owns the chunk's rows
-// [16w, 16w + 16) of every [64 x *] result; value columns are taken 32 at a
-// time.
+// bwd_chunk: per (chunk, q/k head), 512 threads.  Wave w owns the chunk's
+// rows [16 rb, 16 rb + 16), rb = w % 4, and the column half h = w / 4 of every
+// [64 x *] result: in a 32-column tile the 16 columns 16h.., of dq and dk the
+// dk tiles 4h .. 4h + 3, of the 64 x 64 products the column tiles 2h, 2h + 1.
+// Two waves per SIMD hide each other's latency.
+
+constexpr int kCT = 512;   // bwd_chunk threads
 
 struct ChunkSmem {
     uint16_t K[kC * kLK];
@@ -774,32 +778,30 @@ struct ChunkSmem {
     } u;
     float gam[kC], e[kC], l[kC], bt[kC];
     float colpart[4][kC];
+    float rowb[2][kC], rowg[2][kC];
     float dgam[kC];
-    float red[256];
+    float red[kCT];
 };
 
-// One 32-column tile of M0^T, dML^T, V and do in flight in registers.
+// One 32-column tile of M0^T, dML^T, V and do in flight in registers: thread
+// t holds piece t of M0^T and of dML^T (row t / 16, 16 bytes t % 16), and
+// threads below 256 a piece of V, the others one of do.
 struct TilePre {
-    u32x4 m[2], d[2], v, o;
+    u32x4 m, d, x;
 };
 
 __device__ __forceinline__ void tile_issue(TilePre &pre, const BwdArgs &a, const ChunkLoc &cl,
                                            int j, int64_t wi, int t0, int tid) {
     const int64_t sofs = wi * (int64_t)kDK * a.dv + (int64_t)t0 * kDK;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + 256 * u;  // row i >> 4 (a column), piece i & 15
-        pre.m[u] = *reinterpret_cast<const u32x4 *>(a.ws_hs + sofs + 8 * i);
-        pre.d[u] = *reinterpret_cast<const u32x4 *>(a.ws_dhs + sofs + 8 * i);
-    }
+    pre.m = *reinterpret_cast<const u32x4 *>(a.ws_hs + sofs + 8 * tid);
+    pre.d = *reinterpret_cast<const u32x4 *>(a.ws_dhs + sofs + 8 * tid);
     const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
     const int64_t xofs = (cl.p * a.Hv + j) * (int64_t)a.dv + t0;
     const uint32_t span = (uint32_t)(cl.L - 1) * xrow + 64;
-    const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint16_t *>(a.v) + xofs, span);
-    const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t *>(a.dout) + xofs, span);
-    const uint32_t off = (uint32_t)(tid >> 2) * xrow + 16 * (tid & 3);
-    pre.v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-    pre.o = __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0);
+    const void *src = tid < 256 ? a.v : a.dout;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(static_cast<const uint16_t *>(src) + xofs, span);
+    const int i = tid & 255;
+    pre.x = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(i >> 2) * xrow + 16 * (i & 3), 0, 0);
 }
 
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
@@ -810,9 +812,27 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
     return s;
 }
 
-__global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
+// Rows [p, p + L) of a [*, H, 128] bf16 tensor at head h into a [64][kLK]
+// tile, 512 threads.
+__device__ __forceinline__ void stage_rows512(uint16_t *dst, const void *src, int64_t p, int L,
+                                              int H, int h, int tid) {
+    const uint32_t row_bytes = (uint32_t)H * kDK * 2;
+    const __amdgpu_buffer_rsrc_t r =
+        rsrc(static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)kDK,
+             (uint32_t)(L - 1) * row_bytes + kDK * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + kCT * u;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15),
+                                                              0, 0);
+        *reinterpret_cast<u32x4 *>(dst + (i >> 4) * kLK + 8 * (i & 15)) = v;
+    }
+}
+
+__global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
     __shared__ ChunkSmem S;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int rb = w & 3, h = w >> 2;
     const int64_t gc = blockIdx.x;
     const int hk = blockIdx.y;
     ChunkLoc cl;
@@ -820,12 +840,12 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
         return;
     const int G = a.Hv / a.Hqk;
     const float scale = a.scale;
-    stage_rows_bf16<kDK>(S.K, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
-    stage_rows_bf16<kDK>(S.Q, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+    stage_rows512(S.K, a.k, cl.p, cl.L, a.Hqk, hk, tid);
+    stage_rows512(S.Q, a.q, cl.p, cl.L, a.Hqk, hk, tid);
 
-    f32x4 dQ[8], dK[8];
+    f32x4 dQ[4], dK[4];   // dk tiles 4h + i
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         dQ[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         dK[i] = dQ[i];
     }
@@ -833,11 +853,22 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
     for (int gi = 0; gi < G; ++gi) {
         const int j = hk * G + gi;
         const int64_t wi = gc * a.Hv + j;
+        TilePre pre;
+        tile_issue(pre, a, cl, j, wi, 0, tid);
         __syncthreads();  // the previous head's readers are done
-        stage_T(S.Th, S.Tl, a.ws_T + wi * (kC * kC), tid);
-        for (int i = tid; i < kC * kC / 8; i += 256)
-            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) =
-                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * i);
+        {
+            const float *Tg = a.ws_T + wi * (kC * kC);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = tid + kCT * u;
+                u32x2 hi, lo;
+                split4(*reinterpret_cast<const f32x4 *>(Tg + 4 * i), hi, lo);
+                *reinterpret_cast<u32x2 *>(S.Th + (i >> 4) * kL64 + 4 * (i & 15)) = hi;
+                *reinterpret_cast<u32x2 *>(S.Tl + (i >> 4) * kL64 + 4 * (i & 15)) = lo;
+            }
+            *reinterpret_cast<u32x4 *>(S.P + (tid >> 3) * kL64 + 8 * (tid & 7)) =
+                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * tid);
+        }
         if (tid < kC) {
             const float gm = a.ws_gam[wi * kC + tid];
             const float gL = a.ws_gam[wi * kC + kC - 1];
@@ -848,244 +879,231 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
         }
         const float eL = __expf(a.ws_gam[wi * kC + kC - 1]);
 
-        f32x4 dP[4], dA[4];
+        f32x4 dP[2], dA[2];   // column tiles 2h + i
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             dP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             dA[i] = dP[i];
         }
-        float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta parts of rows 16w + 4lg + r
-        float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma parts
+        float pb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta parts of rows 16rb + 4lg + r
+        float pg[4] = {0.f, 0.f, 0.f, 0.f};   // dgamma parts
         float dgL = 0.0f;                     // this thread's part of d gamma_L
 
-        TilePre pre;
-        tile_issue(pre, a, cl, j, wi, 0, tid);
         for (int t0 = 0; t0 < a.dv; t0 += 32) {
+            // The lane indices pass through an empty asm so that the many
+            // addresses formed from them are computed here, not hoisted out
+            // of the loop and held (or spilled) across it.
+            int lrv = lane & 15, lgv = lane >> 4;
+            asm volatile("" : "+v"(lrv), "+v"(lgv));
+            const int lr = lrv, lg = lgv;
+            const int cc = 16 * h + lr;           // this lane's column in a tile
             __syncthreads();
-            // M0^T and dML^T rows (columns t0 .. t0 + 31 of the states), V, do.
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = tid + 256 * u;
-                *reinterpret_cast<u32x4 *>(S.u.t.M0 + (i >> 4) * kLK + 8 * (i & 15)) = pre.m[u];
-                *reinterpret_cast<u32x4 *>(S.u.t.dM + (i >> 4) * kLK + 8 * (i & 15)) = pre.d[u];
-                dgL += eL * dot8(pre.m[u], pre.d[u]);
+            *reinterpret_cast<u32x4 *>(S.u.t.M0 + (tid >> 4) * kLK + 8 * (tid & 15)) = pre.m;
+            *reinterpret_cast<u32x4 *>(S.u.t.dM + (tid >> 4) * kLK + 8 * (tid & 15)) = pre.d;
+            dgL += eL * dot8(pre.m, pre.d);
+            {
+                const int i = tid & 255;
+                uint16_t *xd = tid < 256 ? S.u.t.V : S.u.t.dO;
+                *reinterpret_cast<u32x4 *>(xd + (i >> 2) * kL32 + 8 * (i & 3)) = pre.x;
             }
-            *reinterpret_cast<u32x4 *>(S.u.t.V + (tid >> 2) * kL32 + 8 * (tid & 3)) = pre.v;
-            *reinterpret_cast<u32x4 *>(S.u.t.dO + (tid >> 2) * kL32 + 8 * (tid & 3)) = pre.o;
             __syncthreads();
             if (t0 + 32 < a.dv)
                 tile_issue(pre, a, cl, j, wi, t0 + 32, tid);
 
-            // X = K M0, Y = Q M0, U = K dML (rows 16w.., columns 16ni..).
-            f32x4 X[2], Y[2], U[2];
+            // X = K M0, Y = Q M0, U = K dML (rows 16rb.., columns 16h..).
+            f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, U = X;
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                X[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-                Y[ni] = X[ni];
-                U[ni] = X[ni];
-#pragma unroll
-                for (int kx = 0; kx < 4; ++kx) {
-                    const bf16x8 fk = frag_rows(S.K, kLK, 16 * w, 32 * kx, lr, lg);
-                    const bf16x8 fq = frag_rows(S.Q, kLK, 16 * w, 32 * kx, lr, lg);
-                    const bf16x8 bm = frag_rows(S.u.t.M0, kLK, 16 * ni, 32 * kx, lr, lg);
-                    const bf16x8 bd = frag_rows(S.u.t.dM, kLK, 16 * ni, 32 * kx, lr, lg);
-                    X[ni] = mma(fk, bm, X[ni]);
-                    Y[ni] = mma(fq, bm, Y[ni]);
-                    U[ni] = mma(fk, bd, U[ni]);
-                }
+            for (int kx = 0; kx < 4; ++kx) {
+                const bf16x8 fk = frag_rows(S.K, kLK, 16 * rb, 32 * kx, lr, lg);
+                const bf16x8 fq = frag_rows(S.Q, kLK, 16 * rb, 32 * kx, lr, lg);
+                const bf16x8 bm = frag_rows(S.u.t.M0, kLK, 16 * h, 32 * kx, lr, lg);
+                const bf16x8 bd = frag_rows(S.u.t.dM, kLK, 16 * h, 32 * kx, lr, lg);
+                X = mma(fk, bm, X);
+                Y = mma(fq, bm, Y);
+                U = mma(fk, bd, U);
             }
             // rhs = diag(beta) (V - diag(e) X), hi and lo.
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
-                    const float rhs =
-                        S.bt[row] * (bf2f(S.u.t.V[row * kL32 + cc]) - S.e[row] * X[ni][r]);
-                    const uint16_t hb = f2bf(rhs);
-                    S.u.t.rh[row * kL32 + cc] = hb;
-                    S.u.t.rl[row * kL32 + cc] = f2bf(rhs - bf2f(hb));
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r;
+                const float rhs = S.bt[row] * (bf2f(S.u.t.V[row * kL32 + cc]) - S.e[row] * X[r]);
+                const uint16_t hb = f2bf(rhs);
+                S.u.t.rh[row * kL32 + cc] = hb;
+                S.u.t.rl[row * kL32 + cc] = f2bf(rhs - bf2f(hb));
+            }
             __syncthreads();
 
             // Delta = T rhs; dDelta = diag(l) U + P^T dO.
-            f32x4 Dl[2], dD[2];
+            f32x4 Dl = {0.f, 0.f, 0.f, 0.f}, v1 = Dl, dD;
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                Dl[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-                f32x4 v1 = Dl[ni];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (32 * kk <= 16 * w + 15) {
-                        const bf16x8 th = frag_rows(S.Th, kL64, 16 * w, 32 * kk, lr, lg);
-                        const bf16x8 tl = frag_rows(S.Tl, kL64, 16 * w, 32 * kk, lr, lg);
-                        const bf16x8 bh = frag_cols(S.u.t.rh, kL32, 32 * kk, 16 * ni, lr, lg);
-                        const bf16x8 bl = frag_cols(S.u.t.rl, kL32, 32 * kk, 16 * ni, lr, lg);
-                        Dl[ni] = mma(th, bh, Dl[ni]);
-                        Dl[ni] = mma(th, bl, Dl[ni]);
-                        Dl[ni] = mma(tl, bh, Dl[ni]);
-                    }
-                    if (32 * kk + 31 >= 16 * w)
-                        v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * w, lr, lg),
-                                 frag_cols(S.u.t.dO, kL32, 32 * kk, 16 * ni, lr, lg), v1);
+            for (int kk = 0; kk < 2; ++kk) {
+                if (32 * kk <= 16 * rb + 15) {
+                    const bf16x8 th = frag_rows(S.Th, kL64, 16 * rb, 32 * kk, lr, lg);
+                    const bf16x8 tl = frag_rows(S.Tl, kL64, 16 * rb, 32 * kk, lr, lg);
+                    const bf16x8 bh = frag_cols(S.u.t.rh, kL32, 32 * kk, 16 * h, lr, lg);
+                    const bf16x8 bl = frag_cols(S.u.t.rl, kL32, 32 * kk, 16 * h, lr, lg);
+                    Dl = mma(th, bh, Dl);
+                    Dl = mma(th, bl, Dl);
+                    Dl = mma(tl, bh, Dl);
                 }
+                if (32 * kk + 31 >= 16 * rb)
+                    v1 = mma(frag_cols(S.P, kL64, 32 * kk, 16 * rb, lr, lg),
+                             frag_cols(S.u.t.dO, kL32, 32 * kk, 16 * h, lr, lg), v1);
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
-                    dD[ni][r] = S.l[row] * U[ni][r] + scale * v1[r];
-                    S.u.t.Dh[row * kL32 + cc] = f2bf(Dl[ni][r]);
-                    const uint16_t hb = f2bf(dD[ni][r]);
-                    S.u.t.zh[row * kL32 + cc] = hb;
-                    S.u.t.zl[row * kL32 + cc] = f2bf(dD[ni][r] - bf2f(hb));
-                    // d l_r = sum_c Delta dW: l_r enters dgamma_r with -l_r, gamma_L with +l_r.
-                    const float dlr = S.l[row] * Dl[ni][r] * U[ni][r];
-                    rg[r] -= dlr;
-                    dgL += dlr;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r;
+                dD[r] = S.l[row] * U[r] + scale * v1[r];
+                S.u.t.Dh[row * kL32 + cc] = f2bf(Dl[r]);
+                const uint16_t hb = f2bf(dD[r]);
+                S.u.t.zh[row * kL32 + cc] = hb;
+                S.u.t.zl[row * kL32 + cc] = f2bf(dD[r] - bf2f(hb));
+                // d l_r = sum_c Delta dW: l_r enters dgamma_r with -l_r, gamma_L with +l_r.
+                const float dlr = S.l[row] * Dl[r] * U[r];
+                pg[r] -= dlr;
+                dgL += dlr;
             }
             __syncthreads();
 
             // drhs = T^T dDelta.
-            f32x4 dR[2];
+            f32x4 dR = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                dR[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (32 * kk + 31 < 16 * w)
-                        continue;
-                    const bf16x8 th = frag_cols(S.Th, kL64, 32 * kk, 16 * w, lr, lg);
-                    const bf16x8 tl = frag_cols(S.Tl, kL64, 32 * kk, 16 * w, lr, lg);
-                    const bf16x8 bh = frag_cols(S.u.t.zh, kL32, 32 * kk, 16 * ni, lr, lg);
-                    const bf16x8 bl = frag_cols(S.u.t.zl, kL32, 32 * kk, 16 * ni, lr, lg);
-                    dR[ni] = mma(th, bh, dR[ni]);
-                    dR[ni] = mma(th, bl, dR[ni]);
-                    dR[ni] = mma(tl, bh, dR[ni]);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                if (32 * kk + 31 < 16 * rb)
+                    continue;
+                const bf16x8 th = frag_cols(S.Th, kL64, 32 * kk, 16 * rb, lr, lg);
+                const bf16x8 tl = frag_cols(S.Tl, kL64, 32 * kk, 16 * rb, lr, lg);
+                const bf16x8 bh = frag_cols(S.u.t.zh, kL32, 32 * kk, 16 * h, lr, lg);
+                const bf16x8 bl = frag_cols(S.u.t.zl, kL32, 32 * kk, 16 * h, lr, lg);
+                dR = mma(th, bh, dR);
+                dR = mma(th, bl, dR);
+                dR = mma(tl, bh, dR);
             }
             // dV, the dbeta and dgamma parts, and the operands of the
             // products over columns.
             uint16_t *dvo = static_cast<uint16_t *>(a.dv_);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * w + 4 * lg + r, cc = 16 * ni + lr;
-                    const float b = S.bt[row], e = S.e[row];
-                    const float vv = bf2f(S.u.t.V[row * kL32 + cc]);
-                    const float dov = scale * bf2f(S.u.t.dO[row * kL32 + cc]);
-                    const float dr = dR[ni][r];
-                    if (row < cl.L)
-                        dvo[((cl.p + row) * a.Hv + j) * (int64_t)a.dv + t0 + cc] = f2bf(b * dr);
-                    rb[r] += dr * (vv - e * X[ni][r]);
-                    rg[r] += e * dov * Y[ni][r] - b * e * dr * X[ni][r];
-                    S.u.t.dR[row * kL32 + cc] = f2bf(dr);
-                    S.u.t.dY[row * kL32 + cc] = f2bf(e * dov);
-                    S.u.t.dX[row * kL32 + cc] = f2bf(-b * e * dr);
-                    S.u.t.W[row * kL32 + cc] = f2bf(S.l[row] * Dl[ni][r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r;
+                const float b = S.bt[row], e = S.e[row];
+                const float vv = bf2f(S.u.t.V[row * kL32 + cc]);
+                const float dov = scale * bf2f(S.u.t.dO[row * kL32 + cc]);
+                const float dr = dR[r];
+                if (row < cl.L)
+                    dvo[((cl.p + row) * a.Hv + j) * (int64_t)a.dv + t0 + cc] = f2bf(b * dr);
+                pb[r] += dr * (vv - e * X[r]);
+                pg[r] += e * dov * Y[r] - b * e * dr * X[r];
+                S.u.t.dR[row * kL32 + cc] = f2bf(dr);
+                S.u.t.dY[row * kL32 + cc] = f2bf(e * dov);
+                S.u.t.dX[row * kL32 + cc] = f2bf(-b * e * dr);
+                S.u.t.W[row * kL32 + cc] = f2bf(S.l[row] * Dl[r]);
+            }
             __syncthreads();
 
-            // dQ += dY M0^T, dK += dX M0^T + W dML^T (rows 16w.., dk tiles).
-            const bf16x8 fy = frag_rows(S.u.t.dY, kL32, 16 * w, 0, lr, lg);
-            const bf16x8 fx = frag_rows(S.u.t.dX, kL32, 16 * w, 0, lr, lg);
-            const bf16x8 fw = frag_rows(S.u.t.W, kL32, 16 * w, 0, lr, lg);
+            // dQ += dY M0^T, dK += dX M0^T + W dML^T (rows 16rb.., dk tiles 4h + i).
+            const bf16x8 fy = frag_rows(S.u.t.dY, kL32, 16 * rb, 0, lr, lg);
+            const bf16x8 fx = frag_rows(S.u.t.dX, kL32, 16 * rb, 0, lr, lg);
+            const bf16x8 fw = frag_rows(S.u.t.W, kL32, 16 * rb, 0, lr, lg);
 #pragma unroll
-            for (int nj = 0; nj < 8; ++nj) {
+            for (int i = 0; i < 4; ++i) {
+                const int nj = 4 * h + i;
                 const bf16x8 bm = frag_cols(S.u.t.M0, kLK, 0, 16 * nj, lr, lg);
                 const bf16x8 bd = frag_cols(S.u.t.dM, kLK, 0, 16 * nj, lr, lg);
-                dQ[nj] = mma(fy, bm, dQ[nj]);
-                dK[nj] = mma(fx, bm, dK[nj]);
-                dK[nj] = mma(fw, bd, dK[nj]);
+                dQ[i] = mma(fy, bm, dQ[i]);
+                dK[i] = mma(fx, bm, dK[i]);
+                dK[i] = mma(fw, bd, dK[i]);
             }
             // dP += do Delta^T (scaled later), dA += drhs Delta^T (negated later).
-            const bf16x8 fo = frag_rows(S.u.t.dO, kL32, 16 * w, 0, lr, lg);
-            const bf16x8 fr = frag_rows(S.u.t.dR, kL32, 16 * w, 0, lr, lg);
+            const bf16x8 fo = frag_rows(S.u.t.dO, kL32, 16 * rb, 0, lr, lg);
+            const bf16x8 fr = frag_rows(S.u.t.dR, kL32, 16 * rb, 0, lr, lg);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const bf16x8 bdl = frag_rows(S.u.t.Dh, kL32, 16 * ni, 0, lr, lg);
-                dP[ni] = mma(fo, bdl, dP[ni]);
-                dA[ni] = mma(fr, bdl, dA[ni]);
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 bdl = frag_rows(S.u.t.Dh, kL32, 16 * (2 * h + i), 0, lr, lg);
+                dP[i] = mma(fo, bdl, dP[i]);
+                dA[i] = mma(fr, bdl, dA[i]);
             }
         }
         __syncthreads();
 
         // K K^T and Q K^T again, for the gradients through A and P.
-        f32x4 kk4[4], qk4[4];
+        int lrv = lane & 15, lgv = lane >> 4;
+        asm volatile("" : "+v"(lrv), "+v"(lgv));
+        const int lr = lrv, lg = lgv;
+        f32x4 kk4[2], qk4[2];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            kk4[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-            qk4[ni] = kk4[ni];
+        for (int i = 0; i < 2; ++i) {
+            kk4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            qk4[i] = kk4[i];
 #pragma unroll
             for (int kx = 0; kx < 4; ++kx) {
-                const bf16x8 b = frag_rows(S.K, kLK, 16 * ni, 32 * kx, lr, lg);
-                kk4[ni] = mma(frag_rows(S.K, kLK, 16 * w, 32 * kx, lr, lg), b, kk4[ni]);
-                qk4[ni] = mma(frag_rows(S.Q, kLK, 16 * w, 32 * kx, lr, lg), b, qk4[ni]);
+                const bf16x8 b = frag_rows(S.K, kLK, 16 * (2 * h + i), 32 * kx, lr, lg);
+                kk4[i] = mma(frag_rows(S.K, kLK, 16 * rb, 32 * kx, lr, lg), b, kk4[i]);
+                qk4[i] = mma(frag_rows(S.Q, kLK, 16 * rb, 32 * kx, lr, lg), b, qk4[i]);
             }
         }
-        float cp[4] = {0.f, 0.f, 0.f, 0.f};  // column parts of dgamma, columns 16ni + lr
+        float cp[2] = {0.f, 0.f};  // column parts of dgamma, columns 16(2h + i) + lr
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * lg + r, s = 16 * ni + lr;
+                const int row = 16 * rb + 4 * lg + r, s = 16 * (2 * h + i) + lr;
                 const float d = s <= row ? __expf(S.gam[row] - S.gam[s]) : 0.0f;
-                const float dpv = scale * dP[ni][r];
-                const float dav = -dA[ni][r];
+                const float dpv = scale * dP[i][r];
+                const float dav = -dA[i][r];
                 const bool incl = s <= row, strict = s < row;
                 S.Th[row * kL64 + s] = f2bf(incl ? dpv * d : 0.0f);
                 S.u.S[row * kLF + s] = strict ? S.bt[row] * dav * d : 0.0f;
                 if (strict)
-                    rb[r] += dav * d * kk4[ni][r];
-                const float dDv = (incl ? dpv * qk4[ni][r] : 0.0f) +
-                                  (strict ? S.bt[row] * dav * kk4[ni][r] : 0.0f);
+                    pb[r] += dav * d * kk4[i][r];
+                const float dDv = (incl ? dpv * qk4[i][r] : 0.0f) +
+                                  (strict ? S.bt[row] * dav * kk4[i][r] : 0.0f);
                 const float dDD = incl ? dDv * d : 0.0f;
-                rg[r] += dDD;
-                cp[ni] -= dDD;
+                pg[r] += dDD;
+                cp[i] -= dDD;
             }
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            float x = cp[ni];
+        for (int i = 0; i < 2; ++i) {
+            float x = cp[i];
             x += __shfl_xor(x, 16);
             x += __shfl_xor(x, 32);
             if (lg == 0)
-                S.colpart[w][16 * ni + lr] = x;
-        }
-        S.red[tid] = dgL;
-        __syncthreads();
-        // S + S^T; the row sums.
-        for (int i = tid; i < kC * kC; i += 256) {
-            const int r = i >> 6, s = i & 63;
-            S.Tl[r * kL64 + s] = f2bf(S.u.S[r * kLF + s] + S.u.S[s * kLF + r]);
+                S.colpart[rb][16 * (2 * h + i) + lr] = x;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float xb = row16_sum(rb[r]);
-            const float xg = row16_sum(rg[r]);
+            const float xb = row16_sum(pb[r]);
+            const float xg = row16_sum(pg[r]);
             if (lr == 0) {
-                const int row = 16 * w + 4 * lg + r;
-                if (row < cl.L)
-                    a.dbeta[(cl.p + row) * a.Hv + j] = xb;
-                S.dgam[row] = xg;
+                const int row = 16 * rb + 4 * lg + r;
+                S.rowb[h][row] = xb;
+                S.rowg[h][row] = xg;
             }
         }
+        S.red[tid] = dgL;
         __syncthreads();
+        // S + S^T; dbeta; dgamma with d gamma_L on the last row.
+        for (int i = tid; i < kC * kC; i += kCT) {
+            const int r = i >> 6, c = i & 63;
+            S.Tl[r * kL64 + c] = f2bf(S.u.S[r * kLF + c] + S.u.S[c * kLF + r]);
+        }
         if (w == 0) {
-            // dgamma, plus d gamma_L on the last row; dg is its reverse
-            // cumulative sum (padded rows carry gamma_{L-1}).
             float tot = 0.0f;
-            for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int i = 0; i < kCT / 64; ++i)
                 tot += S.red[64 * i + lane];
             float gl = tot;
             for (int o = 32; o >= 1; o >>= 1)
                 gl += __shfl_xor(gl, o);
-            float dgm = S.dgam[lane] + S.colpart[0][lane] + S.colpart[1][lane] +
-                        S.colpart[2][lane] + S.colpart[3][lane];
+            float dgm = S.rowg[0][lane] + S.rowg[1][lane] + S.colpart[0][lane] +
+                        S.colpart[1][lane] + S.colpart[2][lane] + S.colpart[3][lane];
             if (lane == kC - 1)
                 dgm += gl;
             S.dgam[lane] = dgm;
+            if (lane < cl.L)
+                a.dbeta[(cl.p + lane) * a.Hv + j] = S.rowb[0][lane] + S.rowb[1][lane];
         }
         __syncthreads();
+        // dg: the reverse cumulative sum of dgamma (padded rows carry gamma_{L-1}).
         if (tid < cl.L) {
             float acc = 0.0f;
             for (int r = kC - 1; r >= tid; --r)
@@ -1094,28 +1112,31 @@ __global__ __launch_bounds__(256) void bwd_chunk(BwdArgs a) {
         }
         // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K.
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj)
+        for (int i = 0; i < 4; ++i) {
+            const int nj = 4 * h + i;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const bf16x8 bk = frag_cols(S.K, kLK, 32 * kk, 16 * nj, lr, lg);
                 const bf16x8 bq = frag_cols(S.Q, kLK, 32 * kk, 16 * nj, lr, lg);
-                dQ[nj] = mma(frag_rows(S.Th, kL64, 16 * w, 32 * kk, lr, lg), bk, dQ[nj]);
-                dK[nj] = mma(frag_cols(S.Th, kL64, 32 * kk, 16 * w, lr, lg), bq, dK[nj]);
-                dK[nj] = mma(frag_rows(S.Tl, kL64, 16 * w, 32 * kk, lr, lg), bk, dK[nj]);
+                dQ[i] = mma(frag_rows(S.Th, kL64, 16 * rb, 32 * kk, lr, lg), bk, dQ[i]);
+                dK[i] = mma(frag_cols(S.Th, kL64, 32 * kk, 16 * rb, lr, lg), bq, dK[i]);
+                dK[i] = mma(frag_rows(S.Tl, kL64, 16 * rb, 32 * kk, lr, lg), bk, dK[i]);
             }
+        }
     }
 
     uint16_t *dqo = static_cast<uint16_t *>(a.dq);
     uint16_t *dko = static_cast<uint16_t *>(a.dk_);
 #pragma unroll
-    for (int nj = 0; nj < 8; ++nj)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * w + 4 * lg + r;
+            const int row = 16 * rb + 4 * lg + r;
             if (row < cl.L) {
-                const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)kDK + 16 * nj + lr;
-                dqo[o] = f2bf(dQ[nj][r]);
-                dko[o] = f2bf(dK[nj][r]);
+                const int64_t o =
+                    ((cl.p + row) * a.Hqk + hk) * (int64_t)kDK + 16 * (4 * h + i) + lr;
+                dqo[o] = f2bf(dQ[i][r]);
+                dko[o] = f2bf(dK[i][r]);
             }
         }
 }
@@ -1163,7 +1184,7 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dstate, dim3((unsigned)seq_blocks), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(bwd_chunk, dim3((unsigned)a.n_chunks, (unsigned)a.Hqk), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bwd_chunk, dim3((unsigned)a.n_chunks, (unsigned)a.Hqk), dim3(kCT), 0, stream,
                        a);
     return hipGetLastError();
 }
