@@ -292,8 +292,8 @@ __device__ __forceinline__ void stage_T(uint16_t *Th, uint16_t *Tl, const float 
 // bwd_prep: per (chunk, value head).
 
 __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
-    __shared__ uint16_t Ks[kC * kLK];
-    __shared__ uint16_t Qs[kC * kLK];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kC * kLK];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[kC * kLK];
     __shared__ float Af[kC * kLF];
     __shared__ float Tf[kC * kLF];
     __shared__ float Wf[32 * 33];
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
 // [128 x 16] lives in eight C-layout tiles: tile mt holds rows 16mt ...
 // 16mt + 15, lane (lr, lg) rows 16mt + 4lg + r of column lr.
 
-struct StateSmem {
+struct alignas(16) StateSmem {
     uint16_t K[kC * kLK];
     uint16_t Q[kC * kLK];
     uint16_t X[kC * kL64];      // V (forward) or dO (reverse) tile
@@ -597,24 +597,27 @@ __device__ __forceinline__ void t_times(const uint16_t *Th, const uint16_t *Tl,
 // The two state recurrences, chunks in order (Rev = false: the forward
 // state, writing each chunk's entering state) or in reverse (Rev = true: the
 // state gradient, writing the gradient of each chunk's leaving state; dh0 at
-// the end).  Each chunk's operands are loaded into registers while the
-// previous chunk is computed.
+// the end).  512 threads: waves 0..3 run the recurrence on the chunk in one
+// LDS buffer while waves 4..7 fill the other with the next chunk's operands,
+// whose global loads were issued a chunk earlier; one barrier per chunk.  The
+// two roles run separate loops with the same number of barriers, so the
+// loaders' registers and the state's never share the budget.
 template <bool Rev>
 __device__ __forceinline__ void state_pass(const BwdArgs &a) {
-    __shared__ StateSmem S;
+    __shared__ StateSmem Sb[2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int n_tiles = a.dv / kVT;
     const int tile = blockIdx.x % n_tiles;
     const int j = (blockIdx.x / n_tiles) % a.Hv;
     const int n = blockIdx.x / (n_tiles * a.Hv);
     const int hk = j / (a.Hv / a.Hqk);
-    const int col = tile * kVT + 16 * w + lr;   // this lane's value column
     const int64_t len = seq_len(a, n);
     const int nch = (int)((len + kC - 1) / kC);
     const int64_t base = chunk_base(a, n);
     const int64_t S_elems = (int64_t)kDK * a.dv;
     const float scale = a.scale;
-    auto loc = [&](int c) {
+    auto loc = [&](int it) {
+        const int c = Rev ? nch - 1 - it : it;
         ChunkLoc cl;
         cl.n = n;
         cl.c = c;
@@ -622,7 +625,30 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
         cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
         return cl;
     };
+    auto wslot = [&](int it) { return (base + (Rev ? nch - 1 - it : it)) * a.Hv + j; };
 
+    if (w >= 4) {
+        const int t = tid - 256;
+        StatePre pre;
+        if (nch > 0) {
+            state_issue<Rev>(pre, a, loc(0), hk, j, tile, wslot(0), t);
+            state_commit<Rev>(Sb[0], pre, t);
+            if (nch > 1)
+                state_issue<Rev>(pre, a, loc(1), hk, j, tile, wslot(1), t);
+        }
+        __syncthreads();
+        for (int it = 0; it < nch; ++it) {
+            if (it + 1 < nch) {
+                state_commit<Rev>(Sb[(it + 1) & 1], pre, t);
+                if (it + 2 < nch)
+                    state_issue<Rev>(pre, a, loc(it + 2), hk, j, tile, wslot(it + 2), t);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int col = tile * kVT + 16 * w + lr;   // this lane's value column
     const float *init = Rev ? a.dht : a.h0;
     f32x4 h[8];
 #pragma unroll
@@ -632,24 +658,12 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
             h[mt][r] = init ? init[((int64_t)n * a.Hv + j) * S_elems +
                                    (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
                             : 0.0f;
-    StatePre pre;
-    if (nch > 0) {
-        const int c0 = Rev ? nch - 1 : 0;
-        state_issue<Rev>(pre, a, loc(c0), hk, j, tile, (base + c0) * a.Hv + j, tid);
-    }
+    __syncthreads();
     for (int it = 0; it < nch; ++it) {
-        const int c = Rev ? nch - 1 - it : it;
-        const ChunkLoc cl = loc(c);
-        const int64_t wi = (base + c) * a.Hv + j;
-        state_commit<Rev>(S, pre, tid);
-        __syncthreads();
-        if (it + 1 < nch) {
-            const int cn = Rev ? c - 1 : c + 1;
-            state_issue<Rev>(pre, a, loc(cn), hk, j, tile, (base + cn) * a.Hv + j, tid);
-        }
-        // Forward: the state entering chunk c; reverse: the gradient of the
+        const StateSmem &S = Sb[it & 1];
+        // Forward: the state entering the chunk; reverse: the gradient of the
         // state leaving it.
-        store_state_t((Rev ? a.ws_dhs : a.ws_hs) + wi * S_elems, h, col, lg);
+        store_state_t((Rev ? a.ws_dhs : a.ws_hs) + wslot(it) * S_elems, h, col, lg);
 
         bf16x8 hb[4];
         state_hi(h, hb);
@@ -735,11 +749,11 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
     }
 }
 
-__global__ __launch_bounds__(256) void bwd_fstate(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_fstate(BwdArgs a) {
     state_pass<false>(a);
 }
 
-__global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_dstate(BwdArgs a) {
     state_pass<true>(a);
 }
 
@@ -752,7 +766,7 @@ __global__ __launch_bounds__(256) void bwd_dstate(BwdArgs a) {
 
 constexpr int kCT = 512;   // bwd_chunk threads
 
-struct ChunkSmem {
+struct alignas(16) ChunkSmem {
     uint16_t K[kC * kLK];
     uint16_t Q[kC * kLK];
     uint16_t Th[kC * kL64];     // after the column tiles: dQK
@@ -1178,10 +1192,10 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess)
         return e;
     const int64_t seq_blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kVT);
-    hipLaunchKernelGGL(bwd_fstate, dim3((unsigned)seq_blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_fstate, dim3((unsigned)seq_blocks), dim3(512), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(bwd_dstate, dim3((unsigned)seq_blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dstate, dim3((unsigned)seq_blocks), dim3(512), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     hipLaunchKernelGGL(bwd_chunk, dim3((unsigned)a.n_chunks, (unsigned)a.Hqk), dim3(kCT), 0, stream,
