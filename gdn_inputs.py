@@ -17,7 +17,12 @@ beta = sigmoid(noise); the workloads here use /16 for g):
   * packed lengths are geometric on {1, 2, ...} with the given mean, drawn
     until they cover the total, the last one clipped so the sum is exact;
   * for the backward, the upstream gradients: do ~ N(0, 1) in the input
-    dtype and dht ~ N(0, 0.02) in fp32.
+    dtype and dht ~ N(0, 0.02) in fp32;
+  * for the in-op preparation (make_raw), q and k rows ~ N(0, qk_std) left
+    unnormalised and the raw gate values z ~ N(0, 1) in fp32, before
+    logsigmoid and sigmoid;
+  * for a decode step, one token per sequence of the same recipe and a state
+    cache ~ N(0, 0.5) in fp32 (the scale of a state after a long prefill).
 
 Every tensor draws from its own PCG64 stream spawned from the config seed, so
 a tensor can be drawn in blocks of tokens (and the blocked draw equals the
@@ -121,6 +126,27 @@ def make(B, T, Hqk, Hv, dk, dv, dtype, seed, h0_std=None, cu_seqlens=None):
     }
 
 
+def make_raw(B, T, Hqk, Hv, dk, dv, dtype, seed, qk_std=1.0):
+    """Inputs for a call with in-op preparation: q, k [B, T, Hqk, dk] rows
+    ~ N(0, qk_std), not normalised; v [B, T, Hv, dv] ~ N(0, 1); and the raw
+    gate values g, beta [B, T, Hv] ~ N(0, 1) fp32 (before logsigmoid and
+    sigmoid).  Same dict layout as `make` (no h0, no cu_seqlens)."""
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(dtype)
+    rs = _streams(seed)
+    q = _normal_rows(rs["q"], B * T * Hqk, dk, std=qk_std, out_dtype=dtype)
+    k = _normal_rows(rs["k"], B * T * Hqk, dk, std=qk_std, out_dtype=dtype)
+    v = _normal_rows(rs["v"], B * T * Hv, dv, out_dtype=dtype)
+    zg = rs["g"].standard_normal(B * T * Hv, dtype=np.float32)
+    zb = rs["beta"].standard_normal(B * T * Hv, dtype=np.float32)
+    return {
+        "q": q.reshape(B, T, Hqk, dk), "k": k.reshape(B, T, Hqk, dk),
+        "v": v.reshape(B, T, Hv, dv), "g": zg.reshape(B, T, Hv), "beta": zb.reshape(B, T, Hv),
+        "h0": None, "cu_seqlens": None,
+        "dtype": dtype, "B": B, "T": T, "Hqk": Hqk, "Hv": Hv, "dk": dk, "dv": dv, "N": B,
+    }
+
+
 def make_upstream(d, seed, dht_std=0.02):
     """Upstream gradients for the inputs `d` of `make`: do [B, T, Hv, dv] in
     d's dtype (uint16 bf16 bits or fp32) and dht [N, Hv, dk, dv] fp32, drawn
@@ -144,6 +170,9 @@ CONFIGS = {
                       seed=1003),
     # the headline inputs with upstream gradients, for the backward
     "fwd_bwd_bf16": dict(B=8, T=2048, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", seed=1004),
+    # one decode step: 256 sequences of one token, a 256-slot state cache (h0)
+    "decode_bf16": dict(B=256, T=1, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", seed=1005,
+                        h0_std=0.5),
 }
 
 

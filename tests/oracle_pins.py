@@ -430,3 +430,126 @@ BWD_PINS = [
     pin_bwd_finite_differences, pin_bwd_single_token, pin_bwd_linear_in_upstream,
     pin_bwd_packed_equals_separate, pin_bwd_chunked_route,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Input preparation and the decode step (oracle/prep.py).  Each pin takes `P`,
+# an object with the functions l2_normalize, logsigmoid, sigmoid and step, and
+# `fwd` (the token-by-token C oracle, pinned above), which the step is checked
+# against.
+
+def pin_l2_known_rows(P, fwd):
+    """Rows whose norms are exact: (3, 4) has norm 5, (1, 1, 1, 1) norm 2."""
+    x = np.array([[3.0, 4.0, 0.0, 0.0], [0.0, 0.0, 0.0, -5.0], [1.0, 1.0, 1.0, 1.0],
+                  [0.0, 0.0, 0.0, 0.0], [0.0, -2.0, 0.0, 0.0]])
+    want = np.array([[0.6, 0.8, 0, 0], [0, 0, 0, -1.0], [0.5] * 4, [0.0] * 4, [0, -1.0, 0, 0]])
+    got = P.l2_normalize(x)
+    assert np.allclose(got, want, rtol=0, atol=1e-15), f"normalised rows {got}"
+
+
+def pin_l2_unit_direction_scale(P, fwd):
+    """Random rows: unit norm, the same direction (x . x/|x| = |x|), and
+    invariance under a positive scale; batched over leading axes."""
+    rng = _rng(40)
+    x = rng.standard_normal((3, 5, 2, 64))
+    n = P.l2_normalize(x)
+    assert n.shape == x.shape
+    assert np.allclose(np.linalg.norm(n, axis=-1), 1.0, rtol=0, atol=1e-14), "not unit"
+    assert np.allclose(np.sum(x * n, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-14), \
+        "direction changed"
+    assert np.allclose(P.l2_normalize(3.7 * x), n, rtol=0, atol=1e-15), "scale changes it"
+
+
+def pin_gate_functions(P, fwd):
+    """Closed forms (logsigmoid(0) = -ln 2, sigmoid(ln 3) = 3/4), the identities
+    logsigmoid(x) - logsigmoid(-x) = x and sigmoid(x) + sigmoid(-x) = 1, the
+    link exp(logsigmoid) = sigmoid, no overflow at |x| = 800, and scipy's
+    expit and log_expit."""
+    from scipy.special import expit, log_expit
+    assert abs(P.logsigmoid(0.0) + math.log(2.0)) < 1e-16
+    assert abs(P.sigmoid(math.log(3.0)) - 0.75) < 1e-16
+    x = np.linspace(-30.0, 30.0, 601)
+    ls, s = P.logsigmoid(x), P.sigmoid(x)
+    assert np.allclose(ls - P.logsigmoid(-x), x, rtol=0, atol=1e-13), "logsigmoid identity"
+    assert np.allclose(s + P.sigmoid(-x), 1.0, rtol=0, atol=1e-15), "sigmoid identity"
+    assert np.allclose(np.exp(ls), s, rtol=1e-14, atol=0), "exp(logsigmoid) != sigmoid"
+    assert np.allclose(ls, log_expit(x), rtol=1e-14, atol=1e-300), "logsigmoid vs scipy"
+    assert np.allclose(s, expit(x), rtol=1e-14, atol=1e-300), "sigmoid vs scipy"
+    big = np.array([-800.0, 800.0])
+    assert np.allclose(P.logsigmoid(big), [-800.0, 0.0], rtol=1e-15, atol=1e-300)
+    assert np.array_equal(P.sigmoid(big) > 0.5, [False, True])
+
+
+def pin_step_hand_worked(P, fwd):
+    """dk = dv = 2 by hand: M = [[1, 0], [0, 2]], k = (1, 0), v = (3, 1),
+    q = (1, 1), a = 1/2, beta = 1/2, scale 2.  y = M^T k = (1, 0);
+    delta = (1/2)((3, 1) - (1/2)(1, 0)) = (1.25, 0.5);
+    M' = M/2 + k delta^T = [[1.75, 0.5], [0, 1]]; o = 2 M'^T q = (3.5, 3)."""
+    M = np.array([[[[1.0, 0.0], [0.0, 2.0]]]])
+    o, new = P.step(np.array([[[1.0, 1.0]]]), np.array([[[1.0, 0.0]]]),
+                    np.array([[[3.0, 1.0]]]), np.array([[math.log(0.5)]]),
+                    np.array([[0.5]]), M, scale=2.0)
+    assert np.allclose(new[0, 0], [[1.75, 0.5], [0.0, 1.0]], rtol=0, atol=1e-15), new[0, 0]
+    assert np.allclose(o[0, 0], [3.5, 3.0], rtol=0, atol=1e-15), o[0, 0]
+    assert np.array_equal(M[0, 0], [[1.0, 0.0], [0.0, 2.0]]), "the input cache was modified"
+
+
+def pin_step_chained_equals_token_oracle(P, fwd):
+    """Steps chained over T tokens from h0 (grouped heads) give the outputs
+    and final states of the token-by-token C oracle over the whole rows."""
+    rng = _rng(41)
+    B, T, Hqk, Hv, dk, dv = 3, 7, 2, 4, 8, 6
+    q, k, v, g, beta = _rand_inputs(rng, B, T, Hqk, Hv, dk, dv)
+    h0 = rng.standard_normal((B, Hv, dk, dv)).astype(np.float32)
+    o_ref, h_ref = fwd(q, k, v, g, beta, scale=0.8, h0=h0)
+    cache = h0.astype(np.float64)
+    for t in range(T):
+        o, cache = P.step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], cache, scale=0.8)
+        _close(o, o_ref[:, t], 1e-13, f"step output at token {t}")
+    _close(cache, h_ref, 1e-13, "chained final state")
+
+
+def pin_step_slots_and_padding(P, fwd):
+    """Slots address the cache: a permuted slot list gives each sequence the
+    state of its slot, a padding slot (negative or past the end) starts from
+    zero and writes nothing, and slots not named keep their state."""
+    rng = _rng(42)
+    N, Hqk, Hv, dk, dv, S = 4, 2, 2, 4, 3, 6
+    q, k, v, g, beta = (x[:, 0] for x in _rand_inputs(rng, N, 1, Hqk, Hv, dk, dv))
+    cache = rng.standard_normal((S, Hv, dk, dv))
+    slots = np.array([4, -1, 0, S])
+    o, new = P.step(q, k, v, g, beta, cache, slots=slots)
+    h0 = np.stack([cache[4], np.zeros((Hv, dk, dv)), cache[0], np.zeros((Hv, dk, dv))])
+    o_ref, h_ref = P.step(q, k, v, g, beta, h0)
+    _close(o, o_ref, 1e-15, "slot outputs")
+    _close(new[4], h_ref[0], 1e-15, "slot 4 state")
+    _close(new[0], h_ref[2], 1e-15, "slot 0 state")
+    for s in (1, 2, 3, 5):
+        assert np.array_equal(new[s], cache[s]), f"slot {s} changed"
+    # With a zero state the step is closed form: o = beta (q . k) v, M = beta k v^T.
+    q1, k1, v1, b1 = (np.asarray(x[1], np.float64) for x in (q, k, v, beta))
+    want = b1[:, None] * np.einsum("hd,hd->h", q1, k1)[:, None] * v1
+    _close(o[1], want, 1e-14, "zero-state closed form")
+
+
+def pin_step_options(P, fwd):
+    """The options act on the inputs: raw gates of 0 are a = beta = 1/2; rows
+    scaled by powers of two normalise back to the given unit rows."""
+    rng = _rng(43)
+    N, Hqk, Hv, dk, dv = 2, 1, 1, 16, 4
+    K = _hadamard(dk)[[3, 9]] / 4.0
+    Q = _hadamard(dk)[[5, 12]] / 4.0
+    v = rng.standard_normal((N, Hv, dv))
+    cache = rng.standard_normal((N, Hv, dk, dv))
+    o_ref, h_ref = P.step(Q[:, None], K[:, None], v, np.full((N, Hv), math.log(0.5)),
+                          np.full((N, Hv), 0.5), cache)
+    o, h = P.step(8.0 * Q[:, None], 0.25 * K[:, None], v, np.zeros((N, Hv)),
+                  np.zeros((N, Hv)), cache, use_qk_l2norm=True, gate_activation=True)
+    _close(o, o_ref, 1e-15, "options output")
+    _close(h, h_ref, 1e-15, "options state")
+
+
+PREP_PINS = [
+    pin_l2_known_rows, pin_l2_unit_direction_scale, pin_gate_functions, pin_step_hand_worked,
+    pin_step_chained_equals_token_oracle, pin_step_slots_and_padding, pin_step_options,
+]

@@ -4,7 +4,8 @@ finite differences and closed forms)."""
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS, BWD_PINS
+from oracle import prep
+from oracle_pins import ALL_PINS, BWD_PINS, PREP_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -15,6 +16,11 @@ def test_oracle_pin(pin):
 @pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
 def test_oracle_bwd_pin(pin):
     pin(oracle.gdn_fwd, oracle.gdn_bwd)
+
+
+@pytest.mark.parametrize("pin", PREP_PINS, ids=lambda p: p.__name__)
+def test_oracle_prep_pin(pin):
+    pin(prep, oracle.gdn_fwd)
 
 
 def test_oracle_rejects_bad_arguments():

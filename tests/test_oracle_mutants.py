@@ -110,3 +110,50 @@ def test_bwd_pins_catch_mutant(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no reverse-mode pin catches the mutant {name}"
+
+
+# Mistakes in the preparation and decode step (oracle/prep.py), planted in a
+# copy of its source that is executed as a module of its own.
+PREP_SRC = os.path.join(os.path.dirname(oracle.__file__), "prep.py")
+PREP_MUTANTS = {
+    "l2_sum_of_squares_not_rooted": ("n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))",
+                                     "n = np.sum(x * x, axis=-1, keepdims=True)"),
+    "l2_wrong_axis": ("n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))",
+                      "n = np.sqrt(np.sum(x * x, axis=0, keepdims=True))"),
+    "logsigmoid_negative_branch_sign": ("np.where(x >= 0.0, pos, x + pos)",
+                                        "np.where(x >= 0.0, pos, x - pos)"),
+    "logsigmoid_one_branch": ("np.where(x >= 0.0, pos, x + pos)", "pos"),
+    "sigmoid_negative_branch": ("np.where(x >= 0.0, 1.0 / (1.0 + e), e / (1.0 + e))",
+                                "np.where(x >= 0.0, 1.0 / (1.0 + e), 1.0 / (1.0 + e))"),
+    "step_prediction_not_decayed": ("delta = beta[n, j] * (v[n, j] - a * y)",
+                                    "delta = beta[n, j] * (v[n, j] - y)"),
+    "step_state_not_decayed": ("M = a * M + np.outer(kv, delta)", "M = M + np.outer(kv, delta)"),
+    "step_output_reads_k": ("o[n, j] = scale * (M.T @ qv)", "o[n, j] = scale * (M.T @ kv)"),
+    "step_scale_dropped": ("o[n, j] = scale * (M.T @ qv)", "o[n, j] = (M.T @ qv)"),
+    "step_grouped_heads_interleaved": ("kv, qv = k[n, j // G], q[n, j // G]",
+                                       "kv, qv = k[n, j % Hqk], q[n, j % Hqk]"),
+    "step_padding_reads_a_slot": ("cached = 0 <= s < S", "cached = s < S"),
+    "step_gate_decay_not_log": ("g, beta = logsigmoid(g), sigmoid(beta)",
+                                "g, beta = sigmoid(g), sigmoid(beta)"),
+    "step_l2_keys_only": ("q, k = l2_normalize(q), l2_normalize(k)",
+                          "q, k = q, l2_normalize(k)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREP_MUTANTS))
+def test_prep_pins_catch_mutant(name):
+    import types
+    from oracle_pins import PREP_PINS
+    old, new = PREP_MUTANTS[name]
+    with open(PREP_SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mod = types.ModuleType(f"prep_{name}")
+    exec(compile(src.replace(old, new), f"prep_{name}.py", "exec"), mod.__dict__)
+    caught = []
+    for pin in PREP_PINS:
+        try:
+            pin(mod, oracle.gdn_fwd)
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant {name}"
