@@ -117,6 +117,101 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup):
             "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
 
 
+def _time_calls(torch, stream, call, steps, warmup):
+    """Milliseconds per call over `steps` back-to-back calls on `stream`."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def decode_algorithmic_bytes(N, Hqk, Hv, dk, dv, in_bytes=2):
+    """One decode step: the state read and written once; q, k, v, g, beta
+    read and o written once."""
+    return (N * Hv * dk * dv * 4 * 2 + N * (2 * Hqk * dk + 2 * Hv * dv) * in_bytes
+            + 2 * N * Hv * 4)
+
+
+def measure_decode(gdn, gi, torch, dev, steps, warmup):
+    """The decode step on its workload (256 sequences, one token each, a
+    256-slot fp32 cache): milliseconds per call, tokens/s, HBM roofline
+    fraction, and a check of one call against the fp64 step on 4 sequences."""
+    from oracle import prep
+    name = "decode_bf16"
+    d = gi.make_config(name)
+    N, Hqk, Hv, dk, dv = d["B"], d["Hqk"], d["Hv"], d["dk"], d["dv"]
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x[:, 0]).view(np.int16)).to(dev) \
+        .view(torch.bfloat16)
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    g = torch.from_numpy(np.ascontiguousarray(d["g"][:, 0])).to(dev)
+    beta = torch.from_numpy(np.ascontiguousarray(d["beta"][:, 0])).to(dev)
+    cache = torch.from_numpy(d["h0"]).to(dev)
+    o = torch.empty((N, Hv, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.gdn_recurrent_step(q, k, v, g, beta, cache, out=o,
+                                          stream=stream.cuda_stream)
+    call()
+    torch.cuda.synchronize()
+    sel = [0, 77, 150, 255]
+    ro, rc = prep.step(*(gi.widen(d[x][sel, 0]) for x in ("q", "k", "v")), d["g"][sel, 0],
+                       d["beta"][sel, 0], d["h0"][sel])
+    err_o = float(np.linalg.norm(o[sel].float().cpu().numpy() - ro) / np.linalg.norm(ro))
+    err_c = float(np.linalg.norm(cache[sel].cpu().numpy() - rc) / np.linalg.norm(rc))
+    ms = _time_calls(torch, stream, call, steps, warmup)
+    nbytes = decode_algorithmic_bytes(N, Hqk, Hv, dk, dv)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] decode step {ms * 1e3:.1f} us/call ({achieved:.0f} GB/s); "
+        f"check rel-L2 output {err_o:.2e}, cache {err_c:.2e}")
+    return {"workload": f"{name}: N={N} sequences x 1 token, H={Hv}, dk={dk}, dv={dv}, "
+                        f"bf16 q/k/v/o, fp32 cache of {N} slots",
+            "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3), "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes, "kernels": ["recurrent_step"]},
+            "check": {"sequences": sel, "rel_l2_output": err_o, "rel_l2_cache": err_c}}
+
+
+def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
+    """In-op preparation (q/k L2 norm and gate activations) on the headline
+    tensors: the forward with both options fused into its staging, against
+    the plain forward, and the separate preparation pass (out of place) with
+    its HBM roofline fraction."""
+    stream = torch.cuda.current_stream(q.device)
+    qo, ko, go, bo = (torch.empty_like(x) for x in (q, k, g, beta))
+    lib = gdn.load()
+    dk = q.shape[-1]
+
+    def call():
+        st = lib.gdn_prepare_inputs(1, q.numel() // dk, dk, q.data_ptr(), k.data_ptr(),
+                                    qo.data_ptr(), ko.data_ptr(), g.numel(), g.data_ptr(),
+                                    beta.data_ptr(), go.data_ptr(), bo.data_ptr(),
+                                    gdn.GDN_QK_L2NORM | gdn.GDN_GATE_ACT, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(gdn.gdn_status_string(st))
+    ms = _time_calls(torch, stream, call, steps, warmup)
+    nbytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * (g.numel() + beta.numel()) * 4
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    o = torch.empty_like(vv)
+    ht = torch.empty((q.shape[0], vv.shape[2], q.shape[3], vv.shape[3]), dtype=torch.float32,
+                     device=q.device)
+    fused = lambda: gdn.gdn_chunk_fwd(q, k, vv, g, beta, out=o, final_state=ht,
+                                      stream=stream.cuda_stream, use_qk_l2norm=True,
+                                      gate_activation=True)
+    fused_ms = _time_calls(torch, stream, fused, 1000, 500)
+    log(f"[bench] preparation pass {ms * 1e3:.1f} us/call ({achieved:.0f} GB/s); forward with "
+        f"fused preparation {fused_ms * 1e3:.1f} us (plain {fwd_ms * 1e3:.1f} us)")
+    return {"ms_per_call": ms, "fwd_fused_prep_ms": fused_ms, "fwd_plain_ms": fwd_ms,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes, "kernels": ["preprocess"]}}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -179,6 +274,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step and preparation measurements")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -292,6 +389,12 @@ def main():
         log("[bench] backward")
         bwd = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20)
 
+    decode = prep = None
+    if not args.no_decode:
+        log("[bench] preparation pass and decode step")
+        prep = measure_prep(gdn, torch, q, k, v, g, beta, ms_per_step, steps=200, warmup=50)
+        decode = measure_decode(gdn, gi, torch, dev, steps=200, warmup=100)
+
     baseline = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -337,6 +440,8 @@ def main():
         "cpu_baseline": baseline,
         "check": {"sampled_head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h},
         "bwd": bwd,
+        "prep": prep,
+        "decode": decode,
         "wall_s_timed_region": wall,
     }
     print(json.dumps(result), flush=True)

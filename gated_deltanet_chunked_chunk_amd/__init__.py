@@ -1,5 +1,5 @@
-"""Python binding of libgdn, the chunkwise Gated DeltaNet forward and backward
-for MI355X.
+"""Python binding of libgdn, the chunkwise Gated DeltaNet forward and backward,
+the input preparation and the decode step, for MI355X.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of libgdn.so.  PyTorch provides device memory and the stream.  The
@@ -11,7 +11,8 @@ import ctypes
 import os
 
 __all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd",
-           "gdn_chunk_bwd_workspace_size", "gdn_status_string",
+           "gdn_chunk_bwd_workspace_size", "gdn_prepare_inputs", "gdn_recurrent_step",
+           "GDN_QK_L2NORM", "GDN_GATE_ACT", "gdn_status_string",
            "gdn_last_hip_error", "gdn_version", "GdnError", "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -19,6 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "libgdn.so")
 _lib = None
 
 GDN_F32, GDN_BF16 = 0, 1
+GDN_QK_L2NORM, GDN_GATE_ACT = 1, 2
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_MISALIGNED", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
 
@@ -42,18 +44,25 @@ def load():
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python -m gated_deltanet_chunked_chunk_amd.build`")
     lib = ctypes.CDLL(_LIB_PATH)
-    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P, I32, I64, U32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     lib.gdn_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
-                                  ctypes.c_float, P, P, P, I32, P, P, P, ctypes.c_size_t, P]
+                                  ctypes.c_float, U32, P, P, P, I32, P, P, P, ctypes.c_size_t,
+                                  P]
     lib.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
     lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_chunk_bwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
                                   ctypes.c_float, P, P, P, I32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
+    lib.gdn_prepare_inputs.restype = ctypes.c_int
+    lib.gdn_prepare_inputs.argtypes = [ctypes.c_int, I64, I32, P, P, P, P, I64, P, P, P, P,
+                                       U32, P]
+    lib.gdn_recurrent_step.restype = ctypes.c_int
+    lib.gdn_recurrent_step.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P,
+                                       ctypes.c_float, U32, P, P, I64, P, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_last_hip_error.restype = ctypes.c_int
@@ -140,8 +149,12 @@ def gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, out=None, final_state=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, use_qk_l2norm=False, gate_activation=False):
     """o, ht = gdn_chunk_fwd(q, k, v, g, beta, ...) on the current HIP stream.
+
+    use_qk_l2norm divides q and k by their row norms, and gate_activation
+    takes g and beta as raw values (logsigmoid and sigmoid), both inside the
+    chunk kernel as it stages each chunk; the inputs are left unchanged.
 
     q, k: [B, T, H_qk, dk]; v: [B, T, H_v, dv] (bf16 or fp32, one dtype);
     g, beta: [B, T, H_v] fp32; initial_state: [N, H_v, dk, dv] fp32 or None;
@@ -169,7 +182,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
     st = lib.gdn_chunk_fwd(dt, B, T, Hqk, Hv, dk, dv, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
-                           float(scale), ptr(initial_state), ptr(cu_seqlens),
+                           float(scale), _flags(use_qk_l2norm, gate_activation),
+                           ptr(initial_state), ptr(cu_seqlens),
                            None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
                            N if cu_seqlens is not None else 0, ptr(out), ptr(final_state),
                            ptr(workspace), 0 if workspace is None else workspace.numel(),
@@ -222,3 +236,90 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
     if st != 0:
         _raise(st)
     return dq, dk_, dv_, dg, dbeta, dh0
+
+
+def _flags(use_qk_l2norm, gate_activation):
+    return (GDN_QK_L2NORM if use_qk_l2norm else 0) | (GDN_GATE_ACT if gate_activation else 0)
+
+
+def _device_contiguous(torch, named):
+    for name, t in named:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise GdnError(1, f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise GdnError(1, f"{name} must be contiguous")
+
+
+def gdn_prepare_inputs(q, k, g, beta, use_qk_l2norm=True, gate_activation=False,
+                       in_place=False, stream=None):
+    """(q', k', g', beta') with each q and k row divided by its L2 norm
+    (use_qk_l2norm) and g, beta passed through logsigmoid and sigmoid
+    (gate_activation); what an option does not touch is returned as given.
+    q, k: [..., dk] (bf16 or fp32, dk <= 128); g, beta: fp32 of one shape."""
+    import torch
+    lib = load()
+    _device_contiguous(torch, [("q", q), ("k", k), ("g", g), ("beta", beta)])
+    dt = _dtype_code(torch, q.dtype)
+    if k.dtype != q.dtype or k.shape != q.shape:
+        raise GdnError(1, "q and k must share one shape and dtype")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32 or g.shape != beta.shape:
+        raise GdnError(1, "g and beta must be fp32 of one shape")
+    flags = _flags(use_qk_l2norm, gate_activation)
+    qo, ko, go, bo = q, k, g, beta
+    if use_qk_l2norm and not in_place:
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+    if gate_activation and not in_place:
+        go, bo = torch.empty_like(g), torch.empty_like(beta)
+    if not flags:
+        return qo, ko, go, bo
+    dk = q.shape[-1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.gdn_prepare_inputs(dt, q.numel() // max(dk, 1), dk, q.data_ptr(), k.data_ptr(),
+                                qo.data_ptr(), ko.data_ptr(), g.numel(), g.data_ptr(),
+                                beta.data_ptr(), go.data_ptr(), bo.data_ptr(), flags, stream)
+    if st != 0:
+        _raise(st)
+    return qo, ko, go, bo
+
+
+def gdn_recurrent_step(q, k, v, g, beta, state, scale=1.0, slots=None, use_qk_l2norm=False,
+                       gate_activation=False, out=None, stream=None):
+    """o = gdn_recurrent_step(q, k, v, g, beta, state, ...): one decode token
+    for each of N sequences, the fp32 state cache [n_slots, H_v, dk, dv]
+    updated in place.  q, k: [N, H_qk, dk]; v: [N, H_v, dv]; g, beta:
+    [N, H_v] fp32; slots: int32 [N] device tensor of cache slots (None: slot
+    n; out of range: padding, zero state, nothing kept).  Returns o
+    [N, H_v, dv] in the dtype of q."""
+    import torch
+    lib = load()
+    named = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)]
+    if slots is not None:
+        named.append(("slots", slots))
+    _device_contiguous(torch, named)
+    dt = _dtype_code(torch, q.dtype)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError(1, "q, k and v must share one dtype")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise GdnError(1, "q, k must be [N, H_qk, dk] and v [N, H_v, dv]")
+    N, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if g.dtype != torch.float32 or beta.dtype != torch.float32 or \
+            g.shape != (N, Hv) or beta.shape != (N, Hv):
+        raise GdnError(1, "g and beta must be fp32 [N, H_v]")
+    if state.dtype != torch.float32 or state.dim() != 4 or state.shape[1:] != (Hv, dk, dv):
+        raise GdnError(1, "state must be fp32 [n_slots, H_v, dk, dv]")
+    if slots is not None and (slots.dtype != torch.int32 or slots.shape != (N,)):
+        raise GdnError(1, "slots must be int32 [N]")
+    if out is None:
+        out = torch.empty((N, Hv, dv), dtype=q.dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.gdn_recurrent_step(dt, N, Hqk, Hv, dk, dv, q.data_ptr(), k.data_ptr(),
+                                v.data_ptr(), g.data_ptr(), beta.data_ptr(), float(scale),
+                                _flags(use_qk_l2norm, gate_activation), state.data_ptr(),
+                                None if slots is None else slots.data_ptr(), state.shape[0],
+                                out.data_ptr(), stream)
+    if st != 0:
+        _raise(st)
+    return out

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["gdn_api.cpp", "gdn_fwd_bf16.hip", "gdn_fwd_f32.hip", "gdn_bwd_bf16.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_fwd_bf16.hip", "gdn_fwd_f32.hip", "gdn_bwd_bf16.hip",
+           "gdn_step.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled: the compiler would otherwise form

@@ -40,13 +40,16 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
 
 gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
                          int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float scale, const float *h0,
+                         const float *g, const float *beta, float scale, uint32_t flags,
+                         const float *h0,
                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                          int32_t n_seqs, void *o, float *ht, void *workspace,
                          size_t workspace_bytes, hipStream_t stream) {
     if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
         return GDN_ERR_INVALID_ARG;
     if (!q || !k || !v || !g || !beta || !o)
+        return GDN_ERR_INVALID_ARG;
+    if ((flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
         return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16)
         return GDN_ERR_UNSUPPORTED;
@@ -98,6 +101,7 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.dv = dv;
     a.n_seqs = N;
     a.scale = scale;
+    a.flags = flags;
 
     const hipError_t e = dtype == GDN_BF16 ? gdn::launch_fwd_bf16(a, stream)
                                            : gdn::launch_fwd_f32(a, stream);
@@ -200,6 +204,109 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.scale = scale;
     gdn::bwd_carve(a, workspace);
     const hipError_t e = gdn::launch_bwd_bf16(a, stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, const void *q,
+                              const void *k, void *q_out, void *k_out, int64_t n_gates,
+                              const float *g, const float *beta, float *g_out,
+                              float *beta_out, uint32_t flags, hipStream_t stream) {
+    if ((flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return GDN_ERR_UNSUPPORTED;
+    const bool l2 = flags & GDN_QK_L2NORM, gate = flags & GDN_GATE_ACT;
+    if (l2) {
+        if (n_qk_rows < 0 || n_qk_rows > INT64_MAX / 256 || dk < 1)
+            return GDN_ERR_INVALID_ARG;
+        if (dk > 128)
+            return GDN_ERR_UNSUPPORTED;
+    }
+    if (gate && (n_gates < 0 || n_gates > INT64_MAX / 2))
+        return GDN_ERR_INVALID_ARG;
+    // Pointers of an option with nothing to do are not read.
+    if (l2 && n_qk_rows > 0) {
+        if (!q || !k || !q_out || !k_out)
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out))
+            return GDN_ERR_MISALIGNED;
+    }
+    if (gate && n_gates > 0) {
+        if (!g || !beta || !g_out || !beta_out)
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned16(g) || !aligned16(beta) || !aligned16(g_out) || !aligned16(beta_out))
+            return GDN_ERR_MISALIGNED;
+    }
+    gdn::PrepArgs a;
+    a.q = q;
+    a.k = k;
+    a.q_out = q_out;
+    a.k_out = k_out;
+    a.g = g;
+    a.beta = beta;
+    a.g_out = g_out;
+    a.beta_out = beta_out;
+    a.qk_rows = l2 ? n_qk_rows : 0;
+    a.gate_n = gate ? n_gates : 0;
+    a.dk = dk;
+    a.flags = flags;
+    a.bf16 = dtype == GDN_BF16;
+    const hipError_t e = gdn::launch_preprocess(a, stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_recurrent_step(gdn_dtype dtype, int64_t N, int32_t H_qk, int32_t H_v,
+                              int32_t dk, int32_t dv, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta, float scale,
+                              uint32_t flags, float *state, const int32_t *slots,
+                              int64_t n_slots, void *o, hipStream_t stream) {
+    if (N < 0 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1 || n_slots < 0)
+        return GDN_ERR_INVALID_ARG;
+    if ((flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return GDN_ERR_UNSUPPORTED;
+    if (H_v % H_qk != 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return GDN_ERR_UNSUPPORTED;
+    if (!slots && n_slots < N)
+        return GDN_ERR_INVALID_ARG;
+    const int64_t per_slot = (int64_t)H_v * dk * dv;
+    if (n_slots > INT64_MAX / per_slot || N > INT32_MAX / ((int64_t)H_v * (dv / 64)))
+        return GDN_ERR_INVALID_ARG;
+    if (N == 0)
+        return GDN_OK;  // nothing to do; the pointers are not read
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return GDN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(slots) || !aligned16(o))
+        return GDN_ERR_MISALIGNED;
+    gdn::StepArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.slots = slots;
+    a.o = o;
+    a.N = N;
+    a.n_slots = n_slots;
+    a.Hqk = H_qk;
+    a.Hv = H_v;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = scale;
+    a.flags = flags;
+    a.bf16 = dtype == GDN_BF16;
+    const hipError_t e = gdn::launch_recurrent_step(a, stream);
     if (e != hipSuccess) {
         g_last_hip_error = e;
         return GDN_ERR_HIP;

@@ -268,6 +268,36 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
+// Sum over the 16 lanes of a DPP row: quad xor 1, quad xor 2, the half-row
+// mirror (quad against quad), the row mirror (half against half).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1, 0xF>(x);
+    x += dpp<0x4E, 0xF>(x);
+    x += dpp<0x141, 0xF>(x);
+    x += dpp<0x140, 0xF>(x);
+    return x;
+}
+
+// In-op L2 normalisation of a staged q or k row: the 16 lanes of a DPP row
+// hold its 128 bf16 values, 8 each.  Every value is divided by the row's
+// fp32 norm and rounded back to bf16 (to nearest even).
+__device__ __forceinline__ void l2_normalize_row(u32x4 &x) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(x[e] << 16);
+        f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        s = fmaf(f[e], f[e], s);
+    const float inv = inv_l2_norm(row16_sum(s));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        x[e] = f2bf(f[2 * e] * inv) | (unsigned)f2bf(f[2 * e + 1] * inv) << 16;
+}
+
 // x from the lane of the quad whose index is Sel.
 template <int Sel>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -521,9 +551,16 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
 // during the products below and the state waves' whole next chunk.
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
                                                int lane, int &meet, const FwdArgs &a,
-                                               const Item &it, int next) {
+                                               const Item &it, int L, int next) {
     hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
     const int lr = lane & 15, lg = lane >> 4;
+    if (a.flags & kStepL2Norm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            l2_normalize_row(st.k[i]);
+            l2_normalize_row(st.q[i]);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int at = kq_slot(t / 16 + 16 * i, t % 16);
@@ -535,12 +572,17 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         *reinterpret_cast<u32x4 *>(B.V + v_at(t / 8 + 32 * i, 2 * (t % 8))) = st.v[i];
     if (hw == 3) {
         // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
-        const float x = wave_prefix_sum(st.g);
+        float gv = st.g, bv = st.b;
+        if (a.flags & kStepGateAct) {
+            gv = lane < L ? logsigmoid_f32(gv) : 0.0f;
+            bv = lane < L ? sigmoid_f32(bv) : 0.0f;
+        }
+        const float x = wave_prefix_sum(gv);
         const float gL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
         B.gam[lane] = x;
         B.eg[lane] = __expf(x);
         B.el[lane] = __expf(gL - x);
-        B.bt[lane] = st.b;
+        B.bt[lane] = bv;
         if (lane == 0)
             B.eL = __expf(gL);
     }
@@ -799,7 +841,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         }
     } else if (it.nchunks > 0) {
         stage_load(st, a, it, 0, t, lane);
-        helper_prepare(S, S.buf[0], st, s, t, lane, meet, a, it, it.nchunks > 1 ? 1 : -1);
+        helper_prepare(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+                       it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
 
@@ -808,7 +851,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
             state_chunk(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
             helper_prepare(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
-                           c + 2 < it.nchunks ? c + 2 : -1);
+                           min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
     }

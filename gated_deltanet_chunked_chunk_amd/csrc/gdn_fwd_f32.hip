@@ -86,17 +86,40 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
             S.V[r][c] = r < L ? v[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + c] : 0.0f;
         }
         if (tid == 0) {
+            const bool act = a.flags & kStepGateAct;
             float acc = 0.0f;
             for (int r = 0; r < kC; ++r) {
                 const bool ok = r < L;
-                acc += ok ? a.g[(p + r) * a.Hv + j] : 0.0f;
+                float gv = ok ? a.g[(p + r) * a.Hv + j] : 0.0f;
+                float bv = ok ? a.beta[(p + r) * a.Hv + j] : 0.0f;
+                if (act && ok) {
+                    gv = logsigmoid_f32(gv);
+                    bv = sigmoid_f32(bv);
+                }
+                acc += gv;
                 S.gam[r] = acc;
-                S.bt[r] = ok ? a.beta[(p + r) * a.Hv + j] : 0.0f;
+                S.bt[r] = bv;
             }
             for (int r = 0; r < kC; ++r)
                 S.el[r] = expf(acc - S.gam[r]);
         }
         __syncthreads();
+        if (a.flags & kStepL2Norm) {
+            // In-op L2 normalisation: one wave per row of K or Q (fp32).
+            const int lane = tid & 63;
+            for (int row = tid >> 6; row < 2 * kC; row += kThreads / 64) {
+                float *x = row < kC ? S.K[row] : S.Q[row - kC];
+                float ss = 0.0f;
+                for (int d = lane; d < DK; d += 64)
+                    ss += x[d] * x[d];
+                for (int o = 32; o >= 1; o >>= 1)
+                    ss += __shfl_xor(ss, o);
+                const float inv = inv_l2_norm(ss);
+                for (int d = lane; d < DK; d += 64)
+                    x[d] *= inv;
+            }
+            __syncthreads();
+        }
 
         // A (strictly lower) and P (lower incl. diagonal).
         for (int e = tid; e < kC * kC; e += kThreads) {

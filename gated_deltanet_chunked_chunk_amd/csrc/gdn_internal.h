@@ -6,6 +6,30 @@
 
 namespace gdn {
 
+// Option bits of the forward, the preparation pass and the recurrent step
+// (GDN_QK_L2NORM and GDN_GATE_ACT in gdn.h).
+constexpr uint32_t kStepL2Norm = 1u;
+constexpr uint32_t kStepGateAct = 2u;
+
+// The gate activations, in fp32 with the accurate expf:
+// logsigmoid(x) = min(x, 0) - log(1 + exp(-|x|)) and sigmoid(x), the latter
+// as exp(x) / (1 + exp(x)) for x < 0 so neither form overflows.
+__device__ __forceinline__ float logsigmoid_f32(float x) {
+    return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) {
+    const float e = expf(-fabsf(x));
+    return x >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+}
+
+// 1 / ||x|| from a row's sum of squares, with the hardware reciprocal square
+// root (within 1 ulp; a correctly rounded 1 / sqrt costs the forward kernel's
+// helper waves 8 us more at 8 x 2048 x 16 heads); a zero row stays zero.
+__device__ __forceinline__ float inv_l2_norm(float sumsq) {
+    return sumsq > 0.0f ? __builtin_amdgcn_rsqf(sumsq) : 0.0f;
+}
+
 // Arguments of one forward call, after validation.  Sizes are as in
 // gdn_chunk_fwd; `n_seqs` is the number of sequences (documents, or B).
 struct FwdArgs {
@@ -22,6 +46,7 @@ struct FwdArgs {
     int32_t Hqk, Hv, dk, dv;
     int32_t n_seqs;
     float scale;
+    uint32_t flags;         // kStepL2Norm | kStepGateAct: in-op preparation
 };
 
 // bf16 q/k/v/o, dk = 128, dv a multiple of 64: one workgroup per
@@ -69,5 +94,45 @@ size_t bwd_workspace_bytes(int64_t n_chunks, int32_t Hv, int32_t dk, int32_t dv)
 void bwd_carve(BwdArgs &a, void *workspace);
 
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+
+// One recurrent step for N sequences, the state updated in place in a cache
+// of n_slots states.  Sizes: dk in {64, 128}, dv a multiple of 64.
+struct StepArgs {
+    const void *q;          // [N, Hqk, dk]
+    const void *k;          // [N, Hqk, dk]
+    const void *v;          // [N, Hv, dv]
+    const float *g;         // [N, Hv]
+    const float *beta;      // [N, Hv]
+    float *state;           // [n_slots, Hv, dk, dv]
+    const int32_t *slots;   // [N] cache slot of each sequence, or null (slot n)
+    void *o;                // [N, Hv, dv]
+    int64_t N, n_slots;
+    int32_t Hqk, Hv, dk, dv;
+    float scale;
+    uint32_t flags;
+    bool bf16;
+};
+
+hipError_t launch_recurrent_step(const StepArgs &a, hipStream_t stream);
+
+// Rows of q and k divided by their L2 norms and the gate activations, written
+// to separate outputs (which may be the inputs).  dk <= 128.
+struct PrepArgs {
+    const void *q;
+    const void *k;
+    void *q_out;
+    void *k_out;
+    const float *g;
+    const float *beta;
+    float *g_out;
+    float *beta_out;
+    int64_t qk_rows;        // rows of dk elements in q (and in k)
+    int64_t gate_n;         // elements of g (and of beta)
+    int32_t dk;
+    uint32_t flags;
+    bool bf16;
+};
+
+hipError_t launch_preprocess(const PrepArgs &a, hipStream_t stream);
 
 }  // namespace gdn

@@ -1,6 +1,7 @@
 /*
  * gdn.h -- C ABI of libgdn: the chunkwise Gated DeltaNet forward and its
- * backward on AMD Instinct MI355X (gfx950).
+ * backward, the input preparation and the single-token decode step, on AMD
+ * Instinct MI355X (gfx950).
  *
  * The operation is the gated delta rule of Gated DeltaNet (the December 2024
  * paper by Yang, Kautz and Hatamizadeh that the Qwen FlashQLA article names
@@ -58,6 +59,10 @@ typedef enum {
     GDN_ERR_HIP = 5          /* a HIP launch failed; see gdn_last_hip_error() */
 } gdn_status;
 
+/* Option bits of gdn_chunk_fwd, gdn_prepare_inputs and gdn_recurrent_step. */
+#define GDN_QK_L2NORM 1u /* divide every q and k row (dk elements) by its L2 norm */
+#define GDN_GATE_ACT 2u  /* g and beta arrive raw: g <- logsigmoid(g), beta <- sigmoid(beta) */
+
 typedef enum {
     GDN_F32 = 0,  /* q, k, v and o in IEEE fp32 */
     GDN_BF16 = 1  /* q, k, v and o in bfloat16 (o rounded to nearest even) */
@@ -87,6 +92,17 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   g            [B, T, H_v] fp32, natural-log decay (a = exp(g)); finite.
  *   beta         [B, T, H_v] fp32, write strength.
  *   scale        multiplies the output (1.0 gives o_t = S_t q_t).
+ *   flags        in-op preparation, 0 for none (the inputs are never
+ *                modified):
+ *                GDN_QK_L2NORM  every q and k row is divided by its L2 norm
+ *                               inside the call (use_qk_l2norm of the
+ *                               jax-linear-attention page's "Quick start"),
+ *                               the norm taken in fp32 and, for bf16, the
+ *                               normalised row rounded to bf16 before use,
+ *                               as gdn_prepare_inputs would store it;
+ *                GDN_GATE_ACT   g and beta are raw values: the decay is
+ *                               logsigmoid(g) and the write strength
+ *                               sigmoid(beta).
  *   h0           [N, H_v, dk, dv] fp32 initial states, or NULL for zeros.
  *   cu_seqlens   device int32 [N + 1] document offsets, or NULL (then the
  *                documents are the B rows and N = B).
@@ -109,7 +125,8 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  */
 gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
                          int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float scale, const float *h0,
+                         const float *g, const float *beta, float scale, uint32_t flags,
+                         const float *h0,
                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                          int32_t n_seqs, void *o, float *ht, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
@@ -165,6 +182,74 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
                          int32_t n_seqs, const void *dout, const float *dht, void *dq,
                          void *dk_, void *dv_, float *dg, float *dbeta, float *dh0,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The input preparation the jax-linear-attention page's "Quick start" call
+ * offers in-op (use_qk_l2norm: q and k divided by their L2 norms) and the gate
+ * activations its example applies to raw gate values (g = logsigmoid(raw) as
+ * the natural-log decay, beta = sigmoid(raw) as the write strength).  Run it
+ * before gdn_chunk_fwd or gdn_chunk_bwd on the prepared copies.
+ *
+ *   dtype        dtype of q, k, q_out and k_out.
+ *   n_qk_rows    rows of dk elements in q (and in k), e.g. B * T * H_qk.
+ *   dk           1 <= dk <= 128.
+ *   q, k         inputs; q_out, k_out: outputs of the same size.  With
+ *                GDN_QK_L2NORM each row x becomes x / ||x||_2, the norm taken
+ *                in fp32 and the result rounded to `dtype` (round to nearest
+ *                even); a row of zeros stays zeros.
+ *   n_gates      elements of g (and of beta), e.g. B * T * H_v.
+ *   g, beta      fp32 inputs; g_out, beta_out: fp32 outputs.  With
+ *                GDN_GATE_ACT, g_out = logsigmoid(g), beta_out = sigmoid(beta).
+ *   flags        GDN_QK_L2NORM | GDN_GATE_ACT; the pointers of an option not
+ *                set, or with no rows or gates, may be NULL and are not read.
+ *
+ * Outputs may be their own inputs (in place); other overlaps are undefined.
+ * Every pointer must be 16-byte aligned.  Unknown flag bits return
+ * GDN_ERR_INVALID_ARG.
+ */
+gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, const void *q,
+                              const void *k, void *q_out, void *k_out, int64_t n_gates,
+                              const float *g, const float *beta, float *g_out,
+                              float *beta_out, uint32_t flags, hipStream_t stream);
+
+/*
+ * One token of the recurrence for each of N sequences (decoding), the state
+ * kept in a cache of n_slots states and updated in place: the token-by-token
+ * form the jax-linear-attention page lists under "How it works", one token
+ * per call, with the per-layer recurrent decode state its inference answer
+ * describes.  With M the state of the sequence's slot (as in gdn_chunk_fwd,
+ * element (i, j) couples key dimension i to value dimension j):
+ *
+ *     y = M^T k,  delta = beta (v - a y),  M <- a M + k delta^T,  o = scale M^T q
+ *
+ * with a = exp(g).  The final states of gdn_chunk_fwd ([N, H_v, dk, dv]) are
+ * valid cache entries, so a prefill hands over to decoding directly.
+ *
+ *   dtype        dtype of q, k, v and o.
+ *   N            sequences this step (N = 0 enqueues nothing and reads no
+ *                pointer).
+ *   H_qk, H_v    as for gdn_chunk_fwd (H_v % H_qk == 0).
+ *   dk, dv       each 64 or 128.
+ *   q, k         [N, H_qk, dk]; v: [N, H_v, dv]; g, beta: [N, H_v] fp32.
+ *   scale        multiplies the output.
+ *   flags        GDN_QK_L2NORM: q and k are divided by their L2 norms (fp32,
+ *                not rounded); GDN_GATE_ACT: g and beta are raw values passed
+ *                through logsigmoid and sigmoid.
+ *   state        [n_slots, H_v, dk, dv] fp32 cache, read and written.
+ *   slots        device int32 [N]: the cache slot of each sequence, or NULL
+ *                for slot n (then n_slots >= N).  A slot outside [0, n_slots)
+ *                is padding: that sequence starts from a zero state and
+ *                nothing is written back.  Two sequences of one call must not
+ *                share a slot.
+ *   o            [N, H_v, dv] output.
+ *
+ * Every pointer must be 16-byte aligned; o must not overlap the inputs.
+ */
+gdn_status gdn_recurrent_step(gdn_dtype dtype, int64_t N, int32_t H_qk, int32_t H_v,
+                              int32_t dk, int32_t dv, const void *q, const void *k,
+                              const void *v, const float *g, const float *beta, float scale,
+                              uint32_t flags, float *state, const int32_t *slots,
+                              int64_t n_slots, void *o, hipStream_t stream);
 
 /* A static, human-readable name for a status. */
 const char *gdn_status_string(gdn_status status);

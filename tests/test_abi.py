@@ -44,13 +44,13 @@ def test_workspace_is_zero():
 
 def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
          beta=FAKE, h0=None, cu=None, cu_host=None, n_seqs=0, o=FAKE, ht=None, ws=None,
-         ws_bytes=0):
+         ws_bytes=0, flags=0):
     lib = gdn.load()
     host = None
     if cu_host is not None:
         host = ctypes.cast((ctypes.c_int32 * len(cu_host))(*cu_host), ctypes.c_void_p)
-    return lib.gdn_chunk_fwd(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, h0, cu, host,
-                             n_seqs, o, ht, ws, ws_bytes, None)
+    return lib.gdn_chunk_fwd(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, flags, h0, cu,
+                             host, n_seqs, o, ht, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -58,6 +58,7 @@ def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE
     (dict(g=None), INVALID), (dict(beta=None), INVALID), (dict(o=None), INVALID),
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(Hqk=0), INVALID), (dict(dk=0), INVALID),
     (dict(dtype=7), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(dk=64), UNSUPPORTED),
+    (dict(flags=4), INVALID), (dict(flags=0x100), INVALID),
     (dict(dv=96), UNSUPPORTED), (dict(dtype=0, dk=96), UNSUPPORTED),
     (dict(q=FAKE + 8), MISALIGNED), (dict(o=FAKE + 4), MISALIGNED),
     (dict(h0=FAKE + 2), MISALIGNED), (dict(ht=FAKE + 12), MISALIGNED),
@@ -127,3 +128,58 @@ def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=
 ])
 def test_bwd_rejects_before_launch(kw, status):
     assert bwd_call(**kw) == status
+
+
+def prep_call(dtype=1, rows=4, dk=128, q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, n_gates=4, g=FAKE,
+              beta=FAKE, go=FAKE, bo=FAKE, flags=3):
+    return gdn.load().gdn_prepare_inputs(dtype, rows, dk, q, k, qo, ko, n_gates, g, beta, go,
+                                         bo, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), INVALID), (dict(flags=0x80000001), INVALID),
+    (dict(q=None), INVALID), (dict(ko=None), INVALID), (dict(rows=-1), INVALID),
+    (dict(dk=0), INVALID), (dict(dk=129), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(g=None), INVALID), (dict(bo=None), INVALID), (dict(n_gates=-1), INVALID),
+    (dict(q=FAKE + 4), MISALIGNED), (dict(go=FAKE + 8), MISALIGNED),
+    # Nothing to do (no option, or zero rows and gates) launches nothing.
+    (dict(flags=0), OK), (dict(rows=0, n_gates=0), OK),
+    # An option not set leaves its pointers unread.
+    (dict(flags=1, g=None, beta=None, go=None, bo=None, rows=0), OK),
+    (dict(flags=2, q=None, k=None, qo=None, ko=None, n_gates=0), OK),
+    (dict(rows=0, n_gates=0, q=None, g=None), OK),
+])
+def test_prepare_rejects_before_launch(kw, status):
+    assert prep_call(**kw) == status
+
+
+def step_call(dtype=1, N=2, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+              beta=FAKE, flags=0, state=FAKE, slots=None, n_slots=2, o=FAKE):
+    return gdn.load().gdn_recurrent_step(dtype, N, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, flags,
+                                         state, slots, n_slots, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(state=None), INVALID),
+    (dict(o=None), INVALID), (dict(N=-1), INVALID), (dict(Hqk=0), INVALID),
+    (dict(flags=8), INVALID), (dict(n_slots=1), INVALID), (dict(n_slots=-1), INVALID),
+    (dict(dtype=9), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
+    (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(state=FAKE + 4), MISALIGNED),
+    (dict(slots=FAKE + 4, n_slots=1), MISALIGNED), (dict(o=FAKE + 2), MISALIGNED),
+    (dict(N=1 << 40, n_slots=1 << 40), INVALID),
+    # N = 0 enqueues nothing and reads no pointer.
+    (dict(N=0, n_slots=0), OK), (dict(N=0, n_slots=0, q=None, state=None, o=None), OK),
+    (dict(N=0, dk=96), UNSUPPORTED),
+])
+def test_step_rejects_before_launch(kw, status):
+    assert step_call(**kw) == status
+
+
+def test_step_binding_checks_tensors_on_host():
+    import torch
+    x = torch.zeros(2, 2, 128)
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_recurrent_step(x, x, x, torch.zeros(2, 2), torch.zeros(2, 2),
+                               torch.zeros(2, 2, 128, 128))
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_prepare_inputs(x, x, torch.zeros(2, 2), torch.zeros(2, 2))
