@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "headline_bf16"
-KERNEL_NAME = "gdn_fwd_bf16_dk128"
+KERNEL_NAME = "gdn_fwd_bf16_dk128<false>"
 KERNEL_SOURCES = ["gated_deltanet_chunked_chunk_amd/csrc/gdn_fwd_bf16.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline_bf16.json")
 
@@ -213,10 +213,16 @@ def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
 
 
 def kernel_source_hash():
+    """sha256 of the kernel's code: its source with // comments, trailing
+    blanks and empty lines removed, so editing a comment does not count as a
+    change of the kernel."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -11,13 +11,18 @@
 //                      accumulators for the whole sequence; per chunk it runs
 //                      the state-dependent steps (a5)-(a7).
 //   helper waves 4..7  prepare the next chunk while the state waves work on
-//                      the current one: stage K, Q, V and the gates from HBM
-//                      into LDS, the cumulative decay (a2), the blocks of
-//                      K K^T and Q K^T (a3) and the diagonal inverses (a4).
+//                      the current one: all four stage K, Q, V and the gates
+//                      from HBM into LDS; helper 3 forms the cumulative decay
+//                      (a2); helpers 1..3 the off-diagonal blocks of K K^T
+//                      and Q K^T (a3); helper 0 the diagonal blocks and their
+//                      inverses (a4).
 // Chunk c is read from LDS buffer c % 2 while chunk c + 1 is written into the
-// other, and one workgroup barrier per chunk hands the buffers over.  The
-// helper waves meet once more among themselves per chunk (an LDS counter)
-// between staging and the products that read the staged rows.
+// other, and one LDS-only workgroup barrier per chunk hands the buffers over.
+// The helper waves meet once more among themselves per chunk (an LDS
+// counter) between staging and the products that read the staged rows.
+//
+// The Prep instance also applies the in-op preparation options (q/k rows
+// divided by their L2 norms, gate activations) as the helpers stage a chunk.
 //
 // The chunk equations (derived from the token recurrence
 // S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T of Gated DeltaNet; the
@@ -32,15 +37,18 @@
 // The UT transform is applied by block forward substitution over four
 // 16-row blocks: Delta_i = D_i (diag(beta_i) Y_i - sum_{j<i} A_ij Delta_j)
 // with D_i = (I + A_ii)^-1, so only the four 16 x 16 diagonal inverses are
-// formed explicitly (fp32 forward substitution, one helper wave each).
+// formed explicitly (fp32 forward substitution; one helper wave does all
+// four, one 16-lane row per block).
 //
 // Precision: K, Q, V are exact bf16 and every product accumulates in fp32.
 // Computed operands on the state chain (D_i, A_ij, the right-hand sides,
 // Delta and Delta') enter the MFMA as hi + lo bf16 pairs (x = hi + lo,
 // hi = bf16(x), lo = bf16(x - hi); split-bfloat16, Henry, Tang & Heinecke,
-// ARITH 2019), three products per pair of split operands and two where one
-// side is exact.  K M0, Q M0 and P Delta use hi parts only: their error stays
-// well inside the output tolerance, and K M0's is damped by the solve.
+// ARITH 2019).  In the block substitution a split product A x takes two
+// 32-deep MFMAs whose A operand holds A's (hi | lo) halves, one against
+// (x_hi | x_hi) and one against (x_lo | x_lo), so all four hi/lo terms are
+// summed with no zero padding.  K M0, Q M0 and P Delta use hi parts only: their error
+// stays well inside the output tolerance, and K M0's is damped by the solve.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16)+j] and
 // B[8(l/16)+j][l%16] (j = 0..7), receives C[4(l/16)+r][l%16] (r = 0..3).  A
@@ -549,12 +557,13 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
 // decay tables, A blocks, P and diagonal inverses.  Once `st` is in LDS it is
 // refilled with chunk `next` (if next >= 0), so those loads are in flight
 // during the products below and the state waves' whole next chunk.
+template <bool Prep>
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
     hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
     const int lr = lane & 15, lg = lane >> 4;
-    if (a.flags & kStepL2Norm) {
+    if (Prep && (a.flags & kStepL2Norm)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             l2_normalize_row(st.k[i]);
@@ -573,7 +582,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     if (hw == 3) {
         // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
         float gv = st.g, bv = st.b;
-        if (a.flags & kStepGateAct) {
+        if (Prep && (a.flags & kStepGateAct)) {
             gv = lane < L ? logsigmoid_f32(gv) : 0.0f;
             bv = lane < L ? sigmoid_f32(bv) : 0.0f;
         }
@@ -776,6 +785,9 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     }
 }
 
+// Prep: the in-op preparation options of a.flags are honoured (a separate
+// instance, so the plain kernel carries none of their code).
+template <bool Prep>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     __shared__ Smem S;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -841,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         }
     } else if (it.nchunks > 0) {
         stage_load(st, a, it, 0, t, lane);
-        helper_prepare(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        helper_prepare<Prep>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
                        it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
@@ -850,7 +862,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         if (state) {
             state_chunk(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+            helper_prepare<Prep>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                            min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
@@ -874,7 +886,12 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
         return hipSuccess;
     if (blocks > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gdn_fwd_bf16_dk128, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    if (a.flags)
+        hipLaunchKernelGGL(gdn_fwd_bf16_dk128<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(gdn_fwd_bf16_dk128<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

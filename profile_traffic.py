@@ -118,18 +118,25 @@ def traffic(fetch_dir, write_dir, command):
     print("\n".join(lines))
 
 
-def stats(dirname, command, name="headline_bf16"):
+def stats(dirname, command, name="headline_bf16", title=None, only=()):
     files = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {dirname}")
     with open(files[0], newline="") as f:
         rows = list(csv.DictReader(f))
-    lines = [f"# Kernel time, bench.py ({name}: B=8 T=2048 H=16 d=128 bf16)",
-             "", "Command:", "", "```", command, "```", "",
-             "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    if only:
+        rows = [r for r in rows if any(s in r["Name"] for s in only)]
+    title = title or f"{name}: B=8 T=2048 H=16 d=128 bf16"
+    lines = [f"# Kernel time, bench.py ({title})",
+             "", "Command:", "", "```", command, "```", ""]
+    if only:
+        lines += [f"Kernels whose names contain {', '.join(repr(s) for s in only)}; "
+                  "the percentages are of the whole run's GPU time.", ""]
+    lines += ["| kernel | calls | average µs | min µs | max µs | % of GPU time |",
+              "|---|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"]
-        short = name if len(name) <= 70 else name[:67] + "..."
+        kname = r["Name"]
+        short = kname if len(kname) <= 70 else kname[:67] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
@@ -151,13 +158,16 @@ def main():
     s.add_argument("stats_dir")
     s.add_argument("--command", required=True)
     s.add_argument("--name", default="headline_bf16")
+    s.add_argument("--title", default=None)
+    s.add_argument("--only", action="append", default=[],
+                   help="keep kernels whose name contains this (repeatable)")
     args = ap.parse_args()
     if args.cmd == "launch":
         launch(args.launches)
     elif args.cmd == "traffic":
         traffic(args.fetch_dir, args.write_dir, args.command)
     else:
-        stats(args.stats_dir, args.command, args.name)
+        stats(args.stats_dir, args.command, args.name, args.title, args.only)
 
 
 if __name__ == "__main__":
