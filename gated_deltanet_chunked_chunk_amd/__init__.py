@@ -149,7 +149,8 @@ def gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
 
 def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, out=None, final_state=None,
-                  workspace=None, stream=None, use_qk_l2norm=False, gate_activation=False):
+                  workspace=None, stream=None, use_qk_l2norm=False, gate_activation=False,
+                  pieces=True):
     """o, ht = gdn_chunk_fwd(q, k, v, g, beta, ...) on the current HIP stream.
 
     use_qk_l2norm divides q and k by their row norms, and gate_activation
@@ -161,7 +162,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
     cu_seqlens: int32 [N + 1] device tensor for a packed row (B = 1), with an
     optional host copy (list or CPU tensor) that is then validated.
     Returns (o [B, T, H_v, dv], ht [N, H_v, dk, dv] fp32 or None).  `out`,
-    `final_state` and `workspace` may be given preallocated.
+    `final_state` and `workspace` may be given preallocated.  Long rows with
+    few heads run as a piece-parallel scan in a workspace allocated here
+    (gdn_chunk_fwd_workspace_size bytes); pieces=False runs whole rows.
     """
     import torch
     lib = load()
@@ -176,7 +179,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
     if not output_final_state:
         final_state = None
     ws_bytes = lib.gdn_chunk_fwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
-    if ws_bytes and workspace is None:
+    if not pieces:
+        workspace = None
+    elif ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream

@@ -28,14 +28,52 @@ bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
     return false;
 }
 
+// Pieces per row for the piece-parallel scan of long rows (1: one pass over
+// whole rows).  Batch-mode bf16 calls whose rows x heads x value tiles leave
+// CUs idle are split so that the output pass has about one workgroup per CU,
+// with pieces of at least kMinPieceChunks chunks.
+constexpr int64_t kCUs = 256;
+constexpr int64_t kMinPieceChunks = 16;
+
+struct PiecePlan {
+    int32_t pieces;
+    int64_t piece_len;  // tokens, a multiple of 64
+};
+
+PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk, int32_t dv,
+                      bool packed) {
+    PiecePlan p{1, T};
+    if (packed || dtype != GDN_BF16 || dk != 128 || dv % 64 != 0)
+        return p;
+    const int64_t items = B * H_v * (dv / 64);
+    const int64_t chunks = (T + 63) / 64;
+    int64_t n = kCUs / items;
+    if (n > chunks / kMinPieceChunks)
+        n = chunks / kMinPieceChunks;
+    if (n < 2)
+        return p;
+    const int64_t per = (chunks + n - 1) / n;  // chunks per piece
+    p.piece_len = per * 64;
+    p.pieces = (int32_t)((chunks + per - 1) / per);
+    if (p.pieces < 2)
+        p = PiecePlan{1, T};
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
                                     int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs) {
-    (void)dtype; (void)B; (void)T; (void)H_qk; (void)H_v; (void)dk; (void)dv; (void)n_seqs;
-    return 0;  // the forward kernels keep every intermediate on chip
+    (void)n_seqs;
+    if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || B > INT32_MAX ||
+        !supported(dtype, dk, dv))
+        return 0;
+    // Only the piece scan of long rows stages anything in HBM: the end states
+    // and start states of its pieces.
+    const PiecePlan p = plan_pieces(dtype, B, T, H_v, dk, dv, false);
+    return gdn::fwd_piece_bytes((int32_t)B, p.pieces, H_v, dk, dv);
 }
 
 gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
@@ -80,9 +118,17 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(o) || !aligned16(h0) || !aligned16(ht) || !aligned16(cu_seqlens))
         return GDN_ERR_MISALIGNED;
-    const size_t need = gdn_chunk_fwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, N);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return GDN_ERR_WORKSPACE;
+    // The piece scan runs when a workspace is given; without one, whole rows.
+    PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
+    if (!workspace)
+        plan = PiecePlan{1, T};
+    const size_t need = gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv);
+    if (need > 0) {
+        if (workspace_bytes < need)
+            return GDN_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return GDN_ERR_MISALIGNED;
+    }
 
     gdn::FwdArgs a;
     a.q = q;
@@ -102,6 +148,16 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.n_seqs = N;
     a.scale = scale;
     a.flags = flags;
+    a.pieces = plan.pieces;
+    a.piece_len = plan.piece_len;
+    a.piece_ends = nullptr;
+    a.piece_starts = nullptr;
+    if (plan.pieces > 1) {
+        const size_t per = (size_t)N * (plan.pieces - 1) * H_v * dk;
+        a.piece_ends = static_cast<float *>(workspace);
+        a.piece_starts = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                                   (per * (dv + dk) * 4 + 255) / 256 * 256);
+    }
 
     const hipError_t e = dtype == GDN_BF16 ? gdn::launch_fwd_bf16(a, stream)
                                            : gdn::launch_fwd_f32(a, stream);

@@ -330,8 +330,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 struct Item {
     int64_t p0;      // first token (flattened over the rows)
     int nchunks;
-    int len;         // tokens in the sequence
+    int len;         // tokens in the sequence (or in the piece)
     int j, hk, c0, n;
+    int piece;       // piece of the row (0 without the piece scan)
+    bool ident;      // a transition tile: V = 0, starting from identity columns
 };
 
 // Helper-wave registers holding the next chunk's global data.
@@ -351,10 +353,11 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
     const uint32_t grow = (uint32_t)a.Hv * 4;
     const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (p * a.Hqk + it.hk) * kDK;
     const uint16_t *qb = static_cast<const uint16_t *>(a.q) + (p * a.Hqk + it.hk) * kDK;
-    const uint16_t *vb = static_cast<const uint16_t *>(a.v) + (p * a.Hv + it.j) * a.dv + it.c0;
+    const uint16_t *vb = static_cast<const uint16_t *>(a.v) + (p * a.Hv + it.j) * a.dv +
+                         (it.ident ? 0 : it.c0);
     const __amdgpu_buffer_rsrc_t rk = rsrc(kb, (L - 1) * krow + kDK * 2);
     const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (L - 1) * krow + kDK * 2);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vb, (L - 1) * vrow + kDVT * 2);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vb, it.ident ? 0u : (L - 1) * vrow + kDVT * 2);
     const __amdgpu_buffer_rsrc_t rg = rsrc(a.g + p * a.Hv + it.j, (L - 1) * grow + 4);
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.beta + p * a.Hv + it.j, (L - 1) * grow + 4);
 #pragma unroll
@@ -607,7 +610,9 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     helper_products(S, B, hw, lr, lg, lane);
 }
 
-// State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16).
+// State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
+// without Out only the state advances (the output is not formed).
+template <bool Out>
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
@@ -747,6 +752,8 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         }
     }
 
+    if constexpr (!Out)
+        return;
     // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
     // its own LDS staging area (no other wave touches it).  The staging copy
     // is column-major: lane (g, c) writes its four rows 16 mi + 4 g .. + 3 of
@@ -787,7 +794,12 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 
 // Prep: the in-op preparation options of a.flags are honoured (a separate
 // instance, so the plain kernel carries none of their code).
-template <bool Prep>
+// Mode 0: the output pass, over whole rows or (with a.pieces > 1) over
+// pieces that start from the states of piece_starts.  Mode 1: the piece
+// ends, for every piece but the last: F from a zero start and real V, and
+// (extra "identity" tiles) the transition Phi, the end state of dk unit
+// columns with V = 0; no output is formed.
+template <bool Prep, int Mode>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     __shared__ Smem S;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -795,7 +807,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     // Work item.  Items that read the same q/k head (the dv tiles and the
     // grouped value heads of one q/k head) are kept on one XCD: blocks are
     // dispatched round-robin over the 8 XCDs, so block b runs on XCD b % 8.
-    const int n_tiles = a.dv / kDVT;
+    const int n_val = a.dv / kDVT;
+    const int n_tiles = Mode == 1 ? n_val + kDK / kDVT : n_val;
+    const int np = a.pieces > 1 ? (Mode == 1 ? a.pieces - 1 : a.pieces) : 1;
     const int G = a.Hv / a.Hqk;
     const int gs = n_tiles * G;
     const int nb = gridDim.x;
@@ -807,16 +821,22 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     Item it;
     const int tile = w % n_tiles;
     it.j = (w / n_tiles) % a.Hv;
-    it.n = w / (n_tiles * a.Hv);
+    const int rest = w / (n_tiles * a.Hv);
+    it.piece = rest % np;
+    it.n = rest / np;
     it.hk = it.j / G;
-    it.c0 = tile * kDVT;
+    it.ident = Mode == 1 && tile >= n_val;
+    it.c0 = (it.ident ? tile - n_val : tile) * kDVT;
     int64_t p1;
     if (a.cu) {
         it.p0 = a.cu[it.n];
         p1 = a.cu[it.n + 1];
     } else {
-        it.p0 = (int64_t)it.n * a.T;
-        p1 = it.p0 + a.T;
+        const int64_t row0 = (int64_t)it.n * a.T;
+        const int64_t s0 = a.pieces > 1 ? it.piece * a.piece_len : 0;
+        const int64_t s1 = a.pieces > 1 && it.piece < a.pieces - 1 ? s0 + a.piece_len : a.T;
+        it.p0 = row0 + s0;
+        p1 = row0 + s1;
     }
     it.len = (int)(p1 - it.p0);
     it.nchunks = (it.len + kC - 1) / kC;
@@ -835,64 +855,162 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     const int lg = lane >> 4, lr = lane & 15;
     const int col = it.c0 + 16 * s + lr;
     const int64_t hbase = ((int64_t)it.n * a.Hv + it.j) * kDK * (int64_t)a.dv;
+    // The slot of (row, piece, head) in the piece arrays.
+    const int64_t pslot = ((int64_t)it.n * (a.pieces - 1) + it.piece) * a.Hv + it.j;
 
     f32x4 h[8];
     Stage st;
     int meet = 0;
     if (state) {
-        if (a.h0) {
+        const float *src = nullptr;
+        if (Mode == 0 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
+            src = a.piece_starts + (pslot - a.Hv) * kDK * (int64_t)a.dv;
+        else if (Mode == 0 && a.h0)
+            src = a.h0 + hbase;
+        if (src) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    h[mt][r] = a.h0[hbase + (int64_t)key_of(mt, lg, r) * a.dv + col];
+                    h[mt][r] = src[(int64_t)key_of(mt, lg, r) * a.dv + col];
         } else {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                h[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
         stage_load(st, a, it, 0, t, lane);
         helper_prepare<Prep>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
-                       it.nchunks > 1 ? 1 : -1);
+                             it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
 
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
-            state_chunk(S, S.buf[c & 1], a, it, c, s, lane, h);
+            state_chunk<Mode == 0>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
             helper_prepare<Prep>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
-                           min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
+                                 min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
     }
 
-    if (state && a.ht) {
+    if (state) {
+        float *dst = nullptr;
+        int64_t stride = a.dv, dcol = col;
+        if (Mode == 1) {
+            stride = a.dv + kDK;
+            dst = a.piece_ends + pslot * kDK * stride;
+            dcol = (it.ident ? a.dv : 0) + col;
+        } else if (a.ht && it.piece == np - 1) {
+            dst = a.ht + hbase;
+        }
+        if (dst) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a.ht[hbase + (int64_t)key_of(mt, lg, r) * a.dv + col] = h[mt][r];
+                for (int r = 0; r < 4; ++r)
+                    dst[(int64_t)key_of(mt, lg, r) * stride + dcol] = h[mt][r];
+        }
     }
+}
+
+// The piece scan between the two passes: for row n, head j and value columns
+// [64 y, 64 y + 64), M_0 = h0 (or zero) and M_{p+1} = Phi_p M_p + F_p for
+// p < pieces - 1, written to piece_starts.  The state map of a piece is
+// affine in its start state (the recurrence is linear in S), so this is
+// exact; fp32 with one fused multiply-add per term.  Lane c owns column c
+// and, with its wave, 32 of the dk rows; Phi_p is staged in LDS.
+constexpr int kScanCols = 64;
+
+__global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
+    __shared__ float Ms[kDK][kScanCols + 1];
+    __shared__ __attribute__((aligned(16))) float Ph[kDK][kDK + 4];
+    const int tid = threadIdx.x, c = tid & 63, rg = tid >> 6;
+    const int n = blockIdx.x / a.Hv, j = blockIdx.x % a.Hv;
+    const int cc = blockIdx.y * kScanCols + c;
+    const int64_t hbase = ((int64_t)n * a.Hv + j) * kDK * (int64_t)a.dv;
+    for (int r = 0; r < 32; ++r) {
+        const int i = 32 * rg + r;
+        Ms[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + cc] : 0.0f;
+    }
+    const int64_t estride = a.dv + kDK;
+    for (int p = 0; p + 1 < a.pieces; ++p) {
+        const int64_t pslot = ((int64_t)n * (a.pieces - 1) + p) * a.Hv + j;
+        const float *ends = a.piece_ends + pslot * kDK * estride;
+        __syncthreads();  // the previous step's reads of Ph are done
+        for (int e = tid; e < kDK * kDK / 4; e += 256) {
+            const int row = e / (kDK / 4), q4 = e % (kDK / 4);
+            *reinterpret_cast<f32x4 *>(&Ph[row][4 * q4]) =
+                *reinterpret_cast<const f32x4 *>(ends + row * estride + a.dv + 4 * q4);
+        }
+        float acc[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+            acc[r] = ends[(32 * rg + r) * estride + cc];
+        __syncthreads();
+        for (int k = 0; k < kDK; k += 4) {
+            const float m0 = Ms[k][c], m1 = Ms[k + 1][c], m2 = Ms[k + 2][c], m3 = Ms[k + 3][c];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[32 * rg + r][k]);
+                acc[r] = fmaf(ph[0], m0, acc[r]);
+                acc[r] = fmaf(ph[1], m1, acc[r]);
+                acc[r] = fmaf(ph[2], m2, acc[r]);
+                acc[r] = fmaf(ph[3], m3, acc[r]);
+            }
+        }
+        __syncthreads();  // every read of Ms is done
+        float *out = a.piece_starts + pslot * kDK * (int64_t)a.dv;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            Ms[32 * rg + r][c] = acc[r];
+            out[(int64_t)(32 * rg + r) * a.dv + cc] = acc[r];
+        }
+    }
+}
+
+template <bool Prep>
+hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
+    const int n_val = a.dv / kDVT;
+    if (a.pieces <= 1) {
+        const int64_t blocks = (int64_t)a.n_seqs * a.Hv * n_val;
+        if (blocks > 0x7fffffff)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 0>), dim3((unsigned)blocks), dim3(kThreads),
+                           0, stream, a);
+        return hipGetLastError();
+    }
+    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + kDK / kDVT);
+    const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
+    const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
+    if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 1>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL(piece_scan, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
+                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 0>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv) {
+    if (pieces <= 1)
+        return 0;
+    const size_t per = (size_t)n_seqs * (pieces - 1) * Hv * dk;
+    const size_t ends = (per * (dv + dk) * 4 + 255) / 256 * 256;
+    return ends + per * dv * 4;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
-    const int n_tiles = a.dv / kDVT;
-    const int64_t blocks = (int64_t)a.n_seqs * a.Hv * n_tiles;
-    if (blocks <= 0)
+    if ((int64_t)a.n_seqs * a.Hv <= 0)
         return hipSuccess;
-    if (blocks > 0x7fffffff)
-        return hipErrorInvalidValue;
-    if (a.flags)
-        hipLaunchKernelGGL(gdn_fwd_bf16_dk128<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL(gdn_fwd_bf16_dk128<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
-    return hipGetLastError();
+    return a.flags ? launch_passes<true>(a, stream) : launch_passes<false>(a, stream);
 }
 
 }  // namespace gdn

@@ -47,7 +47,17 @@ struct FwdArgs {
     int32_t n_seqs;
     float scale;
     uint32_t flags;         // kStepL2Norm | kStepGateAct: in-op preparation
+    // Piece-parallel scan of long rows (batch mode only; pieces <= 1: off).
+    // Row n is split into `pieces` runs of piece_len tokens (a multiple of
+    // 64; the last takes the rest).
+    int32_t pieces;
+    int64_t piece_len;
+    float *piece_ends;      // [n_seqs, pieces - 1, Hv, dk, dv + dk]: F | Phi of each piece but the last
+    float *piece_starts;    // [n_seqs, pieces - 1, Hv, dk, dv]: the state entering pieces 1..
 };
+
+// Workspace bytes of the piece scan for `pieces` pieces per row.
+size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv);
 
 // bf16 q/k/v/o, dk = 128, dv a multiple of 64: one workgroup per
 // (sequence, value head, 64 value columns).

@@ -69,11 +69,19 @@ typedef enum {
 } gdn_dtype;
 
 /*
- * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 when it
- * needs none; the pointer may then be NULL).  Returns 0 as well for sizes the
- * forward would reject, so validate through gdn_chunk_fwd.
+ * Bytes of device workspace gdn_chunk_fwd can use for these sizes (0 when it
+ * uses none).  Only the piece scan of long rows uses a workspace: batch-mode
+ * bf16 calls with so few rows x heads that most compute units would idle are
+ * split along the rows into pieces that run in parallel (the exact piece
+ * scan the jax-linear-attention page names under "Where we lose": each
+ * piece's end state is an affine map of its start state, F + Phi S, so the
+ * start states follow from a short scan over the pieces, then every piece
+ * is run again from its true start).  The workspace holds, per piece but the
+ * last and head, F and Phi (dk x (dv + dk) fp32) and the start state
+ * (dk x dv fp32).  Returns 0 as well for sizes the forward would reject.
  *
- * n_seqs: the number of documents when cu_seqlens will be passed, else B.
+ * n_seqs: the number of documents when cu_seqlens will be passed, else B
+ * (packed calls never use the piece scan).
  */
 size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
                                     int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs);
@@ -115,9 +123,11 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   n_seqs       N when cu_seqlens is given (>= 1); ignored otherwise.
  *   o            [B, T, H_v, dv] output, dtype `dtype`.
  *   ht           [N, H_v, dk, dv] fp32 final states, or NULL to skip them.
- *   workspace    device scratch of at least gdn_chunk_fwd_workspace_size()
- *                bytes, 256-byte aligned, owned by the caller and not read
- *                after the call's work completes.
+ *   workspace    device scratch of gdn_chunk_fwd_workspace_size() bytes,
+ *                256-byte aligned, owned by the caller and not read after the
+ *                call's work completes; or NULL, which runs whole rows (the
+ *                same result up to rounding).  A non-NULL workspace that is
+ *                smaller than the query returns GDN_ERR_WORKSPACE.
  *   stream       HIP stream to enqueue on (NULL = the default stream).
  *
  * Every pointer must be 16-byte aligned.  o and ht must not overlap the

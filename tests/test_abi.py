@@ -40,6 +40,34 @@ def test_status_strings_and_version():
 
 def test_workspace_is_zero():
     assert gdn.gdn_chunk_fwd_workspace_size(1, 8, 2048, 16, 16, 128, 128, 8) == 0
+    # fp32, short rows, and sizes the forward rejects use no workspace either.
+    assert gdn.gdn_chunk_fwd_workspace_size(0, 1, 1 << 20, 1, 1, 128, 128, 1) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1000, 1, 1, 128, 128, 1) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1 << 20, 2, 3, 128, 128, 1) == 0
+
+
+def piece_bytes(B, pieces, Hv, dk, dv):
+    per = B * (pieces - 1) * Hv * dk
+    return -(-per * (dv + dk) * 4 // 256) * 256 + per * dv * 4
+
+
+def test_piece_scan_workspace():
+    """Long rows with few heads: one output-pass workgroup per CU, pieces of
+    at least 16 chunks.  The long row (1 x 1,064,960 tokens, 16 heads, two
+    64-column tiles) splits into 8 pieces of 2,080 chunks."""
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 128, 128, 1) == \
+        piece_bytes(1, 8, 16, 128, 128)
+    # 65 chunks, 4 items: min(256 / 4, 65 // 16) = 4 pieces of 17 chunks.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 128, 1) == \
+        piece_bytes(1, 4, 2, 128, 128)
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == \
+        piece_bytes(2, 2, 1, 128, 64)
+
+
+def test_piece_scan_workspace_checked_before_launch():
+    need = gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 128, 1)
+    assert call(T=4133, Hqk=1, Hv=2, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert call(T=4133, Hqk=1, Hv=2, ws=FAKE + 16, ws_bytes=need) == MISALIGNED
 
 
 def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,

@@ -106,8 +106,9 @@ def test_chained_halves():
 
 def test_long_row_full_size():
     """The long row (T = 1,064,960; 16,640 chunks per head) at full size: run
-    whole and as two chained halves (equal bitwise: the halves split at a chunk
-    boundary), and both compared with the oracle on two sampled heads."""
+    whole (the piece scan: 8 pieces per head) and as two chained halves (8
+    pieces each), which agree within tolerance, and compared with the oracle
+    on two sampled heads; the whole row without the piece scan agrees too."""
     import gated_deltanet_chunked_chunk_amd as gdn
     c = gi.CONFIGS["long_bf16"]
     B, T, H, dk, dv = c["B"], c["T"], c["Hv"], c["dk"], c["dv"]
@@ -120,15 +121,22 @@ def test_long_row_full_size():
     o1, h1 = gdn.gdn_chunk_fwd(q[:, :s], k[:, :s], v[:, :s], g[:, :s], beta[:, :s])
     o2, h2 = gdn.gdn_chunk_fwd(q[:, s:], k[:, s:], v[:, s:], g[:, s:], beta[:, s:],
                                initial_state=h1)
+    o3, h3 = gdn.gdn_chunk_fwd(q, k, v, g, beta, pieces=False)
     torch.cuda.synchronize()
-    assert torch.equal(o[:, :s], o1) and torch.equal(o[:, s:], o2) and torch.equal(ht, h2)
+    tol_o, tol_h = TOL["bf16"]
+    f = lambda x: x.float().cpu().numpy()
+    e_halves = (rel_l2(f(torch.cat([o1, o2], dim=1)), f(o)), rel_l2(f(h2), f(ht)))
+    e_serial = (rel_l2(f(o3), f(o)), rel_l2(f(h3), f(ht)))
+    print(f"  halves vs whole {e_halves[0]:.2e} {e_halves[1]:.2e}; whole rows vs pieces "
+          f"{e_serial[0]:.2e} {e_serial[1]:.2e}", flush=True)
+    assert e_halves[0] <= tol_o and e_halves[1] <= tol_h
+    assert e_serial[0] <= tol_o and e_serial[1] <= tol_h
     heads = gi.sampled_heads(c["seed"], H)
     sel = lambda x: x[:, :, heads].float().cpu().numpy()
     ro, rht = run_oracle({"q": sel(q), "k": sel(k), "v": sel(v), "g": sel(g), "beta": sel(beta),
                           "h0": None, "cu_seqlens": None})
     eo = rel_l2(sel(o), ro)
     eh = rel_l2(ht[:, heads].cpu().numpy(), rht)
-    tol_o, tol_h = TOL["bf16"]
     print(f"  heads {heads}: rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} "
           f"(tol {tol_h:.0e})", flush=True)
     assert eo <= tol_o and eh <= tol_h
@@ -167,3 +175,64 @@ def test_no_final_state_and_preallocated_output():
     assert ht is None and o.data_ptr() == out.data_ptr()
     ro, _ = run_oracle(d)
     assert rel_l2(o.float().cpu().numpy(), ro) <= TOL["bf16"][0]
+
+
+PIECE_CASES = [
+    # B, T, Hqk, Hv, dv, h0 std, pieces the host plan picks
+    (1, 4096 + 37, 1, 2, 128, 0.1, 4),  # ragged last piece, grouped heads
+    (2, 3000, 1, 1, 64, 0.1, 2),        # two rows, dv = 64
+    (1, 2048, 1, 1, 128, None, 2),      # pieces of exactly 16 chunks
+]
+
+
+@pytest.mark.parametrize("case", PIECE_CASES, ids=lambda c: f"B{c[0]}-T{c[1]}-dv{c[4]}")
+def test_piece_scan_matches_oracle(case):
+    """The piece scan (zero-start ends and transitions, the scan of start
+    states, the output pass) against the oracle and against whole rows."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    B, T, Hqk, Hv, dv, h0_std, pieces = case
+    lib = gdn.load()
+    need = lib.gdn_chunk_fwd_workspace_size(1, B, T, Hqk, Hv, 128, dv, B)
+    per = B * (pieces - 1) * Hv * 128
+    assert need == -(-per * (dv + 128) * 4 // 256) * 256 + per * dv * 4
+    d = gi.make(B, T, Hqk, Hv, 128, dv, "bf16", 3900 + T, h0_std=h0_std)
+    check(d, scale=0.8, label=f"piece scan, {pieces} pieces")
+    o1, h1 = run_gpu(d, scale=0.8)
+    from gpu_util import to_device
+    t = to_device(d)
+    o2, h2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=0.8,
+                               initial_state=t["h0"], pieces=False)
+    tol_o, tol_h = TOL["bf16"]
+    assert rel_l2(o1, o2.float().cpu().numpy()) <= tol_o
+    assert rel_l2(h1, h2.cpu().numpy()) <= tol_h
+
+
+def test_piece_scan_carries_state():
+    """No decay and a weak write (g = 0, beta = 0.02): each piece's transition
+    stays near the identity, so the start states the scan hands over carry
+    most of the result; 4 pieces of 17 chunks, a large initial state."""
+    d = gi.make(1, 4096 + 37, 1, 2, 128, 128, "bf16", 3950, h0_std=1.0)
+    d["g"] = np.zeros_like(d["g"])
+    d["beta"] = np.full_like(d["beta"], 0.02)
+    check(d, label="piece scan, g = 0, beta = 0.02")
+
+
+def test_piece_scan_with_in_op_preparation():
+    import gated_deltanet_chunked_chunk_amd as gdn
+    import oracle
+    from oracle import prep
+    from gpu_util import to_device
+    d = gi.make_raw(1, 4096 + 37, 1, 2, 128, 128, "bf16", 3960, qk_std=2.0)
+    print("[gpu case] piece scan with in-op preparation", flush=True)
+    t = to_device(d)
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], use_qk_l2norm=True,
+                              gate_activation=True)
+    torch.cuda.synchronize()
+    qn, kn = (gi.widen(gi.bf16_bits(prep.l2_normalize(gi.widen(d[x])).astype(np.float32)))
+              for x in ("q", "k"))
+    ro, rht = oracle.gdn_fwd(qn, kn, gi.widen(d["v"]), prep.logsigmoid(d["g"]).astype(np.float32),
+                             prep.sigmoid(d["beta"]).astype(np.float32))
+    tol_o, tol_h = TOL["bf16"]
+    eo, eh = rel_l2(o.float().cpu().numpy(), ro), rel_l2(ht.cpu().numpy(), rht)
+    print(f"  rel-L2 output {eo:.3e}, state {eh:.3e}", flush=True)
+    assert eo <= tol_o and eh <= tol_h
