@@ -212,6 +212,34 @@ def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
                          "algorithmic_bytes_per_call": nbytes, "kernels": ["preprocess"]}}
 
 
+def measure_long(gdn, gi, torch, dev, steps=3):
+    """The long row (B=1, T=1,064,960, H=16, d=128, bf16; inputs drawn on the
+    device with the same recipe): milliseconds per forward with the piece
+    scan and with whole rows, and the HBM roofline fraction of each."""
+    c = gi.CONFIGS["long_bf16"]
+    B, T, Hqk, Hv, dk, dv = c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"]
+    t = gi.make_device(B, T, Hqk, Hv, dk, dv, c["seed"], device=dev)
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    o = torch.empty_like(v)
+    ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {"workload": f"long_bf16: B={B} T={T} H={Hv} dk={dk} dv={dv}, zero initial state"}
+    nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
+    for name, kw in (("pieces", dict(workspace=ws)), ("whole_rows", dict(pieces=False))):
+        call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht,
+                                         stream=stream.cuda_stream, **kw)
+        ms = _time_calls(torch, stream, call, steps, 1)
+        out[name] = {"ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"[bench] long row, {name}: {ms:.2f} ms/call")
+    out["algorithmic_bytes_per_call"] = nbytes
+    del q, k, v, g, beta, o, t
+    torch.cuda.empty_cache()
+    return out
+
+
 def kernel_source_hash():
     """sha256 of the kernel's code: its source with // comments, trailing
     blanks and empty lines removed, so editing a comment does not count as a
@@ -282,6 +310,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step and preparation measurements")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-row measurement")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -401,6 +430,11 @@ def main():
         prep = measure_prep(gdn, torch, q, k, v, g, beta, ms_per_step, steps=200, warmup=50)
         decode = measure_decode(gdn, gi, torch, dev, steps=200, warmup=100)
 
+    long_row = None
+    if not args.no_long:
+        log("[bench] long row")
+        long_row = measure_long(gdn, gi, torch, dev)
+
     baseline = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -448,6 +482,7 @@ def main():
         "bwd": bwd,
         "prep": prep,
         "decode": decode,
+        "long_row": long_row,
         "wall_s_timed_region": wall,
     }
     print(json.dumps(result), flush=True)

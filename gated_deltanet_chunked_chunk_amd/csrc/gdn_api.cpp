@@ -29,11 +29,17 @@ bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
 }
 
 // Pieces per row for the piece-parallel scan of long rows (1: one pass over
-// whole rows).  Batch-mode bf16 calls whose rows x heads x value tiles leave
-// CUs idle are split so that the output pass has about one workgroup per CU,
-// with pieces of at least kMinPieceChunks chunks.
+// whole rows), for batch-mode bf16 calls.  With P pieces the first pass runs
+// (P - 1) pieces x (value tiles + dk / 64 transition tiles) workgroups and
+// the output pass P pieces x value tiles, each workgroup walking about
+// chunks / P chunks; one workgroup per CU is resident.  The plan minimises
+// rounds x chunks per piece over P, with a first-pass chunk costing
+// kEndsCost of an output-pass chunk (measured on the long row), and is used
+// only when it beats whole rows by a tenth.  Pieces hold at least
+// kMinPieceChunks chunks.
 constexpr int64_t kCUs = 256;
 constexpr int64_t kMinPieceChunks = 16;
+constexpr double kEndsCost = 0.8;
 
 struct PiecePlan {
     int32_t pieces;
@@ -42,22 +48,28 @@ struct PiecePlan {
 
 PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk, int32_t dv,
                       bool packed) {
-    PiecePlan p{1, T};
+    PiecePlan best{1, T};
     if (packed || dtype != GDN_BF16 || dk != 128 || dv % 64 != 0)
-        return p;
-    const int64_t items = B * H_v * (dv / 64);
+        return best;
+    const int64_t rows = B * H_v;
+    const int64_t items = rows * (dv / 64);
+    const int64_t items_ends = rows * (dv / 64 + dk / 64);
     const int64_t chunks = (T + 63) / 64;
-    int64_t n = kCUs / items;
-    if (n > chunks / kMinPieceChunks)
-        n = chunks / kMinPieceChunks;
-    if (n < 2)
-        return p;
-    const int64_t per = (chunks + n - 1) / n;  // chunks per piece
-    p.piece_len = per * 64;
-    p.pieces = (int32_t)((chunks + per - 1) / per);
-    if (p.pieces < 2)
-        p = PiecePlan{1, T};
-    return p;
+    const auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+    const double whole = rounds(items) * (double)chunks;
+    double best_cost = 0.9 * whole;
+    const int64_t max_p = chunks / kMinPieceChunks < 256 ? chunks / kMinPieceChunks : 256;
+    for (int64_t n = 2; n <= max_p; ++n) {
+        const int64_t per = (chunks + n - 1) / n;
+        const int64_t pieces = (chunks + per - 1) / per;
+        const double cost = (rounds((pieces - 1) * items_ends) * kEndsCost +
+                             rounds(pieces * items)) * (double)per;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = PiecePlan{(int32_t)pieces, per * 64};
+        }
+    }
+    return best;
 }
 
 }  // namespace

@@ -344,6 +344,8 @@ struct Stage {
     float g, b;   // row = lane
 };
 
+// Without Full (the piece ends, which form no output) Q is not loaded.
+template <bool Full>
 __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const Item &it, int c,
                                            int t, int lane) {
     const int64_t p = it.p0 + (int64_t)kC * c;
@@ -364,7 +366,8 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
     for (int i = 0; i < 4; ++i) {
         const uint32_t off = (t / 16 + 16 * i) * krow + 16 * (t % 16);
         st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        if (Full)
+            st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -503,6 +506,8 @@ __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int
 // The per-chunk products, split over the helper waves: helper 0 forms the
 // four diagonal blocks of A and their inverses; helpers 1 .. 3 form the
 // off-diagonal blocks of A and the blocks of P (six, five and five blocks).
+// Without WithP (no output is formed) the P blocks are skipped.
+template <bool WithP>
 __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg, int lane) {
     const KqBase kb = kq_base(lr, lg);
     if (hw == 0) {
@@ -523,12 +528,15 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
         load_block(q, B.Q, kb, 0);
         load_block(kj[1], B.K, kb, 1);
         a_block<3, 0>(B, k3, kj[0], lr, lg);
-        p_block<0, 0>(B, q, kj[0], lr, lg);
+        if constexpr (WithP)
+            p_block<0, 0>(B, q, kj[0], lr, lg);
         load_block(q, B.Q, kb, 1);
         a_block<3, 1>(B, k3, kj[1], lr, lg);
-        p_block<1, 0>(B, q, kj[0], lr, lg);
+        if constexpr (WithP)
+            p_block<1, 0>(B, q, kj[0], lr, lg);
         load_block(kj[0], B.K, kb, 2);
-        p_block<1, 1>(B, q, kj[1], lr, lg);
+        if constexpr (WithP)
+            p_block<1, 1>(B, q, kj[1], lr, lg);
         a_block<3, 2>(B, k3, kj[0], lr, lg);
     } else if (hw == 2) {  // A20 A21, P20 P21 P22
         bf16x8 k2[4], q2[4], kj[2][4];
@@ -537,10 +545,13 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
         load_block(kj[0], B.K, kb, 0);
         load_block(kj[1], B.K, kb, 1);
         a_block<2, 0>(B, k2, kj[0], lr, lg);
-        p_block<2, 0>(B, q2, kj[0], lr, lg);
+        if constexpr (WithP)
+            p_block<2, 0>(B, q2, kj[0], lr, lg);
         a_block<2, 1>(B, k2, kj[1], lr, lg);
-        p_block<2, 1>(B, q2, kj[1], lr, lg);
-        p_block<2, 2>(B, q2, k2, lr, lg);
+        if constexpr (WithP)
+            p_block<2, 1>(B, q2, kj[1], lr, lg);
+        if constexpr (WithP)
+            p_block<2, 2>(B, q2, k2, lr, lg);
     } else {  // A10, P30 P31 P32 P33
         bf16x8 k1[4], q3[4], kj[2][4];
         load_block(k1, B.K, kb, 1);
@@ -548,11 +559,15 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
         load_block(kj[0], B.K, kb, 0);
         load_block(kj[1], B.K, kb, 2);
         a_block<1, 0>(B, k1, kj[0], lr, lg);
-        p_block<3, 0>(B, q3, kj[0], lr, lg);
-        p_block<3, 1>(B, q3, k1, lr, lg);
+        if constexpr (WithP)
+            p_block<3, 0>(B, q3, kj[0], lr, lg);
+        if constexpr (WithP)
+            p_block<3, 1>(B, q3, k1, lr, lg);
         load_block(kj[0], B.K, kb, 3);
-        p_block<3, 2>(B, q3, kj[1], lr, lg);
-        p_block<3, 3>(B, q3, kj[0], lr, lg);
+        if constexpr (WithP)
+            p_block<3, 2>(B, q3, kj[1], lr, lg);
+        if constexpr (WithP)
+            p_block<3, 3>(B, q3, kj[0], lr, lg);
     }
 }
 
@@ -560,7 +575,7 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
 // decay tables, A blocks, P and diagonal inverses.  Once `st` is in LDS it is
 // refilled with chunk `next` (if next >= 0), so those loads are in flight
 // during the products below and the state waves' whole next chunk.
-template <bool Prep>
+template <bool Prep, bool Full>
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
@@ -570,14 +585,16 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             l2_normalize_row(st.k[i]);
-            l2_normalize_row(st.q[i]);
+            if (Full)
+                l2_normalize_row(st.q[i]);
         }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int at = kq_slot(t / 16 + 16 * i, t % 16);
         *reinterpret_cast<u32x4 *>(B.K + at) = st.k[i];
-        *reinterpret_cast<u32x4 *>(B.Q + at) = st.q[i];
+        if (Full)
+            *reinterpret_cast<u32x4 *>(B.Q + at) = st.q[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -603,11 +620,11 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     if (lane == 0)
         __hip_atomic_fetch_add(&S.hsync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (next >= 0)
-        stage_load(st, a, it, next, t, lane);
+        stage_load<Full>(st, a, it, next, t, lane);
     while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
         __builtin_amdgcn_s_sleep(1);
 
-    helper_products(S, B, hw, lr, lg, lane);
+    helper_products<Full>(S, B, hw, lr, lg, lane);
 }
 
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
@@ -881,8 +898,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
-        stage_load(st, a, it, 0, t, lane);
-        helper_prepare<Prep>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        stage_load<Mode == 0>(st, a, it, 0, t, lane);
+        helper_prepare<Prep, Mode == 0>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
                              it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
@@ -891,7 +908,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         if (state) {
             state_chunk<Mode == 0>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare<Prep>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+            helper_prepare<Prep, Mode == 0>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();

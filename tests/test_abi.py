@@ -52,16 +52,20 @@ def piece_bytes(B, pieces, Hv, dk, dv):
 
 
 def test_piece_scan_workspace():
-    """Long rows with few heads: one output-pass workgroup per CU, pieces of
-    at least 16 chunks.  The long row (1 x 1,064,960 tokens, 16 heads, two
+    """Long rows with few heads are split into pieces (at least 16 chunks
+    each) where the planner's cost (workgroup rounds x chunks per piece)
+    beats whole rows.  The long row (1 x 1,064,960 tokens, 16 heads, two
     64-column tiles) splits into 8 pieces of 2,080 chunks."""
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 128, 128, 1) == \
         piece_bytes(1, 8, 16, 128, 128)
-    # 65 chunks, 4 items: min(256 / 4, 65 // 16) = 4 pieces of 17 chunks.
+    # 65 chunks, 2 heads: 4 pieces of 17 chunks (the last 14).
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 128, 1) == \
         piece_bytes(1, 4, 2, 128, 128)
-    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == \
-        piece_bytes(2, 2, 1, 128, 64)
+    # 94 chunks, two rows, dv = 64: 5 pieces of 19 chunks.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 6000, 1, 1, 128, 64, 2) == \
+        piece_bytes(2, 5, 1, 128, 64)
+    # Short rows do not gain enough: whole rows, no workspace.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == 0
 
 
 def test_piece_scan_workspace_checked_before_launch():

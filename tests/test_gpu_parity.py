@@ -180,8 +180,8 @@ def test_no_final_state_and_preallocated_output():
 PIECE_CASES = [
     # B, T, Hqk, Hv, dv, h0 std, pieces the host plan picks
     (1, 4096 + 37, 1, 2, 128, 0.1, 4),  # ragged last piece, grouped heads
-    (2, 3000, 1, 1, 64, 0.1, 2),        # two rows, dv = 64
-    (1, 2048, 1, 1, 128, None, 2),      # pieces of exactly 16 chunks
+    (2, 6000, 1, 1, 64, 0.1, 5),        # two rows, dv = 64, a partial last chunk
+    (1, 4096, 1, 1, 128, None, 4),      # pieces of exactly 16 chunks
 ]
 
 
