@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "headline_bf16"
-KERNEL_NAME = "gdn_fwd_bf16_dk128<false>"
+KERNEL_NAME = "gdn_fwd_bf16<false, 0, 128>"
 KERNEL_SOURCES = ["gated_deltanet_chunked_chunk_amd/csrc/gdn_fwd_bf16.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline_bf16.json")
 

@@ -22,7 +22,7 @@ bool aligned16(const void *p) {
 
 bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
     if (dtype == GDN_BF16)
-        return dk == 128 && (dv == 64 || dv == 128);
+        return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
     if (dtype == GDN_F32)
         return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
     return false;
@@ -49,7 +49,7 @@ struct PiecePlan {
 PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk, int32_t dv,
                       bool packed) {
     PiecePlan best{1, T};
-    if (packed || dtype != GDN_BF16 || dk != 128 || dv % 64 != 0)
+    if (packed || dtype != GDN_BF16 || dv % 64 != 0)
         return best;
     const int64_t rows = B * H_v;
     const int64_t items = rows * (dv / 64);

@@ -344,27 +344,35 @@ struct Stage {
     float g, b;   // row = lane
 };
 
-// Without Full (the piece ends, which form no output) Q is not loaded.
-template <bool Full>
+// Without Full (the piece ends, which form no output) Q is not loaded.  DK
+// is the key dimension in HBM; with DK = 64 the LDS rows keep their 128
+// columns and the lanes of the upper 64 stage zeros.
+template <bool Full, int DK>
 __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const Item &it, int c,
                                            int t, int lane) {
     const int64_t p = it.p0 + (int64_t)kC * c;
     const int L = min(kC, it.len - kC * c);
-    const uint32_t krow = (uint32_t)a.Hqk * kDK * 2;  // bytes between tokens
+    const uint32_t krow = (uint32_t)a.Hqk * DK * 2;  // bytes between tokens
     const uint32_t vrow = (uint32_t)a.Hv * a.dv * 2;
     const uint32_t grow = (uint32_t)a.Hv * 4;
-    const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (p * a.Hqk + it.hk) * kDK;
-    const uint16_t *qb = static_cast<const uint16_t *>(a.q) + (p * a.Hqk + it.hk) * kDK;
+    const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (p * a.Hqk + it.hk) * DK;
+    const uint16_t *qb = static_cast<const uint16_t *>(a.q) + (p * a.Hqk + it.hk) * DK;
     const uint16_t *vb = static_cast<const uint16_t *>(a.v) + (p * a.Hv + it.j) * a.dv +
                          (it.ident ? 0 : it.c0);
-    const __amdgpu_buffer_rsrc_t rk = rsrc(kb, (L - 1) * krow + kDK * 2);
-    const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (L - 1) * krow + kDK * 2);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kb, (L - 1) * krow + DK * 2);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (L - 1) * krow + DK * 2);
+    const bool kq_pad = DK < kDK && (t % 16) * 8 >= DK;  // a column slot past DK
     const __amdgpu_buffer_rsrc_t rv = rsrc(vb, it.ident ? 0u : (L - 1) * vrow + kDVT * 2);
     const __amdgpu_buffer_rsrc_t rg = rsrc(a.g + p * a.Hv + it.j, (L - 1) * grow + 4);
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.beta + p * a.Hv + it.j, (L - 1) * grow + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t off = (t / 16 + 16 * i) * krow + 16 * (t % 16);
+        if (kq_pad) {
+            st.k[i] = u32x4{0u, 0u, 0u, 0u};
+            st.q[i] = st.k[i];
+            continue;
+        }
         st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
         if (Full)
             st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
@@ -575,7 +583,7 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
 // decay tables, A blocks, P and diagonal inverses.  Once `st` is in LDS it is
 // refilled with chunk `next` (if next >= 0), so those loads are in flight
 // during the products below and the state waves' whole next chunk.
-template <bool Prep, bool Full>
+template <bool Prep, bool Full, int DK>
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
@@ -620,7 +628,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     if (lane == 0)
         __hip_atomic_fetch_add(&S.hsync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (next >= 0)
-        stage_load<Full>(st, a, it, next, t, lane);
+        stage_load<Full, DK>(st, a, it, next, t, lane);
     while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
         __builtin_amdgcn_s_sleep(1);
 
@@ -816,8 +824,8 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 // ends, for every piece but the last: F from a zero start and real V, and
 // (extra "identity" tiles) the transition Phi, the end state of dk unit
 // columns with V = 0; no output is formed.
-template <bool Prep, int Mode>
-__global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
+template <bool Prep, int Mode, int DK>
+__global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     __shared__ Smem S;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
@@ -825,7 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     // grouped value heads of one q/k head) are kept on one XCD: blocks are
     // dispatched round-robin over the 8 XCDs, so block b runs on XCD b % 8.
     const int n_val = a.dv / kDVT;
-    const int n_tiles = Mode == 1 ? n_val + kDK / kDVT : n_val;
+    const int n_tiles = Mode == 1 ? n_val + DK / kDVT : n_val;
     const int np = a.pieces > 1 ? (Mode == 1 ? a.pieces - 1 : a.pieces) : 1;
     const int G = a.Hv / a.Hqk;
     const int gs = n_tiles * G;
@@ -871,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     const int t = tid - 256;   // helper thread index
     const int lg = lane >> 4, lr = lane & 15;
     const int col = it.c0 + 16 * s + lr;
-    const int64_t hbase = ((int64_t)it.n * a.Hv + it.j) * kDK * (int64_t)a.dv;
+    const int64_t hbase = ((int64_t)it.n * a.Hv + it.j) * DK * (int64_t)a.dv;
     // The slot of (row, piece, head) in the piece arrays.
     const int64_t pslot = ((int64_t)it.n * (a.pieces - 1) + it.piece) * a.Hv + it.j;
 
@@ -881,15 +889,17 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
     if (state) {
         const float *src = nullptr;
         if (Mode == 0 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
-            src = a.piece_starts + (pslot - a.Hv) * kDK * (int64_t)a.dv;
+            src = a.piece_starts + (pslot - a.Hv) * DK * (int64_t)a.dv;
         else if (Mode == 0 && a.h0)
             src = a.h0 + hbase;
         if (src) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[mt][r] = src[(int64_t)key_of(mt, lg, r) * a.dv + col];
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key_of(mt, lg, r);
+                    h[mt][r] = key < DK ? src[(int64_t)key * a.dv + col] : 0.f;
+                }
         } else {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
@@ -898,8 +908,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
-        stage_load<Mode == 0>(st, a, it, 0, t, lane);
-        helper_prepare<Prep, Mode == 0>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        stage_load<Mode == 0, DK>(st, a, it, 0, t, lane);
+        helper_prepare<Prep, Mode == 0, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
                              it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
@@ -908,7 +918,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         if (state) {
             state_chunk<Mode == 0>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare<Prep, Mode == 0>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+            helper_prepare<Prep, Mode == 0, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
@@ -918,8 +928,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
         float *dst = nullptr;
         int64_t stride = a.dv, dcol = col;
         if (Mode == 1) {
-            stride = a.dv + kDK;
-            dst = a.piece_ends + pslot * kDK * stride;
+            stride = a.dv + DK;
+            dst = a.piece_ends + pslot * DK * stride;
             dcol = (it.ident ? a.dv : 0) + col;
         } else if (a.ht && it.piece == np - 1) {
             dst = a.ht + hbase;
@@ -928,8 +938,11 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(int64_t)key_of(mt, lg, r) * stride + dcol] = h[mt][r];
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key_of(mt, lg, r);
+                    if (key < DK)
+                        dst[(int64_t)key * stride + dcol] = h[mt][r];
+                }
         }
     }
 }
@@ -942,37 +955,39 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16_dk128(FwdArgs a) {
 // and, with its wave, 32 of the dk rows; Phi_p is staged in LDS.
 constexpr int kScanCols = 64;
 
+template <int DK>
 __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
-    __shared__ float Ms[kDK][kScanCols + 1];
-    __shared__ __attribute__((aligned(16))) float Ph[kDK][kDK + 4];
+    constexpr int RW = DK / 4;  // rows per wave
+    __shared__ float Ms[DK][kScanCols + 1];
+    __shared__ __attribute__((aligned(16))) float Ph[DK][DK + 4];
     const int tid = threadIdx.x, c = tid & 63, rg = tid >> 6;
     const int n = blockIdx.x / a.Hv, j = blockIdx.x % a.Hv;
     const int cc = blockIdx.y * kScanCols + c;
-    const int64_t hbase = ((int64_t)n * a.Hv + j) * kDK * (int64_t)a.dv;
-    for (int r = 0; r < 32; ++r) {
-        const int i = 32 * rg + r;
+    const int64_t hbase = ((int64_t)n * a.Hv + j) * DK * (int64_t)a.dv;
+    for (int r = 0; r < RW; ++r) {
+        const int i = RW * rg + r;
         Ms[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + cc] : 0.0f;
     }
-    const int64_t estride = a.dv + kDK;
+    const int64_t estride = a.dv + DK;
     for (int p = 0; p + 1 < a.pieces; ++p) {
         const int64_t pslot = ((int64_t)n * (a.pieces - 1) + p) * a.Hv + j;
-        const float *ends = a.piece_ends + pslot * kDK * estride;
+        const float *ends = a.piece_ends + pslot * DK * estride;
         __syncthreads();  // the previous step's reads of Ph are done
-        for (int e = tid; e < kDK * kDK / 4; e += 256) {
-            const int row = e / (kDK / 4), q4 = e % (kDK / 4);
+        for (int e = tid; e < DK * DK / 4; e += 256) {
+            const int row = e / (DK / 4), q4 = e % (DK / 4);
             *reinterpret_cast<f32x4 *>(&Ph[row][4 * q4]) =
                 *reinterpret_cast<const f32x4 *>(ends + row * estride + a.dv + 4 * q4);
         }
-        float acc[32];
+        float acc[RW];
 #pragma unroll
-        for (int r = 0; r < 32; ++r)
-            acc[r] = ends[(32 * rg + r) * estride + cc];
+        for (int r = 0; r < RW; ++r)
+            acc[r] = ends[(RW * rg + r) * estride + cc];
         __syncthreads();
-        for (int k = 0; k < kDK; k += 4) {
+        for (int k = 0; k < DK; k += 4) {
             const float m0 = Ms[k][c], m1 = Ms[k + 1][c], m2 = Ms[k + 2][c], m3 = Ms[k + 3][c];
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[32 * rg + r][k]);
+            for (int r = 0; r < RW; ++r) {
+                const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[RW * rg + r][k]);
                 acc[r] = fmaf(ph[0], m0, acc[r]);
                 acc[r] = fmaf(ph[1], m1, acc[r]);
                 acc[r] = fmaf(ph[2], m2, acc[r]);
@@ -980,38 +995,47 @@ __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
             }
         }
         __syncthreads();  // every read of Ms is done
-        float *out = a.piece_starts + pslot * kDK * (int64_t)a.dv;
+        float *out = a.piece_starts + pslot * DK * (int64_t)a.dv;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            Ms[32 * rg + r][c] = acc[r];
-            out[(int64_t)(32 * rg + r) * a.dv + cc] = acc[r];
+        for (int r = 0; r < RW; ++r) {
+            Ms[RW * rg + r][c] = acc[r];
+            out[(int64_t)(RW * rg + r) * a.dv + cc] = acc[r];
         }
     }
 }
 
-template <bool Prep>
+template <bool Prep, int DK>
 hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
     const int n_val = a.dv / kDVT;
     if (a.pieces <= 1) {
         const int64_t blocks = (int64_t)a.n_seqs * a.Hv * n_val;
         if (blocks > 0x7fffffff)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 0>), dim3((unsigned)blocks), dim3(kThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 0, DK>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
         return hipGetLastError();
     }
-    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + kDK / kDVT);
+    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
     const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
     const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
     if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 1>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
                        stream, a);
-    hipLaunchKernelGGL(piece_scan, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
+    hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
                        dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((gdn_fwd_bf16_dk128<Prep, 0>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 0, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
+}
+
+template <bool Prep>
+hipError_t launch_dk(const FwdArgs &a, hipStream_t stream) {
+    if (a.dk == 128)
+        return launch_passes<Prep, 128>(a, stream);
+    if (a.dk == 64)
+        return launch_passes<Prep, 64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1027,7 +1051,7 @@ size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, i
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {
     if ((int64_t)a.n_seqs * a.Hv <= 0)
         return hipSuccess;
-    return a.flags ? launch_passes<true>(a, stream) : launch_passes<false>(a, stream);
+    return a.flags ? launch_dk<true>(a, stream) : launch_dk<false>(a, stream);
 }
 
 }  // namespace gdn

@@ -93,8 +93,8 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   B, T         batch rows and tokens per row (T >= 1).  With cu_seqlens,
  *                B must be 1 and T is the total packed length.
  *   H_qk, H_v    q/k heads and value heads; H_v % H_qk == 0.
- *   dk, dv       key and value head dimensions.  Supported: bf16 with
- *                dk = 128 and dv in {64, 128}; fp32 with dk, dv in {64, 128}.
+ *   dk, dv       key and value head dimensions.  Supported: dk, dv in
+ *                {64, 128} for both dtypes.
  *   q, k         [B, T, H_qk, dk]
  *   v            [B, T, H_v, dv]
  *   g            [B, T, H_v] fp32, natural-log decay (a = exp(g)); finite.

@@ -89,7 +89,7 @@ def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
     (dict(g=None), INVALID), (dict(beta=None), INVALID), (dict(o=None), INVALID),
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(Hqk=0), INVALID), (dict(dk=0), INVALID),
-    (dict(dtype=7), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(dk=64), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(dk=32), UNSUPPORTED),
     (dict(flags=4), INVALID), (dict(flags=0x100), INVALID),
     (dict(dv=96), UNSUPPORTED), (dict(dtype=0, dk=96), UNSUPPORTED),
     (dict(q=FAKE + 8), MISALIGNED), (dict(o=FAKE + 4), MISALIGNED),

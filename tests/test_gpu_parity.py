@@ -236,3 +236,32 @@ def test_piece_scan_with_in_op_preparation():
     eo, eh = rel_l2(o.float().cpu().numpy(), ro), rel_l2(ht.cpu().numpy(), rht)
     print(f"  rel-L2 output {eo:.3e}, state {eh:.3e}", flush=True)
     assert eo <= tol_o and eh <= tol_h
+
+
+@pytest.mark.parametrize("T,dv", [(1, 128), (65, 64), (200, 128)])
+def test_bf16_dk64(T, dv):
+    """bf16 with dk = 64 (the key rows are staged into the 128-wide LDS
+    layout with zero upper halves): ragged T, grouped heads, h0, scale."""
+    d = gi.make(2, T, 1, 2, 64, dv, "bf16", 4100 + T, h0_std=0.1)
+    check(d, scale=0.9, label=f"bf16 dk64 T={T} dv={dv}")
+
+
+def test_bf16_dk64_packed_with_empty_document():
+    cu = gi.cu_from_lengths([70, 0, 129, 1])
+    d = gi.make(1, 200, 2, 4, 64, 64, "bf16", 4150, h0_std=0.05, cu_seqlens=cu)
+    check(d, label="bf16 dk64 packed")
+
+
+def test_bf16_dk64_piece_scan():
+    """dk = 64 through the piece scan: 4 pieces, one transition tile."""
+    d = gi.make(1, 4096 + 37, 1, 2, 64, 128, "bf16", 4160, h0_std=0.5)
+    d["g"] = (d["g"] / 8).astype(np.float32)  # slower decay: carried states matter
+    eo, eh = check(d, label="bf16 dk64 piece scan")
+    import gated_deltanet_chunked_chunk_amd as gdn
+    from gpu_util import to_device
+    t = to_device(d)
+    o2, h2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"],
+                               pieces=False)
+    ro, rht = run_oracle(d)
+    print(f"  whole rows: rel-L2 output {rel_l2(o2.float().cpu().numpy(), ro):.3e}, state "
+          f"{rel_l2(h2.cpu().numpy(), rht):.3e}", flush=True)

@@ -72,6 +72,7 @@ FUSED_CASES = [
     # dtype, B, T, Hqk, Hv, dk, dv, document lengths (None: B rows)
     ("bf16", 2, 200, 2, 4, 128, 128, None),
     ("bf16", 1, 65, 1, 1, 128, 64, None),
+    ("bf16", 2, 130, 1, 2, 64, 128, None),
     ("bf16", 1, 300, 2, 2, 128, 128, [70, 0, 129, 101]),
     ("f32", 1, 100, 2, 2, 64, 64, None),
     ("f32", 1, 150, 1, 2, 128, 128, [1, 85, 64]),
