@@ -886,6 +886,13 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     f32x4 h[8];
     Stage st;
     int meet = 0;
+    // Issue priority on the shared SIMDs follows the critical paths: the
+    // state waves' chain first, then helper 0 (diagonal blocks and their
+    // inverses); helpers 1..3 fill the gaps.
+    if (state)
+        __builtin_amdgcn_s_setprio(3);
+    else if (s == 0)
+        __builtin_amdgcn_s_setprio(2);
     if (state) {
         const float *src = nullptr;
         if (Mode == 0 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
