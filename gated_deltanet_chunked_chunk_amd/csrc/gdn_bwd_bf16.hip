@@ -292,10 +292,13 @@ __device__ __forceinline__ void stage_T(uint16_t *Th, uint16_t *Tl, const float 
 // bwd_prep: per (chunk, value head).
 
 __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kC * kLK];
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[kC * kLK];
-    __shared__ float Af[kC * kLF];
-    __shared__ float Tf[kC * kLF];
+    // K and Q are dead once K K^T and Q K^T are in registers: A (fp32) then
+    // takes K's space and T Q's, which keeps LDS under a third of a CU's.
+    static_assert(kC * kLF * sizeof(float) <= kC * kLK * sizeof(uint16_t), "A, T fit K, Q");
+    __shared__ __attribute__((aligned(16))) uint16_t KsAf[kC * kLK];
+    __shared__ __attribute__((aligned(16))) uint16_t QsTf[kC * kLK];
+    uint16_t *Ks = KsAf, *Qs = QsTf;
+    float *Af = reinterpret_cast<float *>(KsAf), *Tf = reinterpret_cast<float *>(QsTf);
     __shared__ float Wf[32 * 33];
     __shared__ uint16_t Ps[kC * kC];   // unpadded: keeps LDS under half a CU's
     __shared__ float gam[kC], bt[kC];
@@ -314,8 +317,6 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
         gam[lane] = wave_prefix_sum(gv);  // padded rows keep gamma_{L-1}
         bt[lane] = bv;
     }
-    for (int i = tid; i < kC * kLF; i += 256)
-        Tf[i] = 0.0f;
     __syncthreads();
 
     // K K^T and Q K^T, rows 16w .. 16w + 15.
@@ -331,6 +332,9 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
             qk[ni] = mma(frag_rows(Qs, kLK, 16 * w, 32 * kx, lr, lg), b, qk[ni]);
         }
     }
+    __syncthreads();  // every read of K and Q is done: A and T take their space
+    for (int i = tid; i < kC * kLF; i += 256)
+        Tf[i] = 0.0f;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
