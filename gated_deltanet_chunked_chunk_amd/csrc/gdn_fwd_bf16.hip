@@ -21,8 +21,10 @@
 // The helper waves meet once more among themselves per chunk (an LDS
 // counter) between staging and the products that read the staged rows.
 //
-// The Prep instance also applies the in-op preparation options (q/k rows
-// divided by their L2 norms, gate activations) as the helpers stage a chunk.
+// The Prep instance also applies the in-op preparation options as the
+// helpers stage a chunk: the gate activations, and the q/k rows' inverse L2
+// norms, applied as fp32 factors in the blocks and the decay tables (the
+// rows themselves are never rescaled).
 //
 // The chunk equations (derived from the token recurrence
 // S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T of Gated DeltaNet; the
@@ -138,6 +140,9 @@ struct alignas(16) ChunkBuf {
     float eg[kC];               // exp(gamma_r)
     float el[kC];               // exp(gamma_L - gamma_r)
     float bt[kC];               // beta_r
+    float nu[kC];               // in-op L2 norm: 1 / ||k_r|| (Prep instance only)
+    float mu[kC];               // in-op L2 norm: 1 / ||q_r|| (Prep instance only)
+    float egq[kC];              // exp(gamma_r) mu_r (Prep instance only)
     float eL;                   // exp(gamma_L)
     float pad_[3];
 };
@@ -286,24 +291,21 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// In-op L2 normalisation of a staged q or k row: the 16 lanes of a DPP row
-// hold its 128 bf16 values, 8 each.  Every value is divided by the row's
-// fp32 norm and rounded back to bf16 (to nearest even).
-__device__ __forceinline__ void l2_normalize_row(u32x4 &x) {
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[2 * e] = __uint_as_float(x[e] << 16);
-        f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
-    }
+// In-op L2 norm of a staged q or k row: the 16 lanes of a DPP row hold its
+// 128 bf16 values, 8 each; returns 1 / ||row|| (fp32) in every lane of the
+// row.  The rows stay as they are: the factors are applied where the rows
+// enter the chunk equations.
+__device__ __forceinline__ float row_inv_norm(const u32x4 &x) {
     float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        s = fmaf(f[e], f[e], s);
-    const float inv = inv_l2_norm(row16_sum(s));
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        x[e] = f2bf(f[2 * e] * inv) | (unsigned)f2bf(f[2 * e + 1] * inv) << 16;
+    for (int e = 0; e < 4; ++e) {
+        // The element goes through a scalar: a bit cast of the vector
+        // element itself read element 0 every time.
+        const unsigned w = x[e];
+        const bf16x2 p = __builtin_bit_cast(bf16x2, w);
+        s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
+    }
+    return inv_l2_norm(row16_sum(s));
 }
 
 // x from the lane of the quad whose index is Sel.
@@ -403,10 +405,13 @@ __device__ __forceinline__ f32x4 block_product(const bf16x8 (&xi)[4], const bf16
 }
 
 // -A block (I, J), I > J: -beta_r exp(gamma_r - gamma_s) (k_r . k_s), hi + lo.
-template <int I, int J>
+// Nrm: k_r . k_s scaled by nu_r nu_s (the in-op L2 norm).
+template <int I, int J, bool Nrm>
 __device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], const bf16x8 (&kj)[4],
                                         int lr, int lg) {
-    const f32x4 c = block_product(ki, kj);
+    f32x4 c = block_product(ki, kj);
+    if (Nrm)
+        c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
     const f32x4 gc = ld4f(B.gam + 16 * J + 4 * lg);
     f32x4 val;
@@ -421,10 +426,13 @@ __device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], cons
 }
 
 // P block (I, J), I >= J: exp(gamma_r - gamma_s) (q_r . k_s), s <= r.
-template <int I, int J>
+// Nrm: q_r . k_s scaled by mu_r nu_s (the in-op L2 norm).
+template <int I, int J, bool Nrm>
 __device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], const bf16x8 (&kj)[4],
                                         int lr, int lg) {
-    const f32x4 c = block_product(qi, kj);
+    f32x4 c = block_product(qi, kj);
+    if (Nrm)
+        c = c * (B.mu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr];
     const f32x4 gc = ld4f(B.gam + 16 * J + 4 * lg);
     f32x4 val;
@@ -441,10 +449,12 @@ __device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], cons
 }
 
 // Diagonal block A_II (strictly lower part, negated) into ad, column-major.
-template <int I>
+template <int I, bool Nrm>
 __device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
                                            int lr, int lg) {
-    const f32x4 c = block_product(ki, ki);
+    f32x4 c = block_product(ki, ki);
+    if (Nrm)
+        c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * I + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
     const f32x4 gc = ld4f(B.gam + 16 * I + 4 * lg);
 #pragma unroll
@@ -514,20 +524,21 @@ __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int
 // The per-chunk products, split over the helper waves: helper 0 forms the
 // four diagonal blocks of A and their inverses; helpers 1 .. 3 form the
 // off-diagonal blocks of A and the blocks of P (six, five and five blocks).
-// Without WithP (no output is formed) the P blocks are skipped.
-template <bool WithP>
+// Without WithP (no output is formed) the P blocks are skipped; Nrm folds
+// the in-op L2 norms of the rows into the blocks.
+template <bool WithP, bool Nrm>
 __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg, int lane) {
     const KqBase kb = kq_base(lr, lg);
     if (hw == 0) {
         bf16x8 k[2][4];
         load_block(k[0], B.K, kb, 0);
         load_block(k[1], B.K, kb, 1);
-        diag_block<0>(S.Ad[0], B, k[0], lr, lg);
+        diag_block<0, Nrm>(S.Ad[0], B, k[0], lr, lg);
         load_block(k[0], B.K, kb, 2);
-        diag_block<1>(S.Ad[1], B, k[1], lr, lg);
+        diag_block<1, Nrm>(S.Ad[1], B, k[1], lr, lg);
         load_block(k[1], B.K, kb, 3);
-        diag_block<2>(S.Ad[2], B, k[0], lr, lg);
-        diag_block<3>(S.Ad[3], B, k[1], lr, lg);
+        diag_block<2, Nrm>(S.Ad[2], B, k[0], lr, lg);
+        diag_block<3, Nrm>(S.Ad[3], B, k[1], lr, lg);
         diag_inverse_all(B, S, lane);
     } else if (hw == 1) {  // A30 A31 A32, P00 P10 P11
         bf16x8 k3[4], q[4], kj[2][4];
@@ -535,47 +546,47 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
         load_block(kj[0], B.K, kb, 0);
         load_block(q, B.Q, kb, 0);
         load_block(kj[1], B.K, kb, 1);
-        a_block<3, 0>(B, k3, kj[0], lr, lg);
+        a_block<3, 0, Nrm>(B, k3, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<0, 0>(B, q, kj[0], lr, lg);
+            p_block<0, 0, Nrm>(B, q, kj[0], lr, lg);
         load_block(q, B.Q, kb, 1);
-        a_block<3, 1>(B, k3, kj[1], lr, lg);
+        a_block<3, 1, Nrm>(B, k3, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<1, 0>(B, q, kj[0], lr, lg);
+            p_block<1, 0, Nrm>(B, q, kj[0], lr, lg);
         load_block(kj[0], B.K, kb, 2);
         if constexpr (WithP)
-            p_block<1, 1>(B, q, kj[1], lr, lg);
-        a_block<3, 2>(B, k3, kj[0], lr, lg);
+            p_block<1, 1, Nrm>(B, q, kj[1], lr, lg);
+        a_block<3, 2, Nrm>(B, k3, kj[0], lr, lg);
     } else if (hw == 2) {  // A20 A21, P20 P21 P22
         bf16x8 k2[4], q2[4], kj[2][4];
         load_block(k2, B.K, kb, 2);
         load_block(q2, B.Q, kb, 2);
         load_block(kj[0], B.K, kb, 0);
         load_block(kj[1], B.K, kb, 1);
-        a_block<2, 0>(B, k2, kj[0], lr, lg);
+        a_block<2, 0, Nrm>(B, k2, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<2, 0>(B, q2, kj[0], lr, lg);
-        a_block<2, 1>(B, k2, kj[1], lr, lg);
+            p_block<2, 0, Nrm>(B, q2, kj[0], lr, lg);
+        a_block<2, 1, Nrm>(B, k2, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<2, 1>(B, q2, kj[1], lr, lg);
+            p_block<2, 1, Nrm>(B, q2, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<2, 2>(B, q2, k2, lr, lg);
+            p_block<2, 2, Nrm>(B, q2, k2, lr, lg);
     } else {  // A10, P30 P31 P32 P33
         bf16x8 k1[4], q3[4], kj[2][4];
         load_block(k1, B.K, kb, 1);
         load_block(q3, B.Q, kb, 3);
         load_block(kj[0], B.K, kb, 0);
         load_block(kj[1], B.K, kb, 2);
-        a_block<1, 0>(B, k1, kj[0], lr, lg);
+        a_block<1, 0, Nrm>(B, k1, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<3, 0>(B, q3, kj[0], lr, lg);
+            p_block<3, 0, Nrm>(B, q3, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<3, 1>(B, q3, k1, lr, lg);
+            p_block<3, 1, Nrm>(B, q3, k1, lr, lg);
         load_block(kj[0], B.K, kb, 3);
         if constexpr (WithP)
-            p_block<3, 2>(B, q3, kj[1], lr, lg);
+            p_block<3, 2, Nrm>(B, q3, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<3, 3>(B, q3, kj[0], lr, lg);
+            p_block<3, 3, Nrm>(B, q3, kj[0], lr, lg);
     }
 }
 
@@ -588,13 +599,25 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
     hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
-    const int lr = lane & 15, lg = lane >> 4;
-    if (Prep && (a.flags & kStepL2Norm)) {
+    int lrv = lane & 15, lgv = lane >> 4;
+    if constexpr (Prep) {
+        // Lane indices re-derived per chunk: without this the compiler hoists
+        // every address built from them out of the chunk loop, which runs out
+        // of registers in this instance.
+        asm volatile("" : "+v"(lrv), "+v"(lgv), "+v"(t));
+    }
+    const int lr = lrv, lg = lgv;
+    if (Prep) {
+        // The rows' inverse L2 norms (1 without the option), one lane per row.
+        const bool l2 = a.flags & kStepL2Norm;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            l2_normalize_row(st.k[i]);
-            if (Full)
-                l2_normalize_row(st.q[i]);
+            const float nk = l2 ? row_inv_norm(st.k[i]) : 1.0f;
+            const float nq = l2 && Full ? row_inv_norm(st.q[i]) : 1.0f;
+            if (t % 16 == 0) {
+                B.nu[t / 16 + 16 * i] = nk;
+                B.mu[t / 16 + 16 * i] = nq;
+            }
         }
     }
 #pragma unroll
@@ -631,13 +654,23 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         stage_load<Full, DK>(st, a, it, next, t, lane);
     while (__hip_atomic_load(&S.hsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < meet)
         __builtin_amdgcn_s_sleep(1);
+    if (Prep && hw == 3) {
+        // Every row's norms are in LDS now: fold them into the tables the
+        // state waves read (K M0 and the update through nu, Q M0 through mu).
+        const float nu = B.nu[lane];
+        B.egq[lane] = B.eg[lane] * B.mu[lane];
+        B.eg[lane] *= nu;
+        B.el[lane] *= nu;
+    }
 
-    helper_products<Full>(S, B, hw, lr, lg, lane);
+    helper_products<Full, Prep>(S, B, hw, lr, lg, lane);
 }
 
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
 // without Out only the state advances (the output is not formed).
-template <bool Out>
+// Nrm: Q M0 is scaled by the egq table (exp(gamma) mu); the in-op L2 norms
+// of K (nu) are already in the eg and el tables.
+template <bool Out, bool Nrm>
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
@@ -677,14 +710,15 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     f32x4 R[4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
+        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);  // with Nrm: exp(gamma) nu
+        const f32x4 egq = Nrm ? ld4f(B.egq + 16 * mi + 4 * lg) : eg4;
         const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
         const u32x2 vv = ld_tr(B.V + vbase + 16 * kDVT * mi);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
             R[mi][r] = bt4[r] * (vr - eg4[r] * X[mi][r]);
-            Oa[mi][r] *= eg4[r];
+            Oa[mi][r] *= egq[r];
         }
     }
     // Operands of the solve.  Each block of -A and each D_i is one A operand
@@ -738,7 +772,7 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         u32x2 ph[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 el4 = ld4f(B.el + 16 * i + 4 * lg);
+            const f32x4 el4 = ld4f(B.el + 16 * i + 4 * lg);  // with Nrm: times nu
             split4(el4 * D[i], ph[i], pl[i]);
         }
         dph[0] = cat(ph[0], ph[1]);
@@ -923,7 +957,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
-            state_chunk<Mode == 0>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            state_chunk<Mode == 0, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
             helper_prepare<Prep, Mode == 0, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
