@@ -310,7 +310,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step and preparation measurements")
-    ap.add_argument("--no-long", action="store_true", help="skip the long-row measurement")
+    ap.add_argument("--long", action="store_true",
+                    help="also time the long row (B=1, T=1,064,960), with and without pieces")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -431,7 +432,7 @@ def main():
         decode = measure_decode(gdn, gi, torch, dev, steps=200, warmup=100)
 
     long_row = None
-    if not args.no_long:
+    if args.long:
         log("[bench] long row")
         long_row = measure_long(gdn, gi, torch, dev)
 

@@ -853,8 +853,9 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 
 // Prep: the in-op preparation options of a.flags are honoured (a separate
 // instance, so the plain kernel carries none of their code).
-// Mode 0: the output pass, over whole rows or (with a.pieces > 1) over
-// pieces that start from the states of piece_starts.  Mode 1: the piece
+// Mode 0: the output pass over whole rows.  Mode 2: the same over pieces
+// that start from the states of piece_starts (an instance of its own, so
+// traces tell the two apart).  Mode 1: the piece
 // ends, for every piece but the last: F from a zero start and real V, and
 // (extra "identity" tiles) the transition Phi, the end state of dk unit
 // columns with V = 0; no output is formed.
@@ -929,9 +930,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         __builtin_amdgcn_s_setprio(2);
     if (state) {
         const float *src = nullptr;
-        if (Mode == 0 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
+        if (Mode != 1 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
             src = a.piece_starts + (pslot - a.Hv) * DK * (int64_t)a.dv;
-        else if (Mode == 0 && a.h0)
+        else if (Mode != 1 && a.h0)
             src = a.h0 + hbase;
         if (src) {
 #pragma unroll
@@ -949,17 +950,17 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
-        stage_load<Mode == 0, DK>(st, a, it, 0, t, lane);
-        helper_prepare<Prep, Mode == 0, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        stage_load<Mode != 1, DK>(st, a, it, 0, t, lane);
+        helper_prepare<Prep, Mode != 1, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
                              it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
 
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
-            state_chunk<Mode == 0, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            state_chunk<Mode != 1, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare<Prep, Mode == 0, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+            helper_prepare<Prep, Mode != 1, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
@@ -1065,7 +1066,7 @@ hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
                        stream, a);
     hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
                        dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 0, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
