@@ -104,10 +104,13 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *                modified):
  *                GDN_QK_L2NORM  every q and k row is divided by its L2 norm
  *                               inside the call (use_qk_l2norm of the
- *                               jax-linear-attention page's "Quick start"),
- *                               the norm taken in fp32 and, for bf16, the
- *                               normalised row rounded to bf16 before use,
- *                               as gdn_prepare_inputs would store it;
+ *                               jax-linear-attention page's "Quick start"):
+ *                               the inverse norm is taken in fp32 and applied
+ *                               as an fp32 factor where the row enters the
+ *                               equations, so the normalised row is never
+ *                               rounded (gdn_prepare_inputs, which stores
+ *                               rows, rounds them to the input dtype); a
+ *                               row of zeros stays zero;
  *                GDN_GATE_ACT   g and beta are raw values: the decay is
  *                               logsigmoid(g) and the write strength
  *                               sigmoid(beta).

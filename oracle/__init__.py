@@ -10,6 +10,8 @@ Two independent routes to the same fp64 result:
   * gdn_bwd   -- its reverse mode, token by token in plain C, threaded over
                  (sequence, head) units;
   * chunked   -- the chunk-parallel algebra in numpy (chunked.py).
+And beside them (prep.py): the in-op L2 normalisation, the gate activations
+and the single-token decode step over a cache of states, in fp64 numpy.
 
 Every function here is pinned by the CPU tests (closed forms, invariants,
 exact rational brute force, and the two routes against each other).
@@ -20,6 +22,7 @@ import os
 import numpy as np
 
 from . import chunked  # noqa: F401  (re-exported for tests)
+from . import prep  # noqa: F401  (re-exported for tests)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
