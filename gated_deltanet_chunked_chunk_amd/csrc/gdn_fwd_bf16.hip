@@ -390,26 +390,30 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
 // K_j X_i^T (X = K or Q), whose C layout puts row 16 i + l%16, columns
 // 16 j + 4 (l/16) .. + 3 of the wanted block in lane l: the row-major 8-byte
 // pieces the A operands of the solve are read in.
+// KK: the 32-wide k-steps that carry data (DK / 32; with DK = 64 the upper
+// half of each staged row is zero and skipped).
+template <int KK = 4>
 __device__ __forceinline__ void load_block(bf16x8 (&f)[4], const uint16_t *t, const KqBase &kb, int m) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
         f[kk] = frag_kq(t, kb, m, kk);
 }
 
+template <int KK = 4>
 __device__ __forceinline__ f32x4 block_product(const bf16x8 (&xi)[4], const bf16x8 (&kj)[4]) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
         c = mma(kj[kk], xi[kk], c);
     return c;
 }
 
 // -A block (I, J), I > J: -beta_r exp(gamma_r - gamma_s) (k_r . k_s), hi + lo.
 // Nrm: k_r . k_s scaled by nu_r nu_s (the in-op L2 norm).
-template <int I, int J, bool Nrm>
+template <int I, int J, bool Nrm, int DK>
 __device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], const bf16x8 (&kj)[4],
                                         int lr, int lg) {
-    f32x4 c = block_product(ki, kj);
+    f32x4 c = block_product<DK / 32>(ki, kj);
     if (Nrm)
         c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
@@ -427,10 +431,10 @@ __device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], cons
 
 // P block (I, J), I >= J: exp(gamma_r - gamma_s) (q_r . k_s), s <= r.
 // Nrm: q_r . k_s scaled by mu_r nu_s (the in-op L2 norm).
-template <int I, int J, bool Nrm>
+template <int I, int J, bool Nrm, int DK>
 __device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], const bf16x8 (&kj)[4],
                                         int lr, int lg) {
-    f32x4 c = block_product(qi, kj);
+    f32x4 c = block_product<DK / 32>(qi, kj);
     if (Nrm)
         c = c * (B.mu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr];
@@ -449,10 +453,10 @@ __device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], cons
 }
 
 // Diagonal block A_II (strictly lower part, negated) into ad, column-major.
-template <int I, bool Nrm>
+template <int I, bool Nrm, int DK>
 __device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
                                            int lr, int lg) {
-    f32x4 c = block_product(ki, ki);
+    f32x4 c = block_product<DK / 32>(ki, ki);
     if (Nrm)
         c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * I + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
@@ -526,67 +530,67 @@ __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int
 // off-diagonal blocks of A and the blocks of P (six, five and five blocks).
 // Without WithP (no output is formed) the P blocks are skipped; Nrm folds
 // the in-op L2 norms of the rows into the blocks.
-template <bool WithP, bool Nrm>
+template <bool WithP, bool Nrm, int DK>
 __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg, int lane) {
     const KqBase kb = kq_base(lr, lg);
     if (hw == 0) {
         bf16x8 k[2][4];
-        load_block(k[0], B.K, kb, 0);
-        load_block(k[1], B.K, kb, 1);
-        diag_block<0, Nrm>(S.Ad[0], B, k[0], lr, lg);
-        load_block(k[0], B.K, kb, 2);
-        diag_block<1, Nrm>(S.Ad[1], B, k[1], lr, lg);
-        load_block(k[1], B.K, kb, 3);
-        diag_block<2, Nrm>(S.Ad[2], B, k[0], lr, lg);
-        diag_block<3, Nrm>(S.Ad[3], B, k[1], lr, lg);
+        load_block<DK / 32>(k[0], B.K, kb, 0);
+        load_block<DK / 32>(k[1], B.K, kb, 1);
+        diag_block<0, Nrm, DK>(S.Ad[0], B, k[0], lr, lg);
+        load_block<DK / 32>(k[0], B.K, kb, 2);
+        diag_block<1, Nrm, DK>(S.Ad[1], B, k[1], lr, lg);
+        load_block<DK / 32>(k[1], B.K, kb, 3);
+        diag_block<2, Nrm, DK>(S.Ad[2], B, k[0], lr, lg);
+        diag_block<3, Nrm, DK>(S.Ad[3], B, k[1], lr, lg);
         diag_inverse_all(B, S, lane);
     } else if (hw == 1) {  // A30 A31 A32, P00 P10 P11
         bf16x8 k3[4], q[4], kj[2][4];
-        load_block(k3, B.K, kb, 3);
-        load_block(kj[0], B.K, kb, 0);
-        load_block(q, B.Q, kb, 0);
-        load_block(kj[1], B.K, kb, 1);
-        a_block<3, 0, Nrm>(B, k3, kj[0], lr, lg);
+        load_block<DK / 32>(k3, B.K, kb, 3);
+        load_block<DK / 32>(kj[0], B.K, kb, 0);
+        load_block<DK / 32>(q, B.Q, kb, 0);
+        load_block<DK / 32>(kj[1], B.K, kb, 1);
+        a_block<3, 0, Nrm, DK>(B, k3, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<0, 0, Nrm>(B, q, kj[0], lr, lg);
-        load_block(q, B.Q, kb, 1);
-        a_block<3, 1, Nrm>(B, k3, kj[1], lr, lg);
+            p_block<0, 0, Nrm, DK>(B, q, kj[0], lr, lg);
+        load_block<DK / 32>(q, B.Q, kb, 1);
+        a_block<3, 1, Nrm, DK>(B, k3, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<1, 0, Nrm>(B, q, kj[0], lr, lg);
-        load_block(kj[0], B.K, kb, 2);
+            p_block<1, 0, Nrm, DK>(B, q, kj[0], lr, lg);
+        load_block<DK / 32>(kj[0], B.K, kb, 2);
         if constexpr (WithP)
-            p_block<1, 1, Nrm>(B, q, kj[1], lr, lg);
-        a_block<3, 2, Nrm>(B, k3, kj[0], lr, lg);
+            p_block<1, 1, Nrm, DK>(B, q, kj[1], lr, lg);
+        a_block<3, 2, Nrm, DK>(B, k3, kj[0], lr, lg);
     } else if (hw == 2) {  // A20 A21, P20 P21 P22
         bf16x8 k2[4], q2[4], kj[2][4];
-        load_block(k2, B.K, kb, 2);
-        load_block(q2, B.Q, kb, 2);
-        load_block(kj[0], B.K, kb, 0);
-        load_block(kj[1], B.K, kb, 1);
-        a_block<2, 0, Nrm>(B, k2, kj[0], lr, lg);
+        load_block<DK / 32>(k2, B.K, kb, 2);
+        load_block<DK / 32>(q2, B.Q, kb, 2);
+        load_block<DK / 32>(kj[0], B.K, kb, 0);
+        load_block<DK / 32>(kj[1], B.K, kb, 1);
+        a_block<2, 0, Nrm, DK>(B, k2, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<2, 0, Nrm>(B, q2, kj[0], lr, lg);
-        a_block<2, 1, Nrm>(B, k2, kj[1], lr, lg);
+            p_block<2, 0, Nrm, DK>(B, q2, kj[0], lr, lg);
+        a_block<2, 1, Nrm, DK>(B, k2, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<2, 1, Nrm>(B, q2, kj[1], lr, lg);
+            p_block<2, 1, Nrm, DK>(B, q2, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<2, 2, Nrm>(B, q2, k2, lr, lg);
+            p_block<2, 2, Nrm, DK>(B, q2, k2, lr, lg);
     } else {  // A10, P30 P31 P32 P33
         bf16x8 k1[4], q3[4], kj[2][4];
-        load_block(k1, B.K, kb, 1);
-        load_block(q3, B.Q, kb, 3);
-        load_block(kj[0], B.K, kb, 0);
-        load_block(kj[1], B.K, kb, 2);
-        a_block<1, 0, Nrm>(B, k1, kj[0], lr, lg);
+        load_block<DK / 32>(k1, B.K, kb, 1);
+        load_block<DK / 32>(q3, B.Q, kb, 3);
+        load_block<DK / 32>(kj[0], B.K, kb, 0);
+        load_block<DK / 32>(kj[1], B.K, kb, 2);
+        a_block<1, 0, Nrm, DK>(B, k1, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<3, 0, Nrm>(B, q3, kj[0], lr, lg);
+            p_block<3, 0, Nrm, DK>(B, q3, kj[0], lr, lg);
         if constexpr (WithP)
-            p_block<3, 1, Nrm>(B, q3, k1, lr, lg);
-        load_block(kj[0], B.K, kb, 3);
+            p_block<3, 1, Nrm, DK>(B, q3, k1, lr, lg);
+        load_block<DK / 32>(kj[0], B.K, kb, 3);
         if constexpr (WithP)
-            p_block<3, 2, Nrm>(B, q3, kj[1], lr, lg);
+            p_block<3, 2, Nrm, DK>(B, q3, kj[1], lr, lg);
         if constexpr (WithP)
-            p_block<3, 3, Nrm>(B, q3, kj[0], lr, lg);
+            p_block<3, 3, Nrm, DK>(B, q3, kj[0], lr, lg);
     }
 }
 
@@ -663,28 +667,31 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         B.el[lane] *= nu;
     }
 
-    helper_products<Full, Prep>(S, B, hw, lr, lg, lane);
+    helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
 }
 
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
 // without Out only the state advances (the output is not formed).
 // Nrm: Q M0 is scaled by the egq table (exp(gamma) mu); the in-op L2 norms
 // of K (nu) are already in the eg and el tables.
-template <bool Out, bool Nrm>
+template <bool Out, bool Nrm, int DK>
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
     // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0),
     // fragments loaded one row block ahead of the products.
+    // Key tiles 0 .. DK/16 - 1 hold the state; with DK = 64 the rest stay
+    // zero and are skipped, as are the zero upper halves of the K, Q rows.
+    constexpr int KK = DK / 32, MT = DK / 16;
     bf16x8 hb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
         hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
     f32x4 X[4], Oa[4];
     bf16x8 fk[2][4], fq[2][4];
     const KqBase kb = kq_base(lr, lg);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
         fk[0][kk] = frag_kq(B.K, kb, 0, kk);
         fq[0][kk] = frag_kq(B.Q, kb, 0, kk);
     }
@@ -692,7 +699,7 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     for (int mi = 0; mi < 4; ++mi) {
         if (mi < 3) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < KK; ++kk) {
                 fk[(mi + 1) & 1][kk] = frag_kq(B.K, kb, mi + 1, kk);
                 fq[(mi + 1) & 1][kk] = frag_kq(B.Q, kb, mi + 1, kk);
             }
@@ -700,7 +707,7 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
         Oa[mi] = X[mi];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             X[mi] = mma(fk[mi & 1][kk], hb[kk], X[mi]);
             Oa[mi] = mma(fq[mi & 1][kk], hb[kk], Oa[mi]);
         }
@@ -797,8 +804,8 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     for (int kk = 0; kk < 2; ++kk)
         kt[0][kk] = ktf(0, kk);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        if (mt < 7) {
+    for (int mt = 0; mt < MT; ++mt) {
+        if (mt < MT - 1) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 kt[(mt + 1) & 1][kk] = ktf(mt + 1, kk);
@@ -958,7 +965,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
-            state_chunk<Mode != 1, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            state_chunk<Mode != 1, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
             helper_prepare<Prep, Mode != 1, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
