@@ -265,3 +265,23 @@ def test_bf16_dk64_piece_scan():
     ro, rht = run_oracle(d)
     print(f"  whole rows: rel-L2 output {rel_l2(o2.float().cpu().numpy(), ro):.3e}, state "
           f"{rel_l2(h2.cpu().numpy(), rht):.3e}", flush=True)
+
+
+def test_many_short_documents():
+    """1,000 packed documents of 0 to 20 tokens (most shorter than one
+    chunk, some empty), with initial states, grouped heads (ratio 4): the
+    schedule built on the host and the one built on the device agree bitwise,
+    and both match the oracle."""
+    rng = np.random.default_rng(4200)
+    lengths = [int(x) for x in rng.integers(0, 21, size=1000)]
+    cu = gi.cu_from_lengths(lengths)
+    d = gi.make(1, int(cu[-1]), 1, 4, 128, 64, "bf16", 4200, h0_std=0.1, cu_seqlens=cu)
+    check(d, label="1000 short documents")
+    o1, h1 = run_gpu(d)
+    o2, h2 = run_gpu(d, host_cu=False)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+
+
+def test_grouped_heads_ratio_four_fp32():
+    d = gi.make(2, 130, 1, 4, 64, 64, "f32", 4300, h0_std=0.2)
+    check(d, scale=0.6, label="fp32 GVA ratio 4")
