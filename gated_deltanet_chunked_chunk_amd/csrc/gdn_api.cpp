@@ -164,6 +164,7 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.piece_len = plan.piece_len;
     a.piece_ends = nullptr;
     a.piece_starts = nullptr;
+    a.chunk_states = nullptr;
     if (plan.pieces > 1) {
         const size_t per = (size_t)N * (plan.pieces - 1) * H_v * dk;
         a.piece_ends = static_cast<float *>(workspace);

@@ -28,22 +28,22 @@
 //                inverses by fp32 forward substitution with row broadcasts,
 //                the blocks below them by block recursion in fp32), and P.
 //                Writes T (fp32), P (bf16) and gamma to the workspace.
-//   bwd_fstate   per (sequence, value head, 64 value columns), chunks in
-//                order: the forward state recurrence with the dense T, writing
-//                each chunk's entering state M0 to the workspace (bf16,
-//                transposed to [dv][dk]).
+//   the forward kernel (gdn_fwd_bf16.hip, launch_fwd_chunk_states) without
+//                its output: the state recurrence by block substitution,
+//                writing each chunk's entering state M0 to the workspace
+//                (bf16, transposed to [dv][dk]).
 //   bwd_dstate   per (sequence, value head, 64 value columns), chunks in
-//                reverse: the state-gradient recurrence, writing each chunk's
-//                dML to the workspace (bf16, [dv][dk]); dh0 is the gradient
-//                after chunk 0.  Both passes load the next chunk's operands
-//                into registers while computing the current one.
+//                reverse: the state-gradient recurrence with the dense T,
+//                writing each chunk's dML to the workspace (bf16, [dv][dk]);
+//                dh0 is the gradient after chunk 0.  Loader waves fill the
+//                next chunk's buffer while four waves run the recurrence.
 //   bwd_chunk    per (chunk, q/k head), all in parallel: the token gradients
 //                of the chunk from M0 and dML, summed over the value heads
 //                that share the q/k head (dq, dk) and over value columns.
 //
-// Precision: products accumulate in fp32 on bf16 MFMA.  The two state
-// recurrences carry fp32 states and use hi + lo bf16 pairs for computed
-// operands (T, the right-hand sides, Delta', dDelta, dX, e dO); the state
+// Precision: products accumulate in fp32 on bf16 MFMA.  The state-gradient
+// recurrence carries an fp32 state and uses hi + lo bf16 pairs for computed
+// operands (T, dDelta, dX, e dO), as the forward does for its own; the state
 // itself enters products as its hi part, as in the forward.  In bwd_chunk the
 // states, Delta and the other computed operands enter as single bf16
 // roundings except T, rhs and dDelta (hi + lo).
@@ -276,18 +276,6 @@ __device__ __forceinline__ void stage_rows_bf16(uint16_t *dst, int ld, const voi
     }
 }
 
-// T (fp32, workspace) into hi and lo bf16 tiles [64][kL64].
-__device__ __forceinline__ void stage_T(uint16_t *Th, uint16_t *Tl, const float *Tg, int tid) {
-    for (int i = tid; i < kC * kC / 4; i += 256) {
-        const int row = i / 16, c4 = i % 16;
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(Tg + row * kC + 4 * c4);
-        u32x2 h, l;
-        split4(x, h, l);
-        *reinterpret_cast<u32x2 *>(Th + row * kL64 + 4 * c4) = h;
-        *reinterpret_cast<u32x2 *>(Tl + row * kL64 + 4 * c4) = l;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // bwd_prep: per (chunk, value head).
 
@@ -422,7 +410,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
 struct alignas(16) StateSmem {
     uint16_t K[kC * kLK];
     uint16_t Q[kC * kLK];
-    uint16_t X[kC * kL64];      // V (forward) or dO (reverse) tile
+    uint16_t X[kC * kL64];      // dO tile
     uint16_t Th[kC * kL64];
     uint16_t Tl[kC * kL64];
     uint16_t P[kC * kL64];
@@ -431,7 +419,7 @@ struct alignas(16) StateSmem {
 };
 
 // One chunk's operands in flight in registers: each of the 256 threads holds
-// its share of K (and Q), the value-column tile of V (or dO), T, P and the
+// its share of K and Q, the value-column tile of dO, T, P and the
 // gate tables, loaded while the previous chunk is computed.
 struct StatePre {
     u32x4 k[4], q[4], x[2], p[2];
@@ -439,7 +427,6 @@ struct StatePre {
     float gm, gL, bt;
 };
 
-template <bool Rev>
 __device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, const ChunkLoc &cl,
                                             int hk, int j, int tile, int64_t wi, int tid) {
     const uint32_t krow = (uint32_t)a.Hqk * kDK * 2;
@@ -453,11 +440,10 @@ __device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, con
         const int i = tid + 256 * u;
         const uint32_t off = (uint32_t)(i >> 4) * krow + 16 * (i & 15);
         pre.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        if (Rev)
-            pre.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        pre.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     }
     const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
-    const void *xs = Rev ? a.dout : a.v;
+    const void *xs = a.dout;
     const __amdgpu_buffer_rsrc_t rx =
         rsrc(static_cast<const uint16_t *>(xs) + (cl.p * a.Hv + j) * (int64_t)a.dv + tile * kVT,
              (uint32_t)(cl.L - 1) * xrow + kVT * 2);
@@ -471,12 +457,10 @@ __device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, con
 #pragma unroll
     for (int u = 0; u < 4; ++u)
         pre.t[u] = *reinterpret_cast<const f32x4 *>(Tg + 4 * (tid + 256 * u));
-    if (Rev) {
-        const uint16_t *Pg = a.ws_P + wi * (kC * kC);
+    const uint16_t *Pg = a.ws_P + wi * (kC * kC);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            pre.p[u] = *reinterpret_cast<const u32x4 *>(Pg + 8 * (tid + 256 * u));
-    }
+    for (int u = 0; u < 2; ++u)
+        pre.p[u] = *reinterpret_cast<const u32x4 *>(Pg + 8 * (tid + 256 * u));
     if (tid < kC) {
         pre.gm = a.ws_gam[wi * kC + tid];
         pre.gL = a.ws_gam[wi * kC + kC - 1];
@@ -484,21 +468,18 @@ __device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, con
     }
 }
 
-template <bool Rev>
 __device__ __forceinline__ void state_commit(StateSmem &S, const StatePre &pre, int tid) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int i = tid + 256 * u;
         *reinterpret_cast<u32x4 *>(S.K + (i >> 4) * kLK + 8 * (i & 15)) = pre.k[u];
-        if (Rev)
-            *reinterpret_cast<u32x4 *>(S.Q + (i >> 4) * kLK + 8 * (i & 15)) = pre.q[u];
+        *reinterpret_cast<u32x4 *>(S.Q + (i >> 4) * kLK + 8 * (i & 15)) = pre.q[u];
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + 256 * u;
         *reinterpret_cast<u32x4 *>(S.X + (i >> 3) * kL64 + 8 * (i & 7)) = pre.x[u];
-        if (Rev)
-            *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) = pre.p[u];
+        *reinterpret_cast<u32x4 *>(S.P + (i >> 3) * kL64 + 8 * (i & 7)) = pre.p[u];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -598,16 +579,15 @@ __device__ __forceinline__ void t_times(const uint16_t *Th, const uint16_t *Tl,
     }
 }
 
-// The two state recurrences, chunks in order (Rev = false: the forward
-// state, writing each chunk's entering state) or in reverse (Rev = true: the
-// state gradient, writing the gradient of each chunk's leaving state; dh0 at
-// the end).  512 threads: waves 0..3 run the recurrence on the chunk in one
+// The state-gradient recurrence, chunks in reverse, writing the gradient of
+// each chunk's leaving state (dh0 at the end); the states entering the chunks
+// come from the forward kernel (launch_fwd_chunk_states).  512 threads:
+// waves 0..3 run the recurrence on the chunk in one
 // LDS buffer while waves 4..7 fill the other with the next chunk's operands,
 // whose global loads were issued a chunk earlier; one barrier per chunk.  The
 // two roles run separate loops with the same number of barriers, so the
 // loaders' registers and the state's never share the budget.
-template <bool Rev>
-__device__ __forceinline__ void state_pass(const BwdArgs &a) {
+__device__ __forceinline__ void dstate_pass(const BwdArgs &a) {
     __shared__ StateSmem Sb[2];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int n_tiles = a.dv / kVT;
@@ -621,7 +601,7 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
     const int64_t S_elems = (int64_t)kDK * a.dv;
     const float scale = a.scale;
     auto loc = [&](int it) {
-        const int c = Rev ? nch - 1 - it : it;
+        const int c = nch - 1 - it;
         ChunkLoc cl;
         cl.n = n;
         cl.c = c;
@@ -629,23 +609,23 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
         cl.L = (int)min<int64_t>(kC, len - (int64_t)kC * c);
         return cl;
     };
-    auto wslot = [&](int it) { return (base + (Rev ? nch - 1 - it : it)) * a.Hv + j; };
+    auto wslot = [&](int it) { return (base + nch - 1 - it) * a.Hv + j; };
 
     if (w >= 4) {
         const int t = tid - 256;
         StatePre pre;
         if (nch > 0) {
-            state_issue<Rev>(pre, a, loc(0), hk, j, tile, wslot(0), t);
-            state_commit<Rev>(Sb[0], pre, t);
+            state_issue(pre, a, loc(0), hk, j, tile, wslot(0), t);
+            state_commit(Sb[0], pre, t);
             if (nch > 1)
-                state_issue<Rev>(pre, a, loc(1), hk, j, tile, wslot(1), t);
+                state_issue(pre, a, loc(1), hk, j, tile, wslot(1), t);
         }
         __syncthreads();
         for (int it = 0; it < nch; ++it) {
             if (it + 1 < nch) {
-                state_commit<Rev>(Sb[(it + 1) & 1], pre, t);
+                state_commit(Sb[(it + 1) & 1], pre, t);
                 if (it + 2 < nch)
-                    state_issue<Rev>(pre, a, loc(it + 2), hk, j, tile, wslot(it + 2), t);
+                    state_issue(pre, a, loc(it + 2), hk, j, tile, wslot(it + 2), t);
             }
             __syncthreads();
         }
@@ -653,7 +633,7 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
     }
 
     const int col = tile * kVT + 16 * w + lr;   // this lane's value column
-    const float *init = Rev ? a.dht : a.h0;
+    const float *init = a.dht;
     f32x4 h[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -665,43 +645,15 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
     __syncthreads();
     for (int it = 0; it < nch; ++it) {
         const StateSmem &S = Sb[it & 1];
-        // Forward: the state entering the chunk; reverse: the gradient of the
-        // state leaving it.
-        store_state_t((Rev ? a.ws_dhs : a.ws_hs) + wslot(it) * S_elems, h, col, lg);
+        // The gradient of the state leaving the chunk.
+        store_state_t(a.ws_dhs + wslot(it) * S_elems, h, col, lg);
 
         bf16x8 hb[4];
         state_hi(h, hb);
         f32x4 Y[4];
         k_times_state(S.K, hb, Y, lr, lg);
         const float eL = S.eL;
-        if (!Rev) {
-            // rhs = diag(beta) (V - diag(e) K M0); Delta' = diag(l) T rhs;
-            // M <- exp(gamma_L) M + K^T Delta'.
-            f32x4 R[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * mi + 4 * lg + r;
-                    R[mi][r] = S.bt[row] *
-                               (bf2f(S.X[row * kL64 + 16 * w + lr]) - S.e[row] * Y[mi][r]);
-                }
-            bf16x8 rh[2], rl[2];
-            tiles_split(R, rh, rl);
-            f32x4 Dl[4];
-            t_times<false>(S.Th, S.Tl, rh, rl, Dl, lr, lg);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Dl[mi][r] *= S.l[16 * mi + 4 * lg + r];
-            bf16x8 dh[2], dl[2];
-            tiles_split(Dl, dh, dl);
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                h[mt] *= eL;
-            add_xt_times(S.K, dh, dl, h, lr, lg);
-        } else {
+        {
             // dDelta = diag(l) K dML + P^T dO; drhs = T^T dDelta;
             // dM <- exp(gamma_L) dM - K^T diag(beta e) drhs + Q^T diag(e) dO.
             f32x4 dD[4];
@@ -743,7 +695,7 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
         }
         __syncthreads();
     }
-    if (Rev && a.dh0) {
+    if (a.dh0) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -753,12 +705,8 @@ __device__ __forceinline__ void state_pass(const BwdArgs &a) {
     }
 }
 
-__global__ __launch_bounds__(512) void bwd_fstate(BwdArgs a) {
-    state_pass<false>(a);
-}
-
 __global__ __launch_bounds__(512) void bwd_dstate(BwdArgs a) {
-    state_pass<true>(a);
+    dstate_pass(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1195,10 +1143,29 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int64_t seq_blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kVT);
-    hipLaunchKernelGGL(bwd_fstate, dim3((unsigned)seq_blocks), dim3(512), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess)
+    // The states entering the chunks come from the forward kernel run
+    // without its output (its helper/state pipeline, block substitution).
+    FwdArgs f{};
+    f.q = a.q;
+    f.k = a.k;
+    f.v = a.v;
+    f.g = a.g;
+    f.beta = a.beta;
+    f.h0 = a.h0;
+    f.cu = a.cu;
+    f.T = a.T;
+    f.Hqk = a.Hqk;
+    f.Hv = a.Hv;
+    f.dk = a.dk;
+    f.dv = a.dv;
+    f.n_seqs = a.n_seqs;
+    f.scale = a.scale;
+    f.pieces = 1;
+    f.piece_len = a.T;
+    f.chunk_states = a.ws_hs;
+    if ((e = launch_fwd_chunk_states(f, stream)) != hipSuccess)
         return e;
+    const int64_t seq_blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kVT);
     hipLaunchKernelGGL(bwd_dstate, dim3((unsigned)seq_blocks), dim3(512), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;

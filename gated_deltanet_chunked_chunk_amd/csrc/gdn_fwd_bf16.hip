@@ -862,7 +862,8 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 // instance, so the plain kernel carries none of their code).
 // Mode 0: the output pass over whole rows.  Mode 2: the same over pieces
 // that start from the states of piece_starts (an instance of its own, so
-// traces tell the two apart).  Mode 1: the piece
+// traces tell the two apart).  Mode 3: no output; the state entering every
+// chunk is stored (bf16, [dv][dk]) to a.chunk_states for the backward.  Mode 1: the piece
 // ends, for every piece but the last: F from a zero start and real V, and
 // (extra "identity" tiles) the transition Phi, the end state of dk unit
 // columns with V = 0; no output is formed.
@@ -957,17 +958,35 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
-        stage_load<Mode != 1, DK>(st, a, it, 0, t, lane);
-        helper_prepare<Prep, Mode != 1, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        stage_load<Mode == 0 || Mode == 2, DK>(st, a, it, 0, t, lane);
+        helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
                              it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
 
+    // Mode 3: this sequence's first chunk in the chunk numbering.
+    int64_t chunk0 = 0;
+    if (Mode == 3) {
+        if (a.cu) {
+            for (int m = 0; m < it.n; ++m)
+                chunk0 += (a.cu[m + 1] - a.cu[m] + kC - 1) / kC;
+        } else {
+            chunk0 = (int64_t)it.n * ((a.T + kC - 1) / kC);
+        }
+    }
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
-            state_chunk<Mode != 1, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            if (Mode == 3) {
+                // Four consecutive keys per tile: one 8-byte store each.
+                uint16_t *dst = a.chunk_states + ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * DK +
+                                (int64_t)col * DK;
+#pragma unroll
+                for (int mt = 0; mt < DK / 16; ++mt)
+                    *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
+            }
+            state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
-            helper_prepare<Prep, Mode != 1, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
+            helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
                                  min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
@@ -980,7 +999,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             stride = a.dv + DK;
             dst = a.piece_ends + pslot * DK * stride;
             dcol = (it.ident ? a.dv : 0) + col;
-        } else if (a.ht && it.piece == np - 1) {
+        } else if (Mode != 3 && a.ht && it.piece == np - 1) {
             dst = a.ht + hbase;
         }
         if (dst) {
@@ -1088,6 +1107,17 @@ hipError_t launch_dk(const FwdArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kDVT);
+    if (blocks <= 0)
+        return hipSuccess;
+    if (blocks > 0x7fffffff || a.dk != 128 || a.pieces > 1 || a.flags || !a.chunk_states)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
 
 size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv) {
     if (pieces <= 1)

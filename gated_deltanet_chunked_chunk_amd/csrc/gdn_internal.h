@@ -54,7 +54,14 @@ struct FwdArgs {
     int64_t piece_len;
     float *piece_ends;      // [n_seqs, pieces - 1, Hv, dk, dv + dk]: F | Phi of each piece but the last
     float *piece_starts;    // [n_seqs, pieces - 1, Hv, dk, dv]: the state entering pieces 1..
+    uint16_t *chunk_states; // launch_fwd_chunk_states only
 };
+
+// The states entering every chunk (bf16, transposed: [n_chunks, Hv, dv, dk],
+// chunks numbered over the sequences in order) by the forward kernel without
+// its output, for the backward.  bf16, dk = 128; `a` as for the forward with
+// pieces = 1, flags = 0 and chunk_states the destination.
+hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream);
 
 // Workspace bytes of the piece scan for `pieces` pieces per row.
 size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv);
