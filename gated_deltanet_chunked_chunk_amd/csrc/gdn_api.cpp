@@ -20,12 +20,11 @@ bool aligned16(const void *p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// The forward's shapes: both dtypes take dk, dv in {64, 128}.
 bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
-    if (dtype == GDN_BF16)
-        return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
-    if (dtype == GDN_F32)
-        return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
-    return false;
+    if (dtype != GDN_BF16 && dtype != GDN_F32)
+        return false;
+    return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
 }
 
 // Pieces per row for the piece-parallel scan of long rows (1: one pass over
