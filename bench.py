@@ -240,6 +240,47 @@ def measure_long(gdn, gi, torch, dev, steps=3):
     return out
 
 
+def measure_k256(gdn, gi, torch, dev, steps, warmup):
+    """Head dimension 256 (B=8, T=2048, H=32, dk=dv=256, bf16; inputs drawn
+    on the device with the same recipe; chunks of 32 tokens): milliseconds
+    per forward, tokens/s, HBM and MFMA fractions, and a check of one head
+    against the fp64 oracle."""
+    import oracle
+    name = "k256_bf16"
+    c = gi.CONFIGS[name]
+    B, T, Hqk, Hv, dk, dv = c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"]
+    t = gi.make_device(B, T, Hqk, Hv, dk, dv, c["seed"], device=dev)
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    o = torch.empty_like(v)
+    ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht,
+                                     stream=stream.cuda_stream)
+    ms = _time_calls(torch, stream, call, steps, warmup)
+    bs, hs = 3, 21
+    sel = lambda x: x[bs:bs + 1, :, hs:hs + 1].float().cpu().numpy()
+    ro, rh = oracle.gdn_fwd(sel(q), sel(k), sel(v), sel(g), sel(beta))
+    err_o = float(np.linalg.norm(sel(o) - ro) / np.linalg.norm(ro))
+    err_h = float(np.linalg.norm(ht[bs:bs + 1, hs:hs + 1].cpu().numpy() - rh) / np.linalg.norm(rh))
+    nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
+    flops = chunked_flops(B, T, Hv, dk, dv, C=32)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] dk=256: {ms * 1e3:.1f} us/call ({achieved:.0f} GB/s); check head "
+        f"(b={bs}, h={hs}) rel-L2 output {err_o:.2e}, state {err_h:.2e}")
+    del q, k, v, g, beta, o, t
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, chunk=32, zero initial "
+                        f"state, output + final state",
+            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes,
+                         "mfma_bf16_tflops": flops / (ms * 1e-3) / 1e12,
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "kernels": ["gdn_fwd_bf16<false, 0, 256>"]},
+            "check": {"head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h}}
+
+
 def kernel_source_hash():
     """sha256 of the kernel's code: its source with // comments, trailing
     blanks and empty lines removed, so editing a comment does not count as a
@@ -310,6 +351,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step and preparation measurements")
+    ap.add_argument("--no-k256", action="store_true",
+                    help="skip the head-dimension-256 measurement")
     ap.add_argument("--long", action="store_true",
                     help="also time the long row (B=1, T=1,064,960), with and without pieces")
     ap.add_argument("--flush-mb", type=int, default=512,
@@ -431,6 +474,11 @@ def main():
         prep = measure_prep(gdn, torch, q, k, v, g, beta, ms_per_step, steps=200, warmup=50)
         decode = measure_decode(gdn, gi, torch, dev, steps=200, warmup=100)
 
+    k256 = None
+    if not args.no_k256:
+        log("[bench] head dimension 256")
+        k256 = measure_k256(gdn, gi, torch, dev, steps=200, warmup=100)
+
     long_row = None
     if args.long:
         log("[bench] long row")
@@ -483,6 +531,7 @@ def main():
         "bwd": bwd,
         "prep": prep,
         "decode": decode,
+        "k256": k256,
         "long_row": long_row,
         "wall_s_timed_region": wall,
     }

@@ -260,7 +260,7 @@ def gdn_prepare_inputs(q, k, g, beta, use_qk_l2norm=True, gate_activation=False,
     """(q', k', g', beta') with each q and k row divided by its L2 norm
     (use_qk_l2norm) and g, beta passed through logsigmoid and sigmoid
     (gate_activation); what an option does not touch is returned as given.
-    q, k: [..., dk] (bf16 or fp32, dk <= 128); g, beta: fp32 of one shape."""
+    q, k: [..., dk] (bf16 or fp32, dk <= 256); g, beta: fp32 of one shape."""
     import torch
     lib = load()
     _device_contiguous(torch, [("q", q), ("k", k), ("g", g), ("beta", beta)])

@@ -20,15 +20,17 @@ bool aligned16(const void *p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-// The forward's shapes: both dtypes take dk, dv in {64, 128}.
+// The forward's shapes: both dtypes take dk, dv in {64, 128, 256}.
 bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
     if (dtype != GDN_BF16 && dtype != GDN_F32)
         return false;
-    return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    return (dk == 64 || dk == 128 || dk == 256) && (dv == 64 || dv == 128 || dv == 256);
 }
 
 // Pieces per row for the piece-parallel scan of long rows (1: one pass over
-// whole rows), for batch-mode bf16 calls.  With P pieces the first pass runs
+// whole rows), for batch-mode bf16 calls with dk <= 128 (the scan's transition
+// tile of a 256-wide key space does not fit in LDS).  With P pieces the
+// first pass runs
 // (P - 1) pieces x (value tiles + dk / 64 transition tiles) workgroups and
 // the output pass P pieces x value tiles, each workgroup walking about
 // chunks / P chunks; one workgroup per CU is resident.  The plan minimises
@@ -48,7 +50,7 @@ struct PiecePlan {
 PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk, int32_t dv,
                       bool packed) {
     PiecePlan best{1, T};
-    if (packed || dtype != GDN_BF16 || dv % 64 != 0)
+    if (packed || dtype != GDN_BF16 || dk > 128 || dv % 64 != 0)
         return best;
     const int64_t rows = B * H_v;
     const int64_t items = rows * (dv / 64);
@@ -291,7 +293,7 @@ gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, co
     if (l2) {
         if (n_qk_rows < 0 || n_qk_rows > INT64_MAX / 256 || dk < 1)
             return GDN_ERR_INVALID_ARG;
-        if (dk > 128)
+        if (dk > 256)
             return GDN_ERR_UNSUPPORTED;
     }
     if (gate && (n_gates < 0 || n_gates > INT64_MAX / 2))
@@ -342,7 +344,8 @@ gdn_status gdn_recurrent_step(gdn_dtype dtype, int64_t N, int32_t H_qk, int32_t 
         return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16)
         return GDN_ERR_UNSUPPORTED;
-    if (H_v % H_qk != 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+    const auto size_ok = [](int32_t d) { return d == 64 || d == 128 || d == 256; };
+    if (H_v % H_qk != 0 || !size_ok(dk) || !size_ok(dv))
         return GDN_ERR_UNSUPPORTED;
     if (!slots && n_slots < N)
         return GDN_ERR_INVALID_ARG;

@@ -99,6 +99,20 @@ constexpr int kSDT = 16;        // D blocks, transposed (one 32-byte row per col
 constexpr int kAD = 20;         // column stride of the helpers' A_ii copies (conflict-free column reads)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 
+// Tokens per chunk.  With dk = 256 a chunk is 32 tokens, and the two key
+// halves of its rows take the places of rows 0..31 and 32..63 of the
+// 64 x 128 K and Q tiles: key 128 h + x of row r is column x of tile row
+// 32 h + r.  Every tile layout, fragment read and LDS size stays as it is.
+template <int DK>
+constexpr int chunk_len() {
+    return DK == 256 ? 32 : kC;
+}
+// Accumulator tiles of the state slice (16 keys each).
+template <int DK>
+constexpr int state_tiles() {
+    return DK == 256 ? 16 : 8;
+}
+
 // K, Q (64 x 128) and V (64 x 64) tiles are unpadded, with the pieces of each
 // row permuted.  A K or Q row is 256 bytes, one bank cycle: its 16-byte slot c
 // is stored at slot c ^ sigma(r), where sigma permutes the bits of r % 16
@@ -295,8 +309,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 // 128 bf16 values, 8 each; returns 1 / ||row|| (fp32) in every lane of the
 // row.  The rows stay as they are: the factors are applied where the rows
 // enter the chunk equations.
-__device__ __forceinline__ float row_inv_norm(const u32x4 &x) {
-    float s = 0.0f;
+__device__ __forceinline__ float sum_sq8(const u32x4 &x, float s) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         // The element goes through a scalar: a bit cast of the vector
@@ -305,7 +318,16 @@ __device__ __forceinline__ float row_inv_norm(const u32x4 &x) {
         const bf16x2 p = __builtin_bit_cast(bf16x2, w);
         s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
     }
-    return inv_l2_norm(row16_sum(s));
+    return s;
+}
+
+__device__ __forceinline__ float row_inv_norm(const u32x4 &x) {
+    return inv_l2_norm(row16_sum(sum_sq8(x, 0.0f)));
+}
+
+// The same for a 256-wide row held as two 128-wide halves by the same lanes.
+__device__ __forceinline__ float row_inv_norm(const u32x4 &x0, const u32x4 &x1) {
+    return inv_l2_norm(row16_sum(sum_sq8(x1, sum_sq8(x0, 0.0f))));
 }
 
 // x from the lane of the quad whose index is Sel.
@@ -348,12 +370,15 @@ struct Stage {
 
 // Without Full (the piece ends, which form no output) Q is not loaded.  DK
 // is the key dimension in HBM; with DK = 64 the LDS rows keep their 128
-// columns and the lanes of the upper 64 stage zeros.
+// columns and the lanes of the upper 64 stage zeros.  With DK = 256, tile
+// row t/16 + 16 i is key half i / 2 of chunk row t/16 + 16 (i % 2), and only
+// the 32 value rows of the chunk are staged.
 template <bool Full, int DK>
 __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const Item &it, int c,
                                            int t, int lane) {
-    const int64_t p = it.p0 + (int64_t)kC * c;
-    const int L = min(kC, it.len - kC * c);
+    constexpr int CL = chunk_len<DK>();
+    const int64_t p = it.p0 + (int64_t)CL * c;
+    const int L = min(CL, it.len - CL * c);
     const uint32_t krow = (uint32_t)a.Hqk * DK * 2;  // bytes between tokens
     const uint32_t vrow = (uint32_t)a.Hv * a.dv * 2;
     const uint32_t grow = (uint32_t)a.Hv * 4;
@@ -369,7 +394,8 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
     const __amdgpu_buffer_rsrc_t rb = rsrc(a.beta + p * a.Hv + it.j, (L - 1) * grow + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (t / 16 + 16 * i) * krow + 16 * (t % 16);
+        const uint32_t off = DK == 256 ? (t / 16 + 16 * (i % 2)) * krow + 16 * (t % 16 + 16 * (i / 2))
+                                       : (t / 16 + 16 * i) * krow + 16 * (t % 16);
         if (kq_pad) {
             st.k[i] = u32x4{0u, 0u, 0u, 0u};
             st.q[i] = st.k[i];
@@ -381,7 +407,8 @@ __device__ __forceinline__ void stage_load(Stage &st, const FwdArgs &a, const It
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (t / 8 + 32 * i) * vrow + 16 * (t % 8), 0, 0);
+        st.v[i] = 32 * i < CL ? __builtin_amdgcn_raw_buffer_load_b128(rv, (t / 8 + 32 * i) * vrow + 16 * (t % 8), 0, 0)
+                              : u32x4{0u, 0u, 0u, 0u};
     st.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane * grow, 0, 0));
     st.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lane * grow, 0, 0));
 }
@@ -408,12 +435,10 @@ __device__ __forceinline__ f32x4 block_product(const bf16x8 (&xi)[4], const bf16
     return c;
 }
 
-// -A block (I, J), I > J: -beta_r exp(gamma_r - gamma_s) (k_r . k_s), hi + lo.
-// Nrm: k_r . k_s scaled by nu_r nu_s (the in-op L2 norm).
-template <int I, int J, bool Nrm, int DK>
-__device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], const bf16x8 (&kj)[4],
-                                        int lr, int lg) {
-    f32x4 c = block_product<DK / 32>(ki, kj);
+// -A block (I, J), I > J, from c = the block of K K^T: -beta_r exp(gamma_r - gamma_s)
+// (k_r . k_s), hi + lo.  Nrm: k_r . k_s scaled by nu_r nu_s (the in-op L2 norm).
+template <int I, int J, bool Nrm>
+__device__ __forceinline__ void a_finish(ChunkBuf &B, f32x4 c, int lr, int lg) {
     if (Nrm)
         c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
@@ -429,12 +454,16 @@ __device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], cons
     *reinterpret_cast<u32x2 *>(B.Anl + o) = lo;
 }
 
-// P block (I, J), I >= J: exp(gamma_r - gamma_s) (q_r . k_s), s <= r.
-// Nrm: q_r . k_s scaled by mu_r nu_s (the in-op L2 norm).
 template <int I, int J, bool Nrm, int DK>
-__device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], const bf16x8 (&kj)[4],
+__device__ __forceinline__ void a_block(ChunkBuf &B, const bf16x8 (&ki)[4], const bf16x8 (&kj)[4],
                                         int lr, int lg) {
-    f32x4 c = block_product<DK / 32>(qi, kj);
+    a_finish<I, J, Nrm>(B, block_product<DK / 32>(ki, kj), lr, lg);
+}
+
+// P block (I, J), I >= J, from c = the block of Q K^T: exp(gamma_r - gamma_s)
+// (q_r . k_s), s <= r.  Nrm: q_r . k_s scaled by mu_r nu_s (the in-op L2 norm).
+template <int I, int J, bool Nrm>
+__device__ __forceinline__ void p_finish(ChunkBuf &B, f32x4 c, int lr, int lg) {
     if (Nrm)
         c = c * (B.mu[16 * I + lr] * ld4f(B.nu + 16 * J + 4 * lg));
     const float g = B.gam[16 * I + lr];
@@ -452,11 +481,16 @@ __device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], cons
     *reinterpret_cast<u32x2 *>(B.P + (16 * I + lr) * kSP + 16 * J + 4 * lg) = pack4(val);
 }
 
-// Diagonal block A_II (strictly lower part, negated) into ad, column-major.
-template <int I, bool Nrm, int DK>
-__device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
-                                           int lr, int lg) {
-    f32x4 c = block_product<DK / 32>(ki, ki);
+template <int I, int J, bool Nrm, int DK>
+__device__ __forceinline__ void p_block(ChunkBuf &B, const bf16x8 (&qi)[4], const bf16x8 (&kj)[4],
+                                        int lr, int lg) {
+    p_finish<I, J, Nrm>(B, block_product<DK / 32>(qi, kj), lr, lg);
+}
+
+// Diagonal block A_II (strictly lower part, negated) into ad, column-major,
+// from c = the block of K K^T.
+template <int I, bool Nrm>
+__device__ __forceinline__ void diag_finish(float *ad, const ChunkBuf &B, f32x4 c, int lr, int lg) {
     if (Nrm)
         c = c * (B.nu[16 * I + lr] * ld4f(B.nu + 16 * I + 4 * lg));
     const float g = B.gam[16 * I + lr], b = B.bt[16 * I + lr];
@@ -467,6 +501,12 @@ __device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const b
         const float e = __expf(fminf(g - gc[r], 0.0f));
         ad[col * kAD + lr] = col < lr ? -(b * e * c[r]) : 0.0f;
     }
+}
+
+template <int I, bool Nrm, int DK>
+__device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
+                                           int lr, int lg) {
+    diag_finish<I, Nrm>(ad, B, block_product<DK / 32>(ki, ki), lr, lg);
 }
 
 // x += (a from lane R of this lane's 16-lane row) * b: one v_fmac_f32 with a
@@ -594,6 +634,44 @@ __device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, in
     }
 }
 
+// dk = 256: block (I, J) of X K^T over the 256 keys, both key halves
+// (tile row blocks I, J and I + 2, J + 2).
+template <int I, int J>
+__device__ __forceinline__ f32x4 gram256(const uint16_t *X, const uint16_t *K, const KqBase &kb) {
+    bf16x8 x[4], k[4];
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        load_block<4>(x, X, kb, I + 2 * hf);
+        load_block<4>(k, K, kb, J + 2 * hf);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            c = mma(k[kk], x[kk], c);
+    }
+    return c;
+}
+
+// The per-chunk products of a 32-token chunk (dk = 256): helper 0 the two
+// diagonal blocks of A and their inverses, helper 1 A10 and P00, helper 2
+// P10, helper 3 P11.
+template <bool Nrm>
+__device__ __forceinline__ void helper_products_k256(Smem &S, ChunkBuf &B, int hw, int lr, int lg,
+                                                     int lane) {
+    const KqBase kb = kq_base(lr, lg);
+    if (hw == 0) {
+        diag_finish<0, Nrm>(S.Ad[0], B, gram256<0, 0>(B.K, B.K, kb), lr, lg);
+        diag_finish<1, Nrm>(S.Ad[1], B, gram256<1, 1>(B.K, B.K, kb), lr, lg);
+        diag_inverse_all(B, S, lane);  // blocks 2, 3 invert the identity left in Ad[2], Ad[3]
+    } else if (hw == 1) {
+        a_finish<1, 0, Nrm>(B, gram256<1, 0>(B.K, B.K, kb), lr, lg);
+        p_finish<0, 0, Nrm>(B, gram256<0, 0>(B.Q, B.K, kb), lr, lg);
+    } else if (hw == 2) {
+        p_finish<1, 0, Nrm>(B, gram256<1, 0>(B.Q, B.K, kb), lr, lg);
+    } else {
+        p_finish<1, 1, Nrm>(B, gram256<1, 1>(B.Q, B.K, kb), lr, lg);
+    }
+}
+
 // Helper waves: put chunk c (already in `st`) into LDS buffer B with its
 // decay tables, A blocks, P and diagonal inverses.  Once `st` is in LDS it is
 // refilled with chunk `next` (if next >= 0), so those loads are in flight
@@ -611,7 +689,20 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         asm volatile("" : "+v"(lrv), "+v"(lgv), "+v"(t));
     }
     const int lr = lrv, lg = lgv;
-    if (Prep) {
+    if (Prep && DK == 256) {
+        // The rows' inverse L2 norms (1 without the option): the lanes that
+        // stage row t/16 + 16 i (i < 2) hold both of its key halves.
+        const bool l2 = a.flags & kStepL2Norm;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float nk = l2 ? row_inv_norm(st.k[i], st.k[i + 2]) : 1.0f;
+            const float nq = l2 && Full ? row_inv_norm(st.q[i], st.q[i + 2]) : 1.0f;
+            if (t % 16 == 0) {
+                B.nu[t / 16 + 16 * i] = nk;
+                B.mu[t / 16 + 16 * i] = nq;
+            }
+        }
+    } else if (Prep) {
         // The rows' inverse L2 norms (1 without the option), one lane per row.
         const bool l2 = a.flags & kStepL2Norm;
 #pragma unroll
@@ -667,7 +758,10 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         B.el[lane] *= nu;
     }
 
-    helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
+    if constexpr (DK == 256)
+        helper_products_k256<Prep>(S, B, hw, lr, lg, lane);
+    else
+        helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
 }
 
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
@@ -858,6 +952,157 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
     }
 }
 
+// State waves, dk = 256: one 32-token chunk of (a5)-(a7) for value columns
+// [16 s, 16 s + 16), with the wave's [256 x 16] state slice in 16
+// accumulator tiles.  The steps are those of state_chunk over two row
+// blocks: K M0 and Q M0 take eight k-steps (key half h of row block i is
+// tile row block i + 2 h), the solve one substitution step, and the update
+// one 32-deep k-step per key tile (keys 128 h + x from tile rows 32 h ..).
+template <bool Out, bool Nrm>
+__device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, const FwdArgs &a,
+                                                 const Item &it, int c, int s, int lane,
+                                                 f32x4 (&h)[16]) {
+    constexpr int CL = 32;
+    const int lr = lane & 15, lg = lane >> 4;
+    bf16x8 hb[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+    // (a5, a7) X = K M0 and Q M0, in four segments (row block sg / 2, key
+    // half sg % 2), fragments loaded one segment ahead.
+    f32x4 X[2], Oa[2];
+    bf16x8 fk[2][4], fq[2][4];
+    const KqBase kb = kq_base(lr, lg);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        fk[0][kk] = frag_kq(B.K, kb, 0, kk);
+        fq[0][kk] = frag_kq(B.Q, kb, 0, kk);
+    }
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+        if (sg < 3) {
+            const int m = ((sg + 1) >> 1) + 2 * ((sg + 1) & 1);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                fk[(sg + 1) & 1][kk] = frag_kq(B.K, kb, m, kk);
+                fq[(sg + 1) & 1][kk] = frag_kq(B.Q, kb, m, kk);
+            }
+        }
+        const int mi = sg >> 1, hf = sg & 1;
+        if (hf == 0) {
+            X[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Oa[mi] = X[mi];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            X[mi] = mma(fk[sg & 1][kk], hb[4 * hf + kk], X[mi]);
+            Oa[mi] = mma(fq[sg & 1][kk], hb[4 * hf + kk], Oa[mi]);
+        }
+    }
+    // Right-hand sides R_i = diag(beta) (V - diag(exp gamma) X); O scaled.
+    const int vbase = v_at(4 * lg + (lr >> 2), 4 * s + (lr & 3));
+    f32x4 R[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
+        const f32x4 egq = Nrm ? ld4f(B.egq + 16 * mi + 4 * lg) : eg4;
+        const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
+        const u32x2 vv = ld_tr(B.V + vbase + 16 * kDVT * mi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float vr = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
+            R[mi][r] = bt4[r] * (vr - eg4[r] * X[mi][r]);
+            Oa[mi][r] *= egq[r];
+        }
+    }
+    // (a4, a5) Delta_0 = D_0 R_0, Delta_1 = D_1 (R_1 - A_10 Delta_0), split
+    // products as in state_chunk.
+    const bf16x8 An = cat(ld8(B.Anh + lr * kSN + 4 * lg), ld8(B.Anl + lr * kSN + 4 * lg));
+    bf16x8 Dd[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int dofs = (16 * i + 4 * lg + (lr >> 2)) * kSDT + 4 * (lr & 3);
+        Dd[i] = cat(ld_tr(B.DhT + dofs), ld_tr(B.DlT + dofs));
+    }
+    u32x2 dh[2], dl[2];
+    f32x4 D[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        u32x2 rh, rl;
+        split4(R[i], rh, rl);
+        f32x4 d = mma(Dd[i], cat(rh, rh), f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mma(Dd[i], cat(rl, rl), d);
+        D[i] = d;
+        split4(d, dh[i], dl[i]);
+        if (i == 0) {
+            R[1] = mma(An, cat(dh[0], dh[0]), R[1]);
+            R[1] = mma(An, cat(dl[0], dl[0]), R[1]);
+        }
+    }
+    // (a6) M_L = exp(gamma_L) M0 + K^T Delta'; the K^T fragment of key tile
+    // mt is tile mt % 8 of tile rows 32 (mt / 8) .., loaded one tile ahead.
+    bf16x8 dph, dpl;
+    {
+        u32x2 ph[2], pl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const f32x4 el4 = ld4f(B.el + 16 * i + 4 * lg);
+            split4(el4 * D[i], ph[i], pl[i]);
+        }
+        dph = cat(ph[0], ph[1]);
+        dpl = cat(pl[0], pl[1]);
+    }
+    const float eL = B.eL;
+    const int ktrow = 4 * lg + (lr >> 2);
+    int ktb = kq_slot(ktrow, lr & 3);
+    asm volatile("" : "+v"(ktb));
+    auto ktf = [&](int mt) {
+        const uint16_t *p = B.K + (ktb ^ (32 * ((mt & 7) >> 1))) + 4 * (mt & 1) + 32 * (mt >> 3) * kDK;
+        return cat(ld_tr(p), ld_tr(p + 16 * kDK));
+    };
+    bf16x8 kt[2];
+    kt[0] = ktf(0);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+        if (mt < 15)
+            kt[(mt + 1) & 1] = ktf(mt + 1);
+        h[mt] *= eL;
+        h[mt] = mma(kt[mt & 1], dph, h[mt]);
+        h[mt] = mma(kt[mt & 1], dpl, h[mt]);
+    }
+
+    if constexpr (!Out)
+        return;
+    // (a7) O += P Delta (hi parts), staged through LDS as in state_chunk.
+    const bf16x8 db = cat(dh[0], dh[1]);
+    bf16x8 pf[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+        pf[mi] = frag_perm(B.P + (16 * mi + lr) * kSP, lg);
+    uint16_t *ost = S.Ost[s];
+    auto ost_x = [](int col) {
+        return (((col >> 1) & 1) << 3) ^ (((col >> 2) & 1) << 1) ^ (((col >> 3) & 1) << 2);
+    };
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        Oa[mi] = mma(pf[mi], db, Oa[mi]);
+        *reinterpret_cast<u32x2 *>(ost + lr * kC + 4 * ((4 * mi + lg) ^ ost_x(lr))) =
+            pack4(a.scale * Oa[mi]);
+    }
+    const int L = min(CL, it.len - CL * c);
+    const int64_t p = it.p0 + (int64_t)CL * c;
+    uint16_t *o = static_cast<uint16_t *>(a.o) + ((p + lane) * a.Hv + it.j) * (int64_t)a.dv + it.c0 + 16 * s;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = 8 * hf + (lr >> 2), c1 = c0 + 4;
+        const int w = 4 * lg + (lr & 3);
+        const u32x2 r0 = ld_tr(ost + c0 * kC + 4 * (w ^ ost_x(c0)));
+        const u32x2 r1 = ld_tr(ost + c1 * kC + 4 * (w ^ ost_x(c1)));
+        if (lane < L)
+            *reinterpret_cast<u32x4 *>(o + 8 * hf) = u32x4{r0.x, r0.y, r1.x, r1.y};
+    }
+}
+
 // Prep: the in-op preparation options of a.flags are honoured (a separate
 // instance, so the plain kernel carries none of their code).
 // Mode 0: the output pass over whole rows.  Mode 2: the same over pieces
@@ -870,6 +1115,7 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 template <bool Prep, int Mode, int DK>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     __shared__ Smem S;
+    constexpr int CL = chunk_len<DK>(), NH = state_tiles<DK>();
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
     // Work item.  Items that read the same q/k head (the dv tiles and the
@@ -907,11 +1153,17 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         p1 = row0 + s1;
     }
     it.len = (int)(p1 - it.p0);
-    it.nchunks = (it.len + kC - 1) / kC;
+    it.nchunks = (it.len + CL - 1) / CL;
 
     for (int i = tid; i < kC * kSP; i += kThreads) {
         S.buf[0].P[i] = 0;
         S.buf[1].P[i] = 0;
+    }
+    if (DK == 256) {  // blocks 2, 3 of the inverses: the identity, never read
+        for (int i = tid; i < 16 * kAD; i += kThreads) {
+            S.Ad[2][i] = 0.0f;
+            S.Ad[3][i] = 0.0f;
+        }
     }
     if (tid == 0)
         S.hsync = 0;
@@ -926,7 +1178,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     // The slot of (row, piece, head) in the piece arrays.
     const int64_t pslot = ((int64_t)it.n * (a.pieces - 1) + it.piece) * a.Hv + it.j;
 
-    f32x4 h[8];
+    f32x4 h[NH];
     Stage st;
     int meet = 0;
     // Issue priority on the shared SIMDs follows the critical paths: the
@@ -944,7 +1196,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             src = a.h0 + hbase;
         if (src) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NH; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = key_of(mt, lg, r);
@@ -952,14 +1204,14 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                 }
         } else {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NH; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
         stage_load<Mode == 0 || Mode == 2, DK>(st, a, it, 0, t, lane);
-        helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(kC, it.len),
+        helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(CL, it.len),
                              it.nchunks > 1 ? 1 : -1);
     }
     lds_barrier();
@@ -969,9 +1221,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     if (Mode == 3) {
         if (a.cu) {
             for (int m = 0; m < it.n; ++m)
-                chunk0 += (a.cu[m + 1] - a.cu[m] + kC - 1) / kC;
+                chunk0 += (a.cu[m + 1] - a.cu[m] + CL - 1) / CL;
         } else {
-            chunk0 = (int64_t)it.n * ((a.T + kC - 1) / kC);
+            chunk0 = (int64_t)it.n * ((a.T + CL - 1) / CL);
         }
     }
     for (int c = 0; c < it.nchunks; ++c) {
@@ -984,10 +1236,13 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                 for (int mt = 0; mt < DK / 16; ++mt)
                     *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
             }
-            state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            if constexpr (DK == 256)
+                state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            else
+                state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
         } else if (c + 1 < it.nchunks) {
             helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
-                                 min(kC, it.len - kC * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
+                                 min(CL, it.len - CL * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
     }
@@ -1004,7 +1259,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         }
         if (dst) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < NH; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = key_of(mt, lg, r);
@@ -1083,18 +1338,22 @@ hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
                            stream, a);
         return hipGetLastError();
     }
-    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
-    const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
-    const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
-    if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
-                       stream, a);
-    hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
-                       dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
-                       stream, a);
-    return hipGetLastError();
+    if constexpr (DK == 256) {
+        return hipErrorInvalidValue;  // the piece scan covers dk <= 128
+    } else {
+        const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
+        const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
+        const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
+        if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
+                           stream, a);
+        hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
+                           dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
 }
 
 template <bool Prep>
@@ -1103,6 +1362,8 @@ hipError_t launch_dk(const FwdArgs &a, hipStream_t stream) {
         return launch_passes<Prep, 128>(a, stream);
     if (a.dk == 64)
         return launch_passes<Prep, 64>(a, stream);
+    if (a.dk == 256)
+        return launch_passes<Prep, 256>(a, stream);
     return hipErrorInvalidValue;
 }
 

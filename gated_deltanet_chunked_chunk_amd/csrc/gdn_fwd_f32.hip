@@ -5,9 +5,10 @@
 // accurate expf.  fp32 inputs come with tolerances tighter than a bf16 MFMA
 // path can meet, and the workloads that use them are small, so this kernel
 // favours plainness: one workgroup per (sequence, value head, 32 value
-// columns), every step an LDS-staged loop separated by barriers.
+// columns), every step an LDS-staged loop separated by barriers.  Chunks are
+// 64 tokens, or 32 with dk = 256 (so that the K and Q tiles fit in LDS).
 //
-// Per chunk of L <= 64 tokens starting from state M0 ([dk][dv], M = S^T):
+// Per chunk of L <= C tokens starting from state M0 ([dk][dv], M = S^T):
 //   gamma_r = g_1 + ... + g_r
 //   A[r][s] = beta_r exp(gamma_r - gamma_s) (k_r . k_s),  s < r
 //   T' = (I + A)^-1 diag(beta)              (forward substitution per column)
@@ -24,11 +25,15 @@
 namespace gdn {
 namespace {
 
-constexpr int kC = 64;
 constexpr int kDVT = 32;
 constexpr int kThreads = 256;
 
 template <int DK>
+constexpr int chunk_f32() {
+    return DK == 256 ? 32 : 64;
+}
+
+template <int DK, int kC = chunk_f32<DK>()>
 struct SmemF32 {
     float K[kC][DK + 1];
     float Q[kC][DK + 1];
@@ -42,6 +47,7 @@ struct SmemF32 {
 
 template <int DK>
 __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
+    constexpr int kC = chunk_f32<DK>();
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SmemF32<DK> &S = *reinterpret_cast<SmemF32<DK> *>(smem_raw);
     const int tid = threadIdx.x;
@@ -224,7 +230,11 @@ hipError_t launch_dk(const FwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream) {
-    return a.dk == 64 ? launch_dk<64>(a, stream) : launch_dk<128>(a, stream);
+    if (a.dk == 64)
+        return launch_dk<64>(a, stream);
+    if (a.dk == 256)
+        return launch_dk<256>(a, stream);
+    return launch_dk<128>(a, stream);
 }
 
 }  // namespace gdn

@@ -81,7 +81,7 @@ __device__ __forceinline__ f32x4 sum_row_quads(f32x4 x) {
 
 template <int DK>
 __global__ __launch_bounds__(256) void recurrent_step(StepArgs a) {
-    __shared__ float ks[128], qs[128], nrm[2];
+    __shared__ float ks[DK], qs[DK], nrm[2];
     __shared__ f32x4 ypart[4][16], opart[4][16];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int cg = lane & 15, rq = lane >> 4;  // 4-column group; row within the wave's four
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void recurrent_step(StepArgs a) {
 }
 
 // Rows of q and k divided by their L2 norms, one wave per row (any dk up to
-// 128), and the gate activations.
+// 256), and the gate activations.
 __global__ __launch_bounds__(256) void preprocess(PrepArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -185,9 +185,9 @@ __global__ __launch_bounds__(256) void preprocess(PrepArgs a) {
         const int64_t row = isq ? wave - a.qk_rows : wave;
         const void *src = isq ? a.q : a.k;
         void *dst = isq ? a.q_out : a.k_out;
-        float x[2], s = 0.0f;
+        float x[4], s = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const int i = lane + 64 * u;
             x[u] = i < a.dk ? load_el(src, row * a.dk + i, bf) : 0.0f;
             s += x[u] * x[u];
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void preprocess(PrepArgs a) {
             s += __shfl_xor(s, o);
         const float inv = inv_l2_norm(s);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 4; ++u) {
             const int i = lane + 64 * u;
             if (i < a.dk)
                 store_el(dst, row * a.dk + i, x[u] * inv, bf);
@@ -307,6 +307,8 @@ hipError_t launch_recurrent_step(const StepArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(recurrent_step<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (a.dk == 64)
         hipLaunchKernelGGL(recurrent_step<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (a.dk == 256)
+        hipLaunchKernelGGL(recurrent_step<256>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -321,6 +323,7 @@ hipError_t launch_preprocess(const PrepArgs &a, hipStream_t stream) {
         case 4: return launch_vec<4, true>(a, stream);
         case 8: return launch_vec<8, true>(a, stream);
         case 16: return launch_vec<16, true>(a, stream);
+        case 32: return launch_vec<32, true>(a, stream);
         }
     } else {
         switch (lpr) {
@@ -328,6 +331,7 @@ hipError_t launch_preprocess(const PrepArgs &a, hipStream_t stream) {
         case 8: return launch_vec<8, false>(a, stream);
         case 16: return launch_vec<16, false>(a, stream);
         case 32: return launch_vec<32, false>(a, stream);
+        case 64: return launch_vec<64, false>(a, stream);
         }
     }
     const int64_t by_rows = (2 * a.qk_rows + 3) / 4;

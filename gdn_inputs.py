@@ -173,6 +173,9 @@ CONFIGS = {
     # one decode step: 256 sequences of one token, a 256-slot state cache (h0)
     "decode_bf16": dict(B=256, T=1, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", seed=1005,
                         h0_std=0.5),
+    # head dim 256: the shape of the B=8, T=2048, H=32, D=256 row of the
+    # flash-linear-attention benchmark table (drawn on the device)
+    "k256_bf16": dict(B=8, T=2048, Hqk=32, Hv=32, dk=256, dv=256, dtype="bf16", seed=1006),
 }
 
 

@@ -78,7 +78,8 @@ typedef enum {
  * start states follow from a short scan over the pieces, then every piece
  * is run again from its true start).  The workspace holds, per piece but the
  * last and head, F and Phi (dk x (dv + dk) fp32) and the start state
- * (dk x dv fp32).  Returns 0 as well for sizes the forward would reject.
+ * (dk x dv fp32).  dk = 256 always runs whole rows (returns 0).  Returns 0
+ * as well for sizes the forward would reject.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B
  * (packed calls never use the piece scan).
@@ -94,7 +95,10 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *                B must be 1 and T is the total packed length.
  *   H_qk, H_v    q/k heads and value heads; H_v % H_qk == 0.
  *   dk, dv       key and value head dimensions.  Supported: dk, dv in
- *                {64, 128} for both dtypes.
+ *                {64, 128, 256} for both dtypes (dk = 256: the key width
+ *                of the Gated DeltaNet 1.3B preset's kernels on the
+ *                jax-linear-attention page, "Benchmarks", footnote (d);
+ *                those calls walk chunks of 32 tokens).
  *   q, k         [B, T, H_qk, dk]
  *   v            [B, T, H_v, dv]
  *   g            [B, T, H_v] fp32, natural-log decay (a = exp(g)); finite.
@@ -205,7 +209,7 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
  *
  *   dtype        dtype of q, k, q_out and k_out.
  *   n_qk_rows    rows of dk elements in q (and in k), e.g. B * T * H_qk.
- *   dk           1 <= dk <= 128.
+ *   dk           1 <= dk <= 256.
  *   q, k         inputs; q_out, k_out: outputs of the same size.  With
  *                GDN_QK_L2NORM each row x becomes x / ||x||_2, the norm taken
  *                in fp32 and the result rounded to `dtype` (round to nearest
@@ -242,7 +246,7 @@ gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, co
  *   N            sequences this step (N = 0 enqueues nothing and reads no
  *                pointer).
  *   H_qk, H_v    as for gdn_chunk_fwd (H_v % H_qk == 0).
- *   dk, dv       each 64 or 128.
+ *   dk, dv       each 64, 128 or 256.
  *   q, k         [N, H_qk, dk]; v: [N, H_v, dv]; g, beta: [N, H_v] fp32.
  *   scale        multiplies the output.
  *   flags        GDN_QK_L2NORM: q and k are divided by their L2 norms (fp32,

@@ -66,6 +66,10 @@ def test_piece_scan_workspace():
         piece_bytes(2, 5, 1, 128, 64)
     # Short rows do not gain enough: whole rows, no workspace.
     assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == 0
+    # dk = 256 always runs whole rows; dv = 256 is tiled like any other dv.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 256, 256, 1) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 256, 1) == \
+        piece_bytes(1, 4, 2, 128, 256)
 
 
 def test_piece_scan_workspace_checked_before_launch():
@@ -92,6 +96,8 @@ def call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE
     (dict(dtype=7), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(dk=32), UNSUPPORTED),
     (dict(flags=4), INVALID), (dict(flags=0x100), INVALID),
     (dict(dv=96), UNSUPPORTED), (dict(dtype=0, dk=96), UNSUPPORTED),
+    (dict(dk=512), UNSUPPORTED), (dict(dv=512), UNSUPPORTED),
+    (dict(dk=256, q=FAKE + 8), MISALIGNED), (dict(dtype=0, dk=256, dv=256, o=FAKE + 4), MISALIGNED),
     (dict(q=FAKE + 8), MISALIGNED), (dict(o=FAKE + 4), MISALIGNED),
     (dict(h0=FAKE + 2), MISALIGNED), (dict(ht=FAKE + 12), MISALIGNED),
     (dict(cu=FAKE, n_seqs=2, B=2), INVALID), (dict(cu=FAKE, n_seqs=0), INVALID),
@@ -171,7 +177,8 @@ def prep_call(dtype=1, rows=4, dk=128, q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, n_gates
 @pytest.mark.parametrize("kw,status", [
     (dict(flags=4), INVALID), (dict(flags=0x80000001), INVALID),
     (dict(q=None), INVALID), (dict(ko=None), INVALID), (dict(rows=-1), INVALID),
-    (dict(dk=0), INVALID), (dict(dk=129), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(dk=0), INVALID), (dict(dk=257), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(dk=256, q=FAKE + 4), MISALIGNED),
     (dict(g=None), INVALID), (dict(bo=None), INVALID), (dict(n_gates=-1), INVALID),
     (dict(q=FAKE + 4), MISALIGNED), (dict(go=FAKE + 8), MISALIGNED),
     # Nothing to do (no option, or zero rows and gates) launches nothing.
@@ -195,8 +202,9 @@ def step_call(dtype=1, N=2, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE,
     (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(state=None), INVALID),
     (dict(o=None), INVALID), (dict(N=-1), INVALID), (dict(Hqk=0), INVALID),
     (dict(flags=8), INVALID), (dict(n_slots=1), INVALID), (dict(n_slots=-1), INVALID),
-    (dict(dtype=9), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
-    (dict(Hqk=2, Hv=3), UNSUPPORTED), (dict(state=FAKE + 4), MISALIGNED),
+    (dict(dtype=9), UNSUPPORTED), (dict(dk=96), UNSUPPORTED), (dict(dv=512), UNSUPPORTED),
+    (dict(dk=32), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED),
+    (dict(state=FAKE + 4), MISALIGNED), (dict(dk=256, dv=256, state=FAKE + 4), MISALIGNED),
     (dict(slots=FAKE + 4, n_slots=1), MISALIGNED), (dict(o=FAKE + 2), MISALIGNED),
     (dict(N=1 << 40, n_slots=1 << 40), INVALID),
     # N = 0 enqueues nothing and reads no pointer.

@@ -285,3 +285,58 @@ def test_many_short_documents():
 def test_grouped_heads_ratio_four_fp32():
     d = gi.make(2, 130, 1, 4, 64, 64, "f32", 4300, h0_std=0.2)
     check(d, scale=0.6, label="fp32 GVA ratio 4")
+
+
+@pytest.mark.parametrize("T,dv", [(1, 128), (31, 64), (32, 256), (33, 128), (200, 128)])
+def test_bf16_dk256(T, dv):
+    """bf16 with dk = 256 (chunks of 32 tokens): ragged T around one chunk,
+    grouped heads, h0, scale, dv in {64, 128, 256}."""
+    d = gi.make(2, T, 1, 2, 256, dv, "bf16", 4400 + T, h0_std=0.1)
+    check(d, scale=0.8, label=f"bf16 dk256 T={T} dv={dv}")
+
+
+def test_bf16_dk256_packed_with_empty_document():
+    cu = gi.cu_from_lengths([45, 0, 97, 1, 32])
+    d = gi.make(1, 175, 2, 4, 256, 64, "bf16", 4450, h0_std=0.05, cu_seqlens=cu)
+    check(d, label="bf16 dk256 packed")
+
+
+def test_bf16_dk256_slow_decay():
+    """Slower decay, so states carried over many chunks matter."""
+    d = gi.make(1, 700, 1, 2, 256, 128, "bf16", 4460, h0_std=0.5)
+    d["g"] = (d["g"] / 8).astype(np.float32)
+    check(d, label="bf16 dk256 slow decay")
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 100])
+def test_fp32_dk256(T):
+    d = gi.make(1, T, 1, 2, 256, 64, "f32", 4470 + T, h0_std=0.2)
+    check(d, scale=0.7, label=f"fp32 dk256 T={T}")
+
+
+def test_bf16_dv256():
+    check(gi.make(1, 150, 2, 2, 128, 256, "bf16", 4480, h0_std=0.1), label="bf16 dk128 dv256")
+
+
+def test_k256_workload_full_size():
+    """B=8, T=2048, H=32, dk=dv=256 (device-drawn inputs), compared with the
+    oracle on two sampled heads."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    c = gi.CONFIGS["k256_bf16"]
+    B, T, H, dk, dv = c["B"], c["T"], c["Hv"], c["dk"], c["dv"]
+    print(f"[gpu case] k256 B={B} T={T} H={H} dk={dk} dv={dv} bf16 (device-drawn inputs)",
+          flush=True)
+    t = gi.make_device(B, T, c["Hqk"], H, dk, dv, c["seed"])
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    o, ht = gdn.gdn_chunk_fwd(q, k, v, g, beta)
+    torch.cuda.synchronize()
+    heads = gi.sampled_heads(c["seed"], H)
+    sel = lambda x: x[:, :, heads].float().cpu().numpy()
+    ro, rht = run_oracle({"q": sel(q), "k": sel(k), "v": sel(v), "g": sel(g), "beta": sel(beta),
+                          "h0": None, "cu_seqlens": None})
+    eo = rel_l2(sel(o), ro)
+    eh = rel_l2(ht[:, heads].cpu().numpy(), rht)
+    tol_o, tol_h = TOL["bf16"]
+    print(f"  heads {heads}: rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} "
+          f"(tol {tol_h:.0e})", flush=True)
+    assert eo <= tol_o and eh <= tol_h

@@ -32,7 +32,8 @@ def _host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 96)])
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 128), ("f32", 64), ("bf16", 96),
+                                      ("bf16", 256), ("f32", 256), ("bf16", 200)])
 @pytest.mark.parametrize("in_place", [False, True])
 def test_prepare_inputs(dtype, dk, in_place):
     seed = 6000 + dk
@@ -78,6 +79,9 @@ FUSED_CASES = [
     ("bf16", 1, 300, 2, 2, 128, 128, [70, 0, 129, 101]),
     ("f32", 1, 100, 2, 2, 64, 64, None),
     ("f32", 1, 150, 1, 2, 128, 128, [1, 85, 64]),
+    ("bf16", 2, 100, 1, 2, 256, 128, None),
+    ("bf16", 1, 180, 2, 4, 256, 64, [33, 0, 100, 47]),
+    ("f32", 1, 70, 1, 1, 256, 64, None),
 ]
 
 
@@ -130,7 +134,8 @@ def _step_inputs(d, t_idx):
     return out
 
 
-@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("f32", 128, 128), ("bf16", 128, 64)])
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("f32", 128, 128), ("bf16", 128, 64),
+                                         ("f32", 256, 256), ("bf16", 256, 128)])
 def test_step_chain_matches_token_oracle(dtype, dk, dv):
     """40 decode steps from an initial state against the token-by-token
     oracle over the whole rows."""
