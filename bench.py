@@ -27,7 +27,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "headline_bf16"
 KERNEL_NAME = "gdn_fwd_bf16<false, 0, 128>"
 KERNEL_SOURCES = ["gated_deltanet_chunked_chunk_amd/csrc/gdn_fwd_bf16.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline_bf16.json")
+K256_KERNEL_NAME = "gdn_fwd_bf16<false, 0, 256>"
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
 def log(*a):
@@ -274,10 +278,11 @@ def measure_k256(gdn, gi, torch, dev, steps, warmup):
             "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic(name),
                          "algorithmic_bytes_per_call": nbytes,
                          "mfma_bf16_tflops": flops / (ms * 1e-3) / 1e12,
                          "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                         "kernels": ["gdn_fwd_bf16<false, 0, 256>"]},
+                         "kernel": K256_KERNEL_NAME},
             "check": {"head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h}}
 
 
@@ -295,11 +300,12 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it is missing or was taken on another version of the kernel."""
+def measured_traffic(workload=WORKLOAD):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    the workload's kernel, or None if it is missing or was taken on another
+    version of the kernel."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None

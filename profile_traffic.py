@@ -1,16 +1,17 @@
 """rocprofv3 helpers behind the roofline figures that bench.py reports.
 
-    python3 profile_traffic.py launch [--launches N]
-        The benchmark's workload launched N times back to back, then the
-        calibration copy: torch.bitwise_not over a 256 MiB int32 buffer into
-        another (reads 256 MiB, writes 256 MiB).  Run it once under
-        `rocprofv3 --pmc FETCH_SIZE` and once under `rocprofv3 --pmc WRITE_SIZE`.
+    python3 profile_traffic.py launch [--launches N] [--workload W]
+        A workload (headline_bf16, the benchmark's, or k256_bf16) launched N
+        times back to back, then the calibration copy: torch.bitwise_not over
+        a 256 MiB int32 buffer into another (reads 256 MiB, writes 256 MiB).
+        Run it once under `rocprofv3 --pmc FETCH_SIZE` and once under
+        `rocprofv3 --pmc WRITE_SIZE`.
 
-    python3 profile_traffic.py traffic FETCH_DIR WRITE_DIR --command CMD
+    python3 profile_traffic.py traffic FETCH_DIR WRITE_DIR --command CMD [--workload W]
         Reads the two counter CSVs, scales the kernel's FETCH_SIZE and
         WRITE_SIZE (KiB per dispatch) by what the same counters read for the
-        calibration copy, and writes profiles/traffic_headline_bf16.json (read
-        by bench.py) and a text summary beside it.
+        calibration copy, and writes profiles/traffic_W.json (read by
+        bench.py) and a text summary beside it.
 
     python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME]
         Writes profiles/kernel_stats_NAME.md (default headline_bf16) from a
@@ -33,17 +34,26 @@ CAL_KERNEL = "bitwise_not"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def launch(n):
+KERNELS = {"headline_bf16": bench.KERNEL_NAME, "k256_bf16": bench.K256_KERNEL_NAME}
+
+
+def launch(n, workload):
     import numpy as np
     import torch
     import gated_deltanet_chunked_chunk_amd as gdn
     import gdn_inputs as gi
     gdn.load()
     dev = torch.device("cuda:0")
-    d = gi.make_config(bench.WORKLOAD)
-    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
-    g, b = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+    if workload == "headline_bf16":
+        d = gi.make_config(workload)
+        up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        g, b = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+    else:
+        c = gi.CONFIGS[workload]
+        d = gi.make_device(c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"], c["seed"],
+                           device=dev)
+        q, k, v, g, b = (d[x] for x in ("q", "k", "v", "g", "beta"))
     o = torch.empty((d["B"], d["T"], d["Hv"], d["dv"]), dtype=torch.bfloat16, device=dev)
     ht = torch.empty((d["B"], d["Hv"], d["dk"], d["dv"]), dtype=torch.float32, device=dev)
     for i in range(n):
@@ -79,9 +89,12 @@ def pick(per, needle):
     return hits[0]
 
 
-def traffic(fetch_dir, write_dir, command):
-    alg = bench.algorithmic_bytes(8, 2048, 16, 16, 128, 128)
-    out = {"kernel": bench.KERNEL_NAME, "workload": bench.WORKLOAD,
+def traffic(fetch_dir, write_dir, command, workload):
+    import gdn_inputs as gi
+    c = gi.CONFIGS[workload]
+    kernel = KERNELS[workload]
+    alg = bench.algorithmic_bytes(c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"])
+    out = {"kernel": kernel, "workload": workload,
            "kernel_source_sha256": bench.kernel_source_hash(),
            "algorithmic_bytes_per_launch": alg,
            "calibration": f"torch.bitwise_not, int32, {CAL_BYTES} bytes read and {CAL_BYTES} written",
@@ -89,7 +102,7 @@ def traffic(fetch_dir, write_dir, command):
     total = 0.0
     for counter, dirname in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = read_counter(dirname, counter)
-        kname, kv = pick(per, bench.KERNEL_NAME)
+        kname, kv = pick(per, kernel)
         cname, cv = pick(per, CAL_KERNEL)
         cal_kib = sum(cv) / len(cv)
         factor = CAL_BYTES / (cal_kib * 1024.0)
@@ -101,9 +114,10 @@ def traffic(fetch_dir, write_dir, command):
     out["bytes_per_launch"] = total
     out["traffic_over_algorithmic"] = total / alg
     os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, "traffic_headline_bf16.json"), "w") as f:
+    with open(os.path.join(PROFILES, f"traffic_{workload}.json"), "w") as f:
         json.dump(out, f, indent=1)
-    lines = [f"# HBM traffic of {bench.KERNEL_NAME}, {bench.WORKLOAD} (B=8 T=2048 H=16 d=128 bf16)",
+    lines = [f"# HBM traffic of {kernel}, {workload} (B={c['B']} T={c['T']} H={c['Hv']} "
+             f"dk={c['dk']} dv={c['dv']} bf16)",
              "", "Commands:", "", "```", command, "```", "",
              "| counter | kernel KiB/dispatch | copy KiB (256 MiB known) | scale | bytes/launch |",
              "|---|---|---|---|---|"]
@@ -113,7 +127,7 @@ def traffic(fetch_dir, write_dir, command):
                      f"{r['scale_factor']:.4f} | {r['bytes']:.0f} |")
     lines += ["", f"Total {total:.0f} B per launch; algorithmic {alg} B; ratio "
                   f"{total / alg:.3f}.", f"Kernel source sha256 {out['kernel_source_sha256']}."]
-    with open(os.path.join(PROFILES, "traffic_headline_bf16.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"traffic_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -150,10 +164,12 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     a = sub.add_parser("launch")
     a.add_argument("--launches", type=int, default=5)
+    a.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
     t.add_argument("--command", required=True)
+    t.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
     s = sub.add_parser("stats")
     s.add_argument("stats_dir")
     s.add_argument("--command", required=True)
@@ -163,9 +179,9 @@ def main():
                    help="keep kernels whose name contains this (repeatable)")
     args = ap.parse_args()
     if args.cmd == "launch":
-        launch(args.launches)
+        launch(args.launches, args.workload)
     elif args.cmd == "traffic":
-        traffic(args.fetch_dir, args.write_dir, args.command)
+        traffic(args.fetch_dir, args.write_dir, args.command, args.workload)
     else:
         stats(args.stats_dir, args.command, args.name, args.title, args.only)
 
