@@ -28,9 +28,7 @@ bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
 }
 
 // Pieces per row for the piece-parallel scan of long rows (1: one pass over
-// whole rows), for batch-mode bf16 calls with dk <= 128 (the scan's transition
-// tile of a 256-wide key space does not fit in LDS).  With P pieces the
-// first pass runs
+// whole rows), for batch-mode bf16 calls.  With P pieces the first pass runs
 // (P - 1) pieces x (value tiles + dk / 64 transition tiles) workgroups and
 // the output pass P pieces x value tiles, each workgroup walking about
 // chunks / P chunks; one workgroup per CU is resident.  The plan minimises
@@ -50,7 +48,7 @@ struct PiecePlan {
 PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk, int32_t dv,
                       bool packed) {
     PiecePlan best{1, T};
-    if (packed || dtype != GDN_BF16 || dk > 128 || dv % 64 != 0)
+    if (packed || dtype != GDN_BF16 || dv % 64 != 0)
         return best;
     const int64_t rows = B * H_v;
     const int64_t items = rows * (dv / 64);

@@ -653,8 +653,9 @@ __device__ __forceinline__ f32x4 gram256(const uint16_t *X, const uint16_t *K, c
 
 // The per-chunk products of a 32-token chunk (dk = 256): helper 0 the two
 // diagonal blocks of A and their inverses, helper 1 A10 and P00, helper 2
-// P10, helper 3 P11.
-template <bool Nrm>
+// P10, helper 3 P11.  Without WithP (no output is formed) the P blocks are
+// skipped.
+template <bool WithP, bool Nrm>
 __device__ __forceinline__ void helper_products_k256(Smem &S, ChunkBuf &B, int hw, int lr, int lg,
                                                      int lane) {
     const KqBase kb = kq_base(lr, lg);
@@ -664,10 +665,11 @@ __device__ __forceinline__ void helper_products_k256(Smem &S, ChunkBuf &B, int h
         diag_inverse_all(B, S, lane);  // blocks 2, 3 invert the identity left in Ad[2], Ad[3]
     } else if (hw == 1) {
         a_finish<1, 0, Nrm>(B, gram256<1, 0>(B.K, B.K, kb), lr, lg);
-        p_finish<0, 0, Nrm>(B, gram256<0, 0>(B.Q, B.K, kb), lr, lg);
-    } else if (hw == 2) {
+        if constexpr (WithP)
+            p_finish<0, 0, Nrm>(B, gram256<0, 0>(B.Q, B.K, kb), lr, lg);
+    } else if (WithP && hw == 2) {
         p_finish<1, 0, Nrm>(B, gram256<1, 0>(B.Q, B.K, kb), lr, lg);
-    } else {
+    } else if (WithP) {
         p_finish<1, 1, Nrm>(B, gram256<1, 1>(B.Q, B.K, kb), lr, lg);
     }
 }
@@ -759,7 +761,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     }
 
     if constexpr (DK == 256)
-        helper_products_k256<Prep>(S, B, hw, lr, lg, lane);
+        helper_products_k256<Full, Prep>(S, B, hw, lr, lg, lane);
     else
         helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
 }
@@ -1275,14 +1277,16 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 // p < pieces - 1, written to piece_starts.  The state map of a piece is
 // affine in its start state (the recurrence is linear in S), so this is
 // exact; fp32 with one fused multiply-add per term.  Lane c owns column c
-// and, with its wave, 32 of the dk rows; Phi_p is staged in LDS.
+// and, with its wave, dk / 4 of the dk rows; Phi_p is staged in LDS, whole
+// for dk <= 128 and in blocks of 64 of its columns for dk = 256.
 constexpr int kScanCols = 64;
 
 template <int DK>
 __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
-    constexpr int RW = DK / 4;  // rows per wave
+    constexpr int RW = DK / 4;                // rows per wave
+    constexpr int KB = DK > 128 ? 64 : DK;    // columns of Phi staged at a time
     __shared__ float Ms[DK][kScanCols + 1];
-    __shared__ __attribute__((aligned(16))) float Ph[DK][DK + 4];
+    __shared__ __attribute__((aligned(16))) float Ph[DK][KB + 4];
     const int tid = threadIdx.x, c = tid & 63, rg = tid >> 6;
     const int n = blockIdx.x / a.Hv, j = blockIdx.x % a.Hv;
     const int cc = blockIdx.y * kScanCols + c;
@@ -1295,26 +1299,29 @@ __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
     for (int p = 0; p + 1 < a.pieces; ++p) {
         const int64_t pslot = ((int64_t)n * (a.pieces - 1) + p) * a.Hv + j;
         const float *ends = a.piece_ends + pslot * DK * estride;
-        __syncthreads();  // the previous step's reads of Ph are done
-        for (int e = tid; e < DK * DK / 4; e += 256) {
-            const int row = e / (DK / 4), q4 = e % (DK / 4);
-            *reinterpret_cast<f32x4 *>(&Ph[row][4 * q4]) =
-                *reinterpret_cast<const f32x4 *>(ends + row * estride + a.dv + 4 * q4);
-        }
         float acc[RW];
 #pragma unroll
         for (int r = 0; r < RW; ++r)
             acc[r] = ends[(RW * rg + r) * estride + cc];
-        __syncthreads();
-        for (int k = 0; k < DK; k += 4) {
-            const float m0 = Ms[k][c], m1 = Ms[k + 1][c], m2 = Ms[k + 2][c], m3 = Ms[k + 3][c];
+        for (int k0 = 0; k0 < DK; k0 += KB) {
+            __syncthreads();  // the previous reads of Ph are done
+            for (int e = tid; e < DK * KB / 4; e += 256) {
+                const int row = e / (KB / 4), q4 = e % (KB / 4);
+                *reinterpret_cast<f32x4 *>(&Ph[row][4 * q4]) =
+                    *reinterpret_cast<const f32x4 *>(ends + row * estride + a.dv + k0 + 4 * q4);
+            }
+            __syncthreads();
+            for (int k = 0; k < KB; k += 4) {
+                const float m0 = Ms[k0 + k][c], m1 = Ms[k0 + k + 1][c], m2 = Ms[k0 + k + 2][c],
+                            m3 = Ms[k0 + k + 3][c];
 #pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[RW * rg + r][k]);
-                acc[r] = fmaf(ph[0], m0, acc[r]);
-                acc[r] = fmaf(ph[1], m1, acc[r]);
-                acc[r] = fmaf(ph[2], m2, acc[r]);
-                acc[r] = fmaf(ph[3], m3, acc[r]);
+                for (int r = 0; r < RW; ++r) {
+                    const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[RW * rg + r][k]);
+                    acc[r] = fmaf(ph[0], m0, acc[r]);
+                    acc[r] = fmaf(ph[1], m1, acc[r]);
+                    acc[r] = fmaf(ph[2], m2, acc[r]);
+                    acc[r] = fmaf(ph[3], m3, acc[r]);
+                }
             }
         }
         __syncthreads();  // every read of Ms is done
@@ -1338,22 +1345,18 @@ hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
                            stream, a);
         return hipGetLastError();
     }
-    if constexpr (DK == 256) {
-        return hipErrorInvalidValue;  // the piece scan covers dk <= 128
-    } else {
-        const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
-        const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
-        const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
-        if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
-            return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
-                           stream, a);
-        hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
-                           dim3(256), 0, stream, a);
-        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
-                           stream, a);
-        return hipGetLastError();
-    }
+    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
+    const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
+    const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
+    if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
+                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
 }
 
 template <bool Prep>

@@ -66,8 +66,12 @@ def test_piece_scan_workspace():
         piece_bytes(2, 5, 1, 128, 64)
     # Short rows do not gain enough: whole rows, no workspace.
     assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == 0
-    # dk = 256 always runs whole rows; dv = 256 is tiled like any other dv.
-    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 256, 256, 1) == 0
+    # dk = 256 (four transition tiles per piece): 3 pieces of 5,547 chunks;
+    # dv = 256 is tiled like any other dv.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 256, 256, 1) == \
+        piece_bytes(1, 3, 16, 256, 256)
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 256, 128, 1) == \
+        piece_bytes(1, 4, 2, 256, 128)
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 256, 1) == \
         piece_bytes(1, 4, 2, 128, 256)
 

@@ -340,3 +340,60 @@ def test_k256_workload_full_size():
     print(f"  heads {heads}: rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} "
           f"(tol {tol_h:.0e})", flush=True)
     assert eo <= tol_o and eh <= tol_h
+
+
+def _dk256_piece_check(d, pieces, label):
+    """The piece scan at dk = 256 against the oracle and against whole rows."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    from gpu_util import to_device
+    B, T, Hqk, Hv, dv = d["B"], d["T"], d["Hqk"], d["Hv"], d["dv"]
+    per = B * (pieces - 1) * Hv * 256
+    assert gdn.load().gdn_chunk_fwd_workspace_size(1, B, T, Hqk, Hv, 256, dv, B) == \
+        -(-per * (dv + 256) * 4 // 256) * 256 + per * dv * 4
+    check(d, label=f"{label}, {pieces} pieces")
+    o1, h1 = run_gpu(d)
+    t = to_device(d)
+    o2, h2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"],
+                               pieces=False)
+    e = (rel_l2(o1, o2.float().cpu().numpy()), rel_l2(h1, h2.cpu().numpy()))
+    print(f"  pieces vs whole rows: output {e[0]:.3e}, state {e[1]:.3e}", flush=True)
+    tol_o, tol_h = TOL["bf16"]
+    assert e[0] <= tol_o and e[1] <= tol_h
+
+
+def test_bf16_dk256_piece_scan():
+    """dk = 256 through the piece scan (four transition tiles per piece, the
+    scan staging Phi in 64-column blocks): 4 pieces of 1,088 tokens."""
+    d = gi.make(1, 4096 + 37, 1, 2, 256, 128, "bf16", 4490, h0_std=0.5)
+    d["g"] = (d["g"] / 8).astype(np.float32)
+    _dk256_piece_check(d, 4, "bf16 dk256 piece scan")
+
+
+def test_bf16_dk256_piece_scan_carries_state():
+    """No decay and a weak write (g = 0, beta = 0.02) at dk = 256: every
+    piece's transition stays near the identity, so the scanned start states
+    (all four 64-column blocks of Phi) carry most of the result."""
+    d = gi.make(1, 3000 + 37, 1, 2, 256, 64, "bf16", 4495, h0_std=1.0)
+    d["g"] = np.zeros_like(d["g"])
+    d["beta"] = np.full_like(d["beta"], 0.02)
+    _dk256_piece_check(d, 3, "bf16 dk256 piece scan, g = 0, beta = 0.02")
+
+
+def test_bf16_dk256_piece_scan_with_in_op_preparation():
+    import gated_deltanet_chunked_chunk_amd as gdn
+    import oracle
+    from oracle import prep
+    from gpu_util import to_device
+    d = gi.make_raw(1, 4096 + 37, 1, 2, 256, 128, "bf16", 4497, qk_std=2.0)
+    print("[gpu case] dk256 piece scan with in-op preparation", flush=True)
+    t = to_device(d)
+    o, ht = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], use_qk_l2norm=True,
+                              gate_activation=True)
+    torch.cuda.synchronize()
+    qn, kn = (prep.l2_normalize(gi.widen(d[x])).astype(np.float32) for x in ("q", "k"))
+    ro, rht = oracle.gdn_fwd(qn, kn, gi.widen(d["v"]), prep.logsigmoid(d["g"]).astype(np.float32),
+                             prep.sigmoid(d["beta"]).astype(np.float32))
+    tol_o, tol_h = TOL["bf16"]
+    eo, eh = rel_l2(o.float().cpu().numpy(), ro), rel_l2(ht.cpu().numpy(), rht)
+    print(f"  rel-L2 output {eo:.3e}, state {eh:.3e}", flush=True)
+    assert eo <= tol_o and eh <= tol_h
