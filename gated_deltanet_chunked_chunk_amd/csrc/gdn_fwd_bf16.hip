@@ -1273,63 +1273,64 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 }
 
 // The piece scan between the two passes: for row n, head j and value columns
-// [64 y, 64 y + 64), M_0 = h0 (or zero) and M_{p+1} = Phi_p M_p + F_p for
+// [16 y, 16 y + 16), M_0 = h0 (or zero) and M_{p+1} = Phi_p M_p + F_p for
 // p < pieces - 1, written to piece_starts.  The state map of a piece is
 // affine in its start state (the recurrence is linear in S), so this is
-// exact; fp32 with one fused multiply-add per term.  Lane c owns column c
-// and, with its wave, dk / 4 of the dk rows; Phi_p is staged in LDS, whole
-// for dk <= 128 and in blocks of 64 of its columns for dk = 256.
-constexpr int kScanCols = 64;
+// exact; fp32 with one fused multiply-add per term, summed in key order.
+// Thread (rg, cg) owns rows dk/64 * rg .. + dk/64 - 1 and columns 4 cg .. + 3
+// of the product; Phi_p is staged transposed in LDS, 64 of its columns at a
+// time, so both operands are read as 16-byte vectors.
+constexpr int kScanCols = 16;
 
 template <int DK>
 __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
-    constexpr int RW = DK / 4;                // rows per wave
-    constexpr int KB = DK > 128 ? 64 : DK;    // columns of Phi staged at a time
-    __shared__ float Ms[DK][kScanCols + 1];
-    __shared__ __attribute__((aligned(16))) float Ph[DK][KB + 4];
-    const int tid = threadIdx.x, c = tid & 63, rg = tid >> 6;
+    constexpr int R = DK / 64;   // rows per thread
+    constexpr int KB = 64;       // columns of Phi staged at a time
+    typedef __attribute__((ext_vector_type(R))) float rowv;
+    __shared__ __attribute__((aligned(16))) float Ms[DK][kScanCols + 4];
+    __shared__ __attribute__((aligned(16))) float PhT[KB][DK + 4];
+    const int tid = threadIdx.x, cg = tid % 4, rg = tid / 4;
     const int n = blockIdx.x / a.Hv, j = blockIdx.x % a.Hv;
-    const int cc = blockIdx.y * kScanCols + c;
+    const int c0 = blockIdx.y * kScanCols;
     const int64_t hbase = ((int64_t)n * a.Hv + j) * DK * (int64_t)a.dv;
-    for (int r = 0; r < RW; ++r) {
-        const int i = RW * rg + r;
-        Ms[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + cc] : 0.0f;
+    for (int e = tid; e < DK * kScanCols; e += 256) {
+        const int i = e / kScanCols, c = e % kScanCols;
+        Ms[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + c0 + c] : 0.0f;
     }
     const int64_t estride = a.dv + DK;
     for (int p = 0; p + 1 < a.pieces; ++p) {
         const int64_t pslot = ((int64_t)n * (a.pieces - 1) + p) * a.Hv + j;
         const float *ends = a.piece_ends + pslot * DK * estride;
-        float acc[RW];
+        f32x4 acc[R];
 #pragma unroll
-        for (int r = 0; r < RW; ++r)
-            acc[r] = ends[(RW * rg + r) * estride + cc];
+        for (int r = 0; r < R; ++r)
+            acc[r] = *reinterpret_cast<const f32x4 *>(ends + (R * rg + r) * estride + c0 + 4 * cg);
         for (int k0 = 0; k0 < DK; k0 += KB) {
-            __syncthreads();  // the previous reads of Ph are done
+            __syncthreads();  // the previous reads of PhT, and the last step's writes of Ms
             for (int e = tid; e < DK * KB / 4; e += 256) {
-                const int row = e / (KB / 4), q4 = e % (KB / 4);
-                *reinterpret_cast<f32x4 *>(&Ph[row][4 * q4]) =
-                    *reinterpret_cast<const f32x4 *>(ends + row * estride + a.dv + k0 + 4 * q4);
+                const int r = e / (KB / 4), q4 = e % (KB / 4);
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(ends + r * estride + a.dv + k0 + 4 * q4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    PhT[4 * q4 + i][r] = x[i];
             }
             __syncthreads();
-            for (int k = 0; k < KB; k += 4) {
-                const float m0 = Ms[k0 + k][c], m1 = Ms[k0 + k + 1][c], m2 = Ms[k0 + k + 2][c],
-                            m3 = Ms[k0 + k + 3][c];
+            for (int kk = 0; kk < KB; ++kk) {
+                const f32x4 m = *reinterpret_cast<const f32x4 *>(&Ms[k0 + kk][4 * cg]);
+                const rowv ph = *reinterpret_cast<const rowv *>(&PhT[kk][R * rg]);
 #pragma unroll
-                for (int r = 0; r < RW; ++r) {
-                    const f32x4 ph = *reinterpret_cast<const f32x4 *>(&Ph[RW * rg + r][k]);
-                    acc[r] = fmaf(ph[0], m0, acc[r]);
-                    acc[r] = fmaf(ph[1], m1, acc[r]);
-                    acc[r] = fmaf(ph[2], m2, acc[r]);
-                    acc[r] = fmaf(ph[3], m3, acc[r]);
-                }
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[r][c] = fmaf(ph[r], m[c], acc[r][c]);
             }
         }
         __syncthreads();  // every read of Ms is done
         float *out = a.piece_starts + pslot * DK * (int64_t)a.dv;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            Ms[RW * rg + r][c] = acc[r];
-            out[(int64_t)(RW * rg + r) * a.dv + cc] = acc[r];
+        for (int r = 0; r < R; ++r) {
+            *reinterpret_cast<f32x4 *>(&Ms[R * rg + r][4 * cg]) = acc[r];
+            *reinterpret_cast<f32x4 *>(out + (R * rg + r) * (int64_t)a.dv + c0 + 4 * cg) = acc[r];
         }
     }
 }
