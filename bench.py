@@ -216,11 +216,12 @@ def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
                          "algorithmic_bytes_per_call": nbytes, "kernels": ["preprocess"]}}
 
 
-def measure_long(gdn, gi, torch, dev, steps=3):
-    """The long row (B=1, T=1,064,960, H=16, d=128, bf16; inputs drawn on the
+def measure_long(gdn, gi, torch, dev, steps=3, name="long_bf16"):
+    """A long-row workload (long_bf16: B=1, T=1,064,960, H=16, d=128;
+    long_k256_bf16: B=1, T=65,536, H=8, d=256; bf16, inputs drawn on the
     device with the same recipe): milliseconds per forward with the piece
     scan and with whole rows, and the HBM roofline fraction of each."""
-    c = gi.CONFIGS["long_bf16"]
+    c = gi.CONFIGS[name]
     B, T, Hqk, Hv, dk, dv = c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"]
     t = gi.make_device(B, T, Hqk, Hv, dk, dv, c["seed"], device=dev)
     q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
@@ -229,15 +230,15 @@ def measure_long(gdn, gi, torch, dev, steps=3):
     ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    out = {"workload": f"long_bf16: B={B} T={T} H={Hv} dk={dk} dv={dv}, zero initial state"}
+    out = {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, zero initial state"}
     nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
-    for name, kw in (("pieces", dict(workspace=ws)), ("whole_rows", dict(pieces=False))):
+    for mode, kw in (("pieces", dict(workspace=ws)), ("whole_rows", dict(pieces=False))):
         call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht,
                                          stream=stream.cuda_stream, **kw)
         ms = _time_calls(torch, stream, call, steps, 1)
-        out[name] = {"ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+        out[mode] = {"ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-        log(f"[bench] long row, {name}: {ms:.2f} ms/call")
+        log(f"[bench] {name}, {mode}: {ms:.2f} ms/call")
     out["algorithmic_bytes_per_call"] = nbytes
     del q, k, v, g, beta, o, t
     torch.cuda.empty_cache()
@@ -360,7 +361,8 @@ def main():
     ap.add_argument("--no-k256", action="store_true",
                     help="skip the head-dimension-256 measurement")
     ap.add_argument("--long", action="store_true",
-                    help="also time the long row (B=1, T=1,064,960), with and without pieces")
+                    help="also time the long rows (B=1, T=1,064,960, d=128; B=1, T=65,536, "
+                         "d=256), with and without pieces")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -485,10 +487,11 @@ def main():
         log("[bench] head dimension 256")
         k256 = measure_k256(gdn, gi, torch, dev, steps=200, warmup=100)
 
-    long_row = None
+    long_row = long_k256 = None
     if args.long:
-        log("[bench] long row")
+        log("[bench] long rows")
         long_row = measure_long(gdn, gi, torch, dev)
+        long_k256 = measure_long(gdn, gi, torch, dev, steps=10, name="long_k256_bf16")
 
     baseline = None
     if not args.no_cpu_baseline:
@@ -539,6 +542,7 @@ def main():
         "decode": decode,
         "k256": k256,
         "long_row": long_row,
+        "long_k256": long_k256,
         "wall_s_timed_region": wall,
     }
     print(json.dumps(result), flush=True)

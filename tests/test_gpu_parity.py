@@ -397,3 +397,33 @@ def test_bf16_dk256_piece_scan_with_in_op_preparation():
     eo, eh = rel_l2(o.float().cpu().numpy(), ro), rel_l2(ht.cpu().numpy(), rht)
     print(f"  rel-L2 output {eo:.3e}, state {eh:.3e}", flush=True)
     assert eo <= tol_o and eh <= tol_h
+
+
+def test_long_k256_row_full_size():
+    """One row of 65,536 tokens at dk = dv = 256, 8 heads (device-drawn): the
+    piece scan against whole rows, and both against the oracle on two sampled
+    heads."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    c = gi.CONFIGS["long_k256_bf16"]
+    B, T, H, dk, dv = c["B"], c["T"], c["Hv"], c["dk"], c["dv"]
+    print(f"[gpu case] long row B={B} T={T} H={H} dk={dk} dv={dv} bf16 (device-drawn inputs)",
+          flush=True)
+    t = gi.make_device(B, T, c["Hqk"], H, dk, dv, c["seed"])
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    assert gdn.gdn_chunk_fwd_workspace_size(1, B, T, H, H, dk, dv, B) > 0
+    o, ht = gdn.gdn_chunk_fwd(q, k, v, g, beta)
+    o2, h2 = gdn.gdn_chunk_fwd(q, k, v, g, beta, pieces=False)
+    torch.cuda.synchronize()
+    tol_o, tol_h = TOL["bf16"]
+    f = lambda x: x.float().cpu().numpy()
+    e = (rel_l2(f(o2), f(o)), rel_l2(f(h2), f(ht)))
+    print(f"  whole rows vs pieces {e[0]:.2e} {e[1]:.2e}", flush=True)
+    assert e[0] <= tol_o and e[1] <= tol_h
+    heads = gi.sampled_heads(c["seed"], H)
+    sel = lambda x: x[:, :, heads].float().cpu().numpy()
+    ro, rht = run_oracle({"q": sel(q), "k": sel(k), "v": sel(v), "g": sel(g), "beta": sel(beta),
+                          "h0": None, "cu_seqlens": None})
+    eo, eh = rel_l2(sel(o), ro), rel_l2(ht[:, heads].cpu().numpy(), rht)
+    print(f"  heads {heads}: rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} "
+          f"(tol {tol_h:.0e})", flush=True)
+    assert eo <= tol_o and eh <= tol_h
