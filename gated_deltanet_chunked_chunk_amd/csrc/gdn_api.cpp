@@ -180,6 +180,11 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     return GDN_OK;
 }
 
+// The backward's shapes: bf16, dk in {64, 128}, dv in {64, 128, 256}.
+static bool bwd_supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
+    return dtype == GDN_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128 || dv == 256);
+}
+
 // Chunks of 64 tokens over all sequences: exact for batch rows; with
 // cu_seqlens the bound ceil(T / 64) + N covers any split into N documents.
 static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N) {
@@ -189,8 +194,8 @@ static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N) {
 
 size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
                                     int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs) {
-    if (dtype != GDN_BF16 || dk != 128 || (dv != 64 && dv != 128) || B < 1 || T < 1 ||
-        H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || n_seqs < 1)
+    if (!bwd_supported(dtype, dk, dv) || B < 1 || T < 1 || H_qk < 1 || H_v < 1 ||
+        H_v % H_qk != 0 || n_seqs < 1)
         return 0;
     // Packed documents need B == 1; the packed bound also covers one row.
     return gdn::bwd_workspace_bytes(bwd_chunks(B, T, B == 1, B == 1 ? n_seqs : (int32_t)B), H_v,
@@ -210,10 +215,11 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
         return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16)
         return GDN_ERR_UNSUPPORTED;
-    if (H_v % H_qk != 0 || dtype != GDN_BF16 || dk != 128 || (dv != 64 && dv != 128))
+    if (H_v % H_qk != 0 || !bwd_supported(dtype, dk, dv))
         return GDN_ERR_UNSUPPORTED;
     const int64_t hmax = H_v > H_qk ? H_v : H_qk;
-    if (B > INT64_MAX / T || B * T > INT64_MAX / (hmax * 128))
+    const int64_t dmax = dv > 128 ? dv : 128;  // the workspace states are 128 keys wide
+    if (B > INT64_MAX / T || B * T > INT64_MAX / (hmax * dmax))
         return GDN_ERR_INVALID_ARG;
     int32_t N = (int32_t)B;
     if (cu_seqlens) {

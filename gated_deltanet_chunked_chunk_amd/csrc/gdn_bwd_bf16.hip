@@ -276,6 +276,20 @@ __device__ __forceinline__ void stage_rows_bf16(uint16_t *dst, int ld, const voi
     }
 }
 
+// Rows of q or k (dk = 64 or 128 elements) into a 128-wide LDS tile; with
+// dk = 64 the upper half of every row is zero, so contractions over the key
+// dimension run at 128 unchanged.  256 threads.
+__device__ __forceinline__ void stage_qk_rows(uint16_t *dst, int ld, const void *src, int64_t p,
+                                              int L, int H, int h, int dk, int tid) {
+    if (dk == kDK) {
+        stage_rows_bf16<kDK>(dst, ld, src, p, L, H, h, 0, kDK, tid);
+        return;
+    }
+    stage_rows_bf16<kDK / 2>(dst, ld, src, p, L, H, h, 0, kDK / 2, tid);
+    for (int i = tid; i < kC * 8; i += 256)
+        *reinterpret_cast<u32x4 *>(dst + (i >> 3) * ld + kDK / 2 + 8 * (i & 7)) = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // bwd_prep: per (chunk, value head).
 
@@ -297,8 +311,8 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     if (!locate(a, gc, cl))
         return;
     const int hk = j / (a.Hv / a.Hqk);
-    stage_rows_bf16<kDK>(Ks, kLK, a.k, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
-    stage_rows_bf16<kDK>(Qs, kLK, a.q, cl.p, cl.L, a.Hqk, hk, 0, kDK, tid);
+    stage_qk_rows(Ks, kLK, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+    stage_qk_rows(Qs, kLK, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
     if (w == 0) {
         const float gv = lane < cl.L ? a.g[(cl.p + lane) * a.Hv + j] : 0.0f;
         const float bv = lane < cl.L ? a.beta[(cl.p + lane) * a.Hv + j] : 0.0f;
@@ -429,18 +443,21 @@ struct StatePre {
 
 __device__ __forceinline__ void state_issue(StatePre &pre, const BwdArgs &a, const ChunkLoc &cl,
                                             int hk, int j, int tile, int64_t wi, int tid) {
-    const uint32_t krow = (uint32_t)a.Hqk * kDK * 2;
-    const int64_t kofs = (cl.p * a.Hqk + hk) * (int64_t)kDK;
+    // K and Q rows hold a.dk elements (64 or 128); the 16-byte slots past
+    // a.dk stage zeros.
+    const uint32_t krow = (uint32_t)a.Hqk * a.dk * 2;
+    const int64_t kofs = (cl.p * a.Hqk + hk) * (int64_t)a.dk;
     const __amdgpu_buffer_rsrc_t rk =
-        rsrc(static_cast<const uint16_t *>(a.k) + kofs, (uint32_t)(cl.L - 1) * krow + kDK * 2);
+        rsrc(static_cast<const uint16_t *>(a.k) + kofs, (uint32_t)(cl.L - 1) * krow + a.dk * 2);
     const __amdgpu_buffer_rsrc_t rq =
-        rsrc(static_cast<const uint16_t *>(a.q) + kofs, (uint32_t)(cl.L - 1) * krow + kDK * 2);
+        rsrc(static_cast<const uint16_t *>(a.q) + kofs, (uint32_t)(cl.L - 1) * krow + a.dk * 2);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int i = tid + 256 * u;
         const uint32_t off = (uint32_t)(i >> 4) * krow + 16 * (i & 15);
-        pre.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        pre.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        const bool in_row = 8 * (i & 15) < a.dk;
+        pre.k[u] = in_row ? __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0) : u32x4{0u, 0u, 0u, 0u};
+        pre.q[u] = in_row ? __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0) : u32x4{0u, 0u, 0u, 0u};
     }
     const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
     const void *xs = a.dout;
@@ -598,7 +615,8 @@ __device__ __forceinline__ void dstate_pass(const BwdArgs &a) {
     const int64_t len = seq_len(a, n);
     const int nch = (int)((len + kC - 1) / kC);
     const int64_t base = chunk_base(a, n);
-    const int64_t S_elems = (int64_t)kDK * a.dv;
+    const int64_t S_elems = (int64_t)kDK * a.dv;      // workspace states: 128 keys
+    const int64_t H_elems = (int64_t)a.dk * a.dv;     // dht, dh0: a.dk keys
     const float scale = a.scale;
     auto loc = [&](int it) {
         const int c = nch - 1 - it;
@@ -639,9 +657,10 @@ __device__ __forceinline__ void dstate_pass(const BwdArgs &a) {
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            h[mt][r] = init ? init[((int64_t)n * a.Hv + j) * S_elems +
-                                   (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
-                            : 0.0f;
+            h[mt][r] = init && 16 * mt + 4 * lg + r < a.dk
+                           ? init[((int64_t)n * a.Hv + j) * H_elems +
+                                  (int64_t)(16 * mt + 4 * lg + r) * a.dv + col]
+                           : 0.0f;
     __syncthreads();
     for (int it = 0; it < nch; ++it) {
         const StateSmem &S = Sb[it & 1];
@@ -700,8 +719,9 @@ __device__ __forceinline__ void dstate_pass(const BwdArgs &a) {
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a.dh0[((int64_t)n * a.Hv + j) * S_elems + (int64_t)(16 * mt + 4 * lg + r) * a.dv +
-                      col] = h[mt][r];
+                if (16 * mt + 4 * lg + r < a.dk)
+                    a.dh0[((int64_t)n * a.Hv + j) * H_elems +
+                          (int64_t)(16 * mt + 4 * lg + r) * a.dv + col] = h[mt][r];
     }
 }
 
@@ -778,19 +798,20 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
     return s;
 }
 
-// Rows [p, p + L) of a [*, H, 128] bf16 tensor at head h into a [64][kLK]
-// tile, 512 threads.
+// Rows [p, p + L) of a [*, H, dk] bf16 tensor (dk = 64 or 128) at head h
+// into a [64][kLK] tile, zeros past dk, 512 threads.
 __device__ __forceinline__ void stage_rows512(uint16_t *dst, const void *src, int64_t p, int L,
-                                              int H, int h, int tid) {
-    const uint32_t row_bytes = (uint32_t)H * kDK * 2;
+                                              int H, int h, int dk, int tid) {
+    const uint32_t row_bytes = (uint32_t)H * dk * 2;
     const __amdgpu_buffer_rsrc_t r =
-        rsrc(static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)kDK,
-             (uint32_t)(L - 1) * row_bytes + kDK * 2);
+        rsrc(static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)dk,
+             (uint32_t)(L - 1) * row_bytes + dk * 2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + kCT * u;
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15),
-                                                              0, 0);
+        const u32x4 v = 8 * (i & 15) < dk
+                            ? __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15), 0, 0)
+                            : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4 *>(dst + (i >> 4) * kLK + 8 * (i & 15)) = v;
     }
 }
@@ -806,8 +827,8 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
         return;
     const int G = a.Hv / a.Hqk;
     const float scale = a.scale;
-    stage_rows512(S.K, a.k, cl.p, cl.L, a.Hqk, hk, tid);
-    stage_rows512(S.Q, a.q, cl.p, cl.L, a.Hqk, hk, tid);
+    stage_rows512(S.K, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+    stage_rows512(S.Q, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
 
     f32x4 dQ[4], dK[4];   // dk tiles 4h + i
 #pragma unroll
@@ -1097,10 +1118,9 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * lg + r;
-            if (row < cl.L) {
-                const int64_t o =
-                    ((cl.p + row) * a.Hqk + hk) * (int64_t)kDK + 16 * (4 * h + i) + lr;
+            const int row = 16 * rb + 4 * lg + r, colk = 16 * (4 * h + i) + lr;
+            if (row < cl.L && colk < a.dk) {
+                const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)a.dk + colk;
                 dqo[o] = f2bf(dQ[i][r]);
                 dko[o] = f2bf(dK[i][r]);
             }
@@ -1115,7 +1135,8 @@ size_t bwd_workspace_bytes(int64_t n_chunks, int32_t Hv, int32_t dk, int32_t dv)
     b += ch * kC * kC * sizeof(float);           // T
     b += ch * kC * kC * sizeof(uint16_t);        // P
     b += ch * kC * sizeof(float);                // gamma
-    b += 2 * ch * (size_t)dk * dv * sizeof(uint16_t);  // chunk states and their gradients
+    (void)dk;  // the states are kept 128 keys wide (zeros past dk)
+    b += 2 * ch * (size_t)kDK * dv * sizeof(uint16_t);  // chunk states and their gradients
     return b;
 }
 
@@ -1129,7 +1150,7 @@ void bwd_carve(BwdArgs &a, void *workspace) {
     a.ws_gam = reinterpret_cast<float *>(p);
     p += ch * kC * sizeof(float);
     a.ws_hs = reinterpret_cast<uint16_t *>(p);
-    p += ch * (size_t)a.dk * a.dv * sizeof(uint16_t);
+    p += ch * (size_t)kDK * a.dv * sizeof(uint16_t);
     a.ws_dhs = reinterpret_cast<uint16_t *>(p);
 }
 

@@ -1231,11 +1231,12 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
             if (Mode == 3) {
-                // Four consecutive keys per tile: one 8-byte store each.
-                uint16_t *dst = a.chunk_states + ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * DK +
-                                (int64_t)col * DK;
+                // Four consecutive keys per tile: one 8-byte store each.  The
+                // rows are 128 keys wide whatever DK is (zeros past DK).
+                uint16_t *dst = a.chunk_states + ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * kDK +
+                                (int64_t)col * kDK;
 #pragma unroll
-                for (int mt = 0; mt < DK / 16; ++mt)
+                for (int mt = 0; mt < 8; ++mt)
                     *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
             }
             if constexpr (DK == 256)
@@ -1377,10 +1378,15 @@ hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kDVT);
     if (blocks <= 0)
         return hipSuccess;
-    if (blocks > 0x7fffffff || a.dk != 128 || a.pieces > 1 || a.flags || !a.chunk_states)
+    if (blocks > 0x7fffffff || (a.dk != 128 && a.dk != 64) || a.pieces > 1 || a.flags ||
+        !a.chunk_states)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, a);
+    if (a.dk == 128)
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -57,10 +57,11 @@ struct FwdArgs {
     uint16_t *chunk_states; // launch_fwd_chunk_states only
 };
 
-// The states entering every chunk (bf16, transposed: [n_chunks, Hv, dv, dk],
-// chunks numbered over the sequences in order) by the forward kernel without
-// its output, for the backward.  bf16, dk = 128; `a` as for the forward with
-// pieces = 1, flags = 0 and chunk_states the destination.
+// The states entering every chunk (bf16, transposed: [n_chunks, Hv, dv, 128],
+// chunks numbered over the sequences in order; zeros past dk) by the forward
+// kernel without its output, for the backward.  bf16, dk = 64 or 128; `a` as
+// for the forward with pieces = 1, flags = 0 and chunk_states the
+// destination.
 hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream);
 
 // Workspace bytes of the piece scan for `pieces` pieces per row.

@@ -153,8 +153,8 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
  * the backward would reject).  The workspace holds, per chunk of 64 tokens and
  * value head, the chunk's inverse (I + A)^-1 (fp32), its gated Q K^T (bf16),
  * its cumulative decay, and (in bf16) the state entering the chunk and the
- * gradient of the state leaving it: 2 * dk * dv * 2 bytes + 24.25 KiB per
- * chunk and head.
+ * gradient of the state leaving it, both 128 keys wide whatever dk is:
+ * 2 * 128 * dv * 2 bytes + 24.25 KiB per chunk and head.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  * With cu_seqlens the size covers any split of the T tokens into n_seqs
@@ -172,8 +172,9 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *
  *   dtype, B, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, h0, cu_seqlens,
  *   cu_seqlens_host, n_seqs
- *                as for gdn_chunk_fwd.  Supported: bf16 with dk = 128 and dv in
- *                {64, 128}; everything else returns GDN_ERR_UNSUPPORTED.
+ *                as for gdn_chunk_fwd.  Supported: bf16 with dk in {64, 128}
+ *                and dv in {64, 128, 256}; everything else returns
+ *                GDN_ERR_UNSUPPORTED.
  *   dout         [B, T, H_v, dv] upstream gradient of o, dtype `dtype`.
  *   dht          [N, H_v, dk, dv] fp32 upstream gradient of the final state,
  *                or NULL for none.

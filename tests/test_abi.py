@@ -140,7 +140,10 @@ def test_bwd_workspace_size():
     # one packed row of 5 documents: at most ceil(T / 64) + 5 chunks
     assert ws(1, 1, 2048, 16, 16, 128, 128, 5) == (32 + 5) * 16 * per
     assert ws(0, 8, 2048, 16, 16, 128, 128, 8) == 0   # fp32: no backward kernel
-    assert ws(1, 8, 2048, 16, 16, 64, 128, 8) == 0    # dk = 64: none either
+    # dk = 64 keeps the chunk states 128 keys wide (zeros past dk): the same size
+    assert ws(1, 8, 2048, 16, 16, 64, 128, 8) == ws(1, 8, 2048, 16, 16, 128, 128, 8)
+    assert ws(1, 8, 2048, 16, 16, 256, 128, 8) == 0   # dk = 256: no backward kernel
+    assert ws(1, 1, 100, 1, 1, 128, 256, 1) > ws(1, 1, 100, 1, 1, 128, 128, 1)
 
 
 def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
@@ -158,8 +161,9 @@ def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=
     (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID),
     (dict(dk_=None), INVALID), (dict(dv_=None), INVALID), (dict(dg=None), INVALID),
     (dict(dbeta=None), INVALID), (dict(T=0), INVALID),
-    (dict(dtype=0), UNSUPPORTED), (dict(dk=64), UNSUPPORTED), (dict(dv=96), UNSUPPORTED),
-    (dict(Hqk=2, Hv=3), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED), (dict(dk=256), UNSUPPORTED), (dict(dv=96), UNSUPPORTED),
+    (dict(dk=32), UNSUPPORTED), (dict(dv=512), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED),
+    (dict(dk=64, do=FAKE + 8), MISALIGNED), (dict(dv=256, dht=FAKE + 4), MISALIGNED),
     (dict(do=FAKE + 8), MISALIGNED), (dict(dht=FAKE + 4), MISALIGNED),
     (dict(dh0=FAKE + 2), MISALIGNED), (dict(dg=FAKE + 4), MISALIGNED),
     (dict(ws=FAKE + 16), MISALIGNED),

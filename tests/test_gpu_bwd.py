@@ -96,3 +96,29 @@ def test_bwd_deterministic():
     b = run_bwd_gpu(d, do, dht)
     for x, y, n in zip(a, b, NAMES):
         assert np.array_equal(x, y), f"{n} differs between runs"
+
+
+@pytest.mark.parametrize("T,dv", [(1, 64), (65, 128), (200, 64)])
+def test_bwd_dk64(T, dv):
+    """dk = 64: q and k staged into the 128-wide tiles with zero upper halves
+    (the chunk states kept 128 keys wide): ragged T, grouped heads, h0, scale."""
+    d = gi.make(2, T, 1, 2, 64, dv, "bf16", 5500 + T, h0_std=0.1)
+    check_bwd(d, 5500 + T, scale=0.8, label=f"dk64 T={T} dv={dv}")
+
+
+def test_bwd_dk64_packed_no_dht():
+    cu = gi.cu_from_lengths([90, 0, 64, 33])
+    d = gi.make(1, 187, 2, 4, 64, 64, "bf16", 5600, h0_std=0.05, cu_seqlens=cu)
+    check_bwd(d, 5600, with_dht=False, label="dk64 packed, no dht")
+
+
+def test_bwd_dv256():
+    d = gi.make(1, 150, 1, 1, 128, 256, "bf16", 5700, h0_std=0.1)
+    check_bwd(d, 5700, label="dv=256")
+
+
+def test_bwd_dk64_fla_shape():
+    """Head dim 64 at the shape of the B=8, T=1024, H=8, D=64 row of the
+    flash-linear-attention benchmark table, all heads against the oracle."""
+    d = gi.make(8, 1024, 8, 8, 64, 64, "bf16", 5800, h0_std=0.02)
+    check_bwd(d, 5800, label="dk64 8x1024x8")
