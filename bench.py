@@ -68,12 +68,13 @@ def bwd_algorithmic_bytes(B, T, Hqk, Hv, dk, dv, in_bytes=2):
     return reads + writes + states
 
 
-def measure_bwd(gdn, gi, torch, dev, steps, warmup):
-    """The backward on its workload (the headline shapes with upstream
-    gradients do and dht): milliseconds per call over `steps` back-to-back
-    calls, its HBM roofline fraction, and the oracle on one sampled head."""
+def measure_bwd(gdn, gi, torch, dev, steps, warmup, name="fwd_bwd_bf16", with_fwd=False):
+    """The backward on a workload with upstream gradients do and dht
+    (fwd_bwd_bf16: the headline shapes; fwd_bwd_dk64_bf16: head dimension 64):
+    milliseconds per call over `steps` back-to-back calls, its HBM roofline
+    fraction, and the oracle on one sampled head; with_fwd adds the forward's
+    time on the same inputs and the forward + backward throughput."""
     import oracle
-    name = "fwd_bwd_bf16"
     d = gi.make_config(name)
     do, dht = gi.make_upstream(d, gi.CONFIGS[name]["seed"])
     B, T, Hqk, Hv, dk, dv = d["B"], d["T"], d["Hqk"], d["Hv"], d["dk"], d["dv"]
@@ -97,7 +98,13 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nbytes = bwd_algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
-    bs, hs = 2, 7
+    fwd_ms = None
+    if with_fwd:
+        o = torch.empty_like(dO)
+        ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+        fwd_ms = _time_calls(torch, stream, lambda: gdn.gdn_chunk_fwd(
+            q, k, v, g, beta, out=o, final_state=ht, stream=stream.cuda_stream), steps, warmup)
+    bs, hs = 2, 7 % Hv
     sl = lambda x: gi.widen(x[bs:bs + 1, :, hs:hs + 1])
     ref = oracle.gdn_bwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), d["g"][bs:bs + 1, :, hs:hs + 1],
                          d["beta"][bs:bs + 1, :, hs:hs + 1], sl(do),
@@ -108,17 +115,24 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup):
     for nm, x, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, ref):
         x = x.float().cpu().numpy()
         errs[nm] = float(np.linalg.norm(x - r) / np.linalg.norm(r))
-    log("[bench] backward %.4f ms/call; sampled head rel-L2 %s" %
-        (ms, ", ".join(f"{n} {e:.2e}" for n, e in errs.items())))
+    log("[bench] backward (%s) %.4f ms/call; sampled head rel-L2 %s" %
+        (name, ms, ", ".join(f"{n} {e:.2e}" for n, e in errs.items())))
     achieved = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, do ~ N(0,1) bf16, "
-                        f"dht ~ N(0,0.02) fp32",
-            "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                         "algorithmic_bytes_per_call": nbytes,
-                         "kernels": ["bwd_prep", "bwd_fstate", "bwd_dstate", "bwd_chunk"]},
-            "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
+    res = {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, do ~ N(0,1) bf16, "
+                       f"dht ~ N(0,0.02) fp32",
+           "ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3), "steps": steps,
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                        "algorithmic_bytes_per_call": nbytes,
+                        "kernels": ["bwd_prep", f"gdn_fwd_bf16<false, 3, {dk}>", "bwd_dstate",
+                                    "bwd_chunk"]},
+           "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
+    if with_fwd:
+        log(f"[bench] forward ({name}) {fwd_ms * 1e3:.1f} us/call; forward + backward "
+            f"{B * T / ((fwd_ms + ms) * 1e-3):.3g} tokens/s")
+        res["fwd_ms_per_call"] = fwd_ms
+        res["fwd_bwd_tokens_per_s"] = B * T / ((fwd_ms + ms) * 1e-3)
+    return res
 
 
 def _time_calls(torch, stream, call, steps, warmup):
@@ -471,10 +485,12 @@ def main():
     err_h = float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))
     log(f"[bench] sampled head (b={bs}, h={hs}) rel-L2: output {err_o:.2e}, state {err_h:.2e}")
 
-    bwd = None
+    bwd = bwd_dk64 = None
     if not args.no_bwd:
         log("[bench] backward")
         bwd = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20)
+        bwd_dk64 = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20,
+                               name="fwd_bwd_dk64_bf16", with_fwd=True)
 
     decode = prep = None
     if not args.no_decode:
@@ -538,6 +554,7 @@ def main():
         "cpu_baseline": baseline,
         "check": {"sampled_head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h},
         "bwd": bwd,
+        "bwd_dk64": bwd_dk64,
         "prep": prep,
         "decode": decode,
         "k256": k256,

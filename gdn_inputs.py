@@ -176,6 +176,9 @@ CONFIGS = {
     # head dim 256: the shape of the B=8, T=2048, H=32, D=256 row of the
     # flash-linear-attention benchmark table (drawn on the device)
     "k256_bf16": dict(B=8, T=2048, Hqk=32, Hv=32, dk=256, dv=256, dtype="bf16", seed=1006),
+    # head dimension 64 with upstream gradients, the shape of the B=8, T=1024,
+    # H=8, D=64 row of the flash-linear-attention benchmark table
+    "fwd_bwd_dk64_bf16": dict(B=8, T=1024, Hqk=8, Hv=8, dk=64, dv=64, dtype="bf16", seed=1008),
     # one long row at head dimension 256 and 8 heads (drawn on the device)
     "long_k256_bf16": dict(B=1, T=65536, Hqk=8, Hv=8, dk=256, dv=256, dtype="bf16", seed=1007),
 }

@@ -13,9 +13,11 @@
         calibration copy, and writes profiles/traffic_W.json (read by
         bench.py) and a text summary beside it.
 
-    python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME]
+    python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME] [--by-grid]
         Writes profiles/kernel_stats_NAME.md (default headline_bf16) from a
-        `rocprofv3 --kernel-trace --stats` run of bench.py.
+        `rocprofv3 --kernel-trace --stats` run of bench.py; with --by-grid,
+        from the per-dispatch trace, one line per kernel and grid size (the
+        same kernel launched on two workloads).
 """
 import argparse
 import csv
@@ -132,12 +134,37 @@ def traffic(fetch_dir, write_dir, command, workload):
     print("\n".join(lines))
 
 
-def stats(dirname, command, name="headline_bf16", title=None, only=()):
-    files = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
+def trace_rows(dirname):
+    """Rows like the stats CSV's, one per (kernel, grid size), from the trace."""
+    files = glob.glob(os.path.join(dirname, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
-        raise SystemExit(f"no kernel_stats.csv under {dirname}")
+        raise SystemExit(f"no kernel_trace.csv under {dirname}")
+    groups = {}
     with open(files[0], newline="") as f:
-        rows = list(csv.DictReader(f))
+        for r in csv.DictReader(f):
+            grid = "x".join(str(int(r[f"Grid_Size_{a}"]) // int(r[f"Workgroup_Size_{a}"]))
+                            for a in "XYZ")
+            key = (r["Kernel_Name"], grid)
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in groups.values())
+    rows = []
+    for (kname, grid), v in groups.items():
+        rows.append({"Name": f"{kname} [grid {grid}]", "Calls": len(v),
+                     "AverageNs": sum(v) / len(v), "MinNs": min(v), "MaxNs": max(v),
+                     "Percentage": 100.0 * sum(v) / total, "TotalNs": sum(v)})
+    rows.sort(key=lambda r: -r["TotalNs"])
+    return rows
+
+
+def stats(dirname, command, name="headline_bf16", title=None, only=(), by_grid=False):
+    if by_grid:
+        rows = trace_rows(dirname)
+    else:
+        files = glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no kernel_stats.csv under {dirname}")
+        with open(files[0], newline="") as f:
+            rows = list(csv.DictReader(f))
     if only:
         rows = [r for r in rows if any(s in r["Name"] for s in only)]
     title = title or f"{name}: B=8 T=2048 H=16 d=128 bf16"
@@ -150,7 +177,12 @@ def stats(dirname, command, name="headline_bf16", title=None, only=()):
               "|---|---|---|---|---|---|"]
     for r in rows:
         kname = r["Name"]
-        short = kname if len(kname) <= 70 else kname[:67] + "..."
+        if by_grid:  # keep the template arguments and the grid tag visible
+            base, tag = kname.rsplit(" [grid ", 1)
+            base = base.replace("void ", "").replace("gdn::(anonymous namespace)::", "")
+            short = (base if len(base) <= 60 else base[:57] + "...") + " [grid " + tag
+        else:
+            short = kname if len(kname) <= 70 else kname[:67] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
@@ -177,13 +209,15 @@ def main():
     s.add_argument("--title", default=None)
     s.add_argument("--only", action="append", default=[],
                    help="keep kernels whose name contains this (repeatable)")
+    s.add_argument("--by-grid", action="store_true",
+                   help="one line per kernel and grid size, from the per-dispatch trace")
     args = ap.parse_args()
     if args.cmd == "launch":
         launch(args.launches, args.workload)
     elif args.cmd == "traffic":
         traffic(args.fetch_dir, args.write_dir, args.command, args.workload)
     else:
-        stats(args.stats_dir, args.command, args.name, args.title, args.only)
+        stats(args.stats_dir, args.command, args.name, args.title, args.only, args.by_grid)
 
 
 if __name__ == "__main__":
