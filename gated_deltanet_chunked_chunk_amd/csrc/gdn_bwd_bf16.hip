@@ -765,7 +765,6 @@ struct alignas(16) ChunkSmem {
     float gam[kC], e[kC], l[kC], bt[kC];
     float colpart[4][kC];
     float rowb[2][kC], rowg[2][kC];
-    float dgam[kC];
     float red[kCT];
 };
 
@@ -1085,18 +1084,17 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
                         S.colpart[1][lane] + S.colpart[2][lane] + S.colpart[3][lane];
             if (lane == kC - 1)
                 dgm += gl;
-            S.dgam[lane] = dgm;
-            if (lane < cl.L)
+            // dg: the reverse cumulative sum of dgamma over the 64 rows
+            // (padded rows carry gamma_{L-1}), as a prefix scan of the
+            // lane-reversed values.
+            const float rev = __shfl(dgm, kC - 1 - lane);
+            const float dgs = __shfl(wave_prefix_sum(rev), kC - 1 - lane);
+            if (lane < cl.L) {
                 a.dbeta[(cl.p + lane) * a.Hv + j] = S.rowb[0][lane] + S.rowb[1][lane];
+                a.dg[(cl.p + lane) * a.Hv + j] = dgs;
+            }
         }
         __syncthreads();
-        // dg: the reverse cumulative sum of dgamma (padded rows carry gamma_{L-1}).
-        if (tid < cl.L) {
-            float acc = 0.0f;
-            for (int r = kC - 1; r >= tid; --r)
-                acc += S.dgam[r];
-            a.dg[(cl.p + tid) * a.Hv + j] = acc;
-        }
         // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
