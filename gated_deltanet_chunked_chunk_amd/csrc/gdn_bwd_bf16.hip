@@ -797,9 +797,10 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
     return s;
 }
 
-// Rows [p, p + L) of a [*, H, dk] bf16 tensor (dk = 64 or 128) at head h
-// into a [64][kLK] tile, zeros past dk, 512 threads.
-__device__ __forceinline__ void stage_rows512(uint16_t *dst, const void *src, int64_t p, int L,
+// Rows [p, p + L) of a [*, H, dk] bf16 tensor (dk = 64 or 128) at head h,
+// for a [64][kLK] tile: issue loads this thread's two 16-byte pieces (zeros
+// past dk), commit stores them.  512 threads.
+__device__ __forceinline__ void rows512_issue(u32x4 (&v)[2], const void *src, int64_t p, int L,
                                               int H, int h, int dk, int tid) {
     const uint32_t row_bytes = (uint32_t)H * dk * 2;
     const __amdgpu_buffer_rsrc_t r =
@@ -808,10 +809,17 @@ __device__ __forceinline__ void stage_rows512(uint16_t *dst, const void *src, in
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + kCT * u;
-        const u32x4 v = 8 * (i & 15) < dk
-                            ? __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15), 0, 0)
-                            : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(dst + (i >> 4) * kLK + 8 * (i & 15)) = v;
+        v[u] = 8 * (i & 15) < dk
+                   ? __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15), 0, 0)
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+__device__ __forceinline__ void rows512_commit(uint16_t *dst, const u32x4 (&v)[2], int tid) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + kCT * u;
+        *reinterpret_cast<u32x4 *>(dst + (i >> 4) * kLK + 8 * (i & 15)) = v[u];
     }
 }
 
@@ -826,8 +834,11 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
         return;
     const int G = a.Hv / a.Hqk;
     const float scale = a.scale;
-    stage_rows512(S.K, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
-    stage_rows512(S.Q, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+    // K and Q are loaded with the first head's data and stored after it is
+    // in flight: the chunk's loads overlap.
+    u32x4 kv[2], qv[2];
+    rows512_issue(kv, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+    rows512_issue(qv, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
 
     f32x4 dQ[4], dK[4];   // dk tiles 4h + i
 #pragma unroll
@@ -841,29 +852,41 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
         const int64_t wi = gc * a.Hv + j;
         TilePre pre;
         tile_issue(pre, a, cl, j, wi, 0, tid);
-        __syncthreads();  // the previous head's readers are done
-        {
-            const float *Tg = a.ws_T + wi * (kC * kC);
+        // This head's T, P and gates are loaded with the first tile, before
+        // the barrier, so their latency is not exposed after it.
+        f32x4 tv[2];
+        const float *Tg = a.ws_T + wi * (kC * kC);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int i = tid + kCT * u;
-                u32x2 hi, lo;
-                split4(*reinterpret_cast<const f32x4 *>(Tg + 4 * i), hi, lo);
-                *reinterpret_cast<u32x2 *>(S.Th + (i >> 4) * kL64 + 4 * (i & 15)) = hi;
-                *reinterpret_cast<u32x2 *>(S.Tl + (i >> 4) * kL64 + 4 * (i & 15)) = lo;
-            }
-            *reinterpret_cast<u32x4 *>(S.P + (tid >> 3) * kL64 + 8 * (tid & 7)) =
-                *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * tid);
-        }
+        for (int u = 0; u < 2; ++u)
+            tv[u] = *reinterpret_cast<const f32x4 *>(Tg + 4 * (tid + kCT * u));
+        const u32x4 pv = *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * tid);
+        const float gL = a.ws_gam[wi * kC + kC - 1];
+        float gm = 0.0f, btv = 0.0f;
         if (tid < kC) {
-            const float gm = a.ws_gam[wi * kC + tid];
-            const float gL = a.ws_gam[wi * kC + kC - 1];
+            gm = a.ws_gam[wi * kC + tid];
+            btv = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+        }
+        if (gi == 0) {
+            rows512_commit(S.K, kv, tid);
+            rows512_commit(S.Q, qv, tid);
+        }
+        __syncthreads();  // the previous head's readers are done
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + kCT * u;
+            u32x2 hi, lo;
+            split4(tv[u], hi, lo);
+            *reinterpret_cast<u32x2 *>(S.Th + (i >> 4) * kL64 + 4 * (i & 15)) = hi;
+            *reinterpret_cast<u32x2 *>(S.Tl + (i >> 4) * kL64 + 4 * (i & 15)) = lo;
+        }
+        *reinterpret_cast<u32x4 *>(S.P + (tid >> 3) * kL64 + 8 * (tid & 7)) = pv;
+        if (tid < kC) {
             S.gam[tid] = gm;
             S.e[tid] = __expf(gm);
             S.l[tid] = __expf(gL - gm);
-            S.bt[tid] = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+            S.bt[tid] = btv;
         }
-        const float eL = __expf(a.ws_gam[wi * kC + kC - 1]);
+        const float eL = __expf(gL);
 
         f32x4 dP[2], dA[2];   // column tiles 2h + i
 #pragma unroll
