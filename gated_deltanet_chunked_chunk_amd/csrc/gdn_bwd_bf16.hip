@@ -834,11 +834,35 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
         return;
     const int G = a.Hv / a.Hqk;
     const float scale = a.scale;
-    // K and Q are loaded with the first head's data and stored after it is
-    // in flight: the chunk's loads overlap.
-    u32x4 kv[2], qv[2];
-    rows512_issue(kv, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
-    rows512_issue(qv, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+    // A head's T, P and gates are loaded with its first tile before the
+    // barrier that opens it, so their latency is not exposed after it.
+    {
+        u32x4 kv[2], qv[2];
+        rows512_issue(kv, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+        rows512_issue(qv, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
+        rows512_commit(S.K, kv, tid);
+        rows512_commit(S.Q, qv, tid);
+    }
+    TilePre pre;
+    f32x4 tv[2];
+    u32x4 pv;
+    float gL, gm, btv;
+    auto head_issue = [&](int j, int64_t wi) {
+        tile_issue(pre, a, cl, j, wi, 0, tid);
+        const float *Tg = a.ws_T + wi * (kC * kC);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            tv[u] = *reinterpret_cast<const f32x4 *>(Tg + 4 * (tid + kCT * u));
+        pv = *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * tid);
+        gL = a.ws_gam[wi * kC + kC - 1];
+        gm = 0.0f;
+        btv = 0.0f;
+        if (tid < kC) {
+            gm = a.ws_gam[wi * kC + tid];
+            btv = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
+        }
+    };
+    head_issue(hk * G, gc * a.Hv + hk * G);
 
     f32x4 dQ[4], dK[4];   // dk tiles 4h + i
 #pragma unroll
@@ -850,26 +874,8 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
     for (int gi = 0; gi < G; ++gi) {
         const int j = hk * G + gi;
         const int64_t wi = gc * a.Hv + j;
-        TilePre pre;
-        tile_issue(pre, a, cl, j, wi, 0, tid);
-        // This head's T, P and gates are loaded with the first tile, before
-        // the barrier, so their latency is not exposed after it.
-        f32x4 tv[2];
-        const float *Tg = a.ws_T + wi * (kC * kC);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            tv[u] = *reinterpret_cast<const f32x4 *>(Tg + 4 * (tid + kCT * u));
-        const u32x4 pv = *reinterpret_cast<const u32x4 *>(a.ws_P + wi * (kC * kC) + 8 * tid);
-        const float gL = a.ws_gam[wi * kC + kC - 1];
-        float gm = 0.0f, btv = 0.0f;
-        if (tid < kC) {
-            gm = a.ws_gam[wi * kC + tid];
-            btv = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
-        }
-        if (gi == 0) {
-            rows512_commit(S.K, kv, tid);
-            rows512_commit(S.Q, qv, tid);
-        }
+        if (gi > 0)
+            head_issue(j, wi);
         __syncthreads();  // the previous head's readers are done
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1133,19 +1139,31 @@ __global__ __launch_bounds__(kCT) void bwd_chunk(BwdArgs a) {
         }
     }
 
-    uint16_t *dqo = static_cast<uint16_t *>(a.dq);
-    uint16_t *dko = static_cast<uint16_t *>(a.dk_);
+    // dq and dk through LDS (the union is free once the last head's S + S^T
+    // pass is done), then 16-byte stores of whole rows.
+    uint16_t *dqs = reinterpret_cast<uint16_t *>(&S.u);
+    uint16_t *dks = dqs + kC * kLK;
+    static_assert(2 * kC * kLK * sizeof(uint16_t) <= sizeof(S.u), "dq, dk tiles fit the union");
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * lg + r, colk = 16 * (4 * h + i) + lr;
-            if (row < cl.L && colk < a.dk) {
-                const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)a.dk + colk;
-                dqo[o] = f2bf(dQ[i][r]);
-                dko[o] = f2bf(dK[i][r]);
-            }
+            dqs[row * kLK + colk] = f2bf(dQ[i][r]);
+            dks[row * kLK + colk] = f2bf(dK[i][r]);
         }
+    __syncthreads();
+    const int pieces = a.dk / 8;  // 16-byte pieces per row
+    for (int e = tid; e < kC * pieces; e += kCT) {
+        const int row = e / pieces, pc = e % pieces;
+        if (row < cl.L) {
+            const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)a.dk + 8 * pc;
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dq) + o) =
+                *reinterpret_cast<const u32x4 *>(dqs + row * kLK + 8 * pc);
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dk_) + o) =
+                *reinterpret_cast<const u32x4 *>(dks + row * kLK + 8 * pc);
+        }
+    }
 }
 
 }  // namespace
