@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     uint16_t *Ks = KsAf, *Qs = QsTf;
     float *Af = reinterpret_cast<float *>(KsAf), *Tf = reinterpret_cast<float *>(QsTf);
     __shared__ float Wf[32 * 33];
-    __shared__ uint16_t Ps[kC * kC];   // unpadded: keeps LDS under half a CU's
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[kC * kC];   // unpadded: keeps LDS under half a CU's
     __shared__ float gam[kC], bt[kC];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const int64_t gc = blockIdx.x;
@@ -407,10 +407,14 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     const int64_t wi = gc * a.Hv + j;
     float *To = a.ws_T + wi * (kC * kC);
     uint16_t *Po = a.ws_P + wi * (kC * kC);
-    for (int i = tid; i < kC * kC; i += 256) {
-        To[i] = Tf[(i >> 6) * kLF + (i & 63)];
-        Po[i] = Ps[i];
+    // 16-byte stores: four fp32 of T (gathered from the padded rows), eight
+    // bf16 of P.
+    for (int i = tid; i < kC * kC / 4; i += 256) {
+        const float *tr = Tf + (i >> 4) * kLF + 4 * (i & 15);
+        *reinterpret_cast<f32x4 *>(To + 4 * i) = f32x4{tr[0], tr[1], tr[2], tr[3]};
     }
+    for (int i = tid; i < kC * kC / 8; i += 256)
+        *reinterpret_cast<u32x4 *>(Po + 8 * i) = *reinterpret_cast<const u32x4 *>(Ps + 8 * i);
     if (tid < kC)
         a.ws_gam[wi * kC + tid] = gam[tid];
 }
