@@ -1,4 +1,5 @@
-// Chunkwise gated delta rule backward, bf16 inputs, dk = 128, for gfx950.
+// Chunkwise gated delta rule backward, bf16 inputs, dk = 128 (and dk = 64,
+// staged into the 128-wide tiles with zero upper halves), for gfx950.
 //
 // Reverse mode of the forward in gdn_fwd_bf16.hip: the gradients of
 // L = sum(do * o) + sum(dht * ht) with respect to q, k, v, g, beta and h0.

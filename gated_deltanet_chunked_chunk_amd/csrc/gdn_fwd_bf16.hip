@@ -1,4 +1,7 @@
-// Chunkwise gated delta rule forward, bf16 inputs, dk = 128, for gfx950.
+// Chunkwise gated delta rule forward, bf16 inputs, for gfx950.  The
+// description below is for dk = 128; dk = 64 stages its rows into the same
+// 128-wide layout, and dk = 256 walks chunks of 32 tokens laid into it (see
+// chunk_len).
 //
 // One workgroup owns one (sequence, value head, 64-column value tile) and
 // walks the sequence's chunks of 64 tokens in order.  Value columns of the

@@ -67,16 +67,16 @@ hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream);
 // Workspace bytes of the piece scan for `pieces` pieces per row.
 size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv);
 
-// bf16 q/k/v/o, dk = 128, dv a multiple of 64: one workgroup per
+// bf16 q/k/v/o, dk in {64, 128, 256}, dv a multiple of 64: one workgroup per
 // (sequence, value head, 64 value columns).
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream);
 
-// fp32 q/k/v/o, dk and dv in {64, 128}: one workgroup per (sequence, value
-// head, 32 value columns).
+// fp32 q/k/v/o, dk and dv in {64, 128, 256}: one workgroup per (sequence,
+// value head, 32 value columns).
 hipError_t launch_fwd_f32(const FwdArgs &a, hipStream_t stream);
 
-// Arguments of one backward call, after validation (bf16, dk = 128, dv a
-// multiple of 64).  The workspace regions are described in gdn_bwd_bf16.hip.
+// Arguments of one backward call, after validation (bf16, dk in {64, 128},
+// dv a multiple of 64).  The workspace regions are described in gdn_bwd_bf16.hip.
 struct BwdArgs {
     const void *q;
     const void *k;
@@ -114,7 +114,7 @@ void bwd_carve(BwdArgs &a, void *workspace);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 
 // One recurrent step for N sequences, the state updated in place in a cache
-// of n_slots states.  Sizes: dk in {64, 128}, dv a multiple of 64.
+// of n_slots states.  Sizes: dk in {64, 128, 256}, dv a multiple of 64.
 struct StepArgs {
     const void *q;          // [N, Hqk, dk]
     const void *k;          // [N, Hqk, dk]
