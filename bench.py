@@ -8,7 +8,12 @@ gdn_inputs.py).  Inputs are resident in HBM before timing starts.
 Prints one JSON line with the throughput (tokens/s), the roofline of the
 kernel (HBM-bound: algorithmic bytes per launch over the measured launch
 time, against the 8 TB/s HBM3E peak), and the CPU oracle timed on this host.
-Everything else goes to stderr.
+Further entries of the same line time the other calls on their own
+workloads: the backward (d = 128 and d = 64, the latter with its forward),
+the preparation pass and the fused preparation, the decode step, head
+dimension 256, and with --long the long rows with and without the piece
+scan; each is checked against the oracle on a sample.  Everything else goes
+to stderr.
 """
 import argparse
 import hashlib
