@@ -686,14 +686,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
                                                int lane, int &meet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
     hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
-    int lrv = lane & 15, lgv = lane >> 4;
-    if constexpr (Prep) {
-        // Lane indices re-derived per chunk: without this the compiler hoists
-        // every address built from them out of the chunk loop, which runs out
-        // of registers in this instance.
-        asm volatile("" : "+v"(lrv), "+v"(lgv), "+v"(t));
-    }
-    const int lr = lrv, lg = lgv;
+    const int lr = lane & 15, lg = lane >> 4;
     if (Prep && DK == 256) {
         // The rows' inverse L2 norms (1 without the option): the lanes that
         // stage row t/16 + 16 i (i < 2) hold both of its key halves.
@@ -1231,6 +1224,28 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             chunk0 = (int64_t)it.n * ((a.T + CL - 1) / CL);
         }
     }
+    if constexpr (Prep) {
+        // One chunk loop per role (the barrier counts match): the state
+        // slice and the helpers' prefetch registers are then never live
+        // together, which the preparation's extra registers need.
+        if (state) {
+            for (int c = 0; c < it.nchunks; ++c) {
+                if constexpr (DK == 256)
+                    state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
+                else
+                    state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
+                lds_barrier();
+            }
+        } else {
+            for (int c = 0; c < it.nchunks; ++c) {
+                if (c + 1 < it.nchunks)
+                    helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a,
+                                                                     it, min(CL, it.len - CL * (c + 1)),
+                                                                     c + 2 < it.nchunks ? c + 2 : -1);
+                lds_barrier();
+            }
+        }
+    } else {
     for (int c = 0; c < it.nchunks; ++c) {
         if (state) {
             if (Mode == 3) {
@@ -1251,6 +1266,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                                  min(CL, it.len - CL * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
         }
         lds_barrier();
+    }
     }
 
     if (state) {
