@@ -723,21 +723,27 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         *reinterpret_cast<u32x4 *>(B.V + v_at(t / 8 + 32 * i, 2 * (t % 8))) = st.v[i];
+    const bool gate_act = Prep && (a.flags & kStepGateAct);
     if (hw == 3) {
         // (a2) gamma; padded rows carry g = 0, so gamma_63 = gamma_{L-1}.
-        float gv = st.g, bv = st.b;
-        if (Prep && (a.flags & kStepGateAct)) {
-            gv = lane < L ? logsigmoid_f32(gv) : 0.0f;
-            bv = lane < L ? sigmoid_f32(bv) : 0.0f;
-        }
+        // With the gate activation, g = logsigmoid(raw) with the hardware
+        // exp and log: gamma is a sum of these, so their absolute error
+        // (about 1e-7) is what counts, and beta's sigmoid runs on helper 2.
+        float gv = st.g;
+        if (gate_act)
+            gv = lane < L ? fminf(gv, 0.0f) - __logf(1.0f + __expf(-fabsf(gv))) : 0.0f;
         const float x = wave_prefix_sum(gv);
         const float gL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
         B.gam[lane] = x;
         B.eg[lane] = __expf(x);
         B.el[lane] = __expf(gL - x);
-        B.bt[lane] = bv;
+        if (!gate_act)
+            B.bt[lane] = st.b;
         if (lane == 0)
             B.eL = __expf(gL);
+    } else if (gate_act && hw == 2) {
+        const float e = __expf(-fabsf(st.b));
+        B.bt[lane] = lane < L ? (st.b >= 0.0f ? 1.0f : e) / (1.0f + e) : 0.0f;
     }
     // Meet the other helper waves: the staged rows and gamma are in LDS.
     meet += 4;
