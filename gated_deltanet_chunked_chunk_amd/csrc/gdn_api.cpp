@@ -31,14 +31,19 @@ bool supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
 // whole rows), for batch-mode bf16 calls.  With P pieces the first pass runs
 // (P - 1) pieces x (value tiles + dk / 64 transition tiles) workgroups and
 // the output pass P pieces x value tiles, each workgroup walking about
-// chunks / P chunks; one workgroup per CU is resident.  The plan minimises
-// rounds x chunks per piece over P, with a first-pass chunk costing
-// kEndsCost of an output-pass chunk (measured on the long row), and is used
-// only when it beats whole rows by a tenth.  Pieces hold at least
+// chunks / P chunks; one workgroup per CU is resident.  The cost, in units of
+// one whole-row chunk step, is rounds x chunks per piece for each pass (a
+// first-pass chunk costs about what an output-pass chunk does), plus P - 1
+// serial steps of the scan over start states (kScanStep, by dk) and a fixed
+// cost for the two extra launches.  These were fitted to forced piece counts
+// on rows of 1,024 to 16,384 tokens with 8 to 128 rows; a plan is used only
+// when it beats whole rows by a twentieth.  Pieces hold at least
 // kMinPieceChunks chunks.
 constexpr int64_t kCUs = 256;
-constexpr int64_t kMinPieceChunks = 16;
-constexpr double kEndsCost = 0.8;
+constexpr int64_t kMinPieceChunks = 4;
+constexpr double kPieceFixed = 2.0;
+
+double scan_step_cost(int32_t dk) { return dk == 64 ? 1.9 : dk == 128 ? 3.9 : 8.3; }
 
 struct PiecePlan {
     int32_t pieces;
@@ -56,13 +61,14 @@ PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_
     const int64_t chunks = (T + 63) / 64;
     const auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
     const double whole = rounds(items) * (double)chunks;
-    double best_cost = 0.9 * whole;
+    double best_cost = 0.95 * whole;
     const int64_t max_p = chunks / kMinPieceChunks < 256 ? chunks / kMinPieceChunks : 256;
     for (int64_t n = 2; n <= max_p; ++n) {
         const int64_t per = (chunks + n - 1) / n;
         const int64_t pieces = (chunks + per - 1) / per;
-        const double cost = (rounds((pieces - 1) * items_ends) * kEndsCost +
-                             rounds(pieces * items)) * (double)per;
+        const double cost = (rounds((pieces - 1) * items_ends) + rounds(pieces * items)) *
+                                (double)per +
+                            scan_step_cost(dk) * (double)(pieces - 1) + kPieceFixed;
         if (cost < best_cost) {
             best_cost = cost;
             best = PiecePlan{(int32_t)pieces, per * 64};

@@ -52,20 +52,27 @@ def piece_bytes(B, pieces, Hv, dk, dv):
 
 
 def test_piece_scan_workspace():
-    """Long rows with few heads are split into pieces (at least 16 chunks
-    each) where the planner's cost (workgroup rounds x chunks per piece)
-    beats whole rows.  The long row (1 x 1,064,960 tokens, 16 heads, two
+    """Rows with few heads are split into pieces (at least 4 chunks each)
+    where the planner's cost (workgroup rounds x chunks per piece for both
+    passes, plus the scan's serial steps and a fixed launch cost) beats whole
+    rows by a twentieth.  The long row (1 x 1,064,960 tokens, 16 heads, two
     64-column tiles) splits into 8 pieces of 2,080 chunks."""
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 128, 128, 1) == \
         piece_bytes(1, 8, 16, 128, 128)
-    # 65 chunks, 2 heads: 4 pieces of 17 chunks (the last 14).
+    # 65 chunks, 2 heads: 6 pieces of 11 chunks (the last 10).
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 128, 1) == \
-        piece_bytes(1, 4, 2, 128, 128)
-    # 94 chunks, two rows, dv = 64: 5 pieces of 19 chunks.
+        piece_bytes(1, 6, 2, 128, 128)
+    # 94 chunks, two rows, dv = 64: 8 pieces of 12 chunks.
     assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 6000, 1, 1, 128, 64, 2) == \
-        piece_bytes(2, 5, 1, 128, 64)
-    # Short rows do not gain enough: whole rows, no workspace.
-    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == 0
+        piece_bytes(2, 8, 1, 128, 64)
+    # 47 chunks, two rows: 6 pieces of 8 chunks.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 2, 3000, 1, 1, 128, 64, 2) == \
+        piece_bytes(2, 6, 1, 128, 64)
+    # 16 chunks over 64 rows (dk = dv = 64): the scan's steps and the extra
+    # launches cost more than they save; whole rows, no workspace.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 8, 1024, 8, 8, 64, 64, 8) == 0
+    # 48 chunks at dk = 256 over 2 rows: the scan's steps are dearer there.
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 3037, 1, 2, 256, 64, 1) == 0
     # dk = 256 (four transition tiles per piece): 3 pieces of 5,547 chunks;
     # dv = 256 is tiled like any other dv.
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 256, 256, 1) == \
@@ -73,7 +80,7 @@ def test_piece_scan_workspace():
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 256, 128, 1) == \
         piece_bytes(1, 4, 2, 256, 128)
     assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 4133, 1, 2, 128, 256, 1) == \
-        piece_bytes(1, 4, 2, 128, 256)
+        piece_bytes(1, 6, 2, 128, 256)
 
 
 def test_piece_scan_workspace_checked_before_launch():

@@ -179,9 +179,9 @@ def test_no_final_state_and_preallocated_output():
 
 PIECE_CASES = [
     # B, T, Hqk, Hv, dv, h0 std, pieces the host plan picks
-    (1, 4096 + 37, 1, 2, 128, 0.1, 4),  # ragged last piece, grouped heads
-    (2, 6000, 1, 1, 64, 0.1, 5),        # two rows, dv = 64, a partial last chunk
-    (1, 4096, 1, 1, 128, None, 4),      # pieces of exactly 16 chunks
+    (1, 4096 + 37, 1, 2, 128, 0.1, 6),  # ragged last piece, grouped heads
+    (2, 6000, 1, 1, 64, 0.1, 8),        # two rows, dv = 64, a partial last chunk
+    (1, 4096, 1, 1, 128, None, 6),      # 11-chunk pieces, a 9-chunk last piece
 ]
 
 
@@ -210,7 +210,7 @@ def test_piece_scan_matches_oracle(case):
 def test_piece_scan_carries_state():
     """No decay and a weak write (g = 0, beta = 0.02): each piece's transition
     stays near the identity, so the start states the scan hands over carry
-    most of the result; 4 pieces of 17 chunks, a large initial state."""
+    most of the result; 6 pieces of 11 chunks, a large initial state."""
     d = gi.make(1, 4096 + 37, 1, 2, 128, 128, "bf16", 3950, h0_std=1.0)
     d["g"] = np.zeros_like(d["g"])
     d["beta"] = np.full_like(d["beta"], 0.02)
@@ -253,7 +253,8 @@ def test_bf16_dk64_packed_with_empty_document():
 
 
 def test_bf16_dk64_piece_scan():
-    """dk = 64 through the piece scan: 4 pieces, one transition tile."""
+    """dk = 64 through the piece scan: 11 pieces of 6 chunks, one transition
+    tile."""
     d = gi.make(1, 4096 + 37, 1, 2, 64, 128, "bf16", 4160, h0_std=0.5)
     d["g"] = (d["g"] / 8).astype(np.float32)  # slower decay: carried states matter
     eo, eh = check(d, label="bf16 dk64 piece scan")
@@ -373,10 +374,10 @@ def test_bf16_dk256_piece_scan_carries_state():
     """No decay and a weak write (g = 0, beta = 0.02) at dk = 256: every
     piece's transition stays near the identity, so the scanned start states
     (all four 64-column blocks of Phi) carry most of the result."""
-    d = gi.make(1, 3000 + 37, 1, 2, 256, 64, "bf16", 4495, h0_std=1.0)
+    d = gi.make(1, 5000 + 37, 1, 2, 256, 64, "bf16", 4495, h0_std=1.0)
     d["g"] = np.zeros_like(d["g"])
     d["beta"] = np.full_like(d["beta"], 0.02)
-    _dk256_piece_check(d, 3, "bf16 dk256 piece scan, g = 0, beta = 0.02")
+    _dk256_piece_check(d, 4, "bf16 dk256 piece scan, g = 0, beta = 0.02")
 
 
 def test_bf16_dk256_piece_scan_with_in_op_preparation():
