@@ -238,3 +238,21 @@ def test_step_binding_checks_tensors_on_host():
                                torch.zeros(2, 2, 128, 128))
     with pytest.raises(gdn.GdnError):
         gdn.gdn_prepare_inputs(x, x, torch.zeros(2, 2), torch.zeros(2, 2))
+
+
+def test_piece_plan_properties():
+    """Over a grid of shapes: the plan never splits rows once the output pass
+    of whole rows already fills every CU (B * H_v * dv / 64 >= 256 workgroups),
+    and whatever it picks is a whole number of pieces between 2 and 256."""
+    for dk in (64, 128, 256):
+        for dv in (64, 128, 256):
+            for B, Hv in ((1, 1), (1, 4), (2, 8), (4, 16), (8, 16), (8, 32), (16, 32)):
+                for T in (1, 255, 4096, 65536, 1 << 20):
+                    need = gdn.gdn_chunk_fwd_workspace_size(1, B, T, 1, Hv, dk, dv, B)
+                    if B * Hv * dv // 64 >= 256:
+                        assert need == 0, (B, T, Hv, dk, dv)
+                    if need == 0:
+                        continue
+                    found = [p for p in range(2, 257) if piece_bytes(B, p, Hv, dk, dv) == need]
+                    assert len(found) == 1, (B, T, Hv, dk, dv, need)
+                    assert found[0] <= -(-T // 64), (B, T, Hv, dk, dv)
