@@ -70,16 +70,19 @@ typedef enum {
 
 /*
  * Bytes of device workspace gdn_chunk_fwd can use for these sizes (0 when it
- * uses none).  Only the piece scan of long rows uses a workspace: batch-mode
- * bf16 calls with so few rows x heads that most compute units would idle are
- * split along the rows into pieces that run in parallel (the exact piece
+ * uses none).  Only the piece scan uses a workspace: batch-mode bf16 calls
+ * with so few rows x heads that compute units would idle are split along the
+ * rows into pieces that run in parallel (the exact piece
  * scan the jax-linear-attention page names under "Where we lose": each
  * piece's end state is an affine map of its start state, F + Phi S, so the
  * start states follow from a short scan over the pieces, then every piece
  * is run again from its true start).  The workspace holds, per piece but the
  * last and head, F and Phi (dk x (dv + dk) fp32) and the start state
- * (dk x dv fp32).  dk = 256 always runs whole rows (returns 0).  Returns 0
- * as well for sizes the forward would reject.
+ * (dk x dv fp32).  The host picks the piece count from the sizes alone (a
+ * cost model of workgroup rounds, the scan's serial steps and the extra
+ * launches); calls whose whole rows already fill every compute unit, or
+ * where pieces would not save a twentieth, return 0.  Returns 0 as well for
+ * fp32, and for sizes the forward would reject.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B
  * (packed calls never use the piece scan).
