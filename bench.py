@@ -11,9 +11,11 @@ time, against the 8 TB/s HBM3E peak), and the CPU oracle timed on this host.
 Further entries of the same line time the other calls on their own
 workloads: the backward (d = 128 and d = 64, the latter with its forward),
 the preparation pass and the fused preparation, the decode step, head
-dimension 256, and with --long the long rows with and without the piece
-scan; each is checked against the oracle on a sample.  Everything else goes
-to stderr.
+dimension 256, the long rows with and without the piece scan, the packed
+workload with grouped heads, and the tiny fp32 workload; each is checked
+against the oracle on a sample.  Before the warm-up steps the step runs back
+to back, untimed, for --settle-ms (clocks ramp up under load); the timed
+region is exactly --steps steps.  Everything else goes to stderr.
 """
 import argparse
 import hashlib
@@ -55,11 +57,13 @@ def algorithmic_bytes(B, T, Hqk, Hv, dk, dv, in_bytes=2, h0=False):
 
 
 def chunked_flops(B, T, Hv, dk, dv, C=64):
-    """Contractions of the chunk form, dense per chunk: K K^T, Q K^T (2 C^2 dk
-    each), K h and Q h (2 C dk dv each), T'Y and P Delta (2 C^2 dv each),
-    K^T Delta (2 C dk dv), the triangular inverse (C^3 / 3)."""
+    """Algorithmic flops of the chunk form, per chunk and value head:
+    2 C^2 (3 dk + 2 dv) for K K^T, Q K^T and W = T' diag(e^gamma) K (the
+    three C x C x dk products) and U = T' V, P Delta (the two C x C x dv
+    ones); 6 C dk dv for W h, Q h and K^T Delta'; 2 C^3 / 3 for the
+    triangular inverse."""
     chunks = B * Hv * (-(-T // C))
-    per = 2 * C * C * (2 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3
+    per = 2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + 2 * C ** 3 / 3
     return chunks * per
 
 
@@ -140,6 +144,39 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup, name="fwd_bwd_bf16", with_fw
     return res
 
 
+def per_launch(torch, stream, call, n, flush=None):
+    """Per-launch durations (ms) with HIP events on the launch stream; with
+    `flush` (a device buffer) it is overwritten before every launch, outside
+    the events, so each launch starts with cold caches (L2 and the 256 MB
+    MALL).  Returns mean, median and minimum."""
+    times = []
+    for i in range(n):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    t = np.array(times)
+    return {"mean": float(t.mean()), "median": float(np.median(t)), "min": float(t.min()),
+            "n": n}
+
+
+def settle_clocks(torch, call, ms):
+    """Launches `call` back to back, untimed, for about `ms` of wall clock so
+    the GPU's clocks have ramped up under this load; returns the count."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(20):
+            call()
+        n += 20
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return n
+
+
 def _time_calls(torch, stream, call, steps, warmup):
     """Milliseconds per call over `steps` back-to-back calls on `stream`."""
     for _ in range(warmup):
@@ -187,16 +224,23 @@ def measure_decode(gdn, gi, torch, dev, steps, warmup):
     err_o = float(np.linalg.norm(o[sel].float().cpu().numpy() - ro) / np.linalg.norm(ro))
     err_c = float(np.linalg.norm(cache[sel].cpu().numpy() - rc) / np.linalg.norm(rc))
     ms = _time_calls(torch, stream, call, steps, warmup)
+    flushed = per_launch(torch, stream, call, 50, flush=flush_buffer(torch, dev))
     nbytes = decode_algorithmic_bytes(N, Hqk, Hv, dk, dv)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] decode step {ms * 1e3:.1f} us/call ({achieved:.0f} GB/s); "
+    log(f"[bench] decode step {ms * 1e3:.1f} us/call back to back ({achieved:.0f} GB/s), "
+        f"{flushed['median'] * 1e3:.1f} us flushed (median); "
         f"check rel-L2 output {err_o:.2e}, cache {err_c:.2e}")
     return {"workload": f"{name}: N={N} sequences x 1 token, H={Hv}, dk={dk}, dv={dv}, "
                         f"bf16 q/k/v/o, fp32 cache of {N} slots",
             "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3), "steps": steps,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "frac_flushed_median": nbytes / (flushed["median"] * 1e-3) / 1e9 /
+                                                HBM_PEAK_GBPS,
+                         "note": "the 272 MB working set fits the 256 MB MALL between "
+                                 "back-to-back calls; the flushed figure is the HBM one",
                          "algorithmic_bytes_per_call": nbytes, "kernels": ["recurrent_step"]},
+            "launch_ms_flushed": flushed,
             "check": {"sequences": sel, "rel_l2_output": err_o, "rel_l2_cache": err_c}}
 
 
@@ -218,6 +262,7 @@ def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
         if st != 0:
             raise RuntimeError(gdn.gdn_status_string(st))
     ms = _time_calls(torch, stream, call, steps, warmup)
+    flushed = per_launch(torch, stream, call, 50, flush=flush_buffer(torch, q.device))
     nbytes = 2 * (q.numel() + k.numel()) * q.element_size() + 2 * (g.numel() + beta.numel()) * 4
     achieved = nbytes / (ms * 1e-3) / 1e9
     o = torch.empty_like(vv)
@@ -227,11 +272,17 @@ def measure_prep(gdn, torch, q, k, vv, g, beta, fwd_ms, steps, warmup):
                                       stream=stream.cuda_stream, use_qk_l2norm=True,
                                       gate_activation=True)
     fused_ms = _time_calls(torch, stream, fused, 1000, 500)
-    log(f"[bench] preparation pass {ms * 1e3:.1f} us/call ({achieved:.0f} GB/s); forward with "
+    log(f"[bench] preparation pass {ms * 1e3:.1f} us/call back to back ({achieved:.0f} GB/s), "
+        f"{flushed['median'] * 1e3:.1f} us flushed (median); forward with "
         f"fused preparation {fused_ms * 1e3:.1f} us (plain {fwd_ms * 1e3:.1f} us)")
     return {"ms_per_call": ms, "fwd_fused_prep_ms": fused_ms, "fwd_plain_ms": fwd_ms,
+            "launch_ms_flushed": flushed,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "frac_flushed_median": nbytes / (flushed["median"] * 1e-3) / 1e9 /
+                                                HBM_PEAK_GBPS,
+                         "note": "back to back, the 273 MB working set largely stays in the "
+                                 "256 MB MALL; the flushed figure is the HBM one",
                          "algorithmic_bytes_per_call": nbytes, "kernels": ["preprocess"]}}
 
 
@@ -239,29 +290,131 @@ def measure_long(gdn, gi, torch, dev, steps=3, name="long_bf16"):
     """A long-row workload (long_bf16: B=1, T=1,064,960, H=16, d=128;
     long_k256_bf16: B=1, T=65,536, H=8, d=256; bf16, inputs drawn on the
     device with the same recipe): milliseconds per forward with the piece
-    scan and with whole rows, and the HBM roofline fraction of each."""
+    scan and with whole rows, the HBM roofline fraction of each, and the
+    agreement of the two routes' outputs and final states (their parity with
+    the oracle is a GPU test)."""
     c = gi.CONFIGS[name]
     B, T, Hqk, Hv, dk, dv = c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"]
     t = gi.make_device(B, T, Hqk, Hv, dk, dv, c["seed"], device=dev)
     q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
-    o = torch.empty_like(v)
-    ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    outs = {}
     ws = torch.empty(max(1, gdn.gdn_chunk_fwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     out = {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, zero initial state"}
     nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
     for mode, kw in (("pieces", dict(workspace=ws)), ("whole_rows", dict(pieces=False))):
+        o = torch.empty_like(v)
+        ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
         call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht,
                                          stream=stream.cuda_stream, **kw)
-        ms = _time_calls(torch, stream, call, steps, 1)
-        out[mode] = {"ms_per_call": ms, "tokens_per_s": B * T / (ms * 1e-3),
+        call()
+        tm = per_launch(torch, stream, call, steps)
+        ms = tm["median"]
+        out[mode] = {"ms_per_call_median": ms, "ms_per_call_min": tm["min"],
+                     "tokens_per_s": B * T / (ms * 1e-3),
                      "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-        log(f"[bench] {name}, {mode}: {ms:.2f} ms/call")
+        outs[mode] = (o, ht)
+        log(f"[bench] {name}, {mode}: {ms:.2f} ms/call (median of {steps})")
+    (o1, h1), (o2, h2) = outs["pieces"], outs["whole_rows"]
+    rel = lambda a, b: float(torch.linalg.vector_norm((a.float() - b.float()).ravel()) /
+                             torch.linalg.vector_norm(b.float().ravel()))
+    out["pieces_vs_whole_rows_rel_l2"] = {"output": rel(o1, o2), "state": rel(h1, h2)}
+    out["pieces"]["speedup_over_whole_rows"] = (out["whole_rows"]["ms_per_call_median"] /
+                                                out["pieces"]["ms_per_call_median"])
     out["algorithmic_bytes_per_call"] = nbytes
-    del q, k, v, g, beta, o, t
+    del q, k, v, g, beta, t, outs, o1, h1, o2, h2
     torch.cuda.empty_cache()
     return out
+
+
+def measure_packed(gdn, gi, torch, dev, steps, warmup):
+    """The packed workload (16,384 tokens in geometric documents of mean
+    length 1024, H_qk=16, H_v=32, d=128, bf16, an initial state per
+    document): milliseconds per forward back to back and flushed, tokens/s,
+    the HBM roofline fraction (initial and final states counted), and the
+    oracle on two sampled (document, head) pairs."""
+    import oracle
+    name = "packed_gva_bf16"
+    d = gi.make_config(name)
+    Hqk, Hv, dk, dv, T, N = d["Hqk"], d["Hv"], d["dk"], d["dv"], d["T"], d["N"]
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    g, beta = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+    h0 = torch.from_numpy(d["h0"]).to(dev)
+    cu = d["cu_seqlens"]
+    cu_dev = torch.from_numpy(cu).to(dev)
+    cu_host = [int(x) for x in cu]
+    o = torch.empty_like(v)
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu_dev,
+                                     cu_seqlens_host=cu_host, out=o, final_state=ht,
+                                     stream=stream.cuda_stream)
+    ms = _time_calls(torch, stream, call, steps, warmup)
+    flushed = per_launch(torch, stream, call, 50, flush=flush_buffer(torch, dev))
+    nbytes = (2 * T * Hqk * dk * 2 + 2 * T * Hv * dv * 2 + 2 * T * Hv * 4 +
+              2 * N * Hv * dk * dv * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    # Two (document, head) pairs drawn with the workload seed.
+    seed = gi.CONFIGS[name]["seed"]
+    rng = np.random.default_rng(seed)
+    lens = np.diff(cu)
+    docs = sorted(int(x) for x in rng.choice(np.flatnonzero(lens > 0), size=2, replace=False))
+    heads = gi.sampled_heads(seed, Hv)
+    errs = []
+    G = Hv // Hqk
+    for n, j in zip(docs, heads):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        sl = lambda x, hh: gi.widen(x[:, t0:t1, hh:hh + 1])
+        ro, rh = oracle.gdn_fwd(sl(d["q"], j // G), sl(d["k"], j // G), sl(d["v"], j),
+                                d["g"][:, t0:t1, j:j + 1], d["beta"][:, t0:t1, j:j + 1],
+                                h0=d["h0"][n:n + 1, j:j + 1].astype(np.float64))
+        go = o[:, t0:t1, j:j + 1].float().cpu().numpy()
+        gh = ht[n:n + 1, j:j + 1].cpu().numpy()
+        errs.append({"document": n, "tokens": t1 - t0, "head": j,
+                     "rel_l2_output": float(np.linalg.norm(go - ro) / np.linalg.norm(ro)),
+                     "rel_l2_state": float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))})
+    log(f"[bench] packed ({N} documents): {ms * 1e3:.1f} us/call back to back, "
+        f"{flushed['median'] * 1e3:.1f} us flushed (median); checks {errs}")
+    return {"workload": f"{name}: {T} tokens in {N} documents (geometric, mean 1024), "
+                        f"H_qk={Hqk} H_v={Hv} dk={dk} dv={dv}, h0 ~ N(0, 0.02)",
+            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3), "steps": steps,
+            "launch_ms_flushed": flushed,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "frac_flushed_median": nbytes / (flushed["median"] * 1e-3) / 1e9 /
+                                                HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes,
+                         "kernel": "gdn_fwd_bf16<false, 0, 128>"},
+            "check": errs}
+
+
+def measure_tiny(gdn, gi, torch, dev):
+    """The tiny fp32 workload (B=1, T=256, H=2, d=64): launch-latency bound,
+    so only its absolute time is reported (per-launch events, back to back),
+    with the whole output checked against the oracle."""
+    import oracle
+    d = gi.make_config("tiny_f32")
+    tt = {x: torch.from_numpy(d[x]).to(dev) for x in ("q", "k", "v", "g", "beta")}
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    call = lambda: res.update(zip(("o", "ht"), gdn.gdn_chunk_fwd(
+        tt["q"], tt["k"], tt["v"], tt["g"], tt["beta"], stream=stream.cuda_stream)))
+    call()
+    tm = per_launch(torch, stream, call, 200)
+    ro, rh = oracle.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    eo = float(np.linalg.norm(res["o"].cpu().numpy() - ro) / np.linalg.norm(ro))
+    eh = float(np.linalg.norm(res["ht"].cpu().numpy() - rh) / np.linalg.norm(rh))
+    log(f"[bench] tiny fp32: {tm['median'] * 1e3:.1f} us per launch (median); rel-L2 output "
+        f"{eo:.2e}, state {eh:.2e}")
+    return {"workload": "tiny_f32: B=1 T=256 H=2 dk=64 dv=64, fp32, zero initial state",
+            "launch_ms": tm, "bound": "launch latency (absolute time only)",
+            "check": {"rel_l2_output": eo, "rel_l2_state": eh}}
+
+
+def flush_buffer(torch, dev, mb=512):
+    return torch.empty(mb << 20, dtype=torch.uint8, device=dev)
 
 
 def measure_k256(gdn, gi, torch, dev, steps, warmup):
@@ -370,18 +523,21 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    # The GPU's clocks take tens of milliseconds of load to settle; 500
-    # launches (about 50 ms) precede the timed region.
     ap.add_argument("--warmup", type=int, default=500)
+    # The GPU's clocks take tens of milliseconds of load to ramp up: before
+    # the warm-up steps the step is launched back to back, untimed, for this
+    # long.  The timed region is still exactly --steps steps.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step and preparation measurements")
     ap.add_argument("--no-k256", action="store_true",
                     help="skip the head-dimension-256 measurement")
-    ap.add_argument("--long", action="store_true",
-                    help="also time the long rows (B=1, T=1,064,960, d=128; B=1, T=65,536, "
-                         "d=256), with and without pieces")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long rows (B=1, T=1,064,960, d=128; B=1, T=65,536, d=256)")
+    ap.add_argument("--no-packed", action="store_true",
+                    help="skip the packed workload and the tiny fp32 one")
     ap.add_argument("--flush-mb", type=int, default=512,
                     help="cache-flush write between the per-launch timings")
     args = ap.parse_args()
@@ -415,7 +571,8 @@ def main():
     def step():
         gdn.gdn_chunk_fwd(q, k, v, g, beta, out=o, final_state=ht, stream=stream.cuda_stream)
 
-    log(f"[bench] warmup {args.warmup}")
+    settle_n = settle_clocks(torch, step, args.settle_ms) if args.settle_ms > 0 else 0
+    log(f"[bench] clocks settled over {settle_n} untimed launches; warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -438,23 +595,9 @@ def main():
 
     # Per-launch durations with HIP events on the launch stream: once back to
     # back, once with the caches flushed by a large write before each launch.
-    def per_launch(n, flush):
-        buf = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if flush else None
-        times = []
-        for i in range(n):
-            if flush:
-                buf.fill_(i & 0xFF)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            b.synchronize()
-            times.append(a.elapsed_time(b))
-        return np.array(times)
-
     n_launch = min(max(args.steps, 10), 100)
-    t_b2b = per_launch(n_launch, False)
-    t_fl = per_launch(n_launch, True)
+    t_b2b = per_launch(torch, stream, step, n_launch)
+    t_fl = per_launch(torch, stream, step, n_launch, flush=flush_buffer(torch, dev, args.flush_mb))
     nbytes = algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
     flops = chunked_flops(B, T, Hv, dk, dv)
     # One launch per step on `stream`: the timed region's events give the
@@ -508,8 +651,14 @@ def main():
         log("[bench] head dimension 256")
         k256 = measure_k256(gdn, gi, torch, dev, steps=200, warmup=100)
 
+    packed = tiny = None
+    if not args.no_packed:
+        log("[bench] packed documents and the tiny fp32 workload")
+        packed = measure_packed(gdn, gi, torch, dev, steps=200, warmup=50)
+        tiny = measure_tiny(gdn, gi, torch, dev)
+
     long_row = long_k256 = None
-    if args.long:
+    if not args.no_long:
         log("[bench] long rows")
         long_row = measure_long(gdn, gi, torch, dev)
         long_k256 = measure_long(gdn, gi, torch, dev, steps=10, name="long_k256_bf16")
@@ -527,6 +676,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"ms": args.settle_ms, "launches": settle_n,
+                         "note": "untimed back-to-back launches before the warm-up steps"},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -548,10 +699,10 @@ def main():
             "kernel": KERNEL_NAME,
             "algorithmic_bytes_per_launch": nbytes,
             "launch_ms_mean": launch_ms,
-            "launch_ms_event_pairs_mean": float(np.mean(t_b2b)),
-            "launch_ms_event_pairs_median": float(np.median(t_b2b)),
-            "launch_ms_flushed_mean": float(np.mean(t_fl)),
-            "frac_flushed": nbytes / (float(np.mean(t_fl)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "launch_ms_back_to_back": t_b2b,
+            "launch_ms_flushed": t_fl,
+            "frac_flushed_median": nbytes / (t_fl["median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "frac_flushed_min": nbytes / (t_fl["min"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "mfma_bf16_tflops": flops / (launch_ms * 1e-3) / 1e12,
             "mfma_frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "copy_gbps": copy_gbps,
@@ -563,6 +714,8 @@ def main():
         "prep": prep,
         "decode": decode,
         "k256": k256,
+        "packed": packed,
+        "tiny": tiny,
         "long_row": long_row,
         "long_k256": long_k256,
         "wall_s_timed_region": wall,

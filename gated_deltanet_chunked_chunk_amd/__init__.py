@@ -108,6 +108,8 @@ def _check_inputs(torch, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens
             raise GdnError(1, f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise GdnError(1, f"{name} must be contiguous")
+        if t.device != q.device:
+            raise GdnError(1, f"{name} must be on {q.device}, the device of q")
     dt = _dtype_code(torch, q.dtype)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise GdnError(1, "q, k and v must share one dtype")
@@ -134,6 +136,31 @@ def _check_inputs(torch, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens
         if initial_state.dtype != torch.float32 or initial_state.shape != (N, Hv, dk, dv):
             raise GdnError(1, "initial_state must be fp32 [N, H_v, dk, dv]")
     return dt, B, T, Hqk, Hv, dk, dv, N, host_arr
+
+
+def _check_buffer(torch, name, t, shape, dtype, device):
+    """A caller-provided output buffer: exact shape and dtype, on the inputs'
+    device, contiguous (the kernels write through its pointer)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise GdnError(1, f"{name} must be a device tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise GdnError(1, f"{name} must be {dtype} of shape {tuple(shape)}, got "
+                          f"{t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise GdnError(1, f"{name} must be contiguous")
+
+
+def _check_workspace(torch, ws, need, device):
+    """A caller-provided workspace: a contiguous device buffer of at least
+    `need` bytes; returns its size in bytes."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device:
+        raise GdnError(1, f"workspace must be a device tensor on {device}")
+    if not ws.is_contiguous():
+        raise GdnError(1, "workspace must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise GdnError(4, f"workspace holds {nbytes} bytes, the call needs {need}")
+    return nbytes
 
 
 def _raise(st):
@@ -174,15 +201,24 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
     dev = q.device
     if out is None:
         out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_buffer(torch, "out", out, (B, T, Hv, dv), q.dtype, dev)
     if not output_final_state:
         final_state = None
+    elif final_state is None:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _check_buffer(torch, "final_state", final_state, (N, Hv, dk, dv), torch.float32, dev)
     ws_bytes = lib.gdn_chunk_fwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
+    ws_len = 0
     if not pieces:
         workspace = None
-    elif ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace is None:
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            ws_len = ws_bytes
+    else:
+        ws_len = _check_workspace(torch, workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
@@ -191,8 +227,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
                            ptr(initial_state), ptr(cu_seqlens),
                            None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
                            N if cu_seqlens is not None else 0, ptr(out), ptr(final_state),
-                           ptr(workspace), 0 if workspace is None else workspace.numel(),
-                           stream)
+                           ptr(workspace), ws_len, stream)
     if st != 0:
         _raise(st)
     return out, final_state
@@ -227,8 +262,13 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
     dbeta = torch.empty_like(beta)
     dh0 = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
     ws_bytes = lib.gdn_chunk_bwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
-    if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0
+    if workspace is None:
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            ws_len = ws_bytes
+    else:
+        ws_len = _check_workspace(torch, workspace, ws_bytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
@@ -237,7 +277,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
                            None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
                            N if cu_seqlens is not None else 0, ptr(do), ptr(dht), ptr(dq),
                            ptr(dk_), ptr(dv_), ptr(dg), ptr(dbeta), ptr(dh0), ptr(workspace),
-                           0 if workspace is None else workspace.numel(), stream)
+                           ws_len, stream)
     if st != 0:
         _raise(st)
     return dq, dk_, dv_, dg, dbeta, dh0
@@ -318,6 +358,11 @@ def gdn_recurrent_step(q, k, v, g, beta, state, scale=1.0, slots=None, use_qk_l2
         raise GdnError(1, "slots must be int32 [N]")
     if out is None:
         out = torch.empty((N, Hv, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check_buffer(torch, "out", out, (N, Hv, dv), q.dtype, q.device)
+    for name, t in named[1:]:
+        if t.device != q.device:
+            raise GdnError(1, f"{name} must be on {q.device}")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.gdn_recurrent_step(dt, N, Hqk, Hv, dk, dv, q.data_ptr(), k.data_ptr(),

@@ -16,6 +16,7 @@ namespace {
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+
 bool aligned16(const void *p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -93,13 +94,14 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
     return gdn::fwd_piece_bytes((int32_t)B, p.pieces, H_v, dk, dv);
 }
 
-gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
-                         int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float scale, uint32_t flags,
-                         const float *h0,
-                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                         int32_t n_seqs, void *o, float *ht, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+// Checks a forward call before anything touches the GPU; on success N is
+// the number of sequences.
+static gdn_status fwd_validate(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                               int32_t dk, int32_t dv, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta, uint32_t flags,
+                               const float *h0, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t n_seqs, const void *o,
+                               const float *ht, int32_t &N) {
     if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
         return GDN_ERR_INVALID_ARG;
     if (!q || !k || !v || !g || !beta || !o)
@@ -115,7 +117,7 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     const int64_t dmax = dk > dv ? dk : dv;
     if (B > INT64_MAX / T || B * T > INT64_MAX / (hmax * dmax))
         return GDN_ERR_INVALID_ARG;
-    int32_t N = (int32_t)B;
+    N = (int32_t)B;
     if (cu_seqlens) {
         if (B != 1 || n_seqs < 1)
             return GDN_ERR_INVALID_ARG;
@@ -135,18 +137,17 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(o) || !aligned16(h0) || !aligned16(ht) || !aligned16(cu_seqlens))
         return GDN_ERR_MISALIGNED;
-    // The piece scan runs when a workspace is given; without one, whole rows.
-    PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
-    if (!workspace)
-        plan = PiecePlan{1, T};
-    const size_t need = gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv);
-    if (need > 0) {
-        if (workspace_bytes < need)
-            return GDN_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-            return GDN_ERR_MISALIGNED;
-    }
+    return GDN_OK;
+}
 
+// Launches a validated forward call with `plan`, whose piece arrays (if any)
+// live at `scratch`.
+static gdn_status fwd_launch(gdn_dtype dtype, int64_t T, int32_t H_qk, int32_t H_v, int32_t dk,
+                             int32_t dv, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float scale, uint32_t flags,
+                             const float *h0, const int32_t *cu_seqlens, int32_t N, void *o,
+                             float *ht, const PiecePlan &plan, void *scratch,
+                             hipStream_t stream) {
     gdn::FwdArgs a;
     a.q = q;
     a.k = k;
@@ -172,11 +173,10 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.chunk_states = nullptr;
     if (plan.pieces > 1) {
         const size_t per = (size_t)N * (plan.pieces - 1) * H_v * dk;
-        a.piece_ends = static_cast<float *>(workspace);
-        a.piece_starts = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+        a.piece_ends = static_cast<float *>(scratch);
+        a.piece_starts = reinterpret_cast<float *>(static_cast<char *>(scratch) +
                                                    (per * (dv + dk) * 4 + 255) / 256 * 256);
     }
-
     const hipError_t e = dtype == GDN_BF16 ? gdn::launch_fwd_bf16(a, stream)
                                            : gdn::launch_fwd_f32(a, stream);
     if (e != hipSuccess) {
@@ -184,6 +184,33 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
         return GDN_ERR_HIP;
     }
     return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                         int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float scale, uint32_t flags,
+                         const float *h0,
+                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                         int32_t n_seqs, void *o, float *ht, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    int32_t N = 0;
+    const gdn_status st = fwd_validate(dtype, B, T, H_qk, H_v, dk, dv, q, k, v, g, beta, flags,
+                                       h0, cu_seqlens, cu_seqlens_host, n_seqs, o, ht, N);
+    if (st != GDN_OK)
+        return st;
+    // The piece scan runs when a workspace is given; without one, whole rows.
+    PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
+    if (!workspace)
+        plan = PiecePlan{1, T};
+    const size_t need = gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv);
+    if (need > 0) {
+        if (workspace_bytes < need)
+            return GDN_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return GDN_ERR_MISALIGNED;
+    }
+    return fwd_launch(dtype, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, flags, h0,
+                      cu_seqlens, N, o, ht, plan, workspace, stream);
 }
 
 // The backward's shapes: bf16, dk in {64, 128}, dv in {64, 128, 256}.

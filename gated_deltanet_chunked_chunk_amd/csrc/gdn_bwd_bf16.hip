@@ -186,24 +186,20 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// x += (a from lane R of this lane's 16-lane row) * b.
+// One step of the forward substitution of a diagonal block (see bwd_prep):
+// x_r2 -= A[r2][R] x_R for r2 > R, the factors read from the block's fp32
+// copy at addresses every lane of the 16-lane row shares (broadcast reads).
 template <int R>
-__device__ __forceinline__ void fmac_rowbcast(float &x, float a, float b) {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(x) : "v"(a), "v"(b), "i"(R));
-}
-
-template <int R>
-__device__ __forceinline__ void dinv_step(float (&x)[16], const float (&na)[16]) {
+__device__ __forceinline__ void dinv_step(float (&x)[16], const float *blk, int ld) {
 #pragma unroll
     for (int r2 = R + 1; r2 < 16; ++r2)
-        fmac_rowbcast<R>(x[r2], na[r2], x[R]);
+        x[r2] = __builtin_fmaf(-blk[r2 * ld + R], x[R], x[r2]);
 }
 
 template <int... R>
-__device__ __forceinline__ void dinv_steps(float (&x)[16], const float (&na)[16],
+__device__ __forceinline__ void dinv_steps(float (&x)[16], const float *blk, int ld,
                                            std::integer_sequence<int, R...>) {
-    (dinv_step<R>(x, na), ...);
+    (dinv_step<R>(x, blk, ld), ...);
 }
 
 // Where chunk gc of the whole call lies.
@@ -353,13 +349,11 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     // = column c; once x_r is final, A[r2][r] x_r leaves every later row.
     if (w == 0) {
         const int c = lr, gb = lg;
-        float na[16], x[16];
+        float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            na[r] = -Af[(16 * gb + r) * kLF + 16 * gb + c];
+        for (int r = 0; r < 16; ++r)
             x[r] = r == c ? 1.0f : 0.0f;
-        }
-        dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
+        dinv_steps(x, Af + 16 * gb * kLF + 16 * gb, kLF, std::make_integer_sequence<int, 15>{});
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             Tf[(16 * gb + r) * kLF + 16 * gb + c] = x[r];

@@ -512,44 +512,39 @@ __device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const b
     diag_finish<I, Nrm>(ad, B, block_product<DK / 32>(ki, ki), lr, lg);
 }
 
-// x += (a from lane R of this lane's 16-lane row) * b: one v_fmac_f32 with a
-// DPP row_newbcast source.
+// (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32, the four blocks
+// in one wave: lane row g works on block g (from its copy of -A_gg in Ad[g],
+// column-major) and lane c of the row computes column c.  Once x_r is final,
+// -A[r2][r] x_r is added to every row r2 > r; the factors -A[r2][r] are
+// column r of the copy, which every lane of the row reads at the same
+// addresses (a broadcast read, one 16-byte read per four factors).  Column c
+// is stored, as hi and lo bf16, as row 16 g + c of D^T.
 template <int R>
-__device__ __forceinline__ void fmac_rowbcast(float &x, float a, float b) {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(x) : "v"(a), "v"(b), "i"(R));
-}
-
-template <int R>
-__device__ __forceinline__ void dinv_step(float (&x)[16], const f32x4 (&na)[4]) {
+__device__ __forceinline__ void dinv_step(float (&x)[16], const float *ad) {
+    constexpr int Q0 = (R + 1) / 4;  // first quad of rows holding an r2 > R
+    f32x4 col[4];
+#pragma unroll
+    for (int q = Q0; q < 4; ++q)
+        col[q] = ld4f(ad + R * kAD + 4 * q);
 #pragma unroll
     for (int r2 = R + 1; r2 < 16; ++r2)
-        fmac_rowbcast<R>(x[r2], na[r2 / 4][r2 % 4], x[R]);
+        x[r2] = __builtin_fmaf(col[r2 / 4][r2 % 4], x[R], x[r2]);
 }
 
 template <int... R>
-__device__ __forceinline__ void dinv_steps(float (&x)[16], const f32x4 (&na)[4],
+__device__ __forceinline__ void dinv_steps(float (&x)[16], const float *ad,
                                            std::integer_sequence<int, R...>) {
-    (dinv_step<R>(x, na), ...);
+    (dinv_step<R>(x, ad), ...);
 }
 
-// (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32, the four blocks
-// in one wave: lane row g works on block g (from its copy of -A_gg in Ad[g]),
-// and lane c of the row computes column c: once x_r is final, A[r2][r] x_r is
-// subtracted from every row r2 > r, with A[r2][r] taken from lane r by a row
-// broadcast.  Column c is stored, as hi and lo bf16, as row 16 g + c of D^T.
 __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int lane) {
     const int c = lane & 15, g = lane >> 4;
     const float *ad = S.Ad[g];
-    f32x4 na[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        na[q] = ld4f(ad + c * kAD + 4 * q);
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         x[r] = (r == c) ? 1.0f : 0.0f;
-    dinv_steps(x, na, std::make_integer_sequence<int, 15>{});
+    dinv_steps(x, ad, std::make_integer_sequence<int, 15>{});
     u32x4 hi[2], lo[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

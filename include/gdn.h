@@ -125,11 +125,11 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   cu_seqlens   device int32 [N + 1] document offsets, or NULL (then the
  *                documents are the B rows and N = B).
  *   cu_seqlens_host  optional host copy of cu_seqlens.  When given it is
- *                validated (cu[0] = 0, non-decreasing, cu[N] = T) and the
- *                chunk schedule is built from it on the host; when NULL the
- *                device array is trusted and the schedule is built on the
- *                device.  Empty documents are allowed: their final state is
- *                their initial state.
+ *                validated (cu[0] = 0, non-decreasing, cu[N] = T) before
+ *                anything is enqueued; when NULL the device array is trusted.
+ *                The kernels read the device array either way.  Empty
+ *                documents are allowed: their final state is their initial
+ *                state.
  *   n_seqs       N when cu_seqlens is given (>= 1); ignored otherwise.
  *   o            [B, T, H_v, dv] output, dtype `dtype`.
  *   ht           [N, H_v, dk, dv] fp32 final states, or NULL to skip them.

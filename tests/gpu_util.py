@@ -53,17 +53,46 @@ def run_oracle(d, scale=1.0):
                           cu_seqlens=d["cu_seqlens"])
 
 
+def per_unit_max(o, ro, ht, rht, cu):
+    """The largest relative L2 error over (sequence, value head) units: the
+    output rows of each document (or batch row) and head, and each final
+    state.  Returns (output max, its unit, state max, its unit)."""
+    B, T, Hv = o.shape[:3]
+    spans = ([(0, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)] if cu is not None
+             else [(b, 0, T) for b in range(B)])
+    wo, uo = 0.0, None
+    for n, (b, t0, t1) in enumerate(spans):
+        if t1 <= t0:
+            continue
+        for j in range(Hv):
+            e = rel_l2(o[b, t0:t1, j], ro[b, t0:t1, j])
+            if e > wo:
+                wo, uo = e, (n, j)
+    wh, uh = 0.0, None
+    for n in range(ht.shape[0]):
+        for j in range(Hv):
+            e = rel_l2(ht[n, j], rht[n, j])
+            if e > wh:
+                wh, uh = e, (n, j)
+    return wo, uo, wh, uh
+
+
 def check(d, scale=1.0, label=""):
-    """Run both sides, assert the tolerances, return the two errors."""
+    """Run both sides, assert the tolerances on the whole tensors and on every
+    (sequence, value head) unit, return the two whole-tensor errors."""
     print(f"[gpu case] {label} B={d['B']} T={d['T']} Hqk={d['Hqk']} Hv={d['Hv']} "
           f"dk={d['dk']} dv={d['dv']} dtype={d['dtype']} N={d['N']}", flush=True)
     o, ht = run_gpu(d, scale)
     ro, rht = run_oracle(d, scale)
     eo, eh = rel_l2(o, ro), rel_l2(ht, rht)
     tol_o, tol_h = TOL[d["dtype"]]
-    print(f"  rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} (tol {tol_h:.0e})",
+    wo, uo, wh, uh = per_unit_max(o, ro, ht, rht, d["cu_seqlens"])
+    print(f"  rel-L2 output {eo:.3e} (tol {tol_o:.0e}), state {eh:.3e} (tol {tol_h:.0e}); "
+          f"worst (sequence, head): output {wo:.3e} at {uo}, state {wh:.3e} at {uh}",
           flush=True)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(ht))
     assert eo <= tol_o, f"output rel-L2 {eo:.3e} > {tol_o}"
     assert eh <= tol_h, f"state rel-L2 {eh:.3e} > {tol_h}"
+    assert wo <= tol_o, f"output rel-L2 {wo:.3e} > {tol_o} for (sequence, head) {uo}"
+    assert wh <= tol_h, f"state rel-L2 {wh:.3e} > {tol_h} for (sequence, head) {uh}"
     return eo, eh
