@@ -10,7 +10,8 @@ raises.
 import ctypes
 import os
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_workspace_size",
+           "gdn_chunk_bwd",
            "gdn_chunk_bwd_workspace_size", "gdn_prepare_inputs", "gdn_recurrent_step",
            "GDN_QK_L2NORM", "GDN_GATE_ACT", "gdn_status_string",
            "gdn_last_hip_error", "gdn_version", "GdnError", "library_path", "load"]
@@ -22,7 +23,9 @@ _lib = None
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM, GDN_GATE_ACT = 1, 2
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
-          3: "GDN_ERR_MISALIGNED", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP"}
+          3: "GDN_ERR_MISALIGNED", 4: "GDN_ERR_WORKSPACE", 5: "GDN_ERR_HIP",
+          6: "GDN_ERR_SCRATCH_LIMIT"}
+GDN_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnError(RuntimeError):
@@ -51,6 +54,9 @@ def load():
     lib.gdn_chunk_fwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
                                   ctypes.c_float, U32, P, P, P, I32, P, P, P, ctypes.c_size_t,
                                   P]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P,
+                                          P, ctypes.c_float, U32, P, P, P, I32, P, P, P]
     lib.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
     lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
@@ -228,6 +234,37 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
                            None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
                            N if cu_seqlens is not None else 0, ptr(out), ptr(final_state),
                            ptr(workspace), ws_len, stream)
+    if st != 0:
+        _raise(st)
+    return out, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,
+                          cu_seqlens_host=None, out=None, final_state=None, stream=None,
+                          use_qk_l2norm=False, gate_activation=False):
+    """gdn_chunk_fwd through the entry point that allocates nothing: the
+    piece scan uses the library's static per-device scratch.  `out` and
+    `final_state` (required: this call allocates nothing either) are the
+    preallocated outputs; final_state may be None to skip it."""
+    import torch
+    lib = load()
+    dt, B, T, Hqk, Hv, dk, dv, N, host_arr = _check_inputs(torch, q, k, v, g, beta,
+                                                            initial_state, cu_seqlens,
+                                                            cu_seqlens_host)
+    _check_buffer(torch, "out", out, (B, T, Hv, dv), q.dtype, q.device)
+    if final_state is not None:
+        _check_buffer(torch, "final_state", final_state, (N, Hv, dk, dv), torch.float32,
+                      q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.gdn_chunk_fwd_noalloc(dt, B, T, Hqk, Hv, dk, dv, ptr(q), ptr(k), ptr(v), ptr(g),
+                                   ptr(beta), float(scale), _flags(use_qk_l2norm, gate_activation),
+                                   ptr(initial_state), ptr(cu_seqlens),
+                                   None if host_arr is None else ctypes.cast(host_arr,
+                                                                             ctypes.c_void_p),
+                                   N if cu_seqlens is not None else 0, ptr(out),
+                                   ptr(final_state), stream)
     if st != 0:
         _raise(st)
     return out, final_state

@@ -9,13 +9,48 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_internal.h"
+
+// Scratch of gdn_chunk_fwd_noalloc: the piece scan's end and start states,
+// for callers that cannot allocate.  A device global, so every GPU the
+// library runs on holds its own copy (at its own address) until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels get the address hipGetSymbolAddress returns for the
+// current device (static_scratch below).
+static constexpr size_t kStaticScratchBytes = GDN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+// The device address of `scratch` on each device, looked up once per device
+// (with that device current) on its first gdn_chunk_fwd_noalloc call.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void *&ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool aligned16(const void *p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -211,6 +246,33 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     }
     return fwd_launch(dtype, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, flags, h0,
                       cu_seqlens, N, o, ht, plan, workspace, stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
+                                 int32_t H_v, int32_t dk, int32_t dv, const void *q,
+                                 const void *k, const void *v, const float *g,
+                                 const float *beta, float scale, uint32_t flags,
+                                 const float *h0, const int32_t *cu_seqlens,
+                                 const int32_t *cu_seqlens_host, int32_t n_seqs, void *o,
+                                 float *ht, hipStream_t stream) {
+    int32_t N = 0;
+    const gdn_status st = fwd_validate(dtype, B, T, H_qk, H_v, dk, dv, q, k, v, g, beta, flags,
+                                       h0, cu_seqlens, cu_seqlens_host, n_seqs, o, ht, N);
+    if (st != GDN_OK)
+        return st;
+    // The same plan gdn_chunk_fwd makes with a workspace; its piece arrays go
+    // to this device's static scratch, which bounds what it may need.
+    const PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
+    if (gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv) > kStaticScratchBytes)
+        return GDN_ERR_SCRATCH_LIMIT;
+    void *scratch_ptr = nullptr;
+    const hipError_t e = static_scratch(scratch_ptr);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return GDN_ERR_HIP;
+    }
+    return fwd_launch(dtype, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, flags, h0,
+                      cu_seqlens, N, o, ht, plan, scratch_ptr, stream);
 }
 
 // The backward's shapes: bf16, dk in {64, 128}, dv in {64, 128, 256}.
@@ -430,6 +492,9 @@ const char *gdn_status_string(gdn_status status) {
     case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED: pointer not 16-byte aligned";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch failed";
+    case GDN_ERR_SCRATCH_LIMIT:
+        return "GDN_ERR_SCRATCH_LIMIT: the call needs more scratch than the library's static "
+               "maximum (GDN_STATIC_SCRATCH_BYTES)";
     }
     return "unknown gdn_status";
 }

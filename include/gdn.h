@@ -56,8 +56,13 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 2, /* a shape or dtype this build has no kernel for */
     GDN_ERR_MISALIGNED = 3,  /* a pointer not aligned to 16 bytes */
     GDN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query said */
-    GDN_ERR_HIP = 5          /* a HIP launch failed; see gdn_last_hip_error() */
+    GDN_ERR_HIP = 5,         /* a HIP launch failed; see gdn_last_hip_error() */
+    GDN_ERR_SCRATCH_LIMIT = 6 /* gdn_chunk_fwd_noalloc: more scratch needed than
+                                 GDN_STATIC_SCRATCH_BYTES */
 } gdn_status;
+
+/* Bytes of the static device scratch behind gdn_chunk_fwd_noalloc (per GPU). */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Option bits of gdn_chunk_fwd, gdn_prepare_inputs and gdn_recurrent_step. */
 #define GDN_QK_L2NORM 1u /* divide every q and k row (dk elements) by its L2 norm */
@@ -150,6 +155,31 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
                          const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
                          int32_t n_seqs, void *o, float *ht, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same result as
+ * gdn_chunk_fwd with a workspace of gdn_chunk_fwd_workspace_size() bytes.
+ * The piece scan's arrays go to a static device scratch of
+ * GDN_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends; its address is looked up once per device,
+ * on the first call with that device current.  Nothing is allocated and no
+ * allocating routine is called.  Returns GDN_ERR_SCRATCH_LIMIT, before
+ * anything is enqueued, when the call's piece plan needs more scratch than
+ * that (gdn_chunk_fwd with a workspace, or with NULL for whole rows, runs
+ * such calls).  Every call on a GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (on different streams, or from different threads) race
+ * and must be ordered by the caller.  Nothing in the scratch needs to start
+ * at zero (each call writes every element it reads).
+ */
+gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
+                                 int32_t H_v, int32_t dk, int32_t dv, const void *q,
+                                 const void *k, const void *v, const float *g,
+                                 const float *beta, float scale, uint32_t flags,
+                                 const float *h0, const int32_t *cu_seqlens,
+                                 const int32_t *cu_seqlens_host, int32_t n_seqs, void *o,
+                                 float *ht, hipStream_t stream);
 
 /*
  * Bytes of device workspace gdn_chunk_bwd needs for these sizes (0 for sizes

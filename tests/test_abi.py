@@ -125,6 +125,49 @@ def test_rejects_before_launch(kw, status):
     assert call(**kw) == status
 
 
+def call_noalloc(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+                 beta=FAKE, h0=None, cu=None, cu_host=None, n_seqs=0, o=FAKE, ht=None, flags=0):
+    lib = gdn.load()
+    host = None
+    if cu_host is not None:
+        host = ctypes.cast((ctypes.c_int32 * len(cu_host))(*cu_host), ctypes.c_void_p)
+    return lib.gdn_chunk_fwd_noalloc(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, flags,
+                                     h0, cu, host, n_seqs, o, ht, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(T=0), INVALID),
+    (dict(dtype=7), UNSUPPORTED), (dict(dk=32), UNSUPPORTED), (dict(flags=4), INVALID),
+    (dict(q=FAKE + 8), MISALIGNED), (dict(ht=FAKE + 12), MISALIGNED),
+    (dict(cu=FAKE, n_seqs=2, cu_host=[0, 30, 20]), INVALID),
+    (dict(B=1 << 40, T=1 << 40), INVALID),
+])
+def test_noalloc_rejects_before_launch(kw, status):
+    """The entry point without a workspace validates exactly as
+    gdn_chunk_fwd does, before any HIP call."""
+    assert call_noalloc(**kw) == status
+
+
+SCRATCH_LIMIT = 6
+
+
+def test_noalloc_scratch_limit():
+    """A call whose piece plan needs more than the static scratch is refused
+    with its own status before anything is enqueued; the planned need is what
+    gdn_chunk_fwd_workspace_size reports."""
+    limit = gdn.GDN_STATIC_SCRATCH_BYTES
+    assert limit == 64 << 20
+    # Three rows of 2^22 tokens at 3 heads, dk = dv = 256: many pieces of a
+    # large state each (216 MiB).
+    need = gdn.gdn_chunk_fwd_workspace_size(1, 3, 1 << 22, 3, 3, 256, 256, 3)
+    assert need > limit
+    assert call_noalloc(B=3, T=1 << 22, Hqk=3, Hv=3, dk=256, dv=256) == SCRATCH_LIMIT
+    # The long rows the library is measured on fit.
+    assert 0 < gdn.gdn_chunk_fwd_workspace_size(1, 1, 1_064_960, 16, 16, 128, 128, 1) <= limit
+    assert 0 < gdn.gdn_chunk_fwd_workspace_size(1, 1, 65536, 8, 8, 256, 256, 1) <= limit
+    assert "GDN_STATIC_SCRATCH_BYTES" in gdn.gdn_status_string(SCRATCH_LIMIT)
+
+
 def test_binding_refuses_to_run_without_library(monkeypatch):
     monkeypatch.setattr(gdn, "_lib", None)
     monkeypatch.setattr(gdn, "_LIB_PATH", os.path.join(ROOT, "no_such_libgdn.so"))
