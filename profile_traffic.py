@@ -13,6 +13,12 @@
         calibration copy, and writes profiles/traffic_W.json (read by
         bench.py) and a text summary beside it.
 
+    python3 profile_traffic.py counters PMC_DIR --command CMD [--workload W]
+        Writes profiles/counters_W.md (and .json) from a `rocprofv3 --pmc`
+        run of `launch` with the SQ counters listed in COUNTERS: MFMA busy
+        cycles, LDS bank conflicts against LDS instruction cycles, waves and
+        the GPU's busy clocks, averaged over the kernel's dispatches.
+
     python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME] [--by-grid]
         Writes profiles/kernel_stats_NAME.md (default headline_bf16) from a
         `rocprofv3 --kernel-trace --stats` run of bench.py; with --by-grid,
@@ -134,6 +140,52 @@ def traffic(fetch_dir, write_dir, command, workload):
     print("\n".join(lines))
 
 
+COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE",
+            "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+
+
+def counters(dirname, command, workload):
+    """Writes profiles/counters_W.md from one `rocprofv3 --pmc` run of
+    `launch`: each counter averaged over the kernel's dispatches, with the
+    ratios the design notes quote.  SQ_VALU_MFMA_BUSY_CYCLES and the LDS
+    counters are summed over the chip; GRBM_GUI_ACTIVE is the GPU's busy
+    clock count over the dispatch."""
+    kernel = KERNELS[workload]
+    vals = {}
+    for c in COUNTERS:
+        per = read_counter(dirname, c)
+        kname, kv = pick(per, kernel)
+        vals[c] = sum(kv) / len(kv)
+    # GRBM_GUI_ACTIVE reads the sum over the 8 XCDs (each has its own
+    # GRBM): one XCD's busy clocks are an eighth of it.  MFMA busy cycles
+    # are summed over the 1024 SIMDs.
+    xcds, simds = 8, 1024
+    clocks = vals["GRBM_GUI_ACTIVE"] / xcds
+    mfma_util = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * simds)
+    conflict = vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1.0)
+    out = {"kernel": kernel, "workload": workload, "command": command,
+           "kernel_source_sha256": bench.kernel_source_hash(), "per_dispatch": vals,
+           "busy_clocks_per_xcd": clocks,
+           "mfma_busy_per_simd": mfma_util,
+           "lds_bank_conflict_over_idx_active": conflict}
+    with open(os.path.join(PROFILES, f"counters_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# SQ counters of {kernel}, {workload}", "", "Command:", "", "```", command, "```",
+             "", "| counter | per dispatch (average) |", "|---|---|"]
+    for c in COUNTERS:
+        lines.append(f"| {c} | {vals[c]:.4g} |")
+    lines += ["",
+              f"- GRBM_GUI_ACTIVE sums the 8 XCDs' busy clocks: {clocks:.4g} clocks per XCD "
+              f"per dispatch ({clocks / 2.4e3:.1f} us at 2.4 GHz).",
+              f"- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 "
+              f"SIMDs) = {mfma_util:.3f}.",
+              f"- SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = {conflict:.3f}.",
+              f"- Kernel source sha256 {out['kernel_source_sha256']}."]
+    with open(os.path.join(PROFILES, f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def trace_rows(dirname):
     """Rows like the stats CSV's, one per (kernel, grid size), from the trace."""
     files = glob.glob(os.path.join(dirname, "**", "*kernel_trace.csv"), recursive=True)
@@ -202,6 +254,10 @@ def main():
     t.add_argument("write_dir")
     t.add_argument("--command", required=True)
     t.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
+    c = sub.add_parser("counters")
+    c.add_argument("pmc_dir")
+    c.add_argument("--command", required=True)
+    c.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
     s = sub.add_parser("stats")
     s.add_argument("stats_dir")
     s.add_argument("--command", required=True)
@@ -216,6 +272,8 @@ def main():
         launch(args.launches, args.workload)
     elif args.cmd == "traffic":
         traffic(args.fetch_dir, args.write_dir, args.command, args.workload)
+    elif args.cmd == "counters":
+        counters(args.pmc_dir, args.command, args.workload)
     else:
         stats(args.stats_dir, args.command, args.name, args.title, args.only, args.by_grid)
 
