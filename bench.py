@@ -328,14 +328,16 @@ def measure_long(gdn, gi, torch, dev, steps=3, name="long_bf16"):
     return out
 
 
-def measure_packed(gdn, gi, torch, dev, steps, warmup):
-    """The packed workload (16,384 tokens in geometric documents of mean
-    length 1024, H_qk=16, H_v=32, d=128, bf16, an initial state per
-    document): milliseconds per forward back to back and flushed, tokens/s,
-    the HBM roofline fraction (initial and final states counted), and the
-    oracle on two sampled (document, head) pairs."""
+def measure_packed(gdn, gi, torch, dev, steps, warmup, name="packed_gva_bf16"):
+    """A packed workload (packed_gva_bf16: 16,384 tokens in geometric
+    documents of mean length 1024, H_qk=16, H_v=32, d=128, bf16, an initial
+    state per document; packed_8h_bf16: the same at 8 heads): milliseconds
+    per forward as planned from the host copy of cu_seqlens (documents
+    longest first, long ones split into pieces where the plan says so) and
+    as whole documents in index order (no workspace), back to back and
+    flushed; tokens/s; the HBM roofline fraction (initial and final states
+    counted); the oracle on two sampled (document, head) pairs."""
     import oracle
-    name = "packed_gva_bf16"
     d = gi.make_config(name)
     Hqk, Hv, dk, dv, T, N = d["Hqk"], d["Hv"], d["dk"], d["dv"], d["T"], d["N"]
     up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -348,15 +350,36 @@ def measure_packed(gdn, gi, torch, dev, steps, warmup):
     o = torch.empty_like(v)
     ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu_dev,
-                                     cu_seqlens_host=cu_host, out=o, final_state=ht,
-                                     stream=stream.cuda_stream)
-    ms = _time_calls(torch, stream, call, steps, warmup)
-    flushed = per_launch(torch, stream, call, 50, flush=flush_buffer(torch, dev))
+    plan = gdn.gdn_chunk_fwd_plan(1, 1, T, Hqk, Hv, dk, dv, cu_host)
     nbytes = (2 * T * Hqk * dk * 2 + 2 * T * Hv * dv * 2 + 2 * T * Hv * 4 +
               2 * N * Hv * dk * dv * 4)
-    achieved = nbytes / (ms * 1e-3) / 1e9
-    # Two (document, head) pairs drawn with the workload seed.
+    cfg = gi.CONFIGS[name]
+    docs = (f"lengths {cfg['lengths']}" if "lengths" in cfg else
+            f"geometric, mean {cfg['mean_len']}")
+    res = {"workload": f"{name}: {T} tokens in {N} documents ({docs}), "
+                       f"H_qk={Hqk} H_v={Hv} dk={dk} dv={dv}, h0 ~ N(0, 0.02)",
+           "plan": {"piece_len": plan[0], "slots": plan[1], "longest_first": plan[2]},
+           "algorithmic_bytes_per_call": nbytes}
+    for mode, kw in (("planned", {}), ("whole_documents_index_order", dict(pieces=False))):
+        call = lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu_dev,
+                                         cu_seqlens_host=cu_host, out=o, final_state=ht,
+                                         stream=stream.cuda_stream, **kw)
+        ms = _time_calls(torch, stream, call, steps, warmup)
+        flushed = per_launch(torch, stream, call, 50, flush=flush_buffer(torch, dev))
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        res[mode] = {"ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+                     "launch_ms_flushed": flushed,
+                     "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                                  "frac_flushed_median": nbytes / (flushed["median"] * 1e-3) /
+                                                         1e9 / HBM_PEAK_GBPS}}
+        log(f"[bench] {name} ({N} documents, {mode}): {ms * 1e3:.1f} us/call back to back, "
+            f"{flushed['median'] * 1e3:.1f} us flushed (median)")
+    # The planned call's output against the oracle on two (document, head)
+    # pairs drawn with the workload seed.
+    gdn.gdn_chunk_fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu_dev,
+                      cu_seqlens_host=cu_host, out=o, final_state=ht, stream=stream.cuda_stream)
+    torch.cuda.synchronize()
     seed = gi.CONFIGS[name]["seed"]
     rng = np.random.default_rng(seed)
     lens = np.diff(cu)
@@ -375,19 +398,14 @@ def measure_packed(gdn, gi, torch, dev, steps, warmup):
         errs.append({"document": n, "tokens": t1 - t0, "head": j,
                      "rel_l2_output": float(np.linalg.norm(go - ro) / np.linalg.norm(ro)),
                      "rel_l2_state": float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))})
-    log(f"[bench] packed ({N} documents): {ms * 1e3:.1f} us/call back to back, "
-        f"{flushed['median'] * 1e3:.1f} us flushed (median); checks {errs}")
-    return {"workload": f"{name}: {T} tokens in {N} documents (geometric, mean 1024), "
-                        f"H_qk={Hqk} H_v={Hv} dk={dk} dv={dv}, h0 ~ N(0, 0.02)",
-            "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3), "steps": steps,
-            "launch_ms_flushed": flushed,
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                         "frac_flushed_median": nbytes / (flushed["median"] * 1e-3) / 1e9 /
-                                                HBM_PEAK_GBPS,
-                         "algorithmic_bytes_per_call": nbytes,
-                         "kernel": "gdn_fwd_bf16<false, 0, 128>"},
-            "check": errs}
+    log(f"[bench] {name} checks {errs}")
+    res["check"] = errs
+    # The headline keys: the planned call.
+    res["ms_per_call"] = res["planned"]["ms_per_call"]
+    res["tokens_per_s"] = res["planned"]["tokens_per_s"]
+    res["roofline"] = dict(res["planned"]["roofline"], algorithmic_bytes_per_call=nbytes,
+                           kernel="gdn_fwd_bf16<false, 0, 128> (or <false, 1|2, 128> with pieces)")
+    return res
 
 
 def measure_tiny(gdn, gi, torch, dev):
@@ -651,10 +669,14 @@ def main():
         log("[bench] head dimension 256")
         k256 = measure_k256(gdn, gi, torch, dev, steps=200, warmup=100)
 
-    packed = tiny = None
+    packed = packed_8h = packed_long_doc = tiny = None
     if not args.no_packed:
         log("[bench] packed documents and the tiny fp32 workload")
         packed = measure_packed(gdn, gi, torch, dev, steps=200, warmup=50)
+        packed_8h = measure_packed(gdn, gi, torch, dev, steps=200, warmup=50,
+                                   name="packed_8h_bf16")
+        packed_long_doc = measure_packed(gdn, gi, torch, dev, steps=100, warmup=20,
+                                         name="packed_long_doc_bf16")
         tiny = measure_tiny(gdn, gi, torch, dev)
 
     long_row = long_k256 = None
@@ -715,6 +737,8 @@ def main():
         "decode": decode,
         "k256": k256,
         "packed": packed,
+        "packed_8h": packed_8h,
+        "packed_long_doc": packed_long_doc,
         "tiny": tiny,
         "long_row": long_row,
         "long_k256": long_k256,

@@ -10,7 +10,8 @@ raises.
 import ctypes
 import os
 
-__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_workspace_size",
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_plan",
+           "gdn_chunk_fwd_workspace_size",
            "gdn_chunk_bwd",
            "gdn_chunk_bwd_workspace_size", "gdn_prepare_inputs", "gdn_recurrent_step",
            "GDN_QK_L2NORM", "GDN_GATE_ACT", "gdn_status_string",
@@ -54,6 +55,8 @@ def load():
     lib.gdn_chunk_fwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
                                   ctypes.c_float, U32, P, P, P, I32, P, P, P, ctypes.c_size_t,
                                   P]
+    lib.gdn_chunk_fwd_plan.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_plan.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, I32, P, P, P]
     lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_fwd_noalloc.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P,
                                           P, ctypes.c_float, U32, P, P, P, I32, P, P, P]
@@ -237,6 +240,25 @@ def gdn_chunk_fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=No
     if st != 0:
         _raise(st)
     return out, final_state
+
+
+def gdn_chunk_fwd_plan(dtype, B, T, H_qk, H_v, dk, dv, cu_seqlens_host=None):
+    """(piece_len, slots, ordered) of the plan gdn_chunk_fwd makes with a
+    workspace: piece_len 0 runs whole rows or documents; ordered is True when
+    packed documents are scheduled longest first.  cu_seqlens_host: a list
+    of document offsets for a packed call (B = 1)."""
+    lib = load()
+    host, n = None, 0
+    if cu_seqlens_host is not None:
+        n = len(cu_seqlens_host) - 1
+        host = (ctypes.c_int32 * (n + 1))(*[int(x) for x in cu_seqlens_host])
+    pl, sl, od = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    st = lib.gdn_chunk_fwd_plan(int(dtype), B, T, H_qk, H_v, dk, dv,
+                                None if host is None else ctypes.cast(host, ctypes.c_void_p), n,
+                                ctypes.byref(pl), ctypes.byref(sl), ctypes.byref(od))
+    if st != 0:
+        _raise(st)
+    return pl.value, sl.value, bool(od.value)
 
 
 def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None,

@@ -113,6 +113,72 @@ PiecePlan plan_pieces(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_
     return best;
 }
 
+// Pieces of packed documents, planned from the host copy of cu_seqlens.
+// Whole documents are scheduled longest first (doc_order), so their cost is
+// about max(longest document, total chunk steps over the CUs); with pieces of
+// piece_len tokens the two passes run every piece but each document's last
+// (with the transition tiles), then all pieces, each pass in rounds of one
+// workgroup per CU times the piece length (pieces are near-equal, so they do
+// not spread below whole rounds: 16 documents x 8 heads measured 162 us in
+// pieces against 123 us whole when the second pass was costed as spread
+// work), plus the scan's serial steps over the most pieces a document has,
+// in the same units as plan_pieces.
+// Pieces may use at most `max_slots` slots, the capacity the size-only
+// workspace query promises (the single-row plan of T tokens).
+struct PackedPlan {
+    int64_t piece_len = 0;   // 0: whole documents
+    int64_t slots = 0;       // sum over documents of (pieces - 1)
+    int64_t items_ends = 0;  // pieces of the first pass
+    int64_t items_all = 0;   // all pieces
+};
+
+PackedPlan plan_packed(gdn_dtype dtype, int32_t H_v, int32_t dk, int32_t dv, const int32_t *cu,
+                       int32_t N, int64_t max_slots) {
+    PackedPlan best;
+    if (dtype != GDN_BF16 || dv % 64 != 0 || max_slots <= 0)
+        return best;
+    const int64_t tiles = dv / 64, ends_tiles = dv / 64 + dk / 64;
+    int64_t total = 0, maxc = 0;
+    for (int32_t n = 0; n < N; ++n) {
+        const int64_t c = ((int64_t)cu[n + 1] - cu[n] + 63) / 64;
+        total += c;
+        maxc = c > maxc ? c : maxc;
+    }
+    const auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+    const double spread = (double)((total * H_v * tiles + kCUs - 1) / kCUs);
+    const double whole = (double)maxc > spread ? (double)maxc : spread;
+    double best_cost = 0.95 * whole;
+    for (int64_t pc = kMinPieceChunks; pc < maxc; pc = pc + 1 + pc / 8) {
+        int64_t slots = 0, np_max = 1;
+        for (int32_t n = 0; n < N; ++n) {
+            const int64_t c = ((int64_t)cu[n + 1] - cu[n] + 63) / 64;
+            const int64_t np = c > pc ? (c + pc - 1) / pc : 1;
+            slots += np - 1;
+            np_max = np > np_max ? np : np_max;
+        }
+        if (slots == 0 || slots > max_slots)
+            continue;
+        const double cost = (rounds(slots * H_v * ends_tiles) +
+                             rounds((slots + N) * H_v * tiles)) * (double)pc +
+                            scan_step_cost(dk) * (double)(np_max - 1) + kPieceFixed;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best.piece_len = pc * 64;
+            best.slots = slots;
+        }
+    }
+    if (best.piece_len > 0) {
+        best.items_ends = best.slots;
+        best.items_all = best.slots + N;
+    }
+    return best;
+}
+
+// Bytes of the document order array of a packed call (0 when not used).
+size_t order_bytes(int32_t N) {
+    return N > 1 && N <= gdn::kMaxOrderedDocs ? ((size_t)N * 4 + 255) / 256 * 256 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,10 +189,12 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
     if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || H_v % H_qk != 0 || B > INT32_MAX ||
         !supported(dtype, dk, dv))
         return 0;
-    // Only the piece scan of long rows stages anything in HBM: the end states
-    // and start states of its pieces.
+    // The piece scan stages the end states and start states of its pieces;
+    // a packed call (B = 1) may also rank its documents.  A packed call's
+    // pieces use at most the slots of the single-row plan of T tokens.
     const PiecePlan p = plan_pieces(dtype, B, T, H_v, dk, dv, false);
-    return gdn::fwd_piece_bytes((int32_t)B, p.pieces, H_v, dk, dv);
+    return gdn::fwd_piece_bytes(B * (p.pieces - 1), H_v, dk, dv) +
+           (B == 1 && dtype == GDN_BF16 ? order_bytes(n_seqs) : 0);
 }
 
 // Checks a forward call before anything touches the GPU; on success N is
@@ -175,13 +243,61 @@ static gdn_status fwd_validate(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_
     return GDN_OK;
 }
 
-// Launches a validated forward call with `plan`, whose piece arrays (if any)
-// live at `scratch`.
+// The plan of one forward call: the piece scan (pieces > 1) over batch rows
+// or packed documents, and the schedule of packed documents.
+struct FwdPlan {
+    int32_t pieces = 1;         // batch rows: pieces per row; packed: 2 when split
+    int64_t piece_len = 0;
+    int64_t slots = 0;
+    int64_t items_ends = 0, items_all = 0;
+    bool order = false;         // packed: rank the documents, longest first
+};
+
+// Bytes of the workspace a plan uses: the order array, then the piece arrays.
+static size_t plan_bytes(const FwdPlan &p, int32_t N, int32_t H_v, int32_t dk, int32_t dv) {
+    return (p.order ? order_bytes(N) : 0) + gdn::fwd_piece_bytes(p.slots, H_v, dk, dv);
+}
+
+// The plan of a validated call given `ws_bytes` of workspace (0: none).
+static FwdPlan plan_call(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_v, int32_t dk,
+                         int32_t dv, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                         int32_t N, bool have_ws) {
+    FwdPlan f;
+    if (!have_ws)
+        return f;
+    if (!cu_seqlens) {
+        const PiecePlan p = plan_pieces(dtype, B, T, H_v, dk, dv, false);
+        f.pieces = p.pieces;
+        f.piece_len = p.piece_len;
+        f.slots = (int64_t)N * (p.pieces - 1);
+        return f;
+    }
+    // Ranking the documents pays only when their workgroups do not all fit
+    // on the CUs at once (then the longest start first); otherwise its launch
+    // is pure cost (about 3 us measured on 16 documents x 8 heads).
+    f.order = dtype == GDN_BF16 && order_bytes(N) > 0 && (int64_t)N * H_v * (dv / 64) > kCUs;
+    if (cu_seqlens_host) {
+        const PiecePlan single = plan_pieces(dtype, 1, T, H_v, dk, dv, false);
+        const PackedPlan pp = plan_packed(dtype, H_v, dk, dv, cu_seqlens_host, N,
+                                          single.pieces - 1);
+        if (pp.piece_len > 0) {
+            f.pieces = 2;
+            f.piece_len = pp.piece_len;
+            f.slots = pp.slots;
+            f.items_ends = pp.items_ends;
+            f.items_all = pp.items_all;
+        }
+    }
+    return f;
+}
+
+// Launches a validated forward call with `plan`, whose arrays (if any) live
+// at `scratch`.
 static gdn_status fwd_launch(gdn_dtype dtype, int64_t T, int32_t H_qk, int32_t H_v, int32_t dk,
                              int32_t dv, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float scale, uint32_t flags,
                              const float *h0, const int32_t *cu_seqlens, int32_t N, void *o,
-                             float *ht, const PiecePlan &plan, void *scratch,
+                             float *ht, const FwdPlan &plan, void *scratch,
                              hipStream_t stream) {
     gdn::FwdArgs a;
     a.q = q;
@@ -203,21 +319,55 @@ static gdn_status fwd_launch(gdn_dtype dtype, int64_t T, int32_t H_qk, int32_t H
     a.flags = flags;
     a.pieces = plan.pieces;
     a.piece_len = plan.piece_len;
+    a.n_slots = plan.slots;
+    a.items_ends = plan.items_ends;
+    a.items_all = plan.items_all;
     a.piece_ends = nullptr;
     a.piece_starts = nullptr;
+    a.order = nullptr;
     a.chunk_states = nullptr;
-    if (plan.pieces > 1) {
-        const size_t per = (size_t)N * (plan.pieces - 1) * H_v * dk;
-        a.piece_ends = static_cast<float *>(scratch);
-        a.piece_starts = reinterpret_cast<float *>(static_cast<char *>(scratch) +
-                                                   (per * (dv + dk) * 4 + 255) / 256 * 256);
+    char *ws = static_cast<char *>(scratch);
+    if (plan.order) {
+        a.order = reinterpret_cast<const int32_t *>(ws);
+        ws += order_bytes(N);
     }
-    const hipError_t e = dtype == GDN_BF16 ? gdn::launch_fwd_bf16(a, stream)
-                                           : gdn::launch_fwd_f32(a, stream);
+    if (plan.pieces > 1) {
+        a.piece_ends = reinterpret_cast<float *>(ws);
+        a.piece_starts =
+            reinterpret_cast<float *>(ws + gdn::fwd_piece_starts_offset(plan.slots, H_v, dk, dv));
+    }
+    hipError_t e = hipSuccess;
+    if (plan.order)
+        e = gdn::launch_doc_order(cu_seqlens, N, reinterpret_cast<int32_t *>(scratch), stream);
+    if (e == hipSuccess)
+        e = dtype == GDN_BF16 ? gdn::launch_fwd_bf16(a, stream) : gdn::launch_fwd_f32(a, stream);
     if (e != hipSuccess) {
         g_last_hip_error = e;
         return GDN_ERR_HIP;
     }
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_plan(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                              int32_t dk, int32_t dv, const int32_t *cu_seqlens_host,
+                              int32_t n_seqs, int64_t *piece_len, int64_t *slots,
+                              int32_t *ordered) {
+    if (!piece_len || !slots || !ordered)
+        return GDN_ERR_INVALID_ARG;
+    // Validated as a call; fake aligned addresses stand in for the tensors.
+    const void *fake = reinterpret_cast<const void *>(uintptr_t{0x10000});
+    const float *ff = static_cast<const float *>(fake);
+    const int32_t *cu = cu_seqlens_host ? static_cast<const int32_t *>(fake) : nullptr;
+    int32_t N = 0;
+    const gdn_status st = fwd_validate(dtype, B, T, H_qk, H_v, dk, dv, fake, fake, fake, ff, ff,
+                                       0u, nullptr, cu, cu_seqlens_host, n_seqs, fake, nullptr,
+                                       N);
+    if (st != GDN_OK)
+        return st;
+    const FwdPlan plan = plan_call(dtype, B, T, H_v, dk, dv, cu, cu_seqlens_host, N, true);
+    *piece_len = plan.pieces > 1 ? plan.piece_len : 0;
+    *slots = plan.slots;
+    *ordered = plan.order ? 1 : 0;
     return GDN_OK;
 }
 
@@ -233,11 +383,11 @@ gdn_status gdn_chunk_fwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
                                        h0, cu_seqlens, cu_seqlens_host, n_seqs, o, ht, N);
     if (st != GDN_OK)
         return st;
-    // The piece scan runs when a workspace is given; without one, whole rows.
-    PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
-    if (!workspace)
-        plan = PiecePlan{1, T};
-    const size_t need = gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv);
+    // The piece scan and the document order run when a workspace is given;
+    // without one, whole rows (documents in index order).
+    const FwdPlan plan = plan_call(dtype, B, T, H_v, dk, dv, cu_seqlens, cu_seqlens_host, N,
+                                   workspace != nullptr);
+    const size_t need = plan_bytes(plan, N, H_v, dk, dv);
     if (need > 0) {
         if (workspace_bytes < need)
             return GDN_ERR_WORKSPACE;
@@ -260,10 +410,11 @@ gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t 
                                        h0, cu_seqlens, cu_seqlens_host, n_seqs, o, ht, N);
     if (st != GDN_OK)
         return st;
-    // The same plan gdn_chunk_fwd makes with a workspace; its piece arrays go
-    // to this device's static scratch, which bounds what it may need.
-    const PiecePlan plan = plan_pieces(dtype, B, T, H_v, dk, dv, cu_seqlens != nullptr);
-    if (gdn::fwd_piece_bytes(N, plan.pieces, H_v, dk, dv) > kStaticScratchBytes)
+    // The same plan gdn_chunk_fwd makes with a workspace; its arrays go to
+    // this device's static scratch, which bounds what it may need.
+    const FwdPlan plan = plan_call(dtype, B, T, H_v, dk, dv, cu_seqlens, cu_seqlens_host, N,
+                                   true);
+    if (plan_bytes(plan, N, H_v, dk, dv) > kStaticScratchBytes)
         return GDN_ERR_SCRATCH_LIMIT;
     void *scratch_ptr = nullptr;
     const hipError_t e = static_scratch(scratch_ptr);

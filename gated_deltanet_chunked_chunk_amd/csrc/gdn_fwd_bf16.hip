@@ -371,6 +371,46 @@ struct Stage {
     float g, b;   // row = lane
 };
 
+// The schedule of packed documents: slot r of the work order is document
+// order[r] (longest first) when the order is given, else document r.
+__device__ __forceinline__ int doc_at(const FwdArgs &a, int64_t r) {
+    return a.order ? a.order[r] : (int)r;
+}
+
+// Packed documents split into pieces of a.piece_len tokens: the pieces of
+// document n (a document no longer than one piece, empty ones included, is
+// one piece).
+__device__ __forceinline__ int64_t doc_pieces(const FwdArgs &a, int n) {
+    const int64_t len = (int64_t)a.cu[n + 1] - a.cu[n];
+    return len > a.piece_len ? (len + a.piece_len - 1) / a.piece_len : 1;
+}
+
+// The first slot of document n in the piece arrays: every piece but a
+// document's last has one, in document index order.
+__device__ __forceinline__ int64_t doc_slot_base(const FwdArgs &a, int n) {
+    int64_t b = 0;
+    for (int m = 0; m < n; ++m)
+        b += doc_pieces(a, m) - 1;
+    return b;
+}
+
+// Document and piece of the r-th piece of a pass (ends: every piece but a
+// document's last; otherwise all), documents taken in schedule order.
+// False when r is past the last piece.
+__device__ __forceinline__ bool locate_piece(const FwdArgs &a, int64_t r, bool ends, int &n,
+                                             int64_t &p) {
+    for (int i = 0; i < a.n_seqs; ++i) {
+        n = doc_at(a, i);
+        const int64_t cnt = doc_pieces(a, n) - (ends ? 1 : 0);
+        if (r < cnt) {
+            p = r;
+            return true;
+        }
+        r -= cnt;
+    }
+    return false;
+}
+
 // Without Full (the piece ends, which form no output) Q is not loaded.  DK
 // is the key dimension in HBM; with DK = 64 the LDS rows keep their 128
 // columns and the lanes of the upper 64 stage zeros.  With DK = 256, tile
@@ -1122,7 +1162,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     // dispatched round-robin over the 8 XCDs, so block b runs on XCD b % 8.
     const int n_val = a.dv / kDVT;
     const int n_tiles = Mode == 1 ? n_val + DK / kDVT : n_val;
-    const int np = a.pieces > 1 ? (Mode == 1 ? a.pieces - 1 : a.pieces) : 1;
+    const bool packed_pieces = a.cu && a.pieces > 1;
+    // Batch rows: pieces of a row in this pass.
+    const int np = a.pieces > 1 && !a.cu ? (Mode == 1 ? a.pieces - 1 : a.pieces) : 1;
     const int G = a.Hv / a.Hqk;
     const int gs = n_tiles * G;
     const int nb = gridDim.x;
@@ -1134,17 +1176,36 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     Item it;
     const int tile = w % n_tiles;
     it.j = (w / n_tiles) % a.Hv;
-    const int rest = w / (n_tiles * a.Hv);
-    it.piece = rest % np;
-    it.n = rest / np;
+    const int64_t rest = w / (n_tiles * a.Hv);
     it.hk = it.j / G;
     it.ident = Mode == 1 && tile >= n_val;
     it.c0 = (it.ident ? tile - n_val : tile) * kDVT;
     int64_t p1;
-    if (a.cu) {
+    int64_t slot_base = 0;  // the sequence's first slot in the piece arrays
+    int64_t seq_pieces = 1; // pieces of the sequence
+    if (packed_pieces) {
+        int n = 0;
+        int64_t pc = 0;
+        if (!locate_piece(a, rest, Mode == 1, n, pc))
+            return;  // past the last piece (a host copy of cu that disagrees with the device's)
+        it.n = n;
+        it.piece = (int)pc;
+        seq_pieces = doc_pieces(a, n);
+        slot_base = doc_slot_base(a, n);
+        if (slot_base + seq_pieces - 1 > a.n_slots)
+            return;  // more pieces than the workspace holds (the same disagreement)
+        it.p0 = a.cu[n] + pc * a.piece_len;
+        p1 = pc + 1 < seq_pieces ? it.p0 + a.piece_len : a.cu[n + 1];
+    } else if (a.cu) {
+        it.piece = 0;
+        it.n = doc_at(a, rest);
         it.p0 = a.cu[it.n];
         p1 = a.cu[it.n + 1];
     } else {
+        it.piece = (int)(rest % np);
+        it.n = (int)(rest / np);
+        seq_pieces = a.pieces > 1 ? a.pieces : 1;
+        slot_base = (int64_t)it.n * (seq_pieces - 1);
         const int64_t row0 = (int64_t)it.n * a.T;
         const int64_t s0 = a.pieces > 1 ? it.piece * a.piece_len : 0;
         const int64_t s1 = a.pieces > 1 && it.piece < a.pieces - 1 ? s0 + a.piece_len : a.T;
@@ -1174,8 +1235,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     const int lg = lane >> 4, lr = lane & 15;
     const int col = it.c0 + 16 * s + lr;
     const int64_t hbase = ((int64_t)it.n * a.Hv + it.j) * DK * (int64_t)a.dv;
-    // The slot of (row, piece, head) in the piece arrays.
-    const int64_t pslot = ((int64_t)it.n * (a.pieces - 1) + it.piece) * a.Hv + it.j;
+    // The slot of (sequence, piece, head) in the piece arrays.
+    const int64_t pslot = (slot_base + it.piece) * a.Hv + it.j;
 
     f32x4 h[NH];
     Stage st;
@@ -1277,7 +1338,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             stride = a.dv + DK;
             dst = a.piece_ends + pslot * DK * stride;
             dcol = (it.ident ? a.dv : 0) + col;
-        } else if (Mode != 3 && a.ht && it.piece == np - 1) {
+        } else if (Mode != 3 && a.ht && it.piece == seq_pieces - 1) {
             dst = a.ht + hbase;
         }
         if (dst) {
@@ -1314,13 +1375,19 @@ __global__ __launch_bounds__(256) void piece_scan(FwdArgs a) {
     const int n = blockIdx.x / a.Hv, j = blockIdx.x % a.Hv;
     const int c0 = blockIdx.y * kScanCols;
     const int64_t hbase = ((int64_t)n * a.Hv + j) * DK * (int64_t)a.dv;
+    // The sequence's slots: batch rows have pieces - 1 each; a packed
+    // document one per piece but its last.
+    const int64_t count = a.cu ? doc_pieces(a, n) - 1 : a.pieces - 1;
+    const int64_t base = a.cu ? doc_slot_base(a, n) : (int64_t)n * (a.pieces - 1);
+    if (count <= 0 || base + count > a.n_slots)
+        return;
     for (int e = tid; e < DK * kScanCols; e += 256) {
         const int i = e / kScanCols, c = e % kScanCols;
         Ms[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + c0 + c] : 0.0f;
     }
     const int64_t estride = a.dv + DK;
-    for (int p = 0; p + 1 < a.pieces; ++p) {
-        const int64_t pslot = ((int64_t)n * (a.pieces - 1) + p) * a.Hv + j;
+    for (int64_t p = 0; p < count; ++p) {
+        const int64_t pslot = (base + p) * a.Hv + j;
         const float *ends = a.piece_ends + pslot * DK * estride;
         f32x4 acc[R];
 #pragma unroll
@@ -1367,13 +1434,16 @@ hipError_t launch_passes(const FwdArgs &a, hipStream_t stream) {
                            stream, a);
         return hipGetLastError();
     }
-    const int64_t blocks_a = (int64_t)a.n_seqs * (a.pieces - 1) * a.Hv * (n_val + DK / kDVT);
-    const int64_t blocks_b = (int64_t)a.n_seqs * a.pieces * a.Hv * n_val;
+    const int64_t items_a = a.cu ? a.items_ends : (int64_t)a.n_seqs * (a.pieces - 1);
+    const int64_t items_b = a.cu ? a.items_all : (int64_t)a.n_seqs * a.pieces;
+    const int64_t blocks_a = items_a * a.Hv * (n_val + DK / kDVT);
+    const int64_t blocks_b = items_b * a.Hv * n_val;
     const int64_t scan_rows = (int64_t)a.n_seqs * a.Hv;
     if (blocks_a > 0x7fffffff || blocks_b > 0x7fffffff || scan_rows > 0x7fffffff)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
-                       stream, a);
+    if (blocks_a > 0)
+        hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 1, DK>), dim3((unsigned)blocks_a), dim3(kThreads), 0,
+                           stream, a);
     hipLaunchKernelGGL(piece_scan<DK>, dim3((unsigned)scan_rows, (unsigned)(a.dv / kScanCols)),
                        dim3(256), 0, stream, a);
     hipLaunchKernelGGL((gdn_fwd_bf16<Prep, 2, DK>), dim3((unsigned)blocks_b), dim3(kThreads), 0,
@@ -1410,12 +1480,47 @@ hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv) {
-    if (pieces <= 1)
+size_t fwd_piece_starts_offset(int64_t slots, int32_t Hv, int32_t dk, int32_t dv) {
+    const size_t per = (size_t)slots * Hv * dk;
+    return (per * (dv + dk) * 4 + 255) / 256 * 256;
+}
+
+size_t fwd_piece_bytes(int64_t slots, int32_t Hv, int32_t dk, int32_t dv) {
+    if (slots <= 0)
         return 0;
-    const size_t per = (size_t)n_seqs * (pieces - 1) * Hv * dk;
-    const size_t ends = (per * (dv + dk) * 4 + 255) / 256 * 256;
-    return ends + per * dv * 4;
+    return fwd_piece_starts_offset(slots, Hv, dk, dv) + (size_t)slots * Hv * dk * dv * 4;
+}
+
+namespace {
+
+// Documents ranked by length, longest first, ties by index: each thread
+// ranks its documents by counting the longer ones among all (lengths staged
+// in LDS, read by every thread at the same address).
+__global__ __launch_bounds__(1024) void doc_order(const int32_t *cu, int32_t n_seqs,
+                                                  int32_t *order) {
+    __shared__ int32_t len[kMaxOrderedDocs];
+    for (int i = threadIdx.x; i < n_seqs; i += blockDim.x)
+        len[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    for (int n = threadIdx.x; n < n_seqs; n += blockDim.x) {
+        const int32_t ln = len[n];
+        int rank = 0;
+        for (int m = 0; m < n_seqs; ++m) {
+            const int32_t lm = len[m];
+            rank += (lm > ln) | ((lm == ln) & (m < n));
+        }
+        order[rank] = n;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_doc_order(const int32_t *cu, int32_t n_seqs, int32_t *order,
+                            hipStream_t stream) {
+    if (n_seqs < 1 || n_seqs > kMaxOrderedDocs)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(doc_order, dim3(1), dim3(1024), 0, stream, cu, n_seqs, order);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, hipStream_t stream) {

@@ -39,7 +39,7 @@ struct SmemF32 {
     float Q[kC][DK + 1];
     float V[kC][kDVT + 1];
     float M[DK][kDVT + 1];      // state slice
-    float T[kC][kC + 1];        // A, then T' = (I + A)^-1 diag(beta)
+    alignas(16) float T[kC][kC + 4];  // A, then T' = (I + A)^-1 diag(beta); 16-byte rows
     float P[kC][kC + 1];        // (Q K^T) * D
     float Y[kC][kDVT + 1];      // V - diag(exp gamma) K M0, then Delta
     float gam[kC], bt[kC], el[kC];
@@ -81,33 +81,62 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
     for (int64_t p = p0; p < p1; p += kC) {
         const int L = (int)min<int64_t>(kC, p1 - p);
         __syncthreads();
-        for (int e = tid; e < kC * DK; e += kThreads) {
-            const int r = e / DK, d = e % DK;
-            const int64_t off = ((p + r) * a.Hqk + hk) * DK + d;
-            S.K[r][d] = r < L ? k[off] : 0.0f;
-            S.Q[r][d] = r < L ? q[off] : 0.0f;
-        }
-        for (int e = tid; e < kC * kDVT; e += kThreads) {
-            const int r = e / kDVT, c = e % kDVT;
-            S.V[r][c] = r < L ? v[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + c] : 0.0f;
-        }
-        if (tid == 0) {
-            const bool act = a.flags & kStepGateAct;
-            float acc = 0.0f;
-            for (int r = 0; r < kC; ++r) {
-                const bool ok = r < L;
-                float gv = ok ? a.g[(p + r) * a.Hv + j] : 0.0f;
-                float bv = ok ? a.beta[(p + r) * a.Hv + j] : 0.0f;
-                if (act && ok) {
-                    gv = logsigmoid_f32(gv);
-                    bv = sigmoid_f32(bv);
-                }
-                acc += gv;
-                S.gam[r] = acc;
-                S.bt[r] = bv;
+        // Every load of the chunk is issued before any is stored, so their
+        // latencies overlap instead of adding up.
+        {
+            constexpr int KPT = kC * DK / kThreads, VPT = kC * kDVT / kThreads;
+            float kr[KPT], qr[KPT], vr[VPT];
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const int e = tid + kThreads * i, r = e / DK, d = e % DK;
+                const int64_t off = ((p + r) * a.Hqk + hk) * DK + d;
+                kr[i] = r < L ? k[off] : 0.0f;
+                qr[i] = r < L ? q[off] : 0.0f;
             }
-            for (int r = 0; r < kC; ++r)
-                S.el[r] = expf(acc - S.gam[r]);
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int e = tid + kThreads * i, r = e / kDVT, c = e % kDVT;
+                vr[i] = r < L ? v[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + c] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                const int e = tid + kThreads * i, r = e / DK, d = e % DK;
+                S.K[r][d] = kr[i];
+                S.Q[r][d] = qr[i];
+            }
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int e = tid + kThreads * i, r = e / kDVT, c = e % kDVT;
+                S.V[r][c] = vr[i];
+            }
+        }
+        if (tid < 64) {
+            // Gates of row r = lane, loaded in parallel (rows past the
+            // chunk's end read as zero).  gamma is summed in row order, the
+            // same sequence of fp32 additions in every lane (lane r keeps the
+            // partial sum after row r): gamma_L - gamma_r then carries only
+            // the rounding of rows r+1..L, which a tree-shaped scan would not.
+            const int r = tid;
+            const bool ok = r < L;
+            float gv = ok ? a.g[(p + r) * a.Hv + j] : 0.0f;
+            float bv = ok ? a.beta[(p + r) * a.Hv + j] : 0.0f;
+            if ((a.flags & kStepGateAct) && ok) {
+                gv = logsigmoid_f32(gv);
+                bv = sigmoid_f32(bv);
+            }
+            float acc = 0.0f, mine = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kC; ++i) {
+                acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, gv), i));
+                if (i == r)
+                    mine = acc;
+            }
+            if (r < kC) {
+                S.gam[r] = mine;
+                S.bt[r] = bv;
+                S.el[r] = expf(acc - mine);
+            }
         }
         __syncthreads();
         if (a.flags & kStepL2Norm) {
@@ -152,20 +181,34 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         __syncthreads();
 
         // T = (I + A)^-1 column by column: thread c of wave 0 solves column c
-        // by forward substitution, reading only A; T' = T diag(beta) replaces A
-        // after the barrier.
+        // by forward substitution, reading only A (every thread reads the
+        // same A[r][s]: broadcast reads); T' = T diag(beta) replaces A after
+        // the barrier.  The loops are unrolled so x stays in registers; its
+        // entries above the diagonal are zero, so the sums can start at 0.
+        // Each row's sum runs in four interleaved partial sums over 16-byte
+        // reads of the row, so the loads and the multiply-adds pipeline.
         float x[kC];
         if (tid < kC) {
             const int c = tid;
+#pragma unroll
             for (int r = 0; r < kC; ++r) {
-                float acc = (r == c) ? 1.0f : 0.0f;
-                for (int s = c; s < r; ++s)
-                    acc -= S.T[r][s] * x[s];
+                float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s4 = 0; 4 * s4 < r; ++s4) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(&S.T[r][4 * s4]);
+                    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * s4 + i < r)
+                            part[i] = __builtin_fmaf(av[i], x[4 * s4 + i], part[i]);
+                }
+                const float acc = ((r == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
                 x[r] = (r < c) ? 0.0f : acc;
             }
         }
         __syncthreads();
         if (tid < kC)
+#pragma unroll
             for (int r = 0; r < kC; ++r)
                 S.T[r][tid] = x[r] * S.bt[tid];
         __syncthreads();

@@ -47,13 +47,21 @@ struct FwdArgs {
     int32_t n_seqs;
     float scale;
     uint32_t flags;         // kStepL2Norm | kStepGateAct: in-op preparation
-    // Piece-parallel scan of long rows (batch mode only; pieces <= 1: off).
-    // Row n is split into `pieces` runs of piece_len tokens (a multiple of
-    // 64; the last takes the rest).
+    // Piece-parallel scan (pieces <= 1: off).  Batch rows: row n is split
+    // into `pieces` runs of piece_len tokens (a multiple of 64; the last
+    // takes the rest).  Packed documents (cu set, pieces > 1): document n is
+    // split into ceil(len / piece_len) runs (one for a shorter or empty
+    // document).  Every piece but a sequence's last has a slot in the piece
+    // arrays, the slots of sequence n following those of sequences < n;
+    // n_slots is their number (the arrays' capacity).
     int32_t pieces;
     int64_t piece_len;
-    float *piece_ends;      // [n_seqs, pieces - 1, Hv, dk, dv + dk]: F | Phi of each piece but the last
-    float *piece_starts;    // [n_seqs, pieces - 1, Hv, dk, dv]: the state entering pieces 1..
+    int64_t n_slots;
+    int64_t items_ends;     // packed pieces: pieces of the first pass (all but each document's last)
+    int64_t items_all;      // packed pieces: all pieces
+    float *piece_ends;      // [n_slots, Hv, dk, dv + dk]: F | Phi of each piece but the last
+    float *piece_starts;    // [n_slots, Hv, dk, dv]: the state entering the piece after each slot's
+    const int32_t *order;   // packed: [n_seqs] documents longest first (doc_order), or null
     uint16_t *chunk_states; // launch_fwd_chunk_states only
 };
 
@@ -64,8 +72,17 @@ struct FwdArgs {
 // destination.
 hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream);
 
-// Workspace bytes of the piece scan for `pieces` pieces per row.
-size_t fwd_piece_bytes(int32_t n_seqs, int32_t pieces, int32_t Hv, int32_t dk, int32_t dv);
+// Workspace bytes of the piece scan for `slots` slots (batch rows:
+// n_seqs * (pieces - 1)); the start states follow the end states at
+// fwd_piece_starts_offset().
+size_t fwd_piece_bytes(int64_t slots, int32_t Hv, int32_t dk, int32_t dv);
+size_t fwd_piece_starts_offset(int64_t slots, int32_t Hv, int32_t dk, int32_t dv);
+
+// Ranks the n_seqs documents of cu by length, longest first (ties by index),
+// into order[n_seqs]: the order in which the forward schedules them.
+// n_seqs <= kMaxOrderedDocs.
+constexpr int32_t kMaxOrderedDocs = 2048;
+hipError_t launch_doc_order(const int32_t *cu, int32_t n_seqs, int32_t *order, hipStream_t stream);
 
 // bf16 q/k/v/o, dk in {64, 128, 256}, dv a multiple of 64: one workgroup per
 // (sequence, value head, 64 value columns).

@@ -181,6 +181,15 @@ CONFIGS = {
     "fwd_bwd_dk64_bf16": dict(B=8, T=1024, Hqk=8, Hv=8, dk=64, dv=64, dtype="bf16", seed=1008),
     # one long row at head dimension 256 and 8 heads (drawn on the device)
     "long_k256_bf16": dict(B=1, T=65536, Hqk=8, Hv=8, dk=256, dv=256, dtype="bf16", seed=1007),
+    # packed documents at few heads: one row of 8 heads, 16,384 tokens in
+    # geometric documents of mean length 1024 (about 16 documents)
+    "packed_8h_bf16": dict(total=16384, mean_len=1024, Hqk=8, Hv=8, dk=128, dv=128,
+                           dtype="bf16", seed=1009, h0_std=0.02),
+    # packed documents at few heads with one long document: one row of 8
+    # heads, 30,000 tokens, a 20,000-token document among seven short ones
+    "packed_long_doc_bf16": dict(lengths=[20000, 2000, 1500, 3000, 900, 1100, 800, 700],
+                                 Hqk=8, Hv=8, dk=128, dv=128, dtype="bf16", seed=1010,
+                                 h0_std=0.02),
 }
 
 
@@ -229,10 +238,10 @@ def make_config(name, **override):
     use them to shrink a workload while keeping its recipe)."""
     c = dict(CONFIGS[name])
     c.update(override)
-    if "total" in c:
-        lengths = geometric_lengths(c["total"], c["mean_len"], c["seed"])
+    if "total" in c or "lengths" in c:
+        lengths = c.get("lengths") or geometric_lengths(c["total"], c["mean_len"], c["seed"])
         cu = cu_from_lengths(lengths)
-        return make(1, c["total"], c["Hqk"], c["Hv"], c["dk"], c["dv"], c["dtype"],
+        return make(1, int(cu[-1]), c["Hqk"], c["Hv"], c["dk"], c["dv"], c["dtype"],
                     c["seed"], h0_std=c.get("h0_std"), cu_seqlens=cu)
     return make(c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"], c["dtype"], c["seed"],
                 h0_std=c.get("h0_std"))

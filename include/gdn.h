@@ -89,11 +89,32 @@ typedef enum {
  * where pieces would not save a twentieth, return 0.  Returns 0 as well for
  * fp32, and for sizes the forward would reject.
  *
- * n_seqs: the number of documents when cu_seqlens will be passed, else B
- * (packed calls never use the piece scan).
+ * Packed calls (cu_seqlens, B = 1) also use the workspace: it holds the
+ * order in which the documents are scheduled, longest first (ranked on the
+ * device, up to 2,048 documents), and, when the host copy of cu_seqlens is
+ * given, the piece scan over long documents: a document longer than the
+ * planned piece length is split into pieces exactly as a long row is.  The
+ * documents' pieces use at most the piece slots of the single-row plan of
+ * T tokens, so the size does not depend on the document lengths.
+ *
+ * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  */
 size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
                                     int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs);
+
+/*
+ * The plan gdn_chunk_fwd makes for a call given a large enough workspace,
+ * without launching anything: *piece_len is the piece length in tokens of
+ * the piece scan (0: whole rows or documents), *slots the number of pieces
+ * that hand a start state on (the piece arrays' rows), *ordered 1 when the
+ * documents of a packed call are scheduled longest first.  Pass
+ * cu_seqlens_host (n_seqs documents, B = 1) to plan a packed call, or NULL
+ * for B batch rows.  The arguments are validated as gdn_chunk_fwd's are.
+ */
+gdn_status gdn_chunk_fwd_plan(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                              int32_t dk, int32_t dv, const int32_t *cu_seqlens_host,
+                              int32_t n_seqs, int64_t *piece_len, int64_t *slots,
+                              int32_t *ordered);
 
 /*
  * The chunked forward.
@@ -129,20 +150,24 @@ size_t gdn_chunk_fwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   h0           [N, H_v, dk, dv] fp32 initial states, or NULL for zeros.
  *   cu_seqlens   device int32 [N + 1] document offsets, or NULL (then the
  *                documents are the B rows and N = B).
- *   cu_seqlens_host  optional host copy of cu_seqlens.  When given it is
- *                validated (cu[0] = 0, non-decreasing, cu[N] = T) before
- *                anything is enqueued; when NULL the device array is trusted.
- *                The kernels read the device array either way.  Empty
- *                documents are allowed: their final state is their initial
- *                state.
+ *   cu_seqlens_host  optional host copy of cu_seqlens, equal to it.  When
+ *                given it is validated (cu[0] = 0, non-decreasing, cu[N] = T)
+ *                before anything is enqueued and, with a workspace, lets the
+ *                host plan the piece scan over long documents (bf16); when
+ *                NULL the device array is trusted and documents run whole.
+ *                The kernels read the device array (a host copy that
+ *                disagrees with it leaves work undone but never writes
+ *                outside the outputs and workspace).  Empty documents are
+ *                allowed: their final state is their initial state.
  *   n_seqs       N when cu_seqlens is given (>= 1); ignored otherwise.
  *   o            [B, T, H_v, dv] output, dtype `dtype`.
  *   ht           [N, H_v, dk, dv] fp32 final states, or NULL to skip them.
  *   workspace    device scratch of gdn_chunk_fwd_workspace_size() bytes,
  *                256-byte aligned, owned by the caller and not read after the
- *                call's work completes; or NULL, which runs whole rows (the
- *                same result up to rounding).  A non-NULL workspace that is
- *                smaller than the query returns GDN_ERR_WORKSPACE.
+ *                call's work completes; or NULL, which runs whole rows and
+ *                documents in index order (the same result up to rounding).
+ *                A non-NULL workspace smaller than the plan needs returns
+ *                GDN_ERR_WORKSPACE.
  *   stream       HIP stream to enqueue on (NULL = the default stream).
  *
  * Every pointer must be 16-byte aligned.  o and ht must not overlap the

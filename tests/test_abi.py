@@ -299,3 +299,52 @@ def test_piece_plan_properties():
                     found = [p for p in range(2, 257) if piece_bytes(B, p, Hv, dk, dv) == need]
                     assert len(found) == 1, (B, T, Hv, dk, dv, need)
                     assert found[0] <= -(-T // 64), (B, T, Hv, dk, dv)
+
+
+def test_packed_plan():
+    """The plan of packed calls (from the host copy of cu_seqlens): documents
+    longest first whenever there is more than one (up to 2,048); long
+    documents split only where the cost model gains, within the slots of the
+    single-row plan of T tokens (the capacity the size-only query promises);
+    short documents never."""
+    import gdn_inputs as gi
+    plan = gdn.gdn_chunk_fwd_plan
+    # One row of 8 heads, ~16 geometric documents of mean 1024: all 256
+    # workgroups run at once, so whole documents (longest first) are best.
+    cu = [int(x) for x in gi.cu_from_lengths(gi.geometric_lengths(16384, 1024, 1009))]
+    assert plan(1, 1, 16384, 8, 8, 128, 128, cu) == (0, 0, True)
+    # One 20,000-token document among seven short ones at 8 heads: split.
+    cu = [int(x) for x in gi.cu_from_lengths([20000, 2000, 1500, 3000, 900, 1100, 800, 700])]
+    T = cu[-1]
+    pl, slots, ordered = plan(1, 1, T, 8, 8, 128, 128, cu)
+    _, budget, _ = plan(1, 1, T, 8, 8, 128, 128)
+    assert ordered and pl > 0 and pl % 64 == 0 and 0 < slots <= budget
+    assert slots == sum(max(0, -(-(b - a) // pl) - 1) for a, b in zip(cu, cu[1:]))
+    # The 32-head packed workload fills the CUs: ordered, not split.
+    cu = [int(x) for x in gi.cu_from_lengths(gi.geometric_lengths(16384, 1024, 1002))]
+    assert plan(1, 1, 16384, 16, 32, 128, 128, cu) == (0, 0, True)
+    # Short documents are never split, whatever the heads.
+    cu = list(range(0, 20 * 500 + 1, 20))
+    assert plan(1, 1, cu[-1], 1, 1, 128, 128, cu)[:2] == (0, 0)
+    # One document: nothing to order.
+    assert plan(1, 1, 5000, 1, 1, 128, 128, [0, 5000])[2] is False
+    # fp32: never split, never ordered.
+    assert plan(0, 1, 16384, 8, 8, 128, 128, [0, 16000, 16384]) == (0, 0, False)
+    # Without the host copy nothing is planned from lengths (batch rows).
+    assert plan(1, 2, 2048, 16, 16, 128, 128)[2] is False
+
+
+def test_packed_workspace_size():
+    """A packed call's workspace: the document order (4 bytes per document,
+    256-aligned, up to 2,048 documents) plus the single-row piece capacity."""
+    base = gdn.gdn_chunk_fwd_workspace_size(1, 1, 16384, 8, 8, 128, 128, 1)
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 16384, 8, 8, 128, 128, 16) == base + 256
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 16384, 8, 8, 128, 128, 100) == base + 512
+    assert gdn.gdn_chunk_fwd_workspace_size(1, 1, 16384, 8, 8, 128, 128, 5000) == base
+    assert gdn.gdn_chunk_fwd_workspace_size(0, 1, 16384, 8, 8, 128, 128, 16) == 0
+
+
+@pytest.mark.parametrize("cu", [[1, 10, 64], [0, 10, 63], [0, 30, 20]])
+def test_plan_rejects_bad_host_offsets(cu):
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_chunk_fwd_plan(1, 1, 64, 1, 1, 128, 128, cu)

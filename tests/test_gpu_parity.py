@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import gdn_inputs as gi
-from gpu_util import TOL, check, rel_l2, run_gpu, run_oracle
+from gpu_util import TOL, check, rel_l2, run_gpu, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -79,11 +79,75 @@ def test_packed_equals_separate_bitwise():
         assert np.array_equal(ht[n:n + 1], hn), f"document {n}: state differs"
 
 
-def test_packed_device_schedule_matches_host_validated():
+def test_packed_order_is_bitwise_neutral():
+    """Scheduling the documents longest first (the workspace's order array)
+    changes no arithmetic: with the order, without it (no workspace: index
+    order), and planned from the host copy or not, the results are bitwise
+    equal when the plan splits no document."""
+    import gated_deltanet_chunked_chunk_amd as gdn
     d = gi.make_config("packed_gva_bf16", total=3000)
+    cu = [int(x) for x in d["cu_seqlens"]]
+    pl, _, ordered = gdn.gdn_chunk_fwd_plan(1, 1, d["T"], d["Hqk"], d["Hv"], 128, 128, cu)
+    assert pl == 0 and ordered
     o1, h1 = run_gpu(d, host_cu=True)
     o2, h2 = run_gpu(d, host_cu=False)
+    t = to_device(d)
+    o3, h3 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"],
+                               cu_seqlens=t["cu"], pieces=False)
+    torch.cuda.synchronize()
     assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+    assert np.array_equal(o1, o3.float().cpu().numpy()) and np.array_equal(h1, h3.cpu().numpy())
+
+
+PACKED_PIECE_CASES = [
+    # label, lengths (or a geometric draw), H_qk, H_v, dk, dv, h0 std, decay divisor
+    ("one long document of eight x 8 heads", [8000, 700, 500, 1200, 300, 64, 0, 900], 8, 8,
+     128, 128, 0.02, 1),
+    ("one long document", [12000, 300, 0, 77, 1500], 2, 4, 128, 128, 0.3, 8),
+    ("dk64", [9000, 0, 2500, 640, 1], 1, 2, 64, 128, 0.3, 8),
+    ("dk256", [6000, 33, 0, 2100], 1, 2, 256, 128, 0.1, 8),
+]
+
+
+@pytest.mark.parametrize("case", PACKED_PIECE_CASES, ids=lambda c: c[0].replace(" ", "_"))
+def test_packed_piece_scan(case):
+    """Long documents of a packed call split into pieces (planned from the
+    host copy of cu_seqlens): against the oracle on every (document, head)
+    and against whole documents (no workspace)."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    label, lengths, Hqk, Hv, dk, dv, h0_std, div = case
+    cu = gi.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    d = gi.make(1, T, Hqk, Hv, dk, dv, "bf16", 5100 + T % 97, h0_std=h0_std, cu_seqlens=cu)
+    d["g"] = (d["g"] / div).astype(np.float32)
+    pl, slots, _ = gdn.gdn_chunk_fwd_plan(1, 1, T, Hqk, Hv, dk, dv, [int(x) for x in cu])
+    print(f"[gpu case] packed pieces {label}: {len(lengths)} documents, piece length {pl}, "
+          f"{slots} slots", flush=True)
+    assert pl > 0 and slots > 0
+    check(d, scale=0.9, label=f"packed pieces {label}")
+    o1, h1 = run_gpu(d, scale=0.9)
+    t = to_device(d)
+    o2, h2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], scale=0.9,
+                               initial_state=t["h0"], cu_seqlens=t["cu"], pieces=False)
+    torch.cuda.synchronize()
+    tol_o, tol_h = TOL["bf16"]
+    assert rel_l2(o1, o2.float().cpu().numpy()) <= tol_o
+    assert rel_l2(h1, h2.cpu().numpy()) <= tol_h
+
+
+def test_packed_piece_scan_carries_state():
+    """No decay and a weak write (g = 0, beta = 0.02) across the pieces of a
+    long document, with a large initial state: the start states the scan
+    hands over carry most of the result."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    cu = gi.cu_from_lengths([10000, 50, 3000, 0])
+    T = int(cu[-1])
+    d = gi.make(1, T, 1, 2, 128, 128, "bf16", 5200, h0_std=1.0, cu_seqlens=cu)
+    d["g"] = np.zeros_like(d["g"])
+    d["beta"] = np.full_like(d["beta"], 0.02)
+    pl, slots, _ = gdn.gdn_chunk_fwd_plan(1, 1, T, 1, 2, 128, 128, [int(x) for x in cu])
+    assert pl > 0 and slots > 0
+    check(d, label="packed pieces, g = 0, beta = 0.02")
 
 
 def test_chained_halves():
@@ -264,15 +328,16 @@ def test_bf16_dk64_piece_scan():
     o2, h2 = gdn.gdn_chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=t["h0"],
                                pieces=False)
     ro, rht = run_oracle(d)
-    print(f"  whole rows: rel-L2 output {rel_l2(o2.float().cpu().numpy(), ro):.3e}, state "
-          f"{rel_l2(h2.cpu().numpy(), rht):.3e}", flush=True)
+    ew = (rel_l2(o2.float().cpu().numpy(), ro), rel_l2(h2.cpu().numpy(), rht))
+    print(f"  whole rows: rel-L2 output {ew[0]:.3e}, state {ew[1]:.3e}", flush=True)
+    assert ew[0] <= TOL["bf16"][0] and ew[1] <= TOL["bf16"][1]
 
 
 def test_many_short_documents():
     """1,000 packed documents of 0 to 20 tokens (most shorter than one
     chunk, some empty), with initial states, grouped heads (ratio 4): the
-    schedule built on the host and the one built on the device agree bitwise,
-    and both match the oracle."""
+    call planned with the host copy of cu_seqlens and the one without agree
+    bitwise (no document is split), and both match the oracle."""
     rng = np.random.default_rng(4200)
     lengths = [int(x) for x in rng.integers(0, 21, size=1000)]
     cu = gi.cu_from_lengths(lengths)
