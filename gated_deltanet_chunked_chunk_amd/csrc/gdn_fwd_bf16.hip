@@ -361,6 +361,7 @@ struct Item {
     int j, hk, c0, n;
     int piece;       // piece of the row (0 without the piece scan)
     bool ident;      // a transition tile: V = 0, starting from identity columns
+    int64_t chunk0;  // the backward's passes: the sequence's first chunk in the chunk numbering
 };
 
 // Helper-wave registers holding the next chunk's global data.
@@ -803,11 +804,40 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
         helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
 }
 
+// Writes a wave's 64 x 16 block, given as four C-layout tiles of bf16 pairs
+// (v[mi]: rows 16 mi + 4 g .. + 3 of column lr in lane (lr, g)), as rows of
+// 16 columns: dst points at row 0, column 0 of the block, rows are
+// row_stride elements apart, and rows >= rows_valid are not written.  The
+// block goes through the wave's own LDS staging area column-major (word w of
+// column c at w ^ x(c)); four transpose reads then give lane L the 16
+// columns of row L, stored as two 16-byte pieces.
+__device__ __forceinline__ void stage_store_rows(uint16_t *ost, const u32x2 (&v)[4], int lane,
+                                                 uint16_t *dst, int64_t row_stride,
+                                                 int rows_valid) {
+    const int lr = lane & 15, lg = lane >> 4;
+    auto ost_x = [](int col) {
+        return (((col >> 1) & 1) << 3) ^ (((col >> 2) & 1) << 1) ^ (((col >> 3) & 1) << 2);
+    };
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+        *reinterpret_cast<u32x2 *>(ost + lr * kC + 4 * ((4 * mi + lg) ^ ost_x(lr))) = v[mi];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int c0 = 8 * hf + (lr >> 2), c1 = c0 + 4;
+        const int w = 4 * lg + (lr & 3);
+        const u32x2 r0 = ld_tr(ost + c0 * kC + 4 * (w ^ ost_x(c0)));
+        const u32x2 r1 = ld_tr(ost + c1 * kC + 4 * (w ^ ost_x(c1)));
+        if (lane < rows_valid)
+            *reinterpret_cast<u32x4 *>(dst + lane * row_stride + 8 * hf) =
+                u32x4{r0.x, r0.y, r1.x, r1.y};
+    }
+}
+
 // State waves: one chunk of (a5)-(a7) for value columns [16 s, 16 s + 16);
 // without Out only the state advances (the output is not formed).
 // Nrm: Q M0 is scaled by the egq table (exp(gamma) mu); the in-op L2 norms
 // of K (nu) are already in the eg and el tables.
-template <bool Out, bool Nrm, int DK>
+template <bool Out, bool Nrm, int DK, bool SaveDelta = false>
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
@@ -905,6 +935,13 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         }
     }
 
+    if constexpr (SaveDelta) {
+        // The backward's forward pass: the chunk's Delta rows (hi part).
+        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)kC * a.dv +
+                        it.c0 + 16 * s;
+        stage_store_rows(S.Ost[s], dh, lane, dst, a.dv, kC);
+    }
+
     // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta,
     // K^T fragments loaded one tile ahead of the products.
     bf16x8 dph[2], dpl[2];
@@ -989,6 +1026,168 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         if (lane < L)
             *reinterpret_cast<u32x4 *>(o + 8 * hf) = u32x4{r0.x, r0.y, r1.x, r1.y};
     }
+}
+
+// State waves, the backward's reverse pass: one chunk of the state-gradient
+// recurrence for value columns [16 s, 16 s + 16).  h holds the wave's slice
+// of dM, the gradient of the state leaving the chunk, in the forward's
+// layout; the value tile holds dO (the upstream gradient of o) instead of V.
+// From the forward's chunk equations (M0 -> Delta -> O, M_L), by the chain
+// rule:
+//   dDelta = diag(l) K dM + scale P^T dO,        l = exp(gamma_L - gamma)
+//   (I + A)^T drhs = dDelta                      (T^T dDelta, T = (I + A)^-1)
+//   dM0 = exp(gamma_L) dM - K^T diag(beta e) drhs + scale Q^T diag(e) dO
+// The transposed solve is the forward's block substitution run backwards,
+// drhs_i = D_i^T (dDelta_i - sum_{j>i} A_ji^T drhs_j), with D_i^T and the
+// A_ji^T read from the forward's tiles by plain and transposing LDS reads,
+// split products as in state_chunk.  K dM and P^T dO use single bf16
+// roundings of dM and P (as the forward's K M0 and P Delta do).  drhs is
+// stored as bf16 rows (the parallel gradient pass reads it) and dV =
+// diag(beta) drhs as the gradient of v.
+template <int DK>
+__device__ __forceinline__ void state_chunk_rev(Smem &S, const ChunkBuf &B, const FwdArgs &a,
+                                                const Item &it, int c, int s, int lane,
+                                                f32x4 (&h)[8]) {
+    const int lr = lane & 15, lg = lane >> 4;
+    constexpr int KK = DK / 32, MT = DK / 16;
+    // Z = K dM (hi part of dM), fragments loaded one row block ahead.
+    bf16x8 hb[4];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+    f32x4 Z[4];
+    bf16x8 fk[2][4];
+    const KqBase kb = kq_base(lr, lg);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        fk[0][kk] = frag_kq(B.K, kb, 0, kk);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi < 3) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                fk[(mi + 1) & 1][kk] = frag_kq(B.K, kb, mi + 1, kk);
+        }
+        Z[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            Z[mi] = mma(fk[mi & 1][kk], hb[kk], Z[mi]);
+    }
+    // W = P^T dO.  A operand of row block mi of P^T: column 16 mi + lr of P,
+    // tokens 32 kk + 8 lg .. + 7 (two transpose reads); B operand: dO at the
+    // same tokens, column 16 s + lr of the value tile.
+    bf16x8 dob[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int r0 = 32 * kk + 8 * lg + (lr >> 2);
+        dob[kk] = cat(ld_tr(B.V + v_at(r0, 4 * s + (lr & 3))), ld_tr(B.V + v_at(r0 + 4, 4 * s + (lr & 3))));
+    }
+    f32x4 dD[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        f32x4 w = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (32 * kk + 31 < 16 * mi)
+                continue;  // P is zero above the diagonal
+            const uint16_t *pp = B.P + (32 * kk + 8 * lg + (lr >> 2)) * kSP + 16 * mi + 4 * (lr & 3);
+            w = mma(cat(ld_tr(pp), ld_tr(pp + 4 * kSP)), dob[kk], w);
+        }
+        const f32x4 el4 = ld4f(B.el + 16 * mi + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dD[mi][r] = el4[r] * Z[mi][r] + a.scale * w[r];
+    }
+    // Operands of the transposed solve: D_i^T (row lr of D_i^T is row
+    // 16 i + lr of the stored D_i^T copy, hi | lo) and (-A_ji)^T for j > i
+    // (transpose reads of the stored -A_ji, hi | lo).
+    bf16x8 Dt[4], At[6];  // At: blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int o = (16 * i + lr) * kSDT + 4 * lg;
+        Dt[i] = cat(ld8(B.DhT + o), ld8(B.DlT + o));
+    }
+#pragma unroll
+    for (int j = 1, n = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < j; ++i, ++n) {
+            const int o = (16 * (j - 1) + 4 * lg + (lr >> 2)) * kSN + 16 * i + 4 * (lr & 3);
+            At[n] = cat(ld_tr(B.Anh + o), ld_tr(B.Anl + o));
+        }
+    // drhs_i = D_i^T (dDelta_i - sum_{j>i} A_ji^T drhs_j), i = 3 .. 0; once
+    // drhs_j is known its products go into every earlier right-hand side.
+    f32x4 DR[4];
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        u32x2 xh, xl;
+        split4(dD[i], xh, xl);
+        f32x4 d = mma(Dt[i], cat(xh, xh), f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mma(Dt[i], cat(xl, xl), d);
+        DR[i] = d;
+        u32x2 dh, dl;
+        split4(d, dh, dl);
+        const bf16x8 bh = cat(dh, dh), bl = cat(dl, dl);
+#pragma unroll
+        for (int r = i - 1; r >= 0; --r) {
+            const int n = (i - 1) * i / 2 + r;  // block (i, r)
+            dD[r] = mma(At[n], bh, dD[r]);
+            dD[r] = mma(At[n], bl, dD[r]);
+        }
+    }
+    // dM0 = exp(gamma_L) dM + K^T x + Q^T y, x = -diag(beta e) drhs,
+    // y = scale diag(e) dO (hi | lo B operands over the chunk's rows).
+    const int vbase = v_at(4 * lg + (lr >> 2), 4 * s + (lr & 3));
+    u32x2 xh[4], xl[4], yh[4], yl[4], dvv[4], drb[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
+        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
+        const u32x2 vv = ld_tr(B.V + vbase + 16 * kDVT * mi);
+        f32x4 x, y, dv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float dov = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
+            x[r] = -(bt4[r] * eg4[r]) * DR[mi][r];
+            y[r] = a.scale * eg4[r] * dov;
+            dv4[r] = bt4[r] * DR[mi][r];
+        }
+        split4(x, xh[mi], xl[mi]);
+        split4(y, yh[mi], yl[mi]);
+        dvv[mi] = pack4(dv4);
+        drb[mi] = pack4(DR[mi]);
+    }
+    const bf16x8 xbh[2] = {cat(xh[0], xh[1]), cat(xh[2], xh[3])};
+    const bf16x8 xbl[2] = {cat(xl[0], xl[1]), cat(xl[2], xl[3])};
+    const bf16x8 ybh[2] = {cat(yh[0], yh[1]), cat(yh[2], yh[3])};
+    const bf16x8 ybl[2] = {cat(yl[0], yl[1]), cat(yl[2], yl[3])};
+    const float eL = B.eL;
+    const int ktrow = 4 * lg + (lr >> 2);
+    int ktb = kq_slot(ktrow, lr & 3);
+    asm volatile("" : "+v"(ktb));
+    auto tf = [&](const uint16_t *X, int mt, int kk) {
+        const uint16_t *p = X + (ktb ^ (32 * (mt >> 1))) + 4 * (mt & 1) + 32 * kk * kDK;
+        return cat(ld_tr(p), ld_tr(p + 16 * kDK));
+    };
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        h[mt] *= eL;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 kt = tf(B.K, mt, kk), qt = tf(B.Q, mt, kk);
+            h[mt] = mma(kt, xbh[kk], h[mt]);
+            h[mt] = mma(kt, xbl[kk], h[mt]);
+            h[mt] = mma(qt, ybh[kk], h[mt]);
+            h[mt] = mma(qt, ybl[kk], h[mt]);
+        }
+    }
+    // drhs rows to the workspace (all 64), dV rows to the output (valid rows).
+    uint16_t *dr = a.chunk_drhs + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)kC * a.dv +
+                   it.c0 + 16 * s;
+    stage_store_rows(S.Ost[s], drb, lane, dr, a.dv, kC);
+    const int L = min(kC, it.len - kC * c);
+    uint16_t *dvo = static_cast<uint16_t *>(a.dv_out) +
+                    ((it.p0 + (int64_t)kC * c) * a.Hv + it.j) * (int64_t)a.dv + it.c0 + 16 * s;
+    stage_store_rows(S.Ost[s], dvv, lane, dvo, (int64_t)a.Hv * a.dv, L);
 }
 
 // State waves, dk = 256: one 32-token chunk of (a5)-(a7) for value columns
@@ -1143,7 +1342,10 @@ __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, con
 }
 
 // Prep: the in-op preparation options of a.flags are honoured (a separate
-// instance, so the plain kernel carries none of their code).
+// instance, so the plain kernel carries none of their code).  Mode 4: the
+// backward's reverse pass (state_chunk_rev), chunks from the last, with dO in
+// place of V; it stores the gradient of every chunk's leaving state, drhs,
+// dV and dh0.
 // Mode 0: the output pass over whole rows.  Mode 2: the same over pieces
 // that start from the states of piece_starts (an instance of its own, so
 // traces tell the two apart).  Mode 3: no output; the state entering every
@@ -1155,6 +1357,8 @@ template <bool Prep, int Mode, int DK>
 __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     __shared__ Smem S;
     constexpr int CL = chunk_len<DK>(), NH = state_tiles<DK>();
+    // Modes that form P (and stage Q): the output passes and the reverse pass.
+    constexpr bool kFull = Mode == 0 || Mode == 2 || Mode == 4;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
     // Work item.  Items that read the same q/k head (the dv tiles and the
@@ -1250,7 +1454,9 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         __builtin_amdgcn_s_setprio(2);
     if (state) {
         const float *src = nullptr;
-        if (Mode != 1 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
+        if (Mode == 4)  // the reverse pass starts from the final state's gradient
+            src = a.dht ? a.dht + hbase : nullptr;
+        else if (Mode != 1 && it.piece > 0)  // the state entering this piece: slot (n, piece - 1, j)
             src = a.piece_starts + (pslot - a.Hv) * DK * (int64_t)a.dv;
         else if (Mode != 1 && a.h0)
             src = a.h0 + hbase;
@@ -1270,15 +1476,18 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                     h[mt][r] = it.ident && key_of(mt, lg, r) == col ? 1.f : 0.f;
         }
     } else if (it.nchunks > 0) {
-        stage_load<Mode == 0 || Mode == 2, DK>(st, a, it, 0, t, lane);
-        helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[0], st, s, t, lane, meet, a, it, min(CL, it.len),
-                             it.nchunks > 1 ? 1 : -1);
+        // The reverse pass (Mode 4) walks the chunks from the last.
+        const int c0 = Mode == 4 ? it.nchunks - 1 : 0;
+        const int c1 = Mode == 4 ? it.nchunks - 2 : 1;
+        stage_load<kFull, DK>(st, a, it, c0, t, lane);
+        helper_prepare<Prep, kFull, DK>(S, S.buf[0], st, s, t, lane, meet, a, it,
+                                        min(CL, it.len - CL * c0), it.nchunks > 1 ? c1 : -1);
     }
     lds_barrier();
 
-    // Mode 3: this sequence's first chunk in the chunk numbering.
+    // Modes 3 and 4: this sequence's first chunk in the chunk numbering.
     int64_t chunk0 = 0;
-    if (Mode == 3) {
+    if (Mode == 3 || Mode == 4) {
         if (a.cu) {
             for (int m = 0; m < it.n; ++m)
                 chunk0 += (a.cu[m + 1] - a.cu[m] + CL - 1) / CL;
@@ -1286,6 +1495,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             chunk0 = (int64_t)it.n * ((a.T + CL - 1) / CL);
         }
     }
+    it.chunk0 = chunk0;
     if constexpr (Prep) {
         // One chunk loop per role (the barrier counts match): the state
         // slice and the helpers' prefetch registers are then never live
@@ -1301,31 +1511,42 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         } else {
             for (int c = 0; c < it.nchunks; ++c) {
                 if (c + 1 < it.nchunks)
-                    helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a,
-                                                                     it, min(CL, it.len - CL * (c + 1)),
-                                                                     c + 2 < it.nchunks ? c + 2 : -1);
+                    helper_prepare<Prep, kFull, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a,
+                                                    it, min(CL, it.len - CL * (c + 1)),
+                                                    c + 2 < it.nchunks ? c + 2 : -1);
                 lds_barrier();
             }
         }
     } else {
-    for (int c = 0; c < it.nchunks; ++c) {
+    // Iteration i works on chunk c(i): in order, or from the last (Mode 4).
+    auto cidx = [&](int i) { return Mode == 4 ? it.nchunks - 1 - i : i; };
+    for (int i = 0; i < it.nchunks; ++i) {
+        const int c = cidx(i);
         if (state) {
-            if (Mode == 3) {
-                // Four consecutive keys per tile: one 8-byte store each.  The
-                // rows are 128 keys wide whatever DK is (zeros past DK).
-                uint16_t *dst = a.chunk_states + ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * kDK +
+            if (Mode == 3 || Mode == 4) {
+                // The state entering the chunk (Mode 3) or the gradient of
+                // the state leaving it (Mode 4): four consecutive keys per
+                // tile, one 8-byte store each.  The rows are 128 keys wide
+                // whatever DK is (zeros past DK).
+                uint16_t *dst = (Mode == 3 ? a.chunk_states : a.chunk_dstates) +
+                                ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * kDK +
                                 (int64_t)col * kDK;
 #pragma unroll
                 for (int mt = 0; mt < 8; ++mt)
                     *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
             }
-            if constexpr (DK == 256)
-                state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
+            if constexpr (Mode == 4)
+                state_chunk_rev<DK>(S, S.buf[i & 1], a, it, c, s, lane, h);
+            else if constexpr (DK == 256)
+                state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[i & 1], a, it, c, s, lane, h);
             else
-                state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
-        } else if (c + 1 < it.nchunks) {
-            helper_prepare<Prep, Mode == 0 || Mode == 2, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a, it,
-                                 min(CL, it.len - CL * (c + 1)), c + 2 < it.nchunks ? c + 2 : -1);
+                state_chunk<Mode == 0 || Mode == 2, Prep, DK, Mode == 3>(S, S.buf[i & 1], a, it, c, s,
+                                                                         lane, h);
+        } else if (i + 1 < it.nchunks) {
+            const int cn = cidx(i + 1);
+            helper_prepare<Prep, kFull, DK>(S, S.buf[(i + 1) & 1], st, s, t, lane, meet, a, it,
+                                            min(CL, it.len - CL * cn),
+                                            i + 2 < it.nchunks ? cidx(i + 2) : -1);
         }
         lds_barrier();
     }
@@ -1338,6 +1559,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             stride = a.dv + DK;
             dst = a.piece_ends + pslot * DK * stride;
             dcol = (it.ident ? a.dv : 0) + col;
+        } else if (Mode == 4) {
+            dst = a.dh0 ? a.dh0 + hbase : nullptr;
         } else if (Mode != 3 && a.ht && it.piece == seq_pieces - 1) {
             dst = a.ht + hbase;
         }
@@ -1464,19 +1687,25 @@ hipError_t launch_dk(const FwdArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.n_seqs * a.Hv * (a.dv / kDVT);
+hipError_t launch_bwd_state_passes(const FwdArgs &fwd, const FwdArgs &rev, hipStream_t stream) {
+    const int64_t blocks = (int64_t)fwd.n_seqs * fwd.Hv * (fwd.dv / kDVT);
     if (blocks <= 0)
         return hipSuccess;
-    if (blocks > 0x7fffffff || (a.dk != 128 && a.dk != 64) || a.pieces > 1 || a.flags ||
-        !a.chunk_states)
+    if (blocks > 0x7fffffff || (fwd.dk != 128 && fwd.dk != 64) || fwd.pieces > 1 || fwd.flags ||
+        !fwd.chunk_states || !fwd.chunk_deltas || !rev.chunk_dstates || !rev.chunk_drhs ||
+        !rev.dv_out)
         return hipErrorInvalidValue;
-    if (a.dk == 128)
+    if (fwd.dk == 128) {
         hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
-    else
+                           stream, fwd);
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 4, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, rev);
+    } else {
         hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           stream, a);
+                           stream, fwd);
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 4, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, rev);
+    }
     return hipGetLastError();
 }
 

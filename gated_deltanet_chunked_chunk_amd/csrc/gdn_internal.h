@@ -62,15 +62,26 @@ struct FwdArgs {
     float *piece_ends;      // [n_slots, Hv, dk, dv + dk]: F | Phi of each piece but the last
     float *piece_starts;    // [n_slots, Hv, dk, dv]: the state entering the piece after each slot's
     const int32_t *order;   // packed: [n_seqs] documents longest first (doc_order), or null
-    uint16_t *chunk_states; // launch_fwd_chunk_states only
+    // The backward's two state passes (launch_bwd_state_passes); chunks are
+    // numbered over the sequences in order, 64 tokens each.
+    uint16_t *chunk_states; // [n_chunks, Hv, dv, 128] bf16: the state entering each chunk
+    uint16_t *chunk_deltas; // [n_chunks, Hv, 64, dv] bf16: each chunk's Delta rows
+    uint16_t *chunk_dstates;// [n_chunks, Hv, dv, 128] bf16: the gradient of the state leaving each chunk
+    uint16_t *chunk_drhs;   // [n_chunks, Hv, 64, dv] bf16: each chunk's drhs rows
+    void *dv_out;           // [B, T, Hv, dv] bf16: the gradient of v
+    const float *dht;       // [n_seqs, Hv, dk, dv] or null
+    float *dh0;             // [n_seqs, Hv, dk, dv] or null
 };
 
-// The states entering every chunk (bf16, transposed: [n_chunks, Hv, dv, 128],
-// chunks numbered over the sequences in order; zeros past dk) by the forward
-// kernel without its output, for the backward.  bf16, dk = 64 or 128; `a` as
-// for the forward with pieces = 1, flags = 0 and chunk_states the
-// destination.
-hipError_t launch_fwd_chunk_states(const FwdArgs &a, hipStream_t stream);
+// The backward's state passes, on the forward kernel's helper/state
+// pipeline (bf16, dk = 64 or 128; `a` as for the forward with pieces = 1,
+// flags = 0):
+//   forward pass (v = the input v): every chunk's entering state M0
+//     (chunk_states, transposed, zeros past dk) and Delta rows (chunk_deltas);
+//   reverse pass (v = dout): the state-gradient recurrence from dht, chunks in
+//     reverse, storing the gradient of every chunk's leaving state
+//     (chunk_dstates), its drhs rows (chunk_drhs), dV (dv_out) and dh0.
+hipError_t launch_bwd_state_passes(const FwdArgs &fwd, const FwdArgs &rev, hipStream_t stream);
 
 // Workspace bytes of the piece scan for `slots` slots (batch rows:
 // n_seqs * (pieces - 1)); the start states follow the end states at
@@ -110,11 +121,10 @@ struct BwdArgs {
     float *dg;              // [B, T, Hv]
     float *dbeta;           // [B, T, Hv]
     float *dh0;             // [n_seqs, Hv, dk, dv] or null
-    float *ws_T;            // [n_chunks, Hv, 64, 64]
-    uint16_t *ws_P;         // [n_chunks, Hv, 64, 64]
-    float *ws_gam;          // [n_chunks, Hv, 64]
-    uint16_t *ws_hs;        // [n_chunks, Hv, dv, dk] bf16: the state entering each chunk
-    uint16_t *ws_dhs;       // [n_chunks, Hv, dv, dk] bf16: the gradient of the state leaving it
+    uint16_t *ws_hs;        // [n_chunks, Hv, dv, 128] bf16: the state entering each chunk
+    uint16_t *ws_dhs;       // [n_chunks, Hv, dv, 128] bf16: the gradient of the state leaving it
+    uint16_t *ws_delta;     // [n_chunks, Hv, 64, dv] bf16: each chunk's Delta rows
+    uint16_t *ws_drhs;      // [n_chunks, Hv, 64, dv] bf16: each chunk's drhs rows
     int64_t T;              // tokens per row (batch mode)
     int64_t n_chunks;       // chunks the workspace holds (an upper bound with cu)
     int32_t Hqk, Hv, dk, dv;

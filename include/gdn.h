@@ -209,10 +209,10 @@ gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t 
 /*
  * Bytes of device workspace gdn_chunk_bwd needs for these sizes (0 for sizes
  * the backward would reject).  The workspace holds, per chunk of 64 tokens and
- * value head, the chunk's inverse (I + A)^-1 (fp32), its gated Q K^T (bf16),
- * its cumulative decay, and (in bf16) the state entering the chunk and the
- * gradient of the state leaving it, both 128 keys wide whatever dk is:
- * 2 * 128 * dv * 2 bytes + 24.25 KiB per chunk and head.
+ * value head, in bf16: the state entering the chunk and the gradient of the
+ * state leaving it (both 128 keys wide whatever dk is), and the chunk's Delta
+ * and drhs rows (the solved right-hand side of the forward and of its
+ * transpose): (2 * 128 + 2 * 64) * dv * 2 bytes per chunk and head.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  * With cu_seqlens the size covers any split of the T tokens into n_seqs

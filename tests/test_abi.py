@@ -184,8 +184,9 @@ def test_binding_checks_tensors_on_host():
 
 def test_bwd_workspace_size():
     ws = gdn.gdn_chunk_bwd_workspace_size
-    # 8 rows of 32 chunks, 16 heads: per chunk-head 64*64*4 + 64*64*2 + 64*4 + 2*128*128*2
-    per = 64 * 64 * 4 + 64 * 64 * 2 + 64 * 4 + 2 * 128 * 128 * 2
+    # 8 rows of 32 chunks, 16 heads: per chunk-head two bf16 states (dv x 128)
+    # and two bf16 row blocks (64 x dv)
+    per = 2 * 128 * 128 * 2 + 2 * 64 * 128 * 2
     assert ws(1, 8, 2048, 16, 16, 128, 128, 8) == 8 * 32 * 16 * per
     # one packed row of 5 documents: at most ceil(T / 64) + 5 chunks
     assert ws(1, 1, 2048, 16, 16, 128, 128, 5) == (32 + 5) * 16 * per
@@ -310,15 +311,17 @@ def test_packed_plan():
     import gdn_inputs as gi
     plan = gdn.gdn_chunk_fwd_plan
     # One row of 8 heads, ~16 geometric documents of mean 1024: all 256
-    # workgroups run at once, so whole documents (longest first) are best.
+    # workgroups run at once, so whole documents are best and their order
+    # does not matter (no ranking launch).
     cu = [int(x) for x in gi.cu_from_lengths(gi.geometric_lengths(16384, 1024, 1009))]
-    assert plan(1, 1, 16384, 8, 8, 128, 128, cu) == (0, 0, True)
+    assert len(cu) - 1 == 16
+    assert plan(1, 1, 16384, 8, 8, 128, 128, cu) == (0, 0, False)
     # One 20,000-token document among seven short ones at 8 heads: split.
     cu = [int(x) for x in gi.cu_from_lengths([20000, 2000, 1500, 3000, 900, 1100, 800, 700])]
     T = cu[-1]
     pl, slots, ordered = plan(1, 1, T, 8, 8, 128, 128, cu)
     _, budget, _ = plan(1, 1, T, 8, 8, 128, 128)
-    assert ordered and pl > 0 and pl % 64 == 0 and 0 < slots <= budget
+    assert pl > 0 and pl % 64 == 0 and 0 < slots <= budget and not ordered
     assert slots == sum(max(0, -(-(b - a) // pl) - 1) for a, b in zip(cu, cu[1:]))
     # The 32-head packed workload fills the CUs: ordered, not split.
     cu = [int(x) for x in gi.cu_from_lengths(gi.geometric_lengths(16384, 1024, 1002))]
@@ -326,8 +329,9 @@ def test_packed_plan():
     # Short documents are never split, whatever the heads.
     cu = list(range(0, 20 * 500 + 1, 20))
     assert plan(1, 1, cu[-1], 1, 1, 128, 128, cu)[:2] == (0, 0)
-    # One document: nothing to order.
+    # One document: nothing to order; few workgroups: nothing gained by it.
     assert plan(1, 1, 5000, 1, 1, 128, 128, [0, 5000])[2] is False
+    assert plan(1, 1, 5000, 1, 1, 128, 128, [0, 1000, 5000])[2] is False
     # fp32: never split, never ordered.
     assert plan(0, 1, 16384, 8, 8, 128, 128, [0, 16000, 16384]) == (0, 0, False)
     # Without the host copy nothing is planned from lengths (batch rows).
