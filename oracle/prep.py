@@ -18,6 +18,10 @@ it).
         y = M^T k,  delta = beta (v - a y),  M <- a M + k delta^T,  o = scale M^T q.
     Chaining it over a sequence is pinned against gdn_fwd, the token-by-token
     oracle in C.
+  * l2_normalize_bwd, logsigmoid_bwd, sigmoid_bwd, chain_options -- the
+    reverse mode of the preparation (derivatives of the three maps, which the
+    pages do not print), so that the gradient of a forward that prepares its
+    inputs in-op can be taken with respect to the raw inputs.
 """
 import numpy as np
 
@@ -85,3 +89,48 @@ def step(q, k, v, g, beta, state, slots=None, scale=1.0, use_qk_l2norm=False,
             if cached:
                 new[s, j] = M
     return o, new
+
+
+# ---------------------------------------------------------------------------
+# Reverse mode of the preparation.  The pages state no gradients; these are
+# the derivatives of the three maps above, written out: each takes the raw
+# input x and the gradient dy of a loss with respect to the prepared value,
+# and returns the gradient with respect to x.
+
+def l2_normalize_bwd(x, dy):
+    """Through y = x / n, n = ||x||: the Jacobian is (I - y y^T) / n, so
+    dx = (dy - (dy . y) y) / n, row by row over the last axis.  A zero row,
+    mapped to the constant zero, gets a zero gradient."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    n = np.linalg.norm(x, axis=-1, keepdims=True)
+    safe = np.where(n > 0.0, n, 1.0)
+    y = x / safe
+    proj = np.sum(dy * y, axis=-1, keepdims=True)
+    return np.where(n > 0.0, (dy - proj * y) / safe, 0.0)
+
+
+def logsigmoid_bwd(x, dy):
+    """d logsigmoid(x) / dx = 1 - sigmoid(x) = sigmoid(-x)."""
+    return np.asarray(dy, np.float64) * sigmoid(-np.asarray(x, np.float64))
+
+
+def sigmoid_bwd(x, dy):
+    """d sigmoid(x) / dx = sigmoid(x) (1 - sigmoid(x)) = sigmoid(x) sigmoid(-x)."""
+    x = np.asarray(x, np.float64)
+    return np.asarray(dy, np.float64) * sigmoid(x) * sigmoid(-x)
+
+
+def chain_options(q, k, g, beta, dq, dk, dg, dbeta, use_qk_l2norm=False,
+                  gate_activation=False):
+    """Gradients with respect to the raw q, k, g, beta of a forward that
+    prepares its inputs in-op, from the gradients (dq, dk, dg, dbeta) with
+    respect to the prepared inputs the recurrence consumed.  An option that
+    is off passes its gradients through unchanged."""
+    dq, dk = np.asarray(dq, np.float64), np.asarray(dk, np.float64)
+    dg, dbeta = np.asarray(dg, np.float64), np.asarray(dbeta, np.float64)
+    if use_qk_l2norm:
+        dq, dk = l2_normalize_bwd(q, dq), l2_normalize_bwd(k, dk)
+    if gate_activation:
+        dg, dbeta = logsigmoid_bwd(g, dg), sigmoid_bwd(beta, dbeta)
+    return dq, dk, dg, dbeta

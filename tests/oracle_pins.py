@@ -553,3 +553,115 @@ PREP_PINS = [
     pin_l2_known_rows, pin_l2_unit_direction_scale, pin_gate_functions, pin_step_hand_worked,
     pin_step_chained_equals_token_oracle, pin_step_slots_and_padding, pin_step_options,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Reverse mode of the preparation (oracle/prep.py).  Same signature as the
+# preparation pins above.
+
+def pin_prep_bwd_closed_forms(P, fwd):
+    """Values by hand.  x = (3, 4), dy = (1, 0): y = (0.6, 0.8), dy . y = 0.6,
+    dx = ((1, 0) - 0.6 (0.6, 0.8)) / 5 = (0.128, -0.096).  logsigmoid'(0) =
+    1/2, sigmoid'(0) = 1/4, sigmoid'(ln 3) = (3/4)(1/4) = 3/16,
+    logsigmoid'(ln 3) = 1/4.  A zero row has a zero gradient."""
+    dx = P.l2_normalize_bwd(np.array([[3.0, 4.0], [0.0, 0.0]]), np.array([[1.0, 0.0], [1.0, 2.0]]))
+    assert np.allclose(dx, [[0.128, -0.096], [0.0, 0.0]], rtol=0, atol=1e-16), dx
+    assert abs(P.logsigmoid_bwd(0.0, 1.0) - 0.5) < 1e-16
+    assert abs(P.sigmoid_bwd(0.0, 1.0) - 0.25) < 1e-16
+    assert abs(P.sigmoid_bwd(math.log(3.0), 2.0) - 0.375) < 1e-16
+    assert abs(P.logsigmoid_bwd(math.log(3.0), 1.0) - 0.25) < 1e-16
+
+
+def pin_prep_bwd_invariants(P, fwd):
+    """The normalisation's gradient is orthogonal to x (moving along x does not
+    change x / |x|), scales as 1 / c under x -> c x, is linear in dy, and a dy
+    along x gives zero; sigmoid'(x) = sigmoid'(-x) and logsigmoid'(x) +
+    logsigmoid'(-x) = 1."""
+    rng = _rng(44)
+    x = rng.standard_normal((4, 3, 32))
+    dy = rng.standard_normal(x.shape)
+    dx = P.l2_normalize_bwd(x, dy)
+    assert np.allclose(np.sum(dx * x, axis=-1), 0.0, rtol=0, atol=1e-14), "not orthogonal to x"
+    assert np.allclose(P.l2_normalize_bwd(2.5 * x, dy), dx / 2.5, rtol=1e-14, atol=1e-16)
+    dy2 = rng.standard_normal(x.shape)
+    assert np.allclose(P.l2_normalize_bwd(x, dy + 3.0 * dy2),
+                       dx + 3.0 * P.l2_normalize_bwd(x, dy2), rtol=1e-13, atol=1e-14)
+    assert np.allclose(P.l2_normalize_bwd(x, 0.7 * x), 0.0, rtol=0, atol=1e-14)
+    t = np.linspace(-25.0, 25.0, 501)
+    one = np.ones_like(t)
+    assert np.allclose(P.sigmoid_bwd(t, one), P.sigmoid_bwd(-t, one), rtol=1e-14, atol=1e-300)
+    assert np.allclose(P.logsigmoid_bwd(t, one) + P.logsigmoid_bwd(-t, one), 1.0,
+                       rtol=0, atol=1e-15)
+
+
+def pin_prep_bwd_finite_differences(P, fwd):
+    """Each gradient equals the central difference of the forward map it
+    reverses (fp64, step 1e-6: truncation error ~1e-12, rounding ~1e-10)."""
+    rng = _rng(45)
+    x = rng.standard_normal((3, 12))
+    dy = rng.standard_normal(x.shape)
+    got = P.l2_normalize_bwd(x, dy)
+    h = 1e-6
+    fd = np.zeros(x.shape)
+    for idx in np.ndindex(x.shape):
+        xp = x.copy(); xp[idx] += h
+        xm = x.copy(); xm[idx] -= h
+        fd[idx] = (np.sum(dy * P.l2_normalize(xp)) - np.sum(dy * P.l2_normalize(xm))) / (2 * h)
+    _close(got, fd, 1e-8, "l2 normalisation gradient")
+    t = np.linspace(-12.0, 12.0, 97)
+    w = rng.standard_normal(t.shape)
+    for f, b, name in ((P.logsigmoid, P.logsigmoid_bwd, "logsigmoid"),
+                       (P.sigmoid, P.sigmoid_bwd, "sigmoid")):
+        fd = w * (f(t + h) - f(t - h)) / (2 * h)
+        _close(b(t, w), fd, 1e-8, f"{name} gradient")
+
+
+def pin_prep_bwd_chain_through_forward(P, fwd):
+    """The gradient of a forward that normalises q, k and activates raw gates
+    in-op, with respect to the raw inputs: the C oracle's reverse mode on the
+    prepared inputs, chained through chain_options, equals the central
+    difference of the whole composition (raw inputs -> preparation -> forward
+    -> loss).  The prepared values are not fp32 numbers, which the C oracle
+    takes, so both sides run the chunk-parallel numpy route (pinned to the C
+    oracle above) in fp64."""
+    from oracle import chunked
+    rng = _rng(46)
+    B, T, Hqk, Hv, dk, dv = 1, 9, 1, 2, 6, 4
+    q = rng.standard_normal((B, T, Hqk, dk)) * 2.0
+    k = rng.standard_normal((B, T, Hqk, dk)) * 0.5
+    v = rng.standard_normal((B, T, Hv, dv))
+    gr = rng.standard_normal((B, T, Hv)) + 2.0
+    br = rng.standard_normal((B, T, Hv))
+    do = rng.standard_normal((B, T, Hv, dv))
+    h0 = rng.standard_normal((B, Hv, dk, dv)) * 0.3
+    dht = rng.standard_normal((B, Hv, dk, dv))
+
+    def prepared(q_, k_, g_, b_):
+        return P.l2_normalize(q_), P.l2_normalize(k_), P.logsigmoid(g_), P.sigmoid(b_)
+
+    def loss(q_, k_, g_, b_):
+        qn, kn, gn, bn = prepared(q_, k_, g_, b_)
+        o, ht = chunked.fwd(qn, kn, v, gn, bn, 4, scale=0.9, h0=h0)
+        return float(np.sum(do * o) + np.sum(dht * ht))
+
+    qn, kn, gn, bn = prepared(q, k, gr, br)
+    dqn, dkn, _, dgn, dbn, _ = chunked.bwd(qn, kn, v, gn, bn, do, 4, scale=0.9, h0=h0, dht=dht)
+    got = P.chain_options(q, k, gr, br, dqn, dkn, dgn, dbn, use_qk_l2norm=True,
+                          gate_activation=True)
+    base = [q, k, gr, br]
+    h = 1e-6
+    for i, name in enumerate(("q", "k", "g", "beta")):
+        fd = np.zeros(base[i].shape)
+        for idx in np.ndindex(base[i].shape):
+            args = list(base)
+            xp = base[i].copy(); xp[idx] += h; args[i] = xp
+            lp = loss(*args)
+            xm = base[i].copy(); xm[idx] -= h; args[i] = xm
+            fd[idx] = (lp - loss(*args)) / (2 * h)
+        _close(got[i], fd, 1e-7, f"d{name} through the preparation")
+
+
+PREP_BWD_PINS = [
+    pin_prep_bwd_closed_forms, pin_prep_bwd_invariants, pin_prep_bwd_finite_differences,
+    pin_prep_bwd_chain_through_forward,
+]

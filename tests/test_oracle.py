@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from oracle import prep
-from oracle_pins import ALL_PINS, BWD_PINS, PREP_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, PREP_BWD_PINS, PREP_PINS
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -20,6 +20,11 @@ def test_oracle_bwd_pin(pin):
 
 @pytest.mark.parametrize("pin", PREP_PINS, ids=lambda p: p.__name__)
 def test_oracle_prep_pin(pin):
+    pin(prep, oracle.gdn_fwd)
+
+
+@pytest.mark.parametrize("pin", PREP_BWD_PINS, ids=lambda p: p.__name__)
+def test_oracle_prep_bwd_pin(pin):
     pin(prep, oracle.gdn_fwd)
 
 

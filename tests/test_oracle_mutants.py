@@ -137,13 +137,27 @@ PREP_MUTANTS = {
                                 "g, beta = sigmoid(g), sigmoid(beta)"),
     "step_l2_keys_only": ("q, k = l2_normalize(q), l2_normalize(k)",
                           "q, k = q, l2_normalize(k)"),
+    "l2_bwd_no_projection": ("return np.where(n > 0.0, (dy - proj * y) / safe, 0.0)",
+                             "return np.where(n > 0.0, dy / safe, 0.0)"),
+    "l2_bwd_not_divided_by_norm": ("return np.where(n > 0.0, (dy - proj * y) / safe, 0.0)",
+                                   "return np.where(n > 0.0, dy - proj * y, 0.0)"),
+    "l2_bwd_projects_on_raw_row": ("proj = np.sum(dy * y, axis=-1, keepdims=True)",
+                                   "proj = np.sum(dy * x, axis=-1, keepdims=True)"),
+    "logsigmoid_bwd_wrong_sign": ("np.asarray(dy, np.float64) * sigmoid(-np.asarray(x, np.float64))",
+                                  "np.asarray(dy, np.float64) * sigmoid(np.asarray(x, np.float64))"),
+    "sigmoid_bwd_one_factor": ("np.asarray(dy, np.float64) * sigmoid(x) * sigmoid(-x)",
+                               "np.asarray(dy, np.float64) * sigmoid(x)"),
+    "chain_gates_swapped": ("dg, dbeta = logsigmoid_bwd(g, dg), sigmoid_bwd(beta, dbeta)",
+                            "dg, dbeta = sigmoid_bwd(g, dg), logsigmoid_bwd(beta, dbeta)"),
+    "chain_keys_use_query_rows": ("dq, dk = l2_normalize_bwd(q, dq), l2_normalize_bwd(k, dk)",
+                                  "dq, dk = l2_normalize_bwd(q, dq), l2_normalize_bwd(q, dk)"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(PREP_MUTANTS))
 def test_prep_pins_catch_mutant(name):
     import types
-    from oracle_pins import PREP_PINS
+    from oracle_pins import PREP_BWD_PINS, PREP_PINS
     old, new = PREP_MUTANTS[name]
     with open(PREP_SRC) as f:
         src = f.read()
@@ -151,7 +165,7 @@ def test_prep_pins_catch_mutant(name):
     mod = types.ModuleType(f"prep_{name}")
     exec(compile(src.replace(old, new), f"prep_{name}.py", "exec"), mod.__dict__)
     caught = []
-    for pin in PREP_PINS:
+    for pin in PREP_PINS + PREP_BWD_PINS:
         try:
             pin(mod, oracle.gdn_fwd)
         except (AssertionError, IndexError, ValueError):
