@@ -133,9 +133,19 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup, name="fwd_bwd_bf16", with_fw
            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                         "algorithmic_bytes_per_call": nbytes,
-                        "kernels": ["bwd_prep", f"gdn_fwd_bf16<false, 3, {dk}>", "bwd_dstate",
-                                    "bwd_chunk"]},
+                        "kernels": [f"gdn_fwd_bf16<false, 3, {dk}>",
+                                    f"gdn_fwd_bf16<false, 4, {dk}>", "bwd_grads"]},
            "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
+    # The same inputs taken as raw ones, with both in-op options: the
+    # preparation into the workspace, the backward, the chain back through it.
+    ws_opt = torch.empty(gdn.gdn_chunk_bwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B, 3),
+                         dtype=torch.uint8, device=dev)
+    opt_ms = _time_calls(torch, stream, lambda: gdn.gdn_chunk_bwd(
+        q, k, v, g, beta, dO, dht=dh, workspace=ws_opt, stream=stream.cuda_stream,
+        use_qk_l2norm=True, gate_activation=True), steps, warmup)
+    del ws_opt
+    log(f"[bench] backward ({name}) with both in-op options {opt_ms:.4f} ms/call")
+    res["ms_per_call_with_options"] = opt_ms
     if with_fwd:
         log(f"[bench] forward ({name}) {fwd_ms * 1e3:.1f} us/call; forward + backward "
             f"{B * T / ((fwd_ms + ms) * 1e-3):.3g} tokens/s")

@@ -61,14 +61,18 @@ def load():
     lib.gdn_chunk_fwd_noalloc.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P,
                                           P, ctypes.c_float, U32, P, P, P, I32, P, P, P]
     lib.gdn_chunk_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, I32,
+                                                 U32]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_chunk_bwd.argtypes = [ctypes.c_int, I64, I64, I32, I32, I32, I32, P, P, P, P, P,
-                                  ctypes.c_float, P, P, P, I32, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_float, U32, P, P, P, I32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
     lib.gdn_prepare_inputs.restype = ctypes.c_int
     lib.gdn_prepare_inputs.argtypes = [ctypes.c_int, I64, I32, P, P, P, P, I64, P, P, P, P,
                                        U32, P]
+    lib.gdn_prepare_inputs_bwd.restype = ctypes.c_int
+    lib.gdn_prepare_inputs_bwd.argtypes = [ctypes.c_int, I64, I32, P, P, P, P, P, P, I64, P, P,
+                                           P, P, P, P, U32, P]
     lib.gdn_recurrent_step.restype = ctypes.c_int
     lib.gdn_recurrent_step.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P,
                                        ctypes.c_float, U32, P, P, I64, P, P]
@@ -292,18 +296,22 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, scale=1.0, initial_state=None, cu_se
     return out, final_state
 
 
-def gdn_chunk_bwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs):
-    return load().gdn_chunk_bwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs)
+def gdn_chunk_bwd_workspace_size(dtype, B, T, H_qk, H_v, dk, dv, n_seqs, flags=0):
+    return load().gdn_chunk_bwd_workspace_size(int(dtype), B, T, H_qk, H_v, dk, dv, n_seqs,
+                                               int(flags))
 
 
 def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
-                  cu_seqlens=None, cu_seqlens_host=None, workspace=None, stream=None):
+                  cu_seqlens=None, cu_seqlens_host=None, workspace=None, stream=None,
+                  use_qk_l2norm=False, gate_activation=False):
     """dq, dk, dv, dg, dbeta, dh0 = gdn_chunk_bwd(q, k, v, g, beta, do, ...):
     the gradients of sum(do * o) + sum(dht * ht) for the forward with the same
     arguments, on the current HIP stream.  do: [B, T, H_v, dv] in the dtype of
     q; dht: [N, H_v, dk, dv] fp32 or None.  dq, dk, dv come back in the input
-    dtype, dg, dbeta and dh0 in fp32.  The workspace (bytes from
-    gdn_chunk_bwd_workspace_size) is allocated here unless given."""
+    dtype, dg, dbeta and dh0 in fp32.  With use_qk_l2norm / gate_activation
+    the inputs are raw, as for gdn_chunk_fwd, and so are the gradients.  The
+    workspace (bytes from gdn_chunk_bwd_workspace_size with the same options)
+    is allocated here unless given."""
     import torch
     lib = load()
     dt, B, T, Hqk, Hv, dk, dv, N, host_arr = _check_inputs(
@@ -320,7 +328,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
     dg = torch.empty_like(g)
     dbeta = torch.empty_like(beta)
     dh0 = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
-    ws_bytes = lib.gdn_chunk_bwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N)
+    flags = _flags(use_qk_l2norm, gate_activation)
+    ws_bytes = lib.gdn_chunk_bwd_workspace_size(dt, B, T, Hqk, Hv, dk, dv, N, flags)
     ws_len = 0
     if workspace is None:
         if ws_bytes:
@@ -332,7 +341,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, do, dht=None, scale=1.0, initial_state=None,
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
     st = lib.gdn_chunk_bwd(dt, B, T, Hqk, Hv, dk, dv, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
-                           float(scale), ptr(initial_state), ptr(cu_seqlens),
+                           float(scale), flags, ptr(initial_state), ptr(cu_seqlens),
                            None if host_arr is None else ctypes.cast(host_arr, ctypes.c_void_p),
                            N if cu_seqlens is not None else 0, ptr(do), ptr(dht), ptr(dq),
                            ptr(dk_), ptr(dv_), ptr(dg), ptr(dbeta), ptr(dh0), ptr(workspace),
@@ -382,6 +391,47 @@ def gdn_prepare_inputs(q, k, g, beta, use_qk_l2norm=True, gate_activation=False,
     st = lib.gdn_prepare_inputs(dt, q.numel() // max(dk, 1), dk, q.data_ptr(), k.data_ptr(),
                                 qo.data_ptr(), ko.data_ptr(), g.numel(), g.data_ptr(),
                                 beta.data_ptr(), go.data_ptr(), bo.data_ptr(), flags, stream)
+    if st != 0:
+        _raise(st)
+    return qo, ko, go, bo
+
+
+def gdn_prepare_inputs_bwd(q, k, g, beta, dq, dk, dg, dbeta, use_qk_l2norm=True,
+                           gate_activation=False, in_place=False, stream=None):
+    """(dq', dk', dg', dbeta'): the gradients with respect to the raw q, k, g,
+    beta of gdn_prepare_inputs with the same options, from dq, dk, dg, dbeta,
+    the gradients with respect to its outputs.  Shapes and dtypes as for
+    gdn_prepare_inputs (dq, dk like q; dg, dbeta fp32 like g).  What an
+    option does not touch is returned as given."""
+    import torch
+    lib = load()
+    _device_contiguous(torch, [("q", q), ("k", k), ("g", g), ("beta", beta), ("dq", dq),
+                               ("dk", dk), ("dg", dg), ("dbeta", dbeta)])
+    dt = _dtype_code(torch, q.dtype)
+    for name, t in (("k", k), ("dq", dq), ("dk", dk)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise GdnError(1, f"{name} must match q in shape and dtype")
+    for name, t in (("beta", beta), ("dg", dg), ("dbeta", dbeta)):
+        if t.dtype != torch.float32 or g.dtype != torch.float32 or t.shape != g.shape:
+            raise GdnError(1, f"g and {name} must be fp32 of one shape")
+    devs = {t.device for t in (q, k, g, beta, dq, dk, dg, dbeta)}
+    if len(devs) != 1:
+        raise GdnError(1, "all tensors must be on one device")
+    flags = _flags(use_qk_l2norm, gate_activation)
+    qo, ko, go, bo = dq, dk, dg, dbeta
+    if use_qk_l2norm and not in_place:
+        qo, ko = torch.empty_like(dq), torch.empty_like(dk)
+    if gate_activation and not in_place:
+        go, bo = torch.empty_like(dg), torch.empty_like(dbeta)
+    if not flags:
+        return qo, ko, go, bo
+    d = q.shape[-1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.gdn_prepare_inputs_bwd(dt, q.numel() // max(d, 1), d, q.data_ptr(), k.data_ptr(),
+                                    dq.data_ptr(), dk.data_ptr(), qo.data_ptr(), ko.data_ptr(),
+                                    g.numel(), g.data_ptr(), beta.data_ptr(), dg.data_ptr(),
+                                    dbeta.data_ptr(), go.data_ptr(), bo.data_ptr(), flags, stream)
     if st != 0:
         _raise(st)
     return qo, ko, go, bo

@@ -438,24 +438,45 @@ static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N) {
     return packed ? per_row + N : B * per_row;
 }
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace bytes after the backward's own for the prepared copies of the
+// inputs an option rewrites: q and k in bf16, g and beta in fp32.
+static size_t bwd_prep_bytes(uint32_t flags, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
+                             int32_t dk) {
+    size_t n = 0;
+    if (flags & GDN_QK_L2NORM)
+        n += 2 * round256((size_t)B * (size_t)T * (size_t)H_qk * (size_t)dk * 2);
+    if (flags & GDN_GATE_ACT)
+        n += 2 * round256((size_t)B * (size_t)T * (size_t)H_v * 4);
+    return n;
+}
+
 size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
-                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs) {
+                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs,
+                                    uint32_t flags) {
     if (!bwd_supported(dtype, dk, dv) || B < 1 || T < 1 || H_qk < 1 || H_v < 1 ||
-        H_v % H_qk != 0 || n_seqs < 1)
+        H_v % H_qk != 0 || n_seqs < 1 || (flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
+        return 0;
+    if (B > INT64_MAX / T || B * T > INT64_MAX / ((int64_t)(H_v > H_qk ? H_v : H_qk) * 256))
         return 0;
     // Packed documents need B == 1; the packed bound also covers one row.
     return gdn::bwd_workspace_bytes(bwd_chunks(B, T, B == 1, B == 1 ? n_seqs : (int32_t)B), H_v,
-                                    dk, dv);
+                                    dk, dv) +
+           bwd_prep_bytes(flags, B, T, H_qk, H_v, dk);
 }
 
 gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
                          int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float scale, const float *h0,
-                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                         int32_t n_seqs, const void *dout, const float *dht, void *dq,
-                         void *dk_, void *dv_, float *dg, float *dbeta, float *dh0,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                         const float *g, const float *beta, float scale, uint32_t flags,
+                         const float *h0, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t n_seqs, const void *dout,
+                         const float *dht, void *dq, void *dk_, void *dv_, float *dg,
+                         float *dbeta, float *dh0, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
     if (B < 1 || T < 1 || H_qk < 1 || H_v < 1 || dk < 1 || dv < 1)
+        return GDN_ERR_INVALID_ARG;
+    if ((flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
         return GDN_ERR_INVALID_ARG;
     if (!q || !k || !v || !g || !beta || !dout || !dq || !dk_ || !dv_ || !dg || !dbeta)
         return GDN_ERR_INVALID_ARG;
@@ -492,18 +513,62 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     const int64_t n_chunks = bwd_chunks(B, T, cu_seqlens != nullptr, N);
     if (n_chunks > INT32_MAX)
         return GDN_ERR_INVALID_ARG;
-    const size_t need = gdn::bwd_workspace_bytes(n_chunks, H_v, dk, dv);
+    const size_t own = gdn::bwd_workspace_bytes(n_chunks, H_v, dk, dv);
+    const size_t need = own + bwd_prep_bytes(flags, B, T, H_qk, H_v, dk);
     if (!workspace || workspace_bytes < need)
         return GDN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return GDN_ERR_MISALIGNED;
 
+    // With an option set, the prepared inputs go to the end of the workspace,
+    // the backward runs on them, and the chain through the preparation then
+    // rewrites dq, dk, dg and dbeta in place.
+    const bool l2 = flags & GDN_QK_L2NORM, gate = flags & GDN_GATE_ACT;
+    const int64_t qk_rows = B * T * H_qk, gates = B * T * H_v;
+    const void *qp = q, *kp = k;
+    const float *gp = g, *bp = beta;
+    if (flags) {
+        unsigned char *w = static_cast<unsigned char *>(workspace) + own;
+        gdn::PrepArgs p;
+        p.q = q;
+        p.k = k;
+        p.g = g;
+        p.beta = beta;
+        p.q_out = p.k_out = nullptr;
+        p.g_out = p.beta_out = nullptr;
+        if (l2) {
+            const size_t rows_bytes = round256((size_t)qk_rows * (size_t)dk * 2);
+            p.q_out = w;
+            p.k_out = w + rows_bytes;
+            w += 2 * rows_bytes;
+            qp = p.q_out;
+            kp = p.k_out;
+        }
+        if (gate) {
+            const size_t gate_bytes = round256((size_t)gates * 4);
+            p.g_out = reinterpret_cast<float *>(w);
+            p.beta_out = reinterpret_cast<float *>(w + gate_bytes);
+            gp = p.g_out;
+            bp = p.beta_out;
+        }
+        p.qk_rows = l2 ? qk_rows : 0;
+        p.gate_n = gate ? gates : 0;
+        p.dk = dk;
+        p.flags = flags;
+        p.bf16 = true;
+        const hipError_t e = gdn::launch_preprocess(p, stream);
+        if (e != hipSuccess) {
+            g_last_hip_error = e;
+            return GDN_ERR_HIP;
+        }
+    }
+
     gdn::BwdArgs a;
-    a.q = q;
-    a.k = k;
+    a.q = qp;
+    a.k = kp;
     a.v = v;
-    a.g = g;
-    a.beta = beta;
+    a.g = gp;
+    a.beta = bp;
     a.h0 = h0;
     a.cu = cu_seqlens;
     a.dout = dout;
@@ -523,7 +588,24 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     a.n_seqs = N;
     a.scale = scale;
     gdn::bwd_carve(a, workspace);
-    const hipError_t e = gdn::launch_bwd_bf16(a, stream);
+    hipError_t e = gdn::launch_bwd_bf16(a, stream);
+    if (e == hipSuccess && flags) {
+        gdn::PrepBwdArgs c;
+        c.q = q;
+        c.k = k;
+        c.dq = c.dq_out = dq;
+        c.dk = c.dk_out = dk_;
+        c.g = g;
+        c.beta = beta;
+        c.dg = c.dg_out = dg;
+        c.dbeta = c.dbeta_out = dbeta;
+        c.qk_rows = l2 ? qk_rows : 0;
+        c.gate_n = gate ? gates : 0;
+        c.dk_dim = dk;
+        c.flags = flags;
+        c.bf16 = true;
+        e = gdn::launch_preprocess_bwd(c, stream);
+    }
     if (e != hipSuccess) {
         g_last_hip_error = e;
         return GDN_ERR_HIP;
@@ -576,6 +658,65 @@ gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, co
     a.flags = flags;
     a.bf16 = dtype == GDN_BF16;
     const hipError_t e = gdn::launch_preprocess(a, stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+gdn_status gdn_prepare_inputs_bwd(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk,
+                                  const void *q, const void *k, const void *dq_in,
+                                  const void *dk_in, void *dq_out, void *dk_out,
+                                  int64_t n_gates, const float *g, const float *beta,
+                                  const float *dg_in, const float *dbeta_in, float *dg_out,
+                                  float *dbeta_out, uint32_t flags, hipStream_t stream) {
+    if ((flags & ~(GDN_QK_L2NORM | GDN_GATE_ACT)) != 0)
+        return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return GDN_ERR_UNSUPPORTED;
+    const bool l2 = flags & GDN_QK_L2NORM, gate = flags & GDN_GATE_ACT;
+    if (l2) {
+        if (n_qk_rows < 0 || n_qk_rows > INT64_MAX / 256 || dk < 1)
+            return GDN_ERR_INVALID_ARG;
+        if (dk > 256)
+            return GDN_ERR_UNSUPPORTED;
+    }
+    if (gate && (n_gates < 0 || n_gates > INT64_MAX / 2))
+        return GDN_ERR_INVALID_ARG;
+    if (l2 && n_qk_rows > 0) {
+        if (!q || !k || !dq_in || !dk_in || !dq_out || !dk_out)
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(dq_in) || !aligned16(dk_in) ||
+            !aligned16(dq_out) || !aligned16(dk_out))
+            return GDN_ERR_MISALIGNED;
+    }
+    if (gate && n_gates > 0) {
+        if (!g || !beta || !dg_in || !dbeta_in || !dg_out || !dbeta_out)
+            return GDN_ERR_INVALID_ARG;
+        if (!aligned16(g) || !aligned16(beta) || !aligned16(dg_in) || !aligned16(dbeta_in) ||
+            !aligned16(dg_out) || !aligned16(dbeta_out))
+            return GDN_ERR_MISALIGNED;
+    }
+    gdn::PrepBwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.dq = dq_in;
+    a.dk = dk_in;
+    a.dq_out = dq_out;
+    a.dk_out = dk_out;
+    a.g = g;
+    a.beta = beta;
+    a.dg = dg_in;
+    a.dbeta = dbeta_in;
+    a.dg_out = dg_out;
+    a.dbeta_out = dbeta_out;
+    a.qk_rows = l2 ? n_qk_rows : 0;
+    a.gate_n = gate ? n_gates : 0;
+    a.dk_dim = dk;
+    a.flags = flags;
+    a.bf16 = dtype == GDN_BF16;
+    const hipError_t e = gdn::launch_preprocess_bwd(a, stream);
     if (e != hipSuccess) {
         g_last_hip_error = e;
         return GDN_ERR_HIP;

@@ -180,4 +180,29 @@ struct PrepArgs {
 
 hipError_t launch_preprocess(const PrepArgs &a, hipStream_t stream);
 
+// The reverse of the preparation: gradients with respect to the raw q, k, g
+// and beta from those with respect to the prepared values.  Outputs may be
+// their gradient inputs (in place).
+struct PrepBwdArgs {
+    const void *q;          // raw rows
+    const void *k;
+    const void *dq;         // gradients with respect to the normalised rows
+    const void *dk;
+    void *dq_out;
+    void *dk_out;
+    const float *g;         // raw gates
+    const float *beta;
+    const float *dg;        // gradients with respect to the activated gates
+    const float *dbeta;
+    float *dg_out;
+    float *dbeta_out;
+    int64_t qk_rows;
+    int64_t gate_n;
+    int32_t dk_dim;
+    uint32_t flags;
+    bool bf16;
+};
+
+hipError_t launch_preprocess_bwd(const PrepBwdArgs &a, hipStream_t stream);
+
 }  // namespace gdn

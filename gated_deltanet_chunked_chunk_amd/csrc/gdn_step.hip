@@ -21,6 +21,11 @@
 // stored back in the input dtype.  Rows whose size is a power-of-two number
 // of 16-byte pieces are spread over that many lanes, several rows in flight
 // per wave; other sizes take one wave per row.
+//
+// The reverse of the preparation, with the same row layout: for y = x / n,
+// n = ||x||, dx = (dy - (dy . y) y) / n (a zero row gets zero); for the gates
+// d logsigmoid(x) = sigmoid(-x) and d sigmoid(x) = sigmoid(x) sigmoid(-x).
+// Both row sums (x . x and dy . x) come from one read of the two rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -280,6 +285,152 @@ __global__ __launch_bounds__(256) void preprocess_vec(PrepArgs a) {
     }
 }
 
+// Reverse of the gate activations, one gate per thread.
+__device__ __forceinline__ void gates_bwd(const PrepBwdArgs &a, int64_t i) {
+    if (i < a.gate_n) {
+        const float b = a.beta[i];
+        a.dg_out[i] = a.dg[i] * sigmoid_f32(-a.g[i]);
+        a.dbeta_out[i] = a.dbeta[i] * (sigmoid_f32(b) * sigmoid_f32(-b));
+    }
+}
+
+// Gradient of one normalised row: with inv = 1 / n and p = (dy . x) inv, the
+// projection dy . y, dx = inv (dy - p inv x).
+__device__ __forceinline__ float l2_bwd_el(float x, float dy, float inv, float p) {
+    return inv * fmaf(-p * inv, x, dy);
+}
+
+// One wave per row (any dk up to 256).
+__global__ __launch_bounds__(256) void preprocess_bwd(PrepBwdArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bool bf = a.bf16;
+    if (wave < 2 * a.qk_rows && (a.flags & kStepL2Norm)) {
+        const bool isq = wave >= a.qk_rows;
+        const int64_t row = isq ? wave - a.qk_rows : wave;
+        const void *xs = isq ? a.q : a.k;
+        const void *ds = isq ? a.dq : a.dk;
+        void *dst = isq ? a.dq_out : a.dk_out;
+        float x[4], d[4], s = 0.0f, t = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = lane + 64 * u;
+            x[u] = i < a.dk_dim ? load_el(xs, row * a.dk_dim + i, bf) : 0.0f;
+            d[u] = i < a.dk_dim ? load_el(ds, row * a.dk_dim + i, bf) : 0.0f;
+            s = fmaf(x[u], x[u], s);
+            t = fmaf(d[u], x[u], t);
+        }
+        for (int o = 32; o >= 1; o >>= 1) {
+            s += __shfl_xor(s, o);
+            t += __shfl_xor(t, o);
+        }
+        const float inv = inv_l2_norm(s);
+        const float p = t * inv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = lane + 64 * u;
+            if (i < a.dk_dim)
+                store_el(dst, row * a.dk_dim + i, l2_bwd_el(x[u], d[u], inv, p), bf);
+        }
+    }
+    if (a.flags & kStepGateAct)
+        gates_bwd(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// 16-byte pieces, as preprocess_vec: a row on Lpr lanes, kPrepGroups groups
+// of rows per wave with all of their loads issued before any reduction.
+template <int Lpr, bool Bf16>
+__global__ __launch_bounds__(256) void preprocess_bwd_vec(PrepBwdArgs a) {
+    constexpr int kRowsPerWave = 64 / Lpr;
+    constexpr int kPer = Bf16 ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (a.flags & kStepL2Norm) {
+        const int64_t total = 2 * a.qk_rows;
+        u32x4 x[kPrepGroups], d[kPrepGroups];
+        int64_t rows[kPrepGroups];
+#pragma unroll
+        for (int u = 0; u < kPrepGroups; ++u) {
+            rows[u] = (wave * kPrepGroups + u) * kRowsPerWave + lane / Lpr;
+            if (rows[u] < total) {
+                const bool isq = rows[u] >= a.qk_rows;
+                const int64_t r = isq ? rows[u] - a.qk_rows : rows[u];
+                const int64_t at = r * Lpr + lane % Lpr;
+                x[u] = reinterpret_cast<const u32x4 *>(isq ? a.q : a.k)[at];
+                d[u] = reinterpret_cast<const u32x4 *>(isq ? a.dq : a.dk)[at];
+            } else {
+                x[u] = u32x4{0u, 0u, 0u, 0u};
+                d[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPrepGroups; ++u) {
+            float fx[kPer], fd[kPer];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (Bf16) {
+                    fx[2 * e] = __uint_as_float(x[u][e] << 16);
+                    fx[2 * e + 1] = __uint_as_float(x[u][e] & 0xffff0000u);
+                    fd[2 * e] = __uint_as_float(d[u][e] << 16);
+                    fd[2 * e + 1] = __uint_as_float(d[u][e] & 0xffff0000u);
+                } else {
+                    fx[e] = __uint_as_float(x[u][e]);
+                    fd[e] = __uint_as_float(d[u][e]);
+                }
+            }
+            float s = 0.0f, t = 0.0f;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                s = fmaf(fx[e], fx[e], s);
+                t = fmaf(fd[e], fx[e], t);
+            }
+#pragma unroll
+            for (int o = Lpr / 2; o >= 1; o >>= 1) {
+                s += __shfl_xor(s, o);
+                t += __shfl_xor(t, o);
+            }
+            const float inv = inv_l2_norm(s);
+            const float p = t * inv;
+            u32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                y[e] = Bf16 ? pack_bf16x2(l2_bwd_el(fx[2 * e], fd[2 * e], inv, p),
+                                          l2_bwd_el(fx[2 * e + 1], fd[2 * e + 1], inv, p))
+                            : __float_as_uint(l2_bwd_el(fx[e], fd[e], inv, p));
+            if (rows[u] < total) {
+                const bool isq = rows[u] >= a.qk_rows;
+                const int64_t r = isq ? rows[u] - a.qk_rows : rows[u];
+                reinterpret_cast<u32x4 *>(isq ? a.dq_out : a.dk_out)[r * Lpr + lane % Lpr] = y;
+            }
+        }
+    }
+    if (a.flags & kStepGateAct)
+        gates_bwd(a, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// Blocks of 256 threads covering `rows` rows at `rows_per_block` and the
+// gates at one per thread; 0 when there is nothing to do, -1 past the grid.
+int64_t prep_blocks(int64_t rows, int64_t rows_per_block, int64_t gates) {
+    const int64_t by_rows = (rows + rows_per_block - 1) / rows_per_block;
+    const int64_t by_gates = (gates + 255) / 256;
+    const int64_t blocks = by_rows > by_gates ? by_rows : by_gates;
+    return blocks > 0x7fffffff ? -1 : blocks;
+}
+
+template <int Lpr, bool Bf16>
+hipError_t launch_bwd_vec(const PrepBwdArgs &a, hipStream_t stream) {
+    const int64_t rows = (a.flags & kStepL2Norm) ? 2 * a.qk_rows : 0;
+    const int64_t gates = (a.flags & kStepGateAct) ? a.gate_n : 0;
+    const int64_t blocks = prep_blocks(rows, 4 * kPrepGroups * (64 / Lpr), gates);
+    if (blocks == 0)
+        return hipSuccess;
+    if (blocks < 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((preprocess_bwd_vec<Lpr, Bf16>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
 template <int Lpr, bool Bf16>
 hipError_t launch_vec(const PrepArgs &a, hipStream_t stream) {
     constexpr int64_t kRowsPerBlock = 4 * kPrepGroups * (64 / Lpr);
@@ -342,6 +493,36 @@ hipError_t launch_preprocess(const PrepArgs &a, hipStream_t stream) {
     if (blocks > 0x7fffffff)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(preprocess, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_preprocess_bwd(const PrepBwdArgs &a, hipStream_t stream) {
+    const int row_bytes = a.dk_dim * (a.bf16 ? 2 : 4);
+    const int lpr = row_bytes % 16 == 0 ? row_bytes / 16 : 0;
+    if (a.bf16) {
+        switch (lpr) {
+        case 4: return launch_bwd_vec<4, true>(a, stream);
+        case 8: return launch_bwd_vec<8, true>(a, stream);
+        case 16: return launch_bwd_vec<16, true>(a, stream);
+        case 32: return launch_bwd_vec<32, true>(a, stream);
+        }
+    } else {
+        switch (lpr) {
+        case 4: return launch_bwd_vec<4, false>(a, stream);
+        case 8: return launch_bwd_vec<8, false>(a, stream);
+        case 16: return launch_bwd_vec<16, false>(a, stream);
+        case 32: return launch_bwd_vec<32, false>(a, stream);
+        case 64: return launch_bwd_vec<64, false>(a, stream);
+        }
+    }
+    const int64_t rows = (a.flags & kStepL2Norm) ? 2 * a.qk_rows : 0;
+    const int64_t gates = (a.flags & kStepGateAct) ? a.gate_n : 0;
+    const int64_t blocks = prep_blocks(rows, 4, gates);
+    if (blocks == 0)
+        return hipSuccess;
+    if (blocks < 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(preprocess_bwd, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

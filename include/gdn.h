@@ -216,10 +216,14 @@ gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t 
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  * With cu_seqlens the size covers any split of the T tokens into n_seqs
- * documents.
+ * documents.  flags: those gdn_chunk_bwd will get; each option adds room for
+ * the prepared copies of the inputs it rewrites (q and k in bf16 for
+ * GDN_QK_L2NORM, g and beta in fp32 for GDN_GATE_ACT, each region rounded up
+ * to 256 bytes).  Unknown flag bits give 0.
  */
 size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk,
-                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs);
+                                    int32_t H_v, int32_t dk, int32_t dv, int32_t n_seqs,
+                                    uint32_t flags);
 
 /*
  * The chunked backward: the gradients of L = sum(do * o) + sum(dht * ht) with
@@ -233,6 +237,15 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *                as for gdn_chunk_fwd.  Supported: bf16 with dk in {64, 128}
  *                and dv in {64, 128, 256}; everything else returns
  *                GDN_ERR_UNSUPPORTED.
+ *   flags        the in-op preparation of the forward (GDN_QK_L2NORM,
+ *                GDN_GATE_ACT, as for gdn_chunk_fwd): q, k, g and beta are
+ *                then the raw inputs, and dq, dk_, dg, dbeta come back with
+ *                respect to them.  The call prepares copies of the inputs in
+ *                the workspace (as gdn_prepare_inputs does), runs the
+ *                backward on them, and chains the gradients through the
+ *                preparation in place (as gdn_prepare_inputs_bwd does); with
+ *                an option set every token of those four outputs is
+ *                written.  Unknown bits return GDN_ERR_INVALID_ARG.
  *   dout         [B, T, H_v, dv] upstream gradient of o, dtype `dtype`.
  *   dht          [N, H_v, dk, dv] fp32 upstream gradient of the final state,
  *                or NULL for none.
@@ -243,8 +256,8 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *   dh0          [N, H_v, dk, dv] fp32 output (the gradient of the initial
  *                state; equal to dht for an empty document), or NULL.
  *   workspace    device scratch of at least gdn_chunk_bwd_workspace_size()
- *                bytes, 256-byte aligned, owned by the caller; its contents
- *                are undefined afterwards.
+ *                bytes (for the same flags), 256-byte aligned, owned by the
+ *                caller; its contents are undefined afterwards.
  *   stream       HIP stream to enqueue on.
  *
  * Every pointer must be 16-byte aligned; outputs must not overlap inputs or
@@ -253,11 +266,12 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  */
 gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, int32_t H_v,
                          int32_t dk, int32_t dv, const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float scale, const float *h0,
-                         const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
-                         int32_t n_seqs, const void *dout, const float *dht, void *dq,
-                         void *dk_, void *dv_, float *dg, float *dbeta, float *dh0,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+                         const float *g, const float *beta, float scale, uint32_t flags,
+                         const float *h0, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t n_seqs, const void *dout,
+                         const float *dht, void *dq, void *dk_, void *dv_, float *dg,
+                         float *dbeta, float *dh0, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * The input preparation the jax-linear-attention page's "Quick start" call
@@ -287,6 +301,37 @@ gdn_status gdn_prepare_inputs(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk, co
                               const void *k, void *q_out, void *k_out, int64_t n_gates,
                               const float *g, const float *beta, float *g_out,
                               float *beta_out, uint32_t flags, hipStream_t stream);
+
+/*
+ * The reverse of gdn_prepare_inputs: from the gradients of a loss with
+ * respect to the prepared values, those with respect to the raw inputs.  The
+ * pages print no gradients; these are the derivatives of the three maps:
+ *
+ *   GDN_QK_L2NORM  y = x / n, n = ||x||_2:  dx = (dy - (dy . y) y) / n, per
+ *                  row of dk elements (a row of zeros gets zeros), in fp32
+ *                  with the norm as gdn_prepare_inputs takes it, the result
+ *                  rounded to `dtype` (round to nearest even).
+ *   GDN_GATE_ACT   g' = logsigmoid(g):  dg = dg' sigmoid(-g);
+ *                  beta' = sigmoid(beta):  dbeta = dbeta' sigmoid(beta) sigmoid(-beta).
+ *
+ *   dtype, n_qk_rows, dk, n_gates, flags   as for gdn_prepare_inputs.
+ *   q, k         the raw rows [n_qk_rows, dk], dtype `dtype`.
+ *   dq_in, dk_in gradients with respect to the normalised rows, same shape
+ *                and dtype; dq_out, dk_out: the results.
+ *   g, beta      the raw gates [n_gates] fp32; dg_in, dbeta_in: gradients
+ *                with respect to the activated gates; dg_out, dbeta_out: the
+ *                results (fp32).
+ *
+ * Each output may be its gradient input (in place); other overlaps are
+ * undefined.  The pointers of an option not set, or with no rows or gates,
+ * may be NULL.  Every pointer must be 16-byte aligned.
+ */
+gdn_status gdn_prepare_inputs_bwd(gdn_dtype dtype, int64_t n_qk_rows, int32_t dk,
+                                  const void *q, const void *k, const void *dq_in,
+                                  const void *dk_in, void *dq_out, void *dk_out,
+                                  int64_t n_gates, const float *g, const float *beta,
+                                  const float *dg_in, const float *dbeta_in, float *dg_out,
+                                  float *dbeta_out, uint32_t flags, hipStream_t stream);
 
 /*
  * One token of the recurrence for each of N sequences (decoding), the state

@@ -195,16 +195,27 @@ def test_bwd_workspace_size():
     assert ws(1, 8, 2048, 16, 16, 64, 128, 8) == ws(1, 8, 2048, 16, 16, 128, 128, 8)
     assert ws(1, 8, 2048, 16, 16, 256, 128, 8) == 0   # dk = 256: no backward kernel
     assert ws(1, 1, 100, 1, 1, 128, 256, 1) > ws(1, 1, 100, 1, 1, 128, 128, 1)
+    # the in-op options add the prepared copies: q and k in bf16, g and beta in fp32
+    base = ws(1, 8, 2048, 16, 16, 128, 128, 8)
+    rows = 8 * 2048 * 16
+    assert ws(1, 8, 2048, 16, 16, 128, 128, 8, 1) == base + 2 * rows * 128 * 2
+    assert ws(1, 8, 2048, 16, 16, 128, 128, 8, 2) == base + 2 * rows * 4
+    assert ws(1, 8, 2048, 16, 16, 128, 128, 8, 3) == base + 2 * rows * 128 * 2 + 2 * rows * 4
+    # each region rounded up to 256 bytes: 3 tokens x 1 head x 4 bytes -> 256
+    assert ws(1, 1, 3, 1, 1, 128, 128, 1, 2) == ws(1, 1, 3, 1, 1, 128, 128, 1) + 2 * 256
+    assert ws(1, 8, 2048, 16, 16, 128, 128, 8, 4) == 0   # unknown option bit
 
 
 def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
              beta=FAKE, h0=None, cu=None, cu_host=None, n_seqs=0, do=FAKE, dht=None, dq=FAKE,
-             dk_=FAKE, dv_=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE, ws_bytes=1 << 40):
+             dk_=FAKE, dv_=FAKE, dg=FAKE, dbeta=FAKE, dh0=None, ws=FAKE, ws_bytes=1 << 40,
+             flags=0):
     lib = gdn.load()
     host = None
     if cu_host is not None:
         host = ctypes.cast((ctypes.c_int32 * len(cu_host))(*cu_host), ctypes.c_void_p)
-    return lib.gdn_chunk_bwd(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, h0, cu, host,
+    return lib.gdn_chunk_bwd(dtype, B, T, Hqk, Hv, dk, dv, q, k, v, g, beta, 1.0, flags, h0, cu,
+                             host,
                              n_seqs, do, dht, dq, dk_, dv_, dg, dbeta, dh0, ws, ws_bytes, None)
 
 
@@ -222,6 +233,7 @@ def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=
     (dict(cu=FAKE, n_seqs=2, B=2), INVALID),
     (dict(cu=FAKE, n_seqs=2, cu_host=[0, 10, 63]), INVALID),
     (dict(cu_host=[0, 64]), INVALID),
+    (dict(flags=4), INVALID), (dict(flags=0x80000002), INVALID),
 ])
 def test_bwd_rejects_before_launch(kw, status):
     assert bwd_call(**kw) == status
@@ -249,6 +261,28 @@ def prep_call(dtype=1, rows=4, dk=128, q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, n_gates
 ])
 def test_prepare_rejects_before_launch(kw, status):
     assert prep_call(**kw) == status
+
+
+def prep_bwd_call(dtype=1, rows=4, dk=128, q=FAKE, k=FAKE, dq=FAKE, dk_=FAKE, dqo=FAKE,
+                  dko=FAKE, n_gates=4, g=FAKE, beta=FAKE, dg=FAKE, db=FAKE, dgo=FAKE, dbo=FAKE,
+                  flags=3):
+    return gdn.load().gdn_prepare_inputs_bwd(dtype, rows, dk, q, k, dq, dk_, dqo, dko, n_gates,
+                                             g, beta, dg, db, dgo, dbo, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), INVALID), (dict(flags=0x80000001), INVALID),
+    (dict(q=None), INVALID), (dict(dk_=None), INVALID), (dict(dko=None), INVALID),
+    (dict(rows=-1), INVALID), (dict(dk=0), INVALID), (dict(dk=257), UNSUPPORTED),
+    (dict(dtype=5), UNSUPPORTED), (dict(dq=FAKE + 4), MISALIGNED),
+    (dict(dko=FAKE + 8), MISALIGNED), (dict(g=None), INVALID), (dict(db=None), INVALID),
+    (dict(dgo=None), INVALID), (dict(n_gates=-1), INVALID), (dict(dbo=FAKE + 4), MISALIGNED),
+    (dict(flags=0), OK), (dict(rows=0, n_gates=0), OK),
+    (dict(flags=1, g=None, beta=None, dg=None, db=None, dgo=None, dbo=None, rows=0), OK),
+    (dict(flags=2, q=None, k=None, dq=None, dk_=None, dqo=None, dko=None, n_gates=0), OK),
+])
+def test_prepare_bwd_rejects_before_launch(kw, status):
+    assert prep_bwd_call(**kw) == status
 
 
 def step_call(dtype=1, N=2, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
