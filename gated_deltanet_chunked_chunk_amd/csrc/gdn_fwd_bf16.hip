@@ -52,8 +52,14 @@
 // ARITH 2019).  In the block substitution a split product A x takes two
 // 32-deep MFMAs whose A operand holds A's (hi | lo) halves, one against
 // (x_hi | x_hi) and one against (x_lo | x_lo), so all four hi/lo terms are
-// summed with no zero padding.  K M0, Q M0 and P Delta use hi parts only: their error
-// stays well inside the output tolerance, and K M0's is damped by the solve.
+// summed with no zero padding.  Q M0 and P Delta feed only the output and
+// use hi parts, well inside its tolerance.  K M0 uses the hi part of M0 at
+// dk = 128 and 256 and hi + lo at dk = 64.  A hi-only M0 there puts a
+// relative error of about 2^-9 into every chunk's right-hand side, which the
+// state keeps for about 1 / (1 - a) tokens; a chunk of 64 keys spans the whole
+// key space at dk = 64 (half of it at dk = 128), so that is where, under slow
+// decay, the error nears the state tolerance.  The low part costs the 128-key
+// kernel about 7% of its time, which is why it is not taken there.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16)+j] and
 // B[8(l/16)+j][l%16] (j = 0..7), receives C[4(l/16)+r][l%16] (r = 0..3).  A
@@ -841,15 +847,27 @@ template <bool Out, bool Nrm, int DK, bool SaveDelta = false>
 __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                             const Item &it, int c, int s, int lane, f32x4 (&h)[8]) {
     const int lr = lane & 15, lg = lane >> 4;
-    // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0),
-    // fragments loaded one row block ahead of the products.
+    // (a5, a7) X = K M0 and Q M0 on this wave's columns (hi part of M0; at
+    // dk = 64 K M0 adds the lo part), fragments loaded one row block ahead
+    // of the products.
     // Key tiles 0 .. DK/16 - 1 hold the state; with DK = 64 the rest stay
     // zero and are skipped, as are the zero upper halves of the K, Q rows.
     constexpr int KK = DK / 32, MT = DK / 16;
-    bf16x8 hb[4];
+    // At dk = 64, K M0 also takes the low part of M0 (LoKM).
+    constexpr bool LoKM = DK == 64;
+    bf16x8 hb[4], hl[4];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+    for (int kk = 0; kk < KK; ++kk) {
+        if constexpr (LoKM) {
+            u32x2 h0, l0, h1, l1;
+            split4(h[2 * kk], h0, l0);
+            split4(h[2 * kk + 1], h1, l1);
+            hb[kk] = cat(h0, h1);
+            hl[kk] = cat(l0, l1);
+        } else {
+            hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+        }
+    }
     f32x4 X[4], Oa[4];
     bf16x8 fk[2][4], fq[2][4];
     const KqBase kb = kq_base(lr, lg);
@@ -872,6 +890,8 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             X[mi] = mma(fk[mi & 1][kk], hb[kk], X[mi]);
+            if constexpr (LoKM)
+                X[mi] = mma(fk[mi & 1][kk], hl[kk], X[mi]);
             Oa[mi] = mma(fq[mi & 1][kk], hb[kk], Oa[mi]);
         }
     }

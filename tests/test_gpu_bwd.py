@@ -18,8 +18,10 @@ from gpu_util import rel_l2, to_device
 pytestmark = pytest.mark.gpu
 
 # bf16 inputs: every gradient within 1e-2 relative L2 of the fp64 oracle (the
-# bf16 rounding of dq, dk, dv alone is about 2e-3).
+# bf16 rounding of dq, dk, dv alone is about 2e-3); dh0, a state gradient kept
+# in fp32, within the forward's state tolerance of 1e-3.
 TOL_BWD = 1e-2
+TOL_DH0 = 1e-3
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
@@ -57,7 +59,8 @@ def check_bwd(d, seed, scale=1.0, with_dht=True, label=""):
         errs[name] = rel_l2(x, y)
     print("  rel-L2 " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for name, e in errs.items():
-        assert e <= TOL_BWD, f"{name} rel-L2 {e:.3e} > {TOL_BWD}"
+        tol = TOL_DH0 if name == "dh0" else TOL_BWD
+        assert e <= tol, f"{name} rel-L2 {e:.3e} > {tol}"
     return errs
 
 

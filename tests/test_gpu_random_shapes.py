@@ -139,4 +139,5 @@ def test_backward_random_configuration(c):
                          dht=None if dht is None else dht.astype(np.float64), cu_seqlens=cu)
     errs = [rel_l2(x.float().cpu().numpy(), r) for x, r in zip(got, ref)]
     print("  rel-L2 " + ", ".join(f"{e:.2e}" for e in errs), flush=True)
-    assert max(errs) <= 1e-2
+    assert max(errs[:5]) <= 1e-2
+    assert errs[5] <= 1e-3, "dh0: a state gradient, held to the state tolerance"
