@@ -34,6 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "headline_bf16"
 KERNEL_NAME = "gdn_fwd_bf16<false, 0, 128>"
 KERNEL_SOURCES = ["gated_deltanet_chunked_chunk_amd/csrc/gdn_fwd_bf16.hip"]
+BWD_KERNEL_SOURCES = KERNEL_SOURCES + ["gated_deltanet_chunked_chunk_amd/csrc/gdn_bwd_bf16.hip"]
 K256_KERNEL_NAME = "gdn_fwd_bf16<false, 0, 256>"
 
 
@@ -487,12 +488,12 @@ def measure_k256(gdn, gi, torch, dev, steps, warmup):
             "check": {"head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h}}
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     """sha256 of the kernel's code: its source with // comments, trailing
     blanks and empty lines removed, so editing a comment does not count as a
     change of the kernel."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel)) as f:
             for line in f:
                 code = line.split("//", 1)[0].rstrip()

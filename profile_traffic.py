@@ -42,7 +42,12 @@ CAL_KERNEL = "bitwise_not"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNELS = {"headline_bf16": bench.KERNEL_NAME, "k256_bf16": bench.K256_KERNEL_NAME}
+KERNELS = {"headline_bf16": bench.KERNEL_NAME, "k256_bf16": bench.K256_KERNEL_NAME,
+           "fwd_bwd_bf16": "bwd_grads", "fwd_bwd_dk64_bf16": "bwd_grads"}
+# The backward's kernels, in launch order: the forward walk that saves each
+# chunk's entering state and Delta rows, the reverse walk of the state
+# gradient, and the per-chunk gradient kernel.
+BWD_KERNELS = ["gdn_fwd_bf16<false, 3, {dk}>", "gdn_fwd_bf16<false, 4, {dk}>", "bwd_grads"]
 
 
 def launch(n, workload):
@@ -52,6 +57,19 @@ def launch(n, workload):
     import gdn_inputs as gi
     gdn.load()
     dev = torch.device("cuda:0")
+    if workload.startswith("fwd_bwd"):
+        d = gi.make_config(workload)
+        do, dht = gi.make_upstream(d, gi.CONFIGS[workload]["seed"])
+        up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        q, k, v, dO = up(d["q"]), up(d["k"]), up(d["v"]), up(do)
+        g, b = torch.from_numpy(d["g"]).to(dev), torch.from_numpy(d["beta"]).to(dev)
+        dh = torch.from_numpy(dht).to(dev)
+        for i in range(n):
+            gdn.gdn_chunk_bwd(q, k, v, g, b, dO, dht=dh)
+            torch.cuda.synchronize()
+            print(f"[launch] backward {i + 1}/{n}", flush=True)
+        _calibration_copy(torch, dev)
+        return
     if workload == "headline_bf16":
         d = gi.make_config(workload)
         up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -68,6 +86,10 @@ def launch(n, workload):
         gdn.gdn_chunk_fwd(q, k, v, g, b, out=o, final_state=ht)
         torch.cuda.synchronize()
         print(f"[launch] {i + 1}/{n}", flush=True)
+    _calibration_copy(torch, dev)
+
+
+def _calibration_copy(torch, dev):
     src = torch.zeros(CAL_BYTES // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.bitwise_not(src, out=dst)
@@ -97,7 +119,52 @@ def pick(per, needle):
     return hits[0]
 
 
+def traffic_bwd(fetch_dir, write_dir, command, workload):
+    """FETCH_SIZE and WRITE_SIZE of each backward kernel, scaled as for the
+    forward, against the backward's algorithmic bytes."""
+    import gdn_inputs as gi
+    c = gi.CONFIGS[workload]
+    alg = bench.bwd_algorithmic_bytes(c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"])
+    names = [k.format(dk=c["dk"]) for k in BWD_KERNELS]
+    fetch, write = read_counter(fetch_dir, "FETCH_SIZE"), read_counter(write_dir, "WRITE_SIZE")
+    scale = {}
+    for counter, per in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        _, cv = pick(per, CAL_KERNEL)
+        scale[counter] = CAL_BYTES / (sum(cv) / len(cv) * 1024.0)
+    rows, total = [], 0.0
+    for kname in names:
+        r = {"kernel": kname}
+        for counter, per in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+            _, kv = pick(per, kname)
+            r[counter] = sum(kv) / len(kv) * 1024.0 * scale[counter]
+        total += r["FETCH_SIZE"] + r["WRITE_SIZE"]
+        rows.append(r)
+    out = {"workload": workload,
+           "kernel_source_sha256": bench.kernel_source_hash(bench.BWD_KERNEL_SOURCES),
+           "algorithmic_bytes_per_call": alg, "scale_factors": scale, "kernels": rows,
+           "bytes_per_call": total, "traffic_over_algorithmic": total / alg,
+           "command": command}
+    with open(os.path.join(PROFILES, f"traffic_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# HBM traffic of the backward, {workload} (B={c['B']} T={c['T']} H={c['Hv']} "
+             f"dk={c['dk']} dv={c['dv']} bf16)", "", "Commands:", "", "```", command, "```", "",
+             "FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same counter reads "
+             f"for a copy of 256 MiB (factors {scale['FETCH_SIZE']:.4f} and "
+             f"{scale['WRITE_SIZE']:.4f}).", "",
+             "| kernel | fetched MB | written MB |", "|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['kernel']}` | {r['FETCH_SIZE'] / 1e6:.1f} | "
+                     f"{r['WRITE_SIZE'] / 1e6:.1f} |")
+    lines += ["", f"Total {total / 1e6:.1f} MB per call; algorithmic {alg / 1e6:.1f} MB; ratio "
+                  f"{total / alg:.3f}.", f"Kernel source sha256 {out['kernel_source_sha256']}."]
+    with open(os.path.join(PROFILES, f"traffic_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic(fetch_dir, write_dir, command, workload):
+    if workload.startswith("fwd_bwd"):
+        return traffic_bwd(fetch_dir, write_dir, command, workload)
     import gdn_inputs as gi
     c = gi.CONFIGS[workload]
     kernel = KERNELS[workload]
@@ -163,8 +230,9 @@ def counters(dirname, command, workload):
     clocks = vals["GRBM_GUI_ACTIVE"] / xcds
     mfma_util = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * simds)
     conflict = vals["SQ_LDS_BANK_CONFLICT"] / max(vals["SQ_LDS_IDX_ACTIVE"], 1.0)
+    sources = bench.BWD_KERNEL_SOURCES if workload.startswith("fwd_bwd") else None
     out = {"kernel": kernel, "workload": workload, "command": command,
-           "kernel_source_sha256": bench.kernel_source_hash(), "per_dispatch": vals,
+           "kernel_source_sha256": bench.kernel_source_hash(sources), "per_dispatch": vals,
            "busy_clocks_per_xcd": clocks,
            "mfma_busy_per_simd": mfma_util,
            "lds_bank_conflict_over_idx_active": conflict}
