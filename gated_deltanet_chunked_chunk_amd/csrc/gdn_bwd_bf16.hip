@@ -51,6 +51,7 @@
 // ds_read_b64_tr_b16: within 16 lanes, lane 16g+i receives element i%4 of the
 // 8-byte words addressed by lanes 16g + 4j + i/4, j = 0..3.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "gdn_internal.h"
@@ -159,6 +160,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                              kRsrcWord3);
 }
 
+// The same for a base and size the caller knows to be equal on every lane
+// (they depend only on the work item): taken from the first lane, so the
+// descriptor sits in scalar registers and each load is issued once instead
+// of in a loop over the distinct descriptors the compiler would otherwise
+// have to allow for.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    return rsrc(reinterpret_cast<const void *>(static_cast<uint64_t>(hi) << 32 | lo),
+                __builtin_amdgcn_readfirstlane(bytes));
+}
+
 template <int Ctrl, int RowMask>
 __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(
@@ -247,28 +261,24 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
 }
 
 // Rows [p, p + L) of a [*, H, dk] bf16 tensor (dk = 64 or 128) at head h,
-// for a [64][kLK] tile: issue loads this thread's two 16-byte pieces (zeros
-// past dk), commit stores them.  512 threads.
-__device__ __forceinline__ void rows512_issue(u32x4 (&v)[2], const void *src, int64_t p, int L,
-                                              int H, int h, int dk, int tid) {
+// written straight into a [64][kLK] LDS tile by buffer loads that store to
+// LDS (no registers): the tile's 64 x 17 slots of 16 bytes
+// (16 of data and the pad per row) are 17 wave-wide loads, wave w issuing
+// loads w, w + 8 and w + 16.  Lane i of load n fills slot 64 n + i.  The pad
+// slots, the slots past dk and the rows past L read out of the buffer's
+// range, which loads zeros.  The data lands after the wave's vmcnt drains.
+__device__ __forceinline__ void rows_to_lds(uint16_t *tile, const void *src, int64_t p, int L,
+                                            int H, int h, int dk, int w, int lane) {
+    constexpr int kSlots = kLK / 8;  // 17 per row
     const uint32_t row_bytes = (uint32_t)H * dk * 2;
     const __amdgpu_buffer_rsrc_t r =
-        rsrc(static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)dk,
-             (uint32_t)(L - 1) * row_bytes + dk * 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + kGT * u;
-        v[u] = 8 * (i & 15) < dk
-                   ? __builtin_amdgcn_raw_buffer_load_b128(r, (i >> 4) * row_bytes + 16 * (i & 15), 0, 0)
-                   : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-__device__ __forceinline__ void rows512_commit(uint16_t *dst, const u32x4 (&v)[2], int tid) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int i = tid + kGT * u;
-        *reinterpret_cast<u32x4 *>(dst + (i >> 4) * kLK + 8 * (i & 15)) = v[u];
+        rsrc_uniform(static_cast<const uint16_t *>(src) + (p * H + h) * (int64_t)dk,
+                     (uint32_t)(L - 1) * row_bytes + dk * 2);
+    for (int n = w; n < kSlots; n += kGT / 64) {
+        const int s = 64 * n + lane, row = s / kSlots, pc = s - kSlots * row;
+        const uint32_t off = pc < 16 && 8 * pc < dk ? row * row_bytes + 16 * pc : 0x40000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(tile + 8 * 64 * n), 16, off, 0, 0, 0);
     }
 }
 
@@ -287,16 +297,15 @@ __device__ __forceinline__ void rows512_commit(uint16_t *dst, const u32x4 (&v)[2
 
 
 struct alignas(16) GradSmem {
-    uint16_t K[kC * kLK];
-    uint16_t Q[kC * kLK];
-    union {
-        struct {
-            uint16_t M0[kC * kLK];   // M0^T of the step's 64 value columns: [col][key]
-            uint16_t dM[kC * kLK];   // dML^T
-        } s;
-        uint16_t out[2][kC * kLK];   // dq, dk rows at the end
-    } m;
-    union {
+    // The small tables and the step tiles first, so that their addresses
+    // fit the 16-bit immediate offsets of LDS instructions.  Every tile
+    // starts 16-byte aligned (alignas): its 16-byte accesses need it.
+    float gam[kC], e[kC], l[kC], bt[kC];
+    float rowb[2][kC], rowg[2][kC];
+    float colpart[4][kC];
+    float red[kGT];
+    float eL;
+    alignas(16) union {
         struct {
             uint16_t V[kC * kL64];   // v rows, the step's 64 columns
             uint16_t dO[kC * kL64];  // do rows (unscaled)
@@ -309,12 +318,19 @@ struct alignas(16) GradSmem {
             float Sf[kC * kLF];      // S = diag(beta) (-dA * D), strictly lower
         } d;
     } u;
-    float gam[kC], e[kC], l[kC], bt[kC];
-    float eL;
-    float rowb[2][kC], rowg[2][kC];
-    float colpart[4][kC];
-    float red[kGT];
+    alignas(16) union {
+        struct {
+            uint16_t M0[kC * kLK];   // M0^T of the step's 64 value columns: [col][key]
+            uint16_t dM[kC * kLK];   // dML^T
+        } s;
+        uint16_t out[2][kC * kLK];   // dq, dk rows at the end
+    } m;
+    alignas(16) uint16_t KQ[2][2][kC * kLK];  // [item parity][K, Q]: the next item's land in the other half
 };
+static_assert(offsetof(GradSmem, u) % 16 == 0 && offsetof(GradSmem, m) % 16 == 0 &&
+                  offsetof(GradSmem, KQ) % 16 == 0 && (kC * kLK * 2) % 16 == 0 &&
+                  (kC * kL64 * 2) % 16 == 0,
+              "16-byte LDS accesses need 16-byte aligned tiles");
 
 // One value step's tiles in flight: thread t holds pieces t and t + 512 of
 // M0^T and dML^T (row i / 16, 16 bytes i % 16) and piece t of the v, do,
@@ -339,17 +355,27 @@ __device__ __forceinline__ void grads_issue(GradPre &pre, const BwdArgs &a, cons
     const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
     const int64_t xofs = (cl.p * a.Hv + j) * (int64_t)a.dv + step_col;
     const uint32_t span = (uint32_t)(cl.L - 1) * xrow + 128;
-    const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint16_t *>(a.v) + xofs, span);
-    const __amdgpu_buffer_rsrc_t ro = rsrc(static_cast<const uint16_t *>(a.dout) + xofs, span);
+    const __amdgpu_buffer_rsrc_t rv =
+        rsrc_uniform(static_cast<const uint16_t *>(a.v) + xofs, span);
+    const __amdgpu_buffer_rsrc_t ro =
+        rsrc_uniform(static_cast<const uint16_t *>(a.dout) + xofs, span);
     pre.v = __builtin_amdgcn_raw_buffer_load_b128(rv, row * xrow + 16 * pc, 0, 0);
     pre.o = __builtin_amdgcn_raw_buffer_load_b128(ro, row * xrow + 16 * pc, 0, 0);
     const int64_t wofs = (wi * kC + row) * (int64_t)a.dv + step_col + 8 * pc;
     pre.dl = *reinterpret_cast<const u32x4 *>(a.ws_delta + wofs);
     pre.dr = *reinterpret_cast<const u32x4 *>(a.ws_drhs + wofs);
-    if (gates && tid < kC) {
-        pre.g = tid < cl.L ? a.g[(cl.p + tid) * a.Hv + j] : 0.0f;
-        pre.b = tid < cl.L ? a.beta[(cl.p + tid) * a.Hv + j] : 0.0f;
-    }
+    // The head's gates (used by wave 0 on a head's first step), loaded by
+    // every thread with no branch: rows past L, and threads past the chunk,
+    // read out of the buffer's range, which loads zeros.  (A conditional
+    // load here made the compiler drain every load in flight before the
+    // step's work.)
+    const uint32_t gspan = (uint32_t)(cl.L - 1) * a.Hv * 4 + 4;
+    const __amdgpu_buffer_rsrc_t rg = rsrc_uniform(a.g + cl.p * a.Hv + j, gspan);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_uniform(a.beta + cl.p * a.Hv + j, gspan);
+    const uint32_t goff = tid < kC ? (uint32_t)(tid * a.Hv * 4) : 0x40000000u;
+    pre.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+    pre.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
+    (void)gates;
 }
 
 __device__ __forceinline__ void grads_commit(GradSmem &S, const GradPre &pre, int tid) {
@@ -420,22 +446,27 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     int64_t item = find(blockIdx.x, cl, gc, hk);
     if (item >= total)
         return;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    rows_to_lds(S.KQ[0][0], a.k, cl.p, cl.L, a.Hqk, hk, a.dk, wu, lane);
+    rows_to_lds(S.KQ[0][1], a.q, cl.p, cl.L, a.Hqk, hk, a.dk, wu, lane);
     GradPre pre;
     grads_issue(pre, a, cl, gc, hk * G, 0, true, tid);
 
-    while (true) {
-    {
-        u32x4 kv[2], qv[2];
-        rows512_issue(kv, a.k, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
-        rows512_issue(qv, a.q, cl.p, cl.L, a.Hqk, hk, a.dk, tid);
-        __syncthreads();  // the previous item's readers are done
-        rows512_commit(S.K, kv, tid);
-        rows512_commit(S.Q, qv, tid);
-    }
+    for (int par = 0;; par ^= 1) {
     ChunkLoc ncl;
     int64_t ngc = 0;
     int nhk = 0;
     const int64_t nitem = find(item + gridDim.x, ncl, ngc, nhk);
+    // This item's K and Q tiles have landed (vmcnt also drains the first
+    // value step's loads, needed next), and every wave is past the previous
+    // item, whose tiles the other half held: the next item's go there now.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    if (nitem < total) {
+        rows_to_lds(S.KQ[par ^ 1][0], a.k, ncl.p, ncl.L, a.Hqk, nhk, a.dk, wu, lane);
+        rows_to_lds(S.KQ[par ^ 1][1], a.q, ncl.p, ncl.L, a.Hqk, nhk, a.dk, wu, lane);
+    }
+    const uint16_t *sK = S.KQ[par][0], *sQ = S.KQ[par][1];
 
     f32x4 dQ[4], dK[4];   // key tiles 4 hd + i
 #pragma unroll
@@ -477,11 +508,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                     S.eL = __expf(gL);
             }
             __syncthreads();
-            if (step + 1 < steps) {
-                const int gn = (step + 1) / nsteps, vn = (step + 1) % nsteps;
-                grads_issue(pre, a, cl, gc, hk * G + gn, 64 * vn, vn == 0, tid);
-            } else if (nitem < total) {
-                grads_issue(pre, a, ncl, ngc, nhk * G, 0, true, tid);
+            {
+                // One issue site with no branch around it (two sites, or a
+                // skipped issue, made the compiler copy the loaded registers
+                // and wait for the loads right after issuing them): the next
+                // step, else the next item's first, else this step again.
+                const bool more = step + 1 < steps, next_item = !more && nitem < total;
+                const int sn = more ? step + 1 : next_item ? 0 : step;
+                const int gn = sn / nsteps, vn = sn % nsteps;
+                grads_issue(pre, a, next_item ? ncl : cl, next_item ? ngc : gc,
+                            (next_item ? nhk : hk) * G + gn, 64 * vn, vn == 0, tid);
             }
             // The lane indices pass through an empty asm so that the many
             // addresses formed from them are computed here, not hoisted out
@@ -500,8 +536,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 const int c0 = 32 * hd + 16 * t;
                 f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, U = X;
                 for (int kx = 0; kx < kx_end; ++kx) {
-                    const bf16x8 fk = frag_rows(S.K, kLK, 16 * rb, 32 * kx, lr, lg);
-                    const bf16x8 fq = frag_rows(S.Q, kLK, 16 * rb, 32 * kx, lr, lg);
+                    const bf16x8 fk = frag_rows(sK, kLK, 16 * rb, 32 * kx, lr, lg);
+                    const bf16x8 fq = frag_rows(sQ, kLK, 16 * rb, 32 * kx, lr, lg);
                     const bf16x8 bm = frag_rows(S.m.s.M0, kLK, c0, 32 * kx, lr, lg);
                     const bf16x8 bd = frag_rows(S.m.s.dM, kLK, c0, 32 * kx, lr, lg);
                     X = mma(fk, bm, X);
@@ -564,9 +600,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             kk4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             qk4[i] = kk4[i];
             for (int kx = 0; kx < kx_end; ++kx) {
-                const bf16x8 b = frag_rows(S.K, kLK, 16 * (2 * hd + i), 32 * kx, lr, lg);
-                kk4[i] = mma(frag_rows(S.K, kLK, 16 * rb, 32 * kx, lr, lg), b, kk4[i]);
-                qk4[i] = mma(frag_rows(S.Q, kLK, 16 * rb, 32 * kx, lr, lg), b, qk4[i]);
+                const bf16x8 b = frag_rows(sK, kLK, 16 * (2 * hd + i), 32 * kx, lr, lg);
+                kk4[i] = mma(frag_rows(sK, kLK, 16 * rb, 32 * kx, lr, lg), b, kk4[i]);
+                qk4[i] = mma(frag_rows(sQ, kLK, 16 * rb, 32 * kx, lr, lg), b, qk4[i]);
             }
         }
         float cp[2] = {0.f, 0.f};  // column parts of dgamma, columns 16 (2 hd + i) + lr
@@ -654,8 +690,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 const int nj = 4 * hd + i;
                 if (nj >= 2 * kx_end)
                     continue;
-                const bf16x8 bk = frag_cols(S.K, kLK, 32 * kk, 16 * nj, lr, lg);
-                const bf16x8 bq = frag_cols(S.Q, kLK, 32 * kk, 16 * nj, lr, lg);
+                const bf16x8 bk = frag_cols(sK, kLK, 32 * kk, 16 * nj, lr, lg);
+                const bf16x8 bq = frag_cols(sQ, kLK, 32 * kk, 16 * nj, lr, lg);
                 dQ[i] = mma(pr, bk, dQ[i]);
                 dK[i] = mma(pc, bq, dK[i]);
                 dK[i] = mma(sr, bk, dK[i]);
