@@ -190,13 +190,23 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
-// Sum over the 16 lanes of this lane's row.
+// Sum over the 16 lanes of this lane's row, by DPP (no LDS round trips):
+// swaps within quads (xor 1, xor 2), then the half-row and row mirrors.
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
+    x += dpp<0xB1, 0xF>(x);
+    x += dpp<0x4E, 0xF>(x);
+    x += dpp<0x141, 0xF>(x);
+    x += dpp<0x140, 0xF>(x);
     return x;
+}
+
+// Sum over the 64 lanes, the same on every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    const int r = __builtin_bit_cast(int, row16_sum(x));
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 48)));
 }
 
 // Where chunk gc of the whole call lies.
@@ -606,24 +616,42 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             }
         }
         float cp[2] = {0.f, 0.f};  // column parts of dgamma, columns 16 (2 hd + i) + lr
+        // The tables of this lane's rows (16 rb + 4 lg + r) and columns
+        // (16 (2 hd + i) + lr) are read once, and every element is formed in
+        // registers before any is stored: with the stores in between, the
+        // compiler re-read the tables for each element, one LDS round trip
+        // after another.
+        const f32x4 grow = ld4f(S.gam + 16 * rb + 4 * lg);
+        const f32x4 brow = ld4f(S.bt + 16 * rb + 4 * lg);
+        const float gcol[2] = {S.gam[32 * hd + lr], S.gam[32 * hd + 16 + lr]};
+        float pdv[2][4], sfv[2][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * lg + r, sc = 16 * (2 * hd + i) + lr;
-                const float d = sc <= row ? __expf(S.gam[row] - S.gam[sc]) : 0.0f;
+                const bool incl = sc <= row, strict = sc < row;
+                // above the diagonal the exponent may overflow: selected away
+                const float d = incl ? __expf(grow[r] - gcol[i]) : 0.0f;
                 const float dpv = scale * dP[i][r];
                 const float dav = -dA[i][r];
-                const bool incl = sc <= row, strict = sc < row;
-                S.u.d.PD[row * kL64 + sc] = f2bf(incl ? dpv * d : 0.0f);
-                S.u.d.Sf[row * kLF + sc] = strict ? S.bt[row] * dav * d : 0.0f;
+                pdv[i][r] = incl ? dpv * d : 0.0f;
+                sfv[i][r] = strict ? brow[r] * dav * d : 0.0f;
                 if (strict)
                     pb[r] += dav * d * kk4[i][r];
                 const float dDv = (incl ? dpv * qk4[i][r] : 0.0f) +
-                                  (strict ? S.bt[row] * dav * kk4[i][r] : 0.0f);
+                                  (strict ? brow[r] * dav * kk4[i][r] : 0.0f);
                 const float dDD = incl ? dDv * d : 0.0f;
                 pg[r] += dDD;
                 cp[i] -= dDD;
+            }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r, sc = 16 * (2 * hd + i) + lr;
+                S.u.d.PD[row * kL64 + sc] = f2bf(pdv[i][r]);
+                S.u.d.Sf[row * kLF + sc] = sfv[i][r];
             }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -656,9 +684,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < kGT / 64; ++i)
                 tot += S.red[64 * i + lane];
-            float gl = tot;
-            for (int o = 32; o >= 1; o >>= 1)
-                gl += __shfl_xor(gl, o);
+            const float gl = wave_sum(tot);
             float dgm = S.rowg[0][lane] + S.rowg[1][lane] + S.colpart[0][lane] +
                         S.colpart[1][lane] + S.colpart[2][lane] + S.colpart[3][lane];
             if (lane == kC - 1)
