@@ -427,6 +427,9 @@ __device__ __forceinline__ f32x4 tile_c(const uint16_t *t, int ld, int row0, int
                  bf2f(static_cast<uint16_t>(v.y & 0xffff)), bf2f(static_cast<uint16_t>(v.y >> 16))};
 }
 
+// KX: 32-wide key steps that carry data (dk / 32), a constant so that the
+// key loops unroll and their LDS reads issue together.
+template <int KX>
 __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     __shared__ GradSmem S;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     const int nsteps = a.dv / 64;
     const int steps = G * nsteps;
     const float scale = a.scale;
-    const int kx_end = a.dk > 64 ? 4 : 2;  // 32-wide key steps that carry data
+    constexpr int kx_end = KX;
     // Persistent: workgroup b takes work items b, b + gridDim.x, ..., item i
     // being chunk i / Hqk and q/k head i % Hqk; chunks past the last
     // document's (the packed bound) are skipped.  The next item's K, Q rows
@@ -541,19 +544,32 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             // from their elementwise products.
             const f32x4 b4 = ld4f(S.bt + 16 * rb + 4 * lg), e4 = ld4f(S.e + 16 * rb + 4 * lg);
             const f32x4 l4 = ld4f(S.l + 16 * rb + 4 * lg);
-#pragma unroll 1
+            // K and Q fragments are read once for both 16-column tiles.
+            f32x4 Xt[2], Yt[2], Ut[2];
+#pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int c0 = 32 * hd + 16 * t;
-                f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, U = X;
-                for (int kx = 0; kx < kx_end; ++kx) {
-                    const bf16x8 fk = frag_rows(sK, kLK, 16 * rb, 32 * kx, lr, lg);
-                    const bf16x8 fq = frag_rows(sQ, kLK, 16 * rb, 32 * kx, lr, lg);
+                Xt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Yt[t] = Xt[t];
+                Ut[t] = Xt[t];
+            }
+#pragma unroll
+            for (int kx = 0; kx < kx_end; ++kx) {
+                const bf16x8 fk = frag_rows(sK, kLK, 16 * rb, 32 * kx, lr, lg);
+                const bf16x8 fq = frag_rows(sQ, kLK, 16 * rb, 32 * kx, lr, lg);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int c0 = 32 * hd + 16 * t;
                     const bf16x8 bm = frag_rows(S.m.s.M0, kLK, c0, 32 * kx, lr, lg);
                     const bf16x8 bd = frag_rows(S.m.s.dM, kLK, c0, 32 * kx, lr, lg);
-                    X = mma(fk, bm, X);
-                    Y = mma(fq, bm, Y);
-                    U = mma(fk, bd, U);
+                    Xt[t] = mma(fk, bm, Xt[t]);
+                    Yt[t] = mma(fq, bm, Yt[t]);
+                    Ut[t] = mma(fk, bd, Ut[t]);
                 }
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int c0 = 32 * hd + 16 * t;
+                const f32x4 X = Xt[t], Y = Yt[t], U = Ut[t];
                 const f32x4 vv = tile_c(S.u.t.V, kL64, 16 * rb, c0, lr, lg);
                 const f32x4 oo = tile_c(S.u.t.dO, kL64, 16 * rb, c0, lr, lg);
                 const f32x4 dl = tile_c(S.u.t.Dl, kL64, 16 * rb, c0, lr, lg);
@@ -609,6 +625,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
         for (int i = 0; i < 2; ++i) {
             kk4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
             qk4[i] = kk4[i];
+#pragma unroll
             for (int kx = 0; kx < kx_end; ++kx) {
                 const bf16x8 b = frag_rows(sK, kLK, 16 * (2 * hd + i), 32 * kx, lr, lg);
                 kk4[i] = mma(frag_rows(sK, kLK, 16 * rb, 32 * kx, lr, lg), b, kk4[i]);
@@ -822,7 +839,10 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
     // One persistent workgroup per CU (one fits: its LDS is 111 KB).
     const int64_t items = a.n_chunks * a.Hqk;
     const unsigned grid = (unsigned)(items < kGradGrid ? items : kGradGrid);
-    hipLaunchKernelGGL(bwd_grads, dim3(grid), dim3(kGT), 0, stream, a);
+    if (a.dk > 64)
+        hipLaunchKernelGGL(bwd_grads<4>, dim3(grid), dim3(kGT), 0, stream, a);
+    else
+        hipLaunchKernelGGL(bwd_grads<2>, dim3(grid), dim3(kGT), 0, stream, a);
     return hipGetLastError();
 }
 
