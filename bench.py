@@ -155,6 +155,61 @@ def measure_bwd(gdn, gi, torch, dev, steps, warmup, name="fwd_bwd_bf16", with_fw
     return res
 
 
+def measure_bwd_k256(gdn, gi, torch, dev, steps, warmup):
+    """The backward at head dimension 256 on the k256 workload's shapes (B=8,
+    T=2048, H=32, D=256: the FLA table's D = 256 row), inputs drawn on the
+    device with the workload's recipe plus do ~ N(0, 1) and dht ~ N(0, 0.02):
+    milliseconds per call, the forward on the same inputs, its HBM roofline
+    fraction, and the oracle on one sampled head."""
+    import oracle
+    name = "k256_bf16"
+    c = gi.CONFIGS[name]
+    B, T, Hqk, Hv, dk, dv = c["B"], c["T"], c["Hqk"], c["Hv"], c["dk"], c["dv"]
+    t = gi.make_device(B, T, Hqk, Hv, dk, dv, c["seed"], device=dev)
+    gen = torch.Generator(device=dev).manual_seed(c["seed"] + 1)
+    dO = torch.randn((B, T, Hv, dv), generator=gen, device=dev).to(torch.bfloat16)
+    dh = 0.02 * torch.randn((B, Hv, dk, dv), generator=gen, device=dev)
+    q, k, v, g, beta = (t[x] for x in ("q", "k", "v", "g", "beta"))
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(1, B, T, Hqk, Hv, dk, dv, B),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = None
+
+    def call():
+        nonlocal out
+        out = gdn.gdn_chunk_bwd(q, k, v, g, beta, dO, dht=dh, workspace=ws,
+                                stream=stream.cuda_stream)
+    ms = _time_calls(torch, stream, call, steps, warmup)
+    o = torch.empty_like(dO)
+    ht = torch.empty((B, Hv, dk, dv), dtype=torch.float32, device=dev)
+    fwd_ms = _time_calls(torch, stream, lambda: gdn.gdn_chunk_fwd(
+        q, k, v, g, beta, out=o, final_state=ht, stream=stream.cuda_stream), steps, warmup)
+    bs, hs = 3, 21
+    sl = lambda x: x[bs:bs + 1, :, hs:hs + 1].float().cpu().numpy()
+    ref = oracle.gdn_bwd(sl(q), sl(k), sl(v), sl(g), sl(beta), sl(dO),
+                         dht=dh[bs:bs + 1, hs:hs + 1].double().cpu().numpy())
+    errs = {}
+    for i, (nm, r) in enumerate(zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), ref)):
+        x = out[i][bs:bs + 1, :, hs:hs + 1] if i < 5 else out[i][bs:bs + 1, hs:hs + 1]
+        x = x.float().cpu().numpy()
+        errs[nm] = float(np.linalg.norm(x - r) / np.linalg.norm(r))
+    nbytes = bwd_algorithmic_bytes(B, T, Hqk, Hv, dk, dv)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log("[bench] backward (%s) %.4f ms/call, forward %.1f us/call; sampled head rel-L2 %s" %
+        (name, ms, fwd_ms * 1e3, ", ".join(f"{n} {e:.2e}" for n, e in errs.items())))
+    return {"workload": f"{name}: B={B} T={T} H={Hv} dk={dk} dv={dv}, chunk=32, do ~ N(0,1) "
+                        f"bf16, dht ~ N(0,0.02) fp32 (drawn on the device)",
+            "ms_per_call": ms, "fwd_ms_per_call": fwd_ms,
+            "tokens_per_s": B * T / (ms * 1e-3),
+            "fwd_bwd_tokens_per_s": B * T / ((fwd_ms + ms) * 1e-3), "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                         "algorithmic_bytes_per_call": nbytes,
+                         "kernels": ["gdn_fwd_bf16<false, 3, 256>",
+                                     "gdn_fwd_bf16<false, 4, 256>", "bwd_grads_k256"]},
+            "check": {"sampled_head": [bs, hs], "rel_l2": errs}}
+
+
 def per_launch(torch, stream, call, n, flush=None):
     """Per-launch durations (ms) with HIP events on the launch stream; with
     `flush` (a device buffer) it is overwritten before every launch, outside
@@ -662,12 +717,14 @@ def main():
     err_h = float(np.linalg.norm(gh - rh) / np.linalg.norm(rh))
     log(f"[bench] sampled head (b={bs}, h={hs}) rel-L2: output {err_o:.2e}, state {err_h:.2e}")
 
-    bwd = bwd_dk64 = None
+    bwd = bwd_dk64 = bwd_k256 = None
     if not args.no_bwd:
         log("[bench] backward")
         bwd = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20)
         bwd_dk64 = measure_bwd(gdn, gi, torch, dev, steps=50, warmup=20,
                                name="fwd_bwd_dk64_bf16", with_fwd=True)
+        if not args.no_k256:
+            bwd_k256 = measure_bwd_k256(gdn, gi, torch, dev, steps=10, warmup=3)
 
     decode = prep = None
     if not args.no_decode:
@@ -744,6 +801,7 @@ def main():
         "check": {"sampled_head": [bs, hs], "rel_l2_output": err_o, "rel_l2_state": err_h},
         "bwd": bwd,
         "bwd_dk64": bwd_dk64,
+        "bwd_k256": bwd_k256,
         "prep": prep,
         "decode": decode,
         "k256": k256,

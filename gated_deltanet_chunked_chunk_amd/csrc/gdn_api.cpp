@@ -426,15 +426,18 @@ gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t 
                       cu_seqlens, N, o, ht, plan, scratch_ptr, stream);
 }
 
-// The backward's shapes: bf16, dk in {64, 128}, dv in {64, 128, 256}.
+// The backward's shapes: bf16, dk in {64, 128, 256}, dv in {64, 128, 256}.
 static bool bwd_supported(gdn_dtype dtype, int32_t dk, int32_t dv) {
-    return dtype == GDN_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128 || dv == 256);
+    return dtype == GDN_BF16 && (dk == 64 || dk == 128 || dk == 256) &&
+           (dv == 64 || dv == 128 || dv == 256);
 }
 
-// Chunks of 64 tokens over all sequences: exact for batch rows; with
-// cu_seqlens the bound ceil(T / 64) + N covers any split into N documents.
-static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N) {
-    const int64_t per_row = (T + 63) / 64;
+// Chunks over all sequences (64 tokens, 32 at dk = 256): exact for batch
+// rows; with cu_seqlens the bound ceil(T / C) + N covers any split into N
+// documents.
+static int64_t bwd_chunks(int64_t B, int64_t T, bool packed, int32_t N, int32_t dk) {
+    const int64_t C = dk == 256 ? 32 : 64;
+    const int64_t per_row = (T + C - 1) / C;
     return packed ? per_row + N : B * per_row;
 }
 
@@ -461,8 +464,8 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
     if (B > INT64_MAX / T || B * T > INT64_MAX / ((int64_t)(H_v > H_qk ? H_v : H_qk) * 256))
         return 0;
     // Packed documents need B == 1; the packed bound also covers one row.
-    return gdn::bwd_workspace_bytes(bwd_chunks(B, T, B == 1, B == 1 ? n_seqs : (int32_t)B), H_v,
-                                    dk, dv) +
+    return gdn::bwd_workspace_bytes(bwd_chunks(B, T, B == 1, B == 1 ? n_seqs : (int32_t)B, dk),
+                                    H_v, dk, dv) +
            bwd_prep_bytes(flags, B, T, H_qk, H_v, dk);
 }
 
@@ -485,7 +488,8 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
     if (H_v % H_qk != 0 || !bwd_supported(dtype, dk, dv))
         return GDN_ERR_UNSUPPORTED;
     const int64_t hmax = H_v > H_qk ? H_v : H_qk;
-    const int64_t dmax = dv > 128 ? dv : 128;  // the workspace states are 128 keys wide
+    // the workspace states are 128 keys wide (256 at dk = 256)
+    const int64_t dmax = dv > 128 || dk > 128 ? 256 : 128;
     if (B > INT64_MAX / T || B * T > INT64_MAX / (hmax * dmax))
         return GDN_ERR_INVALID_ARG;
     int32_t N = (int32_t)B;
@@ -510,7 +514,7 @@ gdn_status gdn_chunk_bwd(gdn_dtype dtype, int64_t B, int64_t T, int32_t H_qk, in
         !aligned16(dq) || !aligned16(dk_) || !aligned16(dv_) || !aligned16(dg) ||
         !aligned16(dbeta) || !aligned16(dh0))
         return GDN_ERR_MISALIGNED;
-    const int64_t n_chunks = bwd_chunks(B, T, cu_seqlens != nullptr, N);
+    const int64_t n_chunks = bwd_chunks(B, T, cu_seqlens != nullptr, N, dk);
     if (n_chunks > INT32_MAX)
         return GDN_ERR_INVALID_ARG;
     const size_t own = gdn::bwd_workspace_bytes(n_chunks, H_v, dk, dv);

@@ -225,19 +225,11 @@ __device__ __forceinline__ int64_t seq_len(const BwdArgs &a, int n) {
     return a.cu ? (int64_t)a.cu[n + 1] - a.cu[n] : a.T;
 }
 
-// First chunk index of sequence n.
-__device__ __forceinline__ int64_t chunk_base(const BwdArgs &a, int n) {
-    if (!a.cu)
-        return (int64_t)n * ((a.T + kC - 1) / kC);
-    int64_t b = 0;
-    for (int m = 0; m < n; ++m)
-        b += (seq_len(a, m) + kC - 1) / kC;
-    return b;
-}
-
+// Where chunk gc (of CL tokens) of the whole call lies; false past the last.
+template <int CL = kC>
 __device__ __forceinline__ bool locate(const BwdArgs &a, int64_t gc, ChunkLoc &cl) {
     if (!a.cu) {
-        const int64_t nch = (a.T + kC - 1) / kC;
+        const int64_t nch = (a.T + CL - 1) / CL;
         const int64_t n = gc / nch;
         if (n >= a.n_seqs)
             return false;
@@ -247,7 +239,7 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int64_t gc, ChunkLoc &c
         int64_t b = 0;
         int n = 0;
         for (; n < a.n_seqs; ++n) {
-            const int64_t nc = (seq_len(a, n) + kC - 1) / kC;
+            const int64_t nc = (seq_len(a, n) + CL - 1) / CL;
             if (gc < b + nc)
                 break;
             b += nc;
@@ -257,8 +249,8 @@ __device__ __forceinline__ bool locate(const BwdArgs &a, int64_t gc, ChunkLoc &c
         cl.n = n;
         cl.c = (int)(gc - b);
     }
-    cl.p = seq_start(a, cl.n) + (int64_t)kC * cl.c;
-    cl.L = (int)min<int64_t>(kC, seq_len(a, cl.n) - (int64_t)kC * cl.c);
+    cl.p = seq_start(a, cl.n) + (int64_t)CL * cl.c;
+    cl.L = (int)min<int64_t>(CL, seq_len(a, cl.n) - (int64_t)CL * cl.c);
     return true;
 }
 
@@ -777,24 +769,436 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bwd_grads_k256: the same per (chunk, q/k head) at dk = 256, where a chunk
+// is 32 tokens (as in the forward's dk = 256 instance), so the workspace
+// holds 256-key states and 32 Delta and drhs rows per chunk.  512 threads,
+// one persistent workgroup per CU.  Wave w works on the chunk's rows
+// [16 rb, 16 rb + 16), rb = w % 2, and the quarter qd = w / 2 of each
+// result: of a 64-column value step the columns 16 qd .. 16 qd + 15, of dq and
+// dk the key tiles 4 qd .. 4 qd + 3; the 32 x 32 products (column tiles
+// qd < 2) fall to the waves with qd < 2.
+
+constexpr int kC2 = 32;    // tokens per chunk at dk = 256
+constexpr int kLK2 = 264;  // row stride (bf16) of 256-wide tiles
+constexpr int kL32 = 40;   // row stride (bf16) of 32-wide tiles
+constexpr int kLF2 = 33;   // row stride (fp32) of 32-wide fp32 tiles
+
+struct alignas(16) GradSmem256 {
+    float gam[kC2], e[kC2], l[kC2], bt[kC2];
+    float rowb[4][kC2], rowg[4][kC2];
+    float colpart[2][kC2];
+    float red[kGT];
+    float eL;
+    alignas(16) uint16_t K[kC2 * kLK2];
+    alignas(16) uint16_t Q[kC2 * kLK2];
+    alignas(16) union {
+        struct {
+            uint16_t V[kC2 * kL64];   // v rows, the step's 64 columns
+            uint16_t dO[kC2 * kL64];  // do rows (unscaled)
+            uint16_t Dl[kC2 * kL64];  // Delta rows
+            uint16_t dR[kC2 * kL64];  // drhs rows
+        } t;
+        struct {
+            uint16_t PD[kC2 * kL32];  // scale dP * D (diagonal included)
+            uint16_t SS[kC2 * kL32];  // S + S^T
+            float Sf[kC2 * kLF2];     // S = diag(beta) (-dA * D), strictly lower
+        } d;
+    } u;
+    alignas(16) union {
+        struct {
+            uint16_t M0[64 * kLK2];   // M0^T of the step's 64 value columns: [col][key]
+            uint16_t dM[64 * kLK2];   // dML^T
+        } s;
+        uint16_t out[2][kC2 * kLK2];  // dq, dk rows at the end
+    } m;
+};
+static_assert(offsetof(GradSmem256, K) % 16 == 0 && offsetof(GradSmem256, u) % 16 == 0 &&
+                  offsetof(GradSmem256, m) % 16 == 0 && (kC2 * kLK2 * 2) % 16 == 0 &&
+                  (kC2 * kL64 * 2) % 16 == 0 && (kC2 * kL32 * 2) % 16 == 0,
+              "16-byte LDS accesses need 16-byte aligned tiles");
+
+// One value step's tiles in flight: thread t holds pieces t + 512 u of M0^T
+// and dML^T (row i / 32, 16 bytes i % 32) and 8 bytes of each of the v, do,
+// Delta and drhs rows (row t / 16, columns 4 (t % 16) ..); the head's gates.
+struct GradPre256 {
+    u32x4 m[4], d[4];
+    u32x2 v, o, dl, dr;
+    float g, b;
+};
+
+__device__ __forceinline__ void grads_issue256(GradPre256 &pre, const BwdArgs &a,
+                                               const ChunkLoc &cl, int64_t gc, int j,
+                                               int step_col, int tid) {
+    const int64_t wi = gc * a.Hv + j;
+    const uint16_t *m0 = a.ws_hs + (wi * a.dv + step_col) * (int64_t)256;
+    const uint16_t *dm = a.ws_dhs + (wi * a.dv + step_col) * (int64_t)256;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + kGT * u;
+        pre.m[u] = *reinterpret_cast<const u32x4 *>(m0 + (i >> 5) * 256 + 8 * (i & 31));
+        pre.d[u] = *reinterpret_cast<const u32x4 *>(dm + (i >> 5) * 256 + 8 * (i & 31));
+    }
+    const int row = tid >> 4, pc = tid & 15;
+    const uint32_t xrow = (uint32_t)a.Hv * a.dv * 2;
+    const int64_t xofs = (cl.p * a.Hv + j) * (int64_t)a.dv + step_col;
+    const uint32_t span = (uint32_t)(cl.L - 1) * xrow + 128;
+    const __amdgpu_buffer_rsrc_t rv =
+        rsrc_uniform(static_cast<const uint16_t *>(a.v) + xofs, span);
+    const __amdgpu_buffer_rsrc_t ro =
+        rsrc_uniform(static_cast<const uint16_t *>(a.dout) + xofs, span);
+    pre.v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, row * xrow + 8 * pc, 0, 0));
+    pre.o = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ro, row * xrow + 8 * pc, 0, 0));
+    const int64_t wofs = (wi * kC2 + row) * (int64_t)a.dv + step_col + 4 * pc;
+    pre.dl = *reinterpret_cast<const u32x2 *>(a.ws_delta + wofs);
+    pre.dr = *reinterpret_cast<const u32x2 *>(a.ws_drhs + wofs);
+    // The gates without a branch (out-of-range rows and threads read zeros).
+    const uint32_t gspan = (uint32_t)(cl.L - 1) * a.Hv * 4 + 4;
+    const __amdgpu_buffer_rsrc_t rg = rsrc_uniform(a.g + cl.p * a.Hv + j, gspan);
+    const __amdgpu_buffer_rsrc_t rb = rsrc_uniform(a.beta + cl.p * a.Hv + j, gspan);
+    const uint32_t goff = tid < kC2 ? (uint32_t)(tid * a.Hv * 4) : 0x40000000u;
+    pre.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+    pre.b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
+}
+
+__device__ __forceinline__ void grads_commit256(GradSmem256 &S, const GradPre256 &pre, int tid) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + kGT * u;
+        *reinterpret_cast<u32x4 *>(S.m.s.M0 + (i >> 5) * kLK2 + 8 * (i & 31)) = pre.m[u];
+        *reinterpret_cast<u32x4 *>(S.m.s.dM + (i >> 5) * kLK2 + 8 * (i & 31)) = pre.d[u];
+    }
+    const int o = (tid >> 4) * kL64 + 4 * (tid & 15);
+    *reinterpret_cast<u32x2 *>(S.u.t.V + o) = pre.v;
+    *reinterpret_cast<u32x2 *>(S.u.t.dO + o) = pre.o;
+    *reinterpret_cast<u32x2 *>(S.u.t.Dl + o) = pre.dl;
+    *reinterpret_cast<u32x2 *>(S.u.t.dR + o) = pre.dr;
+}
+
+__global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
+    __shared__ GradSmem256 S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rb = w & 1, qd = w >> 1;
+    const int G = a.Hv / a.Hqk;
+    const int nsteps = a.dv / 64;
+    const int steps = G * nsteps;
+    const float scale = a.scale;
+    const int64_t total = a.n_chunks * a.Hqk;
+    auto find = [&](int64_t from, ChunkLoc &c, int64_t &g, int &h) {
+        for (int64_t i = from; i < total; i += gridDim.x) {
+            g = i / a.Hqk;
+            h = (int)(i % a.Hqk);
+            if (locate<kC2>(a, g, c))
+                return i;
+        }
+        return total;
+    };
+    ChunkLoc cl;
+    int64_t gc = 0;
+    int hk = 0;
+    int64_t item = find(blockIdx.x, cl, gc, hk);
+    if (item >= total)
+        return;
+    GradPre256 pre;
+    grads_issue256(pre, a, cl, gc, hk * G, 0, tid);
+
+    while (true) {
+    {
+        // This item's K and Q rows: 32 rows of 512 bytes each, two 16-byte
+        // pieces per thread; rows past L read as zeros.
+        const uint32_t row_bytes = (uint32_t)a.Hqk * 256 * 2;
+        const uint32_t span = (uint32_t)(cl.L - 1) * row_bytes + 512;
+        const int64_t base = (cl.p * a.Hqk + hk) * (int64_t)256;
+        const __amdgpu_buffer_rsrc_t rk = rsrc_uniform(static_cast<const uint16_t *>(a.k) + base, span);
+        const __amdgpu_buffer_rsrc_t rq = rsrc_uniform(static_cast<const uint16_t *>(a.q) + base, span);
+        u32x4 kv[2], qv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + kGT * u;
+            const uint32_t off = (i >> 5) * row_bytes + 16 * (i & 31);
+            kv[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+            qv[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        }
+        __syncthreads();  // the previous item's readers are done
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + kGT * u;
+            *reinterpret_cast<u32x4 *>(S.K + (i >> 5) * kLK2 + 8 * (i & 31)) = kv[u];
+            *reinterpret_cast<u32x4 *>(S.Q + (i >> 5) * kLK2 + 8 * (i & 31)) = qv[u];
+        }
+    }
+    ChunkLoc ncl;
+    int64_t ngc = 0;
+    int nhk = 0;
+    const int64_t nitem = find(item + gridDim.x, ncl, ngc, nhk);
+
+    f32x4 dQ[4], dK[4];  // key tiles 4 qd + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dQ[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dK[i] = dQ[i];
+    }
+
+    for (int gi = 0; gi < G; ++gi) {
+        const int j = hk * G + gi;
+        f32x4 dP = {0.f, 0.f, 0.f, 0.f}, dA = dP;  // column tile qd (qd < 2)
+        float pb[4] = {0.f, 0.f, 0.f, 0.f};
+        float pg[4] = {0.f, 0.f, 0.f, 0.f};
+        float msum = 0.0f, lsum = 0.0f;
+        for (int vs = 0; vs < nsteps; ++vs) {
+            const int step = gi * nsteps + vs;
+            __syncthreads();  // the previous step's (or head's) readers are done
+            grads_commit256(S, pre, tid);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                msum += dot8(pre.m[u], pre.d[u]);
+            if (vs == 0 && w == 0) {
+                // Rows past the chunk carry g = 0, so lane 31 holds gamma_{L-1}.
+                const float x = wave_prefix_sum(pre.g);
+                const float gL = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC2 - 1));
+                if (lane < kC2) {
+                    S.gam[lane] = x;
+                    S.e[lane] = __expf(x);
+                    S.l[lane] = __expf(gL - x);
+                    S.bt[lane] = pre.b;
+                }
+                if (lane == 0)
+                    S.eL = __expf(gL);
+            }
+            __syncthreads();
+            {
+                const bool more = step + 1 < steps, next_item = !more && nitem < total;
+                const int sn = more ? step + 1 : next_item ? 0 : step;
+                const int gn = sn / nsteps, vn = sn % nsteps;
+                grads_issue256(pre, a, next_item ? ncl : cl, next_item ? ngc : gc,
+                               (next_item ? nhk : hk) * G + gn, 64 * vn, tid);
+            }
+            int lrv = lane & 15, lgv = lane >> 4;
+            asm volatile("" : "+v"(lrv), "+v"(lgv));
+            const int lr = lrv, lg = lgv;
+
+            // X = K M0, Y = Q M0, U = K dML on rows 16 rb, columns 16 qd.
+            const int c0 = 16 * qd;
+            const f32x4 b4 = ld4f(S.bt + 16 * rb + 4 * lg), e4 = ld4f(S.e + 16 * rb + 4 * lg);
+            const f32x4 l4 = ld4f(S.l + 16 * rb + 4 * lg);
+            f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = X, U = X;
+#pragma unroll
+            for (int kx = 0; kx < 8; ++kx) {
+                const bf16x8 fk = frag_rows(S.K, kLK2, 16 * rb, 32 * kx, lr, lg);
+                const bf16x8 fq = frag_rows(S.Q, kLK2, 16 * rb, 32 * kx, lr, lg);
+                const bf16x8 bm = frag_rows(S.m.s.M0, kLK2, c0, 32 * kx, lr, lg);
+                const bf16x8 bd = frag_rows(S.m.s.dM, kLK2, c0, 32 * kx, lr, lg);
+                X = mma(fk, bm, X);
+                Y = mma(fq, bm, Y);
+                U = mma(fk, bd, U);
+            }
+            {
+                const f32x4 vv = tile_c(S.u.t.V, kL64, 16 * rb, c0, lr, lg);
+                const f32x4 oo = tile_c(S.u.t.dO, kL64, 16 * rb, c0, lr, lg);
+                const f32x4 dl = tile_c(S.u.t.Dl, kL64, 16 * rb, c0, lr, lg);
+                const f32x4 dr = tile_c(S.u.t.dR, kL64, 16 * rb, c0, lr, lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pb[r] += dr[r] * (vv[r] - e4[r] * X[r]);
+                    const float lu = l4[r] * dl[r] * U[r];
+                    pg[r] += e4[r] * scale * oo[r] * Y[r] - b4[r] * e4[r] * dr[r] * X[r] - lu;
+                    lsum += lu;
+                }
+            }
+            // dQ += diag(e) dO M0^T, dK += -diag(beta e) drhs M0^T + diag(l) Delta dML^T
+            // (rows 16 rb, key tiles 4 qd + i); dP += do Delta^T, dA += drhs Delta^T.
+            const int rrow = 16 * rb + lr;
+            const float fe = scale * S.e[rrow], fx = -S.bt[rrow] * S.e[rrow], fl = S.l[rrow];
+#pragma unroll 1
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 ye = frag_rows_scaled(S.u.t.dO, kL64, 16 * rb, 32 * kk, lr, lg, fe);
+                const bf16x8 xe = frag_rows_scaled(S.u.t.dR, kL64, 16 * rb, 32 * kk, lr, lg, fx);
+                const bf16x8 wl = frag_rows_scaled(S.u.t.Dl, kL64, 16 * rb, 32 * kk, lr, lg, fl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int nj = 4 * qd + i;
+                    const bf16x8 bm = frag_cols(S.m.s.M0, kLK2, 32 * kk, 16 * nj, lr, lg);
+                    const bf16x8 bd = frag_cols(S.m.s.dM, kLK2, 32 * kk, 16 * nj, lr, lg);
+                    dQ[i] = mma(ye, bm, dQ[i]);
+                    dK[i] = mma(xe, bm, dK[i]);
+                    dK[i] = mma(wl, bd, dK[i]);
+                }
+                if (qd < 2) {
+                    const bf16x8 fo = frag_rows(S.u.t.dO, kL64, 16 * rb, 32 * kk, lr, lg);
+                    const bf16x8 fr = frag_rows(S.u.t.dR, kL64, 16 * rb, 32 * kk, lr, lg);
+                    const bf16x8 bdl = frag_rows(S.u.t.Dl, kL64, 16 * qd, 32 * kk, lr, lg);
+                    dP = mma(fo, bdl, dP);
+                    dA = mma(fr, bdl, dA);
+                }
+            }
+        }
+        __syncthreads();  // every read of the step tiles is done: the D-phase tiles take their space
+
+        int lrv = lane & 15, lgv = lane >> 4;
+        asm volatile("" : "+v"(lrv), "+v"(lgv));
+        const int lr = lrv, lg = lgv;
+        if (qd < 2) {
+            // K K^T and Q K^T on tile (rb, qd), D, S = diag(beta) (-dA * D),
+            // dP * D and their dbeta and dgamma terms.
+            f32x4 kk4 = {0.f, 0.f, 0.f, 0.f}, qk4 = kk4;
+#pragma unroll
+            for (int kx = 0; kx < 8; ++kx) {
+                const bf16x8 b = frag_rows(S.K, kLK2, 16 * qd, 32 * kx, lr, lg);
+                kk4 = mma(frag_rows(S.K, kLK2, 16 * rb, 32 * kx, lr, lg), b, kk4);
+                qk4 = mma(frag_rows(S.Q, kLK2, 16 * rb, 32 * kx, lr, lg), b, qk4);
+            }
+            const f32x4 grow = ld4f(S.gam + 16 * rb + 4 * lg);
+            const f32x4 brow = ld4f(S.bt + 16 * rb + 4 * lg);
+            const float gcol = S.gam[16 * qd + lr];
+            float cp = 0.0f;
+            float pdv[4], sfv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r, sc = 16 * qd + lr;
+                const bool incl = sc <= row, strict = sc < row;
+                // above the diagonal the exponent may overflow: selected away
+                const float d = incl ? __expf(grow[r] - gcol) : 0.0f;
+                const float dpv = scale * dP[r];
+                const float dav = -dA[r];
+                pdv[r] = incl ? dpv * d : 0.0f;
+                sfv[r] = strict ? brow[r] * dav * d : 0.0f;
+                if (strict)
+                    pb[r] += dav * d * kk4[r];
+                const float dDv = (incl ? dpv * qk4[r] : 0.0f) +
+                                  (strict ? brow[r] * dav * kk4[r] : 0.0f);
+                const float dDD = incl ? dDv * d : 0.0f;
+                pg[r] += dDD;
+                cp -= dDD;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r, sc = 16 * qd + lr;
+                S.u.d.PD[row * kL32 + sc] = f2bf(pdv[r]);
+                S.u.d.Sf[row * kLF2 + sc] = sfv[r];
+            }
+            cp += __shfl_xor(cp, 16);
+            cp += __shfl_xor(cp, 32);
+            if (lg == 0)
+                S.colpart[rb][16 * qd + lr] = cp;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float xb = row16_sum(pb[r]);
+            const float xg = row16_sum(pg[r]);
+            if (lr == 0) {
+                const int row = 16 * rb + 4 * lg + r;
+                S.rowb[qd][row] = xb;
+                S.rowg[qd][row] = xg;
+            }
+        }
+        S.red[tid] = S.eL * msum + lsum;
+        __syncthreads();
+        for (int i = tid; i < kC2 * kC2; i += kGT) {
+            const int r = i >> 5, c = i & 31;
+            S.u.d.SS[r * kL32 + c] = f2bf(S.u.d.Sf[r * kLF2 + c] + S.u.d.Sf[c * kLF2 + r]);
+        }
+        if (w == 0) {
+            float tot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kGT / 64; ++i)
+                tot += S.red[64 * i + lane];
+            const float gl = wave_sum(tot);
+            const int rl = lane & (kC2 - 1);
+            float dgm = S.rowg[0][rl] + S.rowg[1][rl] + S.rowg[2][rl] + S.rowg[3][rl] +
+                        S.colpart[0][rl] + S.colpart[1][rl];
+            if (lane == kC2 - 1)
+                dgm += gl;
+            if (lane >= kC2)
+                dgm = 0.0f;
+            // dg: the reverse cumulative sum over the 32 rows, as a prefix
+            // scan of the row-reversed values.
+            const float rev = __shfl(dgm, (kC2 - 1 - lane) & 63);
+            const float ps = wave_prefix_sum(lane < kC2 ? rev : 0.0f);
+            const float dgs = __shfl(ps, (kC2 - 1 - lane) & 63);
+            int row = lane;
+            asm volatile("" : "+v"(row));
+            if (row < cl.L) {
+                const int64_t o = (cl.p + row) * a.Hv + j;
+                a.dbeta[o] = S.rowb[0][row] + S.rowb[1][row] + S.rowb[2][row] + S.rowb[3][row];
+                a.dg[o] = dgs;
+            }
+        }
+        __syncthreads();
+        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K, over the 32 tokens.
+        {
+            const bf16x8 pr = frag_rows(S.u.d.PD, kL32, 16 * rb, 0, lr, lg);
+            const bf16x8 pc = frag_cols(S.u.d.PD, kL32, 0, 16 * rb, lr, lg);
+            const bf16x8 sr = frag_rows(S.u.d.SS, kL32, 16 * rb, 0, lr, lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int nj = 4 * qd + i;
+                const bf16x8 bk = frag_cols(S.K, kLK2, 0, 16 * nj, lr, lg);
+                const bf16x8 bq = frag_cols(S.Q, kLK2, 0, 16 * nj, lr, lg);
+                dQ[i] = mma(pr, bk, dQ[i]);
+                dK[i] = mma(pc, bq, dK[i]);
+                dK[i] = mma(sr, bk, dK[i]);
+            }
+        }
+    }
+    __syncthreads();  // the last head's readers of the state tiles are done
+
+    // dq and dk through LDS, then 16-byte stores of whole rows.
+    {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rb + 4 * lg + r, colk = 16 * (4 * qd + i) + lr;
+                S.m.out[0][row * kLK2 + colk] = f2bf(dQ[i][r]);
+                S.m.out[1][row * kLK2 + colk] = f2bf(dK[i][r]);
+            }
+    }
+    __syncthreads();
+    for (int e = tid; e < kC2 * 32; e += kGT) {
+        const int row = e >> 5, pc = e & 31;
+        if (row < cl.L) {
+            const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)256 + 8 * pc;
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dq) + o) =
+                *reinterpret_cast<const u32x4 *>(S.m.out[0] + row * kLK2 + 8 * pc);
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dk_) + o) =
+                *reinterpret_cast<const u32x4 *>(S.m.out[1] + row * kLK2 + 8 * pc);
+        }
+    }
+    if (nitem >= total)
+        break;
+    item = nitem;
+    cl = ncl;
+    gc = ngc;
+    hk = nhk;
+    }
+}
+
+// State rows and chunk rows of the workspace: 128-key states and 64-token
+// chunks at dk = 64 and 128 (zeros past dk), 256-key states and 32-token
+// chunks at dk = 256.
+int ws_state_width(int32_t dk) { return dk == 256 ? 256 : kDK; }
+int ws_chunk_rows(int32_t dk) { return dk == 256 ? kC2 : kC; }
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int64_t n_chunks, int32_t Hv, int32_t dk, int32_t dv) {
-    (void)dk;  // the states are kept 128 keys wide (zeros past dk)
     const size_t ch = (size_t)n_chunks * (size_t)Hv;
-    // M0^T and dML^T ([dv][128] bf16), Delta and drhs rows ([64][dv] bf16).
-    return ch * (size_t)dv * (2 * kDK + 2 * kC) * sizeof(uint16_t);
+    // M0^T and dML^T ([dv][width] bf16), Delta and drhs rows ([rows][dv] bf16).
+    return ch * (size_t)dv * (2 * ws_state_width(dk) + 2 * ws_chunk_rows(dk)) * sizeof(uint16_t);
 }
 
 void bwd_carve(BwdArgs &a, void *workspace) {
     const size_t ch = (size_t)a.n_chunks * (size_t)a.Hv;
+    const size_t sw = (size_t)ws_state_width(a.dk), cr = (size_t)ws_chunk_rows(a.dk);
     uint16_t *p = static_cast<uint16_t *>(workspace);
     a.ws_hs = p;
-    p += ch * (size_t)kDK * a.dv;
+    p += ch * sw * a.dv;
     a.ws_dhs = p;
-    p += ch * (size_t)kDK * a.dv;
+    p += ch * sw * a.dv;
     a.ws_delta = p;
-    p += ch * (size_t)kC * a.dv;
+    p += ch * cr * a.dv;
     a.ws_drhs = p;
 }
 
@@ -836,10 +1240,13 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = launch_bwd_state_passes(f, r, stream);
     if (e != hipSuccess)
         return e;
-    // One persistent workgroup per CU (one fits: its LDS is 111 KB).
+    // One persistent workgroup per CU (one fits: its LDS is 146 KB, 124 KB
+    // at dk = 256).
     const int64_t items = a.n_chunks * a.Hqk;
     const unsigned grid = (unsigned)(items < kGradGrid ? items : kGradGrid);
-    if (a.dk > 64)
+    if (a.dk == 256)
+        hipLaunchKernelGGL(bwd_grads_k256, dim3(grid), dim3(kGT), 0, stream, a);
+    else if (a.dk > 64)
         hipLaunchKernelGGL(bwd_grads<4>, dim3(grid), dim3(kGT), 0, stream, a);
     else
         hipLaunchKernelGGL(bwd_grads<2>, dim3(grid), dim3(kGT), 0, stream, a);

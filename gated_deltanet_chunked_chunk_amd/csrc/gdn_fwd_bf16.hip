@@ -1216,7 +1216,7 @@ __device__ __forceinline__ void state_chunk_rev(Smem &S, const ChunkBuf &B, cons
 // blocks: K M0 and Q M0 take eight k-steps (key half h of row block i is
 // tile row block i + 2 h), the solve one substitution step, and the update
 // one 32-deep k-step per key tile (keys 128 h + x from tile rows 32 h ..).
-template <bool Out, bool Nrm>
+template <bool Out, bool Nrm, bool SaveDelta = false>
 __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, const FwdArgs &a,
                                                  const Item &it, int c, int s, int lane,
                                                  f32x4 (&h)[16]) {
@@ -1297,6 +1297,13 @@ __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, con
             R[1] = mma(An, cat(dl[0], dl[0]), R[1]);
         }
     }
+    if constexpr (SaveDelta) {
+        // The backward's forward pass: the chunk's 32 Delta rows (hi part).
+        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)CL * a.dv +
+                        it.c0 + 16 * s;
+        const u32x2 rows[4] = {dh[0], dh[1], kZero2, kZero2};
+        stage_store_rows(S.Ost[s], rows, lane, dst, a.dv, CL);
+    }
     // (a6) M_L = exp(gamma_L) M0 + K^T Delta'; the K^T fragment of key tile
     // mt is tile mt % 8 of tile rows 32 (mt / 8) .., loaded one tile ahead.
     bf16x8 dph, dpl;
@@ -1359,6 +1366,137 @@ __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, con
         if (lane < L)
             *reinterpret_cast<u32x4 *>(o + 8 * hf) = u32x4{r0.x, r0.y, r1.x, r1.y};
     }
+}
+
+// The reverse pass at dk = 256: state_chunk_rev over a chunk of 32 tokens
+// laid into the tiles as in state_chunk_k256 (key half h of chunk row r is
+// tile row 32 h + r): Z = K dM over eight k-steps in four segments, W = P^T
+// dO over the chunk's 32 tokens, one transposed substitution step, and the
+// update of the sixteen key tiles with one 32-deep k-step each.
+__device__ __forceinline__ void state_chunk_rev_k256(Smem &S, const ChunkBuf &B, const FwdArgs &a,
+                                                     const Item &it, int c, int s, int lane,
+                                                     f32x4 (&h)[16]) {
+    constexpr int CL = 32;
+    const int lr = lane & 15, lg = lane >> 4;
+    bf16x8 hb[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+        hb[kk] = cat(pack4(h[2 * kk]), pack4(h[2 * kk + 1]));
+    // Z = K dM (hi part of dM): segment sg is row block sg / 2 and key half
+    // sg % 2 (tile row block m = row block + 2 key half), fragments loaded one
+    // segment ahead.
+    f32x4 Z[2];
+    bf16x8 fk[2][4];
+    const KqBase kb = kq_base(lr, lg);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        fk[0][kk] = frag_kq(B.K, kb, 0, kk);
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+        if (sg < 3) {
+            const int m = ((sg + 1) >> 1) + 2 * ((sg + 1) & 1);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                fk[(sg + 1) & 1][kk] = frag_kq(B.K, kb, m, kk);
+        }
+        const int mi = sg >> 1, hf = sg & 1;
+        if (hf == 0)
+            Z[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            Z[mi] = mma(fk[sg & 1][kk], hb[4 * hf + kk], Z[mi]);
+    }
+    // W = P^T dO over the 32 tokens (A operand: column 16 mi + lr of P,
+    // tokens 8 lg .. + 7; B operand: dO at those tokens, column 16 s + lr).
+    const int r0 = 8 * lg + (lr >> 2);
+    const bf16x8 dob = cat(ld_tr(B.V + v_at(r0, 4 * s + (lr & 3))),
+                           ld_tr(B.V + v_at(r0 + 4, 4 * s + (lr & 3))));
+    f32x4 dD[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const uint16_t *pp = B.P + r0 * kSP + 16 * mi + 4 * (lr & 3);
+        const f32x4 w = mma(cat(ld_tr(pp), ld_tr(pp + 4 * kSP)), dob, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 el4 = ld4f(B.el + 16 * mi + 4 * lg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dD[mi][r] = el4[r] * Z[mi][r] + a.scale * w[r];
+    }
+    // drhs_1 = D_1^T dDelta_1, drhs_0 = D_0^T (dDelta_0 - A_10^T drhs_1).
+    bf16x8 Dt[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int o = (16 * i + lr) * kSDT + 4 * lg;
+        Dt[i] = cat(ld8(B.DhT + o), ld8(B.DlT + o));
+    }
+    const int ao = (4 * lg + (lr >> 2)) * kSN + 4 * (lr & 3);
+    const bf16x8 At = cat(ld_tr(B.Anh + ao), ld_tr(B.Anl + ao));
+    f32x4 DR[2];
+#pragma unroll
+    for (int i = 1; i >= 0; --i) {
+        u32x2 xh, xl;
+        split4(dD[i], xh, xl);
+        f32x4 d = mma(Dt[i], cat(xh, xh), f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mma(Dt[i], cat(xl, xl), d);
+        DR[i] = d;
+        if (i == 1) {
+            u32x2 dh, dl;
+            split4(d, dh, dl);
+            dD[0] = mma(At, cat(dh, dh), dD[0]);
+            dD[0] = mma(At, cat(dl, dl), dD[0]);
+        }
+    }
+    // dM0 = exp(gamma_L) dM + K^T x + Q^T y, x = -diag(beta e) drhs,
+    // y = scale diag(e) dO, as in state_chunk_rev.
+    const int vbase = v_at(4 * lg + (lr >> 2), 4 * s + (lr & 3));
+    u32x2 xh[2], xl[2], yh[2], yl[2], dvv[4], drb[4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const f32x4 bt4 = ld4f(B.bt + 16 * mi + 4 * lg);
+        const f32x4 eg4 = ld4f(B.eg + 16 * mi + 4 * lg);
+        const u32x2 vv = ld_tr(B.V + vbase + 16 * kDVT * mi);
+        f32x4 x, y, dv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float dov = bf2f(static_cast<uint16_t>(vv[r / 2] >> (16 * (r % 2))));
+            x[r] = -(bt4[r] * eg4[r]) * DR[mi][r];
+            y[r] = a.scale * eg4[r] * dov;
+            dv4[r] = bt4[r] * DR[mi][r];
+        }
+        split4(x, xh[mi], xl[mi]);
+        split4(y, yh[mi], yl[mi]);
+        dvv[mi] = pack4(dv4);
+        drb[mi] = pack4(DR[mi]);
+    }
+    dvv[2] = dvv[3] = drb[2] = drb[3] = kZero2;
+    const bf16x8 xbh = cat(xh[0], xh[1]), xbl = cat(xl[0], xl[1]);
+    const bf16x8 ybh = cat(yh[0], yh[1]), ybl = cat(yl[0], yl[1]);
+    const float eL = B.eL;
+    const int ktrow = 4 * lg + (lr >> 2);
+    int ktb = kq_slot(ktrow, lr & 3);
+    asm volatile("" : "+v"(ktb));
+    // The transposed fragment of key tile mt: tile mt % 8 of tile rows
+    // 32 (mt / 8) .., as in state_chunk_k256.
+    auto tf = [&](const uint16_t *X, int mt) {
+        const uint16_t *p = X + (ktb ^ (32 * ((mt & 7) >> 1))) + 4 * (mt & 1) + 32 * (mt >> 3) * kDK;
+        return cat(ld_tr(p), ld_tr(p + 16 * kDK));
+    };
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+        h[mt] *= eL;
+        const bf16x8 kt = tf(B.K, mt), qt = tf(B.Q, mt);
+        h[mt] = mma(kt, xbh, h[mt]);
+        h[mt] = mma(kt, xbl, h[mt]);
+        h[mt] = mma(qt, ybh, h[mt]);
+        h[mt] = mma(qt, ybl, h[mt]);
+    }
+    // drhs rows to the workspace (all 32), dV rows to the output (valid rows).
+    uint16_t *dr = a.chunk_drhs + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)CL * a.dv +
+                   it.c0 + 16 * s;
+    stage_store_rows(S.Ost[s], drb, lane, dr, a.dv, CL);
+    const int L = min(CL, it.len - CL * c);
+    uint16_t *dvo = static_cast<uint16_t *>(a.dv_out) +
+                    ((it.p0 + (int64_t)CL * c) * a.Hv + it.j) * (int64_t)a.dv + it.c0 + 16 * s;
+    stage_store_rows(S.Ost[s], dvv, lane, dvo, (int64_t)a.Hv * a.dv, L);
 }
 
 // Prep: the in-op preparation options of a.flags are honoured (a separate
@@ -1547,18 +1685,22 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                 // The state entering the chunk (Mode 3) or the gradient of
                 // the state leaving it (Mode 4): four consecutive keys per
                 // tile, one 8-byte store each.  The rows are 128 keys wide
-                // whatever DK is (zeros past DK).
+                // at dk = 64 and 128 (zeros past DK), 256 at dk = 256.
+                constexpr int SW = DK == 256 ? 256 : kDK;
                 uint16_t *dst = (Mode == 3 ? a.chunk_states : a.chunk_dstates) +
-                                ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * kDK +
-                                (int64_t)col * kDK;
+                                ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * SW +
+                                (int64_t)col * SW;
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
+                for (int mt = 0; mt < NH; ++mt)
                     *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
             }
-            if constexpr (Mode == 4)
+            if constexpr (Mode == 4 && DK == 256)
+                state_chunk_rev_k256(S, S.buf[i & 1], a, it, c, s, lane, h);
+            else if constexpr (Mode == 4)
                 state_chunk_rev<DK>(S, S.buf[i & 1], a, it, c, s, lane, h);
             else if constexpr (DK == 256)
-                state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[i & 1], a, it, c, s, lane, h);
+                state_chunk_k256<Mode == 0 || Mode == 2, Prep, Mode == 3>(S, S.buf[i & 1], a, it, c,
+                                                                         s, lane, h);
             else
                 state_chunk<Mode == 0 || Mode == 2, Prep, DK, Mode == 3>(S, S.buf[i & 1], a, it, c, s,
                                                                          lane, h);
@@ -1711,11 +1853,16 @@ hipError_t launch_bwd_state_passes(const FwdArgs &fwd, const FwdArgs &rev, hipSt
     const int64_t blocks = (int64_t)fwd.n_seqs * fwd.Hv * (fwd.dv / kDVT);
     if (blocks <= 0)
         return hipSuccess;
-    if (blocks > 0x7fffffff || (fwd.dk != 128 && fwd.dk != 64) || fwd.pieces > 1 || fwd.flags ||
-        !fwd.chunk_states || !fwd.chunk_deltas || !rev.chunk_dstates || !rev.chunk_drhs ||
-        !rev.dv_out)
+    if (blocks > 0x7fffffff || (fwd.dk != 128 && fwd.dk != 64 && fwd.dk != 256) ||
+        fwd.pieces > 1 || fwd.flags || !fwd.chunk_states || !fwd.chunk_deltas ||
+        !rev.chunk_dstates || !rev.chunk_drhs || !rev.dv_out)
         return hipErrorInvalidValue;
-    if (fwd.dk == 128) {
+    if (fwd.dk == 256) {
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 256>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, fwd);
+        hipLaunchKernelGGL((gdn_fwd_bf16<false, 4, 256>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, rev);
+    } else if (fwd.dk == 128) {
         hipLaunchKernelGGL((gdn_fwd_bf16<false, 3, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,
                            stream, fwd);
         hipLaunchKernelGGL((gdn_fwd_bf16<false, 4, 128>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -208,11 +208,12 @@ gdn_status gdn_chunk_fwd_noalloc(gdn_dtype dtype, int64_t B, int64_t T, int32_t 
 
 /*
  * Bytes of device workspace gdn_chunk_bwd needs for these sizes (0 for sizes
- * the backward would reject).  The workspace holds, per chunk of 64 tokens and
- * value head, in bf16: the state entering the chunk and the gradient of the
- * state leaving it (both 128 keys wide whatever dk is), and the chunk's Delta
- * and drhs rows (the solved right-hand side of the forward and of its
- * transpose): (2 * 128 + 2 * 64) * dv * 2 bytes per chunk and head.
+ * the backward would reject).  The workspace holds, per chunk and value head,
+ * in bf16: the state entering the chunk and the gradient of the state leaving
+ * it, and the chunk's Delta and drhs rows (the solved right-hand side of the
+ * forward and of its transpose).  At dk = 64 and 128 a chunk is 64 tokens and
+ * the states are 128 keys wide: (2 * 128 + 2 * 64) * dv * 2 bytes per chunk
+ * and head; at dk = 256 a chunk is 32 tokens: (2 * 256 + 2 * 32) * dv * 2.
  *
  * n_seqs: the number of documents when cu_seqlens will be passed, else B.
  * With cu_seqlens the size covers any split of the T tokens into n_seqs
@@ -234,8 +235,8 @@ size_t gdn_chunk_bwd_workspace_size(gdn_dtype dtype, int64_t B, int64_t T, int32
  *
  *   dtype, B, T, H_qk, H_v, dk, dv, q, k, v, g, beta, scale, h0, cu_seqlens,
  *   cu_seqlens_host, n_seqs
- *                as for gdn_chunk_fwd.  Supported: bf16 with dk in {64, 128}
- *                and dv in {64, 128, 256}; everything else returns
+ *                as for gdn_chunk_fwd.  Supported: bf16 with dk and dv in
+ *                {64, 128, 256}; everything else returns
  *                GDN_ERR_UNSUPPORTED.
  *   flags        the in-op preparation of the forward (GDN_QK_L2NORM,
  *                GDN_GATE_ACT, as for gdn_chunk_fwd): q, k, g and beta are

@@ -193,7 +193,10 @@ def test_bwd_workspace_size():
     assert ws(0, 8, 2048, 16, 16, 128, 128, 8) == 0   # fp32: no backward kernel
     # dk = 64 keeps the chunk states 128 keys wide (zeros past dk): the same size
     assert ws(1, 8, 2048, 16, 16, 64, 128, 8) == ws(1, 8, 2048, 16, 16, 128, 128, 8)
-    assert ws(1, 8, 2048, 16, 16, 256, 128, 8) == 0   # dk = 256: no backward kernel
+    # dk = 256: chunks of 32 tokens, 256-key states and 32 Delta and drhs rows
+    assert ws(1, 8, 2048, 16, 16, 256, 128, 8) == 8 * 64 * 16 * (2 * 256 * 128 * 2 + 2 * 32 * 128 * 2)
+    assert ws(1, 1, 2048, 16, 16, 256, 128, 5) == (64 + 5) * 16 * (2 * 256 * 128 * 2 + 2 * 32 * 128 * 2)
+    assert ws(1, 8, 2048, 16, 16, 512, 128, 8) == 0   # no such head dimension
     assert ws(1, 1, 100, 1, 1, 128, 256, 1) > ws(1, 1, 100, 1, 1, 128, 128, 1)
     # the in-op options add the prepared copies: q and k in bf16, g and beta in fp32
     base = ws(1, 8, 2048, 16, 16, 128, 128, 8)
@@ -223,7 +226,7 @@ def bwd_call(dtype=1, B=1, T=64, Hqk=2, Hv=2, dk=128, dv=128, q=FAKE, k=FAKE, v=
     (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(dq=None), INVALID),
     (dict(dk_=None), INVALID), (dict(dv_=None), INVALID), (dict(dg=None), INVALID),
     (dict(dbeta=None), INVALID), (dict(T=0), INVALID),
-    (dict(dtype=0), UNSUPPORTED), (dict(dk=256), UNSUPPORTED), (dict(dv=96), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED), (dict(dk=512), UNSUPPORTED), (dict(dv=96), UNSUPPORTED),
     (dict(dk=32), UNSUPPORTED), (dict(dv=512), UNSUPPORTED), (dict(Hqk=2, Hv=3), UNSUPPORTED),
     (dict(dk=64, do=FAKE + 8), MISALIGNED), (dict(dv=256, dht=FAKE + 4), MISALIGNED),
     (dict(do=FAKE + 8), MISALIGNED), (dict(dht=FAKE + 4), MISALIGNED),

@@ -125,3 +125,57 @@ def test_bwd_dk64_fla_shape():
     flash-linear-attention benchmark table, all heads against the oracle."""
     d = gi.make(8, 1024, 8, 8, 64, 64, "bf16", 5800, h0_std=0.02)
     check_bwd(d, 5800, label="dk64 8x1024x8")
+
+
+@pytest.mark.parametrize("T,dv", [(1, 64), (31, 128), (33, 64), (100, 256)])
+def test_bwd_dk256(T, dv):
+    """dk = 256: chunks of 32 tokens (the forward's dk = 256 instance), ragged
+    around the chunk, grouped heads, h0, dht and scale."""
+    d = gi.make(2, T, 1, 2, 256, dv, "bf16", 5800 + T, h0_std=0.1)
+    check_bwd(d, 5800 + T, scale=0.8, label=f"dk256 T={T} dv={dv}")
+
+
+def test_bwd_dk256_packed_no_dht():
+    cu = gi.cu_from_lengths([40, 0, 64, 17])
+    d = gi.make(1, 121, 2, 4, 256, 64, "bf16", 5900, h0_std=0.05, cu_seqlens=cu)
+    check_bwd(d, 5900, with_dht=False, label="dk256 packed, no dht")
+
+
+def test_bwd_dk256_deterministic():
+    d = gi.make(1, 90, 1, 1, 256, 128, "bf16", 5950, h0_std=0.1)
+    do, dht = gi.make_upstream(d, 5950)
+    a = run_bwd_gpu(d, do, dht)
+    b = run_bwd_gpu(d, do, dht)
+    for x, y, n in zip(a, b, NAMES):
+        assert np.array_equal(x, y), f"{n} differs between runs"
+
+
+def test_bwd_k256_workload_sampled_heads():
+    """The head-dimension-256 shape of the FLA benchmark table (B=8, T=2048,
+    H=32, D=256) at full size on the GPU; the oracle checks two sampled
+    (row, head) pairs, all six gradients."""
+    import gated_deltanet_chunked_chunk_amd as gdn
+    name = "k256_bf16"
+    c = gi.CONFIGS[name]
+    B, T, H, D = c["B"], c["T"], c["Hv"], c["dk"]
+    dev = torch.device("cuda")
+    t = gi.make_device(B, T, c["Hqk"], H, D, c["dv"], c["seed"], device=dev)
+    gen = torch.Generator(device=dev).manual_seed(c["seed"] + 1)
+    do = torch.randn((B, T, H, c["dv"]), generator=gen, device=dev).to(torch.bfloat16)
+    dht = 0.02 * torch.randn((B, H, D, c["dv"]), generator=gen, device=dev)
+    print(f"[gpu bwd case] k256 workload B={B} T={T} H={H} D={D}", flush=True)
+    got = gdn.gdn_chunk_bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], do, dht=dht)
+    torch.cuda.synchronize()
+    for n in range(6):
+        assert torch.isfinite(got[n]).all(), NAMES[n]
+    for i, h in enumerate(gi.sampled_heads(c["seed"], H, n=2)):
+        b = (3 + 4 * i) % B
+        sl = lambda x: x[b:b + 1, :, h:h + 1].float().cpu().numpy()
+        ref = oracle.gdn_bwd(sl(t["q"]), sl(t["k"]), sl(t["v"]), sl(t["g"]), sl(t["beta"]),
+                             sl(do), dht=dht[b:b + 1, h:h + 1].double().cpu().numpy())
+        for n, (x, y) in enumerate(zip(got, ref)):
+            x = (x[b:b + 1, :, h:h + 1] if n < 5 else x[b:b + 1, h:h + 1]).float().cpu().numpy()
+            e = rel_l2(x, y)
+            tol = TOL_DH0 if NAMES[n] == "dh0" else TOL_BWD
+            print(f"  (b={b}, h={h}) {NAMES[n]} rel-L2 {e:.2e}", flush=True)
+            assert e <= tol, f"{NAMES[n]} (b={b}, h={h}) rel-L2 {e:.3e} > {tol}"

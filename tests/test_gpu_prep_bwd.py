@@ -123,6 +123,7 @@ OPTION_CASES = [
     ("l2 only, dk64, packed", 1, 200, 2, 2, 64, 64, [70, 0, 129, 1], True, False),
     ("gates only, dv256", 1, 150, 1, 1, 128, 256, None, False, True),
     ("both, dk64, ragged", 2, 65, 2, 4, 64, 128, None, True, True),
+    ("both, dk256, packed", 1, 90, 1, 2, 256, 64, [33, 0, 57], True, True),
 ]
 
 
