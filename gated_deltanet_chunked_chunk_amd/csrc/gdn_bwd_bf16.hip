@@ -462,10 +462,12 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     int64_t ngc = 0;
     int nhk = 0;
     const int64_t nitem = find(item + gridDim.x, ncl, ngc, nhk);
-    // This item's K and Q tiles have landed (vmcnt also drains the first
-    // value step's loads, needed next), and every wave is past the previous
-    // item, whose tiles the other half held: the next item's go there now.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    // This item's K and Q tiles have landed (with the first value step's
+    // loads, needed next), and every wave is past the previous item, whose
+    // tiles the other half held: the next item's go there now.  Vector
+    // memory operations complete in order, so waiting until at most KX are
+    // outstanding (the previous item's dq and dk stores) suffices.
+    __builtin_amdgcn_s_waitcnt(0x0f70 | KX);  // vmcnt(KX)
     __syncthreads();
     if (nitem < total) {
         rows_to_lds(S.KQ[par ^ 1][0], a.k, ncl.p, ncl.L, a.Hqk, nhk, a.dk, wu, lane);
@@ -749,15 +751,24 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             }
     }
     __syncthreads();
-    const int pieces = a.dk / 8;  // 16-byte pieces per row
-    for (int e = tid; e < kC * pieces; e += kGT) {
-        const int row = e / pieces, pc = e % pieces;
-        if (row < cl.L) {
-            const int64_t o = ((cl.p + row) * a.Hqk + hk) * (int64_t)a.dk + 8 * pc;
-            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dq) + o) =
-                *reinterpret_cast<const u32x4 *>(S.m.out[0] + row * kLK + 8 * pc);
-            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.dk_) + o) =
-                *reinterpret_cast<const u32x4 *>(S.m.out[1] + row * kLK + 8 * pc);
+    // KX stores per thread, with no branch (rows past L fall outside the
+    // buffer's range and are dropped): the next item waits for everything
+    // but these last KX vector-memory operations.
+    {
+        constexpr int pieces = 4 * KX;  // 16-byte pieces per row (dk / 8)
+        const uint32_t row_bytes = (uint32_t)a.Hqk * a.dk * 2;
+        const uint32_t span = (uint32_t)(cl.L - 1) * row_bytes + a.dk * 2;
+        const int64_t base = (cl.p * a.Hqk + hk) * (int64_t)a.dk;
+        const __amdgpu_buffer_rsrc_t rq = rsrc_uniform(static_cast<uint16_t *>(a.dq) + base, span);
+        const __amdgpu_buffer_rsrc_t rk = rsrc_uniform(static_cast<uint16_t *>(a.dk_) + base, span);
+#pragma unroll
+        for (int e0 = 0; e0 < kC * pieces; e0 += kGT) {
+            const int e = e0 + tid, row = e / pieces, pc = e % pieces;
+            const uint32_t off = row * row_bytes + 16 * pc;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                *reinterpret_cast<const u32x4 *>(S.m.out[0] + row * kLK + 8 * pc), rq, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                *reinterpret_cast<const u32x4 *>(S.m.out[1] + row * kLK + 8 * pc), rk, off, 0, 0);
         }
     }
     if (nitem >= total)
