@@ -107,6 +107,7 @@ constexpr int kSN = 48 + 8;     // -A (rows 16..63, columns 0..47)
 constexpr int kSDT = 16;        // D blocks, transposed (one 32-byte row per column)
 constexpr int kAD = 20;         // column stride of the helpers' A_ii copies (conflict-free column reads)
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
+constexpr float kLog2e = 1.44269504088896341f;
 
 // Tokens per chunk.  With dk = 256 a chunk is 32 tokens, and the two key
 // halves of its rows take the places of rows 0..31 and 32..63 of the
@@ -159,7 +160,7 @@ struct alignas(16) ChunkBuf {
     uint16_t Anl[48 * kSN];     // -A lo
     uint16_t DhT[kC * kSDT];    // D_i^T hi: row 16 i + c is column c of D_i
     uint16_t DlT[kC * kSDT];    // D_i^T lo
-    float gam[kC];              // gamma_r
+    float gam[kC];              // gamma_r log2(e): the decay factors are exp2 of differences
     float eg[kC];               // exp(gamma_r)
     float el[kC];               // exp(gamma_L - gamma_r)
     float bt[kC];               // beta_r
@@ -170,11 +171,14 @@ struct alignas(16) ChunkBuf {
     float pad_[3];
 };
 
+// The fixed-address parts first: below 64 KiB their addresses fit the
+// immediate offset of LDS instructions.
 struct alignas(16) Smem {
-    ChunkBuf buf[2];
-    float Ad[4][16 * kAD];      // -A_ii of the diagonal blocks, column-major (helper wave 0)
+    float Ad[4][16 * kAD];      // -A_ii of the diagonal blocks, column-major (helpers 1..3 write, 0 reads)
     uint16_t Ost[4][16 * kC];   // state wave s: output staging, [col][row], words permuted
     int hsync;                  // helper-wave meeting counter
+    int dsync;                  // diagonal blocks written (helpers 1..3, three per chunk)
+    ChunkBuf buf[2];
 };
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -271,7 +275,9 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
 }
 
 __device__ __forceinline__ u32x2 pack4(f32x4 x) {
-    return u32x2{f2bf(x[0]) | (unsigned)f2bf(x[1]) << 16, f2bf(x[2]) | (unsigned)f2bf(x[3]) << 16};
+    const bf16x2 h01 = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+    const bf16x2 h23 = {static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+    return u32x2{__builtin_bit_cast(unsigned, h01), __builtin_bit_cast(unsigned, h23)};
 }
 
 constexpr u32x2 kZero2 = {0u, 0u};
@@ -496,7 +502,7 @@ __device__ __forceinline__ void a_finish(ChunkBuf &B, f32x4 c, int lr, int lg) {
     f32x4 val;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        val[r] = -b * __expf(g - gc[r]) * c[r];
+        val[r] = -b * __builtin_amdgcn_exp2f(g - gc[r]) * c[r];
     u32x2 hi, lo;
     split4(val, hi, lo);
     const int o = (16 * I + lr - 16) * kSN + 16 * J + 4 * lg;
@@ -522,9 +528,9 @@ __device__ __forceinline__ void p_finish(ChunkBuf &B, f32x4 c, int lr, int lg) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         if (J < I) {
-            val[r] = __expf(g - gc[r]) * c[r];
+            val[r] = __builtin_amdgcn_exp2f(g - gc[r]) * c[r];
         } else {
-            const float e = __expf(fminf(g - gc[r], 0.0f));
+            const float e = __builtin_amdgcn_exp2f(fminf(g - gc[r], 0.0f));
             val[r] = 4 * lg + r <= lr ? e * c[r] : 0.0f;
         }
     }
@@ -548,15 +554,9 @@ __device__ __forceinline__ void diag_finish(float *ad, const ChunkBuf &B, f32x4 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int col = 4 * lg + r;  // column within the block; the row is lr
-        const float e = __expf(fminf(g - gc[r], 0.0f));
+        const float e = __builtin_amdgcn_exp2f(fminf(g - gc[r], 0.0f));
         ad[col * kAD + lr] = col < lr ? -(b * e * c[r]) : 0.0f;
     }
-}
-
-template <int I, bool Nrm, int DK>
-__device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const bf16x8 (&ki)[4],
-                                           int lr, int lg) {
-    diag_finish<I, Nrm>(ad, B, block_product<DK / 32>(ki, ki), lr, lg);
 }
 
 // (a4) D_i = (I + A_ii)^-1 by forward substitution in fp32, the four blocks
@@ -564,34 +564,51 @@ __device__ __forceinline__ void diag_block(float *ad, const ChunkBuf &B, const b
 // column-major) and lane c of the row computes column c.  Once x_r is final,
 // -A[r2][r] x_r is added to every row r2 > r; the factors -A[r2][r] are
 // column r of the copy, which every lane of the row reads at the same
-// addresses (a broadcast read, one 16-byte read per four factors).  Column c
-// is stored, as hi and lo bf16, as row 16 g + c of D^T.
+// addresses (a broadcast read, one 16-byte read per four factors).  The
+// reads run a few steps ahead of the multiply-adds, so the dependent steps
+// do not each wait for LDS.  Column c is stored, as hi and lo bf16, as
+// row 16 g + c of D^T.
 template <int R>
-__device__ __forceinline__ void dinv_step(float (&x)[16], const float *ad) {
-    constexpr int Q0 = (R + 1) / 4;  // first quad of rows holding an r2 > R
-    f32x4 col[4];
+__device__ __forceinline__ void dinv_load(f32x4 (&col)[15][4], const float *ad) {
+    if constexpr (R < 15) {
 #pragma unroll
-    for (int q = Q0; q < 4; ++q)
-        col[q] = ld4f(ad + R * kAD + 4 * q);
+        for (int q = (R + 1) / 4; q < 4; ++q)
+            col[R][q] = ld4f(ad + R * kAD + 4 * q);
+    }
+}
+
+template <int Ahead, int R>
+__device__ __forceinline__ void dinv_step(float (&x)[16], f32x4 (&col)[15][4], const float *ad) {
+    dinv_load<R + Ahead>(col, ad);
 #pragma unroll
     for (int r2 = R + 1; r2 < 16; ++r2)
-        x[r2] = __builtin_fmaf(col[r2 / 4][r2 % 4], x[R], x[r2]);
+        x[r2] = __builtin_fmaf(col[R][r2 / 4][r2 % 4], x[R], x[r2]);
 }
 
 template <int... R>
-__device__ __forceinline__ void dinv_steps(float (&x)[16], const float *ad,
+__device__ __forceinline__ void dinv_loads(f32x4 (&col)[15][4], const float *ad,
                                            std::integer_sequence<int, R...>) {
-    (dinv_step<R>(x, ad), ...);
+    (dinv_load<R>(col, ad), ...);
 }
 
+template <int Ahead, int... R>
+__device__ __forceinline__ void dinv_steps(float (&x)[16], f32x4 (&col)[15][4], const float *ad,
+                                           std::integer_sequence<int, R...>) {
+    (dinv_step<Ahead, R>(x, col, ad), ...);
+}
+
+// Ahead: how many steps the reads run ahead of the multiply-adds.
+template <int Ahead>
 __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int lane) {
     const int c = lane & 15, g = lane >> 4;
     const float *ad = S.Ad[g];
+    f32x4 col[15][4];  // col[r][q]: rows 4 q .. 4 q + 3 of column r (quads holding a row > r)
+    dinv_loads(col, ad, std::make_integer_sequence<int, Ahead>{});
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         x[r] = (r == c) ? 1.0f : 0.0f;
-    dinv_steps(x, ad, std::make_integer_sequence<int, 15>{});
+    dinv_steps<Ahead>(x, col, ad, std::make_integer_sequence<int, 15>{});
     u32x4 hi[2], lo[2];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -610,72 +627,86 @@ __device__ __forceinline__ void diag_inverse_all(ChunkBuf &B, const Smem &S, int
     dl[1] = lo[1];
 }
 
-// The per-chunk products, split over the helper waves: helper 0 forms the
-// four diagonal blocks of A and their inverses; helpers 1 .. 3 form the
-// off-diagonal blocks of A and the blocks of P (six, five and five blocks).
-// Without WithP (no output is formed) the P blocks are skipped; Nrm folds
-// the in-op L2 norms of the rows into the blocks.
+// The per-chunk products, split over the helper waves.  The diagonal blocks
+// of A come first on helpers 1..3 (A11; A00, A22; A33), each from row blocks
+// of K the helper loads for its other products anyway; once a helper's are in
+// LDS it counts itself on dsync.  Helper 0 forms P00, waits for the three
+// counts and inverts the four blocks, the longest dependent piece of work;
+// the rest of A and P is spread so that helpers 1..3 end at about the same
+// time.  Without WithP (no output is formed) the P blocks are skipped; Nrm
+// folds the in-op L2 norms of the rows into the blocks.  dmeet counts the
+// diagonal-block signals helper 0 has waited for.
 template <bool WithP, bool Nrm, int DK>
-__device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg, int lane) {
+__device__ __forceinline__ void helper_products(Smem &S, ChunkBuf &B, int hw, int lr, int lg,
+                                                int lane, int &dmeet) {
+    constexpr int KK = DK / 32;
     const KqBase kb = kq_base(lr, lg);
-    if (hw == 0) {
-        bf16x8 k[2][4];
-        load_block<DK / 32>(k[0], B.K, kb, 0);
-        load_block<DK / 32>(k[1], B.K, kb, 1);
-        diag_block<0, Nrm, DK>(S.Ad[0], B, k[0], lr, lg);
-        load_block<DK / 32>(k[0], B.K, kb, 2);
-        diag_block<1, Nrm, DK>(S.Ad[1], B, k[1], lr, lg);
-        load_block<DK / 32>(k[1], B.K, kb, 3);
-        diag_block<2, Nrm, DK>(S.Ad[2], B, k[0], lr, lg);
-        diag_block<3, Nrm, DK>(S.Ad[3], B, k[1], lr, lg);
-        diag_inverse_all(B, S, lane);
-    } else if (hw == 1) {  // A30 A31 A32, P00 P10 P11
-        bf16x8 k3[4], q[4], kj[2][4];
-        load_block<DK / 32>(k3, B.K, kb, 3);
-        load_block<DK / 32>(kj[0], B.K, kb, 0);
-        load_block<DK / 32>(q, B.Q, kb, 0);
-        load_block<DK / 32>(kj[1], B.K, kb, 1);
-        a_block<3, 0, Nrm, DK>(B, k3, kj[0], lr, lg);
+    auto diag_done = [&]() {
+        if (lane == 0)
+            __hip_atomic_fetch_add(&S.dsync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    dmeet += 3;
+    if (hw == 0) {  // P00, then the inverses
+        if constexpr (WithP) {
+            bf16x8 q0[4], k0[4];
+            load_block<KK>(q0, B.Q, kb, 0);
+            load_block<KK>(k0, B.K, kb, 0);
+            p_block<0, 0, Nrm, DK>(B, q0, k0, lr, lg);
+        }
+        while (__hip_atomic_load(&S.dsync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < dmeet)
+            __builtin_amdgcn_s_sleep(1);
+        diag_inverse_all<4>(B, S, lane);
+    } else if (hw == 1) {  // A11; A31 A30 A32, P10 P11
+        bf16x8 k1[4], k3[4], kj[4], q1[4];
+        load_block<KK>(k1, B.K, kb, 1);
+        load_block<KK>(k3, B.K, kb, 3);
+        diag_finish<1, Nrm>(S.Ad[1], B, block_product<KK>(k1, k1), lr, lg);
+        diag_done();
+        load_block<KK>(kj, B.K, kb, 0);
+        load_block<KK>(q1, B.Q, kb, 1);
+        a_block<3, 1, Nrm, DK>(B, k3, k1, lr, lg);
+        a_block<3, 0, Nrm, DK>(B, k3, kj, lr, lg);
         if constexpr (WithP)
-            p_block<0, 0, Nrm, DK>(B, q, kj[0], lr, lg);
-        load_block<DK / 32>(q, B.Q, kb, 1);
-        a_block<3, 1, Nrm, DK>(B, k3, kj[1], lr, lg);
+            p_block<1, 0, Nrm, DK>(B, q1, kj, lr, lg);
+        load_block<KK>(kj, B.K, kb, 2);
         if constexpr (WithP)
-            p_block<1, 0, Nrm, DK>(B, q, kj[0], lr, lg);
-        load_block<DK / 32>(kj[0], B.K, kb, 2);
+            p_block<1, 1, Nrm, DK>(B, q1, k1, lr, lg);
+        a_block<3, 2, Nrm, DK>(B, k3, kj, lr, lg);
+    } else if (hw == 2) {  // A00 A22; A20 A21, P20 P21 P22
+        bf16x8 k0[4], k2[4], q2[4], k1[4];
+        load_block<KK>(k0, B.K, kb, 0);
+        load_block<KK>(k2, B.K, kb, 2);
+        diag_finish<0, Nrm>(S.Ad[0], B, block_product<KK>(k0, k0), lr, lg);
+        diag_finish<2, Nrm>(S.Ad[2], B, block_product<KK>(k2, k2), lr, lg);
+        diag_done();
+        load_block<KK>(q2, B.Q, kb, 2);
+        load_block<KK>(k1, B.K, kb, 1);
+        a_block<2, 0, Nrm, DK>(B, k2, k0, lr, lg);
         if constexpr (WithP)
-            p_block<1, 1, Nrm, DK>(B, q, kj[1], lr, lg);
-        a_block<3, 2, Nrm, DK>(B, k3, kj[0], lr, lg);
-    } else if (hw == 2) {  // A20 A21, P20 P21 P22
-        bf16x8 k2[4], q2[4], kj[2][4];
-        load_block<DK / 32>(k2, B.K, kb, 2);
-        load_block<DK / 32>(q2, B.Q, kb, 2);
-        load_block<DK / 32>(kj[0], B.K, kb, 0);
-        load_block<DK / 32>(kj[1], B.K, kb, 1);
-        a_block<2, 0, Nrm, DK>(B, k2, kj[0], lr, lg);
-        if constexpr (WithP)
-            p_block<2, 0, Nrm, DK>(B, q2, kj[0], lr, lg);
-        a_block<2, 1, Nrm, DK>(B, k2, kj[1], lr, lg);
-        if constexpr (WithP)
-            p_block<2, 1, Nrm, DK>(B, q2, kj[1], lr, lg);
-        if constexpr (WithP)
+            p_block<2, 0, Nrm, DK>(B, q2, k0, lr, lg);
+        a_block<2, 1, Nrm, DK>(B, k2, k1, lr, lg);
+        if constexpr (WithP) {
+            p_block<2, 1, Nrm, DK>(B, q2, k1, lr, lg);
             p_block<2, 2, Nrm, DK>(B, q2, k2, lr, lg);
-    } else {  // A10, P30 P31 P32 P33
-        bf16x8 k1[4], q3[4], kj[2][4];
-        load_block<DK / 32>(k1, B.K, kb, 1);
-        load_block<DK / 32>(q3, B.Q, kb, 3);
-        load_block<DK / 32>(kj[0], B.K, kb, 0);
-        load_block<DK / 32>(kj[1], B.K, kb, 2);
-        a_block<1, 0, Nrm, DK>(B, k1, kj[0], lr, lg);
+        }
+    } else {  // A33; A10, P33 P30 P31 P32
+        bf16x8 k3[4], q3[4], k1[4], kj[4];
+        load_block<KK>(k3, B.K, kb, 3);
         if constexpr (WithP)
-            p_block<3, 0, Nrm, DK>(B, q3, kj[0], lr, lg);
+            load_block<KK>(q3, B.Q, kb, 3);
+        diag_finish<3, Nrm>(S.Ad[3], B, block_product<KK>(k3, k3), lr, lg);
+        diag_done();
+        load_block<KK>(k1, B.K, kb, 1);
+        load_block<KK>(kj, B.K, kb, 0);
         if constexpr (WithP)
+            p_block<3, 3, Nrm, DK>(B, q3, k3, lr, lg);
+        a_block<1, 0, Nrm, DK>(B, k1, kj, lr, lg);
+        if constexpr (WithP) {
+            p_block<3, 0, Nrm, DK>(B, q3, kj, lr, lg);
             p_block<3, 1, Nrm, DK>(B, q3, k1, lr, lg);
-        load_block<DK / 32>(kj[0], B.K, kb, 3);
-        if constexpr (WithP)
-            p_block<3, 2, Nrm, DK>(B, q3, kj[1], lr, lg);
-        if constexpr (WithP)
-            p_block<3, 3, Nrm, DK>(B, q3, kj[0], lr, lg);
+            load_block<KK>(kj, B.K, kb, 2);
+            p_block<3, 2, Nrm, DK>(B, q3, kj, lr, lg);
+        }
     }
 }
 
@@ -707,7 +738,8 @@ __device__ __forceinline__ void helper_products_k256(Smem &S, ChunkBuf &B, int h
     if (hw == 0) {
         diag_finish<0, Nrm>(S.Ad[0], B, gram256<0, 0>(B.K, B.K, kb), lr, lg);
         diag_finish<1, Nrm>(S.Ad[1], B, gram256<1, 1>(B.K, B.K, kb), lr, lg);
-        diag_inverse_all(B, S, lane);  // blocks 2, 3 invert the identity left in Ad[2], Ad[3]
+        // blocks 2, 3 invert the identity left in Ad[2], Ad[3]
+        diag_inverse_all<3>(B, S, lane);
     } else if (hw == 1) {
         a_finish<1, 0, Nrm>(B, gram256<1, 0>(B.K, B.K, kb), lr, lg);
         if constexpr (WithP)
@@ -725,7 +757,7 @@ __device__ __forceinline__ void helper_products_k256(Smem &S, ChunkBuf &B, int h
 // during the products below and the state waves' whole next chunk.
 template <bool Prep, bool Full, int DK>
 __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, int hw, int t,
-                                               int lane, int &meet, const FwdArgs &a,
+                                               int lane, int &meet, int &dmeet, const FwdArgs &a,
                                                const Item &it, int L, int next) {
     hw = __builtin_amdgcn_readfirstlane(hw);  // uniform: scalar branches below
     const int lr = lane & 15, lg = lane >> 4;
@@ -776,7 +808,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
             gv = lane < L ? fminf(gv, 0.0f) - __logf(1.0f + __expf(-fabsf(gv))) : 0.0f;
         const float x = wave_prefix_sum(gv);
         const float gL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-        B.gam[lane] = x;
+        B.gam[lane] = x * kLog2e;
         B.eg[lane] = __expf(x);
         B.el[lane] = __expf(gL - x);
         if (!gate_act)
@@ -807,7 +839,7 @@ __device__ __forceinline__ void helper_prepare(Smem &S, ChunkBuf &B, Stage &st, 
     if constexpr (DK == 256)
         helper_products_k256<Full, Prep>(S, B, hw, lr, lg, lane);
     else
-        helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane);
+        helper_products<Full, Prep, DK>(S, B, hw, lr, lg, lane, dmeet);
 }
 
 // Writes a wave's 64 x 16 block, given as four C-layout tiles of bf16 pairs
@@ -1587,8 +1619,10 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             S.Ad[3][i] = 0.0f;
         }
     }
-    if (tid == 0)
+    if (tid == 0) {
         S.hsync = 0;
+        S.dsync = 0;
+    }
     __syncthreads();
 
     const bool state = wv < 4;
@@ -1602,7 +1636,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 
     f32x4 h[NH];
     Stage st;
-    int meet = 0;
+    int meet = 0, dmeet = 0;
     // Issue priority on the shared SIMDs follows the critical paths: the
     // state waves' chain first, then helper 0 (diagonal blocks and their
     // inverses); helpers 1..3 fill the gaps.
@@ -1638,7 +1672,7 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         const int c0 = Mode == 4 ? it.nchunks - 1 : 0;
         const int c1 = Mode == 4 ? it.nchunks - 2 : 1;
         stage_load<kFull, DK>(st, a, it, c0, t, lane);
-        helper_prepare<Prep, kFull, DK>(S, S.buf[0], st, s, t, lane, meet, a, it,
+        helper_prepare<Prep, kFull, DK>(S, S.buf[0], st, s, t, lane, meet, dmeet, a, it,
                                         min(CL, it.len - CL * c0), it.nchunks > 1 ? c1 : -1);
     }
     lds_barrier();
@@ -1654,33 +1688,13 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
         }
     }
     it.chunk0 = chunk0;
-    if constexpr (Prep) {
-        // One chunk loop per role (the barrier counts match): the state
-        // slice and the helpers' prefetch registers are then never live
-        // together, which the preparation's extra registers need.
-        if (state) {
-            for (int c = 0; c < it.nchunks; ++c) {
-                if constexpr (DK == 256)
-                    state_chunk_k256<Mode == 0 || Mode == 2, Prep>(S, S.buf[c & 1], a, it, c, s, lane, h);
-                else
-                    state_chunk<Mode == 0 || Mode == 2, Prep, DK>(S, S.buf[c & 1], a, it, c, s, lane, h);
-                lds_barrier();
-            }
-        } else {
-            for (int c = 0; c < it.nchunks; ++c) {
-                if (c + 1 < it.nchunks)
-                    helper_prepare<Prep, kFull, DK>(S, S.buf[(c + 1) & 1], st, s, t, lane, meet, a,
-                                                    it, min(CL, it.len - CL * (c + 1)),
-                                                    c + 2 < it.nchunks ? c + 2 : -1);
-                lds_barrier();
-            }
-        }
-    } else {
+    // One chunk loop per role (the barrier counts match): the state slice and
+    // the helpers' prefetch registers are then never live together.
     // Iteration i works on chunk c(i): in order, or from the last (Mode 4).
     auto cidx = [&](int i) { return Mode == 4 ? it.nchunks - 1 - i : i; };
-    for (int i = 0; i < it.nchunks; ++i) {
-        const int c = cidx(i);
-        if (state) {
+    if (state) {
+        for (int i = 0; i < it.nchunks; ++i) {
+            const int c = cidx(i);
             if (Mode == 3 || Mode == 4) {
                 // The state entering the chunk (Mode 3) or the gradient of
                 // the state leaving it (Mode 4): four consecutive keys per
@@ -1704,14 +1718,16 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             else
                 state_chunk<Mode == 0 || Mode == 2, Prep, DK, Mode == 3>(S, S.buf[i & 1], a, it, c, s,
                                                                          lane, h);
-        } else if (i + 1 < it.nchunks) {
-            const int cn = cidx(i + 1);
-            helper_prepare<Prep, kFull, DK>(S, S.buf[(i + 1) & 1], st, s, t, lane, meet, a, it,
-                                            min(CL, it.len - CL * cn),
-                                            i + 2 < it.nchunks ? cidx(i + 2) : -1);
+            lds_barrier();
         }
-        lds_barrier();
-    }
+    } else {
+        for (int i = 0; i < it.nchunks; ++i) {
+            if (i + 1 < it.nchunks)
+                helper_prepare<Prep, kFull, DK>(S, S.buf[(i + 1) & 1], st, s, t, lane, meet, dmeet, a,
+                                                it, min(CL, it.len - CL * cidx(i + 1)),
+                                                i + 2 < it.nchunks ? cidx(i + 2) : -1);
+            lds_barrier();
+        }
     }
 
     if (state) {
