@@ -50,6 +50,23 @@ def test_bf16_strong_decay_and_zero_beta():
     check(d, label="bf16 gate extremes")
 
 
+@pytest.mark.parametrize("g", [-0.1, -0.3, -1.0])
+def test_bf16_steady_decay_rescaling(g):
+    """Steady decays of about g per token: the state loses a factor of e^6 to
+    e^64 per chunk, so the carried state ranges from mattering over several
+    chunks to vanishing within one."""
+    d = gi.make(1, 400, 2, 2, 128, 128, "bf16", 3500, h0_std=0.3)
+    rng = np.random.default_rng(1)
+    d["g"] = (g * (1.0 + 0.1 * rng.standard_normal(d["g"].shape))).astype(np.float32)
+    check(d, label=f"bf16 steady decay {g}")
+
+
+def test_bf16_negative_scale():
+    """A negative attention scale."""
+    d = gi.make(1, 150, 2, 2, 128, 128, "bf16", 3600, h0_std=0.2)
+    check(d, scale=-0.25, label="bf16 negative scale")
+
+
 def test_headline_workload_full_size():
     """B=8, T=2048, H=16, d=128, bf16, zero state: the benchmarked launch."""
     check(gi.make_config("headline_bf16"), label="headline 8x2048x16x128")
