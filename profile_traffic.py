@@ -19,6 +19,13 @@
         cycles, LDS bank conflicts against LDS instruction cycles, waves and
         the GPU's busy clocks, averaged over the kernel's dispatches.
 
+    python3 profile_traffic.py issue PMC_DIR_A PMC_DIR_B --command CMD [--workload W]
+        Writes profiles/counters_issue_W.md (and .json) from two `rocprofv3
+        --pmc` runs of `launch` with the two counter lists of ISSUE_COUNTERS:
+        the fractions of the waves' cycles spent executing VALU and LDS
+        instructions, waiting to issue and waiting for anything, and the
+        instruction counts per wave.
+
     python3 profile_traffic.py stats STATS_DIR --command CMD [--name NAME] [--by-grid]
         Writes profiles/kernel_stats_NAME.md (default headline_bf16) from a
         `rocprofv3 --kernel-trace --stats` run of bench.py; with --by-grid,
@@ -254,6 +261,60 @@ def counters(dirname, command, workload):
     print("\n".join(lines))
 
 
+ISSUE_COUNTERS = [
+    ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+     "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_VALU_MFMA_BUSY_CYCLES",
+     "GRBM_GUI_ACTIVE"],
+    ["SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+     "SQ_WAIT_INST_LDS", "SQ_LDS_CMD_FIFO_FULL", "SQ_LDS_DATA_FIFO_FULL", "SQ_WAVES",
+     "GRBM_GUI_ACTIVE"],
+]
+
+
+def issue(dir_a, dir_b, command, workload):
+    """Writes profiles/counters_issue_W.md from two `rocprofv3 --pmc` runs of
+    `launch` with the two lists in ISSUE_COUNTERS: how the waves spend their
+    cycles (executing VALU or LDS instructions, waiting to issue, waiting for
+    anything) as fractions of SQ_WAVE_CYCLES (all four in quad-cycles, summed
+    over the waves), and instruction counts per wave and dispatch."""
+    kernel = KERNELS[workload]
+    vals = {}
+    for d, names in ((dir_a, ISSUE_COUNTERS[0]), (dir_b, ISSUE_COUNTERS[1])):
+        for c in names:
+            per = read_counter(d, c)
+            _, kv = pick(per, kernel)
+            vals[c if c not in vals else c + " (2nd run)"] = sum(kv) / len(kv)
+    wc = vals["SQ_WAVE_CYCLES"]
+    waves = vals["SQ_WAVES"]
+    clocks = vals["GRBM_GUI_ACTIVE"] / 8
+    frac = {k: vals[k] / wc for k in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                                      "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")}
+    per_wave = {k: vals[k] / waves for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS")}
+    sources = bench.BWD_KERNEL_SOURCES if workload.startswith("fwd_bwd") else None
+    out = {"kernel": kernel, "workload": workload, "command": command,
+           "kernel_source_sha256": bench.kernel_source_hash(sources), "per_dispatch": vals,
+           "fraction_of_wave_cycles": frac, "instructions_per_wave": per_wave,
+           "mfma_busy_per_simd": vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (clocks * 1024),
+           "valu_mfma_coexec_per_simd": vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / (clocks * 1024)}
+    with open(os.path.join(PROFILES, f"counters_issue_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# Issue and wait counters of {kernel}, {workload}", "", "Commands:", "", "```",
+             command, "```", "", "| counter | per dispatch (average) |", "|---|---|"]
+    for c, v in vals.items():
+        lines.append(f"| {c} | {v:.4g} |")
+    lines += ["", "Fractions of SQ_WAVE_CYCLES (the waves' lifetimes; two waves share each SIMD):", ""]
+    for k, v in frac.items():
+        lines.append(f"- {k}: {v:.3f}")
+    lines += ["", "Per wave and dispatch: " + ", ".join(f"{k} {v:.0f}" for k, v in per_wave.items()) + ".",
+              f"MFMA busy per SIMD {out['mfma_busy_per_simd']:.3f}; MFMA and another VALU "
+              f"instruction together {out['valu_mfma_coexec_per_simd']:.3f} of each SIMD's clocks "
+              f"(both over GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).",
+              f"Kernel source sha256 {out['kernel_source_sha256']}."]
+    with open(os.path.join(PROFILES, f"counters_issue_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def trace_rows(dirname):
     """Rows like the stats CSV's, one per (kernel, grid size), from the trace."""
     files = glob.glob(os.path.join(dirname, "**", "*kernel_trace.csv"), recursive=True)
@@ -326,6 +387,11 @@ def main():
     c.add_argument("pmc_dir")
     c.add_argument("--command", required=True)
     c.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
+    i = sub.add_parser("issue")
+    i.add_argument("dir_a")
+    i.add_argument("dir_b")
+    i.add_argument("--command", required=True)
+    i.add_argument("--workload", default="headline_bf16", choices=sorted(KERNELS))
     s = sub.add_parser("stats")
     s.add_argument("stats_dir")
     s.add_argument("--command", required=True)
@@ -342,6 +408,8 @@ def main():
         traffic(args.fetch_dir, args.write_dir, args.command, args.workload)
     elif args.cmd == "counters":
         counters(args.pmc_dir, args.command, args.workload)
+    elif args.cmd == "issue":
+        issue(args.dir_a, args.dir_b, args.command, args.workload)
     else:
         stats(args.stats_dir, args.command, args.name, args.title, args.only, args.by_grid)
 
