@@ -71,6 +71,7 @@ constexpr int kLK = 136;   // row stride (bf16) of K and Q tiles
 constexpr int kL64 = 72;   // row stride (bf16) of 64-wide tiles
 constexpr int kLF = 65;    // row stride (fp32) of 64-wide fp32 tiles
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
+constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kGT = 512;   // bwd_grads threads
 constexpr int64_t kGradGrid = 256;  // bwd_grads workgroups: one per CU
 
@@ -302,7 +303,7 @@ struct alignas(16) GradSmem {
     // The small tables and the step tiles first, so that their addresses
     // fit the 16-bit immediate offsets of LDS instructions.  Every tile
     // starts 16-byte aligned (alignas): its 16-byte accesses need it.
-    float gam[kC], e[kC], l[kC], bt[kC];
+    float gam[kC], e[kC], l[kC], bt[kC];  // gam: gamma log2(e), the decays are exp2 of differences
     float rowb[2][kC], rowg[2][kC];
     float colpart[4][kC];
     float red[kGT];
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 const float x = wave_prefix_sum(pre.g);
                 const float gL = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC - 1));
-                S.gam[lane] = x;
+                S.gam[lane] = x * kLog2e;
                 S.e[lane] = __expf(x);
                 S.l[lane] = __expf(gL - x);
                 S.bt[lane] = pre.b;
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 const int row = 16 * rb + 4 * lg + r, sc = 16 * (2 * hd + i) + lr;
                 const bool incl = sc <= row, strict = sc < row;
                 // above the diagonal the exponent may overflow: selected away
-                const float d = incl ? __expf(grow[r] - gcol[i]) : 0.0f;
+                const float d = incl ? __builtin_amdgcn_exp2f(grow[r] - gcol[i]) : 0.0f;
                 const float dpv = scale * dP[i][r];
                 const float dav = -dA[i][r];
                 pdv[i][r] = incl ? dpv * d : 0.0f;
@@ -969,7 +970,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 const float gL = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), kC2 - 1));
                 if (lane < kC2) {
-                    S.gam[lane] = x;
+                    S.gam[lane] = x * kLog2e;
                     S.e[lane] = __expf(x);
                     S.l[lane] = __expf(gL - x);
                     S.bt[lane] = pre.b;
@@ -1069,7 +1070,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 const int row = 16 * rb + 4 * lg + r, sc = 16 * qd + lr;
                 const bool incl = sc <= row, strict = sc < row;
                 // above the diagonal the exponent may overflow: selected away
-                const float d = incl ? __expf(grow[r] - gcol) : 0.0f;
+                const float d = incl ? __builtin_amdgcn_exp2f(grow[r] - gcol) : 0.0f;
                 const float dpv = scale * dP[r];
                 const float dav = -dA[r];
                 pdv[r] = incl ? dpv * d : 0.0f;

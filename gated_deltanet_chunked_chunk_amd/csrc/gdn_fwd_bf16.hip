@@ -1697,16 +1697,19 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
             const int c = cidx(i);
             if (Mode == 3 || Mode == 4) {
                 // The state entering the chunk (Mode 3) or the gradient of
-                // the state leaving it (Mode 4): four consecutive keys per
-                // tile, one 8-byte store each.  The rows are 128 keys wide
-                // at dk = 64 and 128 (zeros past DK), 256 at dk = 256.
+                // the state leaving it (Mode 4): the tiles 2 k and 2 k + 1
+                // hold keys 32 k + 8 lg .. + 7 of column col in order, one
+                // 16-byte store.  The rows are 128 keys wide at dk = 64 and
+                // 128 (zeros past DK), 256 at dk = 256.
                 constexpr int SW = DK == 256 ? 256 : kDK;
                 uint16_t *dst = (Mode == 3 ? a.chunk_states : a.chunk_dstates) +
                                 ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * SW +
                                 (int64_t)col * SW;
 #pragma unroll
-                for (int mt = 0; mt < NH; ++mt)
-                    *reinterpret_cast<u32x2 *>(dst + key_of(mt, lg, 0)) = pack4(h[mt]);
+                for (int mt = 0; mt < NH; mt += 2) {
+                    const u32x2 lo = pack4(h[mt]), hi = pack4(h[mt + 1]);
+                    *reinterpret_cast<u32x4 *>(dst + key_of(mt, lg, 0)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
             }
             if constexpr (Mode == 4 && DK == 256)
                 state_chunk_rev_k256(S, S.buf[i & 1], a, it, c, s, lane, h);
