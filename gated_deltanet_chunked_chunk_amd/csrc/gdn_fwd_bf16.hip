@@ -987,13 +987,6 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         }
     }
 
-    if constexpr (SaveDelta) {
-        // The backward's forward pass: the chunk's Delta rows (hi part).
-        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)kC * a.dv +
-                        it.c0 + 16 * s;
-        stage_store_rows(S.Ost[s], dh, lane, dst, a.dv, kC);
-    }
-
     // (a6) M_L = exp(gamma_L) M0 + K^T Delta', Delta' = diag(exp(gamma_L - gamma)) Delta,
     // K^T fragments loaded one tile ahead of the products.
     bf16x8 dph[2], dpl[2];
@@ -1040,6 +1033,13 @@ __device__ __forceinline__ void state_chunk(Smem &S, const ChunkBuf &B, const Fw
         }
     }
 
+    if constexpr (SaveDelta) {
+        // The backward's forward pass: the chunk's Delta rows (hi part),
+        // after the update, which does not wait for them.
+        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)kC * a.dv +
+                        it.c0 + 16 * s;
+        stage_store_rows(S.Ost[s], dh, lane, dst, a.dv, kC);
+    }
     if constexpr (!Out)
         return;
     // (a7) O += P Delta (hi parts); this wave's 64 x 16 block to HBM through
