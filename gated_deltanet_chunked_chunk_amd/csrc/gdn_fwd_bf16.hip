@@ -1329,13 +1329,6 @@ __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, con
             R[1] = mma(An, cat(dl[0], dl[0]), R[1]);
         }
     }
-    if constexpr (SaveDelta) {
-        // The backward's forward pass: the chunk's 32 Delta rows (hi part).
-        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)CL * a.dv +
-                        it.c0 + 16 * s;
-        const u32x2 rows[4] = {dh[0], dh[1], kZero2, kZero2};
-        stage_store_rows(S.Ost[s], rows, lane, dst, a.dv, CL);
-    }
     // (a6) M_L = exp(gamma_L) M0 + K^T Delta'; the K^T fragment of key tile
     // mt is tile mt % 8 of tile rows 32 (mt / 8) .., loaded one tile ahead.
     bf16x8 dph, dpl;
@@ -1368,6 +1361,14 @@ __device__ __forceinline__ void state_chunk_k256(Smem &S, const ChunkBuf &B, con
         h[mt] = mma(kt[mt & 1], dpl, h[mt]);
     }
 
+    if constexpr (SaveDelta) {
+        // The backward's forward pass: the chunk's 32 Delta rows (hi part),
+        // after the update, which does not wait for them.
+        uint16_t *dst = a.chunk_deltas + ((it.chunk0 + c) * a.Hv + it.j) * (int64_t)CL * a.dv +
+                        it.c0 + 16 * s;
+        const u32x2 rows[4] = {dh[0], dh[1], kZero2, kZero2};
+        stage_store_rows(S.Ost[s], rows, lane, dst, a.dv, CL);
+    }
     if constexpr (!Out)
         return;
     // (a7) O += P Delta (hi parts), staged through LDS as in state_chunk.
