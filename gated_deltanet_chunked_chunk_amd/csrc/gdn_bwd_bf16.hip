@@ -69,11 +69,21 @@ constexpr int kC = 64;     // chunk length
 constexpr int kDK = 128;   // key dimension
 constexpr int kLK = 136;   // row stride (bf16) of K and Q tiles
 constexpr int kL64 = 72;   // row stride (bf16) of 64-wide tiles
-constexpr int kLF = 65;    // row stride (fp32) of 64-wide fp32 tiles
 constexpr unsigned kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit elements
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kGT = 512;   // bwd_grads threads
 constexpr int64_t kGradGrid = 256;  // bwd_grads workgroups: one per CU
+
+// Barrier for LDS hand-offs between the waves: waits for this wave's LDS
+// operations only, so vector-memory loads in flight (the prefetched tiles)
+// stay in flight across it.  Loads that write LDS directly are waited for
+// explicitly (vmcnt) where their tiles are first read.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+}
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -288,9 +298,12 @@ __device__ __forceinline__ void rows_to_lds(uint16_t *tile, const void *src, int
 
 // ---------------------------------------------------------------------------
 // bwd_grads: per (chunk, q/k head), 512 threads, one persistent workgroup per
-// CU walking the (chunk, q/k head) items; each item's first value step is
-// loaded during the previous item's last one.  Wave w works on the
-// chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the half hd = w / 4 of
+// CU walking the (chunk, q/k head) items.  Each item's K and Q rows are
+// loaded into registers at the start of the item before it and stored to the
+// other half of the K/Q tiles once that item's value steps are done; its
+// first value step is loaded during that item's last one.  The barriers wait
+// for LDS operations only, so these loads stay in flight across them.  Wave
+// w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the half hd = w / 4 of
 // every [64 x *] result: of a 64-column value step the columns 32 hd ..,
 // of dq and dk the key tiles 4 hd .. 4 hd + 3, of the 64 x 64 products the
 // column tiles 2 hd, 2 hd + 1.  The value heads of the q/k head are taken in
@@ -317,8 +330,7 @@ struct alignas(16) GradSmem {
         } t;
         struct {
             uint16_t PD[kC * kL64];  // scale dP * D (diagonal included)
-            uint16_t SS[kC * kL64];  // S + S^T
-            float Sf[kC * kLF];      // S = diag(beta) (-dA * D), strictly lower
+            uint16_t SS[kC * kL64];  // S + S^T, S = diag(beta) (-dA * D) strictly lower
         } d;
     } u;
     alignas(16) union {
@@ -395,6 +407,45 @@ __device__ __forceinline__ void grads_commit(GradSmem &S, const GradPre &pre, in
     *reinterpret_cast<u32x4 *>(S.u.t.dR + o) = pre.dr;
 }
 
+// The next item's K and Q rows in registers: thread t holds 16-byte pieces
+// t + kGT u (row i / (dk / 8), piece i % (dk / 8)) of each; rows past L, and
+// every piece when there is no next item (a buffer of no bytes), read as
+// zeros.  Loaded at an item's start, stored to the other K/Q half of LDS once
+// the item's value steps are done.
+template <int KX>
+struct KQPre {
+    u32x4 k[KX / 2], q[KX / 2];
+};
+
+template <int KX>
+__device__ __forceinline__ void kq_issue(KQPre<KX> &pre, const BwdArgs &a, const ChunkLoc &cl,
+                                         int hk, bool any, int tid) {
+    constexpr int pieces = 4 * KX;  // per row
+    const uint32_t row_bytes = (uint32_t)a.Hqk * a.dk * 2;
+    const uint32_t span = any ? (uint32_t)(cl.L - 1) * row_bytes + a.dk * 2 : 0u;
+    const int64_t base = (cl.p * a.Hqk + hk) * (int64_t)a.dk;
+    const __amdgpu_buffer_rsrc_t rk = rsrc_uniform(static_cast<const uint16_t *>(a.k) + base, span);
+    const __amdgpu_buffer_rsrc_t rq = rsrc_uniform(static_cast<const uint16_t *>(a.q) + base, span);
+#pragma unroll
+    for (int u = 0; u < KX / 2; ++u) {
+        const int i = tid + kGT * u, row = i / pieces, pc = i % pieces;
+        const uint32_t off = row * row_bytes + 16 * pc;
+        pre.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        pre.q[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    }
+}
+
+template <int KX>
+__device__ __forceinline__ void kq_commit(uint16_t *sK, uint16_t *sQ, const KQPre<KX> &pre, int tid) {
+    constexpr int pieces = 4 * KX;
+#pragma unroll
+    for (int u = 0; u < KX / 2; ++u) {
+        const int i = tid + kGT * u, row = i / pieces, pc = i % pieces;
+        *reinterpret_cast<u32x4 *>(sK + row * kLK + 8 * pc) = pre.k[u];
+        *reinterpret_cast<u32x4 *>(sQ + row * kLK + 8 * pc) = pre.q[u];
+    }
+}
+
 // An A operand (rows row0 + lr, k0 + 8 lg .. + 7 of a row-major bf16 tile)
 // multiplied by the row's factor f and rounded back to bf16.
 __device__ __forceinline__ bf16x8 frag_rows_scaled(const uint16_t *t, int ld, int row0, int k0,
@@ -463,17 +514,17 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     int64_t ngc = 0;
     int nhk = 0;
     const int64_t nitem = find(item + gridDim.x, ncl, ngc, nhk);
-    // This item's K and Q tiles have landed (with the first value step's
-    // loads, needed next), and every wave is past the previous item, whose
-    // tiles the other half held: the next item's go there now.  Vector
-    // memory operations complete in order, so waiting until at most KX are
-    // outstanding (the previous item's dq and dk stores) suffices.
+    // This item's K and Q tiles are in LDS (the first item's loaded straight
+    // into LDS above, later ones stored from registers by every wave before
+    // this barrier) and its first value step's loads, needed next, have
+    // landed; every wave is past the previous item, whose tiles the other
+    // half held, so the next item's K and Q can be loaded for that half now.
+    // Vector memory operations complete in order, so waiting until at most
+    // KX are outstanding (the previous item's dq and dk stores) suffices.
     __builtin_amdgcn_s_waitcnt(0x0f70 | KX);  // vmcnt(KX)
-    __syncthreads();
-    if (nitem < total) {
-        rows_to_lds(S.KQ[par ^ 1][0], a.k, ncl.p, ncl.L, a.Hqk, nhk, a.dk, wu, lane);
-        rows_to_lds(S.KQ[par ^ 1][1], a.q, ncl.p, ncl.L, a.Hqk, nhk, a.dk, wu, lane);
-    }
+    lds_barrier();
+    KQPre<KX> kqn;
+    kq_issue<KX>(kqn, a, nitem < total ? ncl : cl, nitem < total ? nhk : hk, nitem < total, tid);
     const uint16_t *sK = S.KQ[par][0], *sQ = S.KQ[par][1];
 
     f32x4 dQ[4], dK[4];   // key tiles 4 hd + i
@@ -497,7 +548,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
         float lsum = 0.0f;                    // this thread's part of sum_r l_r Delta U
         for (int vs = 0; vs < nsteps; ++vs) {
             const int step = gi * nsteps + vs;
-            __syncthreads();  // the previous step's (or head's) readers are done
+            lds_barrier();  // the previous step's (or head's) readers are done
             grads_commit(S, pre, tid);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -515,7 +566,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 if (lane == 0)
                     S.eL = __expf(gL);
             }
-            __syncthreads();
+            lds_barrier();
             {
                 // One issue site with no branch around it (two sites, or a
                 // skipped issue, made the compiler copy the loaded registers
@@ -607,7 +658,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 }
             }
         }
-        __syncthreads();  // every read of the step tiles is done: the D-phase tiles take their space
+        lds_barrier();  // every read of the step tiles is done: the D-phase tiles take their space
+        if (gi + 1 == G)
+            kq_commit<KX>(S.KQ[par ^ 1][0], S.KQ[par ^ 1][1], kqn, tid);
 
         // Through A and P: D, S = diag(beta) (-dA * D), dP * D, and their
         // dbeta and dgamma terms.
@@ -663,7 +716,16 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * lg + r, sc = 16 * (2 * hd + i) + lr;
                 S.u.d.PD[row * kL64 + sc] = f2bf(pdv[i][r]);
-                S.u.d.Sf[row * kLF + sc] = sfv[i][r];
+                // S is strictly lower, so S + S^T holds S's element at (row,
+                // sc) and at (sc, row) and zero on the diagonal: each wave
+                // writes its own tile's nonzeros to both places.
+                if (sc < row) {
+                    const uint16_t sv = f2bf(sfv[i][r] + 0.0f);  // a -0 is stored as +0, the sum with S^T's zero
+                    S.u.d.SS[row * kL64 + sc] = sv;
+                    S.u.d.SS[sc * kL64 + row] = sv;
+                } else if (sc == row) {
+                    S.u.d.SS[row * kL64 + sc] = 0;
+                }
             }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -686,11 +748,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
         // d gamma_L: exp(gamma_L) sum(M0 * dML) from the state term and
         // sum_r l_r Delta U from the l terms.
         S.red[tid] = S.eL * msum + lsum;
-        __syncthreads();
-        for (int i = tid; i < kC * kC; i += kGT) {
-            const int r = i >> 6, c = i & 63;
-            S.u.d.SS[r * kL64 + c] = f2bf(S.u.d.Sf[r * kLF + c] + S.u.d.Sf[c * kLF + r]);
-        }
+        lds_barrier();
         if (w == 0) {
             float tot = 0.0f;
 #pragma unroll
@@ -716,8 +774,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 a.dg[o] = dgs;
             }
         }
-        __syncthreads();
-        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K.
+        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K (wave 0's tables
+        // above are not written again before the next head's barriers).
 #pragma unroll 1
         for (int kk = 0; kk < 2; ++kk) {
             const bf16x8 pr = frag_rows(S.u.d.PD, kL64, 16 * rb, 32 * kk, lr, lg);
@@ -736,7 +794,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             }
         }
     }
-    __syncthreads();  // the last head's readers of the state tiles are done
+    lds_barrier();  // the last head's readers of the state tiles are done
 
     // dq and dk through LDS, then 16-byte stores of whole rows.
     {
@@ -751,7 +809,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
                 dks[row * kLK + colk] = f2bf(dK[i][r]);
             }
     }
-    __syncthreads();
+    lds_barrier();
     // KX stores per thread, with no branch (rows past L fall outside the
     // buffer's range and are dropped): the next item waits for everything
     // but these last KX vector-memory operations.
@@ -794,7 +852,6 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
 constexpr int kC2 = 32;    // tokens per chunk at dk = 256
 constexpr int kLK2 = 264;  // row stride (bf16) of 256-wide tiles
 constexpr int kL32 = 40;   // row stride (bf16) of 32-wide tiles
-constexpr int kLF2 = 33;   // row stride (fp32) of 32-wide fp32 tiles
 
 struct alignas(16) GradSmem256 {
     float gam[kC2], e[kC2], l[kC2], bt[kC2];
@@ -813,8 +870,7 @@ struct alignas(16) GradSmem256 {
         } t;
         struct {
             uint16_t PD[kC2 * kL32];  // scale dP * D (diagonal included)
-            uint16_t SS[kC2 * kL32];  // S + S^T
-            float Sf[kC2 * kLF2];     // S = diag(beta) (-dA * D), strictly lower
+            uint16_t SS[kC2 * kL32];  // S + S^T, S = diag(beta) (-dA * D) strictly lower
         } d;
     } u;
     alignas(16) union {
@@ -931,7 +987,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
             kv[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
             qv[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         }
-        __syncthreads();  // the previous item's readers are done
+        lds_barrier();  // the previous item's readers are done
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = tid + kGT * u;
@@ -959,7 +1015,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
         float msum = 0.0f, lsum = 0.0f;
         for (int vs = 0; vs < nsteps; ++vs) {
             const int step = gi * nsteps + vs;
-            __syncthreads();  // the previous step's (or head's) readers are done
+            lds_barrier();  // the previous step's (or head's) readers are done
             grads_commit256(S, pre, tid);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -978,7 +1034,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 if (lane == 0)
                     S.eL = __expf(gL);
             }
-            __syncthreads();
+            lds_barrier();
             {
                 const bool more = step + 1 < steps, next_item = !more && nitem < total;
                 const int sn = more ? step + 1 : next_item ? 0 : step;
@@ -1045,7 +1101,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 }
             }
         }
-        __syncthreads();  // every read of the step tiles is done: the D-phase tiles take their space
+        lds_barrier();  // every read of the step tiles is done: the D-phase tiles take their space
 
         int lrv = lane & 15, lgv = lane >> 4;
         asm volatile("" : "+v"(lrv), "+v"(lgv));
@@ -1087,7 +1143,14 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rb + 4 * lg + r, sc = 16 * qd + lr;
                 S.u.d.PD[row * kL32 + sc] = f2bf(pdv[r]);
-                S.u.d.Sf[row * kLF2 + sc] = sfv[r];
+                // S + S^T from S's strictly lower elements, as at dk <= 128.
+                if (sc < row) {
+                    const uint16_t sv = f2bf(sfv[r] + 0.0f);  // a -0 is stored as +0, the sum with S^T's zero
+                    S.u.d.SS[row * kL32 + sc] = sv;
+                    S.u.d.SS[sc * kL32 + row] = sv;
+                } else if (sc == row) {
+                    S.u.d.SS[row * kL32 + sc] = 0;
+                }
             }
             cp += __shfl_xor(cp, 16);
             cp += __shfl_xor(cp, 32);
@@ -1105,11 +1168,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
             }
         }
         S.red[tid] = S.eL * msum + lsum;
-        __syncthreads();
-        for (int i = tid; i < kC2 * kC2; i += kGT) {
-            const int r = i >> 5, c = i & 31;
-            S.u.d.SS[r * kL32 + c] = f2bf(S.u.d.Sf[r * kLF2 + c] + S.u.d.Sf[c * kLF2 + r]);
-        }
+        lds_barrier();
         if (w == 0) {
             float tot = 0.0f;
 #pragma unroll
@@ -1136,8 +1195,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 a.dg[o] = dgs;
             }
         }
-        __syncthreads();
-        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K, over the 32 tokens.
+        // dQ += (dP * D) K; dK += (dP * D)^T Q + (S + S^T) K, over the 32 tokens
+        // (wave 0's tables above are not written again before the next
+        // head's barriers).
         {
             const bf16x8 pr = frag_rows(S.u.d.PD, kL32, 16 * rb, 0, lr, lg);
             const bf16x8 pc = frag_cols(S.u.d.PD, kL32, 0, 16 * rb, lr, lg);
@@ -1153,7 +1213,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
             }
         }
     }
-    __syncthreads();  // the last head's readers of the state tiles are done
+    lds_barrier();  // the last head's readers of the state tiles are done
 
     // dq and dk through LDS, then 16-byte stores of whole rows.
     {
@@ -1167,7 +1227,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
                 S.m.out[1][row * kLK2 + colk] = f2bf(dK[i][r]);
             }
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < kC2 * 32; e += kGT) {
         const int row = e >> 5, pc = e & 31;
         if (row < cl.L) {
