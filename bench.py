@@ -475,9 +475,11 @@ def measure_packed(gdn, gi, torch, dev, steps, warmup, name="packed_gva_bf16"):
 
 
 def measure_tiny(gdn, gi, torch, dev):
-    """The tiny fp32 workload (B=1, T=256, H=2, d=64): launch-latency bound,
-    so only its absolute time is reported (per-launch events, back to back),
-    with the whole output checked against the oracle."""
+    """The tiny fp32 workload (B=1, T=256, H=2, d=64): four workgroups (one
+    per head and 32 value columns) walk four chunks each, so the time is the
+    latency of one workgroup's chunk steps in fp32 vector arithmetic, not
+    bandwidth; only its absolute time is reported (per-launch events, back to
+    back), with the whole output checked against the oracle."""
     import oracle
     d = gi.make_config("tiny_f32")
     tt = {x: torch.from_numpy(d[x]).to(dev) for x in ("q", "k", "v", "g", "beta")}
@@ -493,7 +495,8 @@ def measure_tiny(gdn, gi, torch, dev):
     log(f"[bench] tiny fp32: {tm['median'] * 1e3:.1f} us per launch (median); rel-L2 output "
         f"{eo:.2e}, state {eh:.2e}")
     return {"workload": "tiny_f32: B=1 T=256 H=2 dk=64 dv=64, fp32, zero initial state",
-            "launch_ms": tm, "bound": "launch latency (absolute time only)",
+            "launch_ms": tm,
+            "bound": "latency of 4 workgroups' fp32 chunk steps (absolute time only)",
             "check": {"rel_l2_output": eo, "rel_l2_state": eh}}
 
 

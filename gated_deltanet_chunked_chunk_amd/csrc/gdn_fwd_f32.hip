@@ -3,9 +3,9 @@
 // The same chunk equations as the bf16 kernel, evaluated entirely in fp32
 // vector arithmetic (products, the triangular solve and the state), with the
 // accurate expf.  fp32 inputs come with tolerances tighter than a bf16 MFMA
-// path can meet, and the workloads that use them are small, so this kernel
-// favours plainness: one workgroup per (sequence, value head, 32 value
-// columns), every step an LDS-staged loop separated by barriers.  Chunks are
+// path can meet, and the workloads that use them are small: one workgroup
+// per (sequence, value head, 32 value columns), every step a loop over
+// register tiles of LDS-staged operands, separated by barriers.  Chunks are
 // 64 tokens, or 32 with dk = 256 (so that the K and Q tiles fit in LDS).
 //
 // Per chunk of L <= C tokens starting from state M0 ([dk][dv], M = S^T):
@@ -33,24 +33,46 @@ constexpr int chunk_f32() {
     return DK == 256 ? 32 : 64;
 }
 
+// K, Q, P and T' are held transposed (a column of the row-major matrix is a
+// row here), so that a thread's register tile of consecutive rows reads one
+// 16-byte word per step of the contraction; rows are 16-byte aligned.
 template <int DK, int kC = chunk_f32<DK>()>
 struct SmemF32 {
-    float K[kC][DK + 1];
-    float Q[kC][DK + 1];
-    float V[kC][kDVT + 1];
-    float M[DK][kDVT + 1];      // state slice
-    alignas(16) float T[kC][kC + 4];  // A, then T' = (I + A)^-1 diag(beta); 16-byte rows
-    float P[kC][kC + 1];        // (Q K^T) * D
-    float Y[kC][kDVT + 1];      // V - diag(exp gamma) K M0, then Delta
-    float gam[kC], bt[kC], el[kC];
+    alignas(16) float KT[DK][kC + 4];    // KT[d][r] = K[r][d]
+    alignas(16) float QT[DK][kC + 4];    // QT[d][r] = Q[r][d]
+    alignas(16) float V[kC][kDVT + 4];   // V rows, then Delta
+    alignas(16) float M[DK][kDVT + 4];   // state slice
+    alignas(16) float A[kC][kC + 4];     // A (strictly lower), row r's column s at (s % 4) C/4 + s / 4
+    alignas(16) float TT[kC][kC + 4];    // TT[s][r] = T'[r][s], T' = (I + A)^-1 diag(beta)
+    alignas(16) float PT[kC][kC + 4];    // PT[s][r] = P[r][s], P = (Q K^T) * D
+    alignas(16) float Y[kC][kDVT + 4];   // V - diag(exp gamma) K M0
+    alignas(16) float gam[kC], bt[kC], el[kC], eg[kC];
 };
 
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ float4 ld4(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+
+__device__ __forceinline__ float2 ld2(const float *p) {
+    return *reinterpret_cast<const float2 *>(p);
+}
+
+// Thread (i, j) = (tid / 16, tid % 16) owns register tiles of consecutive
+// rows TR i .. of the chunk (TR = C / 16) and, for [C x 32] results, the
+// value columns 2 j, 2 j + 1; for the C x C products the rows TR j .. of the
+// other operand; for the state update the keys TD i .. (TD = dk / 16).  Each
+// element is still one running sum in the order of its contraction index.
 template <int DK>
 __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
     constexpr int kC = chunk_f32<DK>();
+    constexpr int TR = kC / 16, TD = DK / 16;
+    typedef __attribute__((ext_vector_type(TR))) float rowv;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SmemF32<DK> &S = *reinterpret_cast<SmemF32<DK> *>(smem_raw);
     const int tid = threadIdx.x;
+    const int ti = tid >> 4, tj = tid & 15;
     const int n_tiles = a.dv / kDVT;
     const int G = a.Hv / a.Hqk;
     const int w = blockIdx.x;
@@ -72,6 +94,15 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
     const float *v = static_cast<const float *>(a.v);
     float *o = static_cast<float *>(a.o);
     const int64_t hbase = ((int64_t)n * a.Hv + j) * DK * (int64_t)a.dv;
+    auto rows = [](const float *p) {  // TR consecutive entries of a 16-byte aligned row
+        if constexpr (TR == 4) {
+            const float4 x = ld4(p);
+            return rowv{x.x, x.y, x.z, x.w};
+        } else {
+            const float2 x = ld2(p);
+            return rowv{x.x, x.y};
+        }
+    };
 
     for (int e = tid; e < DK * kDVT; e += kThreads) {
         const int i = e / kDVT, c = e % kDVT;
@@ -82,32 +113,47 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         const int L = (int)min<int64_t>(kC, p1 - p);
         __syncthreads();
         // Every load of the chunk is issued before any is stored, so their
-        // latencies overlap instead of adding up.
+        // latencies overlap instead of adding up.  K and Q: a wave-wide load
+        // covers 16 rows x 16 keys (a 16-byte piece per lane) and stores it
+        // transposed with no two lanes on one LDS bank.  Rows past the
+        // chunk's end load row L - 1 and are replaced by zeros (a select of
+        // values: the loads stay unconditional).
         {
-            constexpr int KPT = kC * DK / kThreads, VPT = kC * kDVT / kThreads;
-            float kr[KPT], qr[KPT], vr[VPT];
+            constexpr int KPT = kC * DK / (4 * kThreads), VPT = kC * kDVT / (4 * kThreads);
+            f32x4 kr[KPT], qr[KPT], vr[VPT];
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
-                const int e = tid + kThreads * i, r = e / DK, d = e % DK;
-                const int64_t off = ((p + r) * a.Hqk + hk) * DK + d;
-                kr[i] = r < L ? k[off] : 0.0f;
-                qr[i] = r < L ? q[off] : 0.0f;
+                const int e = tid + kThreads * i, blk = e >> 6, l = e & 63;
+                const int r = 16 * (blk % (kC / 16)) + (l & 15), d = 16 * (blk / (kC / 16)) + 4 * (l >> 4);
+                const int64_t off = ((p + min(r, L - 1)) * a.Hqk + hk) * DK + d;
+                const f32x4 kx = *reinterpret_cast<const f32x4 *>(k + off);
+                const f32x4 qx = *reinterpret_cast<const f32x4 *>(q + off);
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                kr[i] = r < L ? kx : z;
+                qr[i] = r < L ? qx : z;
             }
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int e = tid + kThreads * i, r = e / kDVT, c = e % kDVT;
-                vr[i] = r < L ? v[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + c] : 0.0f;
+                const int e = tid + kThreads * i, r = e / (kDVT / 4), c = 4 * (e % (kDVT / 4));
+                const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 vx = *reinterpret_cast<const f32x4 *>(
+                    v + ((p + min(r, L - 1)) * a.Hv + j) * (int64_t)a.dv + c0 + c);
+                vr[i] = r < L ? vx : z;
             }
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
-                const int e = tid + kThreads * i, r = e / DK, d = e % DK;
-                S.K[r][d] = kr[i];
-                S.Q[r][d] = qr[i];
+                const int e = tid + kThreads * i, blk = e >> 6, l = e & 63;
+                const int r = 16 * (blk % (kC / 16)) + (l & 15), d = 16 * (blk / (kC / 16)) + 4 * (l >> 4);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    S.KT[d + u][r] = kr[i][u];
+                    S.QT[d + u][r] = qr[i][u];
+                }
             }
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int e = tid + kThreads * i, r = e / kDVT, c = e % kDVT;
-                S.V[r][c] = vr[i];
+                const int e = tid + kThreads * i, r = e / (kDVT / 4), c = 4 * (e % (kDVT / 4));
+                *reinterpret_cast<f32x4 *>(&S.V[r][c]) = vr[i];
             }
         }
         if (tid < 64) {
@@ -136,6 +182,7 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
                 S.gam[r] = mine;
                 S.bt[r] = bv;
                 S.el[r] = expf(acc - mine);
+                S.eg[r] = expf(mine);
             }
         }
         __syncthreads();
@@ -143,105 +190,221 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
             // In-op L2 normalisation: one wave per row of K or Q (fp32).
             const int lane = tid & 63;
             for (int row = tid >> 6; row < 2 * kC; row += kThreads / 64) {
-                float *x = row < kC ? S.K[row] : S.Q[row - kC];
+                float(*x)[kC + 4] = row < kC ? S.KT : S.QT;
+                const int rr = row < kC ? row : row - kC;
                 float ss = 0.0f;
                 for (int d = lane; d < DK; d += 64)
-                    ss += x[d] * x[d];
+                    ss += x[d][rr] * x[d][rr];
                 for (int o = 32; o >= 1; o >>= 1)
                     ss += __shfl_xor(ss, o);
                 const float inv = inv_l2_norm(ss);
                 for (int d = lane; d < DK; d += 64)
-                    x[d] *= inv;
+                    x[d][rr] *= inv;
             }
             __syncthreads();
         }
 
-        // A (strictly lower) and P (lower incl. diagonal).
-        for (int e = tid; e < kC * kC; e += kThreads) {
-            const int r = e / kC, s = e % kC;
-            float kk = 0.0f, qk = 0.0f;
-            if (s <= r) {
-                for (int d = 0; d < DK; ++d) {
-                    kk += S.K[r][d] * S.K[s][d];
-                    qk += S.Q[r][d] * S.K[s][d];
+        // A (strictly lower) and P (lower incl. diagonal) on the register
+        // tile rows TR ti .., columns TR tj .. (tiles above the diagonal
+        // are never read and not formed).
+        if (tj <= ti) {
+            rowv kk[TR], qk[TR];  // [row t][column u]
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                kk[t] = rowv{};
+                qk[t] = rowv{};
+            }
+#pragma unroll 8
+            for (int d = 0; d < DK; ++d) {
+                const rowv kr = rows(&S.KT[d][TR * ti]), qr = rows(&S.QT[d][TR * ti]);
+                const rowv ks = rows(&S.KT[d][TR * tj]);
+#pragma unroll
+                for (int t = 0; t < TR; ++t)
+#pragma unroll
+                    for (int u = 0; u < TR; ++u) {
+                        kk[t][u] = __builtin_fmaf(kr[t], ks[u], kk[t][u]);
+                        qk[t][u] = __builtin_fmaf(qr[t], ks[u], qk[t][u]);
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < TR; ++t)
+#pragma unroll
+                for (int u = 0; u < TR; ++u) {
+                    const int r = TR * ti + t, s = TR * tj + u;
+                    const float dec = s <= r ? expf(S.gam[r] - S.gam[s]) : 0.0f;
+                    S.A[r][(s & 3) * (kC / 4) + (s >> 2)] = s < r ? S.bt[r] * dec * kk[t][u] : 0.0f;
+                    S.PT[s][r] = dec * qk[t][u];
+                }
+        }
+        // Y = V - diag(exp gamma) K M0 on rows TR ti .., columns 2 tj, 2 tj + 1.
+        {
+            rowv x0 = rowv{}, x1 = rowv{};
+#pragma unroll 8
+            for (int d = 0; d < DK; ++d) {
+                const rowv kr = rows(&S.KT[d][TR * ti]);
+                const float2 m = ld2(&S.M[d][2 * tj]);
+#pragma unroll
+                for (int t = 0; t < TR; ++t) {
+                    x0[t] = __builtin_fmaf(kr[t], m.x, x0[t]);
+                    x1[t] = __builtin_fmaf(kr[t], m.y, x1[t]);
                 }
             }
-            const float dec = s <= r ? expf(S.gam[r] - S.gam[s]) : 0.0f;
-            S.T[r][s] = s < r ? S.bt[r] * dec * kk : 0.0f;
-            S.P[r][s] = dec * qk;
-        }
-        // Y = V - diag(exp gamma) K M0
-        for (int e = tid; e < kC * kDVT; e += kThreads) {
-            const int r = e / kDVT, c = e % kDVT;
-            float x = 0.0f;
-            for (int d = 0; d < DK; ++d)
-                x += S.K[r][d] * S.M[d][c];
-            S.Y[r][c] = S.V[r][c] - expf(S.gam[r]) * x;
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                const int r = TR * ti + t;
+                const float2 vv = ld2(&S.V[r][2 * tj]);
+                *reinterpret_cast<float2 *>(&S.Y[r][2 * tj]) =
+                    float2{vv.x - S.eg[r] * x0[t], vv.y - S.eg[r] * x1[t]};
+            }
         }
         __syncthreads();
 
-        // T = (I + A)^-1 column by column: thread c of wave 0 solves column c
-        // by forward substitution, reading only A (every thread reads the
-        // same A[r][s]: broadcast reads); T' = T diag(beta) replaces A after
-        // the barrier.  The loops are unrolled so x stays in registers; its
-        // entries above the diagonal are zero, so the sums can start at 0.
-        // Each row's sum runs in four interleaved partial sums over 16-byte
-        // reads of the row, so the loads and the multiply-adds pipeline.
-        float x[kC];
-        if (tid < kC) {
-            const int c = tid;
+        // T = (I + A)^-1 column by column, x = (I + A)^-1 e_c by forward
+        // substitution: x_r = [r == c] - sum_{s < r} A[r][s] x_s.  Four lanes
+        // share column c: lane q of the quad sums the terms s = q, q + 4, ..
+        // in order and keeps those x_s, and the quad adds its four partial
+        // sums as (p0 + p1) + (p2 + p3) (the same value in every lane).  A's
+        // residue-permuted rows make each lane's terms one run of 16-byte
+        // words, read the same by every column (broadcast reads).  Column c
+        // of T' = T diag(beta) is written as row c of TT.
+        if (tid < 4 * kC) {
+            constexpr int MQ = kC / 4;  // terms per lane
+            const int c = tid >> 2, qd = tid & 3;
+            float xq[MQ];
+#pragma unroll
+            for (int m = 0; m < MQ; ++m)
+                xq[m] = 0.0f;
 #pragma unroll
             for (int r = 0; r < kC; ++r) {
-                float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                // terms s = 4 m + qd < r: m < (r - qd + 3) / 4
+                const int mq = (r - qd + 3) >> 2;
+                float part = 0.0f;
 #pragma unroll
-                for (int s4 = 0; 4 * s4 < r; ++s4) {
-                    const float4 a4 = *reinterpret_cast<const float4 *>(&S.T[r][4 * s4]);
+                for (int u = 0; 4 * u < (r + 3) / 4; ++u) {
+                    const float4 a4 = ld4(&S.A[r][qd * MQ + 4 * u]);
                     const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (4 * s4 + i < r)
-                            part[i] = __builtin_fmaf(av[i], x[4 * s4 + i], part[i]);
+                        if (4 * u + i < (r + 3) / 4)
+                            part = 4 * u + i < mq ? __builtin_fmaf(av[i], xq[4 * u + i], part) : part;
                 }
-                const float acc = ((r == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
-                x[r] = (r < c) ? 0.0f : acc;
+                float sum = part + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                              0, __builtin_bit_cast(int, part), 0xB1, 0xF, 0xF, false));
+                sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                          0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+                const float acc = ((r == c) ? 1.0f : 0.0f) - sum;
+                const float xr = (r < c) ? 0.0f : acc;
+                if ((r & 3) == qd)
+                    xq[r >> 2] = xr;
+            }
+            const float b = S.bt[c];
+#pragma unroll
+            for (int m = 0; m < MQ; ++m)
+                S.TT[c][4 * m + qd] = xq[m] * b;
+        }
+        __syncthreads();
+
+        // Delta = T' Y (into V's storage): row r sums s = 0 .. r in order.
+        {
+            rowv d0 = rowv{}, d1 = rowv{};
+            for (int sb = 0; sb <= ti; ++sb) {
+                rowv tt[TR];
+                float2 y[TR];
+#pragma unroll
+                for (int u = 0; u < TR; ++u) {
+                    tt[u] = rows(&S.TT[TR * sb + u][TR * ti]);
+                    y[u] = ld2(&S.Y[TR * sb + u][2 * tj]);
+                }
+#pragma unroll
+                for (int u = 0; u < TR; ++u)
+#pragma unroll
+                    for (int t = 0; t < TR; ++t) {
+                        const bool on = TR * sb + u <= TR * ti + t;
+                        d0[t] = on ? __builtin_fmaf(tt[u][t], y[u].x, d0[t]) : d0[t];
+                        d1[t] = on ? __builtin_fmaf(tt[u][t], y[u].y, d1[t]) : d1[t];
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < TR; ++t)
+                *reinterpret_cast<float2 *>(&S.V[TR * ti + t][2 * tj]) = float2{d0[t], d1[t]};
+        }
+        __syncthreads();
+        // O = scale (diag(exp gamma) Q M0 + P Delta), rows of this chunk only.
+        {
+            rowv q0 = rowv{}, q1 = rowv{}, p0v = rowv{}, p1v = rowv{};
+#pragma unroll 8
+            for (int d = 0; d < DK; ++d) {
+                const rowv qr = rows(&S.QT[d][TR * ti]);
+                const float2 m = ld2(&S.M[d][2 * tj]);
+#pragma unroll
+                for (int t = 0; t < TR; ++t) {
+                    q0[t] = __builtin_fmaf(qr[t], m.x, q0[t]);
+                    q1[t] = __builtin_fmaf(qr[t], m.y, q1[t]);
+                }
+            }
+            for (int sb = 0; sb <= ti; ++sb) {
+                rowv pr[TR];
+                float2 dl[TR];
+#pragma unroll
+                for (int u = 0; u < TR; ++u) {
+                    pr[u] = rows(&S.PT[TR * sb + u][TR * ti]);
+                    dl[u] = ld2(&S.V[TR * sb + u][2 * tj]);
+                }
+#pragma unroll
+                for (int u = 0; u < TR; ++u)
+#pragma unroll
+                    for (int t = 0; t < TR; ++t) {
+                        const bool on = TR * sb + u <= TR * ti + t;
+                        p0v[t] = on ? __builtin_fmaf(pr[u][t], dl[u].x, p0v[t]) : p0v[t];
+                        p1v[t] = on ? __builtin_fmaf(pr[u][t], dl[u].y, p1v[t]) : p1v[t];
+                    }
+            }
+#pragma unroll
+            for (int t = 0; t < TR; ++t) {
+                const int r = TR * ti + t;
+                if (r < L) {
+                    const float e = S.eg[r];
+                    *reinterpret_cast<float2 *>(o + ((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + 2 * tj) =
+                        float2{a.scale * (e * q0[t] + p0v[t]), a.scale * (e * q1[t] + p1v[t])};
+                }
             }
         }
         __syncthreads();
-        if (tid < kC)
+        // M_L = exp(gamma_L) M0 + K^T diag(exp(gamma_L - gamma)) Delta on keys
+        // TD ti .., columns 2 tj, 2 tj + 1, summed over the rows in order.
+        {
+            const float eL = expf(S.gam[kC - 1]);
+            float m0[TD], m1[TD];
 #pragma unroll
-            for (int r = 0; r < kC; ++r)
-                S.T[r][tid] = x[r] * S.bt[tid];
-        __syncthreads();
-
-        // Delta = T' Y (into V's storage), then the output and the state.
-        for (int e = tid; e < kC * kDVT; e += kThreads) {
-            const int r = e / kDVT, c = e % kDVT;
-            float acc = 0.0f;
-            for (int s = 0; s <= r; ++s)
-                acc += S.T[r][s] * S.Y[s][c];
-            S.V[r][c] = acc;
-        }
-        __syncthreads();
-        for (int e = tid; e < kC * kDVT; e += kThreads) {
-            const int r = e / kDVT, c = e % kDVT;
-            if (r >= L)
-                continue;
-            float qm = 0.0f;
-            for (int d = 0; d < DK; ++d)
-                qm += S.Q[r][d] * S.M[d][c];
-            float pd = 0.0f;
-            for (int s = 0; s <= r; ++s)
-                pd += S.P[r][s] * S.V[s][c];
-            o[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + c] = a.scale * (expf(S.gam[r]) * qm + pd);
-        }
-        __syncthreads();
-        const float gL = S.gam[kC - 1];
-        for (int e = tid; e < DK * kDVT; e += kThreads) {
-            const int d = e / kDVT, c = e % kDVT;
-            float acc = 0.0f;
-            for (int r = 0; r < kC; ++r)
-                acc += S.K[r][d] * S.el[r] * S.V[r][c];
-            S.M[d][c] = expf(gL) * S.M[d][c] + acc;
+            for (int t = 0; t < TD; ++t) {
+                m0[t] = 0.0f;
+                m1[t] = 0.0f;
+            }
+#pragma unroll 4
+            for (int r = 0; r < kC; r += 4) {
+                const float4 el4 = ld4(&S.el[r]);
+                const float elv[4] = {el4.x, el4.y, el4.z, el4.w};
+                float2 dl[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    dl[u] = ld2(&S.V[r + u][2 * tj]);
+#pragma unroll
+                for (int t = 0; t < TD; ++t) {
+                    const float4 k4 = ld4(&S.KT[TD * ti + t][r]);
+                    const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        m0[t] = __builtin_fmaf(kv[u] * elv[u], dl[u].x, m0[t]);
+                        m1[t] = __builtin_fmaf(kv[u] * elv[u], dl[u].y, m1[t]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TD; ++t) {
+                float *mp = &S.M[TD * ti + t][2 * tj];
+                const float2 old = ld2(mp);
+                *reinterpret_cast<float2 *>(mp) = float2{eL * old.x + m0[t], eL * old.y + m1[t]};
+            }
         }
     }
     __syncthreads();
