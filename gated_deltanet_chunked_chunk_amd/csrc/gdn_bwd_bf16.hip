@@ -299,9 +299,9 @@ __device__ __forceinline__ void rows_to_lds(uint16_t *tile, const void *src, int
 // ---------------------------------------------------------------------------
 // bwd_grads: per (chunk, q/k head), 512 threads, one persistent workgroup per
 // CU walking the (chunk, q/k head) items.  Each item's K and Q rows are
-// loaded into registers at the start of the item before it and stored to the
-// other half of the K/Q tiles once that item's value steps are done; its
-// first value step is loaded during that item's last one.  The barriers wait
+// loaded into registers once the value steps of the item before it are done
+// and stored to the other half of the K/Q tiles before that item's epilogue;
+// its first value step is loaded during that item's last one.  The barriers wait
 // for LDS operations only, so these loads stay in flight across them.  Wave
 // w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the half hd = w / 4 of
 // every [64 x *] result: of a 64-column value step the columns 32 hd ..,
@@ -410,8 +410,9 @@ __device__ __forceinline__ void grads_commit(GradSmem &S, const GradPre &pre, in
 // The next item's K and Q rows in registers: thread t holds 16-byte pieces
 // t + kGT u (row i / (dk / 8), piece i % (dk / 8)) of each; rows past L, and
 // every piece when there is no next item (a buffer of no bytes), read as
-// zeros.  Loaded at an item's start, stored to the other K/Q half of LDS once
-// the item's value steps are done.
+// zeros.  Loaded when an item's value steps are done (behind the next item's
+// first value step, so neither delays the loads of this item's steps),
+// stored to the other K/Q half of LDS before the item's dq/dk epilogue.
 template <int KX>
 struct KQPre {
     u32x4 k[KX / 2], q[KX / 2];
@@ -518,13 +519,12 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     // into LDS above, later ones stored from registers by every wave before
     // this barrier) and its first value step's loads, needed next, have
     // landed; every wave is past the previous item, whose tiles the other
-    // half held, so the next item's K and Q can be loaded for that half now.
+    // half held, so the next item's K and Q can go to that half.
     // Vector memory operations complete in order, so waiting until at most
     // KX are outstanding (the previous item's dq and dk stores) suffices.
     __builtin_amdgcn_s_waitcnt(0x0f70 | KX);  // vmcnt(KX)
     lds_barrier();
     KQPre<KX> kqn;
-    kq_issue<KX>(kqn, a, nitem < total ? ncl : cl, nitem < total ? nhk : hk, nitem < total, tid);
     const uint16_t *sK = S.KQ[par][0], *sQ = S.KQ[par][1];
 
     f32x4 dQ[4], dK[4];   // key tiles 4 hd + i
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
         }
         lds_barrier();  // every read of the step tiles is done: the D-phase tiles take their space
         if (gi + 1 == G)
-            kq_commit<KX>(S.KQ[par ^ 1][0], S.KQ[par ^ 1][1], kqn, tid);
+            kq_issue<KX>(kqn, a, nitem < total ? ncl : cl, nitem < total ? nhk : hk, nitem < total, tid);
 
         // Through A and P: D, S = diag(beta) (-dA * D), dP * D, and their
         // dbeta and dgamma terms.
@@ -794,6 +794,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
             }
         }
     }
+    kq_commit<KX>(S.KQ[par ^ 1][0], S.KQ[par ^ 1][1], kqn, tid);
     lds_barrier();  // the last head's readers of the state tiles are done
 
     // dq and dk through LDS, then 16-byte stores of whole rows.
