@@ -26,7 +26,7 @@ namespace gdn {
 namespace {
 
 constexpr int kDVT = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 template <int DK>
 constexpr int chunk_f32() {
@@ -59,20 +59,25 @@ __device__ __forceinline__ float2 ld2(const float *p) {
     return *reinterpret_cast<const float2 *>(p);
 }
 
-// Thread (i, j) = (tid / 16, tid % 16) owns register tiles of consecutive
-// rows TR i .. of the chunk (TR = C / 16) and, for [C x 32] results, the
-// value columns 2 j, 2 j + 1; for the C x C products the rows TR j .. of the
-// other operand; for the state update the keys TD i .. (TD = dk / 16).  Each
-// element is still one running sum in the order of its contraction index.
+// Thread (h, i, j) = (tid / 256, tid / 16 % 16, tid % 16) owns register
+// tiles of consecutive rows TR i .. of the chunk (TR = C / 16) and, for
+// [C x 32] results, the value column 2 j + h; for the C x C products the
+// columns TR j + TR/2 h .. + TR/2 - 1 of the other operand; for the state
+// update the keys TD i .. (TD = dk / 16).  Two waves share each SIMD, so one
+// waits for LDS while the other computes.  Each element is still one running
+// sum in the order of its contraction index.
 template <int DK>
 __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
     constexpr int kC = chunk_f32<DK>();
     constexpr int TR = kC / 16, TD = DK / 16;
+    constexpr int TH = TR / 2;  // columns of the C x C tile per thread
     typedef __attribute__((ext_vector_type(TR))) float rowv;
+    typedef __attribute__((ext_vector_type(TH))) float colv;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SmemF32<DK> &S = *reinterpret_cast<SmemF32<DK> *>(smem_raw);
     const int tid = threadIdx.x;
-    const int ti = tid >> 4, tj = tid & 15;
+    const int th = tid >> 8, ti = (tid >> 4) & 15, tj = tid & 15;
+    const int vc = 2 * tj + th;  // value column of the [C x 32] tiles
     const int n_tiles = a.dv / kDVT;
     const int G = a.Hv / a.Hqk;
     const int w = blockIdx.x;
@@ -104,6 +109,15 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         }
     };
 
+    auto cols = [](const float *p) {  // TH consecutive entries, 8-byte aligned when TH = 2
+        if constexpr (TH == 2) {
+            const float2 x = ld2(p);
+            return colv{x.x, x.y};
+        } else {
+            return colv{p[0]};
+        }
+    };
+
     for (int e = tid; e < DK * kDVT; e += kThreads) {
         const int i = e / kDVT, c = e % kDVT;
         S.M[i][c] = a.h0 ? a.h0[hbase + (int64_t)i * a.dv + c0 + c] : 0.0f;
@@ -119,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         // chunk's end load row L - 1 and are replaced by zeros (a select of
         // values: the loads stay unconditional).
         {
-            constexpr int KPT = kC * DK / (4 * kThreads), VPT = kC * kDVT / (4 * kThreads);
+            constexpr int KPT = kC * DK / (4 * kThreads);
+            constexpr int VPT = (kC * kDVT / 4 + kThreads - 1) / kThreads;
             f32x4 kr[KPT], qr[KPT], vr[VPT];
 #pragma unroll
             for (int i = 0; i < KPT; ++i) {
@@ -134,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int e = tid + kThreads * i, r = e / (kDVT / 4), c = 4 * (e % (kDVT / 4));
+                // pieces past the tile (at 32-token chunks, half the threads
+                // have none) load row 0 and are not stored
+                const int e = tid + kThreads * i, r = min(e / (kDVT / 4), kC - 1), c = 4 * (e % (kDVT / 4));
                 const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const f32x4 vx = *reinterpret_cast<const f32x4 *>(
                     v + ((p + min(r, L - 1)) * a.Hv + j) * (int64_t)a.dv + c0 + c);
@@ -153,7 +170,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int e = tid + kThreads * i, r = e / (kDVT / 4), c = 4 * (e % (kDVT / 4));
-                *reinterpret_cast<f32x4 *>(&S.V[r][c]) = vr[i];
+                if (e < kC * kDVT / 4)
+                    *reinterpret_cast<f32x4 *>(&S.V[r][c]) = vr[i];
             }
         }
         if (tid < 64) {
@@ -208,20 +226,21 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         // tile rows TR ti .., columns TR tj .. (tiles above the diagonal
         // are never read and not formed).
         if (tj <= ti) {
-            rowv kk[TR], qk[TR];  // [row t][column u]
+            const int s0 = TR * tj + TH * th;  // this thread's first column
+            colv kk[TR], qk[TR];  // [row t][column u]
 #pragma unroll
             for (int t = 0; t < TR; ++t) {
-                kk[t] = rowv{};
-                qk[t] = rowv{};
+                kk[t] = colv{};
+                qk[t] = colv{};
             }
 #pragma unroll 8
             for (int d = 0; d < DK; ++d) {
                 const rowv kr = rows(&S.KT[d][TR * ti]), qr = rows(&S.QT[d][TR * ti]);
-                const rowv ks = rows(&S.KT[d][TR * tj]);
+                const colv ks = cols(&S.KT[d][s0]);
 #pragma unroll
                 for (int t = 0; t < TR; ++t)
 #pragma unroll
-                    for (int u = 0; u < TR; ++u) {
+                    for (int u = 0; u < TH; ++u) {
                         kk[t][u] = __builtin_fmaf(kr[t], ks[u], kk[t][u]);
                         qk[t][u] = __builtin_fmaf(qr[t], ks[u], qk[t][u]);
                     }
@@ -229,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
             for (int t = 0; t < TR; ++t)
 #pragma unroll
-                for (int u = 0; u < TR; ++u) {
-                    const int r = TR * ti + t, s = TR * tj + u;
+                for (int u = 0; u < TH; ++u) {
+                    const int r = TR * ti + t, s = s0 + u;
                     const float dec = s <= r ? expf(S.gam[r] - S.gam[s]) : 0.0f;
                     S.A[r][(s & 3) * (kC / 4) + (s >> 2)] = s < r ? S.bt[r] * dec * kk[t][u] : 0.0f;
                     S.PT[s][r] = dec * qk[t][u];
@@ -238,23 +257,19 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         }
         // Y = V - diag(exp gamma) K M0 on rows TR ti .., columns 2 tj, 2 tj + 1.
         {
-            rowv x0 = rowv{}, x1 = rowv{};
+            rowv x0 = rowv{};
 #pragma unroll 8
             for (int d = 0; d < DK; ++d) {
                 const rowv kr = rows(&S.KT[d][TR * ti]);
-                const float2 m = ld2(&S.M[d][2 * tj]);
+                const float m = S.M[d][vc];
 #pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    x0[t] = __builtin_fmaf(kr[t], m.x, x0[t]);
-                    x1[t] = __builtin_fmaf(kr[t], m.y, x1[t]);
-                }
+                for (int t = 0; t < TR; ++t)
+                    x0[t] = __builtin_fmaf(kr[t], m, x0[t]);
             }
 #pragma unroll
             for (int t = 0; t < TR; ++t) {
                 const int r = TR * ti + t;
-                const float2 vv = ld2(&S.V[r][2 * tj]);
-                *reinterpret_cast<float2 *>(&S.Y[r][2 * tj]) =
-                    float2{vv.x - S.eg[r] * x0[t], vv.y - S.eg[r] * x1[t]};
+                S.Y[r][vc] = S.V[r][vc] - S.eg[r] * x0[t];
             }
         }
         __syncthreads();
@@ -306,67 +321,60 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
 
         // Delta = T' Y (into V's storage): row r sums s = 0 .. r in order.
         {
-            rowv d0 = rowv{}, d1 = rowv{};
+            rowv d0 = rowv{};
             for (int sb = 0; sb <= ti; ++sb) {
                 rowv tt[TR];
-                float2 y[TR];
+                float y[TR];
 #pragma unroll
                 for (int u = 0; u < TR; ++u) {
                     tt[u] = rows(&S.TT[TR * sb + u][TR * ti]);
-                    y[u] = ld2(&S.Y[TR * sb + u][2 * tj]);
+                    y[u] = S.Y[TR * sb + u][vc];
                 }
 #pragma unroll
                 for (int u = 0; u < TR; ++u)
 #pragma unroll
                     for (int t = 0; t < TR; ++t) {
                         const bool on = TR * sb + u <= TR * ti + t;
-                        d0[t] = on ? __builtin_fmaf(tt[u][t], y[u].x, d0[t]) : d0[t];
-                        d1[t] = on ? __builtin_fmaf(tt[u][t], y[u].y, d1[t]) : d1[t];
+                        d0[t] = on ? __builtin_fmaf(tt[u][t], y[u], d0[t]) : d0[t];
                     }
             }
 #pragma unroll
             for (int t = 0; t < TR; ++t)
-                *reinterpret_cast<float2 *>(&S.V[TR * ti + t][2 * tj]) = float2{d0[t], d1[t]};
+                S.V[TR * ti + t][vc] = d0[t];
         }
         __syncthreads();
         // O = scale (diag(exp gamma) Q M0 + P Delta), rows of this chunk only.
         {
-            rowv q0 = rowv{}, q1 = rowv{}, p0v = rowv{}, p1v = rowv{};
+            rowv q0 = rowv{}, p0v = rowv{};
 #pragma unroll 8
             for (int d = 0; d < DK; ++d) {
                 const rowv qr = rows(&S.QT[d][TR * ti]);
-                const float2 m = ld2(&S.M[d][2 * tj]);
+                const float m = S.M[d][vc];
 #pragma unroll
-                for (int t = 0; t < TR; ++t) {
-                    q0[t] = __builtin_fmaf(qr[t], m.x, q0[t]);
-                    q1[t] = __builtin_fmaf(qr[t], m.y, q1[t]);
-                }
+                for (int t = 0; t < TR; ++t)
+                    q0[t] = __builtin_fmaf(qr[t], m, q0[t]);
             }
             for (int sb = 0; sb <= ti; ++sb) {
                 rowv pr[TR];
-                float2 dl[TR];
+                float dl[TR];
 #pragma unroll
                 for (int u = 0; u < TR; ++u) {
                     pr[u] = rows(&S.PT[TR * sb + u][TR * ti]);
-                    dl[u] = ld2(&S.V[TR * sb + u][2 * tj]);
+                    dl[u] = S.V[TR * sb + u][vc];
                 }
 #pragma unroll
                 for (int u = 0; u < TR; ++u)
 #pragma unroll
                     for (int t = 0; t < TR; ++t) {
                         const bool on = TR * sb + u <= TR * ti + t;
-                        p0v[t] = on ? __builtin_fmaf(pr[u][t], dl[u].x, p0v[t]) : p0v[t];
-                        p1v[t] = on ? __builtin_fmaf(pr[u][t], dl[u].y, p1v[t]) : p1v[t];
+                        p0v[t] = on ? __builtin_fmaf(pr[u][t], dl[u], p0v[t]) : p0v[t];
                     }
             }
 #pragma unroll
             for (int t = 0; t < TR; ++t) {
                 const int r = TR * ti + t;
-                if (r < L) {
-                    const float e = S.eg[r];
-                    *reinterpret_cast<float2 *>(o + ((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + 2 * tj) =
-                        float2{a.scale * (e * q0[t] + p0v[t]), a.scale * (e * q1[t] + p1v[t])};
-                }
+                if (r < L)
+                    o[((p + r) * a.Hv + j) * (int64_t)a.dv + c0 + vc] = a.scale * (S.eg[r] * q0[t] + p0v[t]);
             }
         }
         __syncthreads();
@@ -374,36 +382,31 @@ __global__ __launch_bounds__(kThreads) void gdn_fwd_f32_kernel(FwdArgs a) {
         // TD ti .., columns 2 tj, 2 tj + 1, summed over the rows in order.
         {
             const float eL = expf(S.gam[kC - 1]);
-            float m0[TD], m1[TD];
+            float m0[TD];
 #pragma unroll
-            for (int t = 0; t < TD; ++t) {
+            for (int t = 0; t < TD; ++t)
                 m0[t] = 0.0f;
-                m1[t] = 0.0f;
-            }
 #pragma unroll 4
             for (int r = 0; r < kC; r += 4) {
                 const float4 el4 = ld4(&S.el[r]);
                 const float elv[4] = {el4.x, el4.y, el4.z, el4.w};
-                float2 dl[4];
+                float dl[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    dl[u] = ld2(&S.V[r + u][2 * tj]);
+                    dl[u] = S.V[r + u][vc];
 #pragma unroll
                 for (int t = 0; t < TD; ++t) {
                     const float4 k4 = ld4(&S.KT[TD * ti + t][r]);
                     const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        m0[t] = __builtin_fmaf(kv[u] * elv[u], dl[u].x, m0[t]);
-                        m1[t] = __builtin_fmaf(kv[u] * elv[u], dl[u].y, m1[t]);
-                    }
+                    for (int u = 0; u < 4; ++u)
+                        m0[t] = __builtin_fmaf(kv[u] * elv[u], dl[u], m0[t]);
                 }
             }
 #pragma unroll
             for (int t = 0; t < TD; ++t) {
-                float *mp = &S.M[TD * ti + t][2 * tj];
-                const float2 old = ld2(mp);
-                *reinterpret_cast<float2 *>(mp) = float2{eL * old.x + m0[t], eL * old.y + m1[t]};
+                float *mp = &S.M[TD * ti + t][vc];
+                *mp = eL * *mp + m0[t];
             }
         }
     }
