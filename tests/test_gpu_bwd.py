@@ -75,6 +75,22 @@ def test_bwd_grouped_dv64():
     check_bwd(d, 5100, label="grouped heads, dv=64")
 
 
+def test_bwd_grouped_dv128():
+    """Two value heads of 128 columns per q/k head: four value steps per
+    (chunk, q/k head) item of the gradient kernel."""
+    d = gi.make(1, 200, 1, 2, 128, 128, "bf16", 5150, h0_std=0.1)
+    check_bwd(d, 5150, scale=0.8, label="grouped heads, dv=128")
+
+
+def test_bwd_more_items_than_workgroups():
+    """260 (chunk, q/k head) items over 256 persistent workgroups: four walk
+    two items (the next item's K, Q and first value step loaded during the
+    first), the rest one (the loads for no next item read nothing), with a
+    ragged last chunk in each sequence."""
+    d = gi.make(2, 4100, 2, 2, 128, 128, "bf16", 5160, h0_std=0.05)
+    check_bwd(d, 5160, label="260 items")
+
+
 def test_bwd_packed_with_empty_document():
     cu = gi.cu_from_lengths([70, 0, 129, 1])
     d = gi.make(1, 200, 2, 4, 128, 128, "bf16", 5200, h0_std=0.05, cu_seqlens=cu)
