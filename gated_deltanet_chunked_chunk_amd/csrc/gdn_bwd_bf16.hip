@@ -301,10 +301,10 @@ __device__ __forceinline__ void rows_to_lds(uint16_t *tile, const void *src, int
 // CU walking the (chunk, q/k head) items.  Each item's K and Q rows are
 // loaded into registers once the value steps of the item before it are done
 // and stored to the other half of the K/Q tiles before that item's epilogue;
-// its first value step is loaded during that item's last one.  The barriers
-// wait for LDS operations only, so these loads stay in flight across them.
-// Wave w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the
-// half hd = w / 4 of every [64 x *] result: of a 64-column value step the columns 32 hd ..,
+// its first value step is loaded during that item's last one.  The barriers wait
+// for LDS operations only, so these loads stay in flight across them.  Wave
+// w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the half hd = w / 4 of
+// every [64 x *] result: of a 64-column value step the columns 32 hd ..,
 // of dq and dk the key tiles 4 hd .. 4 hd + 3, of the 64 x 64 products the
 // column tiles 2 hd, 2 hd + 1.  The value heads of the q/k head are taken in
 // turn, each in steps of 64 value columns whose tiles (v, do, Delta, drhs
@@ -486,9 +486,8 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     constexpr int kx_end = KX;
     // Persistent: workgroup b takes work items b, b + gridDim.x, ..., item i
     // being chunk i / Hqk and q/k head i % Hqk; chunks past the last
-    // document's (the packed bound) are skipped.  The next item's first
-    // value step is loaded during the current item's last step, its K and Q
-    // rows once the current item's value steps are done.
+    // document's (the packed bound) are skipped.  The next item's K, Q rows
+    // and first value step are loaded during the current item's last step.
     const int64_t total = a.n_chunks * a.Hqk;
     auto find = [&](int64_t from, ChunkLoc &c, int64_t &g, int &h) {
         for (int64_t i = from; i < total; i += gridDim.x) {
@@ -970,18 +969,19 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
     if (item >= total)
         return;
     GradPre256 pre;
-    grads_issue256(pre, a, cl, gc, hk * G, 0, tid);
-
-    while (true) {
-    {
-        // This item's K and Q rows: 32 rows of 512 bytes each, two 16-byte
-        // pieces per thread; rows past L read as zeros.
+    // An item's K and Q rows: 32 rows of 512 bytes each, two 16-byte pieces
+    // per thread; rows past L, and every piece when there is no item (a
+    // buffer of no bytes), read as zeros.  The first item's are loaded here,
+    // each next item's at the start of the epilogue of the item before (its
+    // last readers of K and Q are done; the registers stay free through the
+    // value steps and the D phase), and stored at the item's start.
+    u32x4 kv[2], qv[2];
+    auto kq_load = [&](const ChunkLoc &c, int h, bool any) {
         const uint32_t row_bytes = (uint32_t)a.Hqk * 256 * 2;
-        const uint32_t span = (uint32_t)(cl.L - 1) * row_bytes + 512;
-        const int64_t base = (cl.p * a.Hqk + hk) * (int64_t)256;
+        const uint32_t span = any ? (uint32_t)(c.L - 1) * row_bytes + 512 : 0u;
+        const int64_t base = (c.p * a.Hqk + h) * (int64_t)256;
         const __amdgpu_buffer_rsrc_t rk = rsrc_uniform(static_cast<const uint16_t *>(a.k) + base, span);
         const __amdgpu_buffer_rsrc_t rq = rsrc_uniform(static_cast<const uint16_t *>(a.q) + base, span);
-        u32x4 kv[2], qv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = tid + kGT * u;
@@ -989,6 +989,12 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
             kv[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
             qv[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
         }
+    };
+    kq_load(cl, hk, true);
+    grads_issue256(pre, a, cl, gc, hk * G, 0, tid);
+
+    while (true) {
+    {
         lds_barrier();  // the previous item's readers are done
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -1216,6 +1222,7 @@ __global__ __launch_bounds__(kGT) void bwd_grads_k256(BwdArgs a) {
         }
     }
     lds_barrier();  // the last head's readers of the state tiles are done
+    kq_load(nitem < total ? ncl : cl, nitem < total ? nhk : hk, nitem < total);
 
     // dq and dk through LDS, then 16-byte stores of whole rows.
     {
