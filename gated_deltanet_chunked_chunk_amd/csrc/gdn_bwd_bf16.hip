@@ -301,10 +301,10 @@ __device__ __forceinline__ void rows_to_lds(uint16_t *tile, const void *src, int
 // CU walking the (chunk, q/k head) items.  Each item's K and Q rows are
 // loaded into registers once the value steps of the item before it are done
 // and stored to the other half of the K/Q tiles before that item's epilogue;
-// its first value step is loaded during that item's last one.  The barriers wait
-// for LDS operations only, so these loads stay in flight across them.  Wave
-// w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the half hd = w / 4 of
-// every [64 x *] result: of a 64-column value step the columns 32 hd ..,
+// its first value step is loaded during that item's last one.  The barriers
+// wait for LDS operations only, so these loads stay in flight across them.
+// Wave w works on the chunk's rows [16 rb, 16 rb + 16), rb = w % 4, and the
+// half hd = w / 4 of every [64 x *] result: of a 64-column value step the columns 32 hd ..,
 // of dq and dk the key tiles 4 hd .. 4 hd + 3, of the 64 x 64 products the
 // column tiles 2 hd, 2 hd + 1.  The value heads of the q/k head are taken in
 // turn, each in steps of 64 value columns whose tiles (v, do, Delta, drhs
@@ -486,8 +486,9 @@ __global__ __launch_bounds__(kGT) void bwd_grads(BwdArgs a) {
     constexpr int kx_end = KX;
     // Persistent: workgroup b takes work items b, b + gridDim.x, ..., item i
     // being chunk i / Hqk and q/k head i % Hqk; chunks past the last
-    // document's (the packed bound) are skipped.  The next item's K, Q rows
-    // and first value step are loaded during the current item's last step.
+    // document's (the packed bound) are skipped.  The next item's first
+    // value step is loaded during the current item's last step, its K and Q
+    // rows once the current item's value steps are done.
     const int64_t total = a.n_chunks * a.Hqk;
     auto find = [&](int64_t from, ChunkLoc &c, int64_t &g, int &h) {
         for (int64_t i = from; i < total; i += gridDim.x) {
