@@ -1638,13 +1638,18 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     f32x4 h[NH];
     Stage st;
     int meet = 0, dmeet = 0;
-    // Issue priority on the shared SIMDs follows the critical paths: the
-    // state waves' chain first, then helper 0 (diagonal blocks and their
-    // inverses); helpers 1..3 fill the gaps.
+    // Issue priority on the shared SIMDs follows the critical paths.  Where
+    // the state waves form an output (Modes 0, 2) or run the reverse chain
+    // (Mode 4), their chain is the longest: state waves first, then helper 0
+    // (diagonal blocks and their inverses), helpers 1..3 filling the gaps.
+    // Where they form no output (piece ends, Mode 1; the backward's forward
+    // state pass, Mode 3) they finish their chunk step before helper 0 does,
+    // so helper 0 goes first there.
+    constexpr bool kHelper0First = Mode == 1 || Mode == 3;
     if (state)
-        __builtin_amdgcn_s_setprio(3);
+        __builtin_amdgcn_s_setprio(kHelper0First ? 2 : 3);
     else if (s == 0)
-        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_s_setprio(kHelper0First ? 3 : 2);
     if (state) {
         const float *src = nullptr;
         if (Mode == 4)  // the reverse pass starts from the final state's gradient
