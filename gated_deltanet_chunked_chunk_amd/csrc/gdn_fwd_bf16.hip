@@ -1644,12 +1644,15 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
     // (diagonal blocks and their inverses), helpers 1..3 filling the gaps.
     // Where they form no output (piece ends, Mode 1; the backward's forward
     // state pass, Mode 3) they finish their chunk step before helper 0 does,
-    // so helper 0 goes first there.
+    // so helper 0 goes first there.  With the in-op preparation helpers 1..3
+    // carry the row norms as well and go before the default.
     constexpr bool kHelper0First = Mode == 1 || Mode == 3;
     if (state)
         __builtin_amdgcn_s_setprio(kHelper0First ? 2 : 3);
     else if (s == 0)
         __builtin_amdgcn_s_setprio(kHelper0First ? 3 : 2);
+    else if (Prep)
+        __builtin_amdgcn_s_setprio(1);
     if (state) {
         const float *src = nullptr;
         if (Mode == 4)  // the reverse pass starts from the final state's gradient
