@@ -1709,7 +1709,11 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
                 // the state leaving it (Mode 4): the tiles 2 k and 2 k + 1
                 // hold keys 32 k + 8 lg .. + 7 of column col in order, one
                 // 16-byte store.  The rows are 128 keys wide at dk = 64 and
-                // 128 (zeros past DK), 256 at dk = 256.
+                // 128 (zeros past DK), 256 at dk = 256.  Non-temporal: the
+                // gradient kernel reads them once, after the other pass has
+                // streamed its own data through the caches (dk = 256
+                // backward 3.26 -> 3.19 ms; the same for the Delta, drhs and
+                // dV rows made the dk = 128 backward twice as slow).
                 constexpr int SW = DK == 256 ? 256 : kDK;
                 uint16_t *dst = (Mode == 3 ? a.chunk_states : a.chunk_dstates) +
                                 ((chunk0 + c) * a.Hv + it.j) * (int64_t)a.dv * SW +
@@ -1717,7 +1721,8 @@ __global__ __launch_bounds__(kThreads, 1) void gdn_fwd_bf16(FwdArgs a) {
 #pragma unroll
                 for (int mt = 0; mt < NH; mt += 2) {
                     const u32x2 lo = pack4(h[mt]), hi = pack4(h[mt + 1]);
-                    *reinterpret_cast<u32x4 *>(dst + key_of(mt, lg, 0)) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y},
+                                                reinterpret_cast<u32x4 *>(dst + key_of(mt, lg, 0)));
                 }
             }
             if constexpr (Mode == 4 && DK == 256)
